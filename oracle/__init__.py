@@ -1,0 +1,124 @@
+"""Plain fp64 CPU oracle for the selective state-space scan and decode step.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke``
+and by the CPU-baseline leg of ``bench.py``.  The HIP library never imports,
+links or calls anything here, and nothing here imports the HIP library.
+
+The arithmetic lives in ``oracle.c`` (compiled with gcc into
+``liboracle.so``); this module only widens inputs to float64 numpy arrays and
+calls it.  The page citations for every step are in the header of
+``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+             "-shared", "-fPIC", "-std=c11"]
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile ``src`` with gcc into the shared library ``out``."""
+    cmd = ["gcc", *GCC_FLAGS, "-o", out + ".tmp", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _declare(lib):
+    i64, dp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.oracle_scan.restype = c_int
+    lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [c_int]
+    lib.oracle_decode_step.restype = c_int
+    lib.oracle_decode_step.argtypes = [i64, i64, i64] + [dp] * 9
+    lib.oracle_zoh.restype = None
+    lib.oracle_zoh.argtypes = [ctypes.c_double, ctypes.c_double,
+                               ctypes.POINTER(ctypes.c_double),
+                               ctypes.POINTER(ctypes.c_double)]
+    return lib
+
+
+def load_library(path: str | None = None):
+    """Load a compiled oracle library (building the default one if absent)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _f64(a):
+    """Widen any array-like (numpy or CPU torch tensor) to contiguous float64."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: exact widening through float64
+        a = a.detach().to("cpu")
+        import torch
+        a = a.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def zoh(delta: float, a: float):
+    """(Abar, Bbar/B) for one diagonal entry, from the compiled oracle."""
+    lib = load_library()
+    abar, bcoef = ctypes.c_double(), ctypes.c_double()
+    lib.oracle_zoh(float(delta), float(a), ctypes.byref(abar), ctypes.byref(bcoef))
+    return abar.value, bcoef.value
+
+
+def scan(x, delta, A, B, C, D=None, z=None, h0=None, nthreads: int = 0, lib=None):
+    """Selective scan in fp64.  Shapes: x, delta, z [b, L, d]; B, C [b, L, n];
+    A [d, n]; D [d]; h0 [b, d, n].  Returns (y [b, L, d], h_last [b, d, n])."""
+    lib = lib or load_library()
+    x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
+    D, z, h0 = _f64(D), _f64(z), _f64(h0)
+    batch, seqlen, dim = x.shape
+    dstate = A.shape[1]
+    assert delta.shape == x.shape and A.shape == (dim, dstate)
+    assert B.shape == (batch, seqlen, dstate) and C.shape == B.shape
+    assert D is None or D.shape == (dim,)
+    assert z is None or z.shape == x.shape
+    assert h0 is None or h0.shape == (batch, dim, dstate)
+    y = np.zeros_like(x)
+    h_last = np.zeros((batch, dim, dstate), dtype=np.float64)
+    rc = lib.oracle_scan(batch, seqlen, dim, dstate, _ptr(x), _ptr(delta), _ptr(A),
+                         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+                         _ptr(h_last), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan rejected its arguments (code {rc})")
+    return y, h_last
+
+
+def decode_step(h, x, delta, A, B, C, D=None, z=None, lib=None):
+    """One recurrent step.  h [b, d, n] float64 numpy array, updated in place;
+    x, delta, z [b, d]; B, C [b, n].  Returns y [b, d]."""
+    lib = lib or load_library()
+    assert isinstance(h, np.ndarray) and h.dtype == np.float64 and h.flags.c_contiguous
+    x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
+    D, z = _f64(D), _f64(z)
+    batch, dim, dstate = h.shape
+    y = np.zeros((batch, dim), dtype=np.float64)
+    rc = lib.oracle_decode_step(batch, dim, dstate, _ptr(h), _ptr(x), _ptr(delta),
+                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_step rejected its arguments (code {rc})")
+    return y

@@ -1,0 +1,303 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes a loaded oracle library (``oracle.load_library``)
+and raises AssertionError when the oracle disagrees with what the pages or
+mathematics fix.  ``test_oracle_pins.py`` runs them on the real oracle and
+``test_oracle_mutants.py`` runs them on copies of the oracle with a planted
+mistake, each of which must be caught by at least one pin.
+
+What pins what (pages cited by title and section):
+
+* ZOH discretisation: integrating the continuous system h' = A h + B x with x
+  held over the step (RK4, 10^4 substeps) must land on Abar h0 + Bbar x
+  (paperlens tutorial, eq.(1)/(2) and the zero-order-hold prose; ultralytics
+  glossary, section on how SSMs work).
+* Recurrence and readout: with delta, B, C constant the scan must equal the
+  convolution with kernel K_k = C . (Abar^k * Bbar), re-running the glossary's
+  worked example (L=64, N=16, delta=0.1) and random variants (ultralytics
+  glossary worked example; paperlens tutorial, section "S4: 再帰は畳み込みでもある").
+* delta -> 0 leaves the state unchanged; large delta overwrites it with the
+  current input (paperlens tutorial, prose under eq.(2) and the selection
+  section).
+* Brute force: explicit unrolled products/sums on tiny inputs.
+* Closed form of one step with the D term and the SiLU gate (ihouse article,
+  output equation; agenticai-flow guide, block diagram).
+* Linearity in (x, h0) without the gate, and associativity of chunking
+  (paperlens tutorial, section on the parallel scan).
+* L decode steps equal one scan (paperlens tutorial, S4 section: recurrent and
+  convolutional faces give the same outputs).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def _rand_problem(rng, b, L, d, n, with_d=True, with_z=True, with_h0=True,
+                  dmin=0.001, dmax=0.5):
+    x = rng.standard_normal((b, L, d))
+    delta = rng.uniform(dmin, dmax, (b, L, d))
+    A = -rng.uniform(0.5, 1.5, (d, n))
+    B = rng.standard_normal((b, L, n))
+    C = rng.standard_normal((b, L, n))
+    D = rng.standard_normal(d) if with_d else None
+    z = rng.standard_normal((b, L, d)) if with_z else None
+    h0 = rng.standard_normal((b, d, n)) if with_h0 else None
+    return dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h0)
+
+
+def _rel(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return float(np.max(np.abs(a - b)) / max(1e-300, np.max(np.abs(b))))
+
+
+# --------------------------------------------------------------------------
+# ZOH against the ODE it discretises
+# --------------------------------------------------------------------------
+def _rk4_step_diag(a, bx, h, dt):
+    k1 = a * h + bx
+    k2 = a * (h + 0.5 * dt * k1) + bx
+    k3 = a * (h + 0.5 * dt * k2) + bx
+    k4 = a * (h + dt * k3) + bx
+    return h + dt / 6.0 * (k1 + 2 * k2 + 2 * k3 + k4)
+
+
+def _integrate(a, bx, h0, delta, steps=10_000):
+    """h' = a h + bx over [0, delta] from h0, classic RK4 (vectorised over n)."""
+    h = np.array(h0, dtype=np.float64)
+    dt = delta / steps
+    for _ in range(steps):
+        h = _rk4_step_diag(a, bx, h, dt)
+    return h
+
+
+def pin_zoh_matches_ode(lib):
+    rng = _rng(11)
+    n = 8
+    for delta in (1e-3, 0.05, 0.3, 1.7):
+        A = np.concatenate([-rng.uniform(0.5, 1.5, n - 2), [0.7, -3e-4]])
+        B = rng.standard_normal(n)
+        x = float(rng.standard_normal())
+        h0 = rng.standard_normal(n)
+        _, h_last = oracle.scan(np.full((1, 1, 1), x), np.full((1, 1, 1), delta),
+                                A[None, :], B[None, None, :], np.zeros((1, 1, n)),
+                                h0=h0[None, None, :], lib=lib)
+        ref = _integrate(A, B * x, h0, delta)
+        err = np.max(np.abs(h_last[0, 0] - ref) / (1.0 + np.abs(ref)))
+        assert err < 1e-12, f"ZOH vs ODE (delta={delta}): {err}"
+
+
+# --------------------------------------------------------------------------
+# Recurrence against the convolution form (constant delta, B, C)
+# --------------------------------------------------------------------------
+def _conv_form(A, B, C, delta, x):
+    """y_t = sum_{k<=t} K_k x_{t-k},  K_k = C . (Abar^k * Bbar)."""
+    Abar = np.exp(delta * A)
+    Bbar = (Abar - 1.0) / A * B
+    L = len(x)
+    K = np.array([C @ (Abar ** k * Bbar) for k in range(L)])
+    return np.array([K[: t + 1][::-1] @ x[: t + 1] for t in range(L)])
+
+
+def _scan_const(lib, A, B, C, delta, x):
+    L, n = len(x), len(A)
+    y, _ = oracle.scan(x.reshape(1, L, 1), np.full((1, L, 1), delta), A[None, :],
+                       np.broadcast_to(B, (1, L, n)), np.broadcast_to(C, (1, L, n)),
+                       lib=lib)
+    return y[0, :, 0]
+
+
+def pin_worked_example_recurrence_equals_convolution(lib):
+    with open(os.path.join(GOLDEN, "worked_example_recurrence_vs_convolution.json")) as f:
+        g = json.load(f)
+    import torch  # the example draws its inputs with torch's seeded CPU RNG
+
+    torch.manual_seed(g["torch_seed"])
+    L, N = g["L"], g["N"]
+    x = torch.randn(L).double().numpy()
+    A = (-(torch.rand(N) + 0.5)).double().numpy()
+    B = torch.randn(N).double().numpy()
+    C = torch.randn(N).double().numpy()
+    delta = g["delta"]
+    y_rec = _scan_const(lib, A, B, C, delta, x)
+    y_conv = _conv_form(A, B, C, delta, x)
+    # the page's own check (atol 1e-5) reports True ...
+    assert bool(np.allclose(y_rec, y_conv, atol=g["atol"], rtol=0)) == g["expected"]
+    # ... and in fp64 the two forms agree to rounding
+    assert _rel(y_rec, y_conv) < 1e-12
+
+
+def pin_random_recurrence_equals_convolution(lib):
+    rng = _rng(12)
+    for L, n, delta in ((40, 4, 0.02), (97, 16, 0.3), (33, 7, 1.3)):
+        A = -rng.uniform(0.05, 2.0, n)
+        B, C, x = rng.standard_normal(n), rng.standard_normal(n), rng.standard_normal(L)
+        assert _rel(_scan_const(lib, A, B, C, delta, x), _conv_form(A, B, C, delta, x)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# delta limits
+# --------------------------------------------------------------------------
+def pin_delta_zero_keeps_state(lib):
+    rng = _rng(13)
+    p = _rand_problem(rng, 2, 9, 3, 5)
+    p["delta"] = np.zeros_like(p["delta"])
+    y, h_last = oracle.scan(lib=lib, **p)
+    assert np.array_equal(h_last, p["h0"]), "delta=0 must leave the state bit-for-bit"
+    # y_t = (C_t . h0 + D x_t) * SiLU(z_t)
+    ch = np.einsum("bln,bdn->bld", p["C"], p["h0"])
+    ref = (ch + p["D"][None, None, :] * p["x"]) * _silu(p["z"])
+    assert _rel(y, ref) < 1e-14
+
+
+def pin_large_delta_overwrites_state(lib):
+    rng = _rng(14)
+    p = _rand_problem(rng, 1, 6, 2, 4, with_z=False, with_d=False)
+    p["delta"] = np.full_like(p["delta"], 60.0)
+    p["A"] = -rng.uniform(0.5, 1.5, p["A"].shape)
+    y, h_last = oracle.scan(lib=lib, **p)
+    # state forgets everything but the last token: h = -B x / A
+    ref_h = -p["B"][0, -1][None, :] * p["x"][0, -1][:, None] / p["A"]
+    assert _rel(h_last[0], ref_h) < 1e-12
+    ref_y = np.einsum("ln,ldn->ld", p["C"][0],
+                      -p["B"][0][:, None, :] * p["x"][0][:, :, None] / p["A"][None])
+    assert _rel(y[0], ref_y) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# brute force, closed form, linearity, chunking, decode
+# --------------------------------------------------------------------------
+def _brute_force(p):
+    x, delta, A, B, C, D, z, h0 = (p[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0"))
+    b, L, d = x.shape
+    n = A.shape[1]
+    y = np.zeros_like(x)
+    for bi in range(b):
+        for di in range(d):
+            a = [np.exp(delta[bi, s, di] * A[di]) for s in range(L)]          # Abar_s
+            u = [(a[s] - 1.0) / A[di] * B[bi, s] * x[bi, s, di] for s in range(L)]
+            for t in range(L):
+                h = np.prod(a[: t + 1], axis=0) * (h0[bi, di] if h0 is not None else 0.0)
+                for s in range(t + 1):
+                    decay = np.prod(a[s + 1: t + 1], axis=0) if s < t else np.ones(n)
+                    h = h + decay * u[s]
+                pre = C[bi, t] @ h + (D[di] if D is not None else 0.0) * x[bi, t, di]
+                y[bi, t, di] = pre * _silu(z[bi, t, di]) if z is not None else pre
+    return y
+
+
+def pin_brute_force_tiny(lib):
+    rng = _rng(15)
+    for (b, L, d, n) in ((1, 1, 1, 1), (2, 7, 3, 4), (1, 16, 4, 2), (2, 5, 2, 3)):
+        for flags in ((True, True, True), (False, False, False), (True, False, True)):
+            p = _rand_problem(rng, b, L, d, n, *flags)
+            y, _ = oracle.scan(lib=lib, **p)
+            assert _rel(y, _brute_force(p)) < 1e-12, (b, L, d, n, flags)
+
+
+def pin_single_step_closed_form(lib):
+    rng = _rng(16)
+    for _ in range(5):
+        delta, a = rng.uniform(0.01, 2.0), -rng.uniform(0.1, 3.0)
+        x, h0, Bv, Cv, Dv, zv = rng.standard_normal(6)
+        y, h = oracle.scan(np.full((1, 1, 1), x), np.full((1, 1, 1), delta),
+                           np.full((1, 1), a), np.full((1, 1, 1), Bv),
+                           np.full((1, 1, 1), Cv), np.full(1, Dv),
+                           np.full((1, 1, 1), zv), np.full((1, 1, 1), h0), lib=lib)
+        abar = np.exp(delta * a)
+        hn = abar * h0 + (abar - 1.0) / a * Bv * x
+        ref = (Cv * hn + Dv * x) * zv / (1.0 + np.exp(-zv))
+        assert abs(y[0, 0, 0] - ref) <= 1e-14 * (1 + abs(ref))
+        assert abs(h[0, 0, 0] - hn) <= 1e-14 * (1 + abs(hn))
+
+
+def pin_linearity(lib):
+    rng = _rng(17)
+    p1 = _rand_problem(rng, 2, 20, 3, 6, with_z=False)
+    p2 = dict(p1, x=rng.standard_normal(p1["x"].shape), h0=rng.standard_normal(p1["h0"].shape))
+    al, be = 0.7, -1.9
+    p3 = dict(p1, x=al * p1["x"] + be * p2["x"], h0=al * p1["h0"] + be * p2["h0"])
+    (y1, h1), (y2, h2), (y3, h3) = (oracle.scan(lib=lib, **p) for p in (p1, p2, p3))
+    assert _rel(y3, al * y1 + be * y2) < 1e-12
+    assert _rel(h3, al * h1 + be * h2) < 1e-12
+
+
+def _slice_t(p, lo, hi):
+    q = dict(p)
+    for k in ("x", "delta", "B", "C", "z"):
+        if q[k] is not None:
+            q[k] = np.ascontiguousarray(q[k][:, lo:hi])
+    return q
+
+
+def pin_chunk_split(lib):
+    rng = _rng(18)
+    p = _rand_problem(rng, 2, 50, 3, 5)
+    y, h = oracle.scan(lib=lib, **p)
+    for cut in (1, 17, 49):
+        ya, ha = oracle.scan(lib=lib, **_slice_t(p, 0, cut))
+        yb, hb = oracle.scan(lib=lib, **dict(_slice_t(p, cut, 50), h0=ha))
+        assert _rel(np.concatenate([ya, yb], axis=1), y) < 1e-12
+        assert _rel(hb, h) < 1e-12
+
+
+def pin_decode_equals_scan(lib):
+    rng = _rng(19)
+    p = _rand_problem(rng, 2, 12, 4, 6)
+    y, h_last = oracle.scan(lib=lib, **p)
+    h = np.ascontiguousarray(p["h0"].copy())
+    for t in range(12):
+        yt = oracle.decode_step(h, p["x"][:, t], p["delta"][:, t], p["A"], p["B"][:, t],
+                                p["C"][:, t], p["D"], p["z"][:, t], lib=lib)
+        assert _rel(yt, y[:, t]) < 1e-12
+    assert _rel(h, h_last) < 1e-12
+
+
+def pin_stability_bound(lib):
+    rng = _rng(20)
+    p = _rand_problem(rng, 1, 200, 2, 8, with_z=False, with_d=False)
+    _, h = oracle.scan(lib=lib, **p)
+    bound = np.abs(p["h0"][0]).copy()
+    for s in range(200):
+        abar = np.exp(p["delta"][0, s][:, None] * p["A"])
+        bound += np.abs((abar - 1) / p["A"] * p["B"][0, s][None, :] * p["x"][0, s][:, None])
+    assert np.all(np.abs(h[0]) <= bound * (1 + 1e-12))
+
+
+def pin_zero_A_is_the_limit(lib):
+    rng = _rng(21)
+    p = _rand_problem(rng, 1, 30, 2, 3)
+    p["A"][:, 1] = 0.0
+    y0, h0 = oracle.scan(lib=lib, **p)
+    for eps in (1e-9, -1e-9):
+        q = dict(p, A=p["A"].copy())
+        q["A"][:, 1] = eps
+        y1, h1 = oracle.scan(lib=lib, **q)
+        assert _rel(y0, y1) < 1e-7 and _rel(h0, h1) < 1e-7
+
+
+def pin_empty_sequence(lib):
+    rng = _rng(22)
+    p = _rand_problem(rng, 2, 0, 3, 4)
+    y, h = oracle.scan(lib=lib, **p)
+    assert y.shape == (2, 0, 3) and np.array_equal(h, p["h0"])
+    q = dict(p, h0=None)
+    _, h = oracle.scan(lib=lib, **q)
+    assert np.all(h == 0.0)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

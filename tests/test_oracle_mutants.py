@@ -1,0 +1,63 @@
+"""Each plausible mistake planted in a copy of the oracle must fail a pin.
+
+The mutants are textual edits of ``oracle/oracle.c`` compiled into temporary
+libraries on the CPU; the real oracle is never modified.  If an edit's target
+text is no longer found, the test fails loudly so the list stays in step with
+the source.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "drop_skip_term": ("double pre = s + dval * xv;", "double pre = s;"),
+    "wrong_sign_in_exp": ("*abar = exp(u);", "*abar = exp(-u);"),
+    "euler_instead_of_zoh": ("*bbar_coef = (a != 0.0) ? expm1(u) / a : delta;",
+                             "*bbar_coef = delta;"),
+    "zero_A_limit_wrong": ("*bbar_coef = (a != 0.0) ? expm1(u) / a : delta;",
+                           "*bbar_coef = (a != 0.0) ? expm1(u) / a : 0.0;"),
+    "C_used_for_B": ("bcoef * B[bc + n] * xv", "bcoef * C[bc + n] * xv"),
+    "state_index_reversed": ("A[d * dstate + n]", "A[d * dstate + (dstate - 1 - n)]"),
+    "no_decay": ("h[n] = abar * h[n] + bcoef", "h[n] = h[n] + bcoef"),
+    "previous_token_B_C": ("int64_t bc = (b * seqlen + t) * dstate;",
+                           "int64_t bc = (b * seqlen + (t > 0 ? t - 1 : 0)) * dstate;"),
+    "h0_ignored": ("h[n] = h0 ? h0[ch * dstate + n] : 0.0;", "h[n] = 0.0;"),
+    "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    "gate_without_silu": ("pre * silu(z[io])", "pre * z[io]"),
+    "readout_before_update": (
+        "        /* state update first: h_t = Abar_t h_{t-1} + Bbar_t x_t */",
+        "        double s0 = 0.0;\n"
+        "        for (int64_t n = 0; n < dstate; ++n) s0 += C[bc + n] * h[n];"),
+    "half_state_read": ("for (int64_t n = 0; n < dstate; ++n) s += C[bc + n] * h[n];",
+                        "for (int64_t n = 0; n < dstate / 2; ++n) s += C[bc + n] * h[n];"),
+}
+
+
+def _fixup(name, src):
+    # the readout-before-update mutant also needs the readout to use s0
+    if name == "readout_before_update":
+        src = src.replace("double pre = s + dval * xv;", "double pre = s0 + dval * xv;")
+    return src
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle._SRC) as f:
+        src = f.read()
+    assert old in src, f"mutation target for {name!r} not found in oracle.c"
+    src = _fixup(name, src.replace(old, new, 1))
+    path = tmp_path / "mutant.c"
+    path.write_text(src)
+    so = oracle.build(str(path), str(tmp_path / "libmutant.so"))
+    lib = oracle.load_library(so)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name!r} passed every pin"

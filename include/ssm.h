@@ -1,0 +1,146 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
+ *
+ * The library computes, per channel d and state index n of a diagonal SSM,
+ *   zero-order hold:  Abar = exp(delta_t * A),  Bbar = (Abar - 1) / A * B_t
+ *   recurrence:       h_t  = Abar * h_{t-1} + Bbar * x_t          (state first)
+ *   readout + gate:   y_t  = (C_t . h_t + D * x_t) * SiLU(z_t)
+ * with delta, B and C given per token and A fixed per (channel, state).
+ * Sources (web pages, cited by title and section):
+ *   - ultralytics glossary "State Space Models (SSM)", section "SSMの仕組み":
+ *     ZOH formulas, the recurrence, and the recurrent/convolution equivalence;
+ *   - paperlens tutorial "Mamba と状態空間モデル": eq.(1)/(2) (continuous
+ *     system and its discretisation), section "Mamba: 状態を「選択的」にする"
+ *     (per-token delta, B, C with fixed A) and the practice notes (state
+ *     snapshot/restore, no silent slow fallback);
+ *   - ihouse article on Mamba-3: the state and output equations with the D
+ *     term, and the decode step being a memory-bound outer-product update;
+ *   - agenticai-flow guide, section "アーキテクチャ図解": the S6 output is
+ *     multiplied by SiLU of the z branch.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major memory,
+ *     16-byte aligned (misaligned pointers return SSM_ERR_INVALID_ARG).
+ *   - The caller owns every buffer, including the workspace; the library
+ *     allocates no device memory and keeps no mutable global state, so
+ *     concurrent calls on different streams are safe.
+ *   - Calls only enqueue work on `stream` (a hipStream_t, NULL = the null
+ *     stream) and never synchronise the host.  Argument errors are returned
+ *     before anything is enqueued; launch failures return SSM_ERR_HIP;
+ *     asynchronous device faults surface at the caller's next synchronisation.
+ *   - There is no fallback: a shape, dtype or state size without a kernel
+ *     returns SSM_ERR_UNSUPPORTED instead of running a slow path.
+ *   - io_dtype selects the type of x, delta, z, B, C and y (all the same).
+ *     A, D and every state tensor are always fp32; arithmetic is fp32.
+ *   - dstate must be 16.
+ *   - NaN/Inf in inputs propagate by IEEE rules; nothing is checked on device.
+ */
+#ifndef SSM_H_
+#define SSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+/* Values of the io_dtype arguments. */
+#define SSM_DTYPE_F32 0
+#define SSM_DTYPE_BF16 1
+
+/* Status codes returned by every entry point. */
+#define SSM_OK 0
+#define SSM_ERR_INVALID_ARG 1 /* NULL required pointer, negative size, aliasing */
+#define SSM_ERR_UNSUPPORTED 2 /* valid request with no kernel (e.g. dstate != 16) */
+#define SSM_ERR_WORKSPACE 3   /* workspace missing or smaller than required */
+#define SSM_ERR_HIP 4         /* a HIP runtime call or kernel launch failed */
+
+/* Version of this ABI (SSM_ABI_VERSION). */
+int ssm_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *ssm_status_str(int status);
+
+/*
+ * Execution plan of a scan: `waves_per_group` (1, 2, 4, 8 or 16) wavefronts
+ * share one group of 64 channels, each owning 16/waves_per_group state
+ * indices; the sequence is cut into `nchunks` chunks that run in parallel
+ * and are stitched by a cross-chunk carry.  The plan changes only the
+ * schedule, never the definition of the result.
+ *
+ * ssm_scan_plan() fills in the plan ssm_scan_fwd() uses for these sizes.
+ * Returns SSM_ERR_INVALID_ARG for negative sizes or NULL outputs.
+ */
+int ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                  int io_dtype, int *waves_per_group, int *nchunks);
+
+/*
+ * Device workspace, in bytes, that ssm_scan_fwd_planned() needs for a scan
+ * cut into `nchunks` chunks (nchunks <= 0: the automatic plan's count, i.e.
+ * what ssm_scan_fwd() needs).  It holds the per-chunk carry state.
+ * Returns -1 for invalid sizes.  A result of 0 means no workspace is needed.
+ */
+int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
+                                 int64_t dstate, int io_dtype, int nchunks);
+
+/*
+ * Selective scan over a whole sequence (forward).
+ *   x, delta, z, y : [batch, seqlen, dim]  io_dtype.  delta is the step size
+ *                    after any softplus, i.e. used as given.
+ *   A              : [dim, dstate] fp32 (real diagonal; A == 0 uses the limit
+ *                    Bbar = delta * B).
+ *   B, C           : [batch, seqlen, dstate] io_dtype, shared by all channels.
+ *   Dskip          : [dim] fp32, NULL => D = 0.
+ *   z              : NULL => no gate (y = C.h + D x).
+ *   h0             : [batch, dim, dstate] fp32 initial state, NULL => zeros.
+ *   y              : output.  h_last: [batch, dim, dstate] fp32 final state,
+ *                    NULL => not written.
+ *   workspace      : device buffer of at least ssm_scan_workspace_bytes(...)
+ *                    bytes (may be NULL when that is 0).
+ * Outputs must not alias inputs (exact pointer equality is rejected).
+ * seqlen == 0 writes h_last (= h0, or zeros) when given and nothing else;
+ * batch == 0 or dim == 0 is a no-op.  Returns an SSM_* status.
+ */
+int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                 int io_dtype, const void *x, const void *delta, const float *A,
+                 const void *B, const void *C, const float *Dskip, const void *z,
+                 const float *h0, void *y, float *h_last, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
+ * ssm_scan_fwd with an explicit plan (for tests and tuning).  A value <= 0
+ * for waves_per_group or nchunks takes the automatic choice for that field.
+ * nchunks is clamped to [1, seqlen].  Unsupported waves_per_group values
+ * return SSM_ERR_UNSUPPORTED.  The workspace must be sized with the same
+ * nchunks.
+ */
+int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int io_dtype, const void *x,
+                         const void *delta, const float *A, const void *B,
+                         const void *C, const float *Dskip, const void *z,
+                         const float *h0, void *y, float *h_last,
+                         void *workspace, size_t workspace_bytes,
+                         int waves_per_group, int nchunks, void *stream);
+
+/*
+ * One recurrent decode step for one new token per sequence (paperlens
+ * tutorial, S4 section and practice notes: constant time and memory per
+ * token; ihouse article, decode arithmetic intensity).
+ *   h        : [batch, dim, dstate] fp32, read and updated IN PLACE.
+ *   x, delta, z, y : [batch, dim] io_dtype.  B, C : [batch, dstate] io_dtype.
+ *   A [dim, dstate] fp32; Dskip [dim] fp32 (NULL => 0); z NULL => no gate.
+ * The result equals one step of ssm_scan_fwd with h0 = h.  y must not alias
+ * an input.  batch == 0 or dim == 0 is a no-op.  Returns an SSM_* status.
+ */
+int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
+                    float *h, const void *x, const void *delta, const float *A,
+                    const void *B, const void *C, const float *Dskip,
+                    const void *z, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_H_ */

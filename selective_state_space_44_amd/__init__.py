@@ -1,0 +1,206 @@
+"""Selective state-space scan (the S6 core of Mamba) on MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/ssm.h`` (library
+``libssm.so``, built in-tree by ``selective_state_space_44_amd._build``).
+This module only checks and marshals arguments: tensors are PyTorch device
+tensors (PyTorch provides device memory and the current stream); every step
+of the computation runs in the HIP kernels.  There is no fallback path: if
+the library is missing or a request has no kernel, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["scan_fwd", "decode_step", "scan_plan", "scan_workspace_bytes", "load_library",
+           "LIB_PATH", "SsmError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm.so")
+
+SSM_DTYPE_F32 = 0
+SSM_DTYPE_BF16 = 1
+SSM_OK = 0
+SSM_ERR_INVALID_ARG = 1
+SSM_ERR_UNSUPPORTED = 2
+SSM_ERR_WORKSPACE = 3
+SSM_ERR_HIP = 4
+
+# Every symbol include/ssm.h declares, with its ctypes signature.
+_i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "ssm_abi_version": (_int, []),
+    "ssm_status_str": (ctypes.c_char_p, [_int]),
+    "ssm_scan_plan": (_int, [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(_int),
+                             ctypes.POINTER(_int)]),
+    "ssm_scan_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _int, _int]),
+    "ssm_scan_fwd": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10 + [_vp, _sz, _vp]),
+    "ssm_scan_fwd_planned": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
+                             + [_vp, _sz, _int, _int, _vp]),
+    "ssm_decode_step": (_int, [_i64, _i64, _i64, _int] + [_vp] * 9 + [_vp]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)}")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libssm.so (raises OSError if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise OSError(f"{path} is missing: build it with "
+                              "`python -m selective_state_space_44_amd._build`")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype, fn.argtypes = res, args
+            _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load_library().ssm_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != SSM_OK:
+        raise SsmError(status, what)
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return SSM_DTYPE_F32
+    if dtype == torch.bfloat16:
+        return SSM_DTYPE_BF16
+    raise ValueError(f"unsupported I/O dtype {dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def scan_plan(batch: int, seqlen: int, dim: int, dstate: int = 16,
+              dtype: torch.dtype = torch.bfloat16):
+    """(waves_per_group, nchunks) that ``scan_fwd`` uses for these sizes."""
+    g, k = ctypes.c_int(), ctypes.c_int()
+    _check(load_library().ssm_scan_plan(batch, seqlen, dim, dstate, _io_code(dtype),
+                                        ctypes.byref(g), ctypes.byref(k)), "ssm_scan_plan")
+    return g.value, k.value
+
+
+def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16,
+                         dtype: torch.dtype = torch.bfloat16, nchunks: int = 0) -> int:
+    n = load_library().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, _io_code(dtype),
+                                                nchunks)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False,
+             waves_per_group: int = 0, nchunks: int = 0, out=None, workspace=None):
+    """Selective scan.  x, delta, z: [batch, L, dim]; B, C: [batch, L, dstate]
+    (all float32 or all bfloat16); A [dim, dstate], D [dim], h0
+    [batch, dim, dstate] float32.  Returns y (and the final state when
+    ``return_last_state``).  ``waves_per_group``/``nchunks`` override the
+    automatic plan (0 = automatic)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a [batch, seqlen, dim] tensor")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    batch, seqlen, dim = x.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a [dim, dstate] tensor")
+    dstate = A.shape[1]
+    io = x.dtype
+    code = _io_code(io)
+    _require(x, "x", (batch, seqlen, dim), io, device)
+    _require(delta, "delta", (batch, seqlen, dim), io, device)
+    _require(A, "A", (dim, dstate), torch.float32, device)
+    _require(B, "B", (batch, seqlen, dstate), io, device)
+    _require(C, "C", (batch, seqlen, dstate), io, device)
+    _require(D, "D", (dim,), torch.float32, device)
+    _require(z, "z", (batch, seqlen, dim), io, device)
+    _require(h0, "h0", (batch, dim, dstate), torch.float32, device)
+    if delta is None or B is None or C is None:
+        raise ValueError("delta, B and C are required")
+    y = out if out is not None else torch.empty_like(x)
+    _require(y, "out", (batch, seqlen, dim), io, device)
+    h_last = (torch.empty((batch, dim, dstate), dtype=torch.float32, device=device)
+              if return_last_state else None)
+    lib = load_library()
+    nbytes = lib.ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, code, nchunks)
+    if nbytes < 0:
+        raise ValueError("invalid sizes")
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_scan_fwd_planned(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
+                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                  _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,
+                                  int(waves_per_group), int(nchunks), _stream(device))
+    _check(st, "ssm_scan_fwd")
+    return (y, h_last) if return_last_state else y
+
+
+def decode_step(h, x, delta, A, B, C, D=None, z=None, out=None):
+    """One recurrent step.  h: [batch, dim, dstate] float32, updated in place;
+    x, delta, z: [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16);
+    A [dim, dstate], D [dim] float32.  Returns y [batch, dim]."""
+    if not isinstance(h, torch.Tensor) or h.dim() != 3:
+        raise ValueError("h must be a [batch, dim, dstate] tensor")
+    device = h.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    batch, dim, dstate = h.shape
+    if not isinstance(x, torch.Tensor):
+        raise ValueError("x must be a tensor")
+    io = x.dtype
+    code = _io_code(io)
+    _require(h, "h", (batch, dim, dstate), torch.float32, device)
+    _require(x, "x", (batch, dim), io, device)
+    _require(delta, "delta", (batch, dim), io, device)
+    _require(A, "A", (dim, dstate), torch.float32, device)
+    _require(B, "B", (batch, dstate), io, device)
+    _require(C, "C", (batch, dstate), io, device)
+    _require(D, "D", (dim,), torch.float32, device)
+    _require(z, "z", (batch, dim), io, device)
+    if delta is None or A is None or B is None or C is None:
+        raise ValueError("delta, A, B and C are required")
+    y = out if out is not None else torch.empty_like(x)
+    _require(y, "out", (batch, dim), io, device)
+    st = load_library().ssm_decode_step(batch, dim, dstate, code, _ptr(h), _ptr(x),
+                                        _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                        _ptr(z), _ptr(y), _stream(device))
+    _check(st, "ssm_decode_step")
+    return y

@@ -1,0 +1,217 @@
+// ssm_abi.cpp -- the extern "C" entry points declared in include/ssm.h:
+// argument validation (entirely on the host, before any HIP call), the
+// execution plan, workspace carving and dispatch to the kernels.
+
+#include "ssm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "ssm_launch.h"
+
+namespace {
+
+constexpr int64_t kWave = 64;
+constexpr int64_t kDState = 16;
+// Design point of the schedule: MI355X has 256 CUs x 4 SIMDs.  The scan's
+// inner loop is bound by VALU issue, which needs several resident waves per
+// SIMD; the plan aims for at least this many waves in flight.
+constexpr int64_t kTargetWaves = 256 * 4 * 4;
+constexpr int64_t kMinChunk = 256;  // shortest chunk the plan will cut
+
+bool valid_dtype(int t) { return t == SSM_DTYPE_F32 || t == SSM_DTYPE_BF16; }
+
+// Automatic plan: the cheapest schedule is one wave per 64 channels holding
+// all 16 states (no cross-wave reduction, no carry).  Split the states over
+// more waves first (each halving costs a little cross-wave work), and cut the
+// sequence into chunks (which costs a second pass over all but the last chunk)
+// only when even 16 waves per group leave the GPU short of waves.
+void auto_plan(int64_t batch, int64_t seqlen, int64_t dim, int* G, int* K) {
+  const int64_t groups = batch * ((dim + kWave - 1) / kWave);
+  int g = 1;
+  while (g < 16 && groups * g < kTargetWaves) g *= 2;
+  int64_t k = 1;
+  if (groups * g < kTargetWaves) {
+    k = (kTargetWaves + groups * g - 1) / (groups * g);
+    k = std::min<int64_t>(k, std::max<int64_t>(1, seqlen / kMinChunk));
+  }
+  *G = g;
+  *K = (int)std::max<int64_t>(1, k);
+}
+
+constexpr int64_t kMaxGridYZ = 65535;  // HIP limit on grid.y and grid.z
+
+// The kernels address one chunk of an [b, L, dim] tensor with 32-bit byte
+// offsets; a chunk spans at most this many bytes.
+constexpr int64_t kMaxChunkBytes = (int64_t)1 << 31;
+
+// Number of chunks actually used for a request of `nchunks`: raised so that
+// no chunk exceeds kMaxChunkBytes, clamped to [1, min(seqlen, grid limit)],
+// then reduced so that, with every chunk ceil(seqlen / nchunks) long, none
+// is empty.
+int effective_chunks(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks) {
+  if (seqlen <= 0) return 1;
+  const int64_t row = std::max<int64_t>(1, dim) * (io_dtype == SSM_DTYPE_BF16 ? 2 : 4);
+  const int64_t max_rows = std::max<int64_t>(1, kMaxChunkBytes / row);
+  nchunks = std::max<int64_t>(nchunks, (seqlen + max_rows - 1) / max_rows);
+  int64_t k = std::max<int64_t>(1, std::min<int64_t>({nchunks, seqlen, kMaxGridYZ}));
+  const int64_t len = (seqlen + k - 1) / k;
+  return (int)((seqlen + len - 1) / len);
+}
+
+bool sizes_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  return batch >= 0 && seqlen >= 0 && dim >= 0 && dstate > 0 &&
+         dim <= (int64_t)INT32_MAX && batch <= (int64_t)INT32_MAX;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
+
+// Every tensor pointer must be 16-byte aligned (the kernels use 16-byte
+// vector and 4-byte scalar accesses on these bases).
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+template <typename... P> bool all_aligned(P... p) { return (aligned(p) && ...); }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_str(int status) {
+  switch (status) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG: invalid argument";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: no kernel for this request";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "SSM_ERR_UNKNOWN: unknown status code";
+}
+
+int ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                  int* waves_per_group, int* nchunks) {
+  if (!waves_per_group || !nchunks || !sizes_ok(batch, seqlen, dim, dstate) ||
+      !valid_dtype(io_dtype))
+    return SSM_ERR_INVALID_ARG;
+  auto_plan(batch, seqlen, dim, waves_per_group, nchunks);
+  *nchunks = effective_chunks(seqlen, dim, io_dtype, *nchunks);
+  return SSM_OK;
+}
+
+int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                 int io_dtype, int nchunks) {
+  if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype)) return -1;
+  if (nchunks <= 0) {
+    int g;
+    auto_plan(batch, seqlen, dim, &g, &nchunks);
+  }
+  nchunks = effective_chunks(seqlen, dim, io_dtype, nchunks);
+  return (int64_t)ssm::scan_workspace_layout(batch, dim, nchunks).total;
+}
+
+int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int io_dtype, const void* x, const void* delta, const float* A,
+                         const void* B, const void* C, const float* Dskip, const void* z,
+                         const float* h0, void* y, float* h_last, void* workspace,
+                         size_t workspace_bytes, int waves_per_group, int nchunks,
+                         void* stream) {
+  if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype))
+    return SSM_ERR_INVALID_ARG;
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (dstate != kDState) return SSM_ERR_UNSUPPORTED;
+  if (!A) return SSM_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (seqlen == 0) {
+    if (!h_last) return SSM_OK;
+    if ((const void*)h_last == (const void*)h0 || (const void*)h_last == (const void*)A)
+      return SSM_ERR_INVALID_ARG;
+    if (!all_aligned(h0, h_last)) return SSM_ERR_INVALID_ARG;
+    return hip_status(ssm::launch_copy_state(h0, h_last, batch * dim * kDState, s));
+  }
+  if (!x || !delta || !B || !C || !y) return SSM_ERR_INVALID_ARG;
+  // outputs must not alias any input
+  const void* ins[] = {x, delta, A, B, C, Dskip, z, h0};
+  for (const void* in : ins) {
+    if (!in) continue;
+    if (in == y || in == (const void*)h_last) return SSM_ERR_INVALID_ARG;
+  }
+  if ((const void*)h_last == y) return SSM_ERR_INVALID_ARG;
+  if (!all_aligned(x, delta, A, B, C, Dskip, z, h0, y, h_last, workspace))
+    return SSM_ERR_INVALID_ARG;
+  if (batch > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+
+  int G = 0, K = 0;
+  auto_plan(batch, seqlen, dim, &G, &K);
+  if (waves_per_group > 0) G = waves_per_group;
+  if (nchunks > 0) K = nchunks;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return SSM_ERR_UNSUPPORTED;
+  K = effective_chunks(seqlen, dim, io_dtype, K);
+
+  const ssm::ScanWorkspace ws = ssm::scan_workspace_layout(batch, dim, K);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return SSM_ERR_WORKSPACE;
+  for (const void* in : ins)
+    if (in && workspace && in == workspace) return SSM_ERR_INVALID_ARG;
+
+  ssm::ScanArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.y = y;
+  a.h_last = h_last;
+  char* wsb = static_cast<char*>(workspace);
+  a.ws_hloc = ws.total ? reinterpret_cast<float*>(wsb + ws.hloc_off) : nullptr;
+  a.ws_hin = ws.total ? reinterpret_cast<float*>(wsb + ws.hin_off) : nullptr;
+  a.ws_sdelta = ws.total ? reinterpret_cast<double*>(wsb + ws.sdelta_off) : nullptr;
+  a.seqlen = seqlen;
+  a.chunk_len = (seqlen + K - 1) / K;
+  a.nchunks = K;
+  a.dim = (int)dim;
+  a.batch = (int)batch;
+  return hip_status(ssm::launch_scan(a, io_dtype == SSM_DTYPE_BF16, G, s));
+}
+
+int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 const void* x, const void* delta, const float* A, const void* B,
+                 const void* C, const float* Dskip, const void* z, const float* h0, void* y,
+                 float* h_last, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssm_scan_fwd_planned(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip,
+                              z, h0, y, h_last, workspace, workspace_bytes, 0, 0, stream);
+}
+
+int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* h,
+                    const void* x, const void* delta, const float* A, const void* B,
+                    const void* C, const float* Dskip, const void* z, void* y,
+                    void* stream) {
+  if (!sizes_ok(batch, 1, dim, dstate) || !valid_dtype(io_dtype)) return SSM_ERR_INVALID_ARG;
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (dstate != kDState) return SSM_ERR_UNSUPPORTED;
+  if (batch * dim * 4 / 256 >= (int64_t)UINT32_MAX) return SSM_ERR_UNSUPPORTED;
+  if (!h || !x || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARG;
+  const void* ins[] = {x, delta, A, B, C, Dskip, z};
+  for (const void* in : ins)
+    if (in && (in == y || in == (const void*)h)) return SSM_ERR_INVALID_ARG;
+  if ((const void*)h == y) return SSM_ERR_INVALID_ARG;
+  if (!all_aligned(h, x, delta, A, B, C, Dskip, z, y)) return SSM_ERR_INVALID_ARG;
+  ssm::DecodeArgs a{};
+  a.h = h;
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.z = z;
+  a.y = y;
+  a.batch = batch;
+  a.dim = (int)dim;
+  return hip_status(ssm::launch_decode(a, io_dtype == SSM_DTYPE_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

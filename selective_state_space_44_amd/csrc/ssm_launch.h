@@ -1,0 +1,65 @@
+// ssm_launch.h -- internal interface between the C ABI (ssm_abi.cpp) and the
+// HIP kernels (ssm_scan.hip, ssm_decode.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Everything a scan launch needs.  Sizes are validated by the ABI layer.
+struct ScanArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;  // nullable
+  const void* z;       // nullable
+  const float* h0;     // nullable
+  void* y;
+  float* h_last;       // nullable
+  // carry workspace (only when nchunks > 1)
+  float* ws_hloc;      // [batch, nchunks, dim, 16]  chunk-local end state from zero
+  float* ws_hin;       // [batch, nchunks, dim, 16]  state entering each chunk
+  double* ws_sdelta;   // [batch, nchunks, dim]      sum of delta over each chunk
+  int64_t seqlen;
+  int64_t chunk_len;
+  int dim;
+  int batch;
+  int nchunks;
+};
+
+struct DecodeArgs {
+  float* h;
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;  // nullable
+  const void* z;       // nullable
+  void* y;
+  int64_t batch;
+  int dim;
+};
+
+// Byte layout of the scan workspace for `nchunks` chunks (0 if nchunks <= 1).
+struct ScanWorkspace {
+  size_t hloc_off, hin_off, sdelta_off, total;
+};
+ScanWorkspace scan_workspace_layout(int64_t batch, int64_t dim, int nchunks);
+
+// Enqueue a full scan.  io_bf16 selects the I/O type; waves_per_group is one
+// of 1, 2, 4, 8, 16.  Returns hipSuccess or the launch error.
+hipError_t launch_scan(const ScanArgs& a, bool io_bf16, int waves_per_group,
+                       hipStream_t stream);
+
+// Enqueue the seqlen == 0 case: h_last = h0 (or zeros).
+hipError_t launch_copy_state(const float* h0, float* h_last, int64_t count,
+                             hipStream_t stream);
+
+hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, hipStream_t stream);
+
+}  // namespace ssm

@@ -1,0 +1,116 @@
+"""C ABI on the host: the library loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_44_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ssm.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert {"ssm_scan_fwd", "ssm_decode_step"} <= set(names)
+    assert set(names) == set(ssm.SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ssm_abi_version() == 1
+    for code in range(5):
+        assert lib.ssm_status_str(code).startswith(b"SSM_")
+    assert b"UNKNOWN" in lib.ssm_status_str(99)
+
+
+def _scan(lib, batch=2, L=8, dim=64, N=16, io=1, x=FAKE, delta=FAKE, A=FAKE, B=FAKE,
+          C=FAKE, D=None, z=None, h0=None, y=ctypes.c_void_p(0x2000), h_last=None,
+          ws=None, ws_bytes=0, G=0, K=0):
+    return lib.ssm_scan_fwd_planned(batch, L, dim, N, io, x, delta, A, B, C, D, z, h0, y,
+                                    h_last, ws, ws_bytes, G, K, None)
+
+
+def test_scan_rejects_bad_arguments(lib):
+    assert _scan(lib, batch=-1) == ssm.SSM_ERR_INVALID_ARG
+    assert _scan(lib, L=-1) == ssm.SSM_ERR_INVALID_ARG
+    assert _scan(lib, io=7) == ssm.SSM_ERR_INVALID_ARG
+    assert _scan(lib, x=None) == ssm.SSM_ERR_INVALID_ARG
+    assert _scan(lib, A=None) == ssm.SSM_ERR_INVALID_ARG
+    assert _scan(lib, y=None) == ssm.SSM_ERR_INVALID_ARG
+    assert _scan(lib, y=FAKE) == ssm.SSM_ERR_INVALID_ARG               # y aliases x
+    assert _scan(lib, h_last=FAKE) == ssm.SSM_ERR_INVALID_ARG          # h_last aliases x
+    assert _scan(lib, N=8) == ssm.SSM_ERR_UNSUPPORTED                   # no kernel, no fallback
+    assert _scan(lib, N=32) == ssm.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, G=3) == ssm.SSM_ERR_UNSUPPORTED
+    # a chunked plan without workspace
+    assert _scan(lib, L=4096, K=4) == ssm.SSM_ERR_WORKSPACE
+    need = lib.ssm_scan_workspace_bytes(2, 4096, 64, 16, 1, 4)
+    assert need > 0
+    assert _scan(lib, L=4096, K=4, ws=ctypes.c_void_p(0x3000), ws_bytes=need - 1) \
+        == ssm.SSM_ERR_WORKSPACE
+
+
+def test_scan_noop_sizes_return_ok_without_launch(lib):
+    assert _scan(lib, batch=0) == ssm.SSM_OK
+    assert _scan(lib, dim=0) == ssm.SSM_OK
+    assert _scan(lib, L=0) == ssm.SSM_OK        # no h_last requested: nothing to do
+
+
+def test_decode_rejects_bad_arguments(lib):
+    def dec(batch=2, dim=64, N=16, io=1, h=ctypes.c_void_p(0x5000), x=FAKE,
+            y=ctypes.c_void_p(0x2000)):
+        return lib.ssm_decode_step(batch, dim, N, io, h, x, FAKE, FAKE, FAKE, FAKE, None,
+                                   None, y, None)
+    assert dec(batch=-1) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(h=None) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(y=FAKE) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(h=FAKE) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(N=4) == ssm.SSM_ERR_UNSUPPORTED
+    assert dec(io=2) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(batch=0) == ssm.SSM_OK
+
+
+def test_plan_and_workspace(lib):
+    g, k = ssm.scan_plan(4, 4096, 5120)
+    assert g in (1, 2, 4, 8, 16) and k >= 1
+    assert ssm.scan_workspace_bytes(4, 4096, 5120, nchunks=1) == 0
+    # hloc + hin (fp32 per state) + sum of delta (fp64 per channel), per chunk
+    n = ssm.scan_workspace_bytes(1, 1000, 100, nchunks=3)
+    assert n >= 2 * 3 * 100 * 16 * 4 + 3 * 100 * 8
+    # the chunk count is clamped to the sequence length
+    assert ssm.scan_workspace_bytes(1, 2, 100, nchunks=50) == \
+        ssm.scan_workspace_bytes(1, 2, 100, nchunks=2)
+    # the long single sequence is cut into chunks for parallelism
+    g3, k3 = ssm.scan_plan(1, 262144, 4096)
+    assert k3 > 1
+    with pytest.raises(ValueError):
+        ssm.scan_workspace_bytes(-1, 10, 10)
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        ssm.scan_fwd(x, x, torch.zeros(8, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))
+    with pytest.raises(ValueError):
+        ssm.decode_step(torch.zeros(1, 8, 16), torch.zeros(1, 8), torch.zeros(1, 8),
+                        torch.zeros(8, 16), torch.zeros(1, 16), torch.zeros(1, 16))

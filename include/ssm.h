@@ -65,7 +65,7 @@ int ssm_abi_version(void);
 const char *ssm_status_str(int status);
 
 /*
- * Execution plan of a scan: `waves_per_group` (1, 2, 4, 8 or 16) wavefronts
+ * Execution plan of a scan: `waves_per_group` (2, 4, 8 or 16) wavefronts
  * share one group of 64 channels, each owning 16/waves_per_group state
  * indices; the sequence is cut into `nchunks` chunks that run in parallel
  * and are stitched by a cross-chunk carry.  The plan changes only the
@@ -124,6 +124,26 @@ int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim,
                          const float *h0, void *y, float *h_last,
                          void *workspace, size_t workspace_bytes,
                          int waves_per_group, int nchunks, void *stream);
+
+/*
+ * The two phases of a chunked scan, for callers that enqueue them apart
+ * (e.g. to time or overlap them):
+ *   phase 1 -- every chunk but the last is run from a zero state and the
+ *              chunk end states are composed into the state entering each
+ *              chunk, written to the workspace (a no-op when nchunks == 1);
+ *   phase 2 -- the main pass: every chunk from its entering state, writing y
+ *              and h_last (reads the workspace written by phase 1);
+ *   phase 3 -- both, in order (what ssm_scan_fwd_planned enqueues).
+ * Arguments, plan and workspace are those of ssm_scan_fwd_planned and must be
+ * identical for the two phases of one scan.  Other phase values return
+ * SSM_ERR_INVALID_ARG.
+ */
+int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int io_dtype, const void *x, const void *delta,
+                       const float *A, const void *B, const void *C,
+                       const float *Dskip, const void *z, const float *h0, void *y,
+                       float *h_last, void *workspace, size_t workspace_bytes,
+                       int waves_per_group, int nchunks, int phase, void *stream);
 
 /*
  * One recurrent decode step for one new token per sequence (paperlens

@@ -39,6 +39,8 @@ SIGNATURES = {
     "ssm_scan_fwd": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10 + [_vp, _sz, _vp]),
     "ssm_scan_fwd_planned": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
                              + [_vp, _sz, _int, _int, _vp]),
+    "ssm_scan_fwd_phase": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
+                           + [_vp, _sz, _int, _int, _int, _vp]),
     "ssm_decode_step": (_int, [_i64, _i64, _i64, _int] + [_vp] * 9 + [_vp]),
 }
 
@@ -127,12 +129,15 @@ def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16,
 
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False,
-             waves_per_group: int = 0, nchunks: int = 0, out=None, workspace=None):
+             waves_per_group: int = 0, nchunks: int = 0, out=None, workspace=None,
+             phase: int = 3):
     """Selective scan.  x, delta, z: [batch, L, dim]; B, C: [batch, L, dstate]
     (all float32 or all bfloat16); A [dim, dstate], D [dim], h0
     [batch, dim, dstate] float32.  Returns y (and the final state when
     ``return_last_state``).  ``waves_per_group``/``nchunks`` override the
-    automatic plan (0 = automatic)."""
+    automatic plan (0 = automatic); ``phase`` 1 or 2 enqueues only the chunk
+    carry passes or only the main pass (see ssm_scan_fwd_phase); both phases
+    of one scan must get the same ``workspace`` and ``out``."""
     if not isinstance(x, torch.Tensor) or x.dim() != 3:
         raise ValueError("x must be a [batch, seqlen, dim] tensor")
     device = x.device
@@ -165,10 +170,11 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
     if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.ssm_scan_fwd_planned(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
-                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                                  _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,
-                                  int(waves_per_group), int(nchunks), _stream(device))
+    st = lib.ssm_scan_fwd_phase(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
+                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,
+                                int(waves_per_group), int(nchunks), int(phase),
+                                _stream(device))
     _check(st, "ssm_scan_fwd")
     return (y, h_last) if return_last_state else y
 

@@ -17,26 +17,24 @@ constexpr int64_t kDState = 16;
 // Design point of the schedule: MI355X has 256 CUs x 4 SIMDs.  The scan's
 // inner loop is bound by VALU issue, which needs several resident waves per
 // SIMD; the plan aims for at least this many waves in flight.
-constexpr int64_t kTargetWaves = 256 * 4 * 4;
+// Design point of the schedule (MI355X: 256 CUs).  The scan's inner loop is
+// bound by VALU issue, which needs several resident waves per SIMD; measured
+// on the benchmark shapes, 4 waves per 64-channel group (4 states each) with
+// the sequence cut so that about five such blocks exist per CU is fastest,
+// even though every chunk but the last then runs a second, cheaper pass.
+constexpr int64_t kCUs = 256;
+constexpr int64_t kTargetBlocks = 5 * kCUs;
 constexpr int64_t kMinChunk = 256;  // shortest chunk the plan will cut
 
 bool valid_dtype(int t) { return t == SSM_DTYPE_F32 || t == SSM_DTYPE_BF16; }
 
-// Automatic plan: the cheapest schedule is one wave per 64 channels holding
-// all 16 states (no cross-wave reduction, no carry).  Split the states over
-// more waves first (each halving costs a little cross-wave work), and cut the
-// sequence into chunks (which costs a second pass over all but the last chunk)
-// only when even 16 waves per group leave the GPU short of waves.
+// Automatic plan: 4 waves per group of 64 channels, and enough chunks to
+// reach about kTargetBlocks blocks (never chunks shorter than kMinChunk).
 void auto_plan(int64_t batch, int64_t seqlen, int64_t dim, int* G, int* K) {
   const int64_t groups = batch * ((dim + kWave - 1) / kWave);
-  int g = 1;
-  while (g < 16 && groups * g < kTargetWaves) g *= 2;
-  int64_t k = 1;
-  if (groups * g < kTargetWaves) {
-    k = (kTargetWaves + groups * g - 1) / (groups * g);
-    k = std::min<int64_t>(k, std::max<int64_t>(1, seqlen / kMinChunk));
-  }
-  *G = g;
+  int64_t k = (kTargetBlocks + groups / 2) / std::max<int64_t>(1, groups);
+  k = std::min<int64_t>(k, std::max<int64_t>(1, seqlen / kMinChunk));
+  *G = 4;
   *K = (int)std::max<int64_t>(1, k);
 }
 
@@ -46,18 +44,29 @@ constexpr int64_t kMaxGridYZ = 65535;  // HIP limit on grid.y and grid.z
 // offsets; a chunk spans at most this many bytes.
 constexpr int64_t kMaxChunkBytes = (int64_t)1 << 31;
 
-// Number of chunks actually used for a request of `nchunks`: raised so that
-// no chunk exceeds kMaxChunkBytes, clamped to [1, min(seqlen, grid limit)],
-// then reduced so that, with every chunk ceil(seqlen / nchunks) long, none
-// is empty.
+// Chunk length for a request of `nchunks`: at least enough chunks that none
+// exceeds kMaxChunkBytes, at most min(seqlen, grid limit); the length is
+// rounded up to whole tiles (chunks start on a tile boundary).
+int64_t chunk_length(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks) {
+  if (seqlen <= 0) return 1;
+  const int64_t tile = ssm::scan_tile_steps();
+  const int64_t row = std::max<int64_t>(1, dim) * (io_dtype == SSM_DTYPE_BF16 ? 2 : 4);
+  const int64_t max_rows = std::max<int64_t>(tile, (kMaxChunkBytes / row) / tile * tile);
+  nchunks = std::max<int64_t>(nchunks, (seqlen + max_rows - 1) / max_rows);
+  const int64_t k = std::max<int64_t>(1, std::min<int64_t>({nchunks, seqlen, kMaxGridYZ}));
+  const int64_t len = (seqlen + k - 1) / k;
+  return (len + tile - 1) / tile * tile;
+}
+
+// Number of chunks of length chunk_length(...) covering the sequence.
 int effective_chunks(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks) {
   if (seqlen <= 0) return 1;
-  const int64_t row = std::max<int64_t>(1, dim) * (io_dtype == SSM_DTYPE_BF16 ? 2 : 4);
-  const int64_t max_rows = std::max<int64_t>(1, kMaxChunkBytes / row);
-  nchunks = std::max<int64_t>(nchunks, (seqlen + max_rows - 1) / max_rows);
-  int64_t k = std::max<int64_t>(1, std::min<int64_t>({nchunks, seqlen, kMaxGridYZ}));
-  const int64_t len = (seqlen + k - 1) / k;
+  const int64_t len = chunk_length(seqlen, dim, io_dtype, nchunks);
   return (int)((seqlen + len - 1) / len);
+}
+
+size_t workspace_for(int64_t batch, int64_t dim, int K) {
+  return ssm::scan_workspace_layout(batch, dim, K).total;
 }
 
 bool sizes_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
@@ -106,24 +115,26 @@ int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int
     int g;
     auto_plan(batch, seqlen, dim, &g, &nchunks);
   }
+  if (batch == 0 || dim == 0 || seqlen == 0) return 0;
   nchunks = effective_chunks(seqlen, dim, io_dtype, nchunks);
-  return (int64_t)ssm::scan_workspace_layout(batch, dim, nchunks).total;
+  return (int64_t)workspace_for(batch, dim, nchunks);
 }
 
-int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                         int io_dtype, const void* x, const void* delta, const float* A,
-                         const void* B, const void* C, const float* Dskip, const void* z,
-                         const float* h0, void* y, float* h_last, void* workspace,
-                         size_t workspace_bytes, int waves_per_group, int nchunks,
-                         void* stream) {
+int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int io_dtype, const void* x, const void* delta, const float* A,
+                       const void* B, const void* C, const float* Dskip, const void* z,
+                       const float* h0, void* y, float* h_last, void* workspace,
+                       size_t workspace_bytes, int waves_per_group, int nchunks, int phase,
+                       void* stream) {
   if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype))
     return SSM_ERR_INVALID_ARG;
+  if (phase < 1 || phase > 3) return SSM_ERR_INVALID_ARG;
   if (batch == 0 || dim == 0) return SSM_OK;
   if (dstate != kDState) return SSM_ERR_UNSUPPORTED;
   if (!A) return SSM_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (seqlen == 0) {
-    if (!h_last) return SSM_OK;
+    if (!h_last || !(phase & 2)) return SSM_OK;
     if ((const void*)h_last == (const void*)h0 || (const void*)h_last == (const void*)A)
       return SSM_ERR_INVALID_ARG;
     if (!all_aligned(h0, h_last)) return SSM_ERR_INVALID_ARG;
@@ -145,13 +156,17 @@ int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
   auto_plan(batch, seqlen, dim, &G, &K);
   if (waves_per_group > 0) G = waves_per_group;
   if (nchunks > 0) K = nchunks;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return SSM_ERR_UNSUPPORTED;
-  K = effective_chunks(seqlen, dim, io_dtype, K);
+  if (G != 2 && G != 4 && G != 8 && G != 16) return SSM_ERR_UNSUPPORTED;
+  const int64_t chunk_len = chunk_length(seqlen, dim, io_dtype, K);
+  K = effective_chunks(seqlen, dim, io_dtype, K);  // == ceil(seqlen / chunk_len)
 
   const ssm::ScanWorkspace ws = ssm::scan_workspace_layout(batch, dim, K);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return SSM_ERR_WORKSPACE;
-  for (const void* in : ins)
-    if (in && workspace && in == workspace) return SSM_ERR_INVALID_ARG;
+  if (ws.total > 0) {
+    for (const void* in : ins)
+      if (in && in == workspace) return SSM_ERR_INVALID_ARG;
+    if (workspace == y || workspace == (void*)h_last) return SSM_ERR_INVALID_ARG;
+  }
 
   ssm::ScanArgs a{};
   a.x = x;
@@ -165,15 +180,26 @@ int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
   a.y = y;
   a.h_last = h_last;
   char* wsb = static_cast<char*>(workspace);
-  a.ws_hloc = ws.total ? reinterpret_cast<float*>(wsb + ws.hloc_off) : nullptr;
-  a.ws_hin = ws.total ? reinterpret_cast<float*>(wsb + ws.hin_off) : nullptr;
-  a.ws_sdelta = ws.total ? reinterpret_cast<double*>(wsb + ws.sdelta_off) : nullptr;
+  a.ws_hloc = K > 1 ? reinterpret_cast<float*>(wsb + ws.hloc_off) : nullptr;
+  a.ws_hin = K > 1 ? reinterpret_cast<float*>(wsb + ws.hin_off) : nullptr;
+  a.ws_sdelta = K > 1 ? reinterpret_cast<double*>(wsb + ws.sdelta_off) : nullptr;
   a.seqlen = seqlen;
-  a.chunk_len = (seqlen + K - 1) / K;
+  a.chunk_len = chunk_len;
   a.nchunks = K;
   a.dim = (int)dim;
   a.batch = (int)batch;
-  return hip_status(ssm::launch_scan(a, io_dtype == SSM_DTYPE_BF16, G, s));
+  return hip_status(ssm::launch_scan(a, io_dtype == SSM_DTYPE_BF16, G, phase, s));
+}
+
+int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int io_dtype, const void* x, const void* delta, const float* A,
+                         const void* B, const void* C, const float* Dskip, const void* z,
+                         const float* h0, void* y, float* h_last, void* workspace,
+                         size_t workspace_bytes, int waves_per_group, int nchunks,
+                         void* stream) {
+  return ssm_scan_fwd_phase(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z,
+                            h0, y, h_last, workspace, workspace_bytes, waves_per_group,
+                            nchunks, 3, stream);
 }
 
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,

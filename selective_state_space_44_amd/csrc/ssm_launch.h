@@ -45,15 +45,20 @@ struct DecodeArgs {
   int dim;
 };
 
-// Byte layout of the scan workspace for `nchunks` chunks (0 if nchunks <= 1).
+// Steps per tile of the scan kernels; chunks start on a tile boundary.
+int scan_tile_steps();
+
+// Byte layout of the scan workspace: the per-chunk carry state (empty when
+// nchunks <= 1).
 struct ScanWorkspace {
   size_t hloc_off, hin_off, sdelta_off, total;
 };
 ScanWorkspace scan_workspace_layout(int64_t batch, int64_t dim, int nchunks);
 
-// Enqueue a full scan.  io_bf16 selects the I/O type; waves_per_group is one
-// of 1, 2, 4, 8, 16.  Returns hipSuccess or the launch error.
-hipError_t launch_scan(const ScanArgs& a, bool io_bf16, int waves_per_group,
+// Enqueue a scan.  io_bf16 selects the I/O type; waves_per_group is one of
+// 2, 4, 8, 16.  phase: 1 = chunk carry passes only, 2 = main pass only,
+// 3 = both.  Returns hipSuccess or the launch error.
+hipError_t launch_scan(const ScanArgs& a, bool io_bf16, int waves_per_group, int phase,
                        hipStream_t stream);
 
 // Enqueue the seqlen == 0 case: h_last = h0 (or zeros).

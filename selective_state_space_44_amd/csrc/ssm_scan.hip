@@ -13,19 +13,28 @@
 //     G waves and wave g holds the NPL = 16/G state indices
 //     n in [g*NPL, (g+1)*NPL) of those 64 channels.  The fp32 state lives in
 //     VGPRs for the whole chunk and never touches HBM.
-//   * B[b,t,n] and C[b,t,n] are the same for all 64 lanes of a wave, so they
-//     are read with scalar loads and fed to the VALU as SGPR operands; x and
-//     delta are read once per lane per step (one coalesced row segment per
-//     wave) through a buffer resource whose row offset is a scalar, so the
-//     inner loop does no per-lane address arithmetic.
-//   * Update form: with q = B*x/A the ZOH step is h' = Abar*(h + q) - q,
-//     i.e. one add and one fma per element after the exp2, with
-//     Abar = exp2(delta * A*log2(e)).
+//   * B[b,t,n] and C[b,t,n] are the same for all 64 lanes of a wave.  B is
+//     loaded into a few VGPRs, 16 (step, state) values per register repeated
+//     in each 16-lane row, and handed to the multiply that needs it through a
+//     DPP row broadcast fused into that instruction.  C is written to a small
+//     per-wave LDS slice one tile ahead and read back with broadcast 16-byte
+//     LDS loads.  x, delta and z are read once per lane per step (one
+//     coalesced row segment per wave) through a buffer resource whose row
+//     offset is a scalar, so the inner loop does no per-lane address
+//     arithmetic.
+//   * Software pipeline: the loads of tile i+1 are in flight while tile i is
+//     computed (ping-pong register sets), and within a tile the exp2 and
+//     input terms of step group j+1 are formed before the serial updates of
+//     group j so that their latency hides behind the recurrence.
+//   * Update form: with q = B*x/A, Bbar*x = (Abar - 1)*q = fma(Abar, q, -q)
+//     and the state update is the single fma h = fma(Abar, h, Bbar*x), with
+//     Abar = exp2(delta * A*log2(e)).  A zero step (Abar == 1, Bbar == 0)
+//     leaves the state bit-for-bit unchanged.
 //   * Readout: each wave forms its partial sum over its NPL states for every
-//     step of a T-step tile, writes it to LDS, and after one barrier wave g
-//     finishes steps s = g, g+G, ... of the tile: sum of the G partials (fixed
-//     order, so results are deterministic), skip term, SiLU gate, and one
-//     coalesced store of y.
+//     step of a T-step tile (wave 0 also adds D*x), writes it to LDS, and
+//     after one barrier wave g finishes steps s = g, g+G, ... of the tile:
+//     sum of the G partials (fixed order, so results are deterministic),
+//     SiLU gate, and one coalesced store of y.
 //   * Sequence chunks (paperlens tutorial, parallel-scan section: the update
 //     h_t = Abar_t h_{t-1} + u_t composes associatively): when the plan cuts
 //     L into K chunks, a first kernel runs every chunk but the last from a
@@ -36,57 +45,49 @@
 //   * A == 0 (which the ZOH formula reaches only as a limit) switches the
 //     affected wave to a form with that limit, Bbar = delta * B.
 
+#include <type_traits>
+
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
 namespace ssm {
 namespace {
 
-// Load NPL consecutive B (or C) values starting at a wave-uniform address.
-template <typename IO, int NPL> struct BCLoad;
-template <int NPL> struct BCLoad<float, NPL> {
-  __device__ __forceinline__ static void load(const float* __restrict__ p, float (&out)[NPL]) {
-#pragma unroll
-    for (int k = 0; k < NPL; ++k) out[k] = p[k];
-  }
-};
-template <int NPL> struct BCLoad<bf16, NPL> {
-  __device__ __forceinline__ static void load(const bf16* __restrict__ p, float (&out)[NPL]) {
-    if constexpr (NPL >= 2) {
-      // NPL is even and the group start n0 is even: whole aligned dwords.
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-      for (int i = 0; i < NPL / 2; ++i) {
-        uint32_t v = w[i];
-        out[2 * i] = __uint_as_float(v << 16);
-        out[2 * i + 1] = __uint_as_float(v & 0xffff0000u);
-      }
-    } else {
-      uintptr_t addr = reinterpret_cast<uintptr_t>(p);
-      uint32_t v = *reinterpret_cast<const uint32_t*>(addr & ~uintptr_t(3));
-      out[0] = (addr & 2) ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
-    }
-  }
-};
+constexpr int kChunkAlign = 16;  // chunks start on a multiple of this many steps
 
-// One ZOH step of NPL states of one channel.
+// One ZOH step of NPL states of one channel (unpipelined form).
 template <int NPL, bool ZERO_A>
-__device__ __forceinline__ void zoh_step(float dv, float xv, const float (&Bv)[NPL],
+__device__ __forceinline__ void zoh_step(float dv, float xv, const float* Bv,
+                                         const float (&A2)[NPL], const float (&iA)[NPL],
+                                         float (&h)[NPL]);
+
+// ZOH coefficients of one (step, state): h' = a*h + b with a = Abar and
+// b = Bbar*x.  With q = B*x/A, Bbar*x = (Abar - 1)*q = fma(Abar, q, -q), so
+// the recurrence itself is a single fma (h' = fma(a, h, b)) and a step of
+// zero length (a == 1, b == 0) leaves the state bit-for-bit unchanged.
+// Where A == 0 (iA is +-inf) the limit Bbar = delta*B is used instead.
+template <bool ZERO_A>
+__device__ __forceinline__ void zoh_coef(float ds, float bx, float A2, float iA, float& a,
+                                         float& b) {
+  a = fast_exp2(ds * A2);
+  if constexpr (!ZERO_A) {
+    const float q = bx * iA;
+    b = __builtin_fmaf(a, q, -q);
+  } else {
+    const bool lim = __builtin_isinf(iA);
+    b = (lim ? ds : (a - 1.0f) * iA) * bx;
+  }
+}
+
+template <int NPL, bool ZERO_A>
+__device__ __forceinline__ void zoh_step(float dv, float xv, const float* Bv,
                                          const float (&A2)[NPL], const float (&iA)[NPL],
                                          float (&h)[NPL]) {
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
-    const float a = fast_exp2(dv * A2[k]);  // Abar
-    const float bx = Bv[k] * xv;
-    if constexpr (!ZERO_A) {
-      const float q = bx * iA[k];            // B x / A
-      h[k] = __builtin_fmaf(a, h[k] + q, -q);
-    } else {
-      // (Abar - 1)/A, or its limit delta where A == 0 (iA is then +-inf).
-      const bool lim = __builtin_isinf(iA[k]);
-      const float w = lim ? dv : (a - 1.0f) * iA[k];
-      h[k] = __builtin_fmaf(a, h[k], w * bx);
-    }
+    float a, b;
+    zoh_coef<ZERO_A>(dv, Bv[k] * xv, A2[k], iA[k], a, b);
+    h[k] = __builtin_fmaf(a, h[k], b);
   }
 }
 
@@ -114,6 +115,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const IO* p, int b, 
   return make_rsrc(p + first, (uint32_t)((size_t)(t_end - t_begin) * dim * sizeof(IO)));
 }
 
+// Raw (undecoded) I/O element as loaded: bf16 bits in the low half, or fp32.
+template <typename IO> struct Raw;
+template <> struct Raw<float> {
+  using T = float;
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+    return buf<float>::load(r, v, s);
+  }
+  __device__ __forceinline__ static float f(T v) { return v; }
+};
+template <> struct Raw<bf16> {
+  using T = uint32_t;
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, v, s, 0);
+  }
+  __device__ __forceinline__ static float f(T v) { return bf16_bits_to_f32(v); }
+};
+
+// Value of lane K of this lane's 16-lane row (DPP row_newbcast).  Written
+// as a DPP move; the compiler folds it into the consuming VOP2 instruction,
+// so the broadcast costs no extra instruction.
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf, true));
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time loop).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 struct Chunk {
   int lane, g, b, c, d;
   bool active;
@@ -134,94 +170,273 @@ __device__ __forceinline__ Chunk chunk_coords(int dim, int64_t seqlen, int64_t c
   return k;
 }
 
+// How one wave holds the B and C values of its NPL states for a tile of
+// T steps (T*NPL values each):
+//  * B lives in NPL VGPRs, 16 values per register, the same 16 in each of the
+//    four 16-lane rows: value v = step*NPL + k sits in register v/16, lane
+//    v%16 of every row, and is read with row_bcast<v%16>;
+//  * C is staged in LDS (16*NPL floats per tile, double buffered, per wave)
+//    and read with one broadcast LDS load per step.
+template <int NPL, int T>
+struct BCLayout {
+  static constexpr int kVals = T * NPL;                           // B (or C) values per tile
+  static constexpr int kBRegs = (kVals + 15) / 16;                // B VGPRs per tile
+  static constexpr int kCVals = kVals;                            // C floats per tile
+  static constexpr int kCPerLane = (kVals + kWave - 1) / kWave;   // C values loaded per lane
+};
+
+template <typename IO, int NPL, int T>
+struct BCRegs {
+  typename Raw<IO>::T b[BCLayout<NPL, T>::kBRegs], c[BCLayout<NPL, T>::kCPerLane];
+};
+
+// Per-lane byte offsets (within a tile's rows of B or C) of the values this
+// lane loads.
+template <typename IO, int NPL, int T>
+struct BCOffsets {
+  using L = BCLayout<NPL, T>;
+  uint32_t b[L::kBRegs], c[L::kCPerLane];
+  int cslot[L::kCPerLane];  // LDS slot of each C value
+  __device__ __forceinline__ BCOffsets(int lane, int n0) {
+    const int p = lane % 16;
+#pragma unroll
+    for (int r = 0; r < L::kBRegs; ++r) {
+      const int v = min(16 * r + p, L::kVals - 1);
+      b[r] = (uint32_t)(((v / NPL) * kDState + n0 + v % NPL) * sizeof(IO));
+    }
+#pragma unroll
+    for (int r = 0; r < L::kCPerLane; ++r) {
+      const int v = (lane + kWave * r) % L::kCVals;
+      cslot[r] = v;
+      c[r] = (uint32_t)(((v / NPL) * kDState + n0 + v % NPL) * sizeof(IO));
+    }
+  }
+};
+
+// Rows of one chunk of a [b, L, 16] tensor (B or C) as a buffer.
+template <typename IO>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bc_rsrc(const IO* p, const Chunk& k,
+                                                          int64_t seqlen) {
+  const size_t first = ((size_t)k.b * seqlen + k.t_begin) * kDState;
+  return make_rsrc(p + first, (uint32_t)((size_t)(k.t_end - k.t_begin) * kDState * sizeof(IO)));
+}
+
 // ---------------------------------------------------------------------------
 // Main scan: one chunk of 64 channels x all 16 states per block.
 // ---------------------------------------------------------------------------
-template <typename IO, int G, int T, bool ZERO_A>
-__device__ __forceinline__ void scan_chunk(
-    const IO* __restrict__ x, const IO* __restrict__ delta, const IO* __restrict__ B,
-    const IO* __restrict__ C, const IO* __restrict__ z, IO* __restrict__ y, float Dd,
-    int64_t seqlen, int dim, const Chunk& k, float* part, const float (&A2)[kDState / G],
-    const float (&iA)[kDState / G], float (&h)[kDState / G]) {
+template <typename IO, int G, int T>
+struct TileRegs {
+  typename Raw<IO>::T x[T], d[T], z[(T + G - 1) / G];
+  BCRegs<IO, kDState / G, T> bc;
+};
+
+template <int NPL>
+__device__ __forceinline__ void read_c(const float* cst, int s, float (&cv)[NPL]) {
+  if constexpr (NPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < NPL / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(cst + s * NPL)[q];
+      cv[4 * q] = v.x;
+      cv[4 * q + 1] = v.y;
+      cv[4 * q + 2] = v.z;
+      cv[4 * q + 3] = v.w;
+    }
+  } else if constexpr (NPL == 2) {
+    const float2 v = reinterpret_cast<const float2*>(cst + s * NPL)[0];
+    cv[0] = v.x;
+    cv[1] = v.y;
+  } else {
+    cv[0] = cst[s];
+  }
+}
+
+template <typename IO, int G, int T, bool HAS_Z, bool ZERO_A>
+__device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* __restrict__ delta,
+                                           const IO* __restrict__ B, const IO* __restrict__ C,
+                                           const IO* __restrict__ z, IO* __restrict__ y,
+                                           float Dd, int64_t seqlen, int dim, const Chunk& k,
+                                           float* part, float* cst,
+                                           const float (&A2)[kDState / G],
+                                           const float (&iA)[kDState / G],
+                                           float (&h)[kDState / G]) {
   constexpr int NPL = kDState / G;
-  const int n0 = k.g * NPL;
+  constexpr int ZT = (T + G - 1) / G;  // steps of a tile this wave finishes (at most)
+  constexpr int SG = NPL >= 8 ? 1 : 8 / NPL;  // steps per coefficient group
+  static_assert(T % SG == 0, "tile must split into groups");
+  using R = Raw<IO>;
+  using L = BCLayout<NPL, T>;
   const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const __amdgpu_buffer_rsrc_t rz = rows_rsrc(z ? z : x, k.b, seqlen, dim, k.t_begin, k.t_end);
+  const __amdgpu_buffer_rsrc_t rz = rows_rsrc(HAS_Z ? z : x, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t ry = rows_rsrc(y, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const bool has_z = z != nullptr;
+  const __amdgpu_buffer_rsrc_t rb = bc_rsrc(B, k, seqlen);
+  const __amdgpu_buffer_rsrc_t rc = bc_rsrc(C, k, seqlen);
+  const BCOffsets<IO, NPL, T> bco(k.lane, k.g * NPL);
   const uint32_t voff = (uint32_t)k.d * sizeof(IO);
+  // lanes past the last channel store out of the buffer's range (dropped)
+  const uint32_t voff_y = k.active ? voff : 0x80000000u;
   const uint32_t row_bytes = (uint32_t)dim * sizeof(IO);
-  const IO* Bp = B + ((size_t)k.b * seqlen + k.t_begin) * kDState + n0;
-  const IO* Cp = C + ((size_t)k.b * seqlen + k.t_begin) * kDState + n0;
   const int nsteps = (int)(k.t_end - k.t_begin);
+  const int nfull = nsteps / T;
+  const float dmul = (k.g == 0) ? Dd : 0.0f;  // wave 0 carries the skip term
+
+  // Loads of tile `tidx` into r.  Prefetches past the last full tile are
+  // clamped onto it (their values are never used).
+  auto issue = [&](TileRegs<IO, G, T>& r, int tidx) {
+    const int s0 = min(tidx, nfull - 1) * T;
+    const uint32_t bcs = (uint32_t)s0 * kDState * sizeof(IO);
+#pragma unroll
+    for (int j = 0; j < L::kCPerLane; ++j) r.bc.c[j] = R::load(rc, bco.c[j], bcs);
+#pragma unroll
+    for (int j = 0; j < L::kBRegs; ++j) r.bc.b[j] = R::load(rb, bco.b[j], bcs);
+#pragma unroll
+    for (int s = 0; s < T; ++s) {
+      const uint32_t so = (uint32_t)(s0 + s) * row_bytes;
+      r.x[s] = R::load(rx, voff, so);
+      r.d[s] = R::load(rd, voff, so);
+    }
+    if constexpr (HAS_Z) {
+#pragma unroll
+      for (int j = 0; j < ZT; ++j)
+        r.z[j] = R::load(rz, voff, (uint32_t)min(s0 + k.g + j * G, nsteps - 1) * row_bytes);
+    }
+  };
+  auto stage_c = [&](const TileRegs<IO, G, T>& r, int cb) {
+#pragma unroll
+    for (int j = 0; j < L::kCPerLane; ++j) cst[cb * L::kCVals + bco.cslot[j]] = R::f(r.bc.c[j]);
+  };
 
   int pbuf = 0;
-  // Finish `ns` steps starting at local step s0 whose partial sums are in p.
-  auto finish = [&](const float* p, int s0, int ns) {
-    if constexpr (G == 1) {
-      for (int s = 0; s < ns; ++s) {
-        const uint32_t so = (uint32_t)(s0 + s) * row_bytes;
-        const float pre = __builtin_fmaf(Dd, buf<IO>::load(rx, voff, so), p[s]);
-        const float yv = has_z ? pre * silu(buf<IO>::load(rz, voff, so)) : pre;
-        if (k.active) buf<IO>::store(yv, ry, voff, so);
-      }
-    } else {
+  auto tile = [&](const TileRegs<IO, G, T>& r, int tidx, int cb, const TileRegs<IO, G, T>& next,
+                  bool has_next) {
+    const int s0 = tidx * T;
+    float bf[L::kBRegs];
+#pragma unroll
+    for (int j = 0; j < L::kBRegs; ++j) bf[j] = R::f(r.bc.b[j]);
+    const float* cs = cst + cb * L::kCVals;
+    // Coefficients (exp2 and the input term) of step group j+1 are formed
+    // before the serial updates of group j, so the exp latency and the
+    // coefficient math overlap the recurrence.
+    float* pw = part + pbuf * (G * T * kWave) + k.g * T * kWave + k.lane;  // this wave's partials
+    float ca[2][SG][NPL], cb2[2][SG][NPL], cc[2][SG][NPL];
+    auto coefs = [&](auto gc, float (&a)[SG][NPL], float (&bb)[SG][NPL], float (&c)[SG][NPL]) {
+      constexpr int g0 = decltype(gc)::value * SG;
+      static_for<SG>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int s = g0 + i;
+        read_c<NPL>(cs, s, c[i]);
+        const float xs = R::f(r.x[s]);
+        const float ds = R::f(r.d[s]);
+        static_for<NPL>([&](auto nc) {
+          constexpr int n = decltype(nc)::value;
+          constexpr int v = s * NPL + n;  // B value (step, state) in the tile
+          zoh_coef<ZERO_A>(ds, row_bcast<v % 16>(bf[v / 16]) * xs, A2[n], iA[n], a[i][n],
+                           bb[i][n]);
+        });
+      });
+    };
+    coefs(std::integral_constant<int, 0>{}, ca[0], cb2[0], cc[0]);
+    static_for<T / SG>([&](auto gc) {
+      constexpr int gi = decltype(gc)::value;
+      if constexpr (gi + 1 < T / SG)
+        coefs(std::integral_constant<int, gi + 1>{}, ca[(gi + 1) & 1], cb2[(gi + 1) & 1],
+              cc[(gi + 1) & 1]);
+      // keep the next group's loads and exp2s ahead of this group's updates
+      // (the scheduler would otherwise sink them next to their uses)
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<SG>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int s = gi * SG + i;
+        float acc = dmul * R::f(r.x[s]);
+        static_for<NPL>([&](auto nc) {
+          constexpr int n = decltype(nc)::value;
+          h[n] = __builtin_fmaf(ca[gi & 1][i][n], h[n], cb2[gi & 1][i][n]);
+          acc = __builtin_fmaf(cc[gi & 1][i][n], h[n], acc);
+        });
+        if constexpr (G == 1) {
+          const float yv = HAS_Z ? acc * silu(R::f(r.z[s])) : acc;
+          buf<IO>::store(yv, ry, voff_y, (uint32_t)(s0 + s) * row_bytes);
+        } else {
+          pw[s * kWave] = acc;
+        }
+      });
+    });
+    if (has_next) stage_c(next, cb ^ 1);
+    if constexpr (G > 1) {
       float* pb = part + pbuf * (G * T * kWave);
-      for (int s = 0; s < ns; ++s) pb[(k.g * T + s) * kWave + k.lane] = p[s];
       __syncthreads();
-      for (int s = k.g; s < ns; s += G) {
+      // all partial sums first (one batch of LDS reads), then the epilogue
+      float ps[ZT][G];
+#pragma unroll
+      for (int j = 0; j < ZT; ++j) {
+        const int s = min(k.g + j * G, T - 1);
+#pragma unroll
+        for (int w = 0; w < G; ++w) ps[j][w] = pb[(w * T + s) * kWave + k.lane];
+      }
+#pragma unroll
+      for (int j = 0; j < ZT; ++j) {
+        const int s = k.g + j * G;
+        if (T % G != 0 && s >= T) break;
         float sum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < G; ++w) sum += pb[(w * T + s) * kWave + k.lane];
-        const uint32_t so = (uint32_t)(s0 + s) * row_bytes;
-        const float pre = __builtin_fmaf(Dd, buf<IO>::load(rx, voff, so), sum);
-        const float yv = has_z ? pre * silu(buf<IO>::load(rz, voff, so)) : pre;
-        if (k.active) buf<IO>::store(yv, ry, voff, so);
+        for (int w = 0; w < G; ++w) sum += ps[j][w];
+        const float yv = HAS_Z ? sum * silu(R::f(r.z[j])) : sum;
+        buf<IO>::store(yv, ry, voff_y, (uint32_t)(s0 + s) * row_bytes);
       }
       pbuf ^= 1;
     }
   };
 
-  int s0 = 0;
-  for (; s0 + T <= nsteps; s0 += T) {
-    float xv[T], dv[T], p[T];
-#pragma unroll
-    for (int s = 0; s < T; ++s) {
-      const uint32_t so = (uint32_t)(s0 + s) * row_bytes;
-      xv[s] = buf<IO>::load(rx, voff, so);
-      dv[s] = buf<IO>::load(rd, voff, so);
-    }
-#pragma unroll
-    for (int s = 0; s < T; ++s) {
-      float Bv[NPL], Cv[NPL];
-      BCLoad<IO, NPL>::load(Bp + (size_t)(s0 + s) * kDState, Bv);
-      BCLoad<IO, NPL>::load(Cp + (size_t)(s0 + s) * kDState, Cv);
-      zoh_step<NPL, ZERO_A>(dv[s], xv[s], Bv, A2, iA, h);
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) acc = __builtin_fmaf(Cv[j], h[j], acc);
-      p[s] = acc;
-    }
-    finish(p, s0, T);
+  // full tiles, two at a time through the ping-pong register sets
+  TileRegs<IO, G, T> ra, rb2;
+  if (nfull > 0) {
+    issue(ra, 0);
+    stage_c(ra, 0);
   }
-  // ragged end of the chunk: one step per tile
-  for (; s0 < nsteps; ++s0) {
+  int i = 0;
+  for (; i + 2 <= nfull; i += 2) {
+    issue(rb2, i + 1);
+    tile(ra, i, 0, rb2, true);
+    issue(ra, i + 2);
+    tile(rb2, i + 1, 1, ra, true);
+  }
+  if (i < nfull) tile(ra, i, 0, ra, false);
+
+  // ragged end of the chunk: one step at a time, no pipelining
+  for (int s0 = nfull * T; s0 < nsteps; ++s0) {
     const uint32_t so = (uint32_t)s0 * row_bytes;
     const float xs = buf<IO>::load(rx, voff, so);
     const float ds = buf<IO>::load(rd, voff, so);
-    float Bv[NPL], Cv[NPL];
-    BCLoad<IO, NPL>::load(Bp + (size_t)s0 * kDState, Bv);
-    BCLoad<IO, NPL>::load(Cp + (size_t)s0 * kDState, Cv);
-    zoh_step<NPL, ZERO_A>(ds, xs, Bv, A2, iA, h);
-    float p[1] = {0.0f};
+    const uint32_t bo = (uint32_t)(s0 * kDState + k.g * NPL) * sizeof(IO);
+    float acc = dmul * xs;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) p[0] = __builtin_fmaf(Cv[j], h[j], p[0]);
-    finish(p, s0, 1);
+    for (int n = 0; n < NPL; ++n) {
+      const float Bn = buf<IO>::load(rb, bo + n * sizeof(IO), 0);
+      const float Cn = buf<IO>::load(rc, bo + n * sizeof(IO), 0);
+      float a, b;
+      zoh_coef<ZERO_A>(ds, Bn * xs, A2[n], iA[n], a, b);
+      h[n] = __builtin_fmaf(a, h[n], b);
+      acc = __builtin_fmaf(Cn, h[n], acc);
+    }
+    if constexpr (G == 1) {
+      const float yv = HAS_Z ? acc * silu(buf<IO>::load(rz, voff, so)) : acc;
+      buf<IO>::store(yv, ry, voff_y, so);
+    } else {
+      float* pb = part + pbuf * (G * T * kWave);
+      pb[(k.g * T) * kWave + k.lane] = acc;
+      __syncthreads();
+      if (k.g == 0) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < G; ++w) sum += pb[(w * T) * kWave + k.lane];
+        const float yv = HAS_Z ? sum * silu(buf<IO>::load(rz, voff, so)) : sum;
+        buf<IO>::store(yv, ry, voff_y, so);
+      }
+      pbuf ^= 1;
+    }
   }
 }
-
-template <typename IO, int G, int T>
+template <typename IO, int G, int T, bool HAS_Z>
 __global__ __launch_bounds__(kWave* G) void scan_fwd_kernel(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
@@ -230,6 +445,7 @@ __global__ __launch_bounds__(kWave* G) void scan_fwd_kernel(
     int64_t chunk_len, int dim, int nchunks) {
   constexpr int NPL = kDState / G;
   __shared__ float part[G > 1 ? 2 * G * T * kWave : 1];
+  __shared__ float cst_all[G * 2 * BCLayout<NPL, T>::kCVals];
   const Chunk k = chunk_coords(dim, seqlen, chunk_len);
   const int n0 = k.g * NPL;
 
@@ -243,11 +459,14 @@ __global__ __launch_bounds__(kWave* G) void scan_fwd_kernel(
 #pragma unroll
   for (int j = 0; j < NPL; ++j) h[j] = hinit ? hinit[j] : 0.0f;
   const float Dd = Dskip ? Dskip[k.d] : 0.0f;
+  float* cst = cst_all + k.g * 2 * BCLayout<NPL, T>::kCVals;
 
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    scan_chunk<IO, G, T, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, part, A2, iA, h);
+    scan_chunk<IO, G, T, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, part, cst, A2,
+                                      iA, h);
   else
-    scan_chunk<IO, G, T, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, part, A2, iA, h);
+    scan_chunk<IO, G, T, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, part, cst, A2,
+                                       iA, h);
 
   if (k.c == nchunks - 1 && h_last && k.active) {
     float* hl = h_last + ((size_t)k.b * dim + k.d) * kDState + n0;
@@ -258,9 +477,10 @@ __global__ __launch_bounds__(kWave* G) void scan_fwd_kernel(
 
 // ---------------------------------------------------------------------------
 // Carry pass 1: end state of every chunk but the last, started from zero,
-// plus the chunk's sum of delta (accumulated in fp64).
+// plus the chunk's sum of delta (accumulated in fp64).  Same pipelining and
+// B layout as the main kernel, without the readout.
 // ---------------------------------------------------------------------------
-template <typename IO, int G, bool ZERO_A>
+template <typename IO, int G, int T, bool ZERO_A>
 __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
                                             const IO* __restrict__ delta,
                                             const IO* __restrict__ B, int64_t seqlen, int dim,
@@ -268,43 +488,74 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
                                             const float (&iA)[kDState / G],
                                             float (&h)[kDState / G], double& sd) {
   constexpr int NPL = kDState / G;
-  constexpr int U = 8;
-  const int n0 = k.g * NPL;
+  using R = Raw<IO>;
+  using L = BCLayout<NPL, T>;
   const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
+  const __amdgpu_buffer_rsrc_t rb = bc_rsrc(B, k, seqlen);
+  const BCOffsets<IO, NPL, T> bco(k.lane, k.g * NPL);
   const uint32_t voff = (uint32_t)k.d * sizeof(IO);
   const uint32_t row_bytes = (uint32_t)dim * sizeof(IO);
-  const IO* Bp = B + ((size_t)k.b * seqlen + k.t_begin) * kDState + n0;
   const int nsteps = (int)(k.t_end - k.t_begin);
-  int s0 = 0;
-  for (; s0 + U <= nsteps; s0 += U) {
-    float xv[U], dv[U];
+  const int nfull = nsteps / T;
+
+  struct Regs {
+    typename R::T x[T], d[T], b[L::kBRegs];
+  };
+  auto issue = [&](Regs& r, int tidx) {
+    const int s0 = min(tidx, nfull - 1) * T;
+    const uint32_t bcs = (uint32_t)s0 * kDState * sizeof(IO);
 #pragma unroll
-    for (int s = 0; s < U; ++s) {
+    for (int j = 0; j < L::kBRegs; ++j) r.b[j] = R::load(rb, bco.b[j], bcs);
+#pragma unroll
+    for (int s = 0; s < T; ++s) {
       const uint32_t so = (uint32_t)(s0 + s) * row_bytes;
-      xv[s] = buf<IO>::load(rx, voff, so);
-      dv[s] = buf<IO>::load(rd, voff, so);
+      r.x[s] = R::load(rx, voff, so);
+      r.d[s] = R::load(rd, voff, so);
     }
+  };
+  auto tile = [&](const Regs& r) {
+    float bf[L::kBRegs];
 #pragma unroll
-    for (int s = 0; s < U; ++s) {
-      float Bv[NPL];
-      BCLoad<IO, NPL>::load(Bp + (size_t)(s0 + s) * kDState, Bv);
-      zoh_step<NPL, ZERO_A>(dv[s], xv[s], Bv, A2, iA, h);
-      sd += (double)dv[s];
-    }
+    for (int j = 0; j < L::kBRegs; ++j) bf[j] = R::f(r.b[j]);
+    static_for<T>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const float xs = R::f(r.x[s]);
+      const float ds = R::f(r.d[s]);
+      static_for<NPL>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        constexpr int v = s * NPL + n;
+        float a, b;
+        zoh_coef<ZERO_A>(ds, row_bcast<v % 16>(bf[v / 16]) * xs, A2[n], iA[n], a, b);
+        h[n] = __builtin_fmaf(a, h[n], b);
+      });
+      sd += (double)ds;
+    });
+  };
+  Regs ra, rb2;
+  if (nfull > 0) issue(ra, 0);
+  int i = 0;
+  for (; i + 2 <= nfull; i += 2) {
+    issue(rb2, i + 1);
+    tile(ra);
+    issue(ra, i + 2);
+    tile(rb2);
   }
-  for (; s0 < nsteps; ++s0) {
+  if (i < nfull) tile(ra);
+  for (int s0 = nfull * T; s0 < nsteps; ++s0) {
     const uint32_t so = (uint32_t)s0 * row_bytes;
     const float xs = buf<IO>::load(rx, voff, so);
     const float ds = buf<IO>::load(rd, voff, so);
+    const uint32_t bo = (uint32_t)(s0 * kDState + k.g * NPL) * sizeof(IO);
     float Bv[NPL];
-    BCLoad<IO, NPL>::load(Bp + (size_t)s0 * kDState, Bv);
+#pragma unroll
+    for (int n = 0; n < NPL; ++n) Bv[n] = buf<IO>::load(rb, bo + n * sizeof(IO), 0);
     zoh_step<NPL, ZERO_A>(ds, xs, Bv, A2, iA, h);
     sd += (double)ds;
   }
 }
 
-template <typename IO, int G>
+template <typename IO, int G, int T>
 __global__ __launch_bounds__(kWave* G) void scan_chunk_state_kernel(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, float* __restrict__ ws_hloc, double* __restrict__ ws_sdelta,
@@ -318,9 +569,9 @@ __global__ __launch_bounds__(kWave* G) void scan_chunk_state_kernel(
   for (int j = 0; j < NPL; ++j) h[j] = 0.0f;
   double sd = 0.0;
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    chunk_state<IO, G, true>(x, delta, B, seqlen, dim, k, A2, iA, h, sd);
+    chunk_state<IO, G, T, true>(x, delta, B, seqlen, dim, k, A2, iA, h, sd);
   else
-    chunk_state<IO, G, false>(x, delta, B, seqlen, dim, k, A2, iA, h, sd);
+    chunk_state<IO, G, T, false>(x, delta, B, seqlen, dim, k, A2, iA, h, sd);
   if (k.active) {
     const size_t cd = ((size_t)k.b * nchunks + k.c) * dim + k.d;
     float* hl = ws_hloc + cd * kDState + n0;
@@ -364,18 +615,17 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
   if (i < count) h_last[i] = h0 ? h0[i] : 0.0f;
 }
 
-constexpr int tile_for(int G) { return G >= 8 ? G : 8; }
-
 template <typename IO, int G>
-hipError_t launch_scan_t(const ScanArgs& a, hipStream_t stream) {
-  constexpr int T = tile_for(G);
+hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
+  constexpr int T = 8;  // steps per tile (chunks are whole multiples of it)
   const IO* x = static_cast<const IO*>(a.x);
   const IO* delta = static_cast<const IO*>(a.delta);
   const IO* B = static_cast<const IO*>(a.B);
+  const IO* C = static_cast<const IO*>(a.C);
   const unsigned gx = (unsigned)((a.dim + kWave - 1) / kWave);
-  if (a.nchunks > 1) {
+  if (a.nchunks > 1 && (phase & 1)) {
     dim3 grid1(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, G>), grid1, dim3(kWave * G), 0, stream, x,
+    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, G, T>), grid1, dim3(kWave * G), 0, stream, x,
                        delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len, a.dim,
                        a.nchunks);
     hipError_t e = hipGetLastError();
@@ -387,44 +637,53 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!(phase & 2)) return hipSuccess;
   dim3 grid(gx, (unsigned)a.nchunks, (unsigned)a.batch);
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, G, T>), grid, dim3(kWave * G), 0, stream, x, delta,
-                     a.A, B, static_cast<const IO*>(a.C), a.Dskip,
-                     static_cast<const IO*>(a.z), a.h0, static_cast<IO*>(a.y), a.h_last,
-                     a.ws_hin, a.seqlen, a.chunk_len, a.dim, a.nchunks);
+  if (a.z)
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, T, true>), grid, dim3(kWave * G), 0, stream, x,
+                       delta, a.A, B, C, a.Dskip, static_cast<const IO*>(a.z), a.h0,
+                       static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
+                       a.nchunks);
+  else
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, T, false>), grid, dim3(kWave * G), 0, stream, x,
+                       delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr), a.h0,
+                       static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
+                       a.nchunks);
   return hipGetLastError();
 }
 
 template <typename IO>
-hipError_t launch_scan_io(const ScanArgs& a, int G, hipStream_t stream) {
+hipError_t launch_scan_io(const ScanArgs& a, int G, int phase, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_scan_t<IO, 1>(a, stream);
-    case 2: return launch_scan_t<IO, 2>(a, stream);
-    case 4: return launch_scan_t<IO, 4>(a, stream);
-    case 8: return launch_scan_t<IO, 8>(a, stream);
-    case 16: return launch_scan_t<IO, 16>(a, stream);
+    case 2: return launch_scan_t<IO, 2>(a, phase, stream);
+    case 4: return launch_scan_t<IO, 4>(a, phase, stream);
+    case 8: return launch_scan_t<IO, 8>(a, phase, stream);
+    case 16: return launch_scan_t<IO, 16>(a, phase, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+int scan_tile_steps() { return kChunkAlign; }
+
 ScanWorkspace scan_workspace_layout(int64_t batch, int64_t dim, int nchunks) {
-  ScanWorkspace w{0, 0, 0, 0};
-  if (nchunks <= 1) return w;
   auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
-  const size_t states = (size_t)batch * nchunks * dim * kDState;
-  w.hloc_off = 0;
-  w.hin_off = align(states * sizeof(float));
-  w.sdelta_off = w.hin_off + align(states * sizeof(float));
-  w.total = w.sdelta_off + align((size_t)batch * nchunks * dim * sizeof(double));
+  ScanWorkspace w{0, 0, 0, 0};
+  if (nchunks > 1) {
+    const size_t states = (size_t)batch * nchunks * dim * kDState;
+    w.hloc_off = 0;
+    w.hin_off = w.hloc_off + align(states * sizeof(float));
+    w.sdelta_off = w.hin_off + align(states * sizeof(float));
+    w.total = w.sdelta_off + align((size_t)batch * nchunks * dim * sizeof(double));
+  }
   return w;
 }
 
-hipError_t launch_scan(const ScanArgs& a, bool io_bf16, int waves_per_group,
+hipError_t launch_scan(const ScanArgs& a, bool io_bf16, int waves_per_group, int phase,
                        hipStream_t stream) {
-  return io_bf16 ? launch_scan_io<bf16>(a, waves_per_group, stream)
-                 : launch_scan_io<float>(a, waves_per_group, stream);
+  return io_bf16 ? launch_scan_io<bf16>(a, waves_per_group, phase, stream)
+                 : launch_scan_io<float>(a, waves_per_group, phase, stream);
 }
 
 hipError_t launch_copy_state(const float* h0, float* h_last, int64_t count,

@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective state-space scan on one MI355X.
+
+One step = one forward scan of the Mamba-2.8B layer shape
+(batch 4, L 4096, D 5120, N 16; bf16 x/delta/z/B/C/y, fp32 A/D and state)
+on seeded synthetic inputs already resident in HBM.  Prints one JSON line
+with whole-job throughput in B*L*D*N elements/s, the roofline of the
+dominant kernel (the main scan pass), the HBM view, the recurrent decode
+sweep (256 sequences x 64 layers of D 5120, N 16) and the fp64 CPU
+baseline timed on a bounded sample on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# ALU roofline of the scan element: per element (b, t, d, n) the main pass
+# issues 6 fp32 VALU ops + 1 transcendental (exp2).  Per SIMD per clock: 32 fp32
+# lanes (157.3 TFLOP/s fp32 vector = 256 CU x 4 SIMD x 32 lanes x 2 x 2.4 GHz)
+# and a quarter of that for transcendentals.
+ALU_OPS_PER_ELEMENT = 7
+SIMDS, CLOCK_HZ, VALU_LANES, TRANS_LANES = 256 * 4, 2.4e9, 32, 8
+ALU_PEAK_ELEMS = SIMDS * CLOCK_HZ / (6 / VALU_LANES + 1 / TRANS_LANES)
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_mamba2p8b_b4_l4096_d5120_traffic.md")
+
+
+def source_hash() -> str:
+    """Hash of the library sources with // comments and blank lines removed
+    (a comment edit does not change a kernel; any code edit does)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "selective_state_space_44_amd", "csrc", "*")))
+    for f in files + [os.path.join(ROOT, "include", "ssm.h")]:
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch of the main kernel, from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, when it was taken on the current sources
+    (its ``source_hash`` line matches); None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    h = re.search(r"^source_hash:\s*(\w+)", text, re.M)
+    b = re.search(r"^hbm_bytes_per_launch:\s*(\d+)", text, re.M)
+    if not h or not b or h.group(1) != source_hash():
+        return None
+    return int(b.group(1))
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(inp, w, target_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    the first ``nb`` batch rows, the first ``nch`` channels of each, over the
+    full sequence."""
+    import torch
+    import oracle
+
+    nthreads = cpu_threads()
+
+    def take(nb, nch):
+        idx = torch.arange(nch, device=inp["x"].device)
+        f64 = lambda t: t.detach().to("cpu").to(torch.float64).numpy()
+        sl = lambda t: f64(t[:nb].index_select(2, idx))
+        return (sl(inp["x"]), sl(inp["delta"]), f64(inp["A"].index_select(0, idx)),
+                f64(inp["B"][:nb]), f64(inp["C"][:nb]), f64(inp["D"].index_select(0, idx)),
+                sl(inp["z"]))
+
+    def run(nb, nch):
+        args = take(nb, nch)
+        t0 = time.perf_counter()
+        oracle.scan(*args, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    # calibrate on a small sample, then size the timed sample to ~target_s
+    probe = min(w.dim, 8 * nthreads)
+    per_chan = run(1, probe) / probe
+    want = max(1, int(target_s / max(per_chan, 1e-9)))
+    if want >= w.dim:
+        nb, nch = min(w.batch, max(1, want // w.dim)), w.dim
+    else:
+        nb, nch = 1, max(probe, want // nthreads * nthreads)
+    dt = run(nb, nch)
+    elems = nb * w.seqlen * nch * w.dstate
+    return {"value": elems / dt, "unit": "elements/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{nb} of {w.batch} batch rows x {nch} of {w.dim} channels, full "
+                      f"L={w.seqlen}, N={w.dstate}: {elems:.3e} elements in {dt:.1f} s "
+                      f"(fp64 C loop, gcc -O2, OpenMP over channels)"}
+
+
+def bench_scan(steps: int, warmup: int):
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.MAMBA_2P8B
+    dev = "cuda:0"
+    # two input sets, alternated, so no step reads what the previous left in
+    # the 256 MB Infinity Cache (one set is ~0.67 GB anyway)
+    sets = [W.make_inputs(w, device=dev, layer=i) for i in range(2)]
+    outs = [torch.empty_like(s["x"]) for s in sets]
+    G, K = ssm.scan_plan(w.batch, w.seqlen, w.dim)
+    nws = ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim, nchunks=K)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        s, y = sets[i % 2], outs[i % 2]
+        args = (s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], None)
+        kw = dict(waves_per_group=G, nchunks=K, out=y, workspace=ws)
+        if ev is not None:
+            ev[0].record()
+        ssm.scan_fwd(*args, phase=1, **kw)
+        if ev is not None:
+            ev[1].record()
+        ssm.scan_fwd(*args, phase=2, **kw)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_step = [e[0].elapsed_time(e[2]) for e in evs]
+    ev_main = [e[1].elapsed_time(e[2]) for e in evs]
+    ev_carry = [e[0].elapsed_time(e[1]) for e in evs]
+    return dict(w=w, G=G, K=K, wall_s=wall, step_ms=sum(ev_step) / steps,
+                main_ms=sum(ev_main) / steps, carry_ms=sum(ev_carry) / steps, inp=sets[0])
+
+
+def bench_decode(sweeps: int):
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.DECODE_64L
+    dev = "cuda:0"
+    layers = [W.make_inputs(w, device=dev, layer=l) for l in range(w.layers)]
+    ys = [torch.empty_like(l["x"]) for l in layers]
+
+    def sweep(ev=None):
+        for i, l in enumerate(layers):
+            if ev is not None:
+                ev[2 * i].record()
+            ssm.decode_step(l["h"], l["x"], l["delta"], l["A"], l["B"], l["C"], l["D"], l["z"],
+                            out=ys[i])
+            if ev is not None:
+                ev[2 * i + 1].record()
+
+    sweep()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * w.layers)]
+           for _ in range(sweeps)]
+    t0 = time.perf_counter()
+    for r in range(sweeps):
+        sweep(evs[r])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sweep_ms = sum(e[0].elapsed_time(e[-1]) for e in evs) / sweeps
+    kern_ms = sum(e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs
+                  for i in range(w.layers)) / (sweeps * w.layers)
+    per_layer_bytes = w.algorithmic_bytes()
+    elems = w.elements * w.layers
+    return {
+        "workload": w.name,
+        "value": elems / (sweep_ms * 1e-3), "unit": "elements/s",
+        "ms_per_sweep_64_layers": sweep_ms,
+        "kernel_us_avg": kern_ms * 1e3,
+        "hbm": {"achieved": per_layer_bytes / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": per_layer_bytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "bytes_per_launch": per_layer_bytes},
+        "sweep_GBps": per_layer_bytes * w.layers / (sweep_ms * 1e-3) / 1e9,
+        "wall_s": wall,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-sweeps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (the known-size "
+                         "kernel that scales the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "channels are independent, so a multi-GPU run would split D with no exchange", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": COPY_BYTES}), flush=True)
+        return
+
+    r = bench_scan(args.steps, args.warmup)
+    w = r["w"]
+    elems = w.elements
+    value = elems / (r["step_ms"] * 1e-3)
+    main_elems = elems / (r["main_ms"] * 1e-3)
+    alg_bytes = w.algorithmic_bytes()
+    traffic = load_traffic()
+    line = {
+        "metric": "selective-scan B·L·D·N elems/s + % peak HBM GB/s, Mamba-2.8B layer shape",
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "dstate": w.dstate, "io_dtype": "bf16", "state_dtype": "f32",
+                   "plan": {"waves_per_group": r["G"], "nchunks": r["K"]}},
+        "roofline": {
+            "bound": "alu",
+            "kernel": "scan_fwd_kernel (main pass)",
+            "achieved": ALU_OPS_PER_ELEMENT * main_elems / 1e12,
+            "peak": ALU_OPS_PER_ELEMENT * ALU_PEAK_ELEMS / 1e12,
+            "unit": "TOP/s",
+            "frac": main_elems / ALU_PEAK_ELEMS,
+            "traffic": traffic,
+            "launch_ms": r["main_ms"],
+        },
+        "hbm": {
+            "algorithmic_bytes": alg_bytes,
+            "achieved": alg_bytes / (r["step_ms"] * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": alg_bytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
+        "carry_ms_per_step": r["carry_ms"],
+        "wall_s_timed": r["wall_s"],
+    }
+    if not args.no_decode:
+        line["decode"] = bench_decode(args.decode_sweeps)
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(r["inp"], w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,41 +7,42 @@
 //   h    = Abar * h + Bbar * x[b,t,d]
 //   y[b,t,d] = (sum_n C[b,t,n] h[n] + D[d] x[b,t,d]) * SiLU(z[b,t,d])
 //
-// Work decomposition (no MFMA: nothing here is a dense contraction).
+// Work decomposition (no MFMA: nothing here is a dense contraction; the
+// kernels are bound by VALU issue, so the design minimises VALU cycles per
+// element).
 //   * A block owns 64 consecutive channels of one batch row and one chunk of
 //     the sequence.  Lane j of every wave holds channel d0 + j; the block has
 //     G waves and wave g holds the NPL = 16/G state indices
 //     n in [g*NPL, (g+1)*NPL) of those 64 channels.  The fp32 state lives in
 //     VGPRs for the whole chunk and never touches HBM.
-//   * B[b,t,n] and C[b,t,n] are the same for all 64 lanes of a wave.  B is
-//     loaded into a few VGPRs, 16 (step, state) values per register repeated
-//     in each 16-lane row, and handed to the multiply that needs it through a
-//     DPP row broadcast fused into that instruction.  C is written to a small
-//     per-wave LDS slice one tile ahead and read back with broadcast 16-byte
-//     LDS loads.  x, delta and z are read once per lane per step (one
-//     coalesced row segment per wave) through a buffer resource whose row
-//     offset is a scalar, so the inner loop does no per-lane address
-//     arithmetic.
-//   * Software pipeline: the loads of tile i+1 are in flight while tile i is
-//     computed (ping-pong register sets), and within a tile the exp2 and
-//     input terms of step group j+1 are formed before the serial updates of
-//     group j so that their latency hides behind the recurrence.
-//   * Update form: with q = B*x/A, Bbar*x = (Abar - 1)*q = fma(Abar, q, -q)
-//     and the state update is the single fma h = fma(Abar, h, Bbar*x), with
-//     Abar = exp2(delta * A*log2(e)).  A zero step (Abar == 1, Bbar == 0)
-//     leaves the state bit-for-bit unchanged.
-//   * Readout: each wave forms its partial sum over its NPL states for every
-//     step of a T-step tile (wave 0 also adds D*x), writes it to LDS, and
-//     after one barrier wave g finishes steps s = g, g+G, ... of the tile:
-//     sum of the G partials (fixed order, so results are deterministic),
-//     SiLU gate, and one coalesced store of y.
+//   * Inputs are staged per block through LDS in tiles of kT steps, two
+//     stages deep: x and delta as fp32 rows [channel][step] (each wave reads
+//     its lane's steps with 16-byte LDS loads), B and C as fp32 [step][state]
+//     (read with broadcast LDS loads: every lane of a wave wants the same
+//     values).  The fetch of a tile from HBM is shared evenly by the G
+//     waves of the block and runs two tiles ahead of its use.  bf16 inputs are widened for
+//     free: the 16 raw bits are written into the upper half of an fp32 LDS
+//     slot whose lower half was zeroed once, so no VALU op converts them.
+//   * Per element the main pass issues 6 fp32 VALU ops and one exp2:
+//     a = exp2(delta * A*log2 e), q = (B*x) * (1/A), Bbar*x = fma(a, q, -q),
+//     h = fma(a, h, Bbar*x), and one fma of the readout.  A zero step
+//     (a == 1, Bbar*x == 0) leaves the state bit-for-bit unchanged.  The exp2
+//     and input terms of step group j+1 are formed before the serial updates
+//     of group j so that their latency hides behind the recurrence.
+//   * Readout: each wave writes its partial sum over its NPL states for every
+//     step of a tile to LDS; after the tile's one barrier, wave g finishes
+//     steps s = g, g+G, ...: sum of the G partials in a fixed order (results
+//     are deterministic), + D*x, SiLU gate, one coalesced store of y.
 //   * Sequence chunks (paperlens tutorial, parallel-scan section: the update
 //     h_t = Abar_t h_{t-1} + u_t composes associatively): when the plan cuts
 //     L into K chunks, a first kernel runs every chunk but the last from a
 //     zero state and records its end state hloc_c and sum of delta; a carry
 //     kernel composes the affine maps h -> P_c h + hloc_c with
 //     P_c = exp(A * sum(delta over chunk c)) in chunk order; the main kernel
-//     then runs every chunk from its true entering state.
+//     then runs every chunk from its true entering state.  The first kernel
+//     needs no readout, so it carries g = A*h instead of h:
+//     g = fma(a, g, fma(a, B*x, -B*x)), one multiply per element fewer, and
+//     converts back (h = g/A) once at the end of the chunk.
 //   * A == 0 (which the ZOH formula reaches only as a limit) switches the
 //     affected wave to a form with that limit, Bbar = delta * B.
 
@@ -54,17 +55,18 @@ namespace ssm {
 namespace {
 
 constexpr int kChunkAlign = 16;  // chunks start on a multiple of this many steps
-
-// One ZOH step of NPL states of one channel (unpipelined form).
-template <int NPL, bool ZERO_A>
-__device__ __forceinline__ void zoh_step(float dv, float xv, const float* Bv,
-                                         const float (&A2)[NPL], const float (&iA)[NPL],
-                                         float (&h)[NPL]);
+constexpr int kT = 8;            // steps per staged tile
+constexpr int kXS = kT + 4;      // floats per channel row of staged x / delta:
+                                 // 16-byte aligned rows, conflict-free 16-byte reads
+constexpr int kTileBC = kT * kDState;        // B (or C) values per tile
+static_assert(kTileBC % kWave == 0, "B/C tile must split evenly over a wave");
+// Register budgets: the main pass keeps 5 waves per SIMD resident (the plan
+// puts 5 blocks of 4 waves on every CU), the carry pass 4.
+constexpr int kMainWavesPerSimd = 5;
+constexpr int kCarryWavesPerSimd = 4;
 
 // ZOH coefficients of one (step, state): h' = a*h + b with a = Abar and
-// b = Bbar*x.  With q = B*x/A, Bbar*x = (Abar - 1)*q = fma(Abar, q, -q), so
-// the recurrence itself is a single fma (h' = fma(a, h, b)) and a step of
-// zero length (a == 1, b == 0) leaves the state bit-for-bit unchanged.
+// b = Bbar*x.  With q = B*x/A, Bbar*x = (Abar - 1)*q = fma(Abar, q, -q).
 // Where A == 0 (iA is +-inf) the limit Bbar = delta*B is used instead.
 template <bool ZERO_A>
 __device__ __forceinline__ void zoh_coef(float ds, float bx, float A2, float iA, float& a,
@@ -76,18 +78,6 @@ __device__ __forceinline__ void zoh_coef(float ds, float bx, float A2, float iA,
   } else {
     const bool lim = __builtin_isinf(iA);
     b = (lim ? ds : (a - 1.0f) * iA) * bx;
-  }
-}
-
-template <int NPL, bool ZERO_A>
-__device__ __forceinline__ void zoh_step(float dv, float xv, const float* Bv,
-                                         const float (&A2)[NPL], const float (&iA)[NPL],
-                                         float (&h)[NPL]) {
-#pragma unroll
-  for (int k = 0; k < NPL; ++k) {
-    float a, b;
-    zoh_coef<ZERO_A>(dv, Bv[k] * xv, A2[k], iA[k], a, b);
-    h[k] = __builtin_fmaf(a, h[k], b);
   }
 }
 
@@ -115,31 +105,65 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const IO* p, int b, 
   return make_rsrc(p + first, (uint32_t)((size_t)(t_end - t_begin) * dim * sizeof(IO)));
 }
 
-// Raw (undecoded) I/O element as loaded: bf16 bits in the low half, or fp32.
+// Raw (undecoded) I/O element as loaded: bf16 bits in the low half, or fp32 bits.
 template <typename IO> struct Raw;
 template <> struct Raw<float> {
-  using T = float;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
-    return buf<float>::load(r, v, s);
+  __device__ __forceinline__ static uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t v,
+                                                  uint32_t s) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, v, s, 0);
   }
-  __device__ __forceinline__ static float f(T v) { return v; }
+  __device__ __forceinline__ static float f(uint32_t v) { return __builtin_bit_cast(float, v); }
+  // Write as fp32 into an LDS slot.
+  __device__ __forceinline__ static void put(float* slot, uint32_t v) {
+    *slot = __builtin_bit_cast(float, v);
+  }
 };
 template <> struct Raw<bf16> {
-  using T = uint32_t;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  __device__ __forceinline__ static uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t v,
+                                                  uint32_t s) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, v, s, 0);
   }
-  __device__ __forceinline__ static float f(T v) { return bf16_bits_to_f32(v); }
+  __device__ __forceinline__ static float f(uint32_t v) { return bf16_bits_to_f32(v); }
+  // The bf16 bits become the upper half of the fp32 slot; its lower half is
+  // zero (cleared at kernel start, never written), so the slot holds the
+  // exact fp32 value.
+  __device__ __forceinline__ static void put(float* slot, uint32_t v) {
+    reinterpret_cast<uint16_t*>(slot)[1] = (uint16_t)v;
+  }
 };
 
-// Value of lane K of this lane's 16-lane row (DPP row_newbcast).  Written
-// as a DPP move; the compiler folds it into the consuming VOP2 instruction,
-// so the broadcast costs no extra instruction.
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf, true));
-}
+// Stores of y: one value, or two values rounded together (bf16: one
+// v_cvt_pk_bf16_f32, then the two halves to their rows).
+template <typename IO> struct Out;
+template <> struct Out<float> {
+  __device__ __forceinline__ static void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+  }
+  __device__ __forceinline__ static void store2(float v0, float v1, __amdgpu_buffer_rsrc_t r,
+                                                uint32_t voff, uint32_t s0, uint32_t s1) {
+    store(v0, r, voff, s0);
+    store(v1, r, voff, s1);
+  }
+};
+template <> struct Out<bf16> {
+  __device__ __forceinline__ static uint32_t pack(float v0, float v1) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf p = __builtin_convertvector((v2f){v0, v1}, v2bf);
+    return __builtin_bit_cast(uint32_t, p);
+  }
+  __device__ __forceinline__ static void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pack(v, v), r, voff, soff, 0);
+  }
+  __device__ __forceinline__ static void store2(float v0, float v1, __amdgpu_buffer_rsrc_t r,
+                                                uint32_t voff, uint32_t s0, uint32_t s1) {
+    const uint32_t p = pack(v0, v1);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)p, r, voff, s0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(p >> 16), r, voff, s1, 0);
+  }
+};
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time loop).
 template <int N, int I = 0, typename F>
@@ -147,6 +171,46 @@ __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(std::integral_constant<int, I>{});
     static_for<N, I + 1>(f);
+  }
+}
+
+// Keeps the computation of v at this point of the program: an empty asm
+// statement that takes v in a VGPR and may change it.  Code motion before
+// instruction scheduling would otherwise sink the exp2s and input terms of
+// the next step down to their uses, or hoist every LDS read of a tile to its
+// top, and either way the live ranges (and VGPR count) grow.
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+
+// NPL consecutive floats of a wave-uniform LDS address (broadcast read).
+template <int NPL>
+__device__ __forceinline__ void read_n(const float* p, float (&v)[NPL]) {
+  if constexpr (NPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < NPL / 4; ++q) {
+      const float4 w = reinterpret_cast<const float4*>(p)[q];
+      v[4 * q] = w.x;
+      v[4 * q + 1] = w.y;
+      v[4 * q + 2] = w.z;
+      v[4 * q + 3] = w.w;
+    }
+  } else if constexpr (NPL == 2) {
+    const float2 w = reinterpret_cast<const float2*>(p)[0];
+    v[0] = w.x;
+    v[1] = w.y;
+  } else {
+    v[0] = p[0];
+  }
+}
+
+// kT floats of one staged row (16-byte aligned) into registers.
+__device__ __forceinline__ void read_row(const float* p, float (&v)[kT]) {
+#pragma unroll
+  for (int q = 0; q < kT / 4; ++q) {
+    const float4 w = reinterpret_cast<const float4*>(p)[q];
+    v[4 * q] = w.x;
+    v[4 * q + 1] = w.y;
+    v[4 * q + 2] = w.z;
+    v[4 * q + 3] = w.w;
   }
 }
 
@@ -170,49 +234,6 @@ __device__ __forceinline__ Chunk chunk_coords(int dim, int64_t seqlen, int64_t c
   return k;
 }
 
-// How one wave holds the B and C values of its NPL states for a tile of
-// T steps (T*NPL values each):
-//  * B lives in NPL VGPRs, 16 values per register, the same 16 in each of the
-//    four 16-lane rows: value v = step*NPL + k sits in register v/16, lane
-//    v%16 of every row, and is read with row_bcast<v%16>;
-//  * C is staged in LDS (16*NPL floats per tile, double buffered, per wave)
-//    and read with one broadcast LDS load per step.
-template <int NPL, int T>
-struct BCLayout {
-  static constexpr int kVals = T * NPL;                           // B (or C) values per tile
-  static constexpr int kBRegs = (kVals + 15) / 16;                // B VGPRs per tile
-  static constexpr int kCVals = kVals;                            // C floats per tile
-  static constexpr int kCPerLane = (kVals + kWave - 1) / kWave;   // C values loaded per lane
-};
-
-template <typename IO, int NPL, int T>
-struct BCRegs {
-  typename Raw<IO>::T b[BCLayout<NPL, T>::kBRegs], c[BCLayout<NPL, T>::kCPerLane];
-};
-
-// Per-lane byte offsets (within a tile's rows of B or C) of the values this
-// lane loads.
-template <typename IO, int NPL, int T>
-struct BCOffsets {
-  using L = BCLayout<NPL, T>;
-  uint32_t b[L::kBRegs], c[L::kCPerLane];
-  int cslot[L::kCPerLane];  // LDS slot of each C value
-  __device__ __forceinline__ BCOffsets(int lane, int n0) {
-    const int p = lane % 16;
-#pragma unroll
-    for (int r = 0; r < L::kBRegs; ++r) {
-      const int v = min(16 * r + p, L::kVals - 1);
-      b[r] = (uint32_t)(((v / NPL) * kDState + n0 + v % NPL) * sizeof(IO));
-    }
-#pragma unroll
-    for (int r = 0; r < L::kCPerLane; ++r) {
-      const int v = (lane + kWave * r) % L::kCVals;
-      cslot[r] = v;
-      c[r] = (uint32_t)(((v / NPL) * kDState + n0 + v % NPL) * sizeof(IO));
-    }
-  }
-};
-
 // Rows of one chunk of a [b, L, 16] tensor (B or C) as a buffer.
 template <typename IO>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t bc_rsrc(const IO* p, const Chunk& k,
@@ -222,232 +243,310 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bc_rsrc(const IO* p, const Chu
 }
 
 // ---------------------------------------------------------------------------
-// Main scan: one chunk of 64 channels x all 16 states per block.
+// Staging of input tiles through LDS.
 // ---------------------------------------------------------------------------
-template <typename IO, int G, int T>
-struct TileRegs {
-  typename Raw<IO>::T x[T], d[T], z[(T + G - 1) / G];
-  BCRegs<IO, kDState / G, T> bc;
+
+// One pipeline stage: x and delta as [channel][kXS] rows, B and C as
+// [step][state].  WITH_C: the main pass also stages C.
+template <bool WITH_C>
+struct Stage {
+  float x[kWave * kXS];
+  float d[kWave * kXS];
+  float b[kTileBC];
+  float c[WITH_C ? kTileBC : 4];
 };
 
-template <int NPL>
-__device__ __forceinline__ void read_c(const float* cst, int s, float (&cv)[NPL]) {
-  if constexpr (NPL % 4 == 0) {
+// The fetch of one tile is shared evenly by the G waves of the block.  The
+// tile has 2*kT rows of 64 channels (x at steps 0..kT-1, then delta) and
+// NBC*kTileBC values of B (and C, when staged); wave g fetches rows
+// r = g + G*j and the 64-value pieces u = g + G*j of the B/C values.
+template <int G, int NBC>
+struct Share {
+  static constexpr int kRows = 2 * kT / G;                     // rows per wave
+  static constexpr int kPieces = NBC * kTileBC / kWave;        // 64-value pieces per tile
+  static constexpr int kBC = (kPieces + G - 1) / G;            // pieces per wave (at most)
+  static_assert(2 * kT % G == 0, "rows must split evenly over the waves");
+};
+
+template <int G, int NBC>
+struct TileRaw {
+  uint32_t row[Share<G, NBC>::kRows];
+  uint32_t bc[Share<G, NBC>::kBC];
+};
+
+template <typename IO, int G, bool WITH_C>
+struct Loader {
+  static constexpr int NBC = WITH_C ? 2 : 1;
+  using S = Share<G, NBC>;
+  __amdgpu_buffer_rsrc_t rx, rd, rb, rc;
+  uint32_t voff_row, row_bytes;
+  int g;
+
+  __device__ __forceinline__ void init(const IO* x, const IO* delta, const IO* B, const IO* C,
+                                       int64_t seqlen, int dim, const Chunk& k) {
+    rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
+    rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
+    rb = bc_rsrc(B, k, seqlen);
+    rc = bc_rsrc(C, k, seqlen);
+    voff_row = (uint32_t)k.d * sizeof(IO);
+    row_bytes = (uint32_t)dim * sizeof(IO);
+    g = k.g;
+  }
+
+  // Global loads of this wave's share of the tile starting at step s0.
+  __device__ __forceinline__ void issue(TileRaw<G, NBC>& r, int s0, int lane) const {
 #pragma unroll
-    for (int q = 0; q < NPL / 4; ++q) {
-      const float4 v = reinterpret_cast<const float4*>(cst + s * NPL)[q];
-      cv[4 * q] = v.x;
-      cv[4 * q + 1] = v.y;
-      cv[4 * q + 2] = v.z;
-      cv[4 * q + 3] = v.w;
+    for (int j = 0; j < S::kRows; ++j) {
+      const int row = g + G * j;  // < 2*kT
+      const bool is_d = row >= kT;
+      const int s = is_d ? row - kT : row;
+      r.row[j] = Raw<IO>::load(is_d ? rd : rx, voff_row, (uint32_t)(s0 + s) * row_bytes);
     }
-  } else if constexpr (NPL == 2) {
-    const float2 v = reinterpret_cast<const float2*>(cst + s * NPL)[0];
-    cv[0] = v.x;
-    cv[1] = v.y;
-  } else {
-    cv[0] = cst[s];
+#pragma unroll
+    for (int j = 0; j < S::kBC; ++j) {
+      const int piece = min(g + G * j, S::kPieces - 1);  // duplicates are not stored
+      const bool is_c = piece * kWave >= kTileBC;
+      const int v = piece * kWave - (is_c ? kTileBC : 0) + lane;
+      r.bc[j] = Raw<IO>::load(is_c ? rc : rb, (uint32_t)(v * sizeof(IO)),
+                              (uint32_t)s0 * kDState * sizeof(IO));
+    }
+  }
+
+  // Write this wave's share of a tile fetched by issue() into an LDS stage.
+  __device__ __forceinline__ void put(const TileRaw<G, NBC>& r, Stage<WITH_C>& st,
+                                      int lane) const {
+#pragma unroll
+    for (int j = 0; j < S::kRows; ++j) {
+      const int row = g + G * j;
+      const bool is_d = row >= kT;
+      const int s = is_d ? row - kT : row;
+      Raw<IO>::put((is_d ? st.d : st.x) + lane * kXS + s, r.row[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < S::kBC; ++j) {
+      const int piece = g + G * j;
+      if (piece < S::kPieces) {
+        const bool is_c = piece * kWave >= kTileBC;
+        const int v = piece * kWave - (is_c ? kTileBC : 0) + lane;
+        Raw<IO>::put((is_c ? st.c : st.b) + v, r.bc[j]);
+      }
+    }
+  }
+};
+
+// Clear both stages (bf16 inputs rely on zero lower halves of the slots).
+template <typename IO, bool WITH_C>
+__device__ __forceinline__ void clear_stages(Stage<WITH_C>* st, int nthreads) {
+  if constexpr (std::is_same<IO, bf16>::value) {
+    static_assert(sizeof(Stage<WITH_C>) % sizeof(float4) == 0, "stage size");
+    float4* p = reinterpret_cast<float4*>(st);
+    constexpr int n = (int)(2 * sizeof(Stage<WITH_C>) / sizeof(float4));
+    for (int i = threadIdx.x; i < n; i += nthreads) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
-template <typename IO, int G, int T, bool HAS_Z, bool ZERO_A>
+// ---------------------------------------------------------------------------
+// Main scan: one chunk of 64 channels x all 16 states per block.
+// ---------------------------------------------------------------------------
+template <int G>
+struct MainSmem {
+  Stage<true> st[2];
+  float part[2][kT * G * kWave];  // [buffer][step][wave][lane]
+};
+
+template <typename IO, int G, bool HAS_Z, bool ZERO_A>
 __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* __restrict__ delta,
                                            const IO* __restrict__ B, const IO* __restrict__ C,
                                            const IO* __restrict__ z, IO* __restrict__ y,
                                            float Dd, int64_t seqlen, int dim, const Chunk& k,
-                                           float* part, float* cst,
-                                           const float (&A2)[kDState / G],
+                                           MainSmem<G>& sm, const float (&A2)[kDState / G],
                                            const float (&iA)[kDState / G],
                                            float (&h)[kDState / G]) {
   constexpr int NPL = kDState / G;
-  constexpr int ZT = (T + G - 1) / G;  // steps of a tile this wave finishes (at most)
-  constexpr int SG = NPL >= 8 ? 1 : 8 / NPL;  // steps per coefficient group
-  static_assert(T % SG == 0, "tile must split into groups");
-  using R = Raw<IO>;
-  using L = BCLayout<NPL, T>;
-  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
+  constexpr int ZT = (kT + G - 1) / G;        // steps of a tile this wave finishes (at most)
+  constexpr int SG = NPL >= 4 ? 1 : 4 / NPL;  // steps per coefficient group
+  static_assert(kT % SG == 0, "tile must split into groups");
+  const int lane = k.lane, g = k.g, n0 = g * NPL;
   const __amdgpu_buffer_rsrc_t rz = rows_rsrc(HAS_Z ? z : x, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t ry = rows_rsrc(y, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const __amdgpu_buffer_rsrc_t rb = bc_rsrc(B, k, seqlen);
-  const __amdgpu_buffer_rsrc_t rc = bc_rsrc(C, k, seqlen);
-  const BCOffsets<IO, NPL, T> bco(k.lane, k.g * NPL);
   const uint32_t voff = (uint32_t)k.d * sizeof(IO);
   // lanes past the last channel store out of the buffer's range (dropped)
   const uint32_t voff_y = k.active ? voff : 0x80000000u;
   const uint32_t row_bytes = (uint32_t)dim * sizeof(IO);
   const int nsteps = (int)(k.t_end - k.t_begin);
-  const int nfull = nsteps / T;
-  const float dmul = (k.g == 0) ? Dd : 0.0f;  // wave 0 carries the skip term
+  const int nfull = nsteps / kT;
 
-  // Loads of tile `tidx` into r.  Prefetches past the last full tile are
-  // clamped onto it (their values are never used).
-  auto issue = [&](TileRegs<IO, G, T>& r, int tidx) {
-    const int s0 = min(tidx, nfull - 1) * T;
-    const uint32_t bcs = (uint32_t)s0 * kDState * sizeof(IO);
-#pragma unroll
-    for (int j = 0; j < L::kCPerLane; ++j) r.bc.c[j] = R::load(rc, bco.c[j], bcs);
-#pragma unroll
-    for (int j = 0; j < L::kBRegs; ++j) r.bc.b[j] = R::load(rb, bco.b[j], bcs);
-#pragma unroll
-    for (int s = 0; s < T; ++s) {
-      const uint32_t so = (uint32_t)(s0 + s) * row_bytes;
-      r.x[s] = R::load(rx, voff, so);
-      r.d[s] = R::load(rd, voff, so);
-    }
+  Loader<IO, G, true> ld;
+  ld.init(x, delta, B, C, seqlen, dim, k);
+  using Raw2 = TileRaw<G, 2>;
+
+  // z of the steps this wave finishes in tile `tidx` (clamped past the end)
+  auto issue_z = [&](uint32_t (&zr)[ZT], int tidx) {
     if constexpr (HAS_Z) {
+      const int s0 = min(tidx, nfull - 1) * kT;
 #pragma unroll
       for (int j = 0; j < ZT; ++j)
-        r.z[j] = R::load(rz, voff, (uint32_t)min(s0 + k.g + j * G, nsteps - 1) * row_bytes);
+        zr[j] = Raw<IO>::load(rz, voff, (uint32_t)min(s0 + g + j * G, nsteps - 1) * row_bytes);
     }
   };
-  auto stage_c = [&](const TileRegs<IO, G, T>& r, int cb) {
-#pragma unroll
-    for (int j = 0; j < L::kCPerLane; ++j) cst[cb * L::kCVals + bco.cslot[j]] = R::f(r.bc.c[j]);
-  };
 
-  int pbuf = 0;
-  auto tile = [&](const TileRegs<IO, G, T>& r, int tidx, int cb, const TileRegs<IO, G, T>& next,
-                  bool has_next) {
-    const int s0 = tidx * T;
-    float bf[L::kBRegs];
+  int pb = 0;
+  // One tile: compute from stage `cur`, write the next tile's data into the
+  // other stage, barrier, then finish this wave's steps of the tile.
+  auto tile = [&](int tidx, int cur, Raw2& rissue, const Raw2& rput,
+                  const uint32_t (&zuse)[ZT], uint32_t (&znext)[ZT]) {
+    const int s0 = tidx * kT;
+    ld.issue(rissue, min(tidx + 2, nfull - 1) * kT, lane);
+    issue_z(znext, tidx + 1);
+    const Stage<true>& st = sm.st[cur];
+    float xv[kT], dv[kT], xe[ZT];
+    read_row(st.x + lane * kXS, xv);
+    read_row(st.d + lane * kXS, dv);
 #pragma unroll
-    for (int j = 0; j < L::kBRegs; ++j) bf[j] = R::f(r.bc.b[j]);
-    const float* cs = cst + cb * L::kCVals;
-    // Coefficients (exp2 and the input term) of step group j+1 are formed
-    // before the serial updates of group j, so the exp latency and the
-    // coefficient math overlap the recurrence.
-    float* pw = part + pbuf * (G * T * kWave) + k.g * T * kWave + k.lane;  // this wave's partials
-    float ca[2][SG][NPL], cb2[2][SG][NPL], cc[2][SG][NPL];
+    for (int j = 0; j < ZT; ++j) xe[j] = st.x[lane * kXS + min(g + j * G, kT - 1)];
+    float* pw = sm.part[pb] + g * kWave + lane;  // + s * G * kWave for step s
+
+    float ca[2][SG][NPL], cb[2][SG][NPL], cc[2][SG][NPL];
     auto coefs = [&](auto gc, float (&a)[SG][NPL], float (&bb)[SG][NPL], float (&c)[SG][NPL]) {
       constexpr int g0 = decltype(gc)::value * SG;
       static_for<SG>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         constexpr int s = g0 + i;
-        read_c<NPL>(cs, s, c[i]);
-        const float xs = R::f(r.x[s]);
-        const float ds = R::f(r.d[s]);
-        static_for<NPL>([&](auto nc) {
-          constexpr int n = decltype(nc)::value;
-          constexpr int v = s * NPL + n;  // B value (step, state) in the tile
-          zoh_coef<ZERO_A>(ds, row_bcast<v % 16>(bf[v / 16]) * xs, A2[n], iA[n], a[i][n],
-                           bb[i][n]);
-        });
+        float bv[NPL];
+        read_n<NPL>(st.b + s * kDState + n0, bv);
+        read_n<NPL>(st.c + s * kDState + n0, c[i]);
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          zoh_coef<ZERO_A>(dv[s], bv[n] * xv[s], A2[n], iA[n], a[i][n], bb[i][n]);
+          pin(a[i][n]);
+          pin(bb[i][n]);
+        }
       });
     };
-    coefs(std::integral_constant<int, 0>{}, ca[0], cb2[0], cc[0]);
-    static_for<T / SG>([&](auto gc) {
+    coefs(std::integral_constant<int, 0>{}, ca[0], cb[0], cc[0]);
+    static_for<kT / SG>([&](auto gc) {
       constexpr int gi = decltype(gc)::value;
-      if constexpr (gi + 1 < T / SG)
-        coefs(std::integral_constant<int, gi + 1>{}, ca[(gi + 1) & 1], cb2[(gi + 1) & 1],
+      if constexpr (gi + 1 < kT / SG)
+        coefs(std::integral_constant<int, gi + 1>{}, ca[(gi + 1) & 1], cb[(gi + 1) & 1],
               cc[(gi + 1) & 1]);
-      // keep the next group's loads and exp2s ahead of this group's updates
-      // (the scheduler would otherwise sink them next to their uses)
+      // keep the next group's exp2s ahead of this group's updates (the
+      // scheduler would otherwise sink them next to their uses)
       __builtin_amdgcn_sched_barrier(0);
       static_for<SG>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         constexpr int s = gi * SG + i;
-        float acc = dmul * R::f(r.x[s]);
-        static_for<NPL>([&](auto nc) {
-          constexpr int n = decltype(nc)::value;
-          h[n] = __builtin_fmaf(ca[gi & 1][i][n], h[n], cb2[gi & 1][i][n]);
+        h[0] = __builtin_fmaf(ca[gi & 1][i][0], h[0], cb[gi & 1][i][0]);
+        float acc = cc[gi & 1][i][0] * h[0];
+#pragma unroll
+        for (int n = 1; n < NPL; ++n) {
+          h[n] = __builtin_fmaf(ca[gi & 1][i][n], h[n], cb[gi & 1][i][n]);
           acc = __builtin_fmaf(cc[gi & 1][i][n], h[n], acc);
-        });
-        if constexpr (G == 1) {
-          const float yv = HAS_Z ? acc * silu(R::f(r.z[s])) : acc;
-          buf<IO>::store(yv, ry, voff_y, (uint32_t)(s0 + s) * row_bytes);
-        } else {
-          pw[s * kWave] = acc;
         }
+        pin(acc);
+        pw[s * G * kWave] = acc;
       });
     });
-    if (has_next) stage_c(next, cb ^ 1);
-    if constexpr (G > 1) {
-      float* pb = part + pbuf * (G * T * kWave);
-      __syncthreads();
-      // all partial sums first (one batch of LDS reads), then the epilogue
-      float ps[ZT][G];
+    ld.put(rput, sm.st[cur ^ 1], lane);
+    __syncthreads();
+    // epilogue: sum of the G partials, skip term, gate, store
+    const float* pr = sm.part[pb] + lane;
+    float ps[ZT][G];
 #pragma unroll
-      for (int j = 0; j < ZT; ++j) {
-        const int s = min(k.g + j * G, T - 1);
+    for (int j = 0; j < ZT; ++j) {
+      const int s = min(g + j * G, kT - 1);
 #pragma unroll
-        for (int w = 0; w < G; ++w) ps[j][w] = pb[(w * T + s) * kWave + k.lane];
-      }
-#pragma unroll
-      for (int j = 0; j < ZT; ++j) {
-        const int s = k.g + j * G;
-        if (T % G != 0 && s >= T) break;
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < G; ++w) sum += ps[j][w];
-        const float yv = HAS_Z ? sum * silu(R::f(r.z[j])) : sum;
-        buf<IO>::store(yv, ry, voff_y, (uint32_t)(s0 + s) * row_bytes);
-      }
-      pbuf ^= 1;
+      for (int w = 0; w < G; ++w) ps[j][w] = pr[(s * G + w) * kWave];
     }
+    float yv[ZT];
+#pragma unroll
+    for (int j = 0; j < ZT; ++j) {
+      float sum = ps[j][0];
+#pragma unroll
+      for (int w = 1; w < G; ++w) sum += ps[j][w];
+      const float pre = __builtin_fmaf(Dd, xe[j], sum);
+      if constexpr (HAS_Z)
+        yv[j] = pre * silu(Raw<IO>::f(zuse[j]));
+      else
+        yv[j] = pre;
+    }
+    if constexpr (ZT == 2 && kT == 2 * G) {
+      Out<IO>::store2(yv[0], yv[1], ry, voff_y, (uint32_t)(s0 + g) * row_bytes,
+                      (uint32_t)(s0 + g + G) * row_bytes);
+    } else {
+#pragma unroll
+      for (int j = 0; j < ZT; ++j) {
+        const int s = g + j * G;
+        if (kT % G != 0 && s >= kT) break;
+        Out<IO>::store(yv[j], ry, voff_y, (uint32_t)(s0 + s) * row_bytes);
+      }
+    }
+    pb ^= 1;
   };
 
-  // full tiles, two at a time through the ping-pong register sets
-  TileRegs<IO, G, T> ra, rb2;
   if (nfull > 0) {
-    issue(ra, 0);
-    stage_c(ra, 0);
+    Raw2 ra, rb;
+    uint32_t za[ZT], zb[ZT];
+    ld.issue(ra, 0, lane);
+    ld.issue(rb, min(1, nfull - 1) * kT, lane);
+    issue_z(za, 0);
+    ld.put(ra, sm.st[0], lane);
+    __syncthreads();
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+      tile(i, 0, ra, rb, za, zb);
+      tile(i + 1, 1, rb, ra, zb, za);
+    }
+    if (i < nfull) tile(i, 0, ra, rb, za, zb);
   }
-  int i = 0;
-  for (; i + 2 <= nfull; i += 2) {
-    issue(rb2, i + 1);
-    tile(ra, i, 0, rb2, true);
-    issue(ra, i + 2);
-    tile(rb2, i + 1, 1, ra, true);
-  }
-  if (i < nfull) tile(ra, i, 0, ra, false);
 
-  // ragged end of the chunk: one step at a time, no pipelining
-  for (int s0 = nfull * T; s0 < nsteps; ++s0) {
+  // ragged end of the chunk: one step at a time from global memory
+  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
+  const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
+  const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
+  const __amdgpu_buffer_rsrc_t rcc = bc_rsrc(C, k, seqlen);
+  for (int s0 = nfull * kT; s0 < nsteps; ++s0) {
     const uint32_t so = (uint32_t)s0 * row_bytes;
     const float xs = buf<IO>::load(rx, voff, so);
     const float ds = buf<IO>::load(rd, voff, so);
-    const uint32_t bo = (uint32_t)(s0 * kDState + k.g * NPL) * sizeof(IO);
-    float acc = dmul * xs;
+    const uint32_t bo = (uint32_t)(s0 * kDState + n0) * sizeof(IO);
+    float acc = 0.0f;
 #pragma unroll
     for (int n = 0; n < NPL; ++n) {
-      const float Bn = buf<IO>::load(rb, bo + n * sizeof(IO), 0);
-      const float Cn = buf<IO>::load(rc, bo + n * sizeof(IO), 0);
+      const float Bn = buf<IO>::load(rbb, bo + n * sizeof(IO), 0);
+      const float Cn = buf<IO>::load(rcc, bo + n * sizeof(IO), 0);
       float a, b;
       zoh_coef<ZERO_A>(ds, Bn * xs, A2[n], iA[n], a, b);
       h[n] = __builtin_fmaf(a, h[n], b);
       acc = __builtin_fmaf(Cn, h[n], acc);
     }
-    if constexpr (G == 1) {
-      const float yv = HAS_Z ? acc * silu(buf<IO>::load(rz, voff, so)) : acc;
-      buf<IO>::store(yv, ry, voff_y, so);
-    } else {
-      float* pb = part + pbuf * (G * T * kWave);
-      pb[(k.g * T) * kWave + k.lane] = acc;
-      __syncthreads();
-      if (k.g == 0) {
-        float sum = 0.0f;
+    float* pbuf = sm.part[pb];
+    pbuf[g * kWave + lane] = acc;
+    __syncthreads();
+    if (g == 0) {
+      float sum = pbuf[lane];
 #pragma unroll
-        for (int w = 0; w < G; ++w) sum += pb[(w * T) * kWave + k.lane];
-        const float yv = HAS_Z ? sum * silu(buf<IO>::load(rz, voff, so)) : sum;
-        buf<IO>::store(yv, ry, voff_y, so);
-      }
-      pbuf ^= 1;
+      for (int w = 1; w < G; ++w) sum += pbuf[w * kWave + lane];
+      const float pre = __builtin_fmaf(Dd, xs, sum);
+      const float yv = HAS_Z ? pre * silu(buf<IO>::load(rz, voff, so)) : pre;
+      Out<IO>::store(yv, ry, voff_y, so);
     }
+    pb ^= 1;
   }
 }
-template <typename IO, int G, int T, bool HAS_Z>
-__global__ __launch_bounds__(kWave* G) void scan_fwd_kernel(
+
+template <typename IO, int G, bool HAS_Z>
+__global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kMainWavesPerSimd)))
+void scan_fwd_kernel(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
     const IO* __restrict__ z, const float* __restrict__ h0, IO* __restrict__ y,
     float* __restrict__ h_last, const float* __restrict__ ws_hin, int64_t seqlen,
     int64_t chunk_len, int dim, int nchunks) {
   constexpr int NPL = kDState / G;
-  __shared__ float part[G > 1 ? 2 * G * T * kWave : 1];
-  __shared__ float cst_all[G * 2 * BCLayout<NPL, T>::kCVals];
+  __shared__ MainSmem<G> sm;
   const Chunk k = chunk_coords(dim, seqlen, chunk_len);
   const int n0 = k.g * NPL;
+  clear_stages<IO, true>(sm.st, kWave * G);
 
   float A2[NPL], iA[NPL], h[NPL];
   const bool zero = load_A<NPL>(A, k.d, n0, A2, iA);
@@ -459,14 +558,12 @@ __global__ __launch_bounds__(kWave* G) void scan_fwd_kernel(
 #pragma unroll
   for (int j = 0; j < NPL; ++j) h[j] = hinit ? hinit[j] : 0.0f;
   const float Dd = Dskip ? Dskip[k.d] : 0.0f;
-  float* cst = cst_all + k.g * 2 * BCLayout<NPL, T>::kCVals;
+  __syncthreads();  // stages cleared
 
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    scan_chunk<IO, G, T, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, part, cst, A2,
-                                      iA, h);
+    scan_chunk<IO, G, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA, h);
   else
-    scan_chunk<IO, G, T, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, part, cst, A2,
-                                       iA, h);
+    scan_chunk<IO, G, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA, h);
 
   if (k.c == nchunks - 1 && h_last && k.active) {
     float* hl = h_last + ((size_t)k.b * dim + k.d) * kDState + n0;
@@ -477,101 +574,138 @@ __global__ __launch_bounds__(kWave* G) void scan_fwd_kernel(
 
 // ---------------------------------------------------------------------------
 // Carry pass 1: end state of every chunk but the last, started from zero,
-// plus the chunk's sum of delta (accumulated in fp64).  Same pipelining and
-// B layout as the main kernel, without the readout.
+// plus the chunk's sum of delta.  Same staging as the main kernel, without
+// C and the readout.  With no A == 0 in the wave it carries g = A*h.
 // ---------------------------------------------------------------------------
-template <typename IO, int G, int T, bool ZERO_A>
+template <typename IO, int G, bool ZERO_A>
 __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
                                             const IO* __restrict__ delta,
                                             const IO* __restrict__ B, int64_t seqlen, int dim,
-                                            const Chunk& k, const float (&A2)[kDState / G],
+                                            const Chunk& k, Stage<false>* stages,
+                                            const float (&A2)[kDState / G],
                                             const float (&iA)[kDState / G],
                                             float (&h)[kDState / G], double& sd) {
   constexpr int NPL = kDState / G;
-  using R = Raw<IO>;
-  using L = BCLayout<NPL, T>;
-  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const __amdgpu_buffer_rsrc_t rb = bc_rsrc(B, k, seqlen);
-  const BCOffsets<IO, NPL, T> bco(k.lane, k.g * NPL);
+  const int lane = k.lane, n0 = k.g * NPL;
   const uint32_t voff = (uint32_t)k.d * sizeof(IO);
   const uint32_t row_bytes = (uint32_t)dim * sizeof(IO);
   const int nsteps = (int)(k.t_end - k.t_begin);
-  const int nfull = nsteps / T;
+  const int nfull = nsteps / kT;
 
-  struct Regs {
-    typename R::T x[T], d[T], b[L::kBRegs];
-  };
-  auto issue = [&](Regs& r, int tidx) {
-    const int s0 = min(tidx, nfull - 1) * T;
-    const uint32_t bcs = (uint32_t)s0 * kDState * sizeof(IO);
+  Loader<IO, G, false> ld;
+  ld.init(x, delta, B, B, seqlen, dim, k);
+  using Raw1 = TileRaw<G, 1>;
+
+  // state carried through the tiles: g = A*h (or h itself when A may be 0)
+  float gs[NPL];
 #pragma unroll
-    for (int j = 0; j < L::kBRegs; ++j) r.b[j] = R::load(rb, bco.b[j], bcs);
-#pragma unroll
-    for (int s = 0; s < T; ++s) {
-      const uint32_t so = (uint32_t)(s0 + s) * row_bytes;
-      r.x[s] = R::load(rx, voff, so);
-      r.d[s] = R::load(rd, voff, so);
-    }
-  };
-  auto tile = [&](const Regs& r) {
-    float bf[L::kBRegs];
-#pragma unroll
-    for (int j = 0; j < L::kBRegs; ++j) bf[j] = R::f(r.b[j]);
-    static_for<T>([&](auto sc) {
+  for (int n = 0; n < NPL; ++n) gs[n] = 0.0f;
+
+  auto tile = [&](int tidx, int cur, Raw1& rissue, const Raw1& rput) {
+    ld.issue(rissue, min(tidx + 2, nfull - 1) * kT, lane);
+    const Stage<false>& st = stages[cur];
+    float xv[kT], dv[kT];
+    read_row(st.x + lane * kXS, xv);
+    read_row(st.d + lane * kXS, dv);
+    // the exp2 and input term of step s+1 are formed before the update of
+    // step s, so their latency hides behind the recurrence
+    float ca[2][NPL], cb[2][NPL];
+    auto coefs = [&](auto sc, float (&a)[NPL], float (&b)[NPL]) {
       constexpr int s = decltype(sc)::value;
-      const float xs = R::f(r.x[s]);
-      const float ds = R::f(r.d[s]);
-      static_for<NPL>([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        constexpr int v = s * NPL + n;
-        float a, b;
-        zoh_coef<ZERO_A>(ds, row_bcast<v % 16>(bf[v / 16]) * xs, A2[n], iA[n], a, b);
-        h[n] = __builtin_fmaf(a, h[n], b);
-      });
-      sd += (double)ds;
+      float bv[NPL];
+      read_n<NPL>(st.b + s * kDState + n0, bv);
+#pragma unroll
+      for (int n = 0; n < NPL; ++n) {
+        const float bx = bv[n] * xv[s];
+        if constexpr (!ZERO_A) {
+          a[n] = fast_exp2(dv[s] * A2[n]);
+          b[n] = __builtin_fmaf(a[n], bx, -bx);
+        } else {
+          zoh_coef<true>(dv[s], bx, A2[n], iA[n], a[n], b[n]);
+        }
+        pin(a[n]);
+        pin(b[n]);
+      }
+    };
+    coefs(std::integral_constant<int, 0>{}, ca[0], cb[0]);
+    static_for<kT>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s + 1 < kT)
+        coefs(std::integral_constant<int, s + 1>{}, ca[(s + 1) & 1], cb[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int n = 0; n < NPL; ++n) {
+        gs[n] = __builtin_fmaf(ca[s & 1][n], gs[n], cb[s & 1][n]);
+        pin(gs[n]);
+      }
     });
+    // sum of delta over the tile: pairwise in fp32, then into fp64
+    float t4[kT / 2];
+#pragma unroll
+    for (int j = 0; j < kT / 2; ++j) t4[j] = dv[2 * j] + dv[2 * j + 1];
+#pragma unroll
+    for (int w = kT / 4; w >= 1; w /= 2)
+#pragma unroll
+      for (int j = 0; j < w; ++j) t4[j] = t4[j] + t4[j + w];
+    sd += (double)t4[0];
+    ld.put(rput, stages[cur ^ 1], lane);
+    __syncthreads();
   };
-  Regs ra, rb2;
-  if (nfull > 0) issue(ra, 0);
-  int i = 0;
-  for (; i + 2 <= nfull; i += 2) {
-    issue(rb2, i + 1);
-    tile(ra);
-    issue(ra, i + 2);
-    tile(rb2);
+
+  if (nfull > 0) {
+    Raw1 ra, rb;
+    ld.issue(ra, 0, lane);
+    ld.issue(rb, min(1, nfull - 1) * kT, lane);
+    ld.put(ra, stages[0], lane);
+    __syncthreads();
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+      tile(i, 0, ra, rb);
+      tile(i + 1, 1, rb, ra);
+    }
+    if (i < nfull) tile(i, 0, ra, rb);
   }
-  if (i < nfull) tile(ra);
-  for (int s0 = nfull * T; s0 < nsteps; ++s0) {
+#pragma unroll
+  for (int n = 0; n < NPL; ++n) h[n] = ZERO_A ? gs[n] : gs[n] * iA[n];
+
+  // ragged end of the chunk
+  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
+  const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
+  const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
+  for (int s0 = nfull * kT; s0 < nsteps; ++s0) {
     const uint32_t so = (uint32_t)s0 * row_bytes;
     const float xs = buf<IO>::load(rx, voff, so);
     const float ds = buf<IO>::load(rd, voff, so);
-    const uint32_t bo = (uint32_t)(s0 * kDState + k.g * NPL) * sizeof(IO);
-    float Bv[NPL];
+    const uint32_t bo = (uint32_t)(s0 * kDState + n0) * sizeof(IO);
 #pragma unroll
-    for (int n = 0; n < NPL; ++n) Bv[n] = buf<IO>::load(rb, bo + n * sizeof(IO), 0);
-    zoh_step<NPL, ZERO_A>(ds, xs, Bv, A2, iA, h);
+    for (int n = 0; n < NPL; ++n) {
+      float a, b;
+      zoh_coef<ZERO_A>(ds, buf<IO>::load(rbb, bo + n * sizeof(IO), 0) * xs, A2[n], iA[n], a, b);
+      h[n] = __builtin_fmaf(a, h[n], b);
+    }
     sd += (double)ds;
   }
 }
 
-template <typename IO, int G, int T>
-__global__ __launch_bounds__(kWave* G) void scan_chunk_state_kernel(
+template <typename IO, int G>
+__global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kCarryWavesPerSimd)))
+void scan_chunk_state_kernel(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, float* __restrict__ ws_hloc, double* __restrict__ ws_sdelta,
     int64_t seqlen, int64_t chunk_len, int dim, int nchunks) {
   constexpr int NPL = kDState / G;
+  __shared__ Stage<false> stages[2];
   const Chunk k = chunk_coords(dim, seqlen, chunk_len);  // k.c in [0, nchunks-2]
   const int n0 = k.g * NPL;
+  clear_stages<IO, false>(stages, kWave * G);
   float A2[NPL], iA[NPL], h[NPL];
   const bool zero = load_A<NPL>(A, k.d, n0, A2, iA);
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) h[j] = 0.0f;
   double sd = 0.0;
+  __syncthreads();  // stages cleared
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    chunk_state<IO, G, T, true>(x, delta, B, seqlen, dim, k, A2, iA, h, sd);
+    chunk_state<IO, G, true>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd);
   else
-    chunk_state<IO, G, T, false>(x, delta, B, seqlen, dim, k, A2, iA, h, sd);
+    chunk_state<IO, G, false>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd);
   if (k.active) {
     const size_t cd = ((size_t)k.b * nchunks + k.c) * dim + k.d;
     float* hl = ws_hloc + cd * kDState + n0;
@@ -617,7 +751,6 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
 
 template <typename IO, int G>
 hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
-  constexpr int T = 8;  // steps per tile (chunks are whole multiples of it)
   const IO* x = static_cast<const IO*>(a.x);
   const IO* delta = static_cast<const IO*>(a.delta);
   const IO* B = static_cast<const IO*>(a.B);
@@ -625,7 +758,7 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
   const unsigned gx = (unsigned)((a.dim + kWave - 1) / kWave);
   if (a.nchunks > 1 && (phase & 1)) {
     dim3 grid1(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, G, T>), grid1, dim3(kWave * G), 0, stream, x,
+    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, G>), grid1, dim3(kWave * G), 0, stream, x,
                        delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len, a.dim,
                        a.nchunks);
     hipError_t e = hipGetLastError();
@@ -640,12 +773,12 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
   if (!(phase & 2)) return hipSuccess;
   dim3 grid(gx, (unsigned)a.nchunks, (unsigned)a.batch);
   if (a.z)
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, T, true>), grid, dim3(kWave * G), 0, stream, x,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, true>), grid, dim3(kWave * G), 0, stream, x,
                        delta, a.A, B, C, a.Dskip, static_cast<const IO*>(a.z), a.h0,
                        static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
                        a.nchunks);
   else
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, T, false>), grid, dim3(kWave * G), 0, stream, x,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, false>), grid, dim3(kWave * G), 0, stream, x,
                        delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr), a.h0,
                        static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
                        a.nchunks);

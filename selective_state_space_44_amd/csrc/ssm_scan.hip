@@ -214,6 +214,18 @@ __device__ __forceinline__ void read_row(const float* p, float (&v)[kT]) {
   }
 }
 
+// Entries [h0, h0 + kT/2) of one staged row into the same entries of v.
+__device__ __forceinline__ void read_half(const float* p, float (&v)[kT], int h0) {
+#pragma unroll
+  for (int q = h0 / 4; q < (h0 + kT / 2) / 4; ++q) {
+    const float4 w = reinterpret_cast<const float4*>(p)[q];
+    v[4 * q] = w.x;
+    v[4 * q + 1] = w.y;
+    v[4 * q + 2] = w.z;
+    v[4 * q + 3] = w.w;
+  }
+}
+
 struct Chunk {
   int lane, g, b, c, d;
   bool active;
@@ -364,8 +376,6 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
                                            float (&h)[kDState / G]) {
   constexpr int NPL = kDState / G;
   constexpr int ZT = (kT + G - 1) / G;        // steps of a tile this wave finishes (at most)
-  constexpr int SG = NPL >= 4 ? 1 : 4 / NPL;  // steps per coefficient group
-  static_assert(kT % SG == 0, "tile must split into groups");
   const int lane = k.lane, g = k.g, n0 = g * NPL;
   const __amdgpu_buffer_rsrc_t rz = rows_rsrc(HAS_Z ? z : x, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t ry = rows_rsrc(y, k.b, seqlen, dim, k.t_begin, k.t_end);
@@ -399,52 +409,66 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
     ld.issue(rissue, min(tidx + 2, nfull - 1) * kT, lane);
     issue_z(znext, tidx + 1);
     const Stage<true>& st = sm.st[cur];
+    // x and delta of the tile, read in two halves (the second half once the
+    // first is no longer needed) to keep the register count down
     float xv[kT], dv[kT], xe[ZT];
-    read_row(st.x + lane * kXS, xv);
-    read_row(st.d + lane * kXS, dv);
+    read_half(st.x + lane * kXS, xv, 0);
+    read_half(st.d + lane * kXS, dv, 0);
 #pragma unroll
     for (int j = 0; j < ZT; ++j) xe[j] = st.x[lane * kXS + min(g + j * G, kT - 1)];
     float* pw = sm.part[pb] + g * kWave + lane;  // + s * G * kWave for step s
 
-    float ca[2][SG][NPL], cb[2][SG][NPL], cc[2][SG][NPL];
-    auto coefs = [&](auto gc, float (&a)[SG][NPL], float (&bb)[SG][NPL], float (&c)[SG][NPL]) {
-      constexpr int g0 = decltype(gc)::value * SG;
-      static_for<SG>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        constexpr int s = g0 + i;
-        float bv[NPL];
-        read_n<NPL>(st.b + s * kDState + n0, bv);
-        read_n<NPL>(st.c + s * kDState + n0, c[i]);
-#pragma unroll
-        for (int n = 0; n < NPL; ++n) {
-          zoh_coef<ZERO_A>(dv[s], bv[n] * xv[s], A2[n], iA[n], a[i][n], bb[i][n]);
-          pin(a[i][n]);
-          pin(bb[i][n]);
-        }
-      });
+    // B and C of step s are read from LDS two steps before their use; the
+    // exp2s and input terms are formed one step before (all exp2s of a step
+    // first, so their latency overlaps the input terms).
+    float bq[2][NPL], cq[2][NPL];
+    auto fetch = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      read_n<NPL>(st.b + s * kDState + n0, bq[s & 1]);
+      read_n<NPL>(st.c + s * kDState + n0, cq[s & 1]);
     };
-    coefs(std::integral_constant<int, 0>{}, ca[0], cb[0], cc[0]);
-    static_for<kT / SG>([&](auto gc) {
-      constexpr int gi = decltype(gc)::value;
-      if constexpr (gi + 1 < kT / SG)
-        coefs(std::integral_constant<int, gi + 1>{}, ca[(gi + 1) & 1], cb[(gi + 1) & 1],
-              cc[(gi + 1) & 1]);
-      // keep the next group's exp2s ahead of this group's updates (the
-      // scheduler would otherwise sink them next to their uses)
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<SG>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        constexpr int s = gi * SG + i;
-        h[0] = __builtin_fmaf(ca[gi & 1][i][0], h[0], cb[gi & 1][i][0]);
-        float acc = cc[gi & 1][i][0] * h[0];
+    float ca[2][NPL], cb[2][NPL], cc[2][NPL];
+    auto coefs = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
 #pragma unroll
-        for (int n = 1; n < NPL; ++n) {
-          h[n] = __builtin_fmaf(ca[gi & 1][i][n], h[n], cb[gi & 1][i][n]);
-          acc = __builtin_fmaf(cc[gi & 1][i][n], h[n], acc);
+      for (int n = 0; n < NPL; ++n) {
+        ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
+        pin(ca[s & 1][n]);
+      }
+#pragma unroll
+      for (int n = 0; n < NPL; ++n) {
+        const float bx = bq[s & 1][n] * xv[s];
+        const float a = ca[s & 1][n];
+        if constexpr (!ZERO_A) {
+          const float q = bx * iA[n];
+          cb[s & 1][n] = __builtin_fmaf(a, q, -q);
+        } else {
+          cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
         }
-        pin(acc);
-        pw[s * G * kWave] = acc;
-      });
+        pin(cb[s & 1][n]);
+        cc[s & 1][n] = cq[s & 1][n];
+      }
+    };
+    fetch(std::integral_constant<int, 0>{});
+    fetch(std::integral_constant<int, 1>{});
+    coefs(std::integral_constant<int, 0>{});
+    static_for<kT>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s + 1 < kT) coefs(std::integral_constant<int, s + 1>{});
+      if constexpr (s + 2 == kT / 2) {
+        read_half(st.x + lane * kXS, xv, kT / 2);
+        read_half(st.d + lane * kXS, dv, kT / 2);
+      }
+      if constexpr (s + 2 < kT) fetch(std::integral_constant<int, s + 2>{});
+      h[0] = __builtin_fmaf(ca[s & 1][0], h[0], cb[s & 1][0]);
+      float acc = cc[s & 1][0] * h[0];
+#pragma unroll
+      for (int n = 1; n < NPL; ++n) {
+        h[n] = __builtin_fmaf(ca[s & 1][n], h[n], cb[s & 1][n]);
+        acc = __builtin_fmaf(cc[s & 1][n], h[n], acc);
+      }
+      pin(acc);
+      pw[s * G * kWave] = acc;
     });
     ld.put(rput, sm.st[cur ^ 1], lane);
     __syncthreads();
@@ -607,32 +631,39 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
     float xv[kT], dv[kT];
     read_row(st.x + lane * kXS, xv);
     read_row(st.d + lane * kXS, dv);
-    // the exp2 and input term of step s+1 are formed before the update of
-    // step s, so their latency hides behind the recurrence
-    float ca[2][NPL], cb[2][NPL];
-    auto coefs = [&](auto sc, float (&a)[NPL], float (&b)[NPL]) {
+    // B of step s is read from LDS two steps before its use; the exp2s and
+    // input terms are formed one step before (all exp2s of a step first)
+    float bq[2][NPL];
+    auto fetch = [&](auto sc) {
       constexpr int s = decltype(sc)::value;
-      float bv[NPL];
-      read_n<NPL>(st.b + s * kDState + n0, bv);
+      read_n<NPL>(st.b + s * kDState + n0, bq[s & 1]);
+    };
+    float ca[2][NPL], cb[2][NPL];
+    auto coefs = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
-        const float bx = bv[n] * xv[s];
-        if constexpr (!ZERO_A) {
-          a[n] = fast_exp2(dv[s] * A2[n]);
-          b[n] = __builtin_fmaf(a[n], bx, -bx);
-        } else {
-          zoh_coef<true>(dv[s], bx, A2[n], iA[n], a[n], b[n]);
-        }
-        pin(a[n]);
-        pin(b[n]);
+        ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
+        pin(ca[s & 1][n]);
+      }
+#pragma unroll
+      for (int n = 0; n < NPL; ++n) {
+        const float bx = bq[s & 1][n] * xv[s];
+        const float a = ca[s & 1][n];
+        if constexpr (!ZERO_A)
+          cb[s & 1][n] = __builtin_fmaf(a, bx, -bx);  // (a - 1) * B x, for g = A h
+        else
+          cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
+        pin(cb[s & 1][n]);
       }
     };
-    coefs(std::integral_constant<int, 0>{}, ca[0], cb[0]);
+    fetch(std::integral_constant<int, 0>{});
+    fetch(std::integral_constant<int, 1>{});
+    coefs(std::integral_constant<int, 0>{});
     static_for<kT>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
-      if constexpr (s + 1 < kT)
-        coefs(std::integral_constant<int, s + 1>{}, ca[(s + 1) & 1], cb[(s + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (s + 1 < kT) coefs(std::integral_constant<int, s + 1>{});
+      if constexpr (s + 2 < kT) fetch(std::integral_constant<int, s + 2>{});
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
         gs[n] = __builtin_fmaf(ca[s & 1][n], gs[n], cb[s & 1][n]);
@@ -757,8 +788,11 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
   const IO* C = static_cast<const IO*>(a.C);
   const unsigned gx = (unsigned)((a.dim + kWave - 1) / kWave);
   if (a.nchunks > 1 && (phase & 1)) {
+    // the carry pass has no readout to share, so it splits the states over
+    // more waves (two per wave) for latency hiding
+    constexpr int GC = G < 8 ? 8 : G;
     dim3 grid1(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, G>), grid1, dim3(kWave * G), 0, stream, x,
+    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, GC>), grid1, dim3(kWave * GC), 0, stream, x,
                        delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len, a.dim,
                        a.nchunks);
     hipError_t e = hipGetLastError();

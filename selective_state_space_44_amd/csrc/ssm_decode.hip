@@ -9,9 +9,11 @@
 //
 // Layout: 4 consecutive lanes own one (b, d) and each holds 4 of its 16
 // states as one float4, so a wave streams 16 channels = 1 KiB of contiguous
-// state with 16-byte loads and stores.  The readout's 16-term sum is the
-// lane's 4-term partial plus two cross-lane butterfly steps; lane 0 of the
-// quad applies the skip term and gate and stores y.
+// state with 16-byte non-temporal loads and stores (the state is touched
+// once per step).  The readout's 16-term sum is the lane's 4-term partial
+// plus two DPP quad swaps; lane 0 of the quad applies the skip term and gate
+// and stores y.  The grid's y dimension is the batch row, so no 64-bit
+// division splits a flat index.
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -33,63 +35,92 @@ template <> struct Quad<bf16> {
   }
 };
 
-__device__ __forceinline__ float zoh_update(float h, float av, float dv, float bv, float xv) {
-  const float a = fast_exp2(dv * (av * kLog2e));  // Abar = exp(delta * A)
-  const float bx = bv * xv;
-  if (av != 0.0f) {
-    const float q = bx * (1.0f / av);              // B x / A
-    return __builtin_fmaf(a, h + q, -q);           // Abar (h + q) - q
-  }
-  return __builtin_fmaf(dv, bx, h);                // A == 0: Bbar = delta * B
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Value of the lane `mask` places away inside each group of 4 lanes (DPP quad
+// permutation; 0xB1 swaps neighbours, 0x4E swaps pairs).
+template <int PERM>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), PERM, 0xf, 0xf, false));
+}
+
+// One ZOH step of one state: h' = Abar*h + Bbar*x with Abar = exp(delta*A),
+// Bbar*x = (Abar - 1) * (B*x/A) = fma(Abar, q, -q).  A zero step leaves h
+// bit-for-bit unchanged; A == 0 takes the limit Bbar = delta*B.
+__device__ __forceinline__ float zoh_update(float h, float av, float iav, float dl, float dv,
+                                           float bx) {
+  const float abar = fast_exp2(dl * av);  // dl = delta * log2(e)
+  const float q = bx * iav;               // iav = 1/A
+  const float b = av != 0.0f ? __builtin_fmaf(abar, q, -q) : dv * bx;
+  return __builtin_fmaf(abar, h, b);
 }
 
 template <typename IO>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t ch = gid >> 2;  // (b, d)
-  const int q = (int)(gid & 3);
-  if (ch >= a.batch * a.dim) return;  // whole quads leave together
-  const int64_t b = ch / a.dim;
-  const int d = (int)(ch % a.dim);
-
-  float4* hp = reinterpret_cast<float4*>(a.h) + ch * 4 + q;
-  float4 h = *hp;
-  const float4 A = reinterpret_cast<const float4*>(a.A)[(size_t)d * 4 + q];
+  const int t = blockIdx.x * 256 + threadIdx.x;  // (channel, quarter) in one batch row
+  const int d = t >> 2;
+  const int q = t & 3;
+  if (d >= a.dim) return;  // whole quads leave together
+  const int64_t b = a.row0 + blockIdx.y;
+  const size_t ch = (size_t)b * a.dim + d;
+  v4f* hp = reinterpret_cast<v4f*>(a.h) + ch * 4 + q;
+  // Every load is issued before any result is waited on.  The small shared
+  // and per-channel inputs go first and the streamed state (touched once per
+  // step, so read and written non-temporally) last; on MI355X this order and
+  // plain loads for x, delta and z measured fastest.
+  const v4f A = reinterpret_cast<const v4f*>(a.A)[(size_t)d * 4 + q];
   const float4 Bq = Quad<IO>::load(static_cast<const IO*>(a.B) + b * kDState + 4 * q);
   const float4 Cq = Quad<IO>::load(static_cast<const IO*>(a.C) + b * kDState + 4 * q);
   const float xv = io<IO>::load(static_cast<const IO*>(a.x) + ch);
   const float dv = io<IO>::load(static_cast<const IO*>(a.delta) + ch);
+  // optional inputs are read unconditionally (from a valid stand-in when
+  // absent): a branch between loads makes the compiler wait for all of them
+  const IO* zsrc = static_cast<const IO*>(a.z ? a.z : a.x);
+  const float* dsrc = a.Dskip ? a.Dskip : a.A;
+  float zv = io<IO>::load(zsrc + ch);
+  float dload = dsrc[d];
+  asm volatile("" : "+v"(zv), "+v"(dload));  // keep both loads here, unconditional
+  v4f h = __builtin_nontemporal_load(hp);
+  const float Dd = a.Dskip ? dload : 0.0f;
+  const float dl = dv * kLog2e;
 
-  h.x = zoh_update(h.x, A.x, dv, Bq.x, xv);
-  h.y = zoh_update(h.y, A.y, dv, Bq.y, xv);
-  h.z = zoh_update(h.z, A.z, dv, Bq.z, xv);
-  h.w = zoh_update(h.w, A.w, dv, Bq.w, xv);
-  *hp = h;
+  h.x = zoh_update(h.x, A.x, __builtin_amdgcn_rcpf(A.x), dl, dv, Bq.x * xv);
+  h.y = zoh_update(h.y, A.y, __builtin_amdgcn_rcpf(A.y), dl, dv, Bq.y * xv);
+  h.z = zoh_update(h.z, A.z, __builtin_amdgcn_rcpf(A.z), dl, dv, Bq.z * xv);
+  h.w = zoh_update(h.w, A.w, __builtin_amdgcn_rcpf(A.w), dl, dv, Bq.w * xv);
+  __builtin_nontemporal_store(h, hp);
 
   float p = Cq.x * h.x;
   p = __builtin_fmaf(Cq.y, h.y, p);
   p = __builtin_fmaf(Cq.z, h.z, p);
   p = __builtin_fmaf(Cq.w, h.w, p);
-  p += __shfl_xor(p, 1);
-  p += __shfl_xor(p, 2);
+  p += quad_swap<0xB1>(p);
+  p += quad_swap<0x4E>(p);
   if (q == 0) {
-    const float Dd = a.Dskip ? a.Dskip[d] : 0.0f;
     const float pre = __builtin_fmaf(Dd, xv, p);
-    const float yv = a.z ? pre * silu(io<IO>::load(static_cast<const IO*>(a.z) + ch)) : pre;
-    io<IO>::store(static_cast<IO*>(a.y) + ch, yv);
+    io<IO>::store(static_cast<IO*>(a.y) + ch, a.z ? pre * silu(zv) : pre);
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, hipStream_t stream) {
-  const int64_t threads = a.batch * a.dim * 4;
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  if (io_bf16)
-    hipLaunchKernelGGL(decode_step_kernel<bf16>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_step_kernel<float>, grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_decode(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
+  const int64_t threads = (int64_t)args.dim * 4;  // per batch row
+  constexpr int64_t kMaxRows = 65535;              // grid y extent per launch
+  for (int64_t r0 = 0; r0 < args.batch; r0 += kMaxRows) {
+    DecodeArgs a = args;
+    a.row0 = r0;
+    const int64_t rows = args.batch - r0 < kMaxRows ? args.batch - r0 : kMaxRows;
+    const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)rows);
+    if (io_bf16)
+      hipLaunchKernelGGL(decode_step_kernel<bf16>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_step_kernel<float>, grid, dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ssm

@@ -43,6 +43,7 @@ struct DecodeArgs {
   void* y;
   int64_t batch;
   int dim;
+  int64_t row0;        // first batch row of this launch (set by launch_decode)
 };
 
 // Steps per tile of the scan kernels; chunks start on a tile boundary.

@@ -208,8 +208,8 @@ def bench_decode(sweeps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-sweeps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU-baseline sample (0 = skip)")

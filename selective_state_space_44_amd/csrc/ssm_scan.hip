@@ -38,8 +38,9 @@
 //     L into K chunks, a first kernel runs every chunk but the last from a
 //     zero state and records its end state hloc_c and sum of delta; a carry
 //     kernel composes the affine maps h -> P_c h + hloc_c with
-//     P_c = exp(A * sum(delta over chunk c)) in chunk order; the main kernel
-//     then runs every chunk from its true entering state.  The first kernel
+//     P_c = exp(A * sum(delta over chunk c)) by an in-wave prefix scan over
+//     lane shuffles; the main kernel then runs every chunk from its true
+//     entering state.  The first kernel
 //     needs no readout, so it carries g = A*h instead of h:
 //     g = fma(a, g, fma(a, B*x, -B*x)), one multiply per element fewer, and
 //     converts back (h = g/A) once at the end of the chunk.
@@ -747,29 +748,54 @@ void scan_chunk_state_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Carry pass 2: compose h -> P_c h + hloc_c over the chunks in order and
-// record the state entering every chunk.  One thread per (b, d, n).
+// Carry pass 2: the state entering every chunk.  Chunk c maps its entering
+// state h to P_c h + hloc_c; the maps compose associatively,
+// (P2, H2) o (P1, H1) = (P2 P1, P2 H1 + H2), so the entering states are an
+// exclusive prefix scan of the maps applied to h0 (paperlens tutorial,
+// parallel-scan section).  Each (b, d, n) owns a segment of S = 2^seg_log2
+// lanes of a wave; lane j holds map j of a round of S maps, and the segment
+// combines them with a Hillis-Steele scan over lane shuffles (log2 S steps).
+// Rounds continue until all nchunks - 1 maps are applied.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scan_carry_kernel(
     const float* __restrict__ A, const float* __restrict__ h0,
     const float* __restrict__ ws_hloc, const double* __restrict__ ws_sdelta,
-    float* __restrict__ ws_hin, int batch, int dim, int nchunks) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int seg_log2) {
+  const int S = 1 << seg_log2;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t seg = gid >> seg_log2;
+  const int j = (int)(gid & (S - 1));
   const int64_t total = (int64_t)batch * dim * kDState;
-  if (i >= total) return;
-  const int n = (int)(i % kDState);
-  const int64_t bd = i / kDState;
+  // segments past the end still take part in the shuffles, with no memory access
+  const bool valid = seg < total;
+  const int64_t segc = valid ? seg : 0;
+  const int n = (int)(segc % kDState);
+  const int64_t bd = segc / kDState;
   const int d = (int)(bd % dim);
   const int64_t b = bd / dim;
   const float A2 = A[(size_t)d * kDState + n] * kLog2e;
-  float h = h0 ? h0[i] : 0.0f;
-  for (int c = 0; c < nchunks; ++c) {
-    const size_t cd = ((size_t)b * nchunks + c) * dim + d;
-    ws_hin[cd * kDState + n] = h;
-    if (c + 1 < nchunks) {
-      const float P = fast_exp2((float)((double)A2 * ws_sdelta[cd]));
-      h = __builtin_fmaf(P, h, ws_hloc[cd * kDState + n]);
+  auto at = [&](int c) { return (((size_t)b * nchunks + c) * dim + d) * kDState + n; };
+  float h = (h0 && valid) ? h0[segc] : 0.0f;
+  if (j == 0 && valid) ws_hin[at(0)] = h;
+  for (int base = 0; base < nchunks - 1; base += S) {
+    const int c = base + j;  // this lane's map: entering state of chunk c -> of chunk c + 1
+    float P = 1.0f, H = 0.0f;
+    if (c < nchunks - 1 && valid) {
+      const size_t cd = ((size_t)b * nchunks + c) * dim + d;
+      P = fast_exp2((float)((double)A2 * ws_sdelta[cd]));
+      H = ws_hloc[cd * kDState + n];
     }
+    for (int off = 1; off < S; off <<= 1) {  // inclusive scan inside the segment
+      const float Pu = __shfl_up(P, off, S);
+      const float Hu = __shfl_up(H, off, S);
+      if (j >= off) {
+        H = __builtin_fmaf(P, Hu, H);
+        P = P * Pu;
+      }
+    }
+    const float hn = __builtin_fmaf(P, h, H);
+    if (c < nchunks - 1 && valid) ws_hin[at(c + 1)] = hn;
+    h = __shfl(hn, S - 1, S);  // state after the round's last map
   }
 }
 
@@ -797,10 +823,12 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
                        a.nchunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t total = (int64_t)a.batch * a.dim * kDState;
-    hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+    int seg_log2 = 0;  // segment of lanes per (b, d, n): next power of two >= the map count
+    while ((1 << seg_log2) < a.nchunks - 1 && seg_log2 < 6) ++seg_log2;
+    const int64_t threads = (int64_t)a.batch * a.dim * kDState << seg_log2;
+    hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        stream, a.A, a.h0, a.ws_hloc, a.ws_sdelta, a.ws_hin, a.batch, a.dim,
-                       a.nchunks);
+                       a.nchunks, seg_log2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -131,6 +131,23 @@ def test_chunk_and_resume_invariance():
     parity.check_state(parity.to_f64(hb), parity.to_f64(h), "resumed h")
 
 
+@pytest.mark.parametrize("K", [2, 17, 65, 100])
+def test_many_chunks_carry_rounds(K):
+    """The carry composes the chunk maps with an in-wave prefix scan over
+    segments of up to 64 lanes; more than 65 chunks take several rounds.
+    fp32 I/O against the oracle, with h0."""
+    w = W.MAMBA_130M
+    inp = _inputs(w, batch=2, seqlen=1600, dim=96)
+    inp = {k: (v.float() if k in ("x", "delta", "z", "B", "C") else v) for k, v in inp.items()}
+    g = torch.Generator(device=DEV).manual_seed(11)
+    inp["h0"] = torch.randn((2, 96, 16), generator=g, device=DEV)
+    y, h = _run(inp, 4, K)
+    torch.cuda.synchronize()
+    y_ref, h_ref = parity.oracle_scan(inp)
+    parity.check_y(parity.to_f64(y), y_ref, torch.float32)
+    parity.check_state(parity.to_f64(h), h_ref)
+
+
 def test_deterministic():
     inp = _inputs(W.MAMBA_130M, batch=2, seqlen=512, dim=256)
     y1, h1 = _run(inp, 8, 3)

@@ -42,6 +42,12 @@ def _declare(lib):
     lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [c_int]
     lib.oracle_decode_step.restype = c_int
     lib.oracle_decode_step.argtypes = [i64, i64, i64] + [dp] * 9
+    lib.oracle_conv1d.restype = c_int
+    lib.oracle_conv1d.argtypes = [i64, i64, i64, i64, dp, dp, dp, c_int, dp]
+    lib.oracle_delta_softplus.restype = c_int
+    lib.oracle_delta_softplus.argtypes = [i64, i64, i64, dp, dp, dp]
+    lib.oracle_softplus.restype = ctypes.c_double
+    lib.oracle_softplus.argtypes = [ctypes.c_double]
     lib.oracle_zoh.restype = None
     lib.oracle_zoh.argtypes = [ctypes.c_double, ctypes.c_double,
                                ctypes.POINTER(ctypes.c_double),
@@ -122,3 +128,48 @@ def decode_step(h, x, delta, A, B, C, D=None, z=None, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_decode_step rejected its arguments (code {rc})")
     return y
+
+
+def softplus(v: float) -> float:
+    """softplus(v) = log(1 + exp(v)) from the compiled oracle."""
+    return load_library().oracle_softplus(float(v))
+
+
+def conv1d(x_raw, w, bias=None, silu: bool = False, lib=None):
+    """Causal depthwise convolution over time.  x_raw [b, L, d]; w [d, d_conv]
+    (tap d_conv-1 multiplies the current step); bias [d].  Returns [b, L, d]."""
+    lib = lib or load_library()
+    x_raw, w, bias = _f64(x_raw), _f64(w), _f64(bias)
+    batch, seqlen, dim = x_raw.shape
+    d_conv = w.shape[1]
+    assert w.shape == (dim, d_conv) and (bias is None or bias.shape == (dim,))
+    out = np.zeros_like(x_raw)
+    rc = lib.oracle_conv1d(batch, seqlen, dim, d_conv, _ptr(x_raw), _ptr(w), _ptr(bias),
+                           int(bool(silu)), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_conv1d rejected its arguments (code {rc})")
+    return out
+
+
+def delta_softplus(delta_raw, bias=None, lib=None):
+    """delta = softplus(delta_raw + bias[d]).  delta_raw [b, L, d]."""
+    lib = lib or load_library()
+    delta_raw, bias = _f64(delta_raw), _f64(bias)
+    batch, seqlen, dim = delta_raw.shape
+    assert bias is None or bias.shape == (dim,)
+    out = np.zeros_like(delta_raw)
+    rc = lib.oracle_delta_softplus(batch, seqlen, dim, _ptr(delta_raw), _ptr(bias), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_delta_softplus rejected its arguments (code {rc})")
+    return out
+
+
+def scan_fused(x_raw, conv_w, conv_b, conv_silu, delta_raw, delta_bias, A, B, C, D=None, z=None,
+               h0=None, nthreads: int = 0, lib=None):
+    """The prologue (conv1d, softplus) followed by the scan, all in fp64.
+    Returns (y, h_last, x, delta) with x and delta the prologue outputs."""
+    lib = lib or load_library()
+    x = conv1d(x_raw, conv_w, conv_b, conv_silu, lib=lib)
+    delta = delta_softplus(delta_raw, delta_bias, lib=lib)
+    y, h_last = scan(x, delta, A, B, C, D, z, h0, nthreads=nthreads, lib=lib)
+    return y, h_last, x, delta

@@ -152,3 +152,60 @@ int oracle_decode_step(int64_t batch, int64_t dim, int64_t dstate, double *h,
                          y + b * dim);
     return ORACLE_OK;
 }
+
+/*
+ * Prologue of the selective scan inside a Mamba block (the step right before
+ * the scan), evaluated on its own so that a fused GPU kernel can be checked
+ * against (prologue -> scan) in fp64.
+ *
+ *  - causal depthwise convolution over time (paperlens tutorial, section
+ *    "現場ではこう使う": a short 1-D convolution of width d_conv in front of
+ *    the SSM; agenticai-flow guide, implementation example: d_conv = 4,
+ *    installed as the causal-conv1d package).  Each channel d has its own
+ *    d_conv taps; tap k multiplies the input d_conv-1-k steps back, so
+ *    w[d, d_conv-1] multiplies the current step.  Steps before the start of
+ *    the sequence are zero.  Optional bias, optional SiLU of the result (the
+ *    pages do not say whether an activation follows the convolution).
+ *      xc[b,t,d] = act( sum_k w[d,k] * x_raw[b, t-(d_conv-1)+k, d] + bias[d] )
+ *
+ *  - step size (paperlens tutorial, section "Mamba: 状態を「選択的」にする":
+ *    delta is a softplus of a per-token projection plus a bias):
+ *      delta[b,t,d] = softplus(delta_raw[b,t,d] + delta_bias[d]),
+ *      softplus(v) = log(1 + exp(v)), evaluated as max(v,0) + log1p(exp(-|v|)).
+ */
+static double softplus(double v) {
+    return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v)));
+}
+
+/* Exposed so that tests can check the formula on its own. */
+double oracle_softplus(double v) { return softplus(v); }
+
+int oracle_conv1d(int64_t batch, int64_t seqlen, int64_t dim, int64_t d_conv,
+                  const double *x_raw, const double *w, const double *bias, int silu_act,
+                  double *out) {
+    if (batch < 0 || seqlen < 0 || dim < 0 || d_conv <= 0) return ORACLE_EINVAL;
+    if (batch == 0 || seqlen == 0 || dim == 0) return ORACLE_OK;
+    if (!x_raw || !w || !out) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t t = 0; t < seqlen; ++t)
+            for (int64_t d = 0; d < dim; ++d) {
+                double acc = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < d_conv; ++k) {
+                    int64_t ts = t - (d_conv - 1) + k;
+                    if (ts >= 0) acc += w[d * d_conv + k] * x_raw[(b * seqlen + ts) * dim + d];
+                }
+                out[(b * seqlen + t) * dim + d] = silu_act ? silu(acc) : acc;
+            }
+    return ORACLE_OK;
+}
+
+int oracle_delta_softplus(int64_t batch, int64_t seqlen, int64_t dim, const double *delta_raw,
+                          const double *bias, double *out) {
+    if (batch < 0 || seqlen < 0 || dim < 0) return ORACLE_EINVAL;
+    if (batch == 0 || seqlen == 0 || dim == 0) return ORACLE_OK;
+    if (!delta_raw || !out) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < batch * seqlen; ++i)
+        for (int64_t d = 0; d < dim; ++d)
+            out[i * dim + d] = softplus(delta_raw[i * dim + d] + (bias ? bias[d] : 0.0));
+    return ORACLE_OK;
+}

@@ -15,9 +15,18 @@ distributions of the benchmark configurations:
 * ``B, C[b,t,n]  ~ N(0, 1)``                          (rounded to the I/O dtype)
 * ``h0 = 0`` for the scan; the decode state is ``h[b,d,n] ~ N(0, 1)`` (fp32).
 
+Inputs of the fused scan (prologue + scan; ``make_fused_inputs``): the raw
+block inputs before the causal depthwise convolution and the softplus:
+
+* ``x_raw[b,t,d] ~ N(0, 1)`` (I/O dtype), taps ``conv_w[d,k] ~ U(-0.5, 0.5)``
+  and ``conv_b[d] ~ U(-0.1, 0.1)`` (fp32, width 4);
+* ``delta_raw[b,t,d] = 0.5 * N(0, 1)`` (I/O dtype) and ``delta_bias[d] = -3``
+  (or the per-channel ``U(-6, -1)`` bias), so that
+  ``softplus(delta_raw + delta_bias)`` has the distribution of ``delta`` above.
+
 Every tensor has its own seed ``1_000_000 * workload.seed_id + 1_000 * layer + k``
 with ``k`` = 0 A, 1 Dskip, 2 x, 3 delta noise, 4 z, 5 B, 6 C, 7 delta bias,
-8 initial decode state.  Values are drawn in fp32 and rounded to bf16 by
+8 initial decode state, 9 x_raw, 10 conv taps, 11 conv bias, 12 delta_raw.  Values are drawn in fp32 and rounded to bf16 by
 round-to-nearest-even (torch's ``.to(torch.bfloat16)``).  The small fp32
 workload is drawn on the CPU so that CPU-only tests see the same bytes as the
 GPU tests; the large ones are drawn with a generator on the target device.
@@ -29,7 +38,8 @@ import dataclasses
 import torch
 import torch.nn.functional as F
 
-K_A, K_DSKIP, K_X, K_DELTA, K_Z, K_B, K_C, K_BIAS, K_HINIT = range(9)
+(K_A, K_DSKIP, K_X, K_DELTA, K_Z, K_B, K_C, K_BIAS, K_HINIT, K_XRAW, K_CONVW, K_CONVB,
+ K_DRAW) = range(13)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -142,3 +152,26 @@ def make_inputs(w: Workload, device="cpu", layer: int = 0,
     else:
         out["h0"] = None
     return out
+
+
+def make_fused_inputs(w: Workload, device="cpu", layer: int = 0, batch: int | None = None,
+                      seqlen: int | None = None, dim: int | None = None,
+                      d_conv: int = 4) -> dict:
+    """Inputs of the fused scan: x_raw, conv_w [d, d_conv], conv_b [d],
+    delta_raw, delta_bias [d], plus A, B, C, D, z of ``make_inputs`` (same
+    seeds) and h0 None."""
+    assert w.kind == "scan"
+    base = make_inputs(w, device, layer, batch, seqlen, dim)
+    b, L, d = base["x"].shape
+    io = w.io_dtype
+    x_raw = _draw("normal", (b, L, d), w, layer, K_XRAW, device).to(io)
+    conv_w = (_draw("uniform", (d, d_conv), w, layer, K_CONVW, device) - 0.5).contiguous()
+    conv_b = 0.2 * (_draw("uniform", (d,), w, layer, K_CONVB, device) - 0.5)
+    delta_raw = (0.5 * _draw("normal", (b, L, d), w, layer, K_DRAW, device)).to(io)
+    if w.per_channel_bias:
+        delta_bias = -6.0 + 5.0 * _draw("uniform", (d,), w, layer, K_BIAS, device)
+    else:
+        delta_bias = torch.full((d,), -3.0, dtype=torch.float32, device=device)
+    return dict(x_raw=x_raw, conv_w=conv_w, conv_b=conv_b, delta_raw=delta_raw,
+                delta_bias=delta_bias, A=base["A"], B=base["B"], C=base["C"], D=base["D"],
+                z=base["z"], h0=None)

@@ -26,6 +26,11 @@ What pins what (pages cited by title and section):
   (paperlens tutorial, section on the parallel scan).
 * L decode steps equal one scan (paperlens tutorial, S4 section: recurrent and
   convolutional faces give the same outputs).
+* Prologue of the fused scan (paperlens tutorial, sections "現場ではこう使う"
+  and "Mamba: 状態を「選択的」にする"): the causal depthwise convolution equals
+  numpy's convolve of each channel with its reversed taps, and cannot see the
+  future; softplus satisfies softplus(0) = ln 2 and softplus(v) - softplus(-v) = v
+  and has the right asymptotes; the bias is added before the softplus.
 """
 from __future__ import annotations
 
@@ -298,6 +303,76 @@ def pin_empty_sequence(lib):
     q = dict(p, h0=None)
     _, h = oracle.scan(lib=lib, **q)
     assert np.all(h == 0.0)
+
+
+# --------------------------------------------------------------------------
+# Prologue: causal depthwise conv1d and softplus of delta
+# --------------------------------------------------------------------------
+
+def pin_conv1d_matches_numpy_convolve(lib):
+    rng = _rng(31)
+    b, L, d = 2, 37, 5
+    for K in (1, 2, 4):
+        x = rng.standard_normal((b, L, d))
+        w = rng.uniform(-1, 1, (d, K))
+        bias = rng.standard_normal(d)
+        out = oracle.conv1d(x, w, bias, silu=False, lib=lib)
+        ref = np.empty_like(x)
+        for bb in range(b):
+            for dd in range(d):
+                ref[bb, :, dd] = np.convolve(x[bb, :, dd], w[dd, ::-1])[:L] + bias[dd]
+        assert _rel(out, ref) < 1e-14, K
+        out0 = oracle.conv1d(x, w, None, silu=False, lib=lib)
+        assert _rel(out0 + bias, ref) < 1e-14
+
+
+def pin_conv1d_is_causal(lib):
+    rng = _rng(32)
+    x = rng.standard_normal((1, 20, 3))
+    w = rng.uniform(0.5, 1.0, (3, 4))  # taps bounded away from zero
+    y0 = oracle.conv1d(x, w, None, silu=True, lib=lib)
+    x2 = x.copy()
+    x2[0, 9, :] += 1.0
+    y1 = oracle.conv1d(x2, w, None, silu=True, lib=lib)
+    assert np.array_equal(y0[0, :9], y1[0, :9])
+    assert np.all(y0[0, 9:13] != y1[0, 9:13])
+    assert np.array_equal(y0[0, 13:], y1[0, 13:])
+
+
+def pin_conv1d_silu_is_applied_after_the_bias(lib):
+    rng = _rng(33)
+    x = rng.standard_normal((1, 16, 4))
+    w = rng.uniform(-1, 1, (4, 3))
+    bias = rng.standard_normal(4)
+    lin = oracle.conv1d(x, w, bias, silu=False, lib=lib)
+    act = oracle.conv1d(x, w, bias, silu=True, lib=lib)
+    # SiLU(v) - SiLU(-v) = v, whatever the form of the sigmoid
+    neg = oracle.conv1d(-x, w, -bias, silu=True, lib=lib)
+    assert _rel(act - neg, lin) < 1e-13
+    assert _rel(act, _silu(lin)) < 1e-13
+
+
+def pin_softplus_values(lib):
+    import math
+    sp = lib.oracle_softplus
+    assert abs(sp(0.0) - math.log(2.0)) < 1e-16
+    rng = _rng(34)
+    for v in rng.uniform(-30, 30, 200):
+        a, b = sp(v), sp(-v)
+        assert a > 0.0 and b > 0.0
+        assert abs((a - b) - v) <= 1e-14 * max(1.0, abs(v))
+    assert abs(sp(60.0) - 60.0) < 1e-13  # softplus(v) = v + log1p(exp(-v))
+    assert abs(sp(-40.0) / math.exp(-40.0) - 1.0) < 1e-15
+
+
+def pin_delta_softplus_adds_the_bias_first(lib):
+    rng = _rng(35)
+    raw = 0.5 * rng.standard_normal((2, 9, 6))
+    bias = rng.uniform(-6, -1, 6)
+    dp = oracle.delta_softplus(raw, bias, lib=lib)
+    dn = oracle.delta_softplus(-raw, -bias, lib=lib)
+    assert _rel(dp - dn, raw + bias) < 1e-13
+    assert np.all(dp > 0)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

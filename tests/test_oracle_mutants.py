@@ -31,6 +31,14 @@ MUTANTS = {
         "        /* state update first: h_t = Abar_t h_{t-1} + Bbar_t x_t */",
         "        double s0 = 0.0;\n"
         "        for (int64_t n = 0; n < dstate; ++n) s0 += C[bc + n] * h[n];"),
+    "conv_taps_reversed": ("acc += w[d * d_conv + k] * x_raw",
+                           "acc += w[d * d_conv + (d_conv - 1 - k)] * x_raw"),
+    "conv_one_step_late": ("int64_t ts = t - (d_conv - 1) + k;",
+                           "int64_t ts = t - d_conv + k;"),
+    "conv_bias_dropped": ("double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
+    "softplus_sign": ("log1p(exp(-fabs(v)))", "log1p(exp(fabs(v)))"),
+    "softplus_bias_dropped": ("softplus(delta_raw[i * dim + d] + (bias ? bias[d] : 0.0))",
+                              "softplus(delta_raw[i * dim + d])"),
     "half_state_read": ("for (int64_t n = 0; n < dstate; ++n) s += C[bc + n] * h[n];",
                         "for (int64_t n = 0; n < dstate / 2; ++n) s += C[bc + n] * h[n];"),
 }

@@ -159,6 +159,41 @@ def bench_scan(steps: int, warmup: int):
                 main_ms=sum(ev_main) / steps, carry_ms=sum(ev_carry) / steps, inp=sets[0])
 
 
+def bench_fused(steps: int, warmup: int):
+    """The scan with its prologue fused (causal depthwise conv1d of width 4 +
+    SiLU, softplus(delta_raw + bias)) at the same shape, automatic plan."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.MAMBA_2P8B
+    dev = "cuda:0"
+    sets = [W.make_fused_inputs(w, device=dev, layer=i) for i in range(2)]
+    outs = [torch.empty_like(s["x_raw"]) for s in sets]
+    nws = ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        f = sets[i % 2]
+        ssm.scan_fwd_fused(f["x_raw"], f["conv_w"], f["conv_b"], f["delta_raw"],
+                           f["delta_bias"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
+                           conv_silu=True, out=outs[i % 2], workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": w.name + "_fused_conv4_silu_softplus", "ms_per_step": ms,
+            "value": w.elements / (ms * 1e-3), "unit": "elements/s",
+            "hbm_algorithmic_GBps": w.algorithmic_bytes() / (ms * 1e-3) / 1e9}
+
+
 def bench_decode(sweeps: int):
     """64 layers stepped back to back, each with its own state, inputs and
     parameters (5.4 GB of state, far beyond the 256 MB cache).  HIP events
@@ -214,6 +249,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the scan with the fused conv1d/softplus prologue")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -282,6 +319,8 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = bench_decode(args.decode_sweeps)
+    if not args.no_fused:
+        line["fused_prologue"] = bench_fused(max(10, args.steps // 4), max(10, args.warmup // 4))
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(r["inp"], w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

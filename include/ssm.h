@@ -146,6 +146,40 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
                        int waves_per_group, int nchunks, int phase, void *stream);
 
 /*
+ * Selective scan with its prologue fused in: the two steps that come right
+ * before the scan in a Mamba block are computed on the way into the kernel
+ * instead of in a separate pass over HBM.
+ *   x[b,t,d]     = act( sum_k conv_w[d,k] * x_raw[b, t-(d_conv-1)+k, d] + conv_b[d] )
+ *                  -- causal depthwise convolution over time, width d_conv
+ *                  (paperlens tutorial, section "現場ではこう使う": the short
+ *                  1-D convolution in front of the SSM; agenticai-flow guide,
+ *                  implementation example: d_conv = 4).  Steps before the
+ *                  start of the sequence count as zero; act is SiLU when
+ *                  conv_silu == 1 and the identity when 0 (the pages do not
+ *                  say which follows the convolution).
+ *   delta[b,t,d] = softplus(delta_raw[b,t,d] + delta_bias[d])
+ *                  -- paperlens tutorial, section "Mamba: 状態を「選択的」にする".
+ * followed by the scan of ssm_scan_fwd on (x, delta).
+ *   x_raw, delta_raw : [batch, seqlen, dim] io_dtype.
+ *   conv_w           : [dim, d_conv] fp32; conv_w[d, d_conv-1] multiplies the
+ *                      current step.  1 <= d_conv <= 4 (larger:
+ *                      SSM_ERR_UNSUPPORTED).
+ *   conv_b, delta_bias : [dim] fp32, NULL => 0.
+ *   Every other argument, the plan (waves_per_group 2, 4 or 8; 16 returns
+ *   SSM_ERR_UNSUPPORTED) and the workspace are those of ssm_scan_fwd_planned.
+ * D multiplies the convolution output x (the scan's input).  Returns an SSM_*
+ * status.
+ */
+int ssm_scan_fwd_fused(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int io_dtype, const void *x_raw, const float *conv_w,
+                       const float *conv_b, int d_conv, int conv_silu,
+                       const void *delta_raw, const float *delta_bias, const float *A,
+                       const void *B, const void *C, const float *Dskip, const void *z,
+                       const float *h0, void *y, float *h_last, void *workspace,
+                       size_t workspace_bytes, int waves_per_group, int nchunks,
+                       void *stream);
+
+/*
  * One recurrent decode step for one new token per sequence (paperlens
  * tutorial, S4 section and practice notes: constant time and memory per
  * token; ihouse article, decode arithmetic intensity).

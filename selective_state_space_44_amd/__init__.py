@@ -15,7 +15,7 @@ import threading
 
 import torch
 
-__all__ = ["scan_fwd", "decode_step", "scan_plan", "scan_workspace_bytes", "load_library",
+__all__ = ["scan_fwd", "scan_fwd_fused", "decode_step", "scan_plan", "scan_workspace_bytes", "load_library",
            "LIB_PATH", "SsmError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm.so")
@@ -41,6 +41,8 @@ SIGNATURES = {
                              + [_vp, _sz, _int, _int, _vp]),
     "ssm_scan_fwd_phase": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
                            + [_vp, _sz, _int, _int, _int, _vp]),
+    "ssm_scan_fwd_fused": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int, _vp,
+                                  _vp] + [_vp] * 8 + [_vp, _sz, _int, _int, _vp]),
     "ssm_decode_step": (_int, [_i64, _i64, _i64, _int] + [_vp] * 9 + [_vp]),
 }
 
@@ -176,6 +178,63 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
                                 int(waves_per_group), int(nchunks), int(phase),
                                 _stream(device))
     _check(st, "ssm_scan_fwd")
+    return (y, h_last) if return_last_state else y
+
+
+def scan_fwd_fused(x_raw, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None, z=None,
+                   h0=None, *, conv_silu: bool, return_last_state=False,
+                   waves_per_group: int = 0, nchunks: int = 0, out=None, workspace=None):
+    """Selective scan with its prologue fused: x = act(causal depthwise
+    conv1d(x_raw) + conv_b), delta = softplus(delta_raw + delta_bias), then the
+    scan of ``scan_fwd``.  x_raw, delta_raw: [batch, L, dim] (float32 or
+    bfloat16); conv_w [dim, d_conv] float32 (d_conv <= 4, the last tap
+    multiplies the current step); conv_b, delta_bias [dim] float32 or None;
+    ``conv_silu`` selects SiLU after the convolution (keyword, no default)."""
+    if not isinstance(x_raw, torch.Tensor) or x_raw.dim() != 3:
+        raise ValueError("x_raw must be a [batch, seqlen, dim] tensor")
+    device = x_raw.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    batch, seqlen, dim = x_raw.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a [dim, dstate] tensor")
+    if not isinstance(conv_w, torch.Tensor) or conv_w.dim() != 2:
+        raise ValueError("conv_w must be a [dim, d_conv] tensor")
+    dstate = A.shape[1]
+    d_conv = conv_w.shape[1]
+    io = x_raw.dtype
+    code = _io_code(io)
+    _require(x_raw, "x_raw", (batch, seqlen, dim), io, device)
+    _require(delta_raw, "delta_raw", (batch, seqlen, dim), io, device)
+    _require(conv_w, "conv_w", (dim, d_conv), torch.float32, device)
+    _require(conv_b, "conv_b", (dim,), torch.float32, device)
+    _require(delta_bias, "delta_bias", (dim,), torch.float32, device)
+    _require(A, "A", (dim, dstate), torch.float32, device)
+    _require(B, "B", (batch, seqlen, dstate), io, device)
+    _require(C, "C", (batch, seqlen, dstate), io, device)
+    _require(D, "D", (dim,), torch.float32, device)
+    _require(z, "z", (batch, seqlen, dim), io, device)
+    _require(h0, "h0", (batch, dim, dstate), torch.float32, device)
+    if delta_raw is None or B is None or C is None:
+        raise ValueError("delta_raw, B and C are required")
+    y = out if out is not None else torch.empty_like(x_raw)
+    _require(y, "out", (batch, seqlen, dim), io, device)
+    h_last = (torch.empty((batch, dim, dstate), dtype=torch.float32, device=device)
+              if return_last_state else None)
+    lib = load_library()
+    nbytes = lib.ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, code, nchunks)
+    if nbytes < 0:
+        raise ValueError("invalid sizes")
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_scan_fwd_fused(batch, seqlen, dim, dstate, code, _ptr(x_raw), _ptr(conv_w),
+                                _ptr(conv_b), int(d_conv), int(bool(conv_silu)),
+                                _ptr(delta_raw), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
+                                _ptr(workspace), ws_bytes, int(waves_per_group), int(nchunks),
+                                _stream(device))
+    _check(st, "ssm_scan_fwd_fused")
     return (y, h_last) if return_last_state else y
 
 

@@ -120,12 +120,17 @@ int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int
   return (int64_t)workspace_for(batch, dim, nchunks);
 }
 
-int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                       int io_dtype, const void* x, const void* delta, const float* A,
-                       const void* B, const void* C, const float* Dskip, const void* z,
-                       const float* h0, void* y, float* h_last, void* workspace,
-                       size_t workspace_bytes, int waves_per_group, int nchunks, int phase,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the plain and the fused scan.  With
+// pro.d_conv > 0, x and delta are x_raw and delta_raw.
+int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+               const void* x, const void* delta, const float* A, const void* B, const void* C,
+               const float* Dskip, const void* z, const float* h0, void* y, float* h_last,
+               void* workspace, size_t workspace_bytes, int waves_per_group, int nchunks,
+               int phase, void* stream, const ssm::Prologue& pro) {
   if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype))
     return SSM_ERR_INVALID_ARG;
   if (phase < 1 || phase > 3) return SSM_ERR_INVALID_ARG;
@@ -142,13 +147,14 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   }
   if (!x || !delta || !B || !C || !y) return SSM_ERR_INVALID_ARG;
   // outputs must not alias any input
-  const void* ins[] = {x, delta, A, B, C, Dskip, z, h0};
+  const void* ins[] = {x, delta, A, B, C, Dskip, z, h0, pro.conv_w, pro.conv_b, pro.delta_bias};
   for (const void* in : ins) {
     if (!in) continue;
     if (in == y || in == (const void*)h_last) return SSM_ERR_INVALID_ARG;
   }
   if ((const void*)h_last == y) return SSM_ERR_INVALID_ARG;
-  if (!all_aligned(x, delta, A, B, C, Dskip, z, h0, y, h_last, workspace))
+  if (!all_aligned(x, delta, A, B, C, Dskip, z, h0, y, h_last, workspace) ||
+      !all_aligned(pro.conv_w, pro.conv_b, pro.delta_bias))
     return SSM_ERR_INVALID_ARG;
   if (batch > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
 
@@ -157,6 +163,7 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   if (waves_per_group > 0) G = waves_per_group;
   if (nchunks > 0) K = nchunks;
   if (G != 2 && G != 4 && G != 8 && G != 16) return SSM_ERR_UNSUPPORTED;
+  if (pro.d_conv > 0 && G == 16) return SSM_ERR_UNSUPPORTED;  // fused loader: G <= 8
   const int64_t chunk_len = chunk_length(seqlen, dim, io_dtype, K);
   K = effective_chunks(seqlen, dim, io_dtype, K);  // == ceil(seqlen / chunk_len)
 
@@ -188,7 +195,47 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   a.nchunks = K;
   a.dim = (int)dim;
   a.batch = (int)batch;
+  a.pro = pro;
   return hip_status(ssm::launch_scan(a, io_dtype == SSM_DTYPE_BF16, G, phase, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int io_dtype, const void* x, const void* delta, const float* A,
+                       const void* B, const void* C, const float* Dskip, const void* z,
+                       const float* h0, void* y, float* h_last, void* workspace,
+                       size_t workspace_bytes, int waves_per_group, int nchunks, int phase,
+                       void* stream) {
+  const ssm::Prologue none{};
+  return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
+                    h_last, workspace, workspace_bytes, waves_per_group, nchunks, phase, stream,
+                    none);
+}
+
+int ssm_scan_fwd_fused(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int io_dtype, const void* x_raw, const float* conv_w,
+                       const float* conv_b, int d_conv, int conv_silu, const void* delta_raw,
+                       const float* delta_bias, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* h0, void* y,
+                       float* h_last, void* workspace, size_t workspace_bytes,
+                       int waves_per_group, int nchunks, void* stream) {
+  if (d_conv < 1 || (conv_silu != 0 && conv_silu != 1)) return SSM_ERR_INVALID_ARG;
+  if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype))
+    return SSM_ERR_INVALID_ARG;
+  if (batch > 0 && dim > 0 && seqlen > 0 && !conv_w) return SSM_ERR_INVALID_ARG;
+  if (d_conv > 4) return SSM_ERR_UNSUPPORTED;
+  ssm::Prologue pro{};
+  pro.conv_w = conv_w;
+  pro.conv_b = conv_b;
+  pro.delta_bias = delta_bias;
+  pro.d_conv = d_conv;
+  pro.conv_silu = conv_silu;
+  return scan_entry(batch, seqlen, dim, dstate, io_dtype, x_raw, delta_raw, A, B, C, Dskip, z,
+                    h0, y, h_last, workspace, workspace_bytes, waves_per_group, nchunks, 3,
+                    stream, pro);
 }
 
 int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,

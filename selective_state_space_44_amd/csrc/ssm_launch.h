@@ -8,6 +8,17 @@
 
 namespace ssm {
 
+// Prologue of the fused scan: x = act(causal depthwise conv1d(x_raw) + conv_b)
+// and delta = softplus(delta_raw + delta_bias).  d_conv == 0: no prologue
+// (x and delta are used as given).
+struct Prologue {
+  const float* conv_w;      // [dim, d_conv], tap d_conv-1 multiplies the current step
+  const float* conv_b;      // [dim], nullable
+  const float* delta_bias;  // [dim], nullable
+  int d_conv;               // 0 (no prologue) or 1..4
+  int conv_silu;            // SiLU after the convolution
+};
+
 // Everything a scan launch needs.  Sizes are validated by the ABI layer.
 struct ScanArgs {
   const void* x;
@@ -29,6 +40,7 @@ struct ScanArgs {
   int dim;
   int batch;
   int nchunks;
+  Prologue pro;        // x and delta above are x_raw and delta_raw when pro.d_conv > 0
 };
 
 struct DecodeArgs {

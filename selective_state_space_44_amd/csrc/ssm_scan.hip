@@ -65,6 +65,8 @@ static_assert(kTileBC % kWave == 0, "B/C tile must split evenly over a wave");
 // puts 5 blocks of 4 waves on every CU), the carry pass 4.
 constexpr int kMainWavesPerSimd = 5;
 constexpr int kCarryWavesPerSimd = 4;
+// the fused prologue's loader registers do not fit in 5 waves' budget
+constexpr int kFusedWavesPerSimd = 4;
 
 // ZOH coefficients of one (step, state): h' = a*h + b with a = Abar and
 // b = Bbar*x.  With q = B*x/A, Bbar*x = (Abar - 1)*q = fma(Abar, q, -q).
@@ -287,16 +289,54 @@ struct TileRaw {
   uint32_t bc[Share<G, NBC>::kBC];
 };
 
+// Per-lane constants of the prologue (fused scan only).
+struct LanePrologue {
+  float w[4];  // taps for steps t-3 .. t (zero-padded when d_conv < 4)
+  float cb, db;
+  bool silu;
+};
+
+__device__ __forceinline__ LanePrologue lane_prologue(const Prologue& pro, int d) {
+  LanePrologue lp;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int u = k - (4 - pro.d_conv);  // user tap index
+    lp.w[k] = u >= 0 ? pro.conv_w[(size_t)d * pro.d_conv + u] : 0.0f;
+  }
+  lp.cb = pro.conv_b ? pro.conv_b[d] : 0.0f;
+  lp.db = pro.delta_bias ? pro.delta_bias[d] : 0.0f;
+  lp.silu = pro.conv_silu != 0;
+  return lp;
+}
+
+// softplus(v) = log(1 + exp(v)) in fp32.  log1p(e) with e = exp(v) uses the
+// series e - e^2/2 + e^3/3 - e^4/4 + e^5/5 when e < 2^-7 (truncation below
+// 2^-29 relative) and log(1 + e) through the hardware log2 otherwise; above
+// v = 20 the result is v to fp32 precision.
+__device__ __forceinline__ float softplus_f32(float v) {
+  const float e = fast_exp2(v * kLog2e);
+  float r;
+  if (e < 0.0078125f) {
+    r = e * __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, 0.2f, -0.25f),
+                                                               0.33333334f), -0.5f), 1.0f);
+  } else {
+    r = __builtin_amdgcn_logf(1.0f + e) * 0.6931471805599453f;
+  }
+  return v > 20.0f ? v : r;
+}
+
 template <typename IO, int G, bool WITH_C>
 struct Loader {
   static constexpr int NBC = WITH_C ? 2 : 1;
   using S = Share<G, NBC>;
+  using RawTile = TileRaw<G, NBC>;
   __amdgpu_buffer_rsrc_t rx, rd, rb, rc;
   uint32_t voff_row, row_bytes;
   int g;
 
   __device__ __forceinline__ void init(const IO* x, const IO* delta, const IO* B, const IO* C,
-                                       int64_t seqlen, int dim, const Chunk& k) {
+                                       int64_t seqlen, int dim, const Chunk& k,
+                                       const LanePrologue&) {
     rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
     rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
     rb = bc_rsrc(B, k, seqlen);
@@ -345,6 +385,119 @@ struct Loader {
       }
     }
   }
+
+  // x and delta of one step (ragged end of a chunk), straight from memory.
+  __device__ __forceinline__ void step(int s, float& xs, float& ds) const {
+    const uint32_t so = (uint32_t)s * row_bytes;
+    xs = buf<IO>::load(rx, voff_row, so);
+    ds = buf<IO>::load(rd, voff_row, so);
+  }
+};
+
+// Loader of the fused scan: the tile's x and delta are computed from x_raw
+// and delta_raw on the way into LDS.  Wave g produces the kT/G consecutive
+// steps [g*kT/G, (g+1)*kT/G) of the tile for its 64 channels: it fetches
+// those steps of delta_raw and of x_raw with the 3 steps before them (the
+// convolution's reach; zeros before the start of the sequence), applies the
+// causal convolution, its bias and optional SiLU, and softplus(delta_raw +
+// bias).  B and C pieces are shared out as in Loader.
+template <int G, int NBC>
+struct FusedRaw {
+  static constexpr int kSteps = kT / G;
+  uint32_t xr[kSteps + 3];
+  uint32_t dr[kSteps];
+  uint32_t bc[Share<G, NBC>::kBC];
+};
+
+template <typename IO, int G, bool WITH_C>
+struct FusedLoader {
+  static constexpr int NBC = WITH_C ? 2 : 1;
+  static constexpr int kSteps = kT / G;
+  static_assert(G <= kT, "the fused loader gives every wave at least one step");
+  using S = Share<G, NBC>;
+  using RawTile = FusedRaw<G, NBC>;
+  __amdgpu_buffer_rsrc_t rx, rd, rb, rc;
+  uint32_t voff_row, row_bytes;
+  int g, xshift;      // xshift: rows of x_raw kept before the chunk start (0..3)
+  int64_t t_begin;
+  LanePrologue lp;
+
+  __device__ __forceinline__ void init(const IO* x_raw, const IO* delta_raw, const IO* B,
+                                       const IO* C, int64_t seqlen, int dim, const Chunk& k,
+                                       const LanePrologue& lpin) {
+    const int64_t xb = k.t_begin >= 3 ? k.t_begin - 3 : 0;
+    xshift = (int)(k.t_begin - xb);
+    rx = rows_rsrc(x_raw, k.b, seqlen, dim, xb, k.t_end);
+    rd = rows_rsrc(delta_raw, k.b, seqlen, dim, k.t_begin, k.t_end);
+    rb = bc_rsrc(B, k, seqlen);
+    rc = bc_rsrc(C, k, seqlen);
+    voff_row = (uint32_t)k.d * sizeof(IO);
+    row_bytes = (uint32_t)dim * sizeof(IO);
+    g = k.g;
+    t_begin = k.t_begin;
+    lp = lpin;
+  }
+
+  // x_raw at step `rel` of the chunk (rel >= -3); zero before the sequence.
+  __device__ __forceinline__ uint32_t load_x(int rel) const {
+    const bool ok = t_begin + rel >= 0;
+    return Raw<IO>::load(rx, ok ? voff_row : 0x80000000u,
+                         ok ? (uint32_t)(rel + xshift) * row_bytes : 0u);
+  }
+
+  __device__ __forceinline__ float conv(const float (&xs)[4]) const {
+    float acc = lp.cb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(lp.w[k], xs[k], acc);
+    return lp.silu ? silu(acc) : acc;
+  }
+
+  __device__ __forceinline__ void issue(RawTile& r, int s0, int lane) const {
+    const int t0 = s0 + g * kSteps;
+#pragma unroll
+    for (int j = 0; j < kSteps + 3; ++j) r.xr[j] = load_x(t0 - 3 + j);
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j)
+      r.dr[j] = Raw<IO>::load(rd, voff_row, (uint32_t)(t0 + j) * row_bytes);
+#pragma unroll
+    for (int j = 0; j < S::kBC; ++j) {
+      const int piece = min(g + G * j, S::kPieces - 1);
+      const bool is_c = piece * kWave >= kTileBC;
+      const int v = piece * kWave - (is_c ? kTileBC : 0) + lane;
+      r.bc[j] = Raw<IO>::load(is_c ? rc : rb, (uint32_t)(v * sizeof(IO)),
+                              (uint32_t)s0 * kDState * sizeof(IO));
+    }
+  }
+
+  __device__ __forceinline__ void put(const RawTile& r, Stage<WITH_C>& st, int lane) const {
+    float* xrow = st.x + lane * kXS + g * kSteps;
+    float* drow = st.d + lane * kXS + g * kSteps;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const float xs[4] = {Raw<IO>::f(r.xr[j]), Raw<IO>::f(r.xr[j + 1]), Raw<IO>::f(r.xr[j + 2]),
+                           Raw<IO>::f(r.xr[j + 3])};
+      xrow[j] = conv(xs);
+      drow[j] = softplus_f32(Raw<IO>::f(r.dr[j]) + lp.db);
+    }
+#pragma unroll
+    for (int j = 0; j < S::kBC; ++j) {
+      const int piece = g + G * j;
+      if (piece < S::kPieces) {
+        const bool is_c = piece * kWave >= kTileBC;
+        const int v = piece * kWave - (is_c ? kTileBC : 0) + lane;
+        Raw<IO>::put((is_c ? st.c : st.b) + v, r.bc[j]);
+      }
+    }
+  }
+
+  // x and delta of one step (ragged end of a chunk), computed from memory.
+  __device__ __forceinline__ void step(int s, float& xs, float& ds) const {
+    float w4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w4[k] = Raw<IO>::f(load_x(s - 3 + k));
+    xs = conv(w4);
+    ds = softplus_f32(Raw<IO>::f(Raw<IO>::load(rd, voff_row, (uint32_t)s * row_bytes)) + lp.db);
+  }
 };
 
 // Clear both stages (bf16 inputs rely on zero lower halves of the slots).
@@ -367,14 +520,14 @@ struct MainSmem {
   float part[2][kT * G * kWave];  // [buffer][step][wave][lane]
 };
 
-template <typename IO, int G, bool HAS_Z, bool ZERO_A>
+template <typename IO, int G, bool HAS_Z, bool ZERO_A, bool FUSED>
 __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* __restrict__ delta,
                                            const IO* __restrict__ B, const IO* __restrict__ C,
                                            const IO* __restrict__ z, IO* __restrict__ y,
                                            float Dd, int64_t seqlen, int dim, const Chunk& k,
                                            MainSmem<G>& sm, const float (&A2)[kDState / G],
                                            const float (&iA)[kDState / G],
-                                           float (&h)[kDState / G]) {
+                                           float (&h)[kDState / G], const LanePrologue& lp) {
   constexpr int NPL = kDState / G;
   constexpr int ZT = (kT + G - 1) / G;        // steps of a tile this wave finishes (at most)
   const int lane = k.lane, g = k.g, n0 = g * NPL;
@@ -387,9 +540,10 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
   const int nsteps = (int)(k.t_end - k.t_begin);
   const int nfull = nsteps / kT;
 
-  Loader<IO, G, true> ld;
-  ld.init(x, delta, B, C, seqlen, dim, k);
-  using Raw2 = TileRaw<G, 2>;
+  using LD = std::conditional_t<FUSED, FusedLoader<IO, G, true>, Loader<IO, G, true>>;
+  using Raw2 = typename LD::RawTile;
+  LD ld;
+  ld.init(x, delta, B, C, seqlen, dim, k, lp);
 
   // z of the steps this wave finishes in tile `tidx` (clamped past the end)
   auto issue_z = [&](uint32_t (&zr)[ZT], int tidx) {
@@ -525,14 +679,12 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
   }
 
   // ragged end of the chunk: one step at a time from global memory
-  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
   const __amdgpu_buffer_rsrc_t rcc = bc_rsrc(C, k, seqlen);
   for (int s0 = nfull * kT; s0 < nsteps; ++s0) {
     const uint32_t so = (uint32_t)s0 * row_bytes;
-    const float xs = buf<IO>::load(rx, voff, so);
-    const float ds = buf<IO>::load(rd, voff, so);
+    float xs, ds;
+    ld.step(s0, xs, ds);
     const uint32_t bo = (uint32_t)(s0 * kDState + n0) * sizeof(IO);
     float acc = 0.0f;
 #pragma unroll
@@ -559,14 +711,15 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
   }
 }
 
-template <typename IO, int G, bool HAS_Z>
-__global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kMainWavesPerSimd)))
+template <typename IO, int G, bool HAS_Z, bool FUSED>
+__global__ __launch_bounds__(kWave* G)
+__attribute__((amdgpu_waves_per_eu(FUSED ? kFusedWavesPerSimd : kMainWavesPerSimd)))
 void scan_fwd_kernel(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
     const IO* __restrict__ z, const float* __restrict__ h0, IO* __restrict__ y,
     float* __restrict__ h_last, const float* __restrict__ ws_hin, int64_t seqlen,
-    int64_t chunk_len, int dim, int nchunks) {
+    int64_t chunk_len, int dim, int nchunks, Prologue pro) {
   constexpr int NPL = kDState / G;
   __shared__ MainSmem<G> sm;
   const Chunk k = chunk_coords(dim, seqlen, chunk_len);
@@ -583,12 +736,16 @@ void scan_fwd_kernel(
 #pragma unroll
   for (int j = 0; j < NPL; ++j) h[j] = hinit ? hinit[j] : 0.0f;
   const float Dd = Dskip ? Dskip[k.d] : 0.0f;
+  LanePrologue lp{};
+  if constexpr (FUSED) lp = lane_prologue(pro, k.d);
   __syncthreads();  // stages cleared
 
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    scan_chunk<IO, G, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA, h);
+    scan_chunk<IO, G, HAS_Z, true, FUSED>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA,
+                                          h, lp);
   else
-    scan_chunk<IO, G, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA, h);
+    scan_chunk<IO, G, HAS_Z, false, FUSED>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA,
+                                           h, lp);
 
   if (k.c == nchunks - 1 && h_last && k.active) {
     float* hl = h_last + ((size_t)k.b * dim + k.d) * kDState + n0;
@@ -602,14 +759,15 @@ void scan_fwd_kernel(
 // plus the chunk's sum of delta.  Same staging as the main kernel, without
 // C and the readout.  With no A == 0 in the wave it carries g = A*h.
 // ---------------------------------------------------------------------------
-template <typename IO, int G, bool ZERO_A>
+template <typename IO, int G, bool ZERO_A, bool FUSED>
 __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
                                             const IO* __restrict__ delta,
                                             const IO* __restrict__ B, int64_t seqlen, int dim,
                                             const Chunk& k, Stage<false>* stages,
                                             const float (&A2)[kDState / G],
                                             const float (&iA)[kDState / G],
-                                            float (&h)[kDState / G], double& sd) {
+                                            float (&h)[kDState / G], double& sd,
+                                            const LanePrologue& lp) {
   constexpr int NPL = kDState / G;
   const int lane = k.lane, n0 = k.g * NPL;
   const uint32_t voff = (uint32_t)k.d * sizeof(IO);
@@ -617,9 +775,10 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
   const int nsteps = (int)(k.t_end - k.t_begin);
   const int nfull = nsteps / kT;
 
-  Loader<IO, G, false> ld;
-  ld.init(x, delta, B, B, seqlen, dim, k);
-  using Raw1 = TileRaw<G, 1>;
+  using LD = std::conditional_t<FUSED, FusedLoader<IO, G, false>, Loader<IO, G, false>>;
+  using Raw1 = typename LD::RawTile;
+  LD ld;
+  ld.init(x, delta, B, B, seqlen, dim, k, lp);
 
   // state carried through the tiles: g = A*h (or h itself when A may be 0)
   float gs[NPL];
@@ -701,13 +860,10 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
   for (int n = 0; n < NPL; ++n) h[n] = ZERO_A ? gs[n] : gs[n] * iA[n];
 
   // ragged end of the chunk
-  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
-  const __amdgpu_buffer_rsrc_t rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
   for (int s0 = nfull * kT; s0 < nsteps; ++s0) {
-    const uint32_t so = (uint32_t)s0 * row_bytes;
-    const float xs = buf<IO>::load(rx, voff, so);
-    const float ds = buf<IO>::load(rd, voff, so);
+    float xs, ds;
+    ld.step(s0, xs, ds);
     const uint32_t bo = (uint32_t)(s0 * kDState + n0) * sizeof(IO);
 #pragma unroll
     for (int n = 0; n < NPL; ++n) {
@@ -719,12 +875,12 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
   }
 }
 
-template <typename IO, int G>
+template <typename IO, int G, bool FUSED>
 __global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kCarryWavesPerSimd)))
 void scan_chunk_state_kernel(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, float* __restrict__ ws_hloc, double* __restrict__ ws_sdelta,
-    int64_t seqlen, int64_t chunk_len, int dim, int nchunks) {
+    int64_t seqlen, int64_t chunk_len, int dim, int nchunks, Prologue pro) {
   constexpr int NPL = kDState / G;
   __shared__ Stage<false> stages[2];
   const Chunk k = chunk_coords(dim, seqlen, chunk_len);  // k.c in [0, nchunks-2]
@@ -733,11 +889,13 @@ void scan_chunk_state_kernel(
   float A2[NPL], iA[NPL], h[NPL];
   const bool zero = load_A<NPL>(A, k.d, n0, A2, iA);
   double sd = 0.0;
+  LanePrologue lp{};
+  if constexpr (FUSED) lp = lane_prologue(pro, k.d);
   __syncthreads();  // stages cleared
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    chunk_state<IO, G, true>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd);
+    chunk_state<IO, G, true, FUSED>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd, lp);
   else
-    chunk_state<IO, G, false>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd);
+    chunk_state<IO, G, false, FUSED>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd, lp);
   if (k.active) {
     const size_t cd = ((size_t)k.b * nchunks + k.c) * dim + k.d;
     float* hl = ws_hloc + cd * kDState + n0;
@@ -806,7 +964,7 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
   if (i < count) h_last[i] = h0 ? h0[i] : 0.0f;
 }
 
-template <typename IO, int G>
+template <typename IO, int G, bool FUSED>
 hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
   const IO* x = static_cast<const IO*>(a.x);
   const IO* delta = static_cast<const IO*>(a.delta);
@@ -818,9 +976,9 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
     // more waves (two per wave) for latency hiding
     constexpr int GC = G < 8 ? 8 : G;
     dim3 grid1(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, GC>), grid1, dim3(kWave * GC), 0, stream, x,
-                       delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len, a.dim,
-                       a.nchunks);
+    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, GC, FUSED>), grid1, dim3(kWave * GC), 0,
+                       stream, x, delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len,
+                       a.dim, a.nchunks, a.pro);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int seg_log2 = 0;  // segment of lanes per (b, d, n): next power of two >= the map count
@@ -835,25 +993,33 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
   if (!(phase & 2)) return hipSuccess;
   dim3 grid(gx, (unsigned)a.nchunks, (unsigned)a.batch);
   if (a.z)
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, true>), grid, dim3(kWave * G), 0, stream, x,
-                       delta, a.A, B, C, a.Dskip, static_cast<const IO*>(a.z), a.h0,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, true, FUSED>), grid, dim3(kWave * G), 0, stream,
+                       x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(a.z), a.h0,
                        static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
-                       a.nchunks);
+                       a.nchunks, a.pro);
   else
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, false>), grid, dim3(kWave * G), 0, stream, x,
-                       delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr), a.h0,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, false, FUSED>), grid, dim3(kWave * G), 0, stream,
+                       x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr), a.h0,
                        static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
-                       a.nchunks);
+                       a.nchunks, a.pro);
   return hipGetLastError();
 }
 
 template <typename IO>
 hipError_t launch_scan_io(const ScanArgs& a, int G, int phase, hipStream_t stream) {
+  if (a.pro.d_conv > 0) {
+    switch (G) {  // the fused loader needs G <= kT
+      case 2: return launch_scan_t<IO, 2, true>(a, phase, stream);
+      case 4: return launch_scan_t<IO, 4, true>(a, phase, stream);
+      case 8: return launch_scan_t<IO, 8, true>(a, phase, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (G) {
-    case 2: return launch_scan_t<IO, 2>(a, phase, stream);
-    case 4: return launch_scan_t<IO, 4>(a, phase, stream);
-    case 8: return launch_scan_t<IO, 8>(a, phase, stream);
-    case 16: return launch_scan_t<IO, 16>(a, phase, stream);
+    case 2: return launch_scan_t<IO, 2, false>(a, phase, stream);
+    case 4: return launch_scan_t<IO, 4, false>(a, phase, stream);
+    case 8: return launch_scan_t<IO, 8, false>(a, phase, stream);
+    case 16: return launch_scan_t<IO, 16, false>(a, phase, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -75,6 +75,25 @@ def test_scan_noop_sizes_return_ok_without_launch(lib):
     assert _scan(lib, L=0) == ssm.SSM_OK        # no h_last requested: nothing to do
 
 
+def test_fused_scan_rejects_bad_arguments(lib):
+    W = ctypes.c_void_p(0x4000)
+
+    def fused(batch=2, L=8, dim=64, N=16, io=1, x_raw=FAKE, conv_w=W, d_conv=4, silu=1,
+              delta_raw=ctypes.c_void_p(0x6000), y=ctypes.c_void_p(0x2000), G=0):
+        return lib.ssm_scan_fwd_fused(batch, L, dim, N, io, x_raw, conv_w, None, d_conv, silu,
+                                      delta_raw, None, ctypes.c_void_p(0x7000), FAKE, FAKE,
+                                      None, None, None, y, None, None, 0, G, 1, None)
+    assert fused(d_conv=0) == ssm.SSM_ERR_INVALID_ARG
+    assert fused(d_conv=5) == ssm.SSM_ERR_UNSUPPORTED
+    assert fused(silu=2) == ssm.SSM_ERR_INVALID_ARG
+    assert fused(conv_w=None) == ssm.SSM_ERR_INVALID_ARG
+    assert fused(x_raw=None) == ssm.SSM_ERR_INVALID_ARG
+    assert fused(y=W) == ssm.SSM_ERR_INVALID_ARG            # y aliases conv_w
+    assert fused(G=16) == ssm.SSM_ERR_UNSUPPORTED           # fused loader needs <= 8 waves
+    assert fused(N=8) == ssm.SSM_ERR_UNSUPPORTED
+    assert fused(batch=0) == ssm.SSM_OK
+
+
 def test_decode_rejects_bad_arguments(lib):
     def dec(batch=2, dim=64, N=16, io=1, h=ctypes.c_void_p(0x5000), x=FAKE,
             y=ctypes.c_void_p(0x2000)):

@@ -51,6 +51,10 @@ extern "C" {
 #define SSM_DTYPE_F32 0
 #define SSM_DTYPE_BF16 1
 
+/* Values of the discretization argument of ssm_scan_fwd_ex. */
+#define SSM_DISC_ZOH 0   /* Bbar = (exp(delta*A) - 1) / A * B  (zero-order hold) */
+#define SSM_DISC_EULER 1 /* Bbar = delta * B                                      */
+
 /* Status codes returned by every entry point. */
 #define SSM_OK 0
 #define SSM_ERR_INVALID_ARG 1 /* NULL required pointer, negative size, aliasing */
@@ -144,6 +148,29 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
                        const float *Dskip, const void *z, const float *h0, void *y,
                        float *h_last, void *workspace, size_t workspace_bytes,
                        int waves_per_group, int nchunks, int phase, void *stream);
+
+/*
+ * ssm_scan_fwd_planned with two variants of the per-element formula:
+ *   a_per_channel = 1 -- A is [dim]: one real value per channel shared by its
+ *                        dstate states (the scalar-A structure of Mamba-2:
+ *                        ihouse article, "Mambaの進化の道のり"; ultralytics
+ *                        glossary, "S4からMambaへ").  0: A is [dim, dstate]
+ *                        as in ssm_scan_fwd.
+ *   discretization    -- SSM_DISC_ZOH, or SSM_DISC_EULER for Bbar = delta * B
+ *                        (paperlens tutorial, pseudo-code of the selection
+ *                        section; ihouse article: Mamba-2 used this form).
+ *                        Abar = exp(delta * A) in both.
+ * The result equals ssm_scan_fwd on A broadcast to [dim, dstate] (ZOH) or on
+ * the Euler recurrence.  Other arguments, plan and workspace as in
+ * ssm_scan_fwd_planned; waves_per_group 16 returns SSM_ERR_UNSUPPORTED.
+ * Other flag values return SSM_ERR_INVALID_ARG.
+ */
+int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                    int io_dtype, const void *x, const void *delta, const float *A,
+                    int a_per_channel, int discretization, const void *B, const void *C,
+                    const float *Dskip, const void *z, const float *h0, void *y,
+                    float *h_last, void *workspace, size_t workspace_bytes,
+                    int waves_per_group, int nchunks, void *stream);
 
 /*
  * Selective scan with its prologue fused in: the two steps that come right

@@ -40,6 +40,9 @@ def _declare(lib):
     i64, dp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.oracle_scan.restype = c_int
     lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [c_int]
+    lib.oracle_scan_ex.restype = c_int
+    lib.oracle_scan_ex.argtypes = ([i64, i64, i64, i64, dp, dp, dp, c_int, c_int]
+                                   + [dp] * 7 + [c_int])
     lib.oracle_decode_step.restype = c_int
     lib.oracle_decode_step.argtypes = [i64, i64, i64] + [dp] * 9
     lib.oracle_conv1d.restype = c_int
@@ -91,24 +94,31 @@ def zoh(delta: float, a: float):
     return abar.value, bcoef.value
 
 
-def scan(x, delta, A, B, C, D=None, z=None, h0=None, nthreads: int = 0, lib=None):
+def scan(x, delta, A, B, C, D=None, z=None, h0=None, nthreads: int = 0, lib=None,
+         discretization: str = "zoh"):
     """Selective scan in fp64.  Shapes: x, delta, z [b, L, d]; B, C [b, L, n];
-    A [d, n]; D [d]; h0 [b, d, n].  Returns (y [b, L, d], h_last [b, d, n])."""
+    A [d, n] (or [d]: one value per channel shared by its states); D [d];
+    h0 [b, d, n].  ``discretization`` is "zoh" or "euler" (Bbar = delta*B).
+    Returns (y [b, L, d], h_last [b, d, n])."""
     lib = lib or load_library()
     x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
     D, z, h0 = _f64(D), _f64(z), _f64(h0)
     batch, seqlen, dim = x.shape
-    dstate = A.shape[1]
-    assert delta.shape == x.shape and A.shape == (dim, dstate)
+    assert discretization in ("zoh", "euler")
+    per_channel = A.ndim == 1
+    dstate = B.shape[2] if per_channel else A.shape[1]
+    assert delta.shape == x.shape
+    assert A.shape == ((dim,) if per_channel else (dim, dstate))
     assert B.shape == (batch, seqlen, dstate) and C.shape == B.shape
     assert D is None or D.shape == (dim,)
     assert z is None or z.shape == x.shape
     assert h0 is None or h0.shape == (batch, dim, dstate)
     y = np.zeros_like(x)
     h_last = np.zeros((batch, dim, dstate), dtype=np.float64)
-    rc = lib.oracle_scan(batch, seqlen, dim, dstate, _ptr(x), _ptr(delta), _ptr(A),
-                         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
-                         _ptr(h_last), int(nthreads))
+    rc = lib.oracle_scan_ex(batch, seqlen, dim, dstate, _ptr(x), _ptr(delta), _ptr(A),
+                            int(per_channel), int(discretization == "euler"),
+                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+                            _ptr(h_last), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_scan rejected its arguments (code {rc})")
     return y, h_last

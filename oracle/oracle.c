@@ -20,7 +20,12 @@
  *   - the readout y_t = C_t . h_t + D x_t (ultralytics glossary, intro
  *     paragraph; ihouse article, the state and output equations);
  *   - the output gate y * SiLU(z) of the Mamba block (agenticai-flow guide,
- *     section "アーキテクチャ図解": S6 output times SiLU of the z branch).
+ *     section "アーキテクチャ図解": S6 output times SiLU of the z branch);
+ *   - variants (oracle_scan_ex): the Euler rule Bbar = delta * B with
+ *     Abar = exp(delta*A) (paperlens tutorial, the selection pseudo-code;
+ *     ihouse article: Mamba-2 simplified the discretisation this way), and A
+ *     as one value per channel shared by its states (ihouse article, section
+ *     on Mamba-2's scalar A; ultralytics glossary, S4-to-Mamba section).
  *
  * Readings taken where the pages are silent:
  *   - A == 0 uses the continuous limit of (exp(delta*A)-1)/A, which is delta;
@@ -35,7 +40,7 @@
  * Layouts (row-major, contiguous):
  *   x, delta, z, y : [batch, seqlen, dim]
  *   B, C           : [batch, seqlen, dstate]   (shared by every channel)
- *   A              : [dim, dstate]
+ *   A              : [dim, dstate]   ([dim] with a_per_channel)
  *   Dskip          : [dim]
  *   h0, h_last, h  : [batch, dim, dstate]
  */
@@ -70,12 +75,25 @@ void oracle_zoh(double delta, double a, double *abar, double *bbar_coef) {
 }
 
 /*
+ * Euler rule for one diagonal entry: Abar = exp(delta * a) as in the zero-
+ * order hold, Bbar = delta * B.
+ */
+static void euler(double delta, double a, double *abar, double *bbar_coef) {
+    *abar = exp(delta * a);
+    *bbar_coef = delta;
+}
+
+/*
  * One channel (b, d) over the whole sequence: a plain loop over t.
- * h is the channel's state, length dstate, updated in place.
+ * h is the channel's state, length dstate, updated in place.  a_row points
+ * at the channel's dstate values of A, a_step is 1 (A[d, n]) or 0 (one A[d]
+ * for every state); disc picks the discretisation rule.
  */
 static void scan_channel(int64_t b, int64_t d, int64_t seqlen, int64_t dim,
                          int64_t dstate, const double *x, const double *delta,
-                         const double *A, const double *B, const double *C,
+                         const double *a_row, int64_t a_step,
+                         void (*disc)(double, double, double *, double *),
+                         const double *B, const double *C,
                          const double *Dskip, const double *z, double *h,
                          double *y) {
     double dval = Dskip ? Dskip[d] : 0.0;
@@ -88,7 +106,7 @@ static void scan_channel(int64_t b, int64_t d, int64_t seqlen, int64_t dim,
         /* state update first: h_t = Abar_t h_{t-1} + Bbar_t x_t */
         for (int64_t n = 0; n < dstate; ++n) {
             double abar, bcoef;
-            zoh(dv, A[d * dstate + n], &abar, &bcoef);
+            disc(dv, a_row[n * a_step], &abar, &bcoef);
             h[n] = abar * h[n] + bcoef * B[bc + n] * xv;
         }
 
@@ -103,13 +121,15 @@ static void scan_channel(int64_t b, int64_t d, int64_t seqlen, int64_t dim,
 /*
  * Full scan.  Channels are independent, so they are spread over nthreads
  * host threads (nthreads <= 0 means all available); within a channel the
- * loop over t is strictly sequential.
+ * loop over t is strictly sequential.  a_per_channel: A is [dim] instead of
+ * [dim, dstate]; use_euler: Bbar = delta * B instead of the zero-order hold.
  */
-int oracle_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                const double *x, const double *delta, const double *A,
-                const double *B, const double *C, const double *Dskip,
-                const double *z, const double *h0, double *y, double *h_last,
-                int nthreads) {
+int oracle_scan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                   const double *x, const double *delta, const double *A,
+                   int a_per_channel, int use_euler,
+                   const double *B, const double *C, const double *Dskip,
+                   const double *z, const double *h0, double *y, double *h_last,
+                   int nthreads) {
     if (batch < 0 || seqlen < 0 || dim < 0 || dstate <= 0) return ORACLE_EINVAL;
     if (batch == 0 || dim == 0) return ORACLE_OK;
     if (!A || (seqlen > 0 && (!x || !delta || !B || !C || !y)))
@@ -123,12 +143,24 @@ int oracle_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
         double *h = (double *)malloc((size_t)dstate * sizeof(double));
         for (int64_t n = 0; n < dstate; ++n)
             h[n] = h0 ? h0[ch * dstate + n] : 0.0;
-        scan_channel(b, d, seqlen, dim, dstate, x, delta, A, B, C, Dskip, z, h, y);
+        const double *a_row = a_per_channel ? A + d : A + d * dstate;
+        scan_channel(b, d, seqlen, dim, dstate, x, delta, a_row, a_per_channel ? 0 : 1,
+                     use_euler ? euler : zoh, B, C, Dskip, z, h, y);
         if (h_last)
             for (int64_t n = 0; n < dstate; ++n) h_last[ch * dstate + n] = h[n];
         free(h);
     }
     return ORACLE_OK;
+}
+
+/* The scan of the method as written: A [dim, dstate], zero-order hold. */
+int oracle_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                const double *x, const double *delta, const double *A,
+                const double *B, const double *C, const double *Dskip,
+                const double *z, const double *h0, double *y, double *h_last,
+                int nthreads) {
+    return oracle_scan_ex(batch, seqlen, dim, dstate, x, delta, A, 0, 0, B, C, Dskip, z,
+                          h0, y, h_last, nthreads);
 }
 
 /*
@@ -146,8 +178,8 @@ int oracle_decode_step(int64_t batch, int64_t dim, int64_t dstate, double *h,
     for (int64_t b = 0; b < batch; ++b)
         for (int64_t d = 0; d < dim; ++d)
             /* a decode step is a scan of length 1 over this channel's state */
-            scan_channel(0, d, 1, dim, dstate, x + b * dim, delta + b * dim, A,
-                         B + b * dstate, C + b * dstate, Dskip,
+            scan_channel(0, d, 1, dim, dstate, x + b * dim, delta + b * dim,
+                         A + d * dstate, 1, zoh, B + b * dstate, C + b * dstate, Dskip,
                          z ? z + b * dim : NULL, h + (b * dim + d) * dstate,
                          y + b * dim);
     return ORACLE_OK;

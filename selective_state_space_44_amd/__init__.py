@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm.so")
 
 SSM_DTYPE_F32 = 0
 SSM_DTYPE_BF16 = 1
+SSM_DISC_ZOH = 0
+SSM_DISC_EULER = 1
 SSM_OK = 0
 SSM_ERR_INVALID_ARG = 1
 SSM_ERR_UNSUPPORTED = 2
@@ -41,6 +43,8 @@ SIGNATURES = {
                              + [_vp, _sz, _int, _int, _vp]),
     "ssm_scan_fwd_phase": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
                            + [_vp, _sz, _int, _int, _int, _vp]),
+    "ssm_scan_fwd_ex": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
+                        + [_vp] * 7 + [_vp, _sz, _int, _int, _vp]),
     "ssm_scan_fwd_fused": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int, _vp,
                                   _vp] + [_vp] * 8 + [_vp, _sz, _int, _int, _vp]),
     "ssm_decode_step": (_int, [_i64, _i64, _i64, _int] + [_vp] * 9 + [_vp]),
@@ -132,28 +136,41 @@ def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16,
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False,
              waves_per_group: int = 0, nchunks: int = 0, out=None, workspace=None,
-             phase: int = 3):
+             phase: int = 3, discretization: str = "zoh"):
     """Selective scan.  x, delta, z: [batch, L, dim]; B, C: [batch, L, dstate]
     (all float32 or all bfloat16); A [dim, dstate], D [dim], h0
     [batch, dim, dstate] float32.  Returns y (and the final state when
     ``return_last_state``).  ``waves_per_group``/``nchunks`` override the
     automatic plan (0 = automatic); ``phase`` 1 or 2 enqueues only the chunk
     carry passes or only the main pass (see ssm_scan_fwd_phase); both phases
-    of one scan must get the same ``workspace`` and ``out``."""
+    of one scan must get the same ``workspace`` and ``out``.
+
+    Variants (``ssm_scan_fwd_ex``): ``A`` of shape [dim] holds one value per
+    channel shared by its states (then ``B``/``C`` fix dstate);
+    ``discretization="euler"`` uses Bbar = delta*B instead of the zero-order
+    hold.  Both run as one call (``phase`` must be 3)."""
     if not isinstance(x, torch.Tensor) or x.dim() != 3:
         raise ValueError("x must be a [batch, seqlen, dim] tensor")
     device = x.device
     if device.type != "cuda":
         raise ValueError(f"tensors must be on a GPU, got {device}")
     batch, seqlen, dim = x.shape
-    if not isinstance(A, torch.Tensor) or A.dim() != 2:
-        raise ValueError("A must be a [dim, dstate] tensor")
-    dstate = A.shape[1]
+    if discretization not in ("zoh", "euler"):
+        raise ValueError("discretization must be 'zoh' or 'euler'")
+    if not isinstance(A, torch.Tensor) or A.dim() not in (1, 2):
+        raise ValueError("A must be a [dim, dstate] or [dim] tensor")
+    if not isinstance(B, torch.Tensor) or B.dim() != 3:
+        raise ValueError("B must be a [batch, seqlen, dstate] tensor")
+    per_channel = A.dim() == 1
+    dstate = B.shape[2] if per_channel else A.shape[1]
+    variant = per_channel or discretization != "zoh"
+    if variant and phase != 3:
+        raise ValueError("the A-per-channel and Euler variants run as one call (phase 3)")
     io = x.dtype
     code = _io_code(io)
     _require(x, "x", (batch, seqlen, dim), io, device)
     _require(delta, "delta", (batch, seqlen, dim), io, device)
-    _require(A, "A", (dim, dstate), torch.float32, device)
+    _require(A, "A", (dim,) if per_channel else (dim, dstate), torch.float32, device)
     _require(B, "B", (batch, seqlen, dstate), io, device)
     _require(C, "C", (batch, seqlen, dstate), io, device)
     _require(D, "D", (dim,), torch.float32, device)
@@ -172,6 +189,15 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
     if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if variant:
+        st = lib.ssm_scan_fwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
+                                 _ptr(A), int(per_channel),
+                                 SSM_DISC_EULER if discretization == "euler" else SSM_DISC_ZOH,
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+                                 _ptr(h_last), _ptr(workspace), ws_bytes, int(waves_per_group),
+                                 int(nchunks), _stream(device))
+        _check(st, "ssm_scan_fwd_ex")
+        return (y, h_last) if return_last_state else y
     st = lib.ssm_scan_fwd_phase(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
                                 _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                                 _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,

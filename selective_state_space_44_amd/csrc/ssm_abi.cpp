@@ -130,7 +130,8 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
                const void* x, const void* delta, const float* A, const void* B, const void* C,
                const float* Dskip, const void* z, const float* h0, void* y, float* h_last,
                void* workspace, size_t workspace_bytes, int waves_per_group, int nchunks,
-               int phase, void* stream, const ssm::Prologue& pro) {
+               int phase, void* stream, const ssm::Prologue& pro, int a_per_channel = 0,
+               int euler = 0) {
   if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype))
     return SSM_ERR_INVALID_ARG;
   if (phase < 1 || phase > 3) return SSM_ERR_INVALID_ARG;
@@ -164,6 +165,7 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
   if (nchunks > 0) K = nchunks;
   if (G != 2 && G != 4 && G != 8 && G != 16) return SSM_ERR_UNSUPPORTED;
   if (pro.d_conv > 0 && G == 16) return SSM_ERR_UNSUPPORTED;  // fused loader: G <= 8
+  if ((a_per_channel || euler) && G == 16) return SSM_ERR_UNSUPPORTED;  // variants: G <= 8
   const int64_t chunk_len = chunk_length(seqlen, dim, io_dtype, K);
   K = effective_chunks(seqlen, dim, io_dtype, K);  // == ceil(seqlen / chunk_len)
 
@@ -196,6 +198,8 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
   a.dim = (int)dim;
   a.batch = (int)batch;
   a.pro = pro;
+  a.a_per_channel = a_per_channel;
+  a.euler = euler;
   return hip_status(ssm::launch_scan(a, io_dtype == SSM_DTYPE_BF16, G, phase, s));
 }
 
@@ -213,6 +217,20 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
                     h_last, workspace, workspace_bytes, waves_per_group, nchunks, phase, stream,
                     none);
+}
+
+int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                    const void* x, const void* delta, const float* A, int a_per_channel,
+                    int discretization, const void* B, const void* C, const float* Dskip,
+                    const void* z, const float* h0, void* y, float* h_last, void* workspace,
+                    size_t workspace_bytes, int waves_per_group, int nchunks, void* stream) {
+  if (a_per_channel != 0 && a_per_channel != 1) return SSM_ERR_INVALID_ARG;
+  if (discretization != SSM_DISC_ZOH && discretization != SSM_DISC_EULER)
+    return SSM_ERR_INVALID_ARG;
+  const ssm::Prologue none{};
+  return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
+                    h_last, workspace, workspace_bytes, waves_per_group, nchunks, 3, stream,
+                    none, a_per_channel, discretization == SSM_DISC_EULER ? 1 : 0);
 }
 
 int ssm_scan_fwd_fused(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,

@@ -41,6 +41,8 @@ struct ScanArgs {
   int batch;
   int nchunks;
   Prologue pro;        // x and delta above are x_raw and delta_raw when pro.d_conv > 0
+  int a_per_channel;   // A is [dim] (one value per channel) instead of [dim, 16]
+  int euler;           // Bbar = delta * B instead of the zero-order hold
 };
 
 struct DecodeArgs {

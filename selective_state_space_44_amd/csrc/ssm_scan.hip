@@ -84,19 +84,40 @@ __device__ __forceinline__ void zoh_coef(float ds, float bx, float A2, float iA,
   }
 }
 
+// Variants of the per-element formula (bits of the template parameter V):
+//  kScalarA -- A holds one value per channel, shared by its 16 states
+//              (A[d] instead of A[d, n]): one exp2 per (t, d) instead of 16;
+//  kEuler   -- Euler-like input term Bbar = delta*B instead of the ZOH
+//              (exp(delta*A) - 1)/A * B (paperlens tutorial, selection-section
+//              pseudo-code); Abar = exp(delta*A) either way.
+constexpr int kScalarA = 1;
+constexpr int kEuler = 2;
+
 // Per-lane constants: A*log2(e) and 1/A for this wave's states.
-template <int NPL>
+template <int NPL, int V = 0>
 __device__ __forceinline__ bool load_A(const float* __restrict__ A, int d, int n0,
                                        float (&A2)[NPL], float (&iA)[NPL]) {
   bool zero = false;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
-    const float av = A[(size_t)d * kDState + n0 + k];
+    const float av = (V & kScalarA) ? A[d] : A[(size_t)d * kDState + n0 + k];
     A2[k] = av * kLog2e;
     iA[k] = 1.0f / av;
     zero |= (av == 0.0f);
   }
   return zero;
+}
+
+// Coefficients of one (step, state) for any variant (unpipelined form).
+template <int V, bool ZERO_A>
+__device__ __forceinline__ void step_coef(float ds, float xs, float Bn, float A2, float iA,
+                                          float& a, float& b) {
+  if constexpr ((V & kEuler) != 0) {
+    a = fast_exp2(ds * A2);
+    b = ds * xs * Bn;
+  } else {
+    zoh_coef<ZERO_A>(ds, Bn * xs, A2, iA, a, b);
+  }
 }
 
 // Rows [t_begin, t_end) of one batch row of an [b, L, dim] tensor as a buffer.
@@ -520,7 +541,7 @@ struct MainSmem {
   float part[2][kT * G * kWave];  // [buffer][step][wave][lane]
 };
 
-template <typename IO, int G, bool HAS_Z, bool ZERO_A, bool FUSED>
+template <typename IO, int G, bool HAS_Z, bool ZERO_A, bool FUSED, int V>
 __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* __restrict__ delta,
                                            const IO* __restrict__ B, const IO* __restrict__ C,
                                            const IO* __restrict__ z, IO* __restrict__ y,
@@ -585,23 +606,48 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
     float ca[2][NPL], cb[2][NPL], cc[2][NPL];
     auto coefs = [&](auto sc) {
       constexpr int s = decltype(sc)::value;
-#pragma unroll
-      for (int n = 0; n < NPL; ++n) {
-        ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
-        pin(ca[s & 1][n]);
-      }
-#pragma unroll
-      for (int n = 0; n < NPL; ++n) {
-        const float bx = bq[s & 1][n] * xv[s];
-        const float a = ca[s & 1][n];
-        if constexpr (!ZERO_A) {
-          const float q = bx * iA[n];
-          cb[s & 1][n] = __builtin_fmaf(a, q, -q);
+      if constexpr ((V & kScalarA) != 0) {
+        // one exp2 and one input term per step, shared by the wave's states
+        float a = fast_exp2(dv[s] * A2[0]);
+        float c;  // Bbar*x / B
+        if constexpr ((V & kEuler) != 0) {
+          c = dv[s] * xv[s];
+        } else if constexpr (!ZERO_A) {
+          const float q = xv[s] * iA[0];
+          c = __builtin_fmaf(a, q, -q);
         } else {
-          cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
+          c = (__builtin_isinf(iA[0]) ? dv[s] : (a - 1.0f) * iA[0]) * xv[s];
         }
-        pin(cb[s & 1][n]);
-        cc[s & 1][n] = cq[s & 1][n];
+        pin(a);
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          ca[s & 1][n] = a;
+          cb[s & 1][n] = c * bq[s & 1][n];
+          pin(cb[s & 1][n]);
+          cc[s & 1][n] = cq[s & 1][n];
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
+          pin(ca[s & 1][n]);
+        }
+        const float dx = dv[s] * xv[s];  // Euler: Bbar*x = (delta*x) * B
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          const float bx = bq[s & 1][n] * xv[s];
+          const float a = ca[s & 1][n];
+          if constexpr ((V & kEuler) != 0) {
+            cb[s & 1][n] = dx * bq[s & 1][n];
+          } else if constexpr (!ZERO_A) {
+            const float q = bx * iA[n];
+            cb[s & 1][n] = __builtin_fmaf(a, q, -q);
+          } else {
+            cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
+          }
+          pin(cb[s & 1][n]);
+          cc[s & 1][n] = cq[s & 1][n];
+        }
       }
     };
     fetch(std::integral_constant<int, 0>{});
@@ -692,7 +738,7 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
       const float Bn = buf<IO>::load(rbb, bo + n * sizeof(IO), 0);
       const float Cn = buf<IO>::load(rcc, bo + n * sizeof(IO), 0);
       float a, b;
-      zoh_coef<ZERO_A>(ds, Bn * xs, A2[n], iA[n], a, b);
+      step_coef<V, ZERO_A>(ds, xs, Bn, A2[n], iA[n], a, b);
       h[n] = __builtin_fmaf(a, h[n], b);
       acc = __builtin_fmaf(Cn, h[n], acc);
     }
@@ -711,7 +757,7 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
   }
 }
 
-template <typename IO, int G, bool HAS_Z, bool FUSED>
+template <typename IO, int G, bool HAS_Z, bool FUSED, int V>
 __global__ __launch_bounds__(kWave* G)
 __attribute__((amdgpu_waves_per_eu(FUSED ? kFusedWavesPerSimd : kMainWavesPerSimd)))
 void scan_fwd_kernel(
@@ -727,7 +773,7 @@ void scan_fwd_kernel(
   clear_stages<IO, true>(sm.st, kWave * G);
 
   float A2[NPL], iA[NPL], h[NPL];
-  const bool zero = load_A<NPL>(A, k.d, n0, A2, iA);
+  const bool zero = load_A<NPL, V>(A, k.d, n0, A2, iA);
   const float* hinit = nullptr;
   if (nchunks > 1)
     hinit = ws_hin + (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
@@ -741,11 +787,11 @@ void scan_fwd_kernel(
   __syncthreads();  // stages cleared
 
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    scan_chunk<IO, G, HAS_Z, true, FUSED>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA,
-                                          h, lp);
+    scan_chunk<IO, G, HAS_Z, true, FUSED, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2,
+                                             iA, h, lp);
   else
-    scan_chunk<IO, G, HAS_Z, false, FUSED>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2, iA,
-                                           h, lp);
+    scan_chunk<IO, G, HAS_Z, false, FUSED, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2,
+                                              iA, h, lp);
 
   if (k.c == nchunks - 1 && h_last && k.active) {
     float* hl = h_last + ((size_t)k.b * dim + k.d) * kDState + n0;
@@ -759,7 +805,7 @@ void scan_fwd_kernel(
 // plus the chunk's sum of delta.  Same staging as the main kernel, without
 // C and the readout.  With no A == 0 in the wave it carries g = A*h.
 // ---------------------------------------------------------------------------
-template <typename IO, int G, bool ZERO_A, bool FUSED>
+template <typename IO, int G, bool ZERO_A, bool FUSED, int V>
 __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
                                             const IO* __restrict__ delta,
                                             const IO* __restrict__ B, int64_t seqlen, int dim,
@@ -801,20 +847,41 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
     float ca[2][NPL], cb[2][NPL];
     auto coefs = [&](auto sc) {
       constexpr int s = decltype(sc)::value;
-#pragma unroll
-      for (int n = 0; n < NPL; ++n) {
-        ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
-        pin(ca[s & 1][n]);
-      }
-#pragma unroll
-      for (int n = 0; n < NPL; ++n) {
-        const float bx = bq[s & 1][n] * xv[s];
-        const float a = ca[s & 1][n];
-        if constexpr (!ZERO_A)
-          cb[s & 1][n] = __builtin_fmaf(a, bx, -bx);  // (a - 1) * B x, for g = A h
+      if constexpr ((V & kScalarA) != 0) {
+        float a = fast_exp2(dv[s] * A2[0]);
+        float c;  // input term / B: (a - 1) x for g = A h (ZOH), delta x (Euler)
+        if constexpr ((V & kEuler) != 0)
+          c = dv[s] * xv[s];
+        else if constexpr (!ZERO_A)
+          c = __builtin_fmaf(a, xv[s], -xv[s]);
         else
-          cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
-        pin(cb[s & 1][n]);
+          c = (__builtin_isinf(iA[0]) ? dv[s] : (a - 1.0f) * iA[0]) * xv[s];
+        pin(a);
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          ca[s & 1][n] = a;
+          cb[s & 1][n] = c * bq[s & 1][n];
+          pin(cb[s & 1][n]);
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
+          pin(ca[s & 1][n]);
+        }
+        const float dx = dv[s] * xv[s];
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          const float bx = bq[s & 1][n] * xv[s];
+          const float a = ca[s & 1][n];
+          if constexpr ((V & kEuler) != 0)
+            cb[s & 1][n] = dx * bq[s & 1][n];
+          else if constexpr (!ZERO_A)
+            cb[s & 1][n] = __builtin_fmaf(a, bx, -bx);  // (a - 1) * B x, for g = A h
+          else
+            cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
+          pin(cb[s & 1][n]);
+        }
       }
     };
     fetch(std::integral_constant<int, 0>{});
@@ -857,7 +924,7 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
     if (i < nfull) tile(i, 0, ra, rb);
   }
 #pragma unroll
-  for (int n = 0; n < NPL; ++n) h[n] = ZERO_A ? gs[n] : gs[n] * iA[n];
+  for (int n = 0; n < NPL; ++n) h[n] = (ZERO_A || (V & kEuler)) ? gs[n] : gs[n] * iA[n];
 
   // ragged end of the chunk
   const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
@@ -868,14 +935,15 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
 #pragma unroll
     for (int n = 0; n < NPL; ++n) {
       float a, b;
-      zoh_coef<ZERO_A>(ds, buf<IO>::load(rbb, bo + n * sizeof(IO), 0) * xs, A2[n], iA[n], a, b);
+      step_coef<V, ZERO_A>(ds, xs, buf<IO>::load(rbb, bo + n * sizeof(IO), 0), A2[n], iA[n], a,
+                           b);
       h[n] = __builtin_fmaf(a, h[n], b);
     }
     sd += (double)ds;
   }
 }
 
-template <typename IO, int G, bool FUSED>
+template <typename IO, int G, bool FUSED, int V>
 __global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kCarryWavesPerSimd)))
 void scan_chunk_state_kernel(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
@@ -887,15 +955,15 @@ void scan_chunk_state_kernel(
   const int n0 = k.g * NPL;
   clear_stages<IO, false>(stages, kWave * G);
   float A2[NPL], iA[NPL], h[NPL];
-  const bool zero = load_A<NPL>(A, k.d, n0, A2, iA);
+  const bool zero = load_A<NPL, V>(A, k.d, n0, A2, iA);
   double sd = 0.0;
   LanePrologue lp{};
   if constexpr (FUSED) lp = lane_prologue(pro, k.d);
   __syncthreads();  // stages cleared
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    chunk_state<IO, G, true, FUSED>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd, lp);
+    chunk_state<IO, G, true, FUSED, V>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd, lp);
   else
-    chunk_state<IO, G, false, FUSED>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd, lp);
+    chunk_state<IO, G, false, FUSED, V>(x, delta, B, seqlen, dim, k, stages, A2, iA, h, sd, lp);
   if (k.active) {
     const size_t cd = ((size_t)k.b * nchunks + k.c) * dim + k.d;
     float* hl = ws_hloc + cd * kDState + n0;
@@ -918,7 +986,7 @@ void scan_chunk_state_kernel(
 __global__ __launch_bounds__(256) void scan_carry_kernel(
     const float* __restrict__ A, const float* __restrict__ h0,
     const float* __restrict__ ws_hloc, const double* __restrict__ ws_sdelta,
-    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int seg_log2) {
+    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int seg_log2, int a_scalar) {
   const int S = 1 << seg_log2;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t seg = gid >> seg_log2;
@@ -931,7 +999,7 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(
   const int64_t bd = segc / kDState;
   const int d = (int)(bd % dim);
   const int64_t b = bd / dim;
-  const float A2 = A[(size_t)d * kDState + n] * kLog2e;
+  const float A2 = A[a_scalar ? (size_t)d : (size_t)d * kDState + n] * kLog2e;
   auto at = [&](int c) { return (((size_t)b * nchunks + c) * dim + d) * kDState + n; };
   float h = (h0 && valid) ? h0[segc] : 0.0f;
   if (j == 0 && valid) ws_hin[at(0)] = h;
@@ -964,7 +1032,7 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
   if (i < count) h_last[i] = h0 ? h0[i] : 0.0f;
 }
 
-template <typename IO, int G, bool FUSED>
+template <typename IO, int G, bool FUSED, int V>
 hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
   const IO* x = static_cast<const IO*>(a.x);
   const IO* delta = static_cast<const IO*>(a.delta);
@@ -976,7 +1044,7 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
     // more waves (two per wave) for latency hiding
     constexpr int GC = G < 8 ? 8 : G;
     dim3 grid1(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, GC, FUSED>), grid1, dim3(kWave * GC), 0,
+    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, GC, FUSED, V>), grid1, dim3(kWave * GC), 0,
                        stream, x, delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len,
                        a.dim, a.nchunks, a.pro);
     hipError_t e = hipGetLastError();
@@ -986,40 +1054,57 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
     const int64_t threads = (int64_t)a.batch * a.dim * kDState << seg_log2;
     hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        stream, a.A, a.h0, a.ws_hloc, a.ws_sdelta, a.ws_hin, a.batch, a.dim,
-                       a.nchunks, seg_log2);
+                       a.nchunks, seg_log2, (V & kScalarA) ? 1 : 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(phase & 2)) return hipSuccess;
   dim3 grid(gx, (unsigned)a.nchunks, (unsigned)a.batch);
   if (a.z)
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, true, FUSED>), grid, dim3(kWave * G), 0, stream,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, true, FUSED, V>), grid, dim3(kWave * G), 0, stream,
                        x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(a.z), a.h0,
                        static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
                        a.nchunks, a.pro);
   else
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, false, FUSED>), grid, dim3(kWave * G), 0, stream,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, G, false, FUSED, V>), grid, dim3(kWave * G), 0, stream,
                        x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr), a.h0,
                        static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
                        a.nchunks, a.pro);
   return hipGetLastError();
 }
 
+template <typename IO, int V>
+hipError_t launch_variant(const ScanArgs& a, int G, int phase, hipStream_t stream) {
+  switch (G) {  // the variants have kernels for 2, 4 and 8 waves per group
+    case 2: return launch_scan_t<IO, 2, false, V>(a, phase, stream);
+    case 4: return launch_scan_t<IO, 4, false, V>(a, phase, stream);
+    case 8: return launch_scan_t<IO, 8, false, V>(a, phase, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename IO>
 hipError_t launch_scan_io(const ScanArgs& a, int G, int phase, hipStream_t stream) {
+  const int V = (a.a_per_channel ? kScalarA : 0) | (a.euler ? kEuler : 0);
   if (a.pro.d_conv > 0) {
+    if (V != 0) return hipErrorInvalidValue;
     switch (G) {  // the fused loader needs G <= kT
-      case 2: return launch_scan_t<IO, 2, true>(a, phase, stream);
-      case 4: return launch_scan_t<IO, 4, true>(a, phase, stream);
-      case 8: return launch_scan_t<IO, 8, true>(a, phase, stream);
+      case 2: return launch_scan_t<IO, 2, true, 0>(a, phase, stream);
+      case 4: return launch_scan_t<IO, 4, true, 0>(a, phase, stream);
+      case 8: return launch_scan_t<IO, 8, true, 0>(a, phase, stream);
     }
     return hipErrorInvalidValue;
   }
+  switch (V) {
+    case kScalarA: return launch_variant<IO, kScalarA>(a, G, phase, stream);
+    case kEuler: return launch_variant<IO, kEuler>(a, G, phase, stream);
+    case kScalarA | kEuler: return launch_variant<IO, kScalarA | kEuler>(a, G, phase, stream);
+  }
   switch (G) {
-    case 2: return launch_scan_t<IO, 2, false>(a, phase, stream);
-    case 4: return launch_scan_t<IO, 4, false>(a, phase, stream);
-    case 8: return launch_scan_t<IO, 8, false>(a, phase, stream);
-    case 16: return launch_scan_t<IO, 16, false>(a, phase, stream);
+    case 2: return launch_scan_t<IO, 2, false, 0>(a, phase, stream);
+    case 4: return launch_scan_t<IO, 4, false, 0>(a, phase, stream);
+    case 8: return launch_scan_t<IO, 8, false, 0>(a, phase, stream);
+    case 16: return launch_scan_t<IO, 16, false, 0>(a, phase, stream);
   }
   return hipErrorInvalidValue;
 }

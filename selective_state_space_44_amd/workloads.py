@@ -39,7 +39,7 @@ import torch
 import torch.nn.functional as F
 
 (K_A, K_DSKIP, K_X, K_DELTA, K_Z, K_B, K_C, K_BIAS, K_HINIT, K_XRAW, K_CONVW, K_CONVB,
- K_DRAW) = range(13)
+ K_DRAW, K_ACH) = range(14)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,6 +152,13 @@ def make_inputs(w: Workload, device="cpu", layer: int = 0,
     else:
         out["h0"] = None
     return out
+
+
+def make_channel_A(w: Workload, device="cpu", layer: int = 0, dim: int | None = None):
+    """A with one value per channel, [dim] fp32, drawn like the per-state A:
+    -(0.5 + U(0, 1))."""
+    d = w.dim if dim is None else dim
+    return -(0.5 + _draw("uniform", (d,), w, layer, K_ACH, device))
 
 
 def make_fused_inputs(w: Workload, device="cpu", layer: int = 0, batch: int | None = None,

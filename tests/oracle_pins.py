@@ -26,6 +26,11 @@ What pins what (pages cited by title and section):
   (paperlens tutorial, section on the parallel scan).
 * L decode steps equal one scan (paperlens tutorial, S4 section: recurrent and
   convolutional faces give the same outputs).
+* Variants: the Euler rule Bbar = delta*B against brute force, its one-step
+  closed form, and its second-order agreement with the hold for small delta;
+  A given per channel against brute force with A broadcast over the states,
+  and the single decay rate it implies (paperlens tutorial, selection
+  pseudo-code; ihouse article, Mamba-2 section).
 * Prologue of the fused scan (paperlens tutorial, sections "現場ではこう使う"
   and "Mamba: 状態を「選択的」にする"): the causal depthwise convolution equals
   numpy's convolve of each channel with its reversed taps, and cannot see the
@@ -186,15 +191,22 @@ def pin_large_delta_overwrites_state(lib):
 # --------------------------------------------------------------------------
 # brute force, closed form, linearity, chunking, decode
 # --------------------------------------------------------------------------
-def _brute_force(p):
+def _brute_force(p, euler=False):
+    """Unrolled products and sums.  A may be [d] (one value per channel, used
+    for each of its states); euler=True uses Bbar = delta * B."""
     x, delta, A, B, C, D, z, h0 = (p[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0"))
     b, L, d = x.shape
-    n = A.shape[1]
+    n = B.shape[2]
+    if A.ndim == 1:
+        A = np.repeat(A[:, None], n, axis=1)
     y = np.zeros_like(x)
     for bi in range(b):
         for di in range(d):
             a = [np.exp(delta[bi, s, di] * A[di]) for s in range(L)]          # Abar_s
-            u = [(a[s] - 1.0) / A[di] * B[bi, s] * x[bi, s, di] for s in range(L)]
+            if euler:
+                u = [delta[bi, s, di] * B[bi, s] * x[bi, s, di] for s in range(L)]
+            else:
+                u = [(a[s] - 1.0) / A[di] * B[bi, s] * x[bi, s, di] for s in range(L)]
             for t in range(L):
                 h = np.prod(a[: t + 1], axis=0) * (h0[bi, di] if h0 is not None else 0.0)
                 for s in range(t + 1):
@@ -239,6 +251,61 @@ def pin_linearity(lib):
     (y1, h1), (y2, h2), (y3, h3) = (oracle.scan(lib=lib, **p) for p in (p1, p2, p3))
     assert _rel(y3, al * y1 + be * y2) < 1e-12
     assert _rel(h3, al * h1 + be * h2) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# variants: Euler rule Bbar = delta*B, and A as one value per channel
+# --------------------------------------------------------------------------
+def pin_euler_brute_force_tiny(lib):
+    rng = _rng(23)
+    for (b, L, d, n) in ((1, 1, 1, 1), (2, 7, 3, 4), (1, 12, 2, 5)):
+        p = _rand_problem(rng, b, L, d, n)
+        y, _ = oracle.scan(lib=lib, discretization="euler", **p)
+        assert _rel(y, _brute_force(p, euler=True)) < 1e-12, (b, L, d, n)
+
+
+def pin_euler_single_step_closed_form(lib):
+    rng = _rng(24)
+    for _ in range(5):
+        delta, a = rng.uniform(0.01, 2.0), -rng.uniform(0.1, 3.0)
+        x, h0, Bv = rng.standard_normal(3)
+        _, h = oracle.scan(np.full((1, 1, 1), x), np.full((1, 1, 1), delta),
+                           np.full((1, 1), a), np.full((1, 1, 1), Bv), np.zeros((1, 1, 1)),
+                           h0=np.full((1, 1, 1), h0), lib=lib, discretization="euler")
+        hn = np.exp(delta * a) * h0 + delta * Bv * x
+        assert abs(h[0, 0, 0] - hn) <= 1e-14 * (1 + abs(hn))
+
+
+def pin_euler_agrees_with_zoh_to_second_order(lib):
+    """(exp(delta a) - 1)/a = delta + a delta^2 / 2 + O(delta^3): one step
+    from h0 = 0 differs between the two rules by a delta^2 B x / 2."""
+    rng = _rng(25)
+    a = -rng.uniform(0.5, 2.0, 4)
+    Bv, x = rng.standard_normal(4), 0.8
+    for delta in (1e-2, 1e-3):
+        args = (np.full((1, 1, 1), x), np.full((1, 1, 1), delta), a[None, :],
+                Bv[None, None, :], np.zeros((1, 1, 4)))
+        _, hz = oracle.scan(*args, lib=lib)
+        _, he = oracle.scan(*args, lib=lib, discretization="euler")
+        lead = a * delta ** 2 / 2 * Bv * x
+        assert np.all(np.abs((hz - he)[0, 0] - lead) <= 2 * np.abs(a) ** 2 * delta ** 3 * abs(x)
+                      * np.abs(Bv)), delta
+
+
+def pin_per_channel_A_brute_force(lib):
+    rng = _rng(26)
+    for euler in (False, True):
+        for (b, L, d, n) in ((1, 4, 3, 5), (2, 9, 4, 3)):
+            p = _rand_problem(rng, b, L, d, n)
+            p["A"] = -rng.uniform(0.2, 2.0, d)
+            y, h = oracle.scan(lib=lib, discretization="euler" if euler else "zoh", **p)
+            assert _rel(y, _brute_force(p, euler=euler)) < 1e-12, (euler, b, L, d, n)
+            # the state decays at the channel's single rate
+            if L and not euler:
+                q = dict(p, x=np.zeros_like(p["x"]))
+                _, hq = oracle.scan(lib=lib, **q)
+                rate = np.exp(p["A"][None, :] * p["delta"].sum(axis=1))
+                assert _rel(hq, p["h0"] * rate[:, :, None]) < 1e-12
 
 
 def _slice_t(p, lo, hi):

@@ -60,9 +60,10 @@ def check_state(got, ref, what="state"):
     return float(np.max(err / bound)) if err.size else 0.0
 
 
-def oracle_scan(inp: dict, channels=None, nthreads: int = 0):
+def oracle_scan(inp: dict, channels=None, nthreads: int = 0, discretization: str = "zoh"):
     """Oracle on the inputs dict of the scan (device tensors); ``channels``
-    optionally restricts to a subset of d (channels are independent)."""
+    optionally restricts to a subset of d (channels are independent).  A may
+    be [d, n] or [d] (one value per channel)."""
     x, delta, A, B, C = inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"]
     D, z, h0 = inp.get("D"), inp.get("z"), inp.get("h0")
     if channels is not None:
@@ -73,7 +74,8 @@ def oracle_scan(inp: dict, channels=None, nthreads: int = 0):
         D = D.index_select(0, idx) if D is not None else None
         h0 = h0.index_select(1, idx) if h0 is not None else None
     return oracle.scan(to_f64(x), to_f64(delta), to_f64(A), to_f64(B), to_f64(C),
-                       to_f64(D), to_f64(z), to_f64(h0), nthreads=nthreads)
+                       to_f64(D), to_f64(z), to_f64(h0), nthreads=nthreads,
+                       discretization=discretization)
 
 
 def pick(t, channels, axis):

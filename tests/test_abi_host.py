@@ -94,6 +94,22 @@ def test_fused_scan_rejects_bad_arguments(lib):
     assert fused(batch=0) == ssm.SSM_OK
 
 
+def test_scan_variants_reject_bad_arguments(lib):
+    def ex(per_channel=1, disc=ssm.SSM_DISC_EULER, batch=2, L=8, G=0, A=FAKE, io=1):
+        return lib.ssm_scan_fwd_ex(batch, L, 64, 16, io, FAKE, ctypes.c_void_p(0x6000), A,
+                                   per_channel, disc, ctypes.c_void_p(0x7000),
+                                   ctypes.c_void_p(0x8000), None, None, None,
+                                   ctypes.c_void_p(0x2000), None, None, 0, G, 1, None)
+    assert ex(per_channel=2) == ssm.SSM_ERR_INVALID_ARG
+    assert ex(per_channel=-1) == ssm.SSM_ERR_INVALID_ARG
+    assert ex(disc=2) == ssm.SSM_ERR_INVALID_ARG
+    assert ex(A=None) == ssm.SSM_ERR_INVALID_ARG
+    assert ex(io=5) == ssm.SSM_ERR_INVALID_ARG
+    assert ex(G=16) == ssm.SSM_ERR_UNSUPPORTED              # variants need <= 8 waves
+    assert ex(batch=0) == ssm.SSM_OK
+    assert ex(L=0) == ssm.SSM_OK
+
+
 def test_decode_rejects_bad_arguments(lib):
     def dec(batch=2, dim=64, N=16, io=1, h=ctypes.c_void_p(0x5000), x=FAKE,
             y=ctypes.c_void_p(0x2000)):

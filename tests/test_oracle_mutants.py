@@ -20,7 +20,13 @@ MUTANTS = {
     "zero_A_limit_wrong": ("*bbar_coef = (a != 0.0) ? expm1(u) / a : delta;",
                            "*bbar_coef = (a != 0.0) ? expm1(u) / a : 0.0;"),
     "C_used_for_B": ("bcoef * B[bc + n] * xv", "bcoef * C[bc + n] * xv"),
-    "state_index_reversed": ("A[d * dstate + n]", "A[d * dstate + (dstate - 1 - n)]"),
+    "state_index_reversed": ("a_row[n * a_step]", "a_row[(dstate - 1 - n) * a_step]"),
+    "euler_drops_delta": ("*bbar_coef = delta;\n}", "*bbar_coef = 1.0;\n}"),
+    "euler_uses_the_hold": ("*bbar_coef = delta;\n}", "*bbar_coef = expm1(delta * a) / a;\n}"),
+    "euler_linear_decay": ("*abar = exp(delta * a);", "*abar = 1.0 + delta * a;"),
+    "per_channel_A_of_channel_0": ("a_per_channel ? A + d : A + d * dstate",
+                                   "a_per_channel ? A : A + d * dstate"),
+    "per_channel_A_stepped": ("a_per_channel ? 0 : 1", "1"),
     "no_decay": ("h[n] = abar * h[n] + bcoef", "h[n] = h[n] + bcoef"),
     "previous_token_B_C": ("int64_t bc = (b * seqlen + t) * dstate;",
                            "int64_t bc = (b * seqlen + (t > 0 ? t - 1 : 0)) * dstate;"),

@@ -194,6 +194,43 @@ def bench_fused(steps: int, warmup: int):
             "hbm_algorithmic_GBps": w.algorithmic_bytes() / (ms * 1e-3) / 1e9}
 
 
+def bench_variants(steps: int, warmup: int):
+    """The scan variants at the same shape and plan: A per channel (one value
+    shared by a channel's states) and the Euler rule Bbar = delta*B."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.MAMBA_2P8B
+    dev = "cuda:0"
+    sets = [W.make_inputs(w, device=dev, layer=i) for i in range(2)]
+    a_ch = [W.make_channel_A(w, device=dev, layer=i) for i in range(2)]
+    outs = [torch.empty_like(s["x"]) for s in sets]
+    nws = ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    res = {}
+    for tag, per_channel, disc in (("A_per_channel", True, "zoh"), ("euler", False, "euler"),
+                                   ("A_per_channel_euler", True, "euler")):
+        def step(i):
+            f = sets[i % 2]
+            A = a_ch[i % 2] if per_channel else f["A"]
+            ssm.scan_fwd(f["x"], f["delta"], A, f["B"], f["C"], f["D"], f["z"], None,
+                         out=outs[i % 2], workspace=ws, discretization=disc)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[tag] = {"ms_per_step": ms, "value": w.elements / (ms * 1e-3), "unit": "elements/s"}
+    return {"workload": w.name, **res}
+
+
 def bench_decode(sweeps: int):
     """64 layers stepped back to back, each with its own state, inputs and
     parameters (5.4 GB of state, far beyond the 256 MB cache).  HIP events
@@ -249,6 +286,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the A-per-channel / Euler scan variants")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the scan with the fused conv1d/softplus prologue")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -321,6 +360,8 @@ def main():
         line["decode"] = bench_decode(args.decode_sweeps)
     if not args.no_fused:
         line["fused_prologue"] = bench_fused(max(10, args.steps // 4), max(10, args.warmup // 4))
+    if not args.no_variants:
+        line["variants"] = bench_variants(max(10, args.steps // 4), max(10, args.warmup // 4))
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(r["inp"], w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

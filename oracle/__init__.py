@@ -43,6 +43,9 @@ def _declare(lib):
     lib.oracle_scan_ex.restype = c_int
     lib.oracle_scan_ex.argtypes = ([i64, i64, i64, i64, dp, dp, dp, c_int, c_int]
                                    + [dp] * 7 + [c_int])
+    lib.oracle_scan_bwd_ex.restype = c_int
+    lib.oracle_scan_bwd_ex.argtypes = ([i64, i64, i64, i64, dp, dp, dp, c_int, c_int]
+                                       + [dp] * 15 + [c_int])
     lib.oracle_decode_step.restype = c_int
     lib.oracle_decode_step.argtypes = [i64, i64, i64] + [dp] * 9
     lib.oracle_conv1d.restype = c_int
@@ -122,6 +125,40 @@ def scan(x, delta, A, B, C, D=None, z=None, h0=None, nthreads: int = 0, lib=None
     if rc != 0:
         raise ValueError(f"oracle_scan rejected its arguments (code {rc})")
     return y, h_last
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None,
+             nthreads: int = 0, lib=None, discretization: str = "zoh"):
+    """Gradients of the scan in fp64 for upstream dy [b, L, d] and optional
+    dh_last [b, d, n].  Returns a dict with dx, ddelta, dz (None without z)
+    [b, L, d]; dA (shape of A); dB, dC [b, L, n]; dD [d]; dh0 [b, d, n]."""
+    lib = lib or load_library()
+    x, delta, A, B, C, dy = map(_f64, (x, delta, A, B, C, dy))
+    D, z, h0, dh_last = _f64(D), _f64(z), _f64(h0), _f64(dh_last)
+    batch, seqlen, dim = x.shape
+    assert discretization in ("zoh", "euler")
+    per_channel = A.ndim == 1
+    dstate = B.shape[2] if per_channel else A.shape[1]
+    assert delta.shape == x.shape and dy.shape == x.shape
+    assert A.shape == ((dim,) if per_channel else (dim, dstate))
+    assert B.shape == (batch, seqlen, dstate) and C.shape == B.shape
+    assert D is None or D.shape == (dim,)
+    assert z is None or z.shape == x.shape
+    for s in (h0, dh_last):
+        assert s is None or s.shape == (batch, dim, dstate)
+    g = dict(dx=np.zeros_like(x), ddelta=np.zeros_like(x), dA=np.zeros_like(A),
+             dB=np.zeros_like(B), dC=np.zeros_like(C), dD=np.zeros(dim),
+             dz=np.zeros_like(x) if z is not None else None,
+             dh0=np.zeros((batch, dim, dstate)))
+    rc = lib.oracle_scan_bwd_ex(batch, seqlen, dim, dstate, _ptr(x), _ptr(delta), _ptr(A),
+                                int(per_channel), int(discretization == "euler"), _ptr(B),
+                                _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last),
+                                _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                                int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_bwd_ex rejected its arguments (code {rc})")
+    return g
 
 
 def decode_step(h, x, delta, A, B, C, D=None, z=None, lib=None):

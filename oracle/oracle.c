@@ -164,6 +164,212 @@ int oracle_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 }
 
 /*
+ * Backward of the scan: the reverse-mode derivative of oracle_scan_ex with
+ * respect to every input, for a loss whose gradients dy = dL/dy and
+ * (optionally) dh_last = dL/dh_last are given.  The recompute-instead-of-
+ * store design of the fused kernel is the GPU's business; here every state
+ * of a channel is kept (paperlens tutorial, section on the hardware-aware
+ * algorithm: the backward needs the states again).
+ *
+ * The chain rule on the forward loop, with g_t = SiLU(z_t) (1 without a
+ * gate) and p_t = C_t . h_t + D x_t the gate's input:
+ *   dp_t      = dy_t g_t,    dz_t = dy_t p_t SiLU'(z_t)
+ *   dh_t      = dp_t C_t + Abar_{t+1} dh_{t+1}      (dh_last joins at t = L-1)
+ *   dx_t      = dp_t D + sum_n dh_t[n] coef_t[n] B_t[n]
+ *   ddelta_t  = sum_n dh_t[n] (dAbar/ddelta h_{t-1}[n] + dcoef/ddelta B_t[n] x_t)
+ *   dA[d,n]  += dh_t[n] (dAbar/dA h_{t-1}[n] + dcoef/dA B_t[n] x_t)
+ *   dB_t[n]  += dh_t[n] coef_t[n] x_t                (summed over channels)
+ *   dC_t[n]  += dp_t h_t[n]                          (summed over channels)
+ *   dD[d]    += dp_t x_t,   dh0 = Abar_0 dh_0
+ * where coef = Bbar/B.  dA and dD are summed over batch and time; with A
+ * given per channel, dA[d] is also summed over the states.
+ */
+typedef struct {
+    double abar, coef;          /* Abar and Bbar / B */
+    double dabar_dd, dabar_da;  /* dAbar/ddelta, dAbar/dA */
+    double dcoef_dd, dcoef_da;  /* dcoef/ddelta, dcoef/dA */
+} disc_grad;
+
+/* Zero-order hold: Abar = exp(delta a), coef = (Abar - 1)/a, and at a = 0
+ * the limits coef = delta, dcoef/da = delta^2 / 2. */
+static void zoh_grad(double delta, double a, disc_grad *g) {
+    double u = delta * a;
+    g->abar = exp(u);
+    g->dabar_dd = a * g->abar;
+    g->dabar_da = delta * g->abar;
+    if (a != 0.0) {
+        g->coef = expm1(u) / a;
+        g->dcoef_dd = g->abar;
+        g->dcoef_da = (delta * g->abar - g->coef) / a;
+    } else {
+        g->coef = delta;
+        g->dcoef_dd = 1.0;
+        g->dcoef_da = 0.5 * delta * delta;
+    }
+}
+
+/* Euler rule: Abar = exp(delta a), coef = delta. */
+static void euler_grad(double delta, double a, disc_grad *g) {
+    g->abar = exp(delta * a);
+    g->dabar_dd = a * g->abar;
+    g->dabar_da = delta * g->abar;
+    g->coef = delta;
+    g->dcoef_dd = 1.0;
+    g->dcoef_da = 0.0;
+}
+
+/* SiLU'(v) = sigmoid(v) (1 + v (1 - sigmoid(v))). */
+static double dsilu(double v) {
+    double sg = 1.0 / (1.0 + exp(-v));
+    return sg * (1.0 + v * (1.0 - sg));
+}
+
+/*
+ * One channel (b, d): forward keeping every state (hist[t+1] = h_t,
+ * hist[0] = h0), then the reverse loop.  e holds dL/dh_t arriving from the
+ * steps after t.  dA_row (dstate entries, or 1 with a_step 0) and *dD_acc
+ * receive this channel's sums; dB_acc and dC_acc ([batch, seqlen, dstate])
+ * receive its share of the channel sums.
+ */
+static void scan_channel_bwd(int64_t b, int64_t d, int64_t seqlen, int64_t dim,
+                             int64_t dstate, const double *x, const double *delta,
+                             const double *a_row, int64_t a_step,
+                             void (*disc)(double, double, disc_grad *),
+                             const double *B, const double *C, const double *Dskip,
+                             const double *z, const double *h0_row, const double *dy,
+                             const double *dh_last_row, double *hist, double *e,
+                             double *dx, double *ddelta, double *dz, double *dA_row,
+                             double *dD_acc, double *dB_acc, double *dC_acc,
+                             double *dh0_row) {
+    double dval = Dskip ? Dskip[d] : 0.0;
+    for (int64_t n = 0; n < dstate; ++n) hist[n] = h0_row ? h0_row[n] : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+        int64_t io = (b * seqlen + t) * dim + d;
+        int64_t bc = (b * seqlen + t) * dstate;
+        for (int64_t n = 0; n < dstate; ++n) {
+            disc_grad g;
+            disc(delta[io], a_row[n * a_step], &g);
+            hist[(t + 1) * dstate + n] =
+                g.abar * hist[t * dstate + n] + g.coef * B[bc + n] * x[io];
+        }
+    }
+    for (int64_t n = 0; n < dstate; ++n) e[n] = dh_last_row ? dh_last_row[n] : 0.0;
+    for (int64_t t = seqlen - 1; t >= 0; --t) {
+        int64_t io = (b * seqlen + t) * dim + d;
+        int64_t bc = (b * seqlen + t) * dstate;
+        const double *h_t = hist + (t + 1) * dstate;
+        const double *h_prev = hist + t * dstate;
+        double xv = x[io], dv = delta[io];
+        double s = 0.0;
+        for (int64_t n = 0; n < dstate; ++n) s += C[bc + n] * h_t[n];
+        double p = s + dval * xv;
+        double dp = z ? dy[io] * silu(z[io]) : dy[io];
+        if (z && dz) dz[io] = dy[io] * p * dsilu(z[io]);
+        double dxv = dp * dval, ddv = 0.0;
+        for (int64_t n = 0; n < dstate; ++n) {
+            disc_grad g;
+            disc(dv, a_row[n * a_step], &g);
+            double dh = e[n] + dp * C[bc + n];
+            dC_acc[bc + n] += dp * h_t[n];
+            dB_acc[bc + n] += dh * g.coef * xv;
+            dxv += dh * g.coef * B[bc + n];
+            ddv += dh * (g.dabar_dd * h_prev[n] + g.dcoef_dd * B[bc + n] * xv);
+            dA_row[n * a_step] += dh * (g.dabar_da * h_prev[n] + g.dcoef_da * B[bc + n] * xv);
+            e[n] = g.abar * dh;
+        }
+        dx[io] = dxv;
+        ddelta[io] = ddv;
+        *dD_acc += dp * xv;
+    }
+    if (dh0_row)
+        for (int64_t n = 0; n < dstate; ++n) dh0_row[n] = e[n];
+}
+
+/*
+ * Full backward.  Inputs as oracle_scan_ex plus dy [batch, seqlen, dim] and
+ * dh_last [batch, dim, dstate] (NULL = 0).  Outputs: dx, ddelta, dz
+ * [batch, seqlen, dim] (dz only with a gate; may be NULL), dA [dim, dstate]
+ * ([dim] with a_per_channel), dB, dC [batch, seqlen, dstate], dD [dim] (may
+ * be NULL), dh0 [batch, dim, dstate] (may be NULL).  Channels run on
+ * nthreads threads in contiguous ranges; the channel sums of dB and dC are
+ * kept per thread and added in thread order, so a result depends on
+ * nthreads only through rounding.
+ */
+int oracle_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       const double *x, const double *delta, const double *A,
+                       int a_per_channel, int use_euler, const double *B, const double *C,
+                       const double *Dskip, const double *z, const double *h0,
+                       const double *dy, const double *dh_last, double *dx, double *ddelta,
+                       double *dA, double *dB, double *dC, double *dD, double *dz,
+                       double *dh0, int nthreads) {
+    if (batch < 0 || seqlen < 0 || dim < 0 || dstate <= 0) return ORACLE_EINVAL;
+    if (!A || !dA) return ORACLE_EINVAL;
+    if (batch > 0 && dim > 0 && seqlen > 0 &&
+        (!x || !delta || !B || !C || !dy || !dx || !ddelta || !dB || !dC))
+        return ORACLE_EINVAL;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    const int64_t na = a_per_channel ? dim : dim * dstate;
+    const int64_t nbc = batch * seqlen * dstate;
+    for (int64_t i = 0; i < na; ++i) dA[i] = 0.0;
+    if (dD)
+        for (int64_t i = 0; i < dim; ++i) dD[i] = 0.0;
+    for (int64_t i = 0; i < nbc; ++i) dB[i] = dC[i] = 0.0;
+    if (batch == 0 || dim == 0) return ORACLE_OK;
+
+    /* per (b, d) sums of dA and dD, added over b in order afterwards */
+    const int64_t a_len = a_per_channel ? 1 : dstate;
+    double *dA_part = (double *)calloc((size_t)(batch * dim * a_len), sizeof(double));
+    double *dD_part = (double *)calloc((size_t)(batch * dim), sizeof(double));
+    double **dB_thr = (double **)calloc((size_t)nthreads, sizeof(double *));
+    double **dC_thr = (double **)calloc((size_t)nthreads, sizeof(double *));
+    int used = 1;
+    const int64_t nch = batch * dim;
+#pragma omp parallel num_threads(nthreads)
+    {
+        int tid = omp_get_thread_num();
+#pragma omp single
+        used = omp_get_num_threads();
+        double *dBt = (double *)calloc((size_t)nbc + 1, sizeof(double));
+        double *dCt = (double *)calloc((size_t)nbc + 1, sizeof(double));
+        double *hist = (double *)malloc((size_t)((seqlen + 1) * dstate) * sizeof(double));
+        double *e = (double *)malloc((size_t)dstate * sizeof(double));
+        dB_thr[tid] = dBt;
+        dC_thr[tid] = dCt;
+#pragma omp for schedule(static)
+        for (int64_t ch = 0; ch < nch; ++ch) {
+            int64_t b = ch / dim, d = ch % dim;
+            const double *a_row = a_per_channel ? A + d : A + d * dstate;
+            scan_channel_bwd(b, d, seqlen, dim, dstate, x, delta, a_row, a_per_channel ? 0 : 1,
+                             use_euler ? euler_grad : zoh_grad, B, C, Dskip, z,
+                             h0 ? h0 + ch * dstate : NULL, dy,
+                             dh_last ? dh_last + ch * dstate : NULL, hist, e, dx, ddelta, dz,
+                             dA_part + ch * a_len, dD_part + ch, dBt, dCt,
+                             dh0 ? dh0 + ch * dstate : NULL);
+        }
+        free(hist);
+        free(e);
+    }
+    for (int th = 0; th < used; ++th) {
+        for (int64_t i = 0; i < nbc; ++i) {
+            dB[i] += dB_thr[th][i];
+            dC[i] += dC_thr[th][i];
+        }
+        free(dB_thr[th]);
+        free(dC_thr[th]);
+    }
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < dim; ++d) {
+            for (int64_t k = 0; k < a_len; ++k) dA[d * a_len + k] += dA_part[(b * dim + d) * a_len + k];
+            if (dD) dD[d] += dD_part[b * dim + d];
+        }
+    free(dA_part);
+    free(dD_part);
+    free(dB_thr);
+    free(dC_thr);
+    return ORACLE_OK;
+}
+
+/*
  * One recurrent decode step: the loop body of the scan applied once per
  * channel to a resident state h [batch, dim, dstate] (updated in place).
  * x, delta, z, y are [batch, dim]; B, C are [batch, dstate].

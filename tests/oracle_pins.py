@@ -26,6 +26,10 @@ What pins what (pages cited by title and section):
   (paperlens tutorial, section on the parallel scan).
 * L decode steps equal one scan (paperlens tutorial, S4 section: recurrent and
   convolutional faces give the same outputs).
+* Backward: every gradient (x, delta, A, B, C, D, z, h0) against central
+  differences of the forward oracle, for both rules, A per channel and A = 0;
+  and Euler's theorem on homogeneous functions for x, B and C (y is linear
+  in each when there is no gate, skip or initial state).
 * Variants: the Euler rule Bbar = delta*B against brute force, its one-step
   closed form, and its second-order agreement with the hold for small delta;
   A given per channel against brute force with A broadcast over the states,
@@ -306,6 +310,77 @@ def pin_per_channel_A_brute_force(lib):
                 _, hq = oracle.scan(lib=lib, **q)
                 rate = np.exp(p["A"][None, :] * p["delta"].sum(axis=1))
                 assert _rel(hq, p["h0"] * rate[:, :, None]) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# backward: every gradient against central differences of the forward oracle
+# --------------------------------------------------------------------------
+def _loss(lib, p, dy, dhl, disc):
+    y, h = oracle.scan(lib=lib, discretization=disc, **p)
+    return float(np.sum(dy * y) + (np.sum(dhl * h) if dhl is not None else 0.0))
+
+
+def _check_grads_fd(lib, p, dy, dhl, disc, rng, per_tensor=12):
+    g = oracle.scan_bwd(lib=lib, dy=dy, dh_last=dhl, discretization=disc, **p)
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+             "z": "dz", "h0": "dh0"}
+    for k, gk in names.items():
+        if p.get(k) is None:
+            continue
+        v = p[k]
+        flat = rng.choice(v.size, size=min(per_tensor, v.size), replace=False)
+        for i in flat:
+            idx = np.unravel_index(i, v.shape)
+            eps = 1e-6 * max(1.0, abs(v[idx]))
+            orig = v[idx]
+            v[idx] = orig + eps
+            lp = _loss(lib, p, dy, dhl, disc)
+            v[idx] = orig - eps
+            lm = _loss(lib, p, dy, dhl, disc)
+            v[idx] = orig
+            fd = (lp - lm) / (2 * eps)
+            an = g[gk][idx]
+            assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (disc, k, idx, fd, an)
+
+
+def pin_backward_matches_finite_differences(lib):
+    rng = _rng(27)
+    for disc in ("zoh", "euler"):
+        for (b, L, d, n, flags) in ((2, 6, 3, 4, (True, True, True)),
+                                    (1, 9, 2, 3, (False, False, False))):
+            p = _rand_problem(rng, b, L, d, n, *flags)
+            dy = rng.standard_normal(p["x"].shape)
+            dhl = rng.standard_normal((b, d, n)) if flags[2] else None
+            _check_grads_fd(lib, p, dy, dhl, disc, rng)
+
+
+def pin_backward_variants_and_zero_A(lib):
+    """A per channel, and A entries of exactly 0 (the limit of the hold)."""
+    rng = _rng(28)
+    p = _rand_problem(rng, 2, 7, 3, 4)
+    p["A"][1, 2] = 0.0
+    p["A"][2, :] = 0.0
+    dy = rng.standard_normal(p["x"].shape)
+    _check_grads_fd(lib, p, dy, rng.standard_normal((2, 3, 4)), "zoh", rng, per_tensor=20)
+    for disc in ("zoh", "euler"):
+        q = _rand_problem(rng, 2, 5, 3, 4)
+        q["A"] = -rng.uniform(0.2, 2.0, 3)
+        _check_grads_fd(lib, q, rng.standard_normal(q["x"].shape),
+                        rng.standard_normal((2, 3, 4)), disc, rng)
+
+
+def pin_backward_gradient_of_a_linear_readout(lib):
+    """With no gate, D = 0 and h0 = 0, y is linear in x: sum(dy * y) equals
+    sum(dx * x) exactly (Euler's theorem for homogeneous functions)."""
+    rng = _rng(29)
+    p = _rand_problem(rng, 2, 11, 3, 5, with_d=False, with_z=False, with_h0=False)
+    dy = rng.standard_normal(p["x"].shape)
+    y, _ = oracle.scan(lib=lib, **p)
+    g = oracle.scan_bwd(lib=lib, dy=dy, **p)
+    assert abs(np.sum(dy * y) - np.sum(g["dx"] * p["x"])) <= 1e-12 * np.sum(np.abs(dy * y))
+    # y is also linear in B and in C separately
+    assert abs(np.sum(dy * y) - np.sum(g["dB"] * p["B"])) <= 1e-12 * np.sum(np.abs(dy * y))
+    assert abs(np.sum(dy * y) - np.sum(g["dC"] * p["C"])) <= 1e-12 * np.sum(np.abs(dy * y))
 
 
 def _slice_t(p, lo, hi):

@@ -27,6 +27,20 @@ MUTANTS = {
     "per_channel_A_of_channel_0": ("a_per_channel ? A + d : A + d * dstate",
                                    "a_per_channel ? A : A + d * dstate"),
     "per_channel_A_stepped": ("a_per_channel ? 0 : 1", "1"),
+    "bwd_coef_derivative_dropped": ("g->dcoef_dd = g->abar;", "g->dcoef_dd = 1.0;"),
+    "bwd_dcoef_da_sign": ("g->dcoef_da = (delta * g->abar - g->coef) / a;",
+                          "g->dcoef_da = (g->coef - delta * g->abar) / a;"),
+    "bwd_zero_A_limit_dropped": ("g->dcoef_da = 0.5 * delta * delta;", "g->dcoef_da = 0.0;"),
+    "bwd_adjoint_not_decayed": ("e[n] = g.abar * dh;", "e[n] = dh;"),
+    "bwd_dC_from_previous_state": ("dC_acc[bc + n] += dp * h_t[n];",
+                                   "dC_acc[bc + n] += dp * h_prev[n];"),
+    "bwd_dB_without_coef": ("dB_acc[bc + n] += dh * g.coef * xv;", "dB_acc[bc + n] += dh * xv;"),
+    "bwd_gate_derivative_is_sigmoid": ("return sg * (1.0 + v * (1.0 - sg));", "return sg;"),
+    "bwd_dh_last_ignored": ("e[n] = dh_last_row ? dh_last_row[n] : 0.0;", "e[n] = 0.0;"),
+    "bwd_skip_in_dx_dropped": ("double dxv = dp * dval, ddv = 0.0;",
+                               "double dxv = 0.0, ddv = 0.0;"),
+    "bwd_ddelta_uses_new_state": ("ddv += dh * (g.dabar_dd * h_prev[n]",
+                                  "ddv += dh * (g.dabar_dd * h_t[n]"),
     "no_decay": ("h[n] = abar * h[n] + bcoef", "h[n] = h[n] + bcoef"),
     "previous_token_B_C": ("int64_t bc = (b * seqlen + t) * dstate;",
                            "int64_t bc = (b * seqlen + (t > 0 ? t - 1 : 0)) * dstate;"),

@@ -29,3 +29,16 @@ def test_zoh_entry_point(lib):
     abar, c = oracle.zoh(0.1, -2.0)
     assert abar == math.exp(-0.2) and abs(c - (math.exp(-0.2) - 1) / -2.0) < 1e-16
     assert oracle.zoh(0.25, 0.0) == (1.0, 0.25)
+
+
+def test_backward_thread_count_changes_only_rounding(lib):
+    import numpy as np
+    rng = np.random.default_rng(4)
+    p = oracle_pins._rand_problem(rng, 2, 40, 19, 16)
+    dy = rng.standard_normal(p["x"].shape)
+    g1 = oracle.scan_bwd(nthreads=1, lib=lib, dy=dy, **p)
+    g8 = oracle.scan_bwd(nthreads=8, lib=lib, dy=dy, **p)
+    for k in ("dx", "ddelta", "dz", "dA", "dD", "dh0"):     # per channel: identical
+        assert np.array_equal(g1[k], g8[k]), k
+    for k in ("dB", "dC"):                                   # channel sums: rounding only
+        assert np.max(np.abs(g1[k] - g8[k])) <= 1e-13 * np.max(np.abs(g1[k]))

@@ -173,6 +173,47 @@ int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                     int waves_per_group, int nchunks, void *stream);
 
 /*
+ * Workspace of ssm_scan_bwd in bytes for these sizes (-1 for invalid sizes,
+ * 0 when nothing is needed).
+ */
+int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
+                                     int64_t dstate, int io_dtype);
+
+/*
+ * Backward of the selective scan: the gradients of a loss with respect to
+ * every input of ssm_scan_fwd_ex, given dy = dL/dy and dh_last = dL/dh_last.
+ * The states are recomputed from the inputs, not read from the forward pass
+ * (paperlens tutorial, section on the hardware-aware algorithm: the backward
+ * recomputes what the forward kept on chip).  The derivative is the chain
+ * rule on the recurrence of ssm_scan_fwd (ultralytics glossary, "SSMの仕組み";
+ * paperlens tutorial, eq. (2) and the selection section).
+ *   inputs      : as ssm_scan_fwd_ex (a_per_channel, discretization select
+ *                 the variant; h0 NULL => zeros).
+ *   dy          : [batch, seqlen, dim] io_dtype.
+ *   dh_last     : [batch, dim, dstate] fp32, NULL => 0.
+ *   dx, ddelta  : [batch, seqlen, dim] io_dtype outputs.
+ *   dz          : [batch, seqlen, dim] io_dtype; required when z is given,
+ *                 must be NULL when it is not.
+ *   dA          : fp32, shape of A ([dim, dstate], or [dim] when
+ *                 a_per_channel), summed over batch and time.
+ *   dB, dC      : [batch, seqlen, dstate] io_dtype, summed over channels.
+ *   dD          : [dim] fp32, NULL => not written (computed with D = 0 when
+ *                 Dskip is NULL).
+ *   dh0         : [batch, dim, dstate] fp32, NULL => not written.
+ *   workspace   : at least ssm_scan_bwd_workspace_bytes(...) bytes.
+ * Results are deterministic: every sum runs in a fixed order.  Outputs must
+ * not alias inputs, each other or the workspace.  seqlen == 0 writes dA = 0,
+ * dD = 0 and dh0 = dh_last (or 0).  dstate other than 16:
+ * SSM_ERR_UNSUPPORTED.  Returns an SSM_* status.
+ */
+int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 const void *x, const void *delta, const float *A, int a_per_channel,
+                 int discretization, const void *B, const void *C, const float *Dskip,
+                 const void *z, const float *h0, const void *dy, const float *dh_last,
+                 void *dx, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
+                 float *dh0, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Selective scan with its prologue fused in: the two steps that come right
  * before the scan in a Mamba block are computed on the way into the kernel
  * instead of in a separate pass over HBM.

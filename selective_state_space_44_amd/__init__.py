@@ -48,6 +48,9 @@ SIGNATURES = {
     "ssm_scan_fwd_fused": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int, _vp,
                                   _vp] + [_vp] * 8 + [_vp, _sz, _int, _int, _vp]),
     "ssm_decode_step": (_int, [_i64, _i64, _i64, _int] + [_vp] * 9 + [_vp]),
+    "ssm_scan_bwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _int]),
+    "ssm_scan_bwd": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
+                     + [_vp] * 15 + [_vp, _sz, _vp]),
 }
 
 _lock = threading.Lock()
@@ -295,3 +298,102 @@ def decode_step(h, x, delta, A, B, C, D=None, z=None, out=None):
                                         _ptr(z), _ptr(y), _stream(device))
     _check(st, "ssm_decode_step")
     return y
+
+
+def scan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16,
+                             dtype: torch.dtype = torch.bfloat16) -> int:
+    n = load_library().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, _io_code(dtype))
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None,
+             discretization: str = "zoh", need_dD: bool = True, need_dh0: bool = True,
+             workspace=None):
+    """Gradients of the scan for upstream dy [batch, L, dim] (and dh_last
+    [batch, dim, dstate] float32).  Inputs as ``scan_fwd``.  Returns a dict:
+    dx, ddelta, dz (None without z) [batch, L, dim] and dB, dC [batch, L,
+    dstate] in the I/O dtype; dA (shape of A), dD [dim] (None unless
+    need_dD), dh0 [batch, dim, dstate] (None unless need_dh0) in float32."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a [batch, seqlen, dim] tensor")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    batch, seqlen, dim = x.shape
+    if discretization not in ("zoh", "euler"):
+        raise ValueError("discretization must be 'zoh' or 'euler'")
+    if not isinstance(A, torch.Tensor) or A.dim() not in (1, 2):
+        raise ValueError("A must be a [dim, dstate] or [dim] tensor")
+    if not isinstance(B, torch.Tensor) or B.dim() != 3:
+        raise ValueError("B must be a [batch, seqlen, dstate] tensor")
+    per_channel = A.dim() == 1
+    dstate = B.shape[2] if per_channel else A.shape[1]
+    io = x.dtype
+    code = _io_code(io)
+    _require(x, "x", (batch, seqlen, dim), io, device)
+    _require(delta, "delta", (batch, seqlen, dim), io, device)
+    _require(A, "A", (dim,) if per_channel else (dim, dstate), torch.float32, device)
+    _require(B, "B", (batch, seqlen, dstate), io, device)
+    _require(C, "C", (batch, seqlen, dstate), io, device)
+    _require(D, "D", (dim,), torch.float32, device)
+    _require(z, "z", (batch, seqlen, dim), io, device)
+    _require(h0, "h0", (batch, dim, dstate), torch.float32, device)
+    _require(dy, "dy", (batch, seqlen, dim), io, device)
+    _require(dh_last, "dh_last", (batch, dim, dstate), torch.float32, device)
+    if delta is None or C is None or dy is None:
+        raise ValueError("delta, C and dy are required")
+    g = {
+        "dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+        "dz": torch.empty_like(x) if z is not None else None,
+        "dA": torch.empty_like(A), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+        "dD": torch.empty(dim, dtype=torch.float32, device=device) if need_dD else None,
+        "dh0": (torch.empty((batch, dim, dstate), dtype=torch.float32, device=device)
+                if need_dh0 else None),
+    }
+    lib = load_library()
+    nbytes = lib.ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, code)
+    if nbytes < 0:
+        raise ValueError("invalid sizes")
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_scan_bwd(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A),
+                          int(per_channel),
+                          SSM_DISC_EULER if discretization == "euler" else SSM_DISC_ZOH,
+                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
+                          _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                          _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                          _ptr(g["dh0"]), _ptr(workspace), ws_bytes, _stream(device))
+    _check(st, "ssm_scan_bwd")
+    return g
+
+
+class SelectiveScan(torch.autograd.Function):
+    """Autograd wrapper: forward = ``scan_fwd`` (returns y and h_last),
+    backward = ``scan_bwd``; both run the HIP kernels only.
+
+    ``y, h_last = SelectiveScan.apply(x, delta, A, B, C, D, z, h0, discretization)``
+    (D, z, h0 may be None)."""
+
+    @staticmethod
+    def forward(ctx, x, delta, A, B, C, D, z, h0, discretization="zoh"):
+        y, h_last = scan_fwd(x, delta, A, B, C, D, z, h0, return_last_state=True,
+                             discretization=discretization)
+        ctx.save_for_backward(x, delta, A, B, C, D, z, h0)
+        ctx.discretization = discretization
+        return y, h_last
+
+    @staticmethod
+    def backward(ctx, dy, dh_last):
+        x, delta, A, B, C, D, z, h0 = ctx.saved_tensors
+        if dy is None:
+            dy = torch.zeros_like(x)
+        g = scan_bwd(x, delta, A, B, C, D, z, h0, dy=dy.contiguous(),
+                     dh_last=None if dh_last is None else dh_last.contiguous(),
+                     discretization=ctx.discretization,
+                     need_dD=D is not None and ctx.needs_input_grad[5],
+                     need_dh0=h0 is not None and ctx.needs_input_grad[7])
+        return (g["dx"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["dh0"],
+                None)

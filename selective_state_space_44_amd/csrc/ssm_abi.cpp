@@ -306,3 +306,128 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, fl
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward of the scan
+// ---------------------------------------------------------------------------
+namespace {
+
+// Chunk length and count of the backward plan: chunks of at most
+// ssm::kBwdChunk steps, starting on tile boundaries.
+void bwd_plan(int64_t seqlen, int64_t* chunk_len, int* nchunks) {
+  const int64_t tile = ssm::scan_tile_steps();
+  const int64_t k = std::max<int64_t>(1, (seqlen + ssm::kBwdChunk - 1) / ssm::kBwdChunk);
+  int64_t len = std::max<int64_t>(1, (seqlen + k - 1) / k);
+  len = (len + tile - 1) / tile * tile;
+  *chunk_len = len;
+  *nchunks = (int)std::max<int64_t>(1, (seqlen + len - 1) / len);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
+                                     int64_t dstate, int io_dtype) {
+  if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype)) return -1;
+  if (batch == 0 || dim == 0 || seqlen == 0) return 0;
+  int64_t len;
+  int K;
+  bwd_plan(seqlen, &len, &K);
+  return (int64_t)ssm::bwd_workspace_layout(batch, seqlen, dim, K).total;
+}
+
+int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 const void* x, const void* delta, const float* A, int a_per_channel,
+                 int discretization, const void* B, const void* C, const float* Dskip,
+                 const void* z, const float* h0, const void* dy, const float* dh_last,
+                 void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                 float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype)) return SSM_ERR_INVALID_ARG;
+  if (a_per_channel != 0 && a_per_channel != 1) return SSM_ERR_INVALID_ARG;
+  if (discretization != SSM_DISC_ZOH && discretization != SSM_DISC_EULER)
+    return SSM_ERR_INVALID_ARG;
+  if (dstate != kDState) return SSM_ERR_UNSUPPORTED;
+  if (!A || !dA) return SSM_ERR_INVALID_ARG;
+  if ((z == nullptr) != (dz == nullptr)) return SSM_ERR_INVALID_ARG;
+  if (seqlen > 0 && batch > 0 && dim > 0 &&
+      (!x || !delta || !B || !C || !dy || !dx || !ddelta || !dB || !dC))
+    return SSM_ERR_INVALID_ARG;
+  const void* ins[] = {x, delta, A, B, C, Dskip, z, h0, dy, dh_last};
+  const void* outs[] = {dx, ddelta, dA, dB, dC, dD, dz, dh0};
+  for (const void* o : outs) {
+    if (!o) continue;
+    for (const void* in : ins)
+      if (in == o) return SSM_ERR_INVALID_ARG;
+    int same = 0;
+    for (const void* o2 : outs) same += (o2 == o);
+    if (same > 1) return SSM_ERR_INVALID_ARG;
+  }
+  if (!all_aligned(x, delta, A, B, C, Dskip, z, h0, dy, dh_last, workspace) ||
+      !all_aligned(dx, ddelta, dA, dB, dC, dD, dz, dh0))
+    return SSM_ERR_INVALID_ARG;
+  if (batch > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  auto s = static_cast<hipStream_t>(stream);
+  if (dim == 0) return SSM_OK;
+  const int64_t na = a_per_channel ? dim : dim * kDState;
+  if (batch == 0 || seqlen == 0) {
+    // no steps: dA = dD = 0, dh0 = dh_last (or 0)
+    hipError_t e = ssm::launch_copy_state(nullptr, dA, na, s);
+    if (e == hipSuccess && dD) e = ssm::launch_copy_state(nullptr, dD, dim, s);
+    if (e == hipSuccess && dh0 && batch > 0)
+      e = ssm::launch_copy_state(dh_last, dh0, batch * dim * kDState, s);
+    return hip_status(e);
+  }
+  int64_t chunk_len;
+  int K;
+  bwd_plan(seqlen, &chunk_len, &K);
+  if (K > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  const ssm::BwdWorkspace w = ssm::bwd_workspace_layout(batch, seqlen, dim, K);
+  if (!workspace || workspace_bytes < w.total) return SSM_ERR_WORKSPACE;
+  for (const void* in : ins)
+    if (in && in == workspace) return SSM_ERR_INVALID_ARG;
+
+  char* base = static_cast<char*>(workspace);
+  ssm::BwdArgs a{};
+  ssm::ScanArgs& f = a.f;
+  f.x = x;
+  f.delta = delta;
+  f.A = A;
+  f.B = B;
+  f.C = C;
+  f.Dskip = Dskip;
+  f.z = z;
+  f.h0 = h0;
+  f.seqlen = seqlen;
+  f.chunk_len = chunk_len;
+  f.dim = (int)dim;
+  f.batch = (int)batch;
+  f.nchunks = K;
+  f.a_per_channel = a_per_channel;
+  f.euler = discretization == SSM_DISC_EULER ? 1 : 0;
+  if (K > 1) {
+    f.ws_hloc = reinterpret_cast<float*>(base + w.fwd.hloc_off);
+    f.ws_hin = reinterpret_cast<float*>(base + w.fwd.hin_off);
+    f.ws_sdelta = reinterpret_cast<double*>(base + w.fwd.sdelta_off);
+    a.ws_eloc = reinterpret_cast<float*>(base + w.rev_base + w.rev.hloc_off);
+    a.ws_ein = reinterpret_cast<float*>(base + w.rev_base + w.rev.hin_off);
+    a.ws_sdr = reinterpret_cast<double*>(base + w.rev_base + w.rev.sdelta_off);
+  }
+  a.ws_pdB = reinterpret_cast<float*>(base + w.pdB_off);
+  a.ws_pdC = reinterpret_cast<float*>(base + w.pdC_off);
+  a.ws_pdA = reinterpret_cast<float*>(base + w.pdA_off);
+  a.ws_pdD = reinterpret_cast<float*>(base + w.pdD_off);
+  a.dy = dy;
+  a.dh_last = dh_last;
+  a.dx = dx;
+  a.ddelta = ddelta;
+  a.dz = dz;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = dD;
+  a.dh0 = dh0;
+  return hip_status(ssm::launch_scan_bwd(a, io_dtype == SSM_DTYPE_BF16, s));
+}
+
+}  // extern "C"

@@ -76,6 +76,48 @@ ScanWorkspace scan_workspace_layout(int64_t batch, int64_t dim, int nchunks);
 hipError_t launch_scan(const ScanArgs& a, bool io_bf16, int waves_per_group, int phase,
                        hipStream_t stream);
 
+// Enqueue the cross-chunk composition alone: ws_in[c] = state entering chunk
+// c, from init (nullable = 0) and each chunk's local result ws_loc and delta
+// sum ws_sdelta (layouts as ScanArgs).  reverse: from the last chunk to the
+// first.
+hipError_t launch_carry(const float* A, int a_per_channel, const float* init,
+                        const float* ws_loc, const double* ws_sdelta, float* ws_in, int batch,
+                        int dim, int nchunks, bool reverse, hipStream_t stream);
+
+// Backward of the scan.  Forward inputs as ScanArgs (x, delta, A, B, C,
+// Dskip, z, h0, variant flags; chunk_len <= kBwdChunk, nchunks chunks);
+// dy, dh_last (nullable) the upstream gradients; outputs dx, ddelta, dz
+// (IO type, dz only with z), dA (fp32, [dim, 16] or [dim]), dB, dC (IO type),
+// dD, dh0 (fp32, nullable).
+constexpr int kBwdChunk = 64;
+struct BwdArgs {
+  ScanArgs f;
+  const void* dy;
+  const float* dh_last;
+  void* dx;
+  void* ddelta;
+  void* dz;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;
+  float* dh0;
+  // workspace pieces
+  float* ws_eloc;     // [batch, nchunks, dim, 16]  chunk-local adjoint from zero
+  float* ws_ein;      // [batch, nchunks, dim, 16]  adjoint entering each chunk from the right
+  double* ws_sdr;     // [batch, nchunks, dim]      delta sum of each chunk
+  float* ws_pdB;      // [batch, groups, seqlen, 16] per 64-channel group
+  float* ws_pdC;      // [batch, groups, seqlen, 16]
+  float* ws_pdA;      // [batch, nchunks, dim, 16]
+  float* ws_pdD;      // [batch, nchunks, dim]
+};
+struct BwdWorkspace {
+  ScanWorkspace fwd, rev;
+  size_t rev_base, pdB_off, pdC_off, pdA_off, pdD_off, total;
+};
+BwdWorkspace bwd_workspace_layout(int64_t batch, int64_t seqlen, int64_t dim, int nchunks);
+hipError_t launch_scan_bwd(const BwdArgs& a, bool io_bf16, hipStream_t stream);
+
 // Enqueue the seqlen == 0 case: h_last = h0 (or zeros).
 hipError_t launch_copy_state(const float* h0, float* h_last, int64_t count,
                              hipStream_t stream);

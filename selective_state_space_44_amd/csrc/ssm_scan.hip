@@ -983,10 +983,16 @@ void scan_chunk_state_kernel(
 // combines them with a Hillis-Steele scan over lane shuffles (log2 S steps).
 // Rounds continue until all nchunks - 1 maps are applied.
 // ---------------------------------------------------------------------------
+//
+// With `reverse` set the same composition runs from the last chunk to the
+// first (chunk c is addressed as nchunks - 1 - c): the backward pass uses it
+// for the adjoint of the state, which flows from the end of the sequence to
+// its start with the same per-chunk decay.
 __global__ __launch_bounds__(256) void scan_carry_kernel(
     const float* __restrict__ A, const float* __restrict__ h0,
     const float* __restrict__ ws_hloc, const double* __restrict__ ws_sdelta,
-    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int seg_log2, int a_scalar) {
+    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int seg_log2, int a_scalar,
+    int reverse) {
   const int S = 1 << seg_log2;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t seg = gid >> seg_log2;
@@ -1000,14 +1006,15 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(
   const int d = (int)(bd % dim);
   const int64_t b = bd / dim;
   const float A2 = A[a_scalar ? (size_t)d : (size_t)d * kDState + n] * kLog2e;
-  auto at = [&](int c) { return (((size_t)b * nchunks + c) * dim + d) * kDState + n; };
+  auto ci = [&](int c) { return reverse ? nchunks - 1 - c : c; };
+  auto at = [&](int c) { return (((size_t)b * nchunks + ci(c)) * dim + d) * kDState + n; };
   float h = (h0 && valid) ? h0[segc] : 0.0f;
   if (j == 0 && valid) ws_hin[at(0)] = h;
   for (int base = 0; base < nchunks - 1; base += S) {
     const int c = base + j;  // this lane's map: entering state of chunk c -> of chunk c + 1
     float P = 1.0f, H = 0.0f;
     if (c < nchunks - 1 && valid) {
-      const size_t cd = ((size_t)b * nchunks + c) * dim + d;
+      const size_t cd = ((size_t)b * nchunks + ci(c)) * dim + d;
       P = fast_exp2((float)((double)A2 * ws_sdelta[cd]));
       H = ws_hloc[cd * kDState + n];
     }
@@ -1054,7 +1061,7 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
     const int64_t threads = (int64_t)a.batch * a.dim * kDState << seg_log2;
     hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        stream, a.A, a.h0, a.ws_hloc, a.ws_sdelta, a.ws_hin, a.batch, a.dim,
-                       a.nchunks, seg_log2, (V & kScalarA) ? 1 : 0);
+                       a.nchunks, seg_log2, (V & kScalarA) ? 1 : 0, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1112,6 +1119,19 @@ hipError_t launch_scan_io(const ScanArgs& a, int G, int phase, hipStream_t strea
 }  // namespace
 
 int scan_tile_steps() { return kChunkAlign; }
+
+hipError_t launch_carry(const float* A, int a_per_channel, const float* init,
+                        const float* ws_loc, const double* ws_sdelta, float* ws_in, int batch,
+                        int dim, int nchunks, bool reverse, hipStream_t stream) {
+  if (nchunks <= 1) return hipSuccess;
+  int seg_log2 = 0;
+  while ((1 << seg_log2) < nchunks - 1 && seg_log2 < 6) ++seg_log2;
+  const int64_t threads = (int64_t)batch * dim * kDState << seg_log2;
+  hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, A, init, ws_loc, ws_sdelta, ws_in, batch, dim, nchunks, seg_log2,
+                     a_per_channel, reverse ? 1 : 0);
+  return hipGetLastError();
+}
 
 ScanWorkspace scan_workspace_layout(int64_t batch, int64_t dim, int nchunks) {
   auto align = [](size_t v) { return (v + 255) & ~size_t(255); };

@@ -17,6 +17,8 @@ import oracle
 FP32_TOL = 1e-4
 BF16_REL = 2e-2
 BF16_FLOOR = 1e-2
+# gradients in fp32: per element, relative to |ref| + rms of the tensor
+GRAD_FP32_TOL = 1e-4
 
 
 def to_f64(t):
@@ -81,3 +83,28 @@ def oracle_scan(inp: dict, channels=None, nthreads: int = 0, discretization: str
 def pick(t, channels, axis):
     idx = torch.as_tensor(channels, device=t.device, dtype=torch.long)
     return to_f64(t.index_select(axis, idx))
+
+
+def check_grad(got, ref, io_dtype, what):
+    """Gradients: fp32 outputs |err| <= GRAD_FP32_TOL * (|ref| + rms(ref));
+    bf16 outputs as check_y's bf16 bound.  The rms term is the scale of the
+    tensor: reduced gradients (sums over channels or time) and the adjoint
+    carry cancellation, so a pure relative bound is undefined near zero."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    if io_dtype == torch.float32:
+        bound = GRAD_FP32_TOL * (np.abs(ref) + rms)
+    else:
+        bound = BF16_REL * np.maximum(np.abs(ref), BF16_FLOOR * rms)
+    bound = np.maximum(bound, 1e-30)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err / bound, 0)), ref.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {ref.size} outside tolerance; "
+                             f"worst at {i}: got {got[i]!r} ref {ref[i]!r} bound {bound[i]!r}")
+    return float(np.max(err / bound))

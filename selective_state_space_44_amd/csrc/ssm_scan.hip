@@ -975,60 +975,54 @@ void scan_chunk_state_kernel(
 
 // ---------------------------------------------------------------------------
 // Carry pass 2: the state entering every chunk.  Chunk c maps its entering
-// state h to P_c h + hloc_c; the maps compose associatively,
-// (P2, H2) o (P1, H1) = (P2 P1, P2 H1 + H2), so the entering states are an
-// exclusive prefix scan of the maps applied to h0 (paperlens tutorial,
-// parallel-scan section).  Each (b, d, n) owns a segment of S = 2^seg_log2
-// lanes of a wave; lane j holds map j of a round of S maps, and the segment
-// combines them with a Hillis-Steele scan over lane shuffles (log2 S steps).
-// Rounds continue until all nchunks - 1 maps are applied.
-// ---------------------------------------------------------------------------
+// state h to P_c h + hloc_c with P_c = exp(A * sum of delta over chunk c) (the
+// product of the chunk's Abar as one exponential); applying the maps in
+// order from h0 gives every chunk's entering state (paperlens tutorial,
+// parallel-scan section: the update composes associatively).  One thread per
+// (b, d, n) walks the chunks in order; consecutive threads take consecutive
+// (d, n), so every load and store of a step is one coalesced row, and the
+// loads of four steps are issued before their updates.
 //
 // With `reverse` set the same composition runs from the last chunk to the
 // first (chunk c is addressed as nchunks - 1 - c): the backward pass uses it
 // for the adjoint of the state, which flows from the end of the sequence to
 // its start with the same per-chunk decay.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scan_carry_kernel(
     const float* __restrict__ A, const float* __restrict__ h0,
     const float* __restrict__ ws_hloc, const double* __restrict__ ws_sdelta,
-    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int seg_log2, int a_scalar,
-    int reverse) {
-  const int S = 1 << seg_log2;
+    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int a_scalar, int reverse) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t seg = gid >> seg_log2;
-  const int j = (int)(gid & (S - 1));
   const int64_t total = (int64_t)batch * dim * kDState;
-  // segments past the end still take part in the shuffles, with no memory access
-  const bool valid = seg < total;
-  const int64_t segc = valid ? seg : 0;
-  const int n = (int)(segc % kDState);
-  const int64_t bd = segc / kDState;
+  if (gid >= total) return;
+  const int n = (int)(gid % kDState);
+  const int64_t bd = gid / kDState;
   const int d = (int)(bd % dim);
   const int64_t b = bd / dim;
-  const float A2 = A[a_scalar ? (size_t)d : (size_t)d * kDState + n] * kLog2e;
-  auto ci = [&](int c) { return reverse ? nchunks - 1 - c : c; };
-  auto at = [&](int c) { return (((size_t)b * nchunks + ci(c)) * dim + d) * kDState + n; };
-  float h = (h0 && valid) ? h0[segc] : 0.0f;
-  if (j == 0 && valid) ws_hin[at(0)] = h;
-  for (int base = 0; base < nchunks - 1; base += S) {
-    const int c = base + j;  // this lane's map: entering state of chunk c -> of chunk c + 1
-    float P = 1.0f, H = 0.0f;
-    if (c < nchunks - 1 && valid) {
-      const size_t cd = ((size_t)b * nchunks + ci(c)) * dim + d;
-      P = fast_exp2((float)((double)A2 * ws_sdelta[cd]));
-      H = ws_hloc[cd * kDState + n];
+  const double A2 = (double)(A[a_scalar ? (size_t)d : (size_t)d * kDState + n] * kLog2e);
+  auto cd = [&](int c) {
+    return ((size_t)b * nchunks + (reverse ? nchunks - 1 - c : c)) * dim + d;
+  };
+  float h = h0 ? h0[gid] : 0.0f;
+  ws_hin[cd(0) * kDState + n] = h;
+  constexpr int U = 4;
+  int c = 0;
+  for (; c + U <= nchunks - 1; c += U) {
+    float P[U], H[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      P[u] = fast_exp2((float)(A2 * ws_sdelta[cd(c + u)]));
+      H[u] = ws_hloc[cd(c + u) * kDState + n];
     }
-    for (int off = 1; off < S; off <<= 1) {  // inclusive scan inside the segment
-      const float Pu = __shfl_up(P, off, S);
-      const float Hu = __shfl_up(H, off, S);
-      if (j >= off) {
-        H = __builtin_fmaf(P, Hu, H);
-        P = P * Pu;
-      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      h = __builtin_fmaf(P[u], h, H[u]);
+      ws_hin[cd(c + u + 1) * kDState + n] = h;
     }
-    const float hn = __builtin_fmaf(P, h, H);
-    if (c < nchunks - 1 && valid) ws_hin[at(c + 1)] = hn;
-    h = __shfl(hn, S - 1, S);  // state after the round's last map
+  }
+  for (; c < nchunks - 1; ++c) {
+    h = __builtin_fmaf(fast_exp2((float)(A2 * ws_sdelta[cd(c)])), h, ws_hloc[cd(c) * kDState + n]);
+    ws_hin[cd(c + 1) * kDState + n] = h;
   }
 }
 
@@ -1056,12 +1050,10 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
                        a.dim, a.nchunks, a.pro);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int seg_log2 = 0;  // segment of lanes per (b, d, n): next power of two >= the map count
-    while ((1 << seg_log2) < a.nchunks - 1 && seg_log2 < 6) ++seg_log2;
-    const int64_t threads = (int64_t)a.batch * a.dim * kDState << seg_log2;
+    const int64_t threads = (int64_t)a.batch * a.dim * kDState;
     hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        stream, a.A, a.h0, a.ws_hloc, a.ws_sdelta, a.ws_hin, a.batch, a.dim,
-                       a.nchunks, seg_log2, (V & kScalarA) ? 1 : 0, 0);
+                       a.nchunks, (V & kScalarA) ? 1 : 0, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1124,11 +1116,9 @@ hipError_t launch_carry(const float* A, int a_per_channel, const float* init,
                         const float* ws_loc, const double* ws_sdelta, float* ws_in, int batch,
                         int dim, int nchunks, bool reverse, hipStream_t stream) {
   if (nchunks <= 1) return hipSuccess;
-  int seg_log2 = 0;
-  while ((1 << seg_log2) < nchunks - 1 && seg_log2 < 6) ++seg_log2;
-  const int64_t threads = (int64_t)batch * dim * kDState << seg_log2;
+  const int64_t threads = (int64_t)batch * dim * kDState;
   hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, A, init, ws_loc, ws_sdelta, ws_in, batch, dim, nchunks, seg_log2,
+                     stream, A, init, ws_loc, ws_sdelta, ws_in, batch, dim, nchunks,
                      a_per_channel, reverse ? 1 : 0);
   return hipGetLastError();
 }

@@ -30,11 +30,9 @@
 //   dx = dp D + sum_n dh coef B, ddelta = sum_n dh (A Abar h_{t-1} + dcoef/ddelta B x),
 //   dA += dh (delta Abar h_{t-1} + dcoef/dA B x), dB += dh coef x, dC += dp h_t,
 //   dD += dp x, dh0 = e_0.
-// Zero-order hold: coef = (Abar - 1)/A, dcoef/ddelta = Abar,
-//   dcoef/dA = delta^2 psi(u), u = delta A, psi(u) = (u e^u - e^u + 1)/u^2;
-//   for |u| < 1/4 coef and psi come from their Taylor series (no cancellation,
-//   and A = 0 needs no special case).  Euler rule: coef = delta,
-//   dcoef/ddelta = 1, dcoef/dA = 0.
+// Zero-order hold: coef = (Abar - 1)/A (delta where A == 0), dcoef/ddelta =
+//   Abar, dcoef/dA = delta^2 psi(delta A) with psi(u) = (u e^u - e^u + 1)/u^2.
+//   Euler rule: coef = delta, dcoef/ddelta = 1, dcoef/dA = 0.
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -42,49 +40,13 @@ namespace ssm {
 namespace {
 
 constexpr int kBT = 8;                   // steps per tile
+// Resident waves per SIMD the main pass is compiled for (register budget);
+// its LDS (tile entry states, staging, partial sums) allows two 4-wave blocks
+// per CU.
+constexpr int kBwdWavesPerSimd = 2;
 constexpr int kBQT = kBwdChunk / kBT;    // tiles per chunk
 constexpr int kVarScalarA = 1;           // A is [dim]
 constexpr int kVarEuler = 2;             // coef = delta
-
-// Abar, coef = Bbar/B and the derivatives of coef for one (step, state).
-struct Disc {
-  float a, coef, dcoef_dd, dcoef_da;
-};
-
-template <int V>
-__device__ __forceinline__ Disc disc(float dv, float Av, float A2) {
-  Disc r;
-  r.a = fast_exp2(dv * A2);
-  if constexpr ((V & kVarEuler) != 0) {
-    r.coef = dv;
-    r.dcoef_dd = 1.0f;
-    r.dcoef_da = 0.0f;
-  } else {
-    const float u = dv * Av;
-    // series: (e^u - 1)/u = sum_k u^k / (k+1)!        (k = 0..6)
-    //         psi(u)      = sum_m (m-1) u^(m-2) / m!  (m = 2..8)
-    // truncation below 1e-8 relative for |u| < 1/4
-    float s1 = __builtin_fmaf(u, 1.0f / 5040.0f, 1.0f / 720.0f);
-    s1 = __builtin_fmaf(u, s1, 1.0f / 120.0f);
-    s1 = __builtin_fmaf(u, s1, 1.0f / 24.0f);
-    s1 = __builtin_fmaf(u, s1, 1.0f / 6.0f);
-    s1 = __builtin_fmaf(u, s1, 0.5f);
-    s1 = __builtin_fmaf(u, s1, 1.0f);
-    float s2 = __builtin_fmaf(u, 1.0f / 5760.0f, 1.0f / 840.0f);
-    s2 = __builtin_fmaf(u, s2, 1.0f / 144.0f);
-    s2 = __builtin_fmaf(u, s2, 1.0f / 30.0f);
-    s2 = __builtin_fmaf(u, s2, 1.0f / 8.0f);
-    s2 = __builtin_fmaf(u, s2, 1.0f / 3.0f);
-    s2 = __builtin_fmaf(u, s2, 0.5f);
-    const bool small = __builtin_fabsf(u) < 0.25f;
-    const float iA = __builtin_amdgcn_rcpf(Av);
-    const float coef_d = (r.a - 1.0f) * iA;
-    r.coef = small ? dv * s1 : coef_d;
-    r.dcoef_dd = r.a;
-    r.dcoef_da = small ? dv * dv * s2 : (dv * r.a - coef_d) * iA;
-  }
-  return r;
-}
 
 struct BwdChunk {
   int lane, g, b, c, d, d0;
@@ -267,16 +229,14 @@ __device__ __forceinline__ void lane_sum(float* v, int lane) {
   }
 }
 
-// Opaque copy: keeps the compiler from merging a recomputation with an
-// earlier identical one (which would hold every intermediate in registers).
-__device__ __forceinline__ float fresh(float v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 // ---------------------------------------------------------------------------
 // Main backward pass.
 // ---------------------------------------------------------------------------
+// Materialises v at this point of the program.  Applied to running sums and
+// recomputed states each step: without it the compiler sinks those updates
+// to the end of the tile, keeping every step's operands alive (registers).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+
 template <int G>
 struct BwdSmem {
   static constexpr int NPL = kDState / G;
@@ -285,39 +245,62 @@ struct BwdSmem {
   float part[3][G][kBT][kWave];   // per-wave sums over its states: dx, ddelta, C.h
 };
 
-template <typename IO, int G, bool HAS_Z, int V>
-__global__ __launch_bounds__(kWave* G) void bwd_main_kernel(
-    const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
-    const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
-    const IO* __restrict__ z, const float* __restrict__ h0, const IO* __restrict__ dy,
-    const float* __restrict__ dh_last, const float* __restrict__ ws_hin,
-    const float* __restrict__ ws_ein, IO* __restrict__ dx, IO* __restrict__ ddelta,
-    IO* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ pdB,
-    float* __restrict__ pdC, float* __restrict__ pdA, float* __restrict__ pdD, int64_t seqlen,
-    int64_t chunk_len, int dim, int nchunks) {
+// coef = Bbar / B from Abar (the hold: (Abar - 1)/A, with the limit delta
+// where A == 0; Euler: delta).
+template <int V, bool ZERO_A>
+__device__ __forceinline__ float coef_of(float a, float dv, float iA) {
+  if constexpr ((V & kVarEuler) != 0) {
+    return dv;
+  } else if constexpr (ZERO_A) {
+    return __builtin_isinf(iA) ? dv : (a - 1.0f) * iA;
+  } else {
+    return __builtin_fmaf(a, iA, -iA);
+  }
+}
+
+// Input term Bbar * x of the forward recurrence from Abar and B x.
+template <int V, bool ZERO_A>
+__device__ __forceinline__ float input_term(float a, float dv, float iA, float bx) {
+  if constexpr ((V & kVarEuler) != 0 || ZERO_A) {
+    return coef_of<V, ZERO_A>(a, dv, iA) * bx;
+  } else {
+    const float q = bx * iA;
+    return __builtin_fmaf(a, q, -q);
+  }
+}
+
+// dcoef/dA of the hold: delta^2 psi(u), u = delta A,
+// psi(u) = (u e^u - e^u + 1) / u^2 = sum_m (m-1) u^(m-2) / m!.  The series
+// (to u^5, truncation < 1e-7 relative) is used for |u| < 1/4, where the
+// closed form (delta Abar - coef) / A would cancel; A == 0 gives delta^2 / 2.
+__device__ __forceinline__ float dcoef_da_hold(float dv, float Av, float a, float coef,
+                                               float iA) {
+  const float u = dv * Av;
+  float s2 = __builtin_fmaf(u, 1.0f / 5760.0f, 1.0f / 840.0f);
+  s2 = __builtin_fmaf(u, s2, 1.0f / 144.0f);
+  s2 = __builtin_fmaf(u, s2, 1.0f / 30.0f);
+  s2 = __builtin_fmaf(u, s2, 1.0f / 8.0f);
+  s2 = __builtin_fmaf(u, s2, 1.0f / 3.0f);
+  s2 = __builtin_fmaf(u, s2, 0.5f);
+  const float closed = __builtin_fmaf(dv, a, -coef) * iA;
+  // chosen with bit operations: as a conditional the compiler branches
+  // around the series, one divergent branch per (step, state)
+  const uint32_t m = 0u - (uint32_t)(__builtin_fabsf(u) < 0.25f);
+  return __uint_as_float((__float_as_uint(dv * dv * s2) & m) | (__float_as_uint(closed) & ~m));
+}
+
+template <typename IO, int G, bool HAS_Z, int V, bool ZERO_A>
+__device__ __forceinline__ void bwd_chunk(
+    BwdSmem<G>& sm, const BwdChunk& k, const IO* __restrict__ x, const IO* __restrict__ delta,
+    const IO* __restrict__ B, const IO* __restrict__ C, const IO* __restrict__ z,
+    const IO* __restrict__ dy, const float (&Af)[kDState / G], const float (&A2)[kDState / G],
+    const float (&iA)[kDState / G], float Dd, float (&h)[kDState / G], float (&e)[kDState / G],
+    float (&dA_acc)[kDState / G], float& dD_acc, IO* __restrict__ dx, IO* __restrict__ ddelta,
+    IO* __restrict__ dz, float* __restrict__ pdB, float* __restrict__ pdC, int64_t seqlen,
+    int dim) {
   constexpr int NPL = kDState / G;
-  __shared__ BwdSmem<G> sm;
-  const BwdChunk k = bwd_coords(blockIdx.y, dim, seqlen, chunk_len);
   const int n0 = k.g * NPL;
   const int groups = (dim + kWave - 1) / kWave;
-
-  float Af[NPL], A2[NPL], h[NPL], e[NPL], dA_acc[NPL];
-  load_A_bwd<NPL, V>(A, k.d, n0, Af, A2);
-  const size_t sidx = ((size_t)k.b * dim + k.d) * kDState + n0;
-  const size_t cidx = (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
-#pragma unroll
-  for (int n = 0; n < NPL; ++n) {
-    if (nchunks > 1) {
-      h[n] = ws_hin[cidx + n];
-      e[n] = ws_ein[cidx + n];
-    } else {
-      h[n] = h0 ? h0[sidx + n] : 0.0f;
-      e[n] = dh_last ? dh_last[sidx + n] : 0.0f;
-    }
-    dA_acc[n] = 0.0f;
-  }
-  const float Dd = Dskip ? Dskip[k.d] : 0.0f;
-  float dD_acc = 0.0f;
   const int nt = (int)((k.t1 - k.t0 + kBT - 1) / kBT);
 
   // tile entry states, recomputed forward through the chunk
@@ -334,8 +317,10 @@ __global__ __launch_bounds__(kWave* G) void bwd_main_kernel(
       const float xv = sm.st.x[s][k.lane], dv = sm.st.dl[s][k.lane];
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
-        const Disc q = disc<V>(dv, Af[n], A2[n]);
-        h[n] = __builtin_fmaf(q.a, h[n], q.coef * sm.st.b[s][n0 + n] * xv);
+        const float a = fast_exp2(dv * A2[n]);
+        h[n] = __builtin_fmaf(a, h[n],
+                              input_term<V, ZERO_A>(a, dv, iA[n], sm.st.b[s][n0 + n] * xv));
+        pin(h[n]);
       }
     }
   }
@@ -346,62 +331,85 @@ __global__ __launch_bounds__(kWave* G) void bwd_main_kernel(
     __syncthreads();
     stage_tile<IO, HAS_Z, false>(sm.st, x, delta, B, C, z, dy, k, seqlen, dim, ts, kWave * G);
     __syncthreads();
+    // the tile's states and Abar, recomputed from the tile entry state
     float hck[NPL], hs[kBT][NPL];
 #pragma unroll
     for (int n = 0; n < NPL; ++n) hck[n] = sm.ck[j][k.g][n][k.lane];
 #pragma unroll
     for (int s = 0; s < kBT; ++s) {
-      const float xv = sm.st.x[s][k.lane], dv = sm.st.dl[s][k.lane];
+      const float xv = sm.st.x[s][k.lane];
+      const float dv = sm.st.dl[s][k.lane];
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
-        const Disc q = disc<V>(dv, Af[n], A2[n]);
-        const float prev = s ? hs[s - 1][n] : hck[n];
-        hs[s][n] = __builtin_fmaf(q.a, prev, q.coef * sm.st.b[s][n0 + n] * xv);
+        const float a = fast_exp2(dv * A2[n]);
+        hs[s][n] = __builtin_fmaf(a, s ? hs[s - 1][n] : hck[n],
+                                  input_term<V, ZERO_A>(a, dv, iA[n], sm.st.b[s][n0 + n] * xv));
+        pin(hs[s][n]);
       }
     }
-    float vb[kBT * NPL];  // dB values [s][n] of this lane's channel
+    // the adjoint backwards through the tile, in two halves of kBT / 2 steps;
+    // after each half its dB values are summed over the wave's 64 channels
+    constexpr int HT = kBT / 2;
+    constexpr int NV = HT * NPL;  // 16 values per lane: lanes 4i..4i+3 end with value i
 #pragma unroll
-    for (int s = kBT - 1; s >= 0; --s) {
-      const float xv = fresh(sm.st.x[s][k.lane]), dv = fresh(sm.st.dl[s][k.lane]);
-      const float dpv = sm.st.dp[s][k.lane];
-      float dxp = 0.0f, ddp = 0.0f, sp = 0.0f;
+    for (int half = 1; half >= 0; --half) {
+      float vb[NV];
 #pragma unroll
-      for (int n = 0; n < NPL; ++n) {
-        const Disc q = disc<V>(dv, Af[n], A2[n]);
-        const float prev = s ? hs[s - 1][n] : hck[n];
-        const float Bn = sm.st.b[s][n0 + n], Cn = sm.st.c[s][n0 + n];
-        const float dh = __builtin_fmaf(dpv, Cn, e[n]);
-        const float ub = dh * Bn;
-        vb[s * NPL + n] = dh * q.coef * xv;
-        dxp = __builtin_fmaf(ub, q.coef, dxp);
-        ddp = __builtin_fmaf(dh * Af[n] * q.a, prev, __builtin_fmaf(ub * xv, q.dcoef_dd, ddp));
-        dA_acc[n] = __builtin_fmaf(dh * dv * q.a, prev,
-                                   __builtin_fmaf(ub * xv, q.dcoef_da, dA_acc[n]));
-        sp = __builtin_fmaf(Cn, hs[s][n], sp);
-        e[n] = q.a * dh;
+      for (int sh = HT - 1; sh >= 0; --sh) {
+        const int s = half * HT + sh;
+        const float xv = sm.st.x[s][k.lane];
+        const float dv = sm.st.dl[s][k.lane];
+        const float dpv = sm.st.dp[s][k.lane];
+        float dxp = 0.0f, ddp = 0.0f, sp = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+          const float a = fast_exp2(dv * A2[n]);
+          const float coef = coef_of<V, ZERO_A>(a, dv, iA[n]);
+          const float prev = s ? hs[s - 1][n] : hck[n];
+          const float Bn = sm.st.b[s][n0 + n], Cn = sm.st.c[s][n0 + n];
+          const float dh = __builtin_fmaf(dpv, Cn, e[n]);
+          const float dc = dh * coef;
+          const float ubx = dh * Bn * xv;
+          const float dhp = dh * prev;
+          vb[sh * NPL + n] = dc * xv;
+          pin(vb[sh * NPL + n]);
+          dxp = __builtin_fmaf(dc, Bn, dxp);
+          if constexpr ((V & kVarEuler) != 0) {
+            ddp = __builtin_fmaf(a * Af[n], dhp, ddp + ubx);
+            dA_acc[n] = __builtin_fmaf(dhp, dv * a, dA_acc[n]);
+          } else {
+            ddp = __builtin_fmaf(a, __builtin_fmaf(dhp, Af[n], ubx), ddp);
+            dA_acc[n] = __builtin_fmaf(dhp, dv * a, dA_acc[n]);
+            dA_acc[n] = __builtin_fmaf(ubx, dcoef_da_hold(dv, Af[n], a, coef, iA[n]), dA_acc[n]);
+          }
+          sp = __builtin_fmaf(Cn, hs[s][n], sp);
+          e[n] = a * dh;
+          pin(dA_acc[n]);
+        }
+        sm.part[0][k.g][s][k.lane] = dxp;
+        sm.part[1][k.g][s][k.lane] = ddp;
+        sm.part[2][k.g][s][k.lane] = sp;
+        dD_acc = __builtin_fmaf(dpv, xv, dD_acc);
+        pin(dD_acc);
       }
-      sm.part[0][k.g][s][k.lane] = dxp;
-      sm.part[1][k.g][s][k.lane] = ddp;
-      sm.part[2][k.g][s][k.lane] = sp;
-      dD_acc = __builtin_fmaf(dpv, xv, dD_acc);
+      lane_sum<NV, 32>(vb, k.lane);
+      const int s_o = half * HT + (k.lane >> 2) / NPL, n_o = (k.lane >> 2) % NPL;
+      const int64_t t_o = ts + s_o;
+      if (t_o < k.t1 && (k.lane & 3) == 0)
+        pdB[(((size_t)k.b * groups + blockIdx.x) * seqlen + t_o) * kDState + n0 + n_o] = vb[0];
     }
-    // dB, then dC = dp h_t: sums over the wave's 64 channels; afterwards
-    // lanes 2i and 2i + 1 hold value i
-    constexpr int NV = kBT * NPL;
-    static_assert(NV == kWave / 2, "lane sums assume 32 values per lane");
+    constexpr int NVC = kBT * NPL;
     const int s_out = (k.lane >> 1) / NPL, n_out = (k.lane >> 1) % NPL;
     const int64_t t_out = ts + s_out;
     const size_t p_out = (((size_t)k.b * groups + blockIdx.x) * seqlen + t_out) * kDState + n0 +
                          n_out;
     const bool w_out = t_out < k.t1 && (k.lane & 1) == 0;
-    lane_sum<NV, 32>(vb, k.lane);
-    if (w_out) pdB[p_out] = vb[0];
-    float vc[NV];
+    float vc[NVC];
 #pragma unroll
     for (int s = 0; s < kBT; ++s)
 #pragma unroll
       for (int n = 0; n < NPL; ++n) vc[s * NPL + n] = sm.st.dp[s][k.lane] * hs[s][n];
-    lane_sum<NV, 32>(vc, k.lane);
+    lane_sum<NVC, 32>(vc, k.lane);
     if (w_out) pdC[p_out] = vc[0];
     __syncthreads();
     // per (t, d) results: wave g finishes steps g, g + G, ...
@@ -422,6 +430,53 @@ __global__ __launch_bounds__(kWave* G) void bwd_main_kernel(
         io<IO>::store(dz + off, sm.st.gd[s][k.lane] * __builtin_fmaf(Dd, sm.st.x[s][k.lane], ssp));
     }
   }
+}
+
+template <typename IO, int G, bool HAS_Z, int V>
+__global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kBwdWavesPerSimd)))
+void bwd_main_kernel(
+    const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
+    const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
+    const IO* __restrict__ z, const float* __restrict__ h0, const IO* __restrict__ dy,
+    const float* __restrict__ dh_last, const float* __restrict__ ws_hin,
+    const float* __restrict__ ws_ein, IO* __restrict__ dx, IO* __restrict__ ddelta,
+    IO* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ pdB,
+    float* __restrict__ pdC, float* __restrict__ pdA, float* __restrict__ pdD, int64_t seqlen,
+    int64_t chunk_len, int dim, int nchunks) {
+  constexpr int NPL = kDState / G;
+  __shared__ BwdSmem<G> sm;
+  const BwdChunk k = bwd_coords(blockIdx.y, dim, seqlen, chunk_len);
+  const int n0 = k.g * NPL;
+
+  float Af[NPL], A2[NPL], iA[NPL], h[NPL], e[NPL], dA_acc[NPL];
+  load_A_bwd<NPL, V>(A, k.d, n0, Af, A2);
+  bool zero = false;
+#pragma unroll
+  for (int n = 0; n < NPL; ++n) {
+    iA[n] = 1.0f / Af[n];
+    zero |= Af[n] == 0.0f;
+  }
+  const size_t sidx = ((size_t)k.b * dim + k.d) * kDState + n0;
+  const size_t cidx = (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
+#pragma unroll
+  for (int n = 0; n < NPL; ++n) {
+    if (nchunks > 1) {
+      h[n] = ws_hin[cidx + n];
+      e[n] = ws_ein[cidx + n];
+    } else {
+      h[n] = h0 ? h0[sidx + n] : 0.0f;
+      e[n] = dh_last ? dh_last[sidx + n] : 0.0f;
+    }
+    dA_acc[n] = 0.0f;
+  }
+  const float Dd = Dskip ? Dskip[k.d] : 0.0f;
+  float dD_acc = 0.0f;
+  if (__builtin_amdgcn_ballot_w64(zero) != 0)
+    bwd_chunk<IO, G, HAS_Z, V, true>(sm, k, x, delta, B, C, z, dy, Af, A2, iA, Dd, h, e, dA_acc,
+                                     dD_acc, dx, ddelta, dz, pdB, pdC, seqlen, dim);
+  else
+    bwd_chunk<IO, G, HAS_Z, V, false>(sm, k, x, delta, B, C, z, dy, Af, A2, iA, Dd, h, e,
+                                      dA_acc, dD_acc, dx, ddelta, dz, pdB, pdC, seqlen, dim);
 
   if (k.active) {
     const size_t pa = (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;

@@ -89,7 +89,7 @@ hipError_t launch_carry(const float* A, int a_per_channel, const float* init,
 // dy, dh_last (nullable) the upstream gradients; outputs dx, ddelta, dz
 // (IO type, dz only with z), dA (fp32, [dim, 16] or [dim]), dB, dC (IO type),
 // dD, dh0 (fp32, nullable).
-constexpr int kBwdChunk = 64;
+constexpr int kBwdChunk = 32;
 struct BwdArgs {
   ScanArgs f;
   const void* dy;

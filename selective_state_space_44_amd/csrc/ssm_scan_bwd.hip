@@ -6,7 +6,7 @@
 // section on the hardware-aware algorithm); here that is done at two levels:
 //
 //   1. Forward chunk entry states: the sequence is cut into chunks of at most
-//      kBwdChunk = 64 steps and the forward scan's own carry passes (chunk
+//      kBwdChunk = 32 steps and the forward scan's own carry passes (chunk
 //      pre-pass + composition) give the state entering every chunk.
 //   2. Adjoint chunk entry values: the adjoint e_t = dL/dh_{t-1} flowing back
 //      through step t obeys e_t = Abar_t (e_{t+1} + dp_t C_t), a linear map
@@ -15,7 +15,7 @@
 //      same composition kernel, run from the last chunk to the first, gives
 //      the adjoint entering every chunk from the right.
 //   3. Main pass, one block per (64 channels, chunk, batch row), G waves
-//      splitting the 16 states: the chunk's tile entry states (8 tiles of 8
+//      splitting the 16 states: the chunk's tile entry states (4 tiles of 8
 //      steps) are recomputed once into LDS; then tiles are visited last to
 //      first, each tile's 8 states are recomputed into registers and the
 //      adjoint runs backwards through them, producing dx, ddelta, dz per
@@ -40,10 +40,12 @@ namespace ssm {
 namespace {
 
 constexpr int kBT = 8;                   // steps per tile
-// Resident waves per SIMD the main pass is compiled for (register budget);
-// its LDS (tile entry states, staging, partial sums) allows two 4-wave blocks
-// per CU.
-constexpr int kBwdWavesPerSimd = 2;
+// Resident waves per SIMD the main pass is compiled for (register budget,
+// at most 168 VGPRs); its LDS (tile entry states 16 KB, staging 9 KB, partial
+// sums 24 KB) allows three 4-wave blocks per CU.  Measured at the Mamba-2.8B
+// shape: 32-step chunks at three waves per SIMD take 0.80x the time of
+// 64-step chunks at two.
+constexpr int kBwdWavesPerSimd = 3;
 constexpr int kBQT = kBwdChunk / kBT;    // tiles per chunk
 constexpr int kVarScalarA = 1;           // A is [dim]
 constexpr int kVarEuler = 2;             // coef = delta
@@ -77,6 +79,20 @@ __device__ __forceinline__ void load_A_bwd(const float* A, int d, int n0, float 
   for (int n = 0; n < NPL; ++n) {
     Af[n] = (V & kVarScalarA) ? A[d] : A[(size_t)d * kDState + n0 + n];
     A2[n] = Af[n] * kLog2e;
+  }
+}
+
+// NPL consecutive floats of an LDS row (16-byte aligned) with b128 reads.
+template <int NPL>
+__device__ __forceinline__ void read_states(const float* p, float (&out)[NPL]) {
+  static_assert(NPL % 4 == 0, "b128 reads");
+#pragma unroll
+  for (int q = 0; q < NPL / 4; ++q) {
+    const float4 v = reinterpret_cast<const float4*>(p)[q];
+    out[4 * q] = v.x;
+    out[4 * q + 1] = v.y;
+    out[4 * q + 2] = v.z;
+    out[4 * q + 3] = v.w;
   }
 }
 
@@ -185,10 +201,12 @@ __global__ __launch_bounds__(kWave* G) void bwd_chunk_adjoint_kernel(
       const float dv = st.dl[s][k.lane];
       const float dpv = st.dp[s][k.lane];
       tsum += dv;
+      float cn[NPL];
+      read_states<NPL>(&st.c[s][n0], cn);
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
         const float a = fast_exp2(dv * A2[n]);
-        e[n] = a * __builtin_fmaf(dpv, st.c[s][n0 + n], e[n]);
+        e[n] = a * __builtin_fmaf(dpv, cn[n], e[n]);
       }
     }
     sd += (double)tsum;
@@ -208,30 +226,59 @@ __global__ __launch_bounds__(kWave* G) void bwd_chunk_adjoint_kernel(
 // copy of the same half; once a lane holds one value the remaining exchanges
 // add the partner's value.  Afterwards v[0] of lane l is the total of value
 // l >> (6 - log2 V).
+//   O = 32, 16: v_permlane32_swap / v_permlane16_swap exchange v[k] of the
+//     upper lanes with v[k + H] of the lower lanes, so that the sum of the
+//     two results is each lane's kept half (no selection needed);
+//   O = 8, 4, 2, 1: DPP row_mirror, row_half_mirror and quad permutations
+//     read the partner lane (all pair lanes that differ in bit O).
 // ---------------------------------------------------------------------------
+template <int O>
+__device__ __forceinline__ float dpp_partner(float v) {
+  constexpr int ctrl = O == 8 ? 0x140 : O == 4 ? 0x141 : O == 2 ? 0x4E : 0xB1;
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               ctrl, 0xf, 0xf, false));
+}
+
+template <int O>
+__device__ __forceinline__ void swap_add(float& lo, float& hi) {
+  // lo <- lo + hi after the exchange: lower lanes end with sum of lo,
+  // upper lanes with sum of hi
+  const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(lo),
+                                                            __float_as_uint(hi), false, false)
+                         : __builtin_amdgcn_permlane16_swap(__float_as_uint(lo),
+                                                            __float_as_uint(hi), false, false);
+  lo = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int V, int O>
 __device__ __forceinline__ void lane_sum(float* v, int lane) {
   if constexpr (O > 0) {
-    if constexpr (V == 1) {
-      v[0] += __shfl_xor(v[0], O, kWave);
-      lane_sum<1, O / 2>(v, lane);
-    } else {
-      constexpr int H = V / 2;
-      const bool up = (lane & O) != 0;
+    constexpr int H = V / 2;
+    if constexpr (O >= 16) {
+      if constexpr (V == 1) {
+        float w = v[0];
+        swap_add<O>(v[0], w);
+      } else {
 #pragma unroll
-      for (int k = 0; k < H; ++k) {
-        const float give = up ? v[k] : v[k + H];
-        const float keep = up ? v[k + H] : v[k];
-        v[k] = keep + __shfl_xor(give, O, kWave);
+        for (int k = 0; k < H; ++k) swap_add<O>(v[k], v[k + H]);
       }
-      lane_sum<H, O / 2>(v, lane);
+    } else {
+      if constexpr (V == 1) {
+        v[0] += dpp_partner<O>(v[0]);
+      } else {
+        const bool up = (lane & O) != 0;
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+          const float give = up ? v[k] : v[k + H];
+          const float keep = up ? v[k + H] : v[k];
+          v[k] = keep + dpp_partner<O>(give);
+        }
+      }
     }
+    lane_sum<(V > 1 ? H : 1), O / 2>(v, lane);
   }
 }
 
-// ---------------------------------------------------------------------------
-// Main backward pass.
-// ---------------------------------------------------------------------------
 // Materialises v at this point of the program.  Applied to running sums and
 // recomputed states each step: without it the compiler sinks those updates
 // to the end of the tile, keeping every step's operands alive (registers).
@@ -315,11 +362,12 @@ __device__ __forceinline__ void bwd_chunk(
 #pragma unroll
     for (int s = 0; s < kBT; ++s) {
       const float xv = sm.st.x[s][k.lane], dv = sm.st.dl[s][k.lane];
+      float bn[NPL];
+      read_states<NPL>(&sm.st.b[s][n0], bn);
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
         const float a = fast_exp2(dv * A2[n]);
-        h[n] = __builtin_fmaf(a, h[n],
-                              input_term<V, ZERO_A>(a, dv, iA[n], sm.st.b[s][n0 + n] * xv));
+        h[n] = __builtin_fmaf(a, h[n], input_term<V, ZERO_A>(a, dv, iA[n], bn[n] * xv));
         pin(h[n]);
       }
     }
@@ -339,11 +387,13 @@ __device__ __forceinline__ void bwd_chunk(
     for (int s = 0; s < kBT; ++s) {
       const float xv = sm.st.x[s][k.lane];
       const float dv = sm.st.dl[s][k.lane];
+      float bn[NPL];
+      read_states<NPL>(&sm.st.b[s][n0], bn);
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
         const float a = fast_exp2(dv * A2[n]);
         hs[s][n] = __builtin_fmaf(a, s ? hs[s - 1][n] : hck[n],
-                                  input_term<V, ZERO_A>(a, dv, iA[n], sm.st.b[s][n0 + n] * xv));
+                                  input_term<V, ZERO_A>(a, dv, iA[n], bn[n] * xv));
         pin(hs[s][n]);
       }
     }
@@ -361,12 +411,15 @@ __device__ __forceinline__ void bwd_chunk(
         const float dv = sm.st.dl[s][k.lane];
         const float dpv = sm.st.dp[s][k.lane];
         float dxp = 0.0f, ddp = 0.0f, sp = 0.0f;
+        float bn[NPL], cn[NPL];
+        read_states<NPL>(&sm.st.b[s][n0], bn);
+        read_states<NPL>(&sm.st.c[s][n0], cn);
 #pragma unroll
         for (int n = 0; n < NPL; ++n) {
           const float a = fast_exp2(dv * A2[n]);
           const float coef = coef_of<V, ZERO_A>(a, dv, iA[n]);
           const float prev = s ? hs[s - 1][n] : hck[n];
-          const float Bn = sm.st.b[s][n0 + n], Cn = sm.st.c[s][n0 + n];
+          const float Bn = bn[n], Cn = cn[n];
           const float dh = __builtin_fmaf(dpv, Cn, e[n]);
           const float dc = dh * coef;
           const float ubx = dh * Bn * xv;
@@ -511,32 +564,47 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   io<IO>::store(dC + i, sc);
 }
 
-// dA, dD: sum of the (batch row, chunk) partials in order; with A given per
-// channel dA also sums the 16 states.
+// dA, dD: sums of the (batch row, chunk) partials.  A block takes 64
+// columns; its four waves sum every fourth row each, then the four partial
+// sums are added in a fixed order (deterministic).  With A given per channel
+// the 16 states of each channel are added last.  Blocks past the dA columns
+// do the same for dD.
 __global__ __launch_bounds__(256) void bwd_reduce_a_kernel(const float* __restrict__ pdA,
                                                            const float* __restrict__ pdD,
                                                            float* __restrict__ dA,
-                                                           float* __restrict__ dD, int batch,
-                                                           int nchunks, int dim,
+                                                           float* __restrict__ dD, int rows,
+                                                           int dim, int a_blocks,
                                                            int a_per_channel) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t na = a_per_channel ? dim : (int64_t)dim * kDState;
-  if (i < na) {
-    float s = 0.0f;
-    for (int bc = 0; bc < batch * nchunks; ++bc) {
-      if (a_per_channel) {
-        const float* p = pdA + ((size_t)bc * dim + i) * kDState;
-        for (int n = 0; n < kDState; ++n) s += p[n];
-      } else {
-        s += pdA[(size_t)bc * dim * kDState + i];
-      }
+  __shared__ float part[4][kWave];
+  const int col = threadIdx.x % kWave, sl = threadIdx.x / kWave;
+  const bool is_a = (int)blockIdx.x < a_blocks;
+  const int64_t ncol = is_a ? (int64_t)dim * kDState : dim;
+  const float* p = is_a ? pdA : pdD;
+  const int64_t c = (int64_t)(is_a ? blockIdx.x : blockIdx.x - a_blocks) * kWave + col;
+  float s = 0.0f;
+  if (c < ncol && (is_a || dD))
+    for (int r = sl; r < rows; r += 4) s += p[(size_t)r * ncol + c];
+  part[sl][col] = s;
+  __syncthreads();
+  if (sl == 0) {
+    const float t = ((part[0][col] + part[1][col]) + part[2][col]) + part[3][col];
+    if (!is_a) {
+      if (dD && c < ncol) dD[c] = t;
+    } else if (!a_per_channel) {
+      if (c < ncol) dA[c] = t;
+    } else {
+      part[0][col] = t;
     }
-    dA[i] = s;
   }
-  if (dD && i < dim) {
-    float s = 0.0f;
-    for (int bc = 0; bc < batch * nchunks; ++bc) s += pdD[(size_t)bc * dim + i];
-    dD[i] = s;
+  if (is_a && a_per_channel) {
+    __syncthreads();
+    const int j = threadIdx.x;  // channel j of the block's four
+    const int64_t d = (int64_t)blockIdx.x * (kWave / kDState) + j;
+    if (j < kWave / kDState && d < dim) {
+      float t = 0.0f;
+      for (int n = 0; n < kDState; ++n) t += part[0][j * kDState + n];
+      dA[d] = t;
+    }
   }
 }
 
@@ -580,10 +648,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      static_cast<IO*>(a.dC), f.batch, f.seqlen, (int)gx);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t na = (int64_t)f.dim * kDState;
-  hipLaunchKernelGGL(bwd_reduce_a_kernel, dim3((unsigned)((na + 255) / 256)), dim3(256), 0,
-                     stream, a.ws_pdA, a.ws_pdD, a.dA, a.dD, f.batch, f.nchunks, f.dim,
-                     (V & kVarScalarA) ? 1 : 0);
+  const int a_blocks = (int)(((int64_t)f.dim * kDState + kWave - 1) / kWave);
+  const int d_blocks = (f.dim + kWave - 1) / kWave;
+  hipLaunchKernelGGL(bwd_reduce_a_kernel, dim3((unsigned)(a_blocks + d_blocks)), dim3(256), 0,
+                     stream, a.ws_pdA, a.ws_pdD, a.dA, a.dD, f.batch * f.nchunks, f.dim,
+                     a_blocks, (V & kVarScalarA) ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ def test_ragged_with_and_without_optional_inputs(dtype):
         _compare(_gpu(p), _ref(p), dtype, tag=f"without {drop}: ")
 
 
-@pytest.mark.parametrize("L", [1, 15, 16, 63, 64, 65, 127, 129, 200])
+@pytest.mark.parametrize("L", [1, 15, 16, 31, 32, 33, 63, 64, 65, 127, 129, 200])
 def test_chunk_boundaries(L):
     print(f"bwd L={L}", flush=True)
     p = _inputs(W.TINY, seqlen=L, batch=2, dim=65)

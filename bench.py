@@ -231,6 +231,40 @@ def bench_variants(steps: int, warmup: int):
     return {"workload": w.name, **res}
 
 
+def bench_backward(steps: int, warmup: int):
+    """Backward of the scan at the same shape: all input gradients for an
+    upstream dy (states recomputed, nothing kept from a forward call)."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.MAMBA_2P8B
+    dev = "cuda:0"
+    sets = [W.make_inputs(w, device=dev, layer=i) for i in range(2)]
+    g = torch.Generator(device=dev).manual_seed(17)
+    dys = [torch.randn(s["x"].shape, generator=g, device=dev).to(s["x"].dtype) for s in sets]
+    nws = ssm.scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, dtype=w.io_dtype)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        f = sets[i % 2]
+        ssm.scan_bwd(f["x"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
+                     dy=dys[i % 2], workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
+            "unit": "elements/s", "workspace_bytes": nws}
+
+
 def bench_decode(sweeps: int):
     """64 layers stepped back to back, each with its own state, inputs and
     parameters (5.4 GB of state, far beyond the 256 MB cache).  HIP events
@@ -286,6 +320,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward of the scan")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the A-per-channel / Euler scan variants")
     ap.add_argument("--no-fused", action="store_true",
@@ -362,6 +398,10 @@ def main():
         line["fused_prologue"] = bench_fused(max(10, args.steps // 4), max(10, args.warmup // 4))
     if not args.no_variants:
         line["variants"] = bench_variants(max(10, args.steps // 4), max(10, args.warmup // 4))
+    if not args.no_backward:
+        bwd = bench_backward(max(10, args.steps // 5), max(5, args.warmup // 20))
+        bwd["time_vs_forward"] = bwd["ms_per_step"] / r["step_ms"]
+        line["backward"] = bwd
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(r["inp"], w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

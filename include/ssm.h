@@ -104,6 +104,13 @@ int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
  *                    NULL => not written.
  *   workspace      : device buffer of at least ssm_scan_workspace_bytes(...)
  *                    bytes (may be NULL when that is 0).
+ * dstate: 16 runs the chunked kernels (plan of ssm_scan_fwd_planned); 32,
+ * 64 and 128 (the larger states of the paperlens tutorial's d_state setting
+ * and of Mamba-3, ihouse article "推論効率") run one pass per sequence with
+ * more waves per channel group: their workspace size is 0, waves_per_group
+ * and nchunks are ignored, ssm_scan_fwd_phase accepts only phase 3 and the
+ * fused prologue is not available (SSM_ERR_UNSUPPORTED).  Other dstate:
+ * SSM_ERR_UNSUPPORTED.
  * Outputs must not alias inputs (exact pointer equality is rejected).
  * seqlen == 0 writes h_last (= h0, or zeros) when given and nothing else;
  * batch == 0 or dim == 0 is a no-op.  Returns an SSM_* status.
@@ -254,6 +261,7 @@ int ssm_scan_fwd_fused(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
  *   h        : [batch, dim, dstate] fp32, read and updated IN PLACE.
  *   x, delta, z, y : [batch, dim] io_dtype.  B, C : [batch, dstate] io_dtype.
  *   A [dim, dstate] fp32; Dskip [dim] fp32 (NULL => 0); z NULL => no gate.
+ * dstate 16, 32, 64 or 128 (other: SSM_ERR_UNSUPPORTED).
  * The result equals one step of ssm_scan_fwd with h0 = h.  y must not alias
  * an input.  batch == 0 or dim == 0 is a no-op.  Returns an SSM_* status.
  */

@@ -116,6 +116,7 @@ int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int
     auto_plan(batch, seqlen, dim, &g, &nchunks);
   }
   if (batch == 0 || dim == 0 || seqlen == 0) return 0;
+  if (dstate != kDState) return 0;  // wide states: one pass, no carry workspace
   nchunks = effective_chunks(seqlen, dim, io_dtype, nchunks);
   return (int64_t)workspace_for(batch, dim, nchunks);
 }
@@ -136,7 +137,11 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
     return SSM_ERR_INVALID_ARG;
   if (phase < 1 || phase > 3) return SSM_ERR_INVALID_ARG;
   if (batch == 0 || dim == 0) return SSM_OK;
-  if (dstate != kDState) return SSM_ERR_UNSUPPORTED;
+  // state sizes other than 16 run the one-pass wide-state kernels: no chunk
+  // plan, no fused prologue, one call
+  const bool wide = dstate != kDState;
+  if (wide && !ssm::scan_wide_supported(dstate)) return SSM_ERR_UNSUPPORTED;
+  if (wide && (pro.d_conv > 0 || phase != 3)) return SSM_ERR_UNSUPPORTED;
   if (!A) return SSM_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (seqlen == 0) {
@@ -144,7 +149,7 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
     if ((const void*)h_last == (const void*)h0 || (const void*)h_last == (const void*)A)
       return SSM_ERR_INVALID_ARG;
     if (!all_aligned(h0, h_last)) return SSM_ERR_INVALID_ARG;
-    return hip_status(ssm::launch_copy_state(h0, h_last, batch * dim * kDState, s));
+    return hip_status(ssm::launch_copy_state(h0, h_last, batch * dim * dstate, s));
   }
   if (!x || !delta || !B || !C || !y) return SSM_ERR_INVALID_ARG;
   // outputs must not alias any input
@@ -158,6 +163,27 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
       !all_aligned(pro.conv_w, pro.conv_b, pro.delta_bias))
     return SSM_ERR_INVALID_ARG;
   if (batch > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  if (wide) {
+    ssm::ScanArgs a{};
+    a.x = x;
+    a.delta = delta;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.Dskip = Dskip;
+    a.z = z;
+    a.h0 = h0;
+    a.y = y;
+    a.h_last = h_last;
+    a.seqlen = seqlen;
+    a.chunk_len = seqlen;
+    a.nchunks = 1;
+    a.dim = (int)dim;
+    a.batch = (int)batch;
+    a.a_per_channel = a_per_channel;
+    a.euler = euler;
+    return hip_status(ssm::launch_scan_wide(a, (int)dstate, io_dtype == SSM_DTYPE_BF16, s));
+  }
 
   int G = 0, K = 0;
   auto_plan(batch, seqlen, dim, &G, &K);
@@ -281,8 +307,8 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, fl
                     void* stream) {
   if (!sizes_ok(batch, 1, dim, dstate) || !valid_dtype(io_dtype)) return SSM_ERR_INVALID_ARG;
   if (batch == 0 || dim == 0) return SSM_OK;
-  if (dstate != kDState) return SSM_ERR_UNSUPPORTED;
-  if (batch * dim * 4 / 256 >= (int64_t)UINT32_MAX) return SSM_ERR_UNSUPPORTED;
+  if (dstate != kDState && !ssm::scan_wide_supported(dstate)) return SSM_ERR_UNSUPPORTED;
+  if (batch * dim * (dstate / 4) / 256 >= (int64_t)UINT32_MAX) return SSM_ERR_UNSUPPORTED;
   if (!h || !x || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARG;
   const void* ins[] = {x, delta, A, B, C, Dskip, z};
   for (const void* in : ins)
@@ -301,6 +327,7 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, fl
   a.y = y;
   a.batch = batch;
   a.dim = (int)dim;
+  a.dstate = (int)dstate;
   return hip_status(ssm::launch_decode(a, io_dtype == SSM_DTYPE_BF16,
                                        static_cast<hipStream_t>(stream)));
 }

@@ -7,13 +7,14 @@
 // update is an outer product with low, constant arithmetic intensity, so the
 // step is bound by memory traffic).
 //
-// Layout: 4 consecutive lanes own one (b, d) and each holds 4 of its 16
-// states as one float4, so a wave streams 16 channels = 1 KiB of contiguous
-// state with 16-byte non-temporal loads and stores (the state is touched
-// once per step).  The readout's 16-term sum is the lane's 4-term partial
-// plus two DPP quad swaps; lane 0 of the quad applies the skip term and gate
-// and stores y.  The grid's y dimension is the batch row, so no 64-bit
-// division splits a flat index.
+// Layout: L = N/4 consecutive lanes own one (b, d) and each holds 4 of its N
+// states (N = 16, 32, 64, 128) as one float4, so a wave streams 1 KiB of
+// contiguous state with 16-byte non-temporal loads and stores (the state is
+// touched once per step).  The readout's N-term sum is the lane's 4-term
+// partial plus DPP quad swaps, row half-mirror and mirror exchanges (and a
+// 16-lane shuffle for N = 128); lane 0 of the channel applies the skip term
+// and gate and stores y.  The grid's y dimension is the batch row, so no
+// 64-bit division splits a flat index.
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -56,22 +57,31 @@ __device__ __forceinline__ float zoh_update(float h, float av, float iav, float 
   return __builtin_fmaf(abar, h, b);
 }
 
-template <typename IO>
+// Value of the lane that DPP control CTRL pairs with (row_half_mirror 0x141,
+// row_mirror 0x140).
+template <int CTRL>
+__device__ __forceinline__ float row_swap(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+template <typename IO, int N>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
+  constexpr int L = N / 4;  // lanes per channel
   const int t = blockIdx.x * 256 + threadIdx.x;  // (channel, quarter) in one batch row
-  const int d = t >> 2;
-  const int q = t & 3;
-  if (d >= a.dim) return;  // whole quads leave together
+  const int d = t / L;
+  const int q = t % L;
+  if (d >= a.dim) return;  // a channel's lanes leave together
   const int64_t b = a.row0 + blockIdx.y;
   const size_t ch = (size_t)b * a.dim + d;
-  v4f* hp = reinterpret_cast<v4f*>(a.h) + ch * 4 + q;
+  v4f* hp = reinterpret_cast<v4f*>(a.h) + ch * L + q;
   // Every load is issued before any result is waited on.  The small shared
   // and per-channel inputs go first and the streamed state (touched once per
   // step, so read and written non-temporally) last; on MI355X this order and
   // plain loads for x, delta and z measured fastest.
-  const v4f A = reinterpret_cast<const v4f*>(a.A)[(size_t)d * 4 + q];
-  const float4 Bq = Quad<IO>::load(static_cast<const IO*>(a.B) + b * kDState + 4 * q);
-  const float4 Cq = Quad<IO>::load(static_cast<const IO*>(a.C) + b * kDState + 4 * q);
+  const v4f A = reinterpret_cast<const v4f*>(a.A)[(size_t)d * L + q];
+  const float4 Bq = Quad<IO>::load(static_cast<const IO*>(a.B) + b * N + 4 * q);
+  const float4 Cq = Quad<IO>::load(static_cast<const IO*>(a.C) + b * N + 4 * q);
   const float xv = io<IO>::load(static_cast<const IO*>(a.x) + ch);
   const float dv = io<IO>::load(static_cast<const IO*>(a.delta) + ch);
   // optional inputs are read unconditionally (from a valid stand-in when
@@ -97,16 +107,18 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   p = __builtin_fmaf(Cq.w, h.w, p);
   p += quad_swap<0xB1>(p);
   p += quad_swap<0x4E>(p);
+  if constexpr (L >= 8) p += row_swap<0x141>(p);  // lanes i and 7 - i: the other quad
+  if constexpr (L >= 16) p += row_swap<0x140>(p);  // lanes i and 15 - i: the other half row
+  if constexpr (L >= 32) p += __shfl_xor(p, 16, kWave);
   if (q == 0) {
     const float pre = __builtin_fmaf(Dd, xv, p);
     io<IO>::store(static_cast<IO*>(a.y) + ch, a.z ? pre * silu(zv) : pre);
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
-  const int64_t threads = (int64_t)args.dim * 4;  // per batch row
+template <int N>
+hipError_t launch_decode_n(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
+  const int64_t threads = (int64_t)args.dim * (N / 4);  // per batch row
   constexpr int64_t kMaxRows = 65535;              // grid y extent per launch
   for (int64_t r0 = 0; r0 < args.batch; r0 += kMaxRows) {
     DecodeArgs a = args;
@@ -114,13 +126,25 @@ hipError_t launch_decode(const DecodeArgs& args, bool io_bf16, hipStream_t strea
     const int64_t rows = args.batch - r0 < kMaxRows ? args.batch - r0 : kMaxRows;
     const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)rows);
     if (io_bf16)
-      hipLaunchKernelGGL(decode_step_kernel<bf16>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_step_kernel<bf16, N>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(decode_step_kernel<float>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_step_kernel<float, N>), grid, dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
+  switch (args.dstate) {
+    case 16: return launch_decode_n<16>(args, io_bf16, stream);
+    case 32: return launch_decode_n<32>(args, io_bf16, stream);
+    case 64: return launch_decode_n<64>(args, io_bf16, stream);
+    case 128: return launch_decode_n<128>(args, io_bf16, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ssm

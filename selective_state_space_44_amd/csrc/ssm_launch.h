@@ -58,6 +58,7 @@ struct DecodeArgs {
   int64_t batch;
   int dim;
   int64_t row0;        // first batch row of this launch (set by launch_decode)
+  int dstate;          // 16, 32, 64 or 128
 };
 
 // Steps per tile of the scan kernels; chunks start on a tile boundary.
@@ -117,6 +118,11 @@ struct BwdWorkspace {
 };
 BwdWorkspace bwd_workspace_layout(int64_t batch, int64_t seqlen, int64_t dim, int nchunks);
 hipError_t launch_scan_bwd(const BwdArgs& a, bool io_bf16, hipStream_t stream);
+
+// Scan for state sizes 32, 64, 128: one pass over the sequence, no
+// workspace (chunk fields of ScanArgs unused; no prologue).
+bool scan_wide_supported(int64_t dstate);
+hipError_t launch_scan_wide(const ScanArgs& a, int dstate, bool io_bf16, hipStream_t stream);
 
 // Enqueue the seqlen == 0 case: h_last = h0 (or zeros).
 hipError_t launch_copy_state(const float* h0, float* h_last, int64_t count,

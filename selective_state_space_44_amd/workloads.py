@@ -117,7 +117,7 @@ def _draw(kind: str, shape, w: Workload, layer: int, k: int, device) -> torch.Te
 
 def make_inputs(w: Workload, device="cpu", layer: int = 0,
                 batch: int | None = None, seqlen: int | None = None,
-                dim: int | None = None) -> dict:
+                dim: int | None = None, dstate: int | None = None) -> dict:
     """Inputs of workload ``w`` (optionally with overridden sizes, which keeps
     the distributions and seeds), as tensors on ``device``.
 
@@ -127,7 +127,7 @@ def make_inputs(w: Workload, device="cpu", layer: int = 0,
     b = w.batch if batch is None else batch
     L = w.seqlen if seqlen is None else seqlen
     d = w.dim if dim is None else dim
-    n = w.dstate
+    n = w.dstate if dstate is None else dstate
     io = w.io_dtype
     shp = (b, d) if w.kind == "decode" else (b, L, d)
     shp_bc = (b, n) if w.kind == "decode" else (b, L, n)

@@ -59,7 +59,8 @@ def test_scan_rejects_bad_arguments(lib):
     assert _scan(lib, y=FAKE) == ssm.SSM_ERR_INVALID_ARG               # y aliases x
     assert _scan(lib, h_last=FAKE) == ssm.SSM_ERR_INVALID_ARG          # h_last aliases x
     assert _scan(lib, N=8) == ssm.SSM_ERR_UNSUPPORTED                   # no kernel, no fallback
-    assert _scan(lib, N=32) == ssm.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, N=24) == ssm.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, N=256) == ssm.SSM_ERR_UNSUPPORTED
     assert _scan(lib, G=3) == ssm.SSM_ERR_UNSUPPORTED
     # a chunked plan without workspace
     assert _scan(lib, L=4096, K=4) == ssm.SSM_ERR_WORKSPACE

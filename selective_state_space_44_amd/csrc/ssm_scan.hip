@@ -897,15 +897,18 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
         pin(gs[n]);
       }
     });
-    // sum of delta over the tile: pairwise in fp32, then into fp64
-    float t4[kT / 2];
+    // sum of delta over the tile: pairwise in fp32, then into fp64; only
+    // wave 0 publishes it, so only wave 0 computes it (a wave-uniform branch)
+    if (k.g == 0) {
+      float t4[kT / 2];
 #pragma unroll
-    for (int j = 0; j < kT / 2; ++j) t4[j] = dv[2 * j] + dv[2 * j + 1];
+      for (int j = 0; j < kT / 2; ++j) t4[j] = dv[2 * j] + dv[2 * j + 1];
 #pragma unroll
-    for (int w = kT / 4; w >= 1; w /= 2)
+      for (int w = kT / 4; w >= 1; w /= 2)
 #pragma unroll
-      for (int j = 0; j < w; ++j) t4[j] = t4[j] + t4[j + w];
-    sd += (double)t4[0];
+        for (int j = 0; j < w; ++j) t4[j] = t4[j] + t4[j + w];
+      sd += (double)t4[0];
+    }
     ld.put(rput, stages[cur ^ 1], lane);
     __syncthreads();
   };

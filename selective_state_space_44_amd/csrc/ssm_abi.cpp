@@ -14,9 +14,6 @@ namespace {
 
 constexpr int64_t kWave = 64;
 constexpr int64_t kDState = 16;
-// Design point of the schedule: MI355X has 256 CUs x 4 SIMDs.  The scan's
-// inner loop is bound by VALU issue, which needs several resident waves per
-// SIMD; the plan aims for at least this many waves in flight.
 // Design point of the schedule (MI355X: 256 CUs).  The scan's inner loop is
 // bound by VALU issue, which needs several resident waves per SIMD; measured
 // on the benchmark shapes, 4 waves per 64-channel group (4 states each) with

@@ -20,8 +20,8 @@
 //     its lane's steps with 16-byte LDS loads), B and C as fp32 [step][state]
 //     (read with broadcast LDS loads: every lane of a wave wants the same
 //     values).  The fetch of a tile from HBM is shared evenly by the G
-//     waves of the block and runs two tiles ahead of its use.  bf16 inputs are widened for
-//     free: the 16 raw bits are written into the upper half of an fp32 LDS
+//     waves of the block and runs two tiles ahead of its use.  bf16 inputs
+//     are widened for free: the 16 raw bits are written into the upper half of an fp32 LDS
 //     slot whose lower half was zeroed once, so no VALU op converts them.
 //   * Per element the main pass issues 6 fp32 VALU ops and one exp2:
 //     a = exp2(delta * A*log2 e), q = (B*x) * (1/A), Bbar*x = fma(a, q, -q),
@@ -38,14 +38,18 @@
 //     L into K chunks, a first kernel runs every chunk but the last from a
 //     zero state and records its end state hloc_c and sum of delta; a carry
 //     kernel composes the affine maps h -> P_c h + hloc_c with
-//     P_c = exp(A * sum(delta over chunk c)) by an in-wave prefix scan over
-//     lane shuffles; the main kernel then runs every chunk from its true
+//     P_c = exp(A * sum(delta over chunk c)) in chunk order, one (b, d, n)
+//     per thread; the main kernel then runs every chunk from its true
 //     entering state.  The first kernel
 //     needs no readout, so it carries g = A*h instead of h:
 //     g = fma(a, g, fma(a, B*x, -B*x)), one multiply per element fewer, and
 //     converts back (h = g/A) once at the end of the chunk.
 //   * A == 0 (which the ZOH formula reaches only as a limit) switches the
 //     affected wave to a form with that limit, Bbar = delta * B.
+//   * Variants (template bit V): A given per channel (one exp2 per step and
+//     lane instead of one per state) and the Euler rule Bbar = delta * B.
+//   * With the fused prologue the loader computes x = act(conv1d(x_raw) + b)
+//     and delta = softplus(delta_raw + bias) on the way into LDS.
 
 #include <type_traits>
 

@@ -317,9 +317,12 @@ __device__ __forceinline__ float input_term(float a, float dv, float iA, float b
 }
 
 // dcoef/dA of the hold: delta^2 psi(u), u = delta A,
-// psi(u) = (u e^u - e^u + 1) / u^2 = sum_m (m-1) u^(m-2) / m!.  The series
-// (to u^5, truncation < 1e-7 relative) is used for |u| < 1/4, where the
-// closed form (delta Abar - coef) / A would cancel; A == 0 gives delta^2 / 2.
+// psi(u) = (u e^u - e^u + 1) / u^2 = sum_m (m-1) u^(m-2) / m!.  Used per
+// element only where the wave holds an A == 0 (delta^2 / 2 there): the series
+// (to u^5, truncation < 1e-7 relative) for |u| < 1/4, the closed form
+// (delta Abar - coef) / A elsewhere.  Waves without a zero A sum
+// ubx (delta Abar - coef) over the chunk and apply 1/A once: its rounding
+// error relative to a term of the Abar part of dA is about eps / |u|.
 __device__ __forceinline__ float dcoef_da_hold(float dv, float Av, float a, float coef,
                                                float iA) {
   const float u = dv * Av;
@@ -349,6 +352,9 @@ __device__ __forceinline__ void bwd_chunk(
   const int n0 = k.g * NPL;
   const int groups = (dim + kWave - 1) / kWave;
   const int nt = (int)((k.t1 - k.t0 + kBT - 1) / kBT);
+  float dAq[NPL];  // hold, A != 0: chunk sum of ubx (delta Abar - coef), times 1/A at the end
+#pragma unroll
+  for (int n = 0; n < NPL; ++n) dAq[n] = 0.0f;
 
   // tile entry states, recomputed forward through the chunk
   for (int j = 0; j < nt; ++j) {
@@ -433,7 +439,15 @@ __device__ __forceinline__ void bwd_chunk(
           } else {
             ddp = __builtin_fmaf(a, __builtin_fmaf(dhp, Af[n], ubx), ddp);
             dA_acc[n] = __builtin_fmaf(dhp, dv * a, dA_acc[n]);
-            dA_acc[n] = __builtin_fmaf(ubx, dcoef_da_hold(dv, Af[n], a, coef, iA[n]), dA_acc[n]);
+            if constexpr (ZERO_A) {
+              dA_acc[n] =
+                  __builtin_fmaf(ubx, dcoef_da_hold(dv, Af[n], a, coef, iA[n]), dA_acc[n]);
+            } else {
+              // dcoef/dA = (delta Abar - coef) / A: the sum over the chunk of
+              // ubx (delta Abar - coef) is scaled by 1/A once, at the end
+              dAq[n] = __builtin_fmaf(ubx, __builtin_fmaf(dv, a, -coef), dAq[n]);
+              pin(dAq[n]);
+            }
           }
           sp = __builtin_fmaf(Cn, hs[s][n], sp);
           e[n] = a * dh;
@@ -482,6 +496,10 @@ __device__ __forceinline__ void bwd_chunk(
       if constexpr (HAS_Z)
         io<IO>::store(dz + off, sm.st.gd[s][k.lane] * __builtin_fmaf(Dd, sm.st.x[s][k.lane], ssp));
     }
+  }
+  if constexpr ((V & kVarEuler) == 0 && !ZERO_A) {
+#pragma unroll
+    for (int n = 0; n < NPL; ++n) dA_acc[n] = __builtin_fmaf(dAq[n], iA[n], dA_acc[n]);
   }
 }
 

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kWave* G) void bwd_chunk_adjoint_kernel(
     for (int s = kBT - 1; s >= 0; --s) {
       const float dv = st.dl[s][k.lane];
       const float dpv = st.dp[s][k.lane];
-      tsum += dv;
+      if (k.g == 0) tsum += dv;  // only wave 0 publishes the delta sum
       float cn[NPL];
       read_states<NPL>(&st.c[s][n0], cn);
 #pragma unroll
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kWave* G) void bwd_chunk_adjoint_kernel(
         e[n] = a * __builtin_fmaf(dpv, cn[n], e[n]);
       }
     }
-    sd += (double)tsum;
+    if (k.g == 0) sd += (double)tsum;
   }
   if (k.active) {
     const size_t cd = ((size_t)k.b * nchunks + k.c) * dim + k.d;

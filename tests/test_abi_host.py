@@ -137,7 +137,7 @@ def test_plan_and_workspace(lib):
         ssm.scan_workspace_bytes(1, 2, 100, nchunks=2)
     # the long single sequence is cut into chunks for parallelism
     g3, k3 = ssm.scan_plan(1, 262144, 4096)
-    assert k3 > 1
+    assert k3 > 1 and 262144 / k3 <= 2048   # chunks of at most 2048 steps
     with pytest.raises(ValueError):
         ssm.scan_workspace_bytes(-1, 10, 10)
 

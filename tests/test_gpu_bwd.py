@@ -183,3 +183,18 @@ def test_long_memory_channels():
         print(f"bwd long-memory {dtype}", flush=True)
         p = _inputs(W.LONG_CTX, dtype, batch=1, seqlen=3000, dim=128)
         _compare(_gpu(p), _ref(p), dtype, tag=f"long memory {dtype}: ")
+
+
+@pytest.mark.parametrize("per_channel,disc", [(True, "zoh"), (False, "euler"), (True, "euler")])
+def test_autograd_function_variants(per_channel, disc):
+    """The autograd wrapper with A given per channel and the Euler rule,
+    against the fp64 oracle's backward."""
+    p = _inputs(W.MAMBA_130M, torch.float32, per_channel=per_channel, batch=2, seqlen=150,
+                dim=64)
+    names = ("x", "delta", "A", "B", "C", "D", "z", "h0")
+    leaves = {k: p[k].clone().requires_grad_(True) for k in names}
+    y, h = ssm.SelectiveScan.apply(*(leaves[k] for k in names), disc)
+    torch.autograd.backward([y, h], [p["dy"], p["dh_last"]])
+    ref = _ref(p, disc)
+    grads = {"d" + ("delta" if k == "delta" else k): leaves[k].grad for k in names}
+    _compare(grads, ref, torch.float32, tag=f"autograd {disc} per_channel={per_channel}: ")

@@ -17,6 +17,8 @@
  *     term, and the decode step being a memory-bound outer-product update;
  *   - agenticai-flow guide, section "アーキテクチャ図解": the S6 output is
  *     multiplied by SiLU of the z branch.
+ * Also: the scan's variants (A per channel, Euler rule), its fused prologue
+ * (causal conv1d, softplus of delta) and its backward (all input gradients).
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers to contiguous row-major memory,
@@ -32,7 +34,8 @@
  *     returns SSM_ERR_UNSUPPORTED instead of running a slow path.
  *   - io_dtype selects the type of x, delta, z, B, C and y (all the same).
  *     A, D and every state tensor are always fp32; arithmetic is fp32.
- *   - dstate must be 16.
+ *   - dstate: 16 everywhere; 32, 64 and 128 for the forward scan (not fused)
+ *     and the decode step; other values return SSM_ERR_UNSUPPORTED.
  *   - NaN/Inf in inputs propagate by IEEE rules; nothing is checked on device.
  */
 #ifndef SSM_H_

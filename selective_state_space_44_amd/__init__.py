@@ -6,6 +6,12 @@ This module only checks and marshals arguments: tensors are PyTorch device
 tensors (PyTorch provides device memory and the current stream); every step
 of the computation runs in the HIP kernels.  There is no fallback path: if
 the library is missing or a request has no kernel, calls raise.
+
+Entry points: ``scan_fwd`` (the scan; A per channel and the Euler rule as
+options; d_state 16, 32, 64, 128), ``scan_fwd_fused`` (with the causal
+conv1d + softplus prologue), ``scan_bwd`` and the autograd wrapper
+``SelectiveScan`` (all input gradients), ``decode_step`` (one recurrent step
+on a resident state).
 """
 from __future__ import annotations
 
@@ -15,7 +21,8 @@ import threading
 
 import torch
 
-__all__ = ["scan_fwd", "scan_fwd_fused", "decode_step", "scan_plan", "scan_workspace_bytes", "load_library",
+__all__ = ["scan_fwd", "scan_fwd_fused", "scan_bwd", "SelectiveScan", "decode_step",
+           "scan_plan", "scan_workspace_bytes", "scan_bwd_workspace_bytes", "load_library",
            "LIB_PATH", "SsmError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm.so")

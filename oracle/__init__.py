@@ -127,6 +127,25 @@ def scan(x, delta, A, B, C, D=None, z=None, h0=None, nthreads: int = 0, lib=None
     return y, h_last
 
 
+def scan_heads(x, dt, A, B, C, D=None, z=None, h0=None, headdim: int = 64,
+               nthreads: int = 0, lib=None, discretization: str = "zoh"):
+    """Selective scan whose step size and decay rate are shared by each head of
+    ``headdim`` consecutive channels (A reduced to one scalar per head, as the
+    ihouse article's section on Mamba's evolution describes for Mamba-2).
+    Shapes: x, z [b, L, H*P]; dt [b, L, H]; A [H]; B, C [b, L, n]; D [H*P];
+    h0 [b, H*P, n].  Channel d = h*P + p takes dt[..., h] and A[h]; everything
+    else is ``scan`` with A given per channel.  Returns (y, h_last)."""
+    x, dt, A = _f64(x), _f64(dt), _f64(A)
+    batch, seqlen, dim = x.shape
+    assert headdim > 0 and dim % headdim == 0
+    nheads = dim // headdim
+    assert dt.shape == (batch, seqlen, nheads) and A.shape == (nheads,)
+    delta = np.repeat(dt, headdim, axis=2)
+    a_chan = np.repeat(A, headdim)
+    return scan(x, delta, a_chan, B, C, D, z, h0, nthreads=nthreads, lib=lib,
+                discretization=discretization)
+
+
 def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None,
              nthreads: int = 0, lib=None, discretization: str = "zoh"):
     """Gradients of the scan in fp64 for upstream dy [b, L, d] and optional

@@ -34,7 +34,9 @@ What pins what (pages cited by title and section):
   closed form, and its second-order agreement with the hold for small delta;
   A given per channel against brute force with A broadcast over the states,
   and the single decay rate it implies (paperlens tutorial, selection
-  pseudo-code; ihouse article, Mamba-2 section).
+  pseudo-code; ihouse article, Mamba-2 section); a step and decay shared by
+  a head of channels against the masked-matrix form of the same scan
+  (ihouse article, section on Mamba's evolution).
 * Prologue of the fused scan (paperlens tutorial, sections "現場ではこう使う"
   and "Mamba: 状態を「選択的」にする"): the causal depthwise convolution equals
   numpy's convolve of each channel with its reversed taps, and cannot see the
@@ -310,6 +312,62 @@ def pin_per_channel_A_brute_force(lib):
                 _, hq = oracle.scan(lib=lib, **q)
                 rate = np.exp(p["A"][None, :] * p["delta"].sum(axis=1))
                 assert _rel(hq, p["h0"] * rate[:, :, None]) < 1e-12
+
+
+def _masked_matrix_form(x, dt, A, B, C, D, z, h0, P, euler):
+    """The scan with a head-shared step written as one masked matrix product per
+    (batch row, head): y = (Lmask * (C B^T) * coef) X + exp(cum) * (C h0^T), with
+    Lmask[t, s] = exp(A * sum(dt over s < r <= t)) for s <= t, 0 above the
+    diagonal (ihouse article, section on Mamba's evolution: the SSM
+    computation as a masked matrix multiplication).  Also returns the final
+    state.  Written independently of the recurrence."""
+    b, L, dim = x.shape
+    H, n = dt.shape[2], B.shape[2]
+    y = np.zeros_like(x)
+    hl = np.zeros((b, dim, n))
+    for bi in range(b):
+        for h in range(H):
+            a = dt[bi, :, h] * A[h]
+            cum = np.cumsum(a)
+            if euler or A[h] == 0.0:
+                coef = dt[bi, :, h]
+            else:
+                coef = np.expm1(a) / A[h]
+            diff = cum[:, None] - cum[None, :]
+            lower = np.tril(np.ones((L, L), dtype=bool))
+            lmask = np.where(lower, np.exp(np.where(lower, diff, 0.0)), 0.0)
+            M = (C[bi] @ B[bi].T) * lmask * coef[None, :]
+            cols = slice(h * P, (h + 1) * P)
+            X = x[bi, :, cols]
+            Y = M @ X
+            w = np.exp(cum[-1] - cum) * coef if L else coef
+            S = (X * w[:, None]).T @ B[bi]                                  # [P, n]
+            if h0 is not None:
+                Y = Y + np.exp(cum)[:, None] * (C[bi] @ h0[bi, cols, :].T)
+                S = S + (np.exp(cum[-1]) if L else 1.0) * h0[bi, cols, :]
+            pre = Y + (D[cols][None, :] * X if D is not None else 0.0)
+            y[bi, :, cols] = pre * _silu(z[bi, :, cols]) if z is not None else pre
+            hl[bi, cols, :] = S
+    return y, hl
+
+
+def pin_head_shared_step_equals_masked_matrix_form(lib):
+    rng = _rng(27)
+    for euler in (False, True):
+        for (b, L, H, P, n) in ((1, 1, 1, 1, 1), (2, 9, 2, 3, 4), (1, 20, 3, 2, 5)):
+            dim = H * P
+            p = _rand_problem(rng, b, L, dim, n)
+            dt = rng.uniform(0.001, 0.5, (b, L, H))
+            A = -rng.uniform(0.2, 2.0, H)
+            if H > 1:
+                A[1] = 0.0                       # the delta*B limit of the hold
+            y, hl = oracle.scan_heads(p["x"], dt, A, p["B"], p["C"], p["D"], p["z"], p["h0"],
+                                      headdim=P, lib=lib,
+                                      discretization="euler" if euler else "zoh")
+            yr, hr = _masked_matrix_form(p["x"], dt, A, p["B"], p["C"], p["D"], p["z"], p["h0"],
+                                         P, euler)
+            assert _rel(y, yr) < 1e-12, (euler, b, L, H, P, n)
+            assert _rel(hl, hr) < 1e-12, (euler, b, L, H, P, n)
 
 
 # --------------------------------------------------------------------------

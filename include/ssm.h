@@ -18,7 +18,8 @@
  *   - agenticai-flow guide, section "アーキテクチャ図解": the S6 output is
  *     multiplied by SiLU of the z branch.
  * Also: the scan's variants (A per channel, Euler rule), its fused prologue
- * (causal conv1d, softplus of delta) and its backward (all input gradients).
+ * (causal conv1d, softplus of delta), its backward (all input gradients) and
+ * its masked-matrix form for a step and decay shared per head (ssm_ssd_fwd).
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers to contiguous row-major memory,
@@ -272,6 +273,40 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
                     float *h, const void *x, const void *delta, const float *A,
                     const void *B, const void *C, const float *Dskip,
                     const void *z, void *y, void *stream);
+
+/*
+ * Selective scan whose step size and decay rate are shared by each head of
+ * `headdim` consecutive channels, computed in the masked-matrix form on the
+ * matrix cores (ihouse article, "Mambaの進化の道のり": with A reduced to a
+ * scalar, most of the SSM's work is a masked matrix multiplication; paperlens
+ * tutorial, "計算量: 系列長との付き合い方": the recurrence composes chunk by
+ * chunk).  Channel d = h * headdim + p of head h uses
+ *   delta[b,t,d] = dt[b,t,h]  and  A[d, n] = A[h]  for every state n,
+ * and otherwise the recurrence, readout, skip and gate of ssm_scan_fwd:
+ *   h_t = exp(dt_t A) h_{t-1} + coef_t x_t B_t,   y_t = (C_t . h_t + D x_t) SiLU(z_t),
+ * with coef_t = (exp(dt_t A) - 1) / A (SSM_DISC_ZOH; dt_t at A = 0) or dt_t
+ * (SSM_DISC_EULER).  The result equals ssm_scan_fwd_ex with A per channel on
+ * dt repeated over each head's channels.
+ *   x, z, y : [batch, seqlen, nheads * headdim] bf16.  dt : [batch, seqlen,
+ *             nheads] bf16, >= 0 (already through softplus).  B, C : [batch,
+ *             seqlen, dstate] bf16, shared by every head.  A : [nheads] fp32.
+ *   Dskip   : [nheads * headdim] fp32, NULL => 0.  z NULL => no gate.
+ *   h0, h_last : [batch, nheads * headdim, dstate] fp32, NULL => zeros / not
+ *             written.
+ * Supported: io_dtype SSM_DTYPE_BF16, headdim 64, dstate 64 or 128; other
+ * values return SSM_ERR_UNSUPPORTED (the fp32 path of the same arithmetic is
+ * ssm_scan_fwd_ex).  Products run on bf16 matrix cores with fp32
+ * accumulation; operands that are not bf16 inputs (masked weights, state,
+ * weighted inputs) are split into two bf16 parts, so results carry fp32-level
+ * accuracy (relative error ~1e-5).  No workspace.  Outputs must not alias
+ * inputs (nor each other); seqlen == 0 sets h_last to h0 (or zeros); batch
+ * == 0 or nheads == 0 is a no-op.  Returns an SSM_* status.
+ */
+int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                int64_t dstate, int io_dtype, int discretization, const void *x,
+                const void *dt, const float *A, const void *B, const void *C,
+                const float *Dskip, const void *z, const float *h0, void *y,
+                float *h_last, void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,8 @@ Entry points: ``scan_fwd`` (the scan; A per channel and the Euler rule as
 options; d_state 16, 32, 64, 128), ``scan_fwd_fused`` (with the causal
 conv1d + softplus prologue), ``scan_bwd`` and the autograd wrapper
 ``SelectiveScan`` (all input gradients), ``decode_step`` (one recurrent step
-on a resident state).
+on a resident state), ``ssd_scan`` (step and decay shared per head of 64
+channels, on the matrix cores).
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import threading
 
 import torch
 
-__all__ = ["scan_fwd", "scan_fwd_fused", "scan_bwd", "SelectiveScan", "decode_step",
+__all__ = ["scan_fwd", "scan_fwd_fused", "scan_bwd", "SelectiveScan", "decode_step", "ssd_scan",
            "scan_plan", "scan_workspace_bytes", "scan_bwd_workspace_bytes", "load_library",
            "LIB_PATH", "SsmError"]
 
@@ -58,6 +59,7 @@ SIGNATURES = {
     "ssm_scan_bwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _int]),
     "ssm_scan_bwd": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
                      + [_vp] * 15 + [_vp, _sz, _vp]),
+    "ssm_ssd_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 10 + [_vp]),
 }
 
 _lock = threading.Lock()
@@ -214,6 +216,55 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
                                 int(waves_per_group), int(nchunks), int(phase),
                                 _stream(device))
     _check(st, "ssm_scan_fwd")
+    return (y, h_last) if return_last_state else y
+
+
+def ssd_scan(x, dt, A, B, C, D=None, z=None, h0=None, return_last_state=False,
+             discretization: str = "zoh", out=None):
+    """Scan with the step and decay rate shared by each head (``ssm_ssd_fwd``).
+    x, z: [batch, L, nheads * headdim]; dt: [batch, L, nheads]; B, C:
+    [batch, L, dstate] (all bfloat16); A [nheads], D [nheads * headdim], h0
+    [batch, nheads * headdim, dstate] float32.  headdim = x.shape[2] //
+    dt.shape[2].  Returns y (and the final state when ``return_last_state``)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a [batch, seqlen, dim] tensor")
+    if not isinstance(dt, torch.Tensor) or dt.dim() != 3:
+        raise ValueError("dt must be a [batch, seqlen, nheads] tensor")
+    if not isinstance(B, torch.Tensor) or B.dim() != 3:
+        raise ValueError("B must be a [batch, seqlen, dstate] tensor")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    if discretization not in ("zoh", "euler"):
+        raise ValueError("discretization must be 'zoh' or 'euler'")
+    batch, seqlen, dim = x.shape
+    nheads = dt.shape[2]
+    if nheads == 0 or dim % nheads:
+        raise ValueError("x's channels must split evenly into dt's heads")
+    headdim = dim // nheads
+    dstate = B.shape[2]
+    io = x.dtype
+    code = _io_code(io)
+    _require(x, "x", (batch, seqlen, dim), io, device)
+    _require(dt, "dt", (batch, seqlen, nheads), io, device)
+    _require(A, "A", (nheads,), torch.float32, device)
+    _require(B, "B", (batch, seqlen, dstate), io, device)
+    _require(C, "C", (batch, seqlen, dstate), io, device)
+    _require(D, "D", (dim,), torch.float32, device)
+    _require(z, "z", (batch, seqlen, dim), io, device)
+    _require(h0, "h0", (batch, dim, dstate), torch.float32, device)
+    if A is None or C is None:
+        raise ValueError("A and C are required")
+    y = out if out is not None else torch.empty_like(x)
+    _require(y, "out", (batch, seqlen, dim), io, device)
+    h_last = (torch.empty((batch, dim, dstate), dtype=torch.float32, device=device)
+              if return_last_state else None)
+    st = load_library().ssm_ssd_fwd(
+        batch, seqlen, nheads, headdim, dstate, code,
+        SSM_DISC_EULER if discretization == "euler" else SSM_DISC_ZOH, _ptr(x), _ptr(dt),
+        _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
+        _stream(device))
+    _check(st, "ssm_ssd_fwd")
     return (y, h_last) if return_last_state else y
 
 

@@ -461,4 +461,56 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   return hip_status(ssm::launch_scan_bwd(a, io_dtype == SSM_DTYPE_BF16, s));
 }
 
+int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                int io_dtype, int discretization, const void* x, const void* dt, const float* A,
+                const void* B, const void* C, const float* Dskip, const void* z,
+                const float* h0, void* y, float* h_last, void* stream) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim <= 0 || dstate <= 0 ||
+      !valid_dtype(io_dtype))
+    return SSM_ERR_INVALID_ARG;
+  if (discretization != SSM_DISC_ZOH && discretization != SSM_DISC_EULER)
+    return SSM_ERR_INVALID_ARG;
+  // the kernel addresses one 64-step chunk of a [b, L, dim] tensor with
+  // 32-bit byte offsets: 64 * dim * 2 bytes must stay below 2^31
+  if (nheads > ((int64_t)1 << 24) / headdim) return SSM_ERR_UNSUPPORTED;
+  if (io_dtype != SSM_DTYPE_BF16 || !ssm::ssd_supported(headdim, dstate))
+    return SSM_ERR_UNSUPPORTED;
+  if (batch == 0 || nheads == 0) return SSM_OK;
+  if (!A) return SSM_ERR_INVALID_ARG;
+  const int64_t dim = nheads * headdim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (seqlen == 0) {
+    if (!h_last) return SSM_OK;
+    if ((const void*)h_last == (const void*)h0 || (const void*)h_last == (const void*)A)
+      return SSM_ERR_INVALID_ARG;
+    if (!all_aligned(h0, h_last)) return SSM_ERR_INVALID_ARG;
+    return hip_status(ssm::launch_copy_state(h0, h_last, batch * dim * dstate, s));
+  }
+  if (!x || !dt || !B || !C || !y) return SSM_ERR_INVALID_ARG;
+  const void* ins[] = {x, dt, A, B, C, Dskip, z, h0};
+  for (const void* in : ins) {
+    if (!in) continue;
+    if (in == y || in == (const void*)h_last) return SSM_ERR_INVALID_ARG;
+  }
+  if ((const void*)h_last == y) return SSM_ERR_INVALID_ARG;
+  if (!all_aligned(x, dt, A, B, C, Dskip, z, h0, y, h_last)) return SSM_ERR_INVALID_ARG;
+  ssm::SsdArgs a{};
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.y = y;
+  a.h_last = h_last;
+  a.seqlen = seqlen;
+  a.batch = batch;
+  a.nheads = (int)nheads;
+  a.dim = (int)dim;
+  a.euler = discretization == SSM_DISC_EULER ? 1 : 0;
+  return hip_status(ssm::launch_ssd(a, (int)dstate, s));
+}
+
 }  // extern "C"

@@ -124,6 +124,31 @@ hipError_t launch_scan_bwd(const BwdArgs& a, bool io_bf16, hipStream_t stream);
 bool scan_wide_supported(int64_t dstate);
 hipError_t launch_scan_wide(const ScanArgs& a, int dstate, bool io_bf16, hipStream_t stream);
 
+// Scan with the step and decay rate shared by each head of 64 channels, in
+// its masked-matrix form on the matrix cores (ssm_ssd.hip).  bf16 x, dt, B,
+// C, z, y; fp32 A [nheads], Dskip [dim], h0 / h_last [batch, dim, dstate].
+struct SsdArgs {
+  const void* x;       // [batch, seqlen, dim]
+  const void* dt;      // [batch, seqlen, nheads]
+  const float* A;      // [nheads]
+  const void* B;       // [batch, seqlen, dstate]
+  const void* C;
+  const float* Dskip;  // nullable
+  const void* z;       // nullable
+  const float* h0;     // nullable
+  void* y;
+  float* h_last;       // nullable
+  int64_t seqlen;
+  int64_t batch;
+  int64_t row0;        // first batch row of a launch (set by launch_ssd)
+  int nheads;
+  int dim;             // nheads * 64
+  int euler;
+};
+bool ssd_supported(int64_t headdim, int64_t dstate);
+size_t ssd_smem_bytes(int64_t dstate);
+hipError_t launch_ssd(const SsdArgs& a, int dstate, hipStream_t stream);
+
 // Enqueue the seqlen == 0 case: h_last = h0 (or zeros).
 hipError_t launch_copy_state(const float* h0, float* h_last, int64_t count,
                              hipStream_t stream);

@@ -1,0 +1,430 @@
+// ssm_ssd.hip -- the selective scan with a step size and a decay rate shared
+// by each head of 64 channels, computed in its masked-matrix form on the
+// matrix cores (gfx950 bf16 MFMA, fp32 accumulation).
+//
+// Method (ihouse article on Mamba-3, section on Mamba's evolution: with A
+// reduced to a scalar the bulk of the SSM's work becomes masked matrix
+// products; paperlens tutorial, section on the parallel scan: the recurrence
+// composes chunk by chunk).  For one batch row, head h (decay rate a, step
+// dt_t) and a chunk of Q = 64 steps, with s_t = a * sum_{r<=t} dt_r inside
+// the chunk and coef_t the input coefficient of step t ((exp(a dt_t) - 1)/a
+// for the zero-order hold, dt_t for the Euler rule, dt_t at a = 0):
+//
+//   y_i   = sum_{j<=i} (C_i . B_j) exp(s_i - s_j) coef_j x_j      in-chunk part
+//         + exp(s_i) C_i . h_in                                   entering state
+//   h_out = exp(s_63) h_in + sum_j exp(s_63 - s_j) coef_j x_j B_j^T
+//
+// and y = (y + D x) * SiLU(z).  Each sum is a matrix product:
+//   * M = C B^T per chunk (64 x 64, contraction over the N states),
+//   * Y_in = P X with P = M masked to j <= i and weighted by
+//     exp(s_i - s_j) coef_j (contraction over the chunk's steps),
+//   * Y_state = C h_in^T (contraction over the states),
+//   * h_out^T = B^T (w x) with w_t = exp(s_63 - s_t) coef_t (contraction over
+//     the steps).
+//
+// Organisation: one block (4 waves) per (head, batch row) walks the chunks in
+// order, so the state never leaves the registers and no carry pass exists.
+// Wave w owns the 16 channels p = 16w..16w+15 of the head: it holds the
+// state h[n][p] of those channels as N/16 MFMA accumulator tiles, computes
+// their outputs for all 64 steps, and updates their state.  The 64 x 64
+// matrix P is shared by the four waves: its ten lower-triangular 16 x 16
+// tiles are computed once per chunk (3, 3, 2, 2 tiles per wave) and passed
+// through LDS.
+//
+// Data movement per chunk: the chunk's x, z (64 steps x 64 channels), B, C
+// (64 steps x N) and dt are loaded into registers one chunk ahead, then
+// written to LDS, x, z and B also transposed (step index contiguous), since
+// every operand must be contiguous in its contraction index.  Three barriers
+// per chunk: staging written, then P and w x written, then (next chunk) all
+// reads done.
+//
+// Precision: B, C and x are bf16 inputs, exact as MFMA operands.  The other
+// operands -- the masked weights P, the state h and the weighted inputs w x --
+// are fp32 values; each is split into a bf16 high part and a bf16 low part
+// (v = hi + lo to about 2^-17 |v|) and both parts are multiplied, so every
+// product carries ~16 significant bits and all sums are fp32.  The state
+// stays fp32 between chunks.
+//
+// MFMA lane layouts used (v_mfma_f32_16x16x32_bf16 only; 16 x 16 tiles, lane
+// l, g = l / 16):
+//   A operand: row l % 16, k slots 8g..8g+7
+//   B operand: column l % 16, the same k slots
+//   result:    column l % 16, rows 4g..4g+3
+// Only the row / column / result layout matters: a product pairs the k
+// slots of A and B one to one, so any permutation of the contraction index
+// applied to both operands gives the same sum.  The kernel uses that freedom
+// where a result tile becomes the next product's operand without a trip
+// through LDS (the state as the B operand of C h^T).
+
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kQ = 64;            // steps per chunk
+constexpr int kHD = 64;           // channels per head
+constexpr int kSsdThreads = 256;  // 4 waves, one per 16 channels of the head
+constexpr int kRowT = kQ + 8;     // bf16 per step-contiguous LDS row: 144 B, so
+                                  // rows start 4 banks apart
+
+template <int N>
+struct SsdSmem {
+  static constexpr int kRowN = N + 8;  // bf16 per state-contiguous row
+  alignas(16) uint16_t cs[kQ][kRowN];  // C of the chunk, [t][n]
+  alignas(16) uint16_t bs[kQ][kRowN];  // B, [t][n]
+  alignas(16) uint16_t bt[N][kRowT];   // B, [n][t]
+  alignas(16) uint16_t xt[kHD][kRowT];   // x, [p][t]
+  alignas(16) uint16_t zt[kHD][kRowT];   // z, [p][t]
+  alignas(16) uint16_t wxh[kHD][kRowT];  // w_t x_t[p], bf16 high part, [p][t]
+  alignas(16) uint16_t wxl[kHD][kRowT];  // low part
+  alignas(16) uint16_t pmh[kQ][kRowT];   // masked weights P[i][j], high part
+  alignas(16) uint16_t pml[kQ][kRowT];   // low part
+  alignas(16) float s2[kQ];     // s_t * log2(e)
+  alignas(16) float coef[kQ];   // coef_t
+  alignas(16) float wgt[kQ];    // exp(s_63 - s_t) coef_t
+  alignas(16) float ein[kQ];    // exp(s_t)
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo_elem, float hi_elem) {
+  bf16x2_t v = {(__bf16)lo_elem, (__bf16)hi_elem};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// (a, b) ~= hi + lo with hi, lo packed bf16 pairs: hi = rounded value, lo =
+// rounded remainder (the remainder itself is exact in fp32).
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16(a, b);
+  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ f32x4_t mfma_k32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t lds128(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x2_t lds64(const uint16_t* p) {
+  return *reinterpret_cast<const u32x2_t*>(p);
+}
+__device__ __forceinline__ u32x4_t cat(u32x2_t a, u32x2_t b) { return {a.x, a.y, b.x, b.y}; }
+
+// The lower-triangular tiles (I, J), J <= I, of P computed by each wave,
+// encoded 16 I + J; -1 = none.
+__constant__ const int kPTiles[4][3] = {
+    {0x00, 0x10, 0x11}, {0x20, 0x21, 0x22}, {0x30, 0x31, -1}, {0x32, 0x33, -1}};
+
+template <int N, bool HAS_Z, bool EULER>
+__global__ __launch_bounds__(kSsdThreads, 1) void ssd_scan_kernel(SsdArgs a) {
+  constexpr int NT = N / 16;    // state tiles per wave
+  constexpr int NPW = N / 4;    // B / C columns staged by each wave
+  constexpr int NV = NPW / 8;   // 16-byte pieces of them
+  extern __shared__ __align__(16) unsigned char ssd_smem_raw[];
+  SsdSmem<N>& sm = *reinterpret_cast<SsdSmem<N>*>(ssd_smem_raw);
+
+  const int h = blockIdx.x;
+  const int64_t b = (int64_t)blockIdx.y + a.row0;
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int r16 = lane & 15, g = lane >> 4;
+  const int dim = a.dim, H = a.nheads;
+  const int64_t L = a.seqlen;
+  const float Ah = a.A[h];
+  const float A2 = Ah * kLog2e;
+  const bool coef_is_dt = EULER || Ah == 0.0f;  // the Euler rule, or the hold's a -> 0 limit
+  const int p = 16 * w + r16;                   // this lane's channel (result column)
+  const int d = h * kHD + p;
+  const float Dp = a.Dskip ? a.Dskip[d] : 0.0f;
+
+  // state tile nt: st[nt][q] = h[n = 16 nt + 4 g + q][p]
+  f32x4_t st[NT];
+  if (a.h0) {
+    const float* src = a.h0 + ((size_t)b * dim + d) * N + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) st[nt] = *reinterpret_cast<const f32x4_t*>(src + 16 * nt);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Staging registers: lane t holds step t of the chunk -- 16 channels
+  // (16w..16w+15) of x and z, NPW states (NPW w ..) of B and C, and (wave 0)
+  // dt.  Rows past the end of the sequence read as zero (buffer bounds), which
+  // makes them steps with dt = 0: no change of state, and their outputs are
+  // not stored.
+  u32x4_t rx[2], rz[2], rb[NV], rc[NV];
+  uint32_t rdt = 0;
+  auto fetch = [&](int64_t t0) {
+    const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
+    const uint16_t* xb = static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim;
+    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(xb, rows * (uint32_t)dim * 2u);
+    const uint32_t ox = (uint32_t)lane * (uint32_t)dim * 2u + (uint32_t)(h * kHD + 16 * w) * 2u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      rx[j] = __builtin_bit_cast(u32x4_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(rsx, ox + 16u * j, 0, 0));
+    if constexpr (HAS_Z) {
+      const uint16_t* zb = static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim;
+      const __amdgpu_buffer_rsrc_t rsz = make_rsrc(zb, rows * (uint32_t)dim * 2u);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        rz[j] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsz, ox + 16u * j, 0, 0));
+    }
+    const __amdgpu_buffer_rsrc_t rsb =
+        make_rsrc(static_cast<const uint16_t*>(a.B) + (b * L + t0) * N, rows * N * 2u);
+    const __amdgpu_buffer_rsrc_t rsc =
+        make_rsrc(static_cast<const uint16_t*>(a.C) + (b * L + t0) * N, rows * N * 2u);
+    const uint32_t ob = (uint32_t)lane * N * 2u + (uint32_t)(NPW * w) * 2u;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      rb[j] = __builtin_bit_cast(u32x4_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(rsb, ob + 16u * j, 0, 0));
+      rc[j] = __builtin_bit_cast(u32x4_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(rsc, ob + 16u * j, 0, 0));
+    }
+    if (w == 0) {
+      const __amdgpu_buffer_rsrc_t rsd =
+          make_rsrc(static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows * (uint32_t)H * 2u);
+      rdt = __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)lane * H * 2u + h * 2u, 0, 0);
+    }
+  };
+
+  const int nck = (int)((L + kQ - 1) / kQ);
+  fetch(0);
+  for (int c = 0; c < nck; ++c) {
+    const int64_t t0 = (int64_t)c * kQ;
+    __syncthreads();  // every read of the previous chunk's LDS is done
+
+    // ---- stage: natural and transposed copies -------------------------
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = 8 * j + 2 * m;
+        sm.xt[16 * w + k][lane] = (uint16_t)(rx[j][m] & 0xffffu);
+        sm.xt[16 * w + k + 1][lane] = (uint16_t)(rx[j][m] >> 16);
+        if constexpr (HAS_Z) {
+          sm.zt[16 * w + k][lane] = (uint16_t)(rz[j][m] & 0xffffu);
+          sm.zt[16 * w + k + 1][lane] = (uint16_t)(rz[j][m] >> 16);
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      *reinterpret_cast<u32x4_t*>(&sm.bs[lane][NPW * w + 8 * j]) = rb[j];
+      *reinterpret_cast<u32x4_t*>(&sm.cs[lane][NPW * w + 8 * j]) = rc[j];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int n = NPW * w + 8 * j + 2 * m;
+        sm.bt[n][lane] = (uint16_t)(rb[j][m] & 0xffffu);
+        sm.bt[n + 1][lane] = (uint16_t)(rb[j][m] >> 16);
+      }
+    }
+    if (w == 0) {
+      // decay exponents: inclusive prefix sum of a * dt over the chunk
+      const float dtv = bf16_bits_to_f32(rdt);
+      float s = dtv * A2;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const float v = __shfl_up(s, o);
+        if (lane >= o) s += v;
+      }
+      const float last = __shfl(s, kWave - 1);
+      const float cf = coef_is_dt ? dtv : expm1f(dtv * Ah) / Ah;
+      sm.s2[lane] = s;
+      sm.coef[lane] = cf;
+      sm.wgt[lane] = fast_exp2(last - s) * cf;
+      sm.ein[lane] = fast_exp2(s);
+    }
+    __syncthreads();
+
+    // ---- weighted inputs w_t x_t (high / low parts), then prefetch ------
+    {
+      const float wt = sm.wgt[lane];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int k = 16 * w + 8 * j + 2 * m;
+          uint32_t hi, lo;
+          split_bf16(wt * bf16_lo(rx[j][m]), wt * bf16_hi(rx[j][m]), hi, lo);
+          sm.wxh[k][lane] = (uint16_t)(hi & 0xffffu);
+          sm.wxh[k + 1][lane] = (uint16_t)(hi >> 16);
+          sm.wxl[k][lane] = (uint16_t)(lo & 0xffffu);
+          sm.wxl[k + 1][lane] = (uint16_t)(lo >> 16);
+        }
+    }
+    if (c + 1 < nck) fetch(t0 + kQ);
+
+    // ---- masked weights P: this wave's lower-triangular tiles -----------
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const int code = kPTiles[w][e];
+      if (code < 0) continue;
+      const int I = code >> 4, J = code & 15;
+      // M^T tile: rows j (B rows), columns i (C rows), k = states
+      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < N / 32; ++k)
+        m = mfma_k32(lds128(&sm.bs[16 * J + r16][32 * k + 8 * g]),
+                     lds128(&sm.cs[16 * I + r16][32 * k + 8 * g]), m);
+      // m[q] = C_i . B_j with i = 16 I + r16, j = 16 J + 4 g + q
+      const int i = 16 * I + r16;
+      const float si = sm.s2[i];
+      const f32x4_t sj = *reinterpret_cast<const f32x4_t*>(&sm.s2[16 * J + 4 * g]);
+      const f32x4_t cj = *reinterpret_cast<const f32x4_t*>(&sm.coef[16 * J + 4 * g]);
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = 16 * J + 4 * g + q;
+        v[q] = (j <= i) ? m[q] * fast_exp2(si - sj[q]) * cj[q] : 0.0f;
+      }
+      uint32_t h0w, l0w, h1w, l1w;
+      split_bf16(v[0], v[1], h0w, l0w);
+      split_bf16(v[2], v[3], h1w, l1w);
+      *reinterpret_cast<u32x2_t*>(&sm.pmh[i][16 * J + 4 * g]) = u32x2_t{h0w, h1w};
+      *reinterpret_cast<u32x2_t*>(&sm.pml[i][16 * J + 4 * g]) = u32x2_t{l0w, l1w};
+    }
+    __syncthreads();
+
+    // ---- outputs of the chunk for this wave's 16 channels ---------------
+    // the entering state as B operands of C h^T: slots 0..3 = tile 2k,
+    // slots 4..7 = tile 2k + 1 (states 32k + 4g + q and 32k + 16 + 4g + q)
+    u32x4_t sh[NT / 2], sl[NT / 2];
+#pragma unroll
+    for (int k = 0; k < NT / 2; ++k) {
+      uint32_t hw[4], lw[4];
+      split_bf16(st[2 * k][0], st[2 * k][1], hw[0], lw[0]);
+      split_bf16(st[2 * k][2], st[2 * k][3], hw[1], lw[1]);
+      split_bf16(st[2 * k + 1][0], st[2 * k + 1][1], hw[2], lw[2]);
+      split_bf16(st[2 * k + 1][2], st[2 * k + 1][3], hw[3], lw[3]);
+      sh[k] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+      sl[k] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+    }
+    const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
+    const __amdgpu_buffer_rsrc_t rsy =
+        make_rsrc(static_cast<uint16_t*>(a.y) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const int i = 16 * I + r16;
+      f32x4_t yin = {0.f, 0.f, 0.f, 0.f}, yst = {0.f, 0.f, 0.f, 0.f};
+      // in-chunk part: tiles J = 0..I of P times x, two tiles per product
+#pragma unroll
+      for (int J = 0; J + 1 <= I; J += 2) {
+        const u32x4_t xo = cat(lds64(&sm.xt[p][16 * J + 4 * g]), lds64(&sm.xt[p][16 * J + 16 + 4 * g]));
+        yin = mfma_k32(cat(lds64(&sm.pmh[i][16 * J + 4 * g]), lds64(&sm.pmh[i][16 * J + 16 + 4 * g])),
+                       xo, yin);
+        yin = mfma_k32(cat(lds64(&sm.pml[i][16 * J + 4 * g]), lds64(&sm.pml[i][16 * J + 16 + 4 * g])),
+                       xo, yin);
+      }
+      if ((I & 1) == 0) {  // odd tile count: the diagonal tile alone, slots 4..7 zero
+        const u32x2_t zero = {0u, 0u};
+        const u32x4_t xo = cat(lds64(&sm.xt[p][16 * I + 4 * g]), zero);
+        yin = mfma_k32(cat(lds64(&sm.pmh[i][16 * I + 4 * g]), zero), xo, yin);
+        yin = mfma_k32(cat(lds64(&sm.pml[i][16 * I + 4 * g]), zero), xo, yin);
+      }
+      // entering state: C rows i times h (states 32k + 4g + q, 32k + 16 + 4g + q)
+#pragma unroll
+      for (int k = 0; k < NT / 2; ++k) {
+        const u32x4_t co = cat(lds64(&sm.cs[i][32 * k + 4 * g]), lds64(&sm.cs[i][32 * k + 16 + 4 * g]));
+        yst = mfma_k32(co, sh[k], yst);
+        yst = mfma_k32(co, sl[k], yst);
+      }
+      // epilogue: rows 16 I + 4 g + q, column p
+      const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ein[16 * I + 4 * g]);
+      const u32x2_t xr = lds64(&sm.xt[p][16 * I + 4 * g]);
+      u32x2_t zr = {0u, 0u};
+      if constexpr (HAS_Z) zr = lds64(&sm.zt[p][16 * I + 4 * g]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t xw = xr[q >> 1];
+        const float xv = (q & 1) ? bf16_hi(xw) : bf16_lo(xw);
+        float out = __builtin_fmaf(e[q], yst[q], yin[q]) + Dp * xv;
+        if constexpr (HAS_Z) {
+          const uint32_t zw = zr[q >> 1];
+          out *= silu((q & 1) ? bf16_hi(zw) : bf16_lo(zw));
+        }
+        const uint32_t row = (uint32_t)(16 * I + 4 * g + q);
+        __builtin_amdgcn_raw_buffer_store_b16(
+            f32_to_bf16_bits(out), rsy, row * (uint32_t)dim * 2u + (uint32_t)(h * kHD + p) * 2u, 0,
+            0);
+      }
+    }
+
+    // ---- state update: h <- exp(s_63) h + (w x)^T B --------------------
+    const float dec = fast_exp2(sm.s2[kQ - 1]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      st[nt] *= dec;
+#pragma unroll
+      for (int k = 0; k < kQ / 32; ++k) {
+        const u32x4_t bo = lds128(&sm.bt[16 * nt + r16][32 * k + 8 * g]);
+        st[nt] = mfma_k32(bo, lds128(&sm.wxh[p][32 * k + 8 * g]), st[nt]);
+        st[nt] = mfma_k32(bo, lds128(&sm.wxl[p][32 * k + 8 * g]), st[nt]);
+      }
+    }
+  }
+
+  if (a.h_last) {
+    float* dst = a.h_last + ((size_t)b * dim + d) * N + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4_t*>(dst + 16 * nt) = st[nt];
+  }
+}
+
+template <int N, bool HAS_Z, bool EULER>
+hipError_t launch_ssd_t(SsdArgs a, hipStream_t stream) {
+  auto kern = ssd_scan_kernel<N, HAS_Z, EULER>;
+  const size_t smem = sizeof(SsdSmem<N>);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  constexpr int64_t kMaxRows = 65535;  // grid.y limit
+  for (int64_t r0 = 0; r0 < a.batch; r0 += kMaxRows) {
+    a.row0 = r0;
+    const int rows = (int)(a.batch - r0 < kMaxRows ? a.batch - r0 : kMaxRows);
+    hipLaunchKernelGGL(kern, dim3(a.nheads, rows), dim3(kSsdThreads), smem, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int N>
+hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {
+  if (a.z) return a.euler ? launch_ssd_t<N, true, true>(a, stream)
+                          : launch_ssd_t<N, true, false>(a, stream);
+  return a.euler ? launch_ssd_t<N, false, true>(a, stream)
+                 : launch_ssd_t<N, false, false>(a, stream);
+}
+
+}  // namespace
+
+bool ssd_supported(int64_t headdim, int64_t dstate) {
+  return headdim == kHD && (dstate == 64 || dstate == 128);
+}
+
+size_t ssd_smem_bytes(int64_t dstate) {
+  return dstate == 64 ? sizeof(SsdSmem<64>) : sizeof(SsdSmem<128>);
+}
+
+hipError_t launch_ssd(const SsdArgs& a, int dstate, hipStream_t stream) {
+  switch (dstate) {
+    case 64: return launch_ssd_n<64>(a, stream);
+    case 128: return launch_ssd_n<128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssm

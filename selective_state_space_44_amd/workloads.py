@@ -15,6 +15,11 @@ distributions of the benchmark configurations:
 * ``B, C[b,t,n]  ~ N(0, 1)``                          (rounded to the I/O dtype)
 * ``h0 = 0`` for the scan; the decode state is ``h[b,d,n] ~ N(0, 1)`` (fp32).
 
+Inputs of the scan with step and decay shared per head (``make_ssd_inputs``;
+heads of 64 channels, Mamba-2-like layer of 80 heads and 128 states): the
+same distributions drawn per head instead of per channel,
+``A[h] = -U(0.5, 1.5)`` and ``dt[b,t,h] = softplus(0.5 * N(0, 1) - 3)``.
+
 Inputs of the fused scan (prologue + scan; ``make_fused_inputs``): the raw
 block inputs before the causal depthwise convolution and the softplus:
 
@@ -46,7 +51,7 @@ import torch.nn.functional as F
 class Workload:
     name: str
     seed_id: int
-    kind: str            # "scan" or "decode"
+    kind: str            # "scan", "decode" or "ssd" (step and decay per head)
     batch: int
     seqlen: int          # 1 for decode
     dim: int
@@ -55,6 +60,7 @@ class Workload:
     layers: int = 1
     per_channel_bias: bool = False
     cpu_draw: bool = False
+    headdim: int = 0     # channels per head ("ssd" workloads)
 
     @property
     def elements(self) -> int:
@@ -71,6 +77,10 @@ class Workload:
         step also reads and writes its fp32 state [b, d, n]."""
         s = self.io_bytes
         b, L, d, n = self.batch, self.seqlen, self.dim, self.dstate
+        if self.kind == "ssd":
+            # x, z in and y out ([b, L, d]); dt ([b, L, heads]); B, C; A [heads], Dskip
+            heads = d // self.headdim
+            return b * L * (3 * d + heads + 2 * n) * s + 4 * heads + 4 * d
         total = b * L * (4 * d + 2 * n) * s + 4 * d * n + 4 * d
         if self.kind == "decode":
             total += 2 * 4 * b * d * n
@@ -88,6 +98,8 @@ WORKLOADS = {
                  torch.bfloat16, per_channel_bias=True),
         Workload("decode_b256_d5120_64layers", 4, "decode", 256, 1, 5120, 16,
                  torch.bfloat16, layers=64),
+        Workload("mamba2_2p7b_b4_l4096_h80_p64_n128", 5, "ssd", 4, 4096, 5120, 128,
+                 torch.bfloat16, headdim=64),
     ]
 }
 TINY = WORKLOADS["tiny_f32_b1_l256_d64"]
@@ -95,6 +107,7 @@ MAMBA_130M = WORKLOADS["mamba130m_b8_l2048_d1536"]
 MAMBA_2P8B = WORKLOADS["mamba2p8b_b4_l4096_d5120"]
 LONG_CTX = WORKLOADS["longctx_b1_l262144_d4096"]
 DECODE_64L = WORKLOADS["decode_b256_d5120_64layers"]
+SSD_2P7B = WORKLOADS["mamba2_2p7b_b4_l4096_h80_p64_n128"]
 
 
 def seed(w: Workload, layer: int, k: int) -> int:
@@ -182,3 +195,26 @@ def make_fused_inputs(w: Workload, device="cpu", layer: int = 0, batch: int | No
     return dict(x_raw=x_raw, conv_w=conv_w, conv_b=conv_b, delta_raw=delta_raw,
                 delta_bias=delta_bias, A=base["A"], B=base["B"], C=base["C"], D=base["D"],
                 z=base["z"], h0=None)
+
+
+def make_ssd_inputs(w: Workload, device="cpu", layer: int = 0, batch: int | None = None,
+                    seqlen: int | None = None, nheads: int | None = None,
+                    dstate: int | None = None) -> dict:
+    """Inputs of the scan with step and decay shared per head: x, z
+    [b, L, heads * headdim], dt [b, L, heads], B, C [b, L, n] in the I/O dtype;
+    A [heads] and Dskip [heads * headdim] fp32; h0 None."""
+    assert w.kind == "ssd" and w.headdim > 0
+    b = w.batch if batch is None else batch
+    L = w.seqlen if seqlen is None else seqlen
+    H = w.dim // w.headdim if nheads is None else nheads
+    n = w.dstate if dstate is None else dstate
+    d = H * w.headdim
+    io = w.io_dtype
+    A = -(0.5 + _draw("uniform", (H,), w, layer, K_A, device))
+    Dskip = _draw("normal", (d,), w, layer, K_DSKIP, device)
+    x = _draw("normal", (b, L, d), w, layer, K_X, device).to(io)
+    dt = F.softplus(0.5 * _draw("normal", (b, L, H), w, layer, K_DELTA, device) - 3.0).to(io)
+    z = _draw("normal", (b, L, d), w, layer, K_Z, device).to(io)
+    B = _draw("normal", (b, L, n), w, layer, K_B, device).to(io)
+    C = _draw("normal", (b, L, n), w, layer, K_C, device).to(io)
+    return dict(x=x, dt=dt, A=A.contiguous(), B=B, C=C, D=Dskip, z=z, h0=None)

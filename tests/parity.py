@@ -108,3 +108,25 @@ def check_grad(got, ref, io_dtype, what):
         raise AssertionError(f"{what}: {int(bad.sum())} of {ref.size} outside tolerance; "
                              f"worst at {i}: got {got[i]!r} ref {ref[i]!r} bound {bound[i]!r}")
     return float(np.max(err / bound))
+
+
+def oracle_ssd(inp: dict, headdim: int = 64, heads=None, nthreads: int = 0,
+               discretization: str = "zoh"):
+    """Oracle of the scan with step and decay shared per head on the inputs
+    dict of ``ssd_scan`` (device tensors); ``heads`` optionally restricts to a
+    subset of heads (heads are independent).  Returns (y, h_last) over the
+    selected heads' channels."""
+    x, dt, A, B, C = inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"]
+    D, z, h0 = inp.get("D"), inp.get("z"), inp.get("h0")
+    if heads is not None:
+        hidx = torch.as_tensor(heads, device=x.device, dtype=torch.long)
+        cidx = (hidx[:, None] * headdim + torch.arange(headdim, device=x.device)).reshape(-1)
+        x = x.index_select(2, cidx)
+        z = z.index_select(2, cidx) if z is not None else None
+        D = D.index_select(0, cidx) if D is not None else None
+        h0 = h0.index_select(1, cidx) if h0 is not None else None
+        dt = dt.index_select(2, hidx)
+        A = A.index_select(0, hidx)
+    return oracle.scan_heads(to_f64(x), to_f64(dt), to_f64(A), to_f64(B), to_f64(C),
+                             to_f64(D), to_f64(z), to_f64(h0), headdim=headdim,
+                             nthreads=nthreads, discretization=discretization)

@@ -125,6 +125,32 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(batch=0) == ssm.SSM_OK
 
 
+def test_ssd_rejects_bad_arguments(lib):
+    """Every case fails validation (or is a no-op) before any launch."""
+    def ssd(batch=2, L=8, H=2, P=64, N=128, io=1, disc=ssm.SSM_DISC_ZOH, x=FAKE, A=FAKE,
+            y=ctypes.c_void_p(0x2000), h_last=None):
+        return lib.ssm_ssd_fwd(batch, L, H, P, N, io, disc, x, ctypes.c_void_p(0x6000), A,
+                               ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), None, None,
+                               None, y, h_last, None)
+    assert ssd(batch=-1) == ssm.SSM_ERR_INVALID_ARG
+    assert ssd(L=-1) == ssm.SSM_ERR_INVALID_ARG
+    assert ssd(P=0) == ssm.SSM_ERR_INVALID_ARG
+    assert ssd(io=7) == ssm.SSM_ERR_INVALID_ARG
+    assert ssd(disc=2) == ssm.SSM_ERR_INVALID_ARG
+    assert ssd(io=0) == ssm.SSM_ERR_UNSUPPORTED               # bf16 only
+    assert ssd(P=32) == ssm.SSM_ERR_UNSUPPORTED               # heads of 64 channels
+    assert ssd(N=16) == ssm.SSM_ERR_UNSUPPORTED               # 64 or 128 states
+    assert ssd(H=(1 << 18) + 1) == ssm.SSM_ERR_UNSUPPORTED    # 32-bit chunk offsets
+    assert ssd(A=None) == ssm.SSM_ERR_INVALID_ARG
+    assert ssd(x=None) == ssm.SSM_ERR_INVALID_ARG
+    assert ssd(y=FAKE) == ssm.SSM_ERR_INVALID_ARG             # y aliases x
+    assert ssd(h_last=FAKE) == ssm.SSM_ERR_INVALID_ARG        # h_last aliases x
+    assert ssd(x=ctypes.c_void_p(0x1001)) == ssm.SSM_ERR_INVALID_ARG  # misaligned
+    assert ssd(batch=0) == ssm.SSM_OK
+    assert ssd(H=0) == ssm.SSM_OK
+    assert ssd(L=0) == ssm.SSM_OK                             # no h_last: nothing to write
+
+
 def test_plan_and_workspace(lib):
     g, k = ssm.scan_plan(4, 4096, 5120)
     assert g in (1, 2, 4, 8, 16) and k >= 1

@@ -68,27 +68,31 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kQ = 64;            // steps per chunk
+constexpr int kQ = 32;            // steps per chunk
 constexpr int kHD = 64;           // channels per head
-constexpr int kSsdThreads = 256;  // 4 waves, one per 16 channels of the head
-constexpr int kRowT = kQ + 8;     // bf16 per step-contiguous LDS row: 144 B, so
-                                  // rows start 4 banks apart
+constexpr int kBC = 32;           // channels per block (half a head)
+constexpr int kSsdThreads = 256;  // 4 waves: 2 channel tiles x 2 state halves
+constexpr int kRowT = kQ + 8;     // bf16 per step-contiguous LDS row: 80 B, so
+                                  // 8 consecutive rows start on distinct banks
 
 template <int N>
 struct SsdSmem {
-  static constexpr int kRowN = N + 8;  // bf16 per state-contiguous row
-  alignas(16) uint16_t cs[kQ][kRowN];  // C of the chunk, [t][n]
-  alignas(16) uint16_t bs[kQ][kRowN];  // B, [t][n]
-  alignas(16) uint16_t bt[N][kRowT];   // B, [n][t]
-  alignas(16) uint16_t xt[kHD][kRowT];   // x, [p][t]
-  alignas(16) uint16_t zt[kHD][kRowT];   // z, [p][t]
-  alignas(16) uint16_t wxh[kHD][kRowT];  // w_t x_t[p], bf16 high part, [p][t]
-  alignas(16) uint16_t wxl[kHD][kRowT];  // low part
+  static constexpr int kRowN = N + 8;    // bf16 per state-contiguous row
+  alignas(16) uint16_t cs[kQ][kRowN];    // C of the chunk, [t][n]
+  alignas(16) uint16_t bs[kQ][kRowN];    // B, [t][n]
+  alignas(16) uint16_t bt[N][kRowT];     // B, [n][t]
+  alignas(16) uint16_t xt[kBC][kRowT];   // x, [p][t]
+  alignas(16) uint16_t zt[kBC][kRowT];   // z, [p][t]
+  alignas(16) uint16_t wxh[kBC][kRowT];  // w_t x_t[p], bf16 high part, [p][t]
+  alignas(16) uint16_t wxl[kBC][kRowT];  // low part
   alignas(16) uint16_t pmh[kQ][kRowT];   // masked weights P[i][j], high part
   alignas(16) uint16_t pml[kQ][kRowT];   // low part
+  // C h over one state half, for the row tile the other half's wave finishes:
+  // [channel tile][row tile][lane][result register]
+  alignas(16) float part[2][2][kWave][4];
   alignas(16) float s2[kQ];     // s_t * log2(e)
   alignas(16) float coef[kQ];   // coef_t
-  alignas(16) float wgt[kQ];    // exp(s_63 - s_t) coef_t
+  alignas(16) float wgt[kQ];    // exp(s_last - s_t) coef_t
   alignas(16) float ein[kQ];    // exp(s_t)
 };
 
@@ -120,160 +124,151 @@ __device__ __forceinline__ u32x2_t lds64(const uint16_t* p) {
 }
 __device__ __forceinline__ u32x4_t cat(u32x2_t a, u32x2_t b) { return {a.x, a.y, b.x, b.y}; }
 
-// The lower-triangular tiles (I, J), J <= I, of P computed by each wave,
-// encoded 16 I + J; -1 = none.
-__constant__ const int kPTiles[4][3] = {
-    {0x00, 0x10, 0x11}, {0x20, 0x21, 0x22}, {0x30, 0x31, -1}, {0x32, 0x33, -1}};
-
 template <int N, bool HAS_Z, bool EULER>
-__global__ __launch_bounds__(kSsdThreads, 1) void ssd_scan_kernel(SsdArgs a) {
-  constexpr int NT = N / 16;    // state tiles per wave
-  constexpr int NPW = N / 4;    // B / C columns staged by each wave
-  constexpr int NV = NPW / 8;   // 16-byte pieces of them
+__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void ssd_scan_kernel(SsdArgs a) {
+  constexpr int NT2 = N / 32;   // state tiles per wave (half of the N/16)
+  constexpr int NK = N / 64;    // 32-state contraction steps per state half
+  constexpr int NB = N / 8;     // B / C columns staged by each thread
+  constexpr int NBV = NB / 8;   // 16-byte pieces of them
   extern __shared__ __align__(16) unsigned char ssd_smem_raw[];
   SsdSmem<N>& sm = *reinterpret_cast<SsdSmem<N>*>(ssd_smem_raw);
 
-  const int h = blockIdx.x;
+  const int h = blockIdx.x >> 1, half = blockIdx.x & 1;
   const int64_t b = (int64_t)blockIdx.y + a.row0;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int w = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
+  const int pt = w & 1, nh = w >> 1;           // channel tile, state half (= row tile)
   const int dim = a.dim, H = a.nheads;
   const int64_t L = a.seqlen;
   const float Ah = a.A[h];
   const float A2 = Ah * kLog2e;
   const bool coef_is_dt = EULER || Ah == 0.0f;  // the Euler rule, or the hold's a -> 0 limit
-  const int p = 16 * w + r16;                   // this lane's channel (result column)
-  const int d = h * kHD + p;
+  const int cb = h * kHD + kBC * half;          // first channel of the block
+  const int p = 16 * pt + r16;                  // this lane's channel in the block
+  const int d = cb + p;
   const float Dp = a.Dskip ? a.Dskip[d] : 0.0f;
+  const int ts = tid & (kQ - 1), cg = tid >> 5;  // staging: step, column group
 
-  // state tile nt: st[nt][q] = h[n = 16 nt + 4 g + q][p]
-  f32x4_t st[NT];
+  // state tile j: st[j][q] = h[n = 16 (nh NT2 + j) + 4 g + q][p]
+  f32x4_t st[NT2];
   if (a.h0) {
-    const float* src = a.h0 + ((size_t)b * dim + d) * N + 4 * g;
+    const float* src = a.h0 + ((size_t)b * dim + d) * N + 16 * nh * NT2 + 4 * g;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) st[nt] = *reinterpret_cast<const f32x4_t*>(src + 16 * nt);
+    for (int j = 0; j < NT2; ++j) st[j] = *reinterpret_cast<const f32x4_t*>(src + 16 * j);
   } else {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT2; ++j) st[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Staging registers: lane t holds step t of the chunk -- 16 channels
-  // (16w..16w+15) of x and z, NPW states (NPW w ..) of B and C, and (wave 0)
-  // dt.  Rows past the end of the sequence read as zero (buffer bounds), which
-  // makes them steps with dt = 0: no change of state, and their outputs are
-  // not stored.
-  u32x4_t rx[2], rz[2], rb[NV], rc[NV];
+  // Staging registers: thread (ts, cg) holds step ts of the chunk -- channels
+  // 4cg..4cg+3 of the block for x and z, states NB cg .. NB cg + NB - 1 of B
+  // and C, and (wave 0, lanes < kQ) dt.  Rows past the end of the sequence
+  // read as zero (buffer bounds): steps with dt = 0, which leave the state
+  // unchanged, and whose outputs are not stored.
+  u32x2_t rx, rz = {0u, 0u};
+  u32x4_t rb[NBV], rc[NBV];
   uint32_t rdt = 0;
   auto fetch = [&](int64_t t0) {
     const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
-    const uint16_t* xb = static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim;
-    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(xb, rows * (uint32_t)dim * 2u);
-    const uint32_t ox = (uint32_t)lane * (uint32_t)dim * 2u + (uint32_t)(h * kHD + 16 * w) * 2u;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      rx[j] = __builtin_bit_cast(u32x4_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(rsx, ox + 16u * j, 0, 0));
+    const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(cb + 4 * cg) * 2u;
+    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(
+        static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
+    rx = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsx, ox, 0, 0));
     if constexpr (HAS_Z) {
-      const uint16_t* zb = static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim;
-      const __amdgpu_buffer_rsrc_t rsz = make_rsrc(zb, rows * (uint32_t)dim * 2u);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        rz[j] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsz, ox + 16u * j, 0, 0));
+      const __amdgpu_buffer_rsrc_t rsz = make_rsrc(
+          static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
+      rz = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsz, ox, 0, 0));
     }
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(static_cast<const uint16_t*>(a.B) + (b * L + t0) * N, rows * N * 2u);
     const __amdgpu_buffer_rsrc_t rsc =
         make_rsrc(static_cast<const uint16_t*>(a.C) + (b * L + t0) * N, rows * N * 2u);
-    const uint32_t ob = (uint32_t)lane * N * 2u + (uint32_t)(NPW * w) * 2u;
+    const uint32_t ob = (uint32_t)ts * N * 2u + (uint32_t)(NB * cg) * 2u;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+    for (int j = 0; j < NBV; ++j) {
       rb[j] = __builtin_bit_cast(u32x4_t,
                                  __builtin_amdgcn_raw_buffer_load_b128(rsb, ob + 16u * j, 0, 0));
       rc[j] = __builtin_bit_cast(u32x4_t,
                                  __builtin_amdgcn_raw_buffer_load_b128(rsc, ob + 16u * j, 0, 0));
     }
     if (w == 0) {
-      const __amdgpu_buffer_rsrc_t rsd =
-          make_rsrc(static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows * (uint32_t)H * 2u);
-      rdt = __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)lane * H * 2u + h * 2u, 0, 0);
+      const __amdgpu_buffer_rsrc_t rsd = make_rsrc(
+          static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows * (uint32_t)H * 2u);
+      rdt = lane < kQ
+                ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)lane * H * 2u + h * 2u, 0, 0)
+                : 0u;
     }
   };
 
-  const int nck = (int)((L + kQ - 1) / kQ);
+  const int64_t nck = (L + kQ - 1) / kQ;
   fetch(0);
-  for (int c = 0; c < nck; ++c) {
-    const int64_t t0 = (int64_t)c * kQ;
+  for (int64_t c = 0; c < nck; ++c) {
+    const int64_t t0 = c * kQ;
     __syncthreads();  // every read of the previous chunk's LDS is done
 
-    // ---- stage: natural and transposed copies -------------------------
+    // ---- stage: natural and transposed copies, decay exponents ----------
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = 8 * j + 2 * m;
-        sm.xt[16 * w + k][lane] = (uint16_t)(rx[j][m] & 0xffffu);
-        sm.xt[16 * w + k + 1][lane] = (uint16_t)(rx[j][m] >> 16);
-        if constexpr (HAS_Z) {
-          sm.zt[16 * w + k][lane] = (uint16_t)(rz[j][m] & 0xffffu);
-          sm.zt[16 * w + k + 1][lane] = (uint16_t)(rz[j][m] >> 16);
-        }
+    for (int m = 0; m < 2; ++m) {
+      sm.xt[4 * cg + 2 * m][ts] = (uint16_t)(rx[m] & 0xffffu);
+      sm.xt[4 * cg + 2 * m + 1][ts] = (uint16_t)(rx[m] >> 16);
+      if constexpr (HAS_Z) {
+        sm.zt[4 * cg + 2 * m][ts] = (uint16_t)(rz[m] & 0xffffu);
+        sm.zt[4 * cg + 2 * m + 1][ts] = (uint16_t)(rz[m] >> 16);
       }
+    }
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      *reinterpret_cast<u32x4_t*>(&sm.bs[lane][NPW * w + 8 * j]) = rb[j];
-      *reinterpret_cast<u32x4_t*>(&sm.cs[lane][NPW * w + 8 * j]) = rc[j];
+    for (int j = 0; j < NBV; ++j) {
+      *reinterpret_cast<u32x4_t*>(&sm.bs[ts][NB * cg + 8 * j]) = rb[j];
+      *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = rc[j];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int n = NPW * w + 8 * j + 2 * m;
-        sm.bt[n][lane] = (uint16_t)(rb[j][m] & 0xffffu);
-        sm.bt[n + 1][lane] = (uint16_t)(rb[j][m] >> 16);
+        const int n = NB * cg + 8 * j + 2 * m;
+        sm.bt[n][ts] = (uint16_t)(rb[j][m] & 0xffffu);
+        sm.bt[n + 1][ts] = (uint16_t)(rb[j][m] >> 16);
       }
     }
     if (w == 0) {
-      // decay exponents: inclusive prefix sum of a * dt over the chunk
+      // inclusive prefix sum of a * dt over the chunk's steps (lanes < kQ)
       const float dtv = bf16_bits_to_f32(rdt);
       float s = dtv * A2;
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
+      for (int o = 1; o < kQ; o <<= 1) {
         const float v = __shfl_up(s, o);
         if (lane >= o) s += v;
       }
-      const float last = __shfl(s, kWave - 1);
-      const float cf = coef_is_dt ? dtv : expm1f(dtv * Ah) / Ah;
-      sm.s2[lane] = s;
-      sm.coef[lane] = cf;
-      sm.wgt[lane] = fast_exp2(last - s) * cf;
-      sm.ein[lane] = fast_exp2(s);
+      const float last = __shfl(s, kQ - 1);
+      if (lane < kQ) {
+        const float cf = coef_is_dt ? dtv : expm1f(dtv * Ah) / Ah;
+        sm.s2[lane] = s;
+        sm.coef[lane] = cf;
+        sm.wgt[lane] = fast_exp2(last - s) * cf;
+        sm.ein[lane] = fast_exp2(s);
+      }
     }
     __syncthreads();
 
     // ---- weighted inputs w_t x_t (high / low parts), then prefetch ------
     {
-      const float wt = sm.wgt[lane];
+      const float wt = sm.wgt[ts];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int k = 16 * w + 8 * j + 2 * m;
-          uint32_t hi, lo;
-          split_bf16(wt * bf16_lo(rx[j][m]), wt * bf16_hi(rx[j][m]), hi, lo);
-          sm.wxh[k][lane] = (uint16_t)(hi & 0xffffu);
-          sm.wxh[k + 1][lane] = (uint16_t)(hi >> 16);
-          sm.wxl[k][lane] = (uint16_t)(lo & 0xffffu);
-          sm.wxl[k + 1][lane] = (uint16_t)(lo >> 16);
-        }
+      for (int m = 0; m < 2; ++m) {
+        uint32_t hi, lo;
+        split_bf16(wt * bf16_lo(rx[m]), wt * bf16_hi(rx[m]), hi, lo);
+        const int k = 4 * cg + 2 * m;
+        sm.wxh[k][ts] = (uint16_t)(hi & 0xffffu);
+        sm.wxh[k + 1][ts] = (uint16_t)(hi >> 16);
+        sm.wxl[k][ts] = (uint16_t)(lo & 0xffffu);
+        sm.wxl[k + 1][ts] = (uint16_t)(lo >> 16);
+      }
     }
     if (c + 1 < nck) fetch(t0 + kQ);
 
-    // ---- masked weights P: this wave's lower-triangular tiles -----------
-#pragma unroll
-    for (int e = 0; e < 3; ++e) {
-      const int code = kPTiles[w][e];
-      if (code < 0) continue;
-      const int I = code >> 4, J = code & 15;
-      // M^T tile: rows j (B rows), columns i (C rows), k = states
+    // ---- masked weights P: tiles (0,0), (1,0), (1,1) on waves 0..2 ------
+    if (w < 3) {
+      const int I = w > 0 ? 1 : 0, J = w == 1 ? 0 : I;
+      // M^T tile: rows j (B rows), columns i (C rows), contraction over states
       f32x4_t m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < N / 32; ++k)
@@ -296,90 +291,84 @@ __global__ __launch_bounds__(kSsdThreads, 1) void ssd_scan_kernel(SsdArgs a) {
       *reinterpret_cast<u32x2_t*>(&sm.pmh[i][16 * J + 4 * g]) = u32x2_t{h0w, h1w};
       *reinterpret_cast<u32x2_t*>(&sm.pml[i][16 * J + 4 * g]) = u32x2_t{l0w, l1w};
     }
-    __syncthreads();
 
-    // ---- outputs of the chunk for this wave's 16 channels ---------------
-    // the entering state as B operands of C h^T: slots 0..3 = tile 2k,
-    // slots 4..7 = tile 2k + 1 (states 32k + 4g + q and 32k + 16 + 4g + q)
-    u32x4_t sh[NT / 2], sl[NT / 2];
+    // ---- C h over this wave's state half, both row tiles ----------------
+    // the entering state as B operands: slots 0..3 = tile 2k, 4..7 = tile
+    // 2k + 1 of the half (states nh N/2 + 32k + 4g + q and + 16)
+    f32x4_t yst[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int k = 0; k < NT / 2; ++k) {
+    for (int k = 0; k < NK; ++k) {
       uint32_t hw[4], lw[4];
       split_bf16(st[2 * k][0], st[2 * k][1], hw[0], lw[0]);
       split_bf16(st[2 * k][2], st[2 * k][3], hw[1], lw[1]);
       split_bf16(st[2 * k + 1][0], st[2 * k + 1][1], hw[2], lw[2]);
       split_bf16(st[2 * k + 1][2], st[2 * k + 1][3], hw[3], lw[3]);
-      sh[k] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-      sl[k] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+      const u32x4_t sh = {hw[0], hw[1], hw[2], hw[3]}, sl = {lw[0], lw[1], lw[2], lw[3]};
+      const int n0 = nh * (N / 2) + 32 * k + 4 * g;
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        const u32x4_t co = cat(lds64(&sm.cs[16 * I + r16][n0]), lds64(&sm.cs[16 * I + r16][n0 + 16]));
+        yst[I] = mfma_k32(co, sh, yst[I]);
+        yst[I] = mfma_k32(co, sl, yst[I]);
+      }
     }
-    const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
-    const __amdgpu_buffer_rsrc_t rsy =
-        make_rsrc(static_cast<uint16_t*>(a.y) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const int i = 16 * I + r16;
-      f32x4_t yin = {0.f, 0.f, 0.f, 0.f}, yst = {0.f, 0.f, 0.f, 0.f};
-      // in-chunk part: tiles J = 0..I of P times x, two tiles per product
-#pragma unroll
-      for (int J = 0; J + 1 <= I; J += 2) {
-        const u32x4_t xo = cat(lds64(&sm.xt[p][16 * J + 4 * g]), lds64(&sm.xt[p][16 * J + 16 + 4 * g]));
-        yin = mfma_k32(cat(lds64(&sm.pmh[i][16 * J + 4 * g]), lds64(&sm.pmh[i][16 * J + 16 + 4 * g])),
-                       xo, yin);
-        yin = mfma_k32(cat(lds64(&sm.pml[i][16 * J + 4 * g]), lds64(&sm.pml[i][16 * J + 16 + 4 * g])),
-                       xo, yin);
-      }
-      if ((I & 1) == 0) {  // odd tile count: the diagonal tile alone, slots 4..7 zero
-        const u32x2_t zero = {0u, 0u};
-        const u32x4_t xo = cat(lds64(&sm.xt[p][16 * I + 4 * g]), zero);
-        yin = mfma_k32(cat(lds64(&sm.pmh[i][16 * I + 4 * g]), zero), xo, yin);
-        yin = mfma_k32(cat(lds64(&sm.pml[i][16 * I + 4 * g]), zero), xo, yin);
-      }
-      // entering state: C rows i times h (states 32k + 4g + q, 32k + 16 + 4g + q)
-#pragma unroll
-      for (int k = 0; k < NT / 2; ++k) {
-        const u32x4_t co = cat(lds64(&sm.cs[i][32 * k + 4 * g]), lds64(&sm.cs[i][32 * k + 16 + 4 * g]));
-        yst = mfma_k32(co, sh[k], yst);
-        yst = mfma_k32(co, sl[k], yst);
-      }
+    // the other half's wave finishes row tile 1 - nh
+    *reinterpret_cast<f32x4_t*>(&sm.part[pt][1 - nh][lane][0]) = nh ? yst[0] : yst[1];
+    __syncthreads();
+
+    // ---- outputs of row tile I = nh for this wave's 16 channels ---------
+    {
+      const int I = nh, i = 16 * I + r16;
+      f32x4_t yin = {0.f, 0.f, 0.f, 0.f};
+      const u32x2_t zero = {0u, 0u};
+      // in-chunk part: row tile 0 has the diagonal tile alone (slots 4..7
+      // zero), row tile 1 the tiles 0 and 1 in one product
+      const u32x4_t xo = cat(lds64(&sm.xt[p][4 * g]), I ? lds64(&sm.xt[p][16 + 4 * g]) : zero);
+      yin = mfma_k32(cat(lds64(&sm.pmh[i][4 * g]), I ? lds64(&sm.pmh[i][16 + 4 * g]) : zero), xo,
+                     yin);
+      yin = mfma_k32(cat(lds64(&sm.pml[i][4 * g]), I ? lds64(&sm.pml[i][16 + 4 * g]) : zero), xo,
+                     yin);
+      const f32x4_t other = *reinterpret_cast<const f32x4_t*>(&sm.part[pt][I][lane][0]);
+      const f32x4_t ys = (nh ? yst[1] : yst[0]) + other;
       // epilogue: rows 16 I + 4 g + q, column p
       const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ein[16 * I + 4 * g]);
       const u32x2_t xr = lds64(&sm.xt[p][16 * I + 4 * g]);
       u32x2_t zr = {0u, 0u};
       if constexpr (HAS_Z) zr = lds64(&sm.zt[p][16 * I + 4 * g]);
+      const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
+      const __amdgpu_buffer_rsrc_t rsy =
+          make_rsrc(static_cast<uint16_t*>(a.y) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t xw = xr[q >> 1];
         const float xv = (q & 1) ? bf16_hi(xw) : bf16_lo(xw);
-        float out = __builtin_fmaf(e[q], yst[q], yin[q]) + Dp * xv;
+        float out = __builtin_fmaf(e[q], ys[q], yin[q]) + Dp * xv;
         if constexpr (HAS_Z) {
           const uint32_t zw = zr[q >> 1];
           out *= silu((q & 1) ? bf16_hi(zw) : bf16_lo(zw));
         }
         const uint32_t row = (uint32_t)(16 * I + 4 * g + q);
-        __builtin_amdgcn_raw_buffer_store_b16(
-            f32_to_bf16_bits(out), rsy, row * (uint32_t)dim * 2u + (uint32_t)(h * kHD + p) * 2u, 0,
-            0);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(out), rsy,
+                                              row * (uint32_t)dim * 2u + (uint32_t)d * 2u, 0, 0);
       }
     }
 
-    // ---- state update: h <- exp(s_63) h + (w x)^T B --------------------
+    // ---- state update: h <- exp(s_last) h + (w x)^T B, this half --------
     const float dec = fast_exp2(sm.s2[kQ - 1]);
+    const u32x4_t wh = lds128(&sm.wxh[p][8 * g]), wl = lds128(&sm.wxl[p][8 * g]);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      st[nt] *= dec;
-#pragma unroll
-      for (int k = 0; k < kQ / 32; ++k) {
-        const u32x4_t bo = lds128(&sm.bt[16 * nt + r16][32 * k + 8 * g]);
-        st[nt] = mfma_k32(bo, lds128(&sm.wxh[p][32 * k + 8 * g]), st[nt]);
-        st[nt] = mfma_k32(bo, lds128(&sm.wxl[p][32 * k + 8 * g]), st[nt]);
-      }
+    for (int j = 0; j < NT2; ++j) {
+      const u32x4_t bo = lds128(&sm.bt[16 * (nh * NT2 + j) + r16][8 * g]);
+      st[j] *= dec;
+      st[j] = mfma_k32(bo, wh, st[j]);
+      st[j] = mfma_k32(bo, wl, st[j]);
     }
   }
 
   if (a.h_last) {
-    float* dst = a.h_last + ((size_t)b * dim + d) * N + 4 * g;
+    float* dst = a.h_last + ((size_t)b * dim + d) * N + 16 * nh * NT2 + 4 * g;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4_t*>(dst + 16 * nt) = st[nt];
+    for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = st[j];
   }
 }
 
@@ -394,7 +383,7 @@ hipError_t launch_ssd_t(SsdArgs a, hipStream_t stream) {
   for (int64_t r0 = 0; r0 < a.batch; r0 += kMaxRows) {
     a.row0 = r0;
     const int rows = (int)(a.batch - r0 < kMaxRows ? a.batch - r0 : kMaxRows);
-    hipLaunchKernelGGL(kern, dim3(a.nheads, rows), dim3(kSsdThreads), smem, stream, a);
+    hipLaunchKernelGGL(kern, dim3(2 * a.nheads, rows), dim3(kSsdThreads), smem, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -22,21 +22,25 @@
 //   * h_out^T = B^T (w x) with w_t = exp(s_63 - s_t) coef_t (contraction over
 //     the steps).
 //
-// Organisation: one block (4 waves) per (head, batch row) walks the chunks in
-// order, so the state never leaves the registers and no carry pass exists.
-// Wave w owns the 16 channels p = 16w..16w+15 of the head: it holds the
-// state h[n][p] of those channels as N/16 MFMA accumulator tiles, computes
-// their outputs for all 64 steps, and updates their state.  The 64 x 64
-// matrix P is shared by the four waves: its ten lower-triangular 16 x 16
-// tiles are computed once per chunk (3, 3, 2, 2 tiles per wave) and passed
-// through LDS.
+// Organisation: one block per (half head of 32 channels, batch row) walks
+// 32-step chunks in order, so the state never leaves the registers and no
+// carry pass exists.  Its 4 waves are 2 channel tiles x 2 state halves: wave
+// (pt, nh) holds the state h[n][p] of channels p = 16pt..16pt+15 and states
+// n in half nh as N/32 MFMA accumulator tiles, updates them, and computes
+// C h over its half for the chunk's two 16-step row tiles; it finishes row
+// tile nh (its partial plus the other half's, passed through LDS).  The
+// chunk's 32 x 32 matrix P has three lower-triangular 16 x 16 tiles, one on
+// each of waves 0..2, passed through LDS.  At the Mamba-2-like shape (4 x 80
+// heads) this makes 640 blocks of ~47 KB LDS, all resident at once (2-3 per
+// CU).
 //
-// Data movement per chunk: the chunk's x, z (64 steps x 64 channels), B, C
-// (64 steps x N) and dt are loaded into registers one chunk ahead, then
+// Data movement per chunk: the chunk's x, z (32 steps x 32 channels), B, C
+// (32 steps x N) and dt are loaded into registers two chunks ahead, then
 // written to LDS, x, z and B also transposed (step index contiguous), since
-// every operand must be contiguous in its contraction index.  Three barriers
-// per chunk: staging written, then P and w x written, then (next chunk) all
-// reads done.
+// every operand must be contiguous in its contraction index.  The decay
+// exponents of a chunk (a prefix sum over its steps) are computed one chunk
+// ahead by the wave that has no P tile.  Three barriers per chunk: staging
+// written; P, w x and the partial C h written; (next chunk) all reads done.
 //
 // Precision: B, C and x are bf16 inputs, exact as MFMA operands.  The other
 // operands -- the masked weights P, the state h and the weighted inputs w x --
@@ -90,10 +94,12 @@ struct SsdSmem {
   // C h over one state half, for the row tile the other half's wave finishes:
   // [channel tile][row tile][lane][result register]
   alignas(16) float part[2][2][kWave][4];
-  alignas(16) float s2[kQ];     // s_t * log2(e)
-  alignas(16) float coef[kQ];   // coef_t
-  alignas(16) float wgt[kQ];    // exp(s_last - s_t) coef_t
-  alignas(16) float ein[kQ];    // exp(s_t)
+  // per-step values of the chunk (two buffers: the next chunk's are
+  // computed while the current one runs)
+  alignas(16) float s2[2][kQ];     // s_t * log2(e)
+  alignas(16) float coef[2][kQ];   // coef_t
+  alignas(16) float wgt[2][kQ];    // exp(s_last - s_t) coef_t
+  alignas(16) float ein[2][kQ];    // exp(s_t)
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo_elem, float hi_elem) {
@@ -162,24 +168,34 @@ void ssd_scan_kernel(SsdArgs a) {
     for (int j = 0; j < NT2; ++j) st[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Staging registers: thread (ts, cg) holds step ts of the chunk -- channels
+  // Staging registers: thread (ts, cg) holds step ts of a chunk -- channels
   // 4cg..4cg+3 of the block for x and z, states NB cg .. NB cg + NB - 1 of B
-  // and C, and (wave 0, lanes < kQ) dt.  Rows past the end of the sequence
-  // read as zero (buffer bounds): steps with dt = 0, which leave the state
-  // unchanged, and whose outputs are not stored.
-  u32x2_t rx, rz = {0u, 0u};
-  u32x4_t rb[NBV], rc[NBV];
-  uint32_t rdt = 0;
-  auto fetch = [&](int64_t t0) {
+  // and C, and (wave 3, lanes < kQ) dt.  Two sets: the loads of chunk c + 2
+  // are issued while chunk c runs.  Rows past the end of the sequence read as
+  // zero (buffer bounds): steps with dt = 0, which leave the state unchanged,
+  // and whose outputs are not stored.
+  struct Stage {
+    u32x2_t x, z;
+    u32x4_t b[NBV], c[NBV];
+    uint32_t dt;
+  };
+  auto fetch = [&](Stage& sg, int64_t t0) {
     const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
+    if (w == 3) {
+      const __amdgpu_buffer_rsrc_t rsd = make_rsrc(
+          static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows * (uint32_t)H * 2u);
+      sg.dt = lane < kQ
+                  ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)lane * H * 2u + h * 2u, 0, 0)
+                  : 0u;
+    }
     const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(cb + 4 * cg) * 2u;
     const __amdgpu_buffer_rsrc_t rsx = make_rsrc(
         static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
-    rx = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsx, ox, 0, 0));
+    sg.x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsx, ox, 0, 0));
     if constexpr (HAS_Z) {
       const __amdgpu_buffer_rsrc_t rsz = make_rsrc(
           static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
-      rz = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsz, ox, 0, 0));
+      sg.z = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsz, ox, 0, 0));
     }
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(static_cast<const uint16_t*>(a.B) + (b * L + t0) * N, rows * N * 2u);
@@ -188,74 +204,68 @@ void ssd_scan_kernel(SsdArgs a) {
     const uint32_t ob = (uint32_t)ts * N * 2u + (uint32_t)(NB * cg) * 2u;
 #pragma unroll
     for (int j = 0; j < NBV; ++j) {
-      rb[j] = __builtin_bit_cast(u32x4_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(rsb, ob + 16u * j, 0, 0));
-      rc[j] = __builtin_bit_cast(u32x4_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(rsc, ob + 16u * j, 0, 0));
+      sg.b[j] = __builtin_bit_cast(u32x4_t,
+                                   __builtin_amdgcn_raw_buffer_load_b128(rsb, ob + 16u * j, 0, 0));
+      sg.c[j] = __builtin_bit_cast(u32x4_t,
+                                   __builtin_amdgcn_raw_buffer_load_b128(rsc, ob + 16u * j, 0, 0));
     }
-    if (w == 0) {
-      const __amdgpu_buffer_rsrc_t rsd = make_rsrc(
-          static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows * (uint32_t)H * 2u);
-      rdt = lane < kQ
-                ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)lane * H * 2u + h * 2u, 0, 0)
-                : 0u;
+  };
+  // wave 3: the chunk's decay exponents (inclusive prefix sum of a * dt over
+  // its steps, lanes < kQ) and per-step weights, into buffer `buf`
+  auto scan = [&](const Stage& sg, int buf) {
+    const float dtv = bf16_bits_to_f32(sg.dt);
+    float s = dtv * A2;
+#pragma unroll
+    for (int o = 1; o < kQ; o <<= 1) {
+      const float v = __shfl_up(s, o);
+      if (lane >= o) s += v;
+    }
+    const float last = __shfl(s, kQ - 1);
+    if (lane < kQ) {
+      const float cf = coef_is_dt ? dtv : expm1f(dtv * Ah) / Ah;
+      sm.s2[buf][lane] = s;
+      sm.coef[buf][lane] = cf;
+      sm.wgt[buf][lane] = fast_exp2(last - s) * cf;
+      sm.ein[buf][lane] = fast_exp2(s);
     }
   };
 
   const int64_t nck = (L + kQ - 1) / kQ;
-  fetch(0);
-  for (int64_t c = 0; c < nck; ++c) {
+  auto chunk = [&](int64_t c, Stage& cur, const Stage& nxt) {
     const int64_t t0 = c * kQ;
+    const int buf = (int)(c & 1);
     __syncthreads();  // every read of the previous chunk's LDS is done
 
-    // ---- stage: natural and transposed copies, decay exponents ----------
+    // ---- stage: natural and transposed copies --------------------------
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      sm.xt[4 * cg + 2 * m][ts] = (uint16_t)(rx[m] & 0xffffu);
-      sm.xt[4 * cg + 2 * m + 1][ts] = (uint16_t)(rx[m] >> 16);
+      sm.xt[4 * cg + 2 * m][ts] = (uint16_t)(cur.x[m] & 0xffffu);
+      sm.xt[4 * cg + 2 * m + 1][ts] = (uint16_t)(cur.x[m] >> 16);
       if constexpr (HAS_Z) {
-        sm.zt[4 * cg + 2 * m][ts] = (uint16_t)(rz[m] & 0xffffu);
-        sm.zt[4 * cg + 2 * m + 1][ts] = (uint16_t)(rz[m] >> 16);
+        sm.zt[4 * cg + 2 * m][ts] = (uint16_t)(cur.z[m] & 0xffffu);
+        sm.zt[4 * cg + 2 * m + 1][ts] = (uint16_t)(cur.z[m] >> 16);
       }
     }
 #pragma unroll
     for (int j = 0; j < NBV; ++j) {
-      *reinterpret_cast<u32x4_t*>(&sm.bs[ts][NB * cg + 8 * j]) = rb[j];
-      *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = rc[j];
+      *reinterpret_cast<u32x4_t*>(&sm.bs[ts][NB * cg + 8 * j]) = cur.b[j];
+      *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = cur.c[j];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int n = NB * cg + 8 * j + 2 * m;
-        sm.bt[n][ts] = (uint16_t)(rb[j][m] & 0xffffu);
-        sm.bt[n + 1][ts] = (uint16_t)(rb[j][m] >> 16);
-      }
-    }
-    if (w == 0) {
-      // inclusive prefix sum of a * dt over the chunk's steps (lanes < kQ)
-      const float dtv = bf16_bits_to_f32(rdt);
-      float s = dtv * A2;
-#pragma unroll
-      for (int o = 1; o < kQ; o <<= 1) {
-        const float v = __shfl_up(s, o);
-        if (lane >= o) s += v;
-      }
-      const float last = __shfl(s, kQ - 1);
-      if (lane < kQ) {
-        const float cf = coef_is_dt ? dtv : expm1f(dtv * Ah) / Ah;
-        sm.s2[lane] = s;
-        sm.coef[lane] = cf;
-        sm.wgt[lane] = fast_exp2(last - s) * cf;
-        sm.ein[lane] = fast_exp2(s);
+        sm.bt[n][ts] = (uint16_t)(cur.b[j][m] & 0xffffu);
+        sm.bt[n + 1][ts] = (uint16_t)(cur.b[j][m] >> 16);
       }
     }
     __syncthreads();
 
     // ---- weighted inputs w_t x_t (high / low parts), then prefetch ------
     {
-      const float wt = sm.wgt[ts];
+      const float wt = sm.wgt[buf][ts];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         uint32_t hi, lo;
-        split_bf16(wt * bf16_lo(rx[m]), wt * bf16_hi(rx[m]), hi, lo);
+        split_bf16(wt * bf16_lo(cur.x[m]), wt * bf16_hi(cur.x[m]), hi, lo);
         const int k = 4 * cg + 2 * m;
         sm.wxh[k][ts] = (uint16_t)(hi & 0xffffu);
         sm.wxh[k + 1][ts] = (uint16_t)(hi >> 16);
@@ -263,10 +273,10 @@ void ssd_scan_kernel(SsdArgs a) {
         sm.wxl[k + 1][ts] = (uint16_t)(lo >> 16);
       }
     }
-    if (c + 1 < nck) fetch(t0 + kQ);
+    if (c + 2 < nck) fetch(cur, t0 + 2 * kQ);
 
-    // ---- masked weights P: tiles (0,0), (1,0), (1,1) on waves 0..2 ------
     if (w < 3) {
+      // ---- masked weights P: tiles (0,0), (1,0), (1,1) on waves 0..2 ----
       const int I = w > 0 ? 1 : 0, J = w == 1 ? 0 : I;
       // M^T tile: rows j (B rows), columns i (C rows), contraction over states
       f32x4_t m = {0.f, 0.f, 0.f, 0.f};
@@ -276,9 +286,9 @@ void ssd_scan_kernel(SsdArgs a) {
                      lds128(&sm.cs[16 * I + r16][32 * k + 8 * g]), m);
       // m[q] = C_i . B_j with i = 16 I + r16, j = 16 J + 4 g + q
       const int i = 16 * I + r16;
-      const float si = sm.s2[i];
-      const f32x4_t sj = *reinterpret_cast<const f32x4_t*>(&sm.s2[16 * J + 4 * g]);
-      const f32x4_t cj = *reinterpret_cast<const f32x4_t*>(&sm.coef[16 * J + 4 * g]);
+      const float si = sm.s2[buf][i];
+      const f32x4_t sj = *reinterpret_cast<const f32x4_t*>(&sm.s2[buf][16 * J + 4 * g]);
+      const f32x4_t cj = *reinterpret_cast<const f32x4_t*>(&sm.coef[buf][16 * J + 4 * g]);
       float v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -290,6 +300,8 @@ void ssd_scan_kernel(SsdArgs a) {
       split_bf16(v[2], v[3], h1w, l1w);
       *reinterpret_cast<u32x2_t*>(&sm.pmh[i][16 * J + 4 * g]) = u32x2_t{h0w, h1w};
       *reinterpret_cast<u32x2_t*>(&sm.pml[i][16 * J + 4 * g]) = u32x2_t{l0w, l1w};
+    } else if (c + 1 < nck) {
+      scan(nxt, buf ^ 1);  // wave 3: the next chunk's per-step values
     }
 
     // ---- C h over this wave's state half, both row tiles ----------------
@@ -331,7 +343,7 @@ void ssd_scan_kernel(SsdArgs a) {
       const f32x4_t other = *reinterpret_cast<const f32x4_t*>(&sm.part[pt][I][lane][0]);
       const f32x4_t ys = (nh ? yst[1] : yst[0]) + other;
       // epilogue: rows 16 I + 4 g + q, column p
-      const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ein[16 * I + 4 * g]);
+      const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ein[buf][16 * I + 4 * g]);
       const u32x2_t xr = lds64(&sm.xt[p][16 * I + 4 * g]);
       u32x2_t zr = {0u, 0u};
       if constexpr (HAS_Z) zr = lds64(&sm.zt[p][16 * I + 4 * g]);
@@ -354,7 +366,7 @@ void ssd_scan_kernel(SsdArgs a) {
     }
 
     // ---- state update: h <- exp(s_last) h + (w x)^T B, this half --------
-    const float dec = fast_exp2(sm.s2[kQ - 1]);
+    const float dec = fast_exp2(sm.s2[buf][kQ - 1]);
     const u32x4_t wh = lds128(&sm.wxh[p][8 * g]), wl = lds128(&sm.wxl[p][8 * g]);
 #pragma unroll
     for (int j = 0; j < NT2; ++j) {
@@ -363,6 +375,16 @@ void ssd_scan_kernel(SsdArgs a) {
       st[j] = mfma_k32(bo, wh, st[j]);
       st[j] = mfma_k32(bo, wl, st[j]);
     }
+  };
+
+  Stage sa, sb;
+  sb.dt = 0u;
+  fetch(sa, 0);
+  if (nck > 1) fetch(sb, kQ);
+  if (w == 3) scan(sa, 0);
+  for (int64_t c = 0; c < nck; c += 2) {
+    chunk(c, sa, sb);
+    if (c + 1 < nck) chunk(c + 1, sb, sa);
   }
 
   if (a.h_last) {

@@ -76,19 +76,17 @@ constexpr int kQ = 32;            // steps per chunk
 constexpr int kHD = 64;           // channels per head
 constexpr int kBC = 32;           // channels per block (half a head)
 constexpr int kSsdThreads = 256;  // 4 waves: 2 channel tiles x 2 state halves
-constexpr int kRowT = kQ + 8;     // bf16 per step-contiguous LDS row: 80 B, so
-                                  // 8 consecutive rows start on distinct banks
+constexpr int kRowT = kQ + 8;     // bf16 per row of P: 80 B, so 8 consecutive
+                                  // rows start on distinct banks
+constexpr int kRowX = kBC + 8;    // bf16 per row of the staged x and z
 
 template <int N>
 struct SsdSmem {
   static constexpr int kRowN = N + 8;    // bf16 per state-contiguous row
   alignas(16) uint16_t cs[kQ][kRowN];    // C of the chunk, [t][n]
   alignas(16) uint16_t bs[kQ][kRowN];    // B, [t][n]
-  alignas(16) uint16_t bt[N][kRowT];     // B, [n][t]
-  alignas(16) uint16_t xt[kBC][kRowT];   // x, [p][t]
-  alignas(16) uint16_t zt[kBC][kRowT];   // z, [p][t]
-  alignas(16) uint16_t wxh[kBC][kRowT];  // w_t x_t[p], bf16 high part, [p][t]
-  alignas(16) uint16_t wxl[kBC][kRowT];  // low part
+  alignas(16) uint16_t xs[kQ][kRowX];    // x of the block's channels, [t][p]
+  alignas(16) uint16_t zs[kQ][kRowX];    // z, [t][p]
   alignas(16) uint16_t pmh[kQ][kRowT];   // masked weights P[i][j], high part
   alignas(16) uint16_t pml[kQ][kRowT];   // low part
   // C h over one state half, for the row tile the other half's wave finishes:
@@ -130,6 +128,38 @@ __device__ __forceinline__ u32x2_t lds64(const uint16_t* p) {
 }
 __device__ __forceinline__ u32x4_t cat(u32x2_t a, u32x2_t b) { return {a.x, a.y, b.x, b.y}; }
 
+// Four values that are bf16 numbers (results of an identity product) as two
+// packed words; the conversion is exact.
+__device__ __forceinline__ u32x2_t to_bf16x4(f32x4_t v) {
+  return {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+}
+
+// B operand of an identity product that picks 16 of the A operand's 32
+// contraction columns: lane (column c = l % 16, slots k = 8g..8g+7) holds 1
+// where k == off + c.  A x I_off is then the 16 x 16 tile A[:, off..off+15] in
+// the result layout (column c, rows 4g..4g+3), which is the operand layout of
+// a product contracting over those rows: the transposes the contractions need
+// are done on the matrix cores instead of through LDS.
+__device__ __forceinline__ u32x4_t identity_pick(int off, int r16, int g) {
+  uint32_t wv[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t lo = (8 * g + 2 * m == off + r16) ? 0x3f80u : 0u;      // bf16 1.0
+    const uint32_t hi = (8 * g + 2 * m + 1 == off + r16) ? 0x3f80u : 0u;
+    wv[m] = lo | (hi << 16);
+  }
+  return {wv[0], wv[1], wv[2], wv[3]};
+}
+
+// B operand of the identity for an A operand that fills slots 0..3 of each
+// lane group with contraction index 4g + s (slots 4..7 zero): lane (column c,
+// group g) holds 1 in slot s < 4 where 4g + s == c.
+__device__ __forceinline__ u32x4_t identity_pick4(int r16, int g) {
+  const uint32_t e0 = (4 * g == r16) ? 0x3f80u : 0u, e1 = (4 * g + 1 == r16) ? 0x3f80u : 0u;
+  const uint32_t e2 = (4 * g + 2 == r16) ? 0x3f80u : 0u, e3 = (4 * g + 3 == r16) ? 0x3f80u : 0u;
+  return {e0 | (e1 << 16), e2 | (e3 << 16), 0u, 0u};
+}
+
 template <int N, bool HAS_Z, bool EULER>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void ssd_scan_kernel(SsdArgs a) {
@@ -167,6 +197,9 @@ void ssd_scan_kernel(SsdArgs a) {
 #pragma unroll
     for (int j = 0; j < NT2; ++j) st[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+
+  const u32x4_t ipick[2] = {identity_pick(0, r16, g), identity_pick(16, r16, g)};
+  const u32x4_t ipick4 = identity_pick4(r16, g);
 
   // Staging registers: thread (ts, cg) holds step ts of a chunk -- channels
   // 4cg..4cg+3 of the block for x and z, states NB cg .. NB cg + NB - 1 of B
@@ -236,43 +269,16 @@ void ssd_scan_kernel(SsdArgs a) {
     const int buf = (int)(c & 1);
     __syncthreads();  // every read of the previous chunk's LDS is done
 
-    // ---- stage: natural and transposed copies --------------------------
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      sm.xt[4 * cg + 2 * m][ts] = (uint16_t)(cur.x[m] & 0xffffu);
-      sm.xt[4 * cg + 2 * m + 1][ts] = (uint16_t)(cur.x[m] >> 16);
-      if constexpr (HAS_Z) {
-        sm.zt[4 * cg + 2 * m][ts] = (uint16_t)(cur.z[m] & 0xffffu);
-        sm.zt[4 * cg + 2 * m + 1][ts] = (uint16_t)(cur.z[m] >> 16);
-      }
-    }
+    // ---- stage the chunk in natural layout ----------------------------
+    *reinterpret_cast<u32x2_t*>(&sm.xs[ts][4 * cg]) = cur.x;
+    if constexpr (HAS_Z) *reinterpret_cast<u32x2_t*>(&sm.zs[ts][4 * cg]) = cur.z;
 #pragma unroll
     for (int j = 0; j < NBV; ++j) {
       *reinterpret_cast<u32x4_t*>(&sm.bs[ts][NB * cg + 8 * j]) = cur.b[j];
       *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = cur.c[j];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int n = NB * cg + 8 * j + 2 * m;
-        sm.bt[n][ts] = (uint16_t)(cur.b[j][m] & 0xffffu);
-        sm.bt[n + 1][ts] = (uint16_t)(cur.b[j][m] >> 16);
-      }
     }
     __syncthreads();
 
-    // ---- weighted inputs w_t x_t (high / low parts), then prefetch ------
-    {
-      const float wt = sm.wgt[buf][ts];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        uint32_t hi, lo;
-        split_bf16(wt * bf16_lo(cur.x[m]), wt * bf16_hi(cur.x[m]), hi, lo);
-        const int k = 4 * cg + 2 * m;
-        sm.wxh[k][ts] = (uint16_t)(hi & 0xffffu);
-        sm.wxh[k + 1][ts] = (uint16_t)(hi >> 16);
-        sm.wxl[k][ts] = (uint16_t)(lo & 0xffffu);
-        sm.wxl[k + 1][ts] = (uint16_t)(lo >> 16);
-      }
-    }
     if (c + 2 < nck) fetch(cur, t0 + 2 * kQ);
 
     if (w < 3) {
@@ -328,52 +334,87 @@ void ssd_scan_kernel(SsdArgs a) {
     *reinterpret_cast<f32x4_t*>(&sm.part[pt][1 - nh][lane][0]) = nh ? yst[0] : yst[1];
     __syncthreads();
 
+    // ---- x (and z) of this wave's channels in result layout ------------
+    // xc[tt][q] = x[16 tt + 4 g + q][p], exact, from identity products
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t xc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) xc[tt] = mfma_k32(lds128(&sm.xs[16 * tt + r16][8 * g]), ipick[pt], zero4);
+
     // ---- outputs of row tile I = nh for this wave's 16 channels ---------
     {
       const int I = nh, i = 16 * I + r16;
-      f32x4_t yin = {0.f, 0.f, 0.f, 0.f};
+      // in-chunk part P x: row tile 0 has the diagonal tile alone (slots
+      // 4..7 zero), row tile 1 the tiles 0 and 1 in one product; x as the B
+      // operand (column p, slots j = 4g + q and 16 + 4g + q)
       const u32x2_t zero = {0u, 0u};
-      // in-chunk part: row tile 0 has the diagonal tile alone (slots 4..7
-      // zero), row tile 1 the tiles 0 and 1 in one product
-      const u32x4_t xo = cat(lds64(&sm.xt[p][4 * g]), I ? lds64(&sm.xt[p][16 + 4 * g]) : zero);
-      yin = mfma_k32(cat(lds64(&sm.pmh[i][4 * g]), I ? lds64(&sm.pmh[i][16 + 4 * g]) : zero), xo,
-                     yin);
+      const u32x4_t xo = cat(to_bf16x4(xc[0]), I ? to_bf16x4(xc[1]) : zero);
+      f32x4_t yin = mfma_k32(cat(lds64(&sm.pmh[i][4 * g]), I ? lds64(&sm.pmh[i][16 + 4 * g]) : zero),
+                             xo, zero4);
       yin = mfma_k32(cat(lds64(&sm.pml[i][4 * g]), I ? lds64(&sm.pml[i][16 + 4 * g]) : zero), xo,
                      yin);
       const f32x4_t other = *reinterpret_cast<const f32x4_t*>(&sm.part[pt][I][lane][0]);
       const f32x4_t ys = (nh ? yst[1] : yst[0]) + other;
       // epilogue: rows 16 I + 4 g + q, column p
       const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ein[buf][16 * I + 4 * g]);
-      const u32x2_t xr = lds64(&sm.xt[p][16 * I + 4 * g]);
-      u32x2_t zr = {0u, 0u};
-      if constexpr (HAS_Z) zr = lds64(&sm.zt[p][16 * I + 4 * g]);
+      const f32x4_t xv = nh ? xc[1] : xc[0];
+      f32x4_t zv = zero4;
+      if constexpr (HAS_Z) zv = mfma_k32(lds128(&sm.zs[16 * I + r16][8 * g]), ipick[pt], zero4);
+      float out[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        out[q] = __builtin_fmaf(e[q], ys[q], yin[q]) + Dp * xv[q];
+        if constexpr (HAS_Z) out[q] *= silu(zv[q]);
+      }
+      // Store: the bf16 outputs (rows 16 I + 4 g + q, column p) taken as an
+      // A operand (row p, slots t) times the identity give the tile
+      // transposed in the result layout, lane (row t = 16 I + r16, channels
+      // 16 pt + 4 g .. + 3): one 8-byte store per lane instead of four
+      // 2-byte ones.  Exact (bf16 values times 1).
+      const u32x4_t ya = {pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3]), 0u, 0u};
+      const f32x4_t yt = mfma_k32(ya, ipick4, zero4);
       const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
       const __amdgpu_buffer_rsrc_t rsy =
           make_rsrc(static_cast<uint16_t*>(a.y) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t xw = xr[q >> 1];
-        const float xv = (q & 1) ? bf16_hi(xw) : bf16_lo(xw);
-        float out = __builtin_fmaf(e[q], ys[q], yin[q]) + Dp * xv;
-        if constexpr (HAS_Z) {
-          const uint32_t zw = zr[q >> 1];
-          out *= silu((q & 1) ? bf16_hi(zw) : bf16_lo(zw));
-        }
-        const uint32_t row = (uint32_t)(16 * I + 4 * g + q);
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(out), rsy,
-                                              row * (uint32_t)dim * 2u + (uint32_t)d * 2u, 0, 0);
-      }
+      __builtin_amdgcn_raw_buffer_store_b64(
+          __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, to_bf16x4(yt)), rsy,
+          (uint32_t)(16 * I + r16) * (uint32_t)dim * 2u + (uint32_t)(cb + 16 * pt + 4 * g) * 2u, 0,
+          0);
     }
 
     // ---- state update: h <- exp(s_last) h + (w x)^T B, this half --------
+    // B operand: w_t x_t[p] (column p, slots t = 4g + q and 16 + 4g + q),
+    // split into bf16 high and low parts
+    u32x4_t wh, wl;
+    {
+      const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(&sm.wgt[buf][4 * g]);
+      const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(&sm.wgt[buf][16 + 4 * g]);
+      uint32_t hw[4], lw[4];
+      split_bf16(w0[0] * xc[0][0], w0[1] * xc[0][1], hw[0], lw[0]);
+      split_bf16(w0[2] * xc[0][2], w0[3] * xc[0][3], hw[1], lw[1]);
+      split_bf16(w1[0] * xc[1][0], w1[1] * xc[1][1], hw[2], lw[2]);
+      split_bf16(w1[2] * xc[1][2], w1[3] * xc[1][3], hw[3], lw[3]);
+      wh = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+      wl = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+    }
     const float dec = fast_exp2(sm.s2[buf][kQ - 1]);
-    const u32x4_t wh = lds128(&sm.wxh[p][8 * g]), wl = lds128(&sm.wxl[p][8 * g]);
 #pragma unroll
-    for (int j = 0; j < NT2; ++j) {
-      const u32x4_t bo = lds128(&sm.bt[16 * (nh * NT2 + j) + r16][8 * g]);
-      st[j] *= dec;
-      st[j] = mfma_k32(bo, wh, st[j]);
-      st[j] = mfma_k32(bo, wl, st[j]);
+    for (int j2 = 0; j2 < NT2 / 2; ++j2) {
+      // states 32 n32 .. 32 n32 + 31 (two tiles of this half) of B, rows t
+      const int n32 = nh * (NT2 / 2) + j2;
+      const u32x4_t b0 = lds128(&sm.bs[r16][32 * n32 + 8 * g]);
+      const u32x4_t b1 = lds128(&sm.bs[16 + r16][32 * n32 + 8 * g]);
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        // A operand: row n = 32 n32 + 16 o + r16, slots t (B transposed by
+        // identity products, exact)
+        const u32x4_t bo = cat(to_bf16x4(mfma_k32(b0, ipick[o], zero4)),
+                               to_bf16x4(mfma_k32(b1, ipick[o], zero4)));
+        f32x4_t& sj = st[2 * j2 + o];
+        sj *= dec;
+        sj = mfma_k32(bo, wh, sj);
+        sj = mfma_k32(bo, wl, sj);
+      }
     }
   };
 

@@ -170,13 +170,27 @@ void ssd_scan_kernel(SsdArgs a) {
   extern __shared__ __align__(16) unsigned char ssd_smem_raw[];
   SsdSmem<N>& sm = *reinterpret_cast<SsdSmem<N>*>(ssd_smem_raw);
 
-  const int h = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int H = a.nheads;
+  // Block -> (head, half): the two halves of a head get block ids 8 apart,
+  // so that they run on the same XCD (blocks are dealt to the 8 XCDs in turn)
+  // and share its L2 for the 128-byte rows of x and z they split.
+  int h, half;
+  {
+    const int i = blockIdx.x, grp = i >> 4, r = i & 15;
+    if (8 * grp + 8 <= H) {
+      h = 8 * grp + (r & 7);
+      half = r >> 3;
+    } else {  // last, partial group of heads: plain order
+      h = 8 * grp + (r >> 1);
+      half = r & 1;
+    }
+  }
   const int64_t b = (int64_t)blockIdx.y + a.row0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
   const int pt = w & 1, nh = w >> 1;           // channel tile, state half (= row tile)
-  const int dim = a.dim, H = a.nheads;
+  const int dim = a.dim;
   const int64_t L = a.seqlen;
   const float Ah = a.A[h];
   const float A2 = Ah * kLog2e;

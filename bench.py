@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 # ALU roofline of the scan element: per element (b, t, d, n) the main pass
 # issues 6 fp32 VALU ops + 1 transcendental (exp2).  Per SIMD per clock: 32 fp32
 # lanes (157.3 TFLOP/s fp32 vector = 256 CU x 4 SIMD x 32 lanes x 2 x 2.4 GHz)
@@ -231,6 +232,72 @@ def bench_variants(steps: int, warmup: int):
     return {"workload": w.name, **res}
 
 
+def bench_ssd(steps: int, warmup: int):
+    """The scan with step and decay shared per head, in its masked-matrix form
+    on the matrix cores (``ssm_ssd_fwd``), at a Mamba-2-like layer: batch 4,
+    L 4096, 80 heads of 64 channels, 128 states, bf16.  Two input sets are
+    alternated (each ~0.5 GB, twice the Infinity Cache).  Also times the
+    per-channel recurrence kernels on the same problem (dt repeated over each
+    head's channels, A per channel)."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.SSD_2P7B
+    dev = "cuda:0"
+    sets = [W.make_ssd_inputs(w, device=dev, layer=i) for i in range(2)]
+    outs = [torch.empty_like(s["x"]) for s in sets]
+
+    def step(i):
+        f = sets[i % 2]
+        ssm.ssd_scan(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
+                     out=outs[i % 2])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+
+    # matrix-core work of the masked-matrix form at the kernel's 32-step chunks:
+    # per (batch row, head, chunk) the lower triangle of C B^T (Q(Q+1)/2 N) and of
+    # P x (Q(Q+1)/2 P), C h (Q N P) and the state update (Q N P) multiply-adds
+    Q, P, N = 32, w.headdim, w.dstate
+    heads = w.dim // P
+    chunks = (w.seqlen + Q - 1) // Q
+    flops = 2 * w.batch * heads * chunks * (Q * (Q + 1) // 2 * (N + P) + 2 * Q * N * P)
+    nbytes = w.algorithmic_bytes()
+
+    # the same problem on the per-channel recurrence kernels (one input set)
+    f = sets[0]
+    delta = f["dt"].repeat_interleave(P, dim=2).contiguous()
+    a_ch = f["A"].repeat_interleave(P).contiguous()
+    y2 = torch.empty_like(f["x"])
+    rec_steps = max(3, steps // 10)
+    ssm.scan_fwd(f["x"], delta, a_ch, f["B"], f["C"], f["D"], f["z"], None, out=y2)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(rec_steps):
+        ssm.scan_fwd(f["x"], delta, a_ch, f["B"], f["C"], f["D"], f["z"], None, out=y2)
+    e1.record()
+    torch.cuda.synchronize()
+    rec_ms = e0.elapsed_time(e1) / rec_steps
+    return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
+            "unit": "elements/s",
+            "mfma": {"algorithmic_flop": flops, "achieved": flops / (ms * 1e-3) / 1e12,
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+            "hbm": {"algorithmic_bytes": nbytes, "achieved": nbytes / (ms * 1e-3) / 1e9,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "recurrence_ms_per_step": rec_ms, "speedup_vs_recurrence": rec_ms / ms}
+
+
 def bench_backward(steps: int, warmup: int):
     """Backward of the scan at the same shape: all input gradients for an
     upstream dy (states recomputed, nothing kept from a forward call)."""
@@ -326,6 +393,8 @@ def main():
                     help="skip the A-per-channel / Euler scan variants")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the scan with the fused conv1d/softplus prologue")
+    ap.add_argument("--no-ssd", action="store_true",
+                    help="skip the masked-matrix scan with step and decay per head")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -398,6 +467,8 @@ def main():
         line["fused_prologue"] = bench_fused(max(10, args.steps // 4), max(10, args.warmup // 4))
     if not args.no_variants:
         line["variants"] = bench_variants(max(10, args.steps // 4), max(10, args.warmup // 4))
+    if not args.no_ssd:
+        line["ssd"] = bench_ssd(max(10, args.steps // 2), max(10, args.warmup // 10))
     if not args.no_backward:
         bwd = bench_backward(max(10, args.steps // 5), max(5, args.warmup // 20))
         bwd["time_vs_forward"] = bwd["ms_per_step"] / r["step_ms"]

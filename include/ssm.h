@@ -117,7 +117,9 @@ int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
  * SSM_ERR_UNSUPPORTED.
  * Outputs must not alias inputs (exact pointer equality is rejected).
  * seqlen == 0 writes h_last (= h0, or zeros) when given and nothing else;
- * batch == 0 or dim == 0 is a no-op.  Returns an SSM_* status.
+ * batch == 0 or dim == 0 is a no-op.  More than 65535 batch rows run as
+ * consecutive launches of at most 65528 rows on the stream (ssm_scan_fwd_phase
+ * then accepts only phase 3).  Returns an SSM_* status.
  */
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                  int io_dtype, const void *x, const void *delta, const float *A,
@@ -214,8 +216,8 @@ int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
  *   workspace   : at least ssm_scan_bwd_workspace_bytes(...) bytes.
  * Results are deterministic: every sum runs in a fixed order.  Outputs must
  * not alias inputs, each other or the workspace.  seqlen == 0 writes dA = 0,
- * dD = 0 and dh0 = dh_last (or 0).  dstate other than 16:
- * SSM_ERR_UNSUPPORTED.  Returns an SSM_* status.
+ * dD = 0 and dh0 = dh_last (or 0).  dstate other than 16, and more than 65535
+ * batch rows: SSM_ERR_UNSUPPORTED.  Returns an SSM_* status.
  */
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                  const void *x, const void *delta, const float *A, int a_per_channel,

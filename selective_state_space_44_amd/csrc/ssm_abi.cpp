@@ -43,6 +43,9 @@ void auto_plan(int64_t batch, int64_t seqlen, int64_t dim, int* G, int* K) {
 }
 
 constexpr int64_t kMaxGridYZ = 65535;  // HIP limit on grid.y and grid.z
+// Batch rows per launch when a scan has more than kMaxGridYZ rows: a multiple
+// of 8, so that every slice's tensor pointers keep 16-byte alignment.
+constexpr int64_t kSliceRows = 65528;
 
 // The kernels address one chunk of an [b, L, dim] tensor with 32-bit byte
 // offsets; a chunk spans at most this many bytes.
@@ -166,7 +169,28 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
   if (!all_aligned(x, delta, A, B, C, Dskip, z, h0, y, h_last, workspace) ||
       !all_aligned(pro.conv_w, pro.conv_b, pro.delta_bias))
     return SSM_ERR_INVALID_ARG;
-  if (batch > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  if (batch > kMaxGridYZ) {
+    // The kernels put batch rows on grid.y (at most 65535): run slices of
+    // kSliceRows rows in order on the stream.  Rows are independent and the
+    // workspace, sized for the whole batch, is reused slice by slice, which
+    // is why the two phases cannot be enqueued apart here.
+    if (phase != 3) return SSM_ERR_UNSUPPORTED;
+    const int64_t io = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+    const int64_t xrow = seqlen * dim * io, bcrow = seqlen * dstate * io, srow = dim * dstate * 4;
+    for (int64_t r0 = 0; r0 < batch; r0 += kSliceRows) {
+      auto at = [r0](const void* p, int64_t per_row) -> const char* {
+        return p ? static_cast<const char*>(p) + r0 * per_row : nullptr;
+      };
+      const int st = scan_entry(
+          std::min(kSliceRows, batch - r0), seqlen, dim, dstate, io_dtype, at(x, xrow),
+          at(delta, xrow), A, at(B, bcrow), at(C, bcrow), Dskip, at(z, xrow),
+          reinterpret_cast<const float*>(at(h0, srow)), const_cast<char*>(at(y, xrow)),
+          reinterpret_cast<float*>(const_cast<char*>(at(h_last, srow))), workspace,
+          workspace_bytes, waves_per_group, nchunks, phase, stream, pro, a_per_channel, euler);
+      if (st != SSM_OK) return st;
+    }
+    return SSM_OK;
+  }
   if (wide) {
     ssm::ScanArgs a{};
     a.x = x;

@@ -125,6 +125,21 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(batch=0) == ssm.SSM_OK
 
 
+def test_batch_limits(lib):
+    """More than 65535 batch rows: the forward scan slices them (but not when
+    its two phases are enqueued apart), the backward refuses; both checks
+    come before any launch."""
+    assert lib.ssm_scan_fwd_phase(65536, 8, 64, 16, 1, FAKE, ctypes.c_void_p(0x6000), FAKE,
+                                  ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), None, None,
+                                  None, ctypes.c_void_p(0x2000), None, None, 0, 0, 0, 1,
+                                  None) == ssm.SSM_ERR_UNSUPPORTED
+    p = [ctypes.c_void_p(0x1000 * k) for k in range(1, 20)]
+    st = lib.ssm_scan_bwd(65536, 8, 64, 16, 1, p[0], p[1], p[2], 0, ssm.SSM_DISC_ZOH, p[3], p[4],
+                          None, None, None, p[5], None, p[6], p[7], p[8], p[9], p[10], None,
+                          None, None, p[11], 1 << 40, None)
+    assert st == ssm.SSM_ERR_UNSUPPORTED
+
+
 def test_ssd_rejects_bad_arguments(lib):
     """Every case fails validation (or is a no-op) before any launch."""
     def ssd(batch=2, L=8, H=2, P=64, N=128, io=1, disc=ssm.SSM_DISC_ZOH, x=FAKE, A=FAKE,

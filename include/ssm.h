@@ -277,6 +277,23 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
                     const void *z, void *y, void *stream);
 
 /*
+ * ssm_decode_step with the variants of ssm_scan_fwd_ex: a_per_channel = 1
+ * takes A as [dim] (one value per channel shared by its states; the scalar A
+ * of Mamba-2, ihouse article "Mambaの進化の道のり"), discretization
+ * SSM_DISC_EULER uses Bbar = delta * B (paperlens tutorial, selection
+ * pseudo-code).  The result equals one step of ssm_scan_fwd_ex with the same
+ * flags and h0 = h.  For a step shared by a head of channels (as in
+ * ssm_ssd_fwd), pass delta and A repeated over the head's channels.  Other
+ * arguments and errors as ssm_decode_step; invalid flags return
+ * SSM_ERR_INVALID_ARG.
+ */
+int ssm_decode_step_ex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
+                       float *h, const void *x, const void *delta, const float *A,
+                       int a_per_channel, int discretization, const void *B,
+                       const void *C, const float *Dskip, const void *z, void *y,
+                       void *stream);
+
+/*
  * Selective scan whose step size and decay rate are shared by each head of
  * `headdim` consecutive channels, computed in the masked-matrix form on the
  * matrix cores (ihouse article, "Mambaの進化の道のり": with A reduced to a

@@ -56,6 +56,8 @@ SIGNATURES = {
     "ssm_scan_fwd_fused": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int, _vp,
                                   _vp] + [_vp] * 8 + [_vp, _sz, _int, _int, _vp]),
     "ssm_decode_step": (_int, [_i64, _i64, _i64, _int] + [_vp] * 9 + [_vp]),
+    "ssm_decode_step_ex": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _int, _int]
+                           + [_vp] * 6),
     "ssm_scan_bwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _int]),
     "ssm_scan_bwd": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
                      + [_vp] * 15 + [_vp, _sz, _vp]),
@@ -325,35 +327,48 @@ def scan_fwd_fused(x_raw, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None
     return (y, h_last) if return_last_state else y
 
 
-def decode_step(h, x, delta, A, B, C, D=None, z=None, out=None):
+def decode_step(h, x, delta, A, B, C, D=None, z=None, out=None, discretization: str = "zoh"):
     """One recurrent step.  h: [batch, dim, dstate] float32, updated in place;
     x, delta, z: [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16);
-    A [dim, dstate], D [dim] float32.  Returns y [batch, dim]."""
+    A [dim, dstate] (or [dim]: one value per channel), D [dim] float32.
+    ``discretization="euler"`` uses Bbar = delta*B.  Returns y [batch, dim]."""
     if not isinstance(h, torch.Tensor) or h.dim() != 3:
         raise ValueError("h must be a [batch, dim, dstate] tensor")
     device = h.device
     if device.type != "cuda":
         raise ValueError(f"tensors must be on a GPU, got {device}")
+    if discretization not in ("zoh", "euler"):
+        raise ValueError("discretization must be 'zoh' or 'euler'")
     batch, dim, dstate = h.shape
     if not isinstance(x, torch.Tensor):
         raise ValueError("x must be a tensor")
+    if not isinstance(A, torch.Tensor) or A.dim() not in (1, 2):
+        raise ValueError("A must be a [dim, dstate] or [dim] tensor")
+    per_channel = A.dim() == 1
     io = x.dtype
     code = _io_code(io)
     _require(h, "h", (batch, dim, dstate), torch.float32, device)
     _require(x, "x", (batch, dim), io, device)
     _require(delta, "delta", (batch, dim), io, device)
-    _require(A, "A", (dim, dstate), torch.float32, device)
+    _require(A, "A", (dim,) if per_channel else (dim, dstate), torch.float32, device)
     _require(B, "B", (batch, dstate), io, device)
     _require(C, "C", (batch, dstate), io, device)
     _require(D, "D", (dim,), torch.float32, device)
     _require(z, "z", (batch, dim), io, device)
-    if delta is None or A is None or B is None or C is None:
-        raise ValueError("delta, A, B and C are required")
+    if delta is None or B is None or C is None:
+        raise ValueError("delta, B and C are required")
     y = out if out is not None else torch.empty_like(x)
     _require(y, "out", (batch, dim), io, device)
-    st = load_library().ssm_decode_step(batch, dim, dstate, code, _ptr(h), _ptr(x),
-                                        _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                        _ptr(z), _ptr(y), _stream(device))
+    lib = load_library()
+    if per_channel or discretization != "zoh":
+        st = lib.ssm_decode_step_ex(batch, dim, dstate, code, _ptr(h), _ptr(x), _ptr(delta),
+                                    _ptr(A), int(per_channel),
+                                    SSM_DISC_EULER if discretization == "euler" else SSM_DISC_ZOH,
+                                    _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(device))
+        _check(st, "ssm_decode_step_ex")
+        return y
+    st = lib.ssm_decode_step(batch, dim, dstate, code, _ptr(h), _ptr(x), _ptr(delta), _ptr(A),
+                             _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(device))
     _check(st, "ssm_decode_step")
     return y
 

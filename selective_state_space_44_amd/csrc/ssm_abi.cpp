@@ -329,10 +329,13 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                               z, h0, y, h_last, workspace, workspace_bytes, 0, 0, stream);
 }
 
-int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* h,
-                    const void* x, const void* delta, const float* A, const void* B,
-                    const void* C, const float* Dskip, const void* z, void* y,
-                    void* stream) {
+int ssm_decode_step_ex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* h,
+                       const void* x, const void* delta, const float* A, int a_per_channel,
+                       int discretization, const void* B, const void* C, const float* Dskip,
+                       const void* z, void* y, void* stream) {
+  if (a_per_channel != 0 && a_per_channel != 1) return SSM_ERR_INVALID_ARG;
+  if (discretization != SSM_DISC_ZOH && discretization != SSM_DISC_EULER)
+    return SSM_ERR_INVALID_ARG;
   if (!sizes_ok(batch, 1, dim, dstate) || !valid_dtype(io_dtype)) return SSM_ERR_INVALID_ARG;
   if (batch == 0 || dim == 0) return SSM_OK;
   if (dstate != kDState && !ssm::scan_wide_supported(dstate)) return SSM_ERR_UNSUPPORTED;
@@ -356,8 +359,18 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, fl
   a.batch = batch;
   a.dim = (int)dim;
   a.dstate = (int)dstate;
+  a.a_per_channel = a_per_channel;
+  a.euler = discretization == SSM_DISC_EULER ? 1 : 0;
   return hip_status(ssm::launch_decode(a, io_dtype == SSM_DTYPE_BF16,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* h,
+                    const void* x, const void* delta, const float* A, const void* B,
+                    const void* C, const float* Dskip, const void* z, void* y,
+                    void* stream) {
+  return ssm_decode_step_ex(batch, dim, dstate, io_dtype, h, x, delta, A, 0, SSM_DISC_ZOH, B,
+                            C, Dskip, z, y, stream);
 }
 
 }  // extern "C"

@@ -14,7 +14,9 @@
 // partial plus DPP quad swaps, row half-mirror and mirror exchanges (and a
 // 16-lane shuffle for N = 128); lane 0 of the channel applies the skip term
 // and gate and stores y.  The grid's y dimension is the batch row, so no
-// 64-bit division splits a flat index.
+// 64-bit division splits a flat index.  Variants (template bit V, as in the
+// scan): A per channel (one exp and one coefficient per lane) and the Euler
+// rule Bbar = delta * B.
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -65,7 +67,19 @@ __device__ __forceinline__ float row_swap(float v) {
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
-template <typename IO, int N>
+// Variant bits of the decode kernel (as in the scan): A given per channel,
+// and the Euler rule Bbar = delta * B.
+constexpr int kDecScalarA = 1;
+constexpr int kDecEuler = 2;
+
+// One step of one state for the variants: Abar = exp(delta * A) (a = Abar
+// shared by the channel's states when A is per channel), coefficient k of B*x:
+// (Abar - 1)/A for the hold (delta at A == 0), delta for Euler.
+__device__ __forceinline__ float var_update(float h, float abar, float k, float bx) {
+  return __builtin_fmaf(abar, h, k * bx);
+}
+
+template <typename IO, int N, int V>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   constexpr int L = N / 4;  // lanes per channel
   const int t = blockIdx.x * 256 + threadIdx.x;  // (channel, quarter) in one batch row
@@ -79,7 +93,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   // and per-channel inputs go first and the streamed state (touched once per
   // step, so read and written non-temporally) last; on MI355X this order and
   // plain loads for x, delta and z measured fastest.
-  const v4f A = reinterpret_cast<const v4f*>(a.A)[(size_t)d * L + q];
+  v4f A;
+  if constexpr (V & kDecScalarA) {
+    const float ad = a.A[d];
+    A = v4f{ad, ad, ad, ad};
+  } else {
+    A = reinterpret_cast<const v4f*>(a.A)[(size_t)d * L + q];
+  }
   const float4 Bq = Quad<IO>::load(static_cast<const IO*>(a.B) + b * N + 4 * q);
   const float4 Cq = Quad<IO>::load(static_cast<const IO*>(a.C) + b * N + 4 * q);
   const float xv = io<IO>::load(static_cast<const IO*>(a.x) + ch);
@@ -95,10 +115,26 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const float Dd = a.Dskip ? dload : 0.0f;
   const float dl = dv * kLog2e;
 
-  h.x = zoh_update(h.x, A.x, __builtin_amdgcn_rcpf(A.x), dl, dv, Bq.x * xv);
-  h.y = zoh_update(h.y, A.y, __builtin_amdgcn_rcpf(A.y), dl, dv, Bq.y * xv);
-  h.z = zoh_update(h.z, A.z, __builtin_amdgcn_rcpf(A.z), dl, dv, Bq.z * xv);
-  h.w = zoh_update(h.w, A.w, __builtin_amdgcn_rcpf(A.w), dl, dv, Bq.w * xv);
+  if constexpr (V == 0) {
+    h.x = zoh_update(h.x, A.x, __builtin_amdgcn_rcpf(A.x), dl, dv, Bq.x * xv);
+    h.y = zoh_update(h.y, A.y, __builtin_amdgcn_rcpf(A.y), dl, dv, Bq.y * xv);
+    h.z = zoh_update(h.z, A.z, __builtin_amdgcn_rcpf(A.z), dl, dv, Bq.z * xv);
+    h.w = zoh_update(h.w, A.w, __builtin_amdgcn_rcpf(A.w), dl, dv, Bq.w * xv);
+  } else if constexpr (V & kDecScalarA) {
+    // one exp and one coefficient for the channel's states
+    const float abar = fast_exp2(dl * A.x);
+    const float k = (V & kDecEuler) ? dv
+                    : (A.x != 0.0f ? (abar - 1.0f) * __builtin_amdgcn_rcpf(A.x) : dv);
+    h.x = var_update(h.x, abar, k, Bq.x * xv);
+    h.y = var_update(h.y, abar, k, Bq.y * xv);
+    h.z = var_update(h.z, abar, k, Bq.z * xv);
+    h.w = var_update(h.w, abar, k, Bq.w * xv);
+  } else {  // Euler with A per state
+    h.x = var_update(h.x, fast_exp2(dl * A.x), dv, Bq.x * xv);
+    h.y = var_update(h.y, fast_exp2(dl * A.y), dv, Bq.y * xv);
+    h.z = var_update(h.z, fast_exp2(dl * A.z), dv, Bq.z * xv);
+    h.w = var_update(h.w, fast_exp2(dl * A.w), dv, Bq.w * xv);
+  }
   __builtin_nontemporal_store(h, hp);
 
   float p = Cq.x * h.x;
@@ -116,7 +152,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   }
 }
 
-template <int N>
+template <int N, int V>
 hipError_t launch_decode_n(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
   const int64_t threads = (int64_t)args.dim * (N / 4);  // per batch row
   constexpr int64_t kMaxRows = 65535;              // grid y extent per launch
@@ -126,9 +162,9 @@ hipError_t launch_decode_n(const DecodeArgs& args, bool io_bf16, hipStream_t str
     const int64_t rows = args.batch - r0 < kMaxRows ? args.batch - r0 : kMaxRows;
     const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)rows);
     if (io_bf16)
-      hipLaunchKernelGGL((decode_step_kernel<bf16, N>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_step_kernel<bf16, N, V>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_step_kernel<float, N>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_step_kernel<float, N, V>), grid, dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -137,14 +173,27 @@ hipError_t launch_decode_n(const DecodeArgs& args, bool io_bf16, hipStream_t str
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
+namespace {
+template <int V>
+hipError_t launch_decode_v(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
   switch (args.dstate) {
-    case 16: return launch_decode_n<16>(args, io_bf16, stream);
-    case 32: return launch_decode_n<32>(args, io_bf16, stream);
-    case 64: return launch_decode_n<64>(args, io_bf16, stream);
-    case 128: return launch_decode_n<128>(args, io_bf16, stream);
+    case 16: return launch_decode_n<16, V>(args, io_bf16, stream);
+    case 32: return launch_decode_n<32, V>(args, io_bf16, stream);
+    case 64: return launch_decode_n<64, V>(args, io_bf16, stream);
+    case 128: return launch_decode_n<128, V>(args, io_bf16, stream);
   }
   return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
+  const int v = (args.a_per_channel ? kDecScalarA : 0) | (args.euler ? kDecEuler : 0);
+  switch (v) {
+    case 0: return launch_decode_v<0>(args, io_bf16, stream);
+    case kDecScalarA: return launch_decode_v<kDecScalarA>(args, io_bf16, stream);
+    case kDecEuler: return launch_decode_v<kDecEuler>(args, io_bf16, stream);
+    default: return launch_decode_v<kDecScalarA | kDecEuler>(args, io_bf16, stream);
+  }
 }
 
 }  // namespace ssm

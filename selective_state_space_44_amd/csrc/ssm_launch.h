@@ -59,6 +59,8 @@ struct DecodeArgs {
   int dim;
   int64_t row0;        // first batch row of this launch (set by launch_decode)
   int dstate;          // 16, 32, 64 or 128
+  int a_per_channel;   // A is [dim] (one value per channel)
+  int euler;           // Bbar = delta * B instead of the zero-order hold
 };
 
 // Steps per tile of the scan kernels; chunks start on a tile boundary.

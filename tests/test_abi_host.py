@@ -166,6 +166,19 @@ def test_ssd_rejects_bad_arguments(lib):
     assert ssd(L=0) == ssm.SSM_OK                             # no h_last: nothing to write
 
 
+def test_decode_variants_reject_bad_arguments(lib):
+    def dec(pc=1, disc=ssm.SSM_DISC_EULER, batch=2, N=16, A=FAKE):
+        return lib.ssm_decode_step_ex(batch, 64, N, 1, ctypes.c_void_p(0x5000), FAKE,
+                                      ctypes.c_void_p(0x6000), A, pc, disc,
+                                      ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), None,
+                                      None, ctypes.c_void_p(0x2000), None)
+    assert dec(pc=2) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(disc=3) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(A=None) == ssm.SSM_ERR_INVALID_ARG
+    assert dec(N=24) == ssm.SSM_ERR_UNSUPPORTED
+    assert dec(batch=0) == ssm.SSM_OK
+
+
 def test_plan_and_workspace(lib):
     g, k = ssm.scan_plan(4, 4096, 5120)
     assert g in (1, 2, 4, 8, 16) and k >= 1

@@ -141,3 +141,30 @@ def test_variant_rejects_sixteen_waves_and_phases():
     assert e.value.status == ssm.SSM_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
         ssm.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], phase=1)
+
+
+@pytest.mark.parametrize("n", [16, 32, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("variant", VARIANTS, ids=_ids)
+def test_decode_variants(variant, dtype, n):
+    """ssm_decode_step_ex: one step on a resident state equals the oracle's
+    scan of length 1 from h0 = that state; 8 sequences x 130 channels (ragged
+    block), A = 0 on two channels."""
+    a_kind, disc = variant
+    print(f"decode variant {variant} {dtype} N={n}", flush=True)
+    d = W.make_inputs(W.DECODE_64L, device=DEV, batch=8, dim=130, dstate=n)
+    d = {k: (v.to(dtype) if k in ("x", "delta", "z", "B", "C") else v) for k, v in d.items()}
+    if a_kind == "channel":
+        d["A"] = W.make_channel_A(W.DECODE_64L, device=DEV, dim=130)
+    d["A"][3] = 0.0
+    d["A"][77] = 0.0
+    h0 = d["h"].clone()
+    y = ssm.decode_step(d["h"], d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                        discretization=disc)
+    torch.cuda.synchronize()
+    as_scan = dict(x=d["x"][:, None, :], delta=d["delta"][:, None, :], A=d["A"],
+                   B=d["B"][:, None, :], C=d["C"][:, None, :], D=d["D"], z=d["z"][:, None, :],
+                   h0=h0)
+    y_ref, h_ref = parity.oracle_scan(as_scan, discretization=disc)
+    parity.check_y(parity.to_f64(y), y_ref[:, 0, :], dtype, what="decode y")
+    parity.check_state(parity.to_f64(d["h"]), h_ref, what="decode state")

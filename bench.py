@@ -400,7 +400,7 @@ def main():
                          "kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "channels are independent, so a multi-GPU run would split D with no exchange", file=sys.stderr)
         sys.exit(2)
 

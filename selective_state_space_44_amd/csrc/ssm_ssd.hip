@@ -6,21 +6,21 @@
 // reduced to a scalar the bulk of the SSM's work becomes masked matrix
 // products; paperlens tutorial, section on the parallel scan: the recurrence
 // composes chunk by chunk).  For one batch row, head h (decay rate a, step
-// dt_t) and a chunk of Q = 64 steps, with s_t = a * sum_{r<=t} dt_r inside
+// dt_t) and a chunk of Q = 32 steps, with s_t = a * sum_{r<=t} dt_r inside
 // the chunk and coef_t the input coefficient of step t ((exp(a dt_t) - 1)/a
 // for the zero-order hold, dt_t for the Euler rule, dt_t at a = 0):
 //
 //   y_i   = sum_{j<=i} (C_i . B_j) exp(s_i - s_j) coef_j x_j      in-chunk part
 //         + exp(s_i) C_i . h_in                                   entering state
-//   h_out = exp(s_63) h_in + sum_j exp(s_63 - s_j) coef_j x_j B_j^T
+//   h_out = exp(s_last) h_in + sum_j exp(s_last - s_j) coef_j x_j B_j^T
 //
 // and y = (y + D x) * SiLU(z).  Each sum is a matrix product:
-//   * M = C B^T per chunk (64 x 64, contraction over the N states),
+//   * M = C B^T per chunk (32 x 32, contraction over the N states),
 //   * Y_in = P X with P = M masked to j <= i and weighted by
 //     exp(s_i - s_j) coef_j (contraction over the chunk's steps),
 //   * Y_state = C h_in^T (contraction over the states),
-//   * h_out^T = B^T (w x) with w_t = exp(s_63 - s_t) coef_t (contraction over
-//     the steps).
+//   * h_out^T = B^T (w x) with w_t = exp(s_last - s_t) coef_t (contraction
+//     over the steps).
 //
 // Organisation: one block per (half head of 32 channels, batch row) walks
 // 32-step chunks in order, so the state never leaves the registers and no
@@ -31,16 +31,19 @@
 // tile nh (its partial plus the other half's, passed through LDS).  The
 // chunk's 32 x 32 matrix P has three lower-triangular 16 x 16 tiles, one on
 // each of waves 0..2, passed through LDS.  At the Mamba-2-like shape (4 x 80
-// heads) this makes 640 blocks of ~47 KB LDS, all resident at once (2-3 per
-// CU).
+// heads) this makes 640 blocks of 32.5 KB LDS (N = 128), all resident at once
+// (2-3 per CU).
 //
 // Data movement per chunk: the chunk's x, z (32 steps x 32 channels), B, C
-// (32 steps x N) and dt are loaded into registers two chunks ahead, then
-// written to LDS, x, z and B also transposed (step index contiguous), since
-// every operand must be contiguous in its contraction index.  The decay
-// exponents of a chunk (a prefix sum over its steps) are computed one chunk
-// ahead by the wave that has no P tile.  Three barriers per chunk: staging
-// written; P, w x and the partial C h written; (next chunk) all reads done.
+// (32 steps x N) and dt are loaded into registers two chunks ahead and
+// staged in LDS in their natural layout.  The operand layouts the
+// contractions need -- x and B with the step index contiguous, x and z in the
+// result layout of the epilogue -- come from products with an identity
+// matrix (see identity_pick), and the outputs are transposed the same way
+// for 8-byte stores.  The decay exponents of a chunk (a prefix sum over its
+// steps) are computed one chunk ahead by the wave that has no P tile.  Three
+// barriers per chunk: staging written; P and the partial C h written; (next
+// chunk) all reads done.
 //
 // Precision: B, C and x are bf16 inputs, exact as MFMA operands.  The other
 // operands -- the masked weights P, the state h and the weighted inputs w x --
@@ -58,7 +61,9 @@
 // slots of A and B one to one, so any permutation of the contraction index
 // applied to both operands gives the same sum.  The kernel uses that freedom
 // where a result tile becomes the next product's operand without a trip
-// through LDS (the state as the B operand of C h^T).
+// through LDS (the state as the B operand of C h^T, the identity products).
+// The 16x16x16 form is not used: in one compiled schedule the result rows
+// 0-1 of such a product were read before it had completed.
 
 #include "ssm_device.h"
 #include "ssm_launch.h"

@@ -216,8 +216,12 @@ int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
  *   workspace   : at least ssm_scan_bwd_workspace_bytes(...) bytes.
  * Results are deterministic: every sum runs in a fixed order.  Outputs must
  * not alias inputs, each other or the workspace.  seqlen == 0 writes dA = 0,
- * dD = 0 and dh0 = dh_last (or 0).  dstate other than 16, and more than 65535
- * batch rows: SSM_ERR_UNSUPPORTED.  Returns an SSM_* status.
+ * dD = 0 and dh0 = dh_last (or 0).  dstate 16 runs the backward kernels
+ * directly; 32, 64 and 128 run them on each 16-state slice in turn (the
+ * states of a channel evolve independently and meet only in sums over n),
+ * with the per-(t, d) sums accumulated in fp32 in the workspace.  Other
+ * dstate, and more than 65535 batch rows: SSM_ERR_UNSUPPORTED.  Returns an
+ * SSM_* status.
  */
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                  const void *x, const void *delta, const float *A, int a_per_channel,

@@ -380,6 +380,9 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, fl
 // ---------------------------------------------------------------------------
 namespace {
 
+// State sizes whose backward runs as 16-state slices.
+bool bwd_sliced(int64_t dstate) { return dstate == 32 || dstate == 64 || dstate == 128; }
+
 // Chunk length and count of the backward plan: chunks of at most
 // ssm::kBwdChunk steps, starting on tile boundaries.
 void bwd_plan(int64_t seqlen, int64_t* chunk_len, int* nchunks) {
@@ -402,6 +405,9 @@ int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
   int64_t len;
   int K;
   bwd_plan(seqlen, &len, &K);
+  if (bwd_sliced(dstate))
+    return (int64_t)ssm::bwd_slice_layout(batch, seqlen, dim, K,
+                                          io_dtype == SSM_DTYPE_BF16 ? 2 : 4).total;
   return (int64_t)ssm::bwd_workspace_layout(batch, seqlen, dim, K).total;
 }
 
@@ -415,7 +421,7 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   if (a_per_channel != 0 && a_per_channel != 1) return SSM_ERR_INVALID_ARG;
   if (discretization != SSM_DISC_ZOH && discretization != SSM_DISC_EULER)
     return SSM_ERR_INVALID_ARG;
-  if (dstate != kDState) return SSM_ERR_UNSUPPORTED;
+  if (dstate != kDState && !bwd_sliced(dstate)) return SSM_ERR_UNSUPPORTED;
   if (!A || !dA) return SSM_ERR_INVALID_ARG;
   if ((z == nullptr) != (dz == nullptr)) return SSM_ERR_INVALID_ARG;
   if (seqlen > 0 && batch > 0 && dim > 0 &&
@@ -437,21 +443,24 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   if (batch > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
   auto s = static_cast<hipStream_t>(stream);
   if (dim == 0) return SSM_OK;
-  const int64_t na = a_per_channel ? dim : dim * kDState;
+  const int64_t na = a_per_channel ? dim : dim * dstate;
   if (batch == 0 || seqlen == 0) {
     // no steps: dA = dD = 0, dh0 = dh_last (or 0)
     hipError_t e = ssm::launch_copy_state(nullptr, dA, na, s);
     if (e == hipSuccess && dD) e = ssm::launch_copy_state(nullptr, dD, dim, s);
     if (e == hipSuccess && dh0 && batch > 0)
-      e = ssm::launch_copy_state(dh_last, dh0, batch * dim * kDState, s);
+      e = ssm::launch_copy_state(dh_last, dh0, batch * dim * dstate, s);
     return hip_status(e);
   }
   int64_t chunk_len;
   int K;
   bwd_plan(seqlen, &chunk_len, &K);
   if (K > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
-  const ssm::BwdWorkspace w = ssm::bwd_workspace_layout(batch, seqlen, dim, K);
-  if (!workspace || workspace_bytes < w.total) return SSM_ERR_WORKSPACE;
+  const bool sliced = dstate != kDState;
+  const ssm::BwdSliceWorkspace ws =
+      ssm::bwd_slice_layout(batch, seqlen, dim, K, io_dtype == SSM_DTYPE_BF16 ? 2 : 4);
+  const ssm::BwdWorkspace& w = ws.base;
+  if (!workspace || workspace_bytes < (sliced ? ws.total : w.total)) return SSM_ERR_WORKSPACE;
   for (const void* in : ins)
     if (in && in == workspace) return SSM_ERR_INVALID_ARG;
 
@@ -495,6 +504,9 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   a.dC = dC;
   a.dD = dD;
   a.dh0 = dh0;
+  if (sliced)
+    return hip_status(
+        ssm::launch_scan_bwd_sliced(a, (int)dstate, io_dtype == SSM_DTYPE_BF16, base, ws, s));
   return hip_status(ssm::launch_scan_bwd(a, io_dtype == SSM_DTYPE_BF16, s));
 }
 

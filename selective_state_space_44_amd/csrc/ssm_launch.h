@@ -113,6 +113,21 @@ struct BwdArgs {
   float* ws_pdC;      // [batch, groups, seqlen, 16]
   float* ws_pdA;      // [batch, nchunks, dim, 16]
   float* ws_pdD;      // [batch, nchunks, dim]
+  // Larger states run as 16-state slices (see launch_scan_bwd_sliced).  When
+  // acc_dx is set, the main kernel adds its per-(t, d) results into these
+  // fp32 [batch, seqlen, dim] buffers (dx with the D term, ddelta, and C.h of
+  // the slice when z is given) instead of storing dx, ddelta and dz.
+  float* acc_dx;
+  float* acc_dd;
+  float* acc_sp;
+  // placement of dB, dC ([.., bc_ld] rows, from column bc_col0) and of a
+  // per-state dA ([dim, a_ld] rows, from column a_col0); 0 = 16 / 0.  With A
+  // per channel, a_accumulate adds the slice's dA to dA instead of storing it.
+  int64_t bc_ld;
+  int bc_col0;
+  int64_t a_ld;
+  int a_col0;
+  int a_accumulate;
 };
 struct BwdWorkspace {
   ScanWorkspace fwd, rev;
@@ -120,6 +135,23 @@ struct BwdWorkspace {
 };
 BwdWorkspace bwd_workspace_layout(int64_t batch, int64_t seqlen, int64_t dim, int nchunks);
 hipError_t launch_scan_bwd(const BwdArgs& a, bool io_bf16, hipStream_t stream);
+
+// Backward for 32, 64 or 128 states: the states of a channel evolve
+// independently and meet only in sums over n (y, and through it dx, ddelta
+// and dz), so the 16-state backward runs on each 16-state slice -- B, C, A,
+// h0 and dh_last slices gathered into the workspace -- with its per-(t, d)
+// results accumulated in fp32, and a last kernel writes dx, ddelta and dz.
+struct BwdSliceWorkspace {
+  BwdWorkspace base;  // of one 16-state slice
+  size_t bs_off, cs_off, as_off, h0s_off, dhls_off, dh0s_off;
+  size_t accx_off, accd_off, accs_off, total;
+};
+BwdSliceWorkspace bwd_slice_layout(int64_t batch, int64_t seqlen, int64_t dim, int nchunks,
+                                   int io_bytes);
+// `a` holds the full problem (dstate states) with the workspace pointers of
+// one slice set up as for the 16-state backward; `wsb` is the workspace base.
+hipError_t launch_scan_bwd_sliced(const BwdArgs& a, int dstate, bool io_bf16, char* wsb,
+                                  const BwdSliceWorkspace& w, hipStream_t stream);
 
 // Scan for state sizes 32, 64, 128: one pass over the sequence, no
 // workspace (chunk fields of ScanArgs unused; no prologue).

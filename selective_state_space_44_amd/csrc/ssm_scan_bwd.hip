@@ -347,7 +347,8 @@ __device__ __forceinline__ void bwd_chunk(
     const float (&iA)[kDState / G], float Dd, float (&h)[kDState / G], float (&e)[kDState / G],
     float (&dA_acc)[kDState / G], float& dD_acc, IO* __restrict__ dx, IO* __restrict__ ddelta,
     IO* __restrict__ dz, float* __restrict__ pdB, float* __restrict__ pdC, int64_t seqlen,
-    int dim) {
+    int dim, float* __restrict__ acc_dx, float* __restrict__ acc_dd,
+    float* __restrict__ acc_sp) {
   constexpr int NPL = kDState / G;
   const int n0 = k.g * NPL;
   const int groups = (dim + kWave - 1) / kWave;
@@ -491,6 +492,12 @@ __device__ __forceinline__ void bwd_chunk(
         ssp += sm.part[2][w][s][k.lane];
       }
       const size_t off = ((size_t)k.b * seqlen + t) * dim + k.d;
+      if (acc_dx) {  // one 16-state slice of a larger state: accumulate in fp32
+        acc_dx[off] += __builtin_fmaf(sm.st.dp[s][k.lane], Dd, sdx);
+        acc_dd[off] += sdd;
+        if constexpr (HAS_Z) acc_sp[off] += ssp;
+        continue;
+      }
       io<IO>::store(dx + off, __builtin_fmaf(sm.st.dp[s][k.lane], Dd, sdx));
       io<IO>::store(ddelta + off, sdd);
       if constexpr (HAS_Z)
@@ -513,7 +520,8 @@ void bwd_main_kernel(
     const float* __restrict__ ws_ein, IO* __restrict__ dx, IO* __restrict__ ddelta,
     IO* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ pdB,
     float* __restrict__ pdC, float* __restrict__ pdA, float* __restrict__ pdD, int64_t seqlen,
-    int64_t chunk_len, int dim, int nchunks) {
+    int64_t chunk_len, int dim, int nchunks, float* __restrict__ acc_dx,
+    float* __restrict__ acc_dd, float* __restrict__ acc_sp) {
   constexpr int NPL = kDState / G;
   __shared__ BwdSmem<G> sm;
   const BwdChunk k = bwd_coords(blockIdx.y, dim, seqlen, chunk_len);
@@ -544,10 +552,12 @@ void bwd_main_kernel(
   float dD_acc = 0.0f;
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
     bwd_chunk<IO, G, HAS_Z, V, true>(sm, k, x, delta, B, C, z, dy, Af, A2, iA, Dd, h, e, dA_acc,
-                                     dD_acc, dx, ddelta, dz, pdB, pdC, seqlen, dim);
+                                     dD_acc, dx, ddelta, dz, pdB, pdC, seqlen, dim, acc_dx,
+                                     acc_dd, acc_sp);
   else
     bwd_chunk<IO, G, HAS_Z, V, false>(sm, k, x, delta, B, C, z, dy, Af, A2, iA, Dd, h, e,
-                                      dA_acc, dD_acc, dx, ddelta, dz, pdB, pdC, seqlen, dim);
+                                      dA_acc, dD_acc, dx, ddelta, dz, pdB, pdC, seqlen, dim,
+                                      acc_dx, acc_dd, acc_sp);
 
   if (k.active) {
     const size_t pa = (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
@@ -562,12 +572,14 @@ void bwd_main_kernel(
 }
 
 // dB, dC: sum of the channel-group partials, in group order.
+// Output (b, t, n) goes to row (b, t) of ldo elements, column col0 + n.
 template <typename IO>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ pdB,
                                                             const float* __restrict__ pdC,
                                                             IO* __restrict__ dB,
                                                             IO* __restrict__ dC, int batch,
-                                                            int64_t seqlen, int groups) {
+                                                            int64_t seqlen, int groups,
+                                                            int64_t ldo, int col0) {
   const int64_t per_b = seqlen * kDState;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= batch * per_b) return;
@@ -578,8 +590,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
     sb += pdB[o];
     sc += pdC[o];
   }
-  io<IO>::store(dB + i, sb);
-  io<IO>::store(dC + i, sc);
+  const int64_t out = (i / kDState) * ldo + col0 + i % kDState;
+  io<IO>::store(dB + out, sb);
+  io<IO>::store(dC + out, sc);
 }
 
 // dA, dD: sums of the (batch row, chunk) partials.  A block takes 64
@@ -592,7 +605,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_a_kernel(const float* __restri
                                                            float* __restrict__ dA,
                                                            float* __restrict__ dD, int rows,
                                                            int dim, int a_blocks,
-                                                           int a_per_channel) {
+                                                           int a_per_channel, int64_t lda,
+                                                           int cola, int accumulate) {
   __shared__ float part[4][kWave];
   const int col = threadIdx.x % kWave, sl = threadIdx.x / kWave;
   const bool is_a = (int)blockIdx.x < a_blocks;
@@ -609,7 +623,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_a_kernel(const float* __restri
     if (!is_a) {
       if (dD && c < ncol) dD[c] = t;
     } else if (!a_per_channel) {
-      if (c < ncol) dA[c] = t;
+      if (c < ncol) dA[(c / kDState) * lda + cola + c % kDState] = t;
     } else {
       part[0][col] = t;
     }
@@ -621,7 +635,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_a_kernel(const float* __restri
     if (j < kWave / kDState && d < dim) {
       float t = 0.0f;
       for (int n = 0; n < kDState; ++n) t += part[0][j * kDState + n];
-      dA[d] = t;
+      dA[d] = accumulate ? dA[d] + t : t;
     }
   }
 }
@@ -657,20 +671,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      stream, x, delta, f.A, B, C, f.Dskip, z, f.h0, dy, a.dh_last, f.ws_hin,
                      a.ws_ein, static_cast<IO*>(a.dx), static_cast<IO*>(a.ddelta),
                      static_cast<IO*>(a.dz), a.dh0, a.ws_pdB, a.ws_pdC, a.ws_pdA, a.ws_pdD,
-                     f.seqlen, f.chunk_len, f.dim, f.nchunks);
+                     f.seqlen, f.chunk_len, f.dim, f.nchunks, a.acc_dx, a.acc_dd, a.acc_sp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = (int64_t)f.batch * f.seqlen * kDState;
   hipLaunchKernelGGL((bwd_reduce_bc_kernel<IO>), dim3((unsigned)((nbc + 255) / 256)), dim3(256),
                      0, stream, a.ws_pdB, a.ws_pdC, static_cast<IO*>(a.dB),
-                     static_cast<IO*>(a.dC), f.batch, f.seqlen, (int)gx);
+                     static_cast<IO*>(a.dC), f.batch, f.seqlen, (int)gx,
+                     a.bc_ld ? a.bc_ld : (int64_t)kDState, a.bc_col0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int a_blocks = (int)(((int64_t)f.dim * kDState + kWave - 1) / kWave);
   const int d_blocks = (f.dim + kWave - 1) / kWave;
   hipLaunchKernelGGL(bwd_reduce_a_kernel, dim3((unsigned)(a_blocks + d_blocks)), dim3(256), 0,
                      stream, a.ws_pdA, a.ws_pdD, a.dA, a.dD, f.batch * f.nchunks, f.dim,
-                     a_blocks, (V & kVarScalarA) ? 1 : 0);
+                     a_blocks, (V & kVarScalarA) ? 1 : 0, a.a_ld ? a.a_ld : (int64_t)kDState,
+                     a.a_col0, a.a_accumulate);
   return hipGetLastError();
 }
 
@@ -711,6 +727,174 @@ BwdWorkspace bwd_workspace_layout(int64_t batch, int64_t seqlen, int64_t dim, in
 
 hipError_t launch_scan_bwd(const BwdArgs& a, bool io_bf16, hipStream_t stream) {
   return io_bf16 ? launch_bwd_io<bf16>(a, stream) : launch_bwd_io<float>(a, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Larger states as 16-state slices
+// ---------------------------------------------------------------------------
+namespace {
+
+// Rows of 16 elements: dst[r * dst_ld + dst_col0 + c] = src[r * src_ld + src_col0 + c].
+template <typename T>
+__global__ __launch_bounds__(256) void copy16_kernel(const T* __restrict__ src, int64_t src_ld,
+                                                     int src_col0, T* __restrict__ dst,
+                                                     int64_t dst_ld, int dst_col0,
+                                                     int64_t rows) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * kDState) return;
+  const int64_t r = i / kDState;
+  const int c = (int)(i % kDState);
+  dst[r * dst_ld + dst_col0 + c] = src[r * src_ld + src_col0 + c];
+}
+
+hipError_t launch_copy16(const void* src, int64_t src_ld, int src_col0, void* dst,
+                         int64_t dst_ld, int dst_col0, int64_t rows, int elem_bytes,
+                         hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows * kDState + 255) / 256));
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(copy16_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), src_ld, src_col0,
+                       static_cast<uint16_t*>(dst), dst_ld, dst_col0, rows);
+  else
+    hipLaunchKernelGGL(copy16_kernel<float>, grid, dim3(256), 0, stream,
+                       static_cast<const float*>(src), src_ld, src_col0,
+                       static_cast<float*>(dst), dst_ld, dst_col0, rows);
+  return hipGetLastError();
+}
+
+// dx, ddelta and dz from the slices' fp32 sums: dz = dy SiLU'(z) (C.h + D x),
+// with SiLU' formed as in stage_tile.
+template <typename IO, bool HAS_Z>
+__global__ __launch_bounds__(256) void bwd_finish_kernel(
+    const float* __restrict__ acc_dx, const float* __restrict__ acc_dd,
+    const float* __restrict__ acc_sp, const IO* __restrict__ x, const IO* __restrict__ z,
+    const IO* __restrict__ dy, const float* __restrict__ Dskip, IO* __restrict__ dx,
+    IO* __restrict__ ddelta, IO* __restrict__ dz, int64_t count, int dim) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  io<IO>::store(dx + i, acc_dx[i]);
+  io<IO>::store(ddelta + i, acc_dd[i]);
+  if constexpr (HAS_Z) {
+    const float zv = io<IO>::load(z + i), dyv = io<IO>::load(dy + i);
+    const float sg = sigmoid_f(zv);
+    const float gd = dyv * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f);
+    const float Dd = Dskip ? Dskip[i % dim] : 0.0f;
+    io<IO>::store(dz + i, gd * __builtin_fmaf(Dd, io<IO>::load(x + i), acc_sp[i]));
+  }
+}
+
+template <typename IO>
+hipError_t launch_bwd_finish(const BwdArgs& a, const float* accx, const float* accd,
+                             const float* accs, hipStream_t stream) {
+  const ScanArgs& f = a.f;
+  const int64_t count = (int64_t)f.batch * f.seqlen * f.dim;
+  const dim3 grid((unsigned)((count + 255) / 256));
+  const IO* x = static_cast<const IO*>(f.x);
+  const IO* z = static_cast<const IO*>(f.z);
+  const IO* dy = static_cast<const IO*>(a.dy);
+  if (f.z)
+    hipLaunchKernelGGL((bwd_finish_kernel<IO, true>), grid, dim3(256), 0, stream, accx, accd,
+                       accs, x, z, dy, f.Dskip, static_cast<IO*>(a.dx),
+                       static_cast<IO*>(a.ddelta), static_cast<IO*>(a.dz), count, f.dim);
+  else
+    hipLaunchKernelGGL((bwd_finish_kernel<IO, false>), grid, dim3(256), 0, stream, accx, accd,
+                       accs, x, z, dy, f.Dskip, static_cast<IO*>(a.dx),
+                       static_cast<IO*>(a.ddelta), static_cast<IO*>(a.dz), count, f.dim);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BwdSliceWorkspace bwd_slice_layout(int64_t batch, int64_t seqlen, int64_t dim, int nchunks,
+                                   int io_bytes) {
+  auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
+  BwdSliceWorkspace w{};
+  w.base = bwd_workspace_layout(batch, seqlen, dim, nchunks);
+  const size_t bc = (size_t)batch * seqlen * kDState * io_bytes;
+  const size_t st = (size_t)batch * dim * kDState * sizeof(float);
+  const size_t acc = (size_t)batch * seqlen * dim * sizeof(float);
+  size_t off = align(w.base.total);
+  w.bs_off = off;
+  off += align(bc);
+  w.cs_off = off;
+  off += align(bc);
+  w.as_off = off;
+  off += align((size_t)dim * kDState * sizeof(float));
+  w.h0s_off = off;
+  off += align(st);
+  w.dhls_off = off;
+  off += align(st);
+  w.dh0s_off = off;
+  off += align(st);
+  w.accx_off = off;
+  off += align(acc);
+  w.accd_off = off;
+  off += align(acc);
+  w.accs_off = off;
+  off += align(acc);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_scan_bwd_sliced(const BwdArgs& a, int dstate, bool io_bf16, char* wsb,
+                                  const BwdSliceWorkspace& w, hipStream_t stream) {
+  const ScanArgs& f = a.f;
+  const int io_bytes = io_bf16 ? 2 : 4;
+  const int64_t rows_bc = (int64_t)f.batch * f.seqlen, rows_st = (int64_t)f.batch * f.dim;
+  const int64_t count = rows_bc * f.dim;
+  float* accx = reinterpret_cast<float*>(wsb + w.accx_off);
+  float* accd = reinterpret_cast<float*>(wsb + w.accd_off);
+  float* accs = reinterpret_cast<float*>(wsb + w.accs_off);
+  void* Bs = wsb + w.bs_off;
+  void* Cs = wsb + w.cs_off;
+  float* As = reinterpret_cast<float*>(wsb + w.as_off);
+  float* h0s = reinterpret_cast<float*>(wsb + w.h0s_off);
+  float* dhls = reinterpret_cast<float*>(wsb + w.dhls_off);
+  float* dh0s = reinterpret_cast<float*>(wsb + w.dh0s_off);
+  hipError_t e = launch_copy_state(nullptr, accx, count, stream);
+  if (e == hipSuccess) e = launch_copy_state(nullptr, accd, count, stream);
+  if (e == hipSuccess && f.z) e = launch_copy_state(nullptr, accs, count, stream);
+  for (int s = 0; s < dstate / kDState && e == hipSuccess; ++s) {
+    const int col = kDState * s;
+    BwdArgs as = a;
+    e = launch_copy16(f.B, dstate, col, Bs, kDState, 0, rows_bc, io_bytes, stream);
+    if (e == hipSuccess) e = launch_copy16(f.C, dstate, col, Cs, kDState, 0, rows_bc, io_bytes, stream);
+    as.f.B = Bs;
+    as.f.C = Cs;
+    if (e == hipSuccess && !f.a_per_channel) {
+      e = launch_copy16(f.A, dstate, col, As, kDState, 0, f.dim, 4, stream);
+      as.f.A = As;
+    }
+    if (e == hipSuccess && f.h0) {
+      e = launch_copy16(f.h0, dstate, col, h0s, kDState, 0, rows_st, 4, stream);
+      as.f.h0 = h0s;
+    }
+    if (e == hipSuccess && a.dh_last) {
+      e = launch_copy16(a.dh_last, dstate, col, dhls, kDState, 0, rows_st, 4, stream);
+      as.dh_last = dhls;
+    }
+    if (e != hipSuccess) break;
+    // the D terms (D dp in dx, dD) belong to the first slice only
+    as.f.Dskip = s == 0 ? f.Dskip : nullptr;
+    as.dD = s == 0 ? a.dD : nullptr;
+    as.dx = as.ddelta = as.dz = nullptr;
+    as.acc_dx = accx;
+    as.acc_dd = accd;
+    as.acc_sp = f.z ? accs : nullptr;
+    as.bc_ld = dstate;
+    as.bc_col0 = col;
+    as.a_ld = dstate;
+    as.a_col0 = col;
+    as.a_accumulate = (f.a_per_channel && s > 0) ? 1 : 0;
+    as.dh0 = a.dh0 ? dh0s : nullptr;
+    e = launch_scan_bwd(as, io_bf16, stream);
+    if (e == hipSuccess && a.dh0)
+      e = launch_copy16(dh0s, kDState, 0, a.dh0, dstate, col, rows_st, 4, stream);
+  }
+  if (e != hipSuccess) return e;
+  return io_bf16 ? launch_bwd_finish<bf16>(a, accx, accd, accs, stream)
+                 : launch_bwd_finish<float>(a, accx, accd, accs, stream);
 }
 
 }  // namespace ssm

@@ -117,9 +117,6 @@ def test_wide_rejections():
     with pytest.raises(ssm.SsmError) as e:                      # no chunk phases
         ssm.scan_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], phase=1)
     assert e.value.status == ssm.SSM_ERR_UNSUPPORTED
-    with pytest.raises(ssm.SsmError) as e:                      # no wide backward
-        ssm.scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dy=p["x"])
-    assert e.value.status == ssm.SSM_ERR_UNSUPPORTED
     q = _inputs(16, seqlen=8, dim=64)
     with pytest.raises(ssm.SsmError) as e:                      # 24 states: no kernel
         ssm.scan_fwd(q["x"], q["delta"], torch.cat([q["A"], q["A"][:, :8]], 1).contiguous(),

@@ -463,6 +463,8 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   if (!workspace || workspace_bytes < (sliced ? ws.total : w.total)) return SSM_ERR_WORKSPACE;
   for (const void* in : ins)
     if (in && in == workspace) return SSM_ERR_INVALID_ARG;
+  for (const void* o : outs)
+    if (o && o == workspace) return SSM_ERR_INVALID_ARG;
 
   char* base = static_cast<char*>(workspace);
   ssm::BwdArgs a{};

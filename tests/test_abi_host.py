@@ -140,6 +140,15 @@ def test_batch_limits(lib):
     assert st == ssm.SSM_ERR_UNSUPPORTED
 
 
+def test_backward_output_may_not_be_the_workspace(lib):
+    p = [ctypes.c_void_p(0x1000 * k) for k in range(1, 20)]
+    ws = p[6]                                                    # also passed as dx
+    st = lib.ssm_scan_bwd(2, 8, 64, 16, 1, p[0], p[1], p[2], 0, ssm.SSM_DISC_ZOH, p[3], p[4],
+                          None, None, None, p[5], None, ws, p[7], p[8], p[9], p[10], None,
+                          None, None, ws, 1 << 40, None)
+    assert st == ssm.SSM_ERR_INVALID_ARG
+
+
 def test_ssd_rejects_bad_arguments(lib):
     """Every case fails validation (or is a no-op) before any launch."""
     def ssd(batch=2, L=8, H=2, P=64, N=128, io=1, disc=ssm.SSM_DISC_ZOH, x=FAKE, A=FAKE,

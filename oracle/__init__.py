@@ -180,6 +180,27 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None,
     return g
 
 
+def scan_heads_bwd(x, dt, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None,
+                   headdim: int = 64, nthreads: int = 0, lib=None,
+                   discretization: str = "zoh"):
+    """Gradients of ``scan_heads``: the per-channel backward of the scan with
+    dt and A repeated over each head's channels; a parameter shared by a
+    head's channels gets the sum of their gradients (chain rule).  Returns the
+    dict of ``scan_bwd`` with ``ddt`` [b, L, H] and dA [H] in place of the
+    per-channel ddelta and dA."""
+    x, dt, A = _f64(x), _f64(dt), _f64(A)
+    batch, seqlen, dim = x.shape
+    assert headdim > 0 and dim % headdim == 0
+    nheads = dim // headdim
+    assert dt.shape == (batch, seqlen, nheads) and A.shape == (nheads,)
+    g = scan_bwd(x, np.repeat(dt, headdim, axis=2), np.repeat(A, headdim), B, C, D, z, h0,
+                 dy=dy, dh_last=dh_last, nthreads=nthreads, lib=lib,
+                 discretization=discretization)
+    g["ddt"] = g.pop("ddelta").reshape(batch, seqlen, nheads, headdim).sum(axis=3)
+    g["dA"] = g["dA"].reshape(nheads, headdim).sum(axis=1)
+    return g
+
+
 def decode_step(h, x, delta, A, B, C, D=None, z=None, lib=None):
     """One recurrent step.  h [b, d, n] float64 numpy array, updated in place;
     x, delta, z [b, d]; B, C [b, n].  Returns y [b, d]."""

@@ -36,7 +36,8 @@ What pins what (pages cited by title and section):
   and the single decay rate it implies (paperlens tutorial, selection
   pseudo-code; ihouse article, Mamba-2 section); a step and decay shared by
   a head of channels against the masked-matrix form of the same scan
-  (ihouse article, section on Mamba's evolution).
+  (ihouse article, section on Mamba's evolution), and the gradients of the
+  head-shared dt and A against central differences.
 * Prologue of the fused scan (paperlens tutorial, sections "現場ではこう使う"
   and "Mamba: 状態を「選択的」にする"): the causal depthwise convolution equals
   numpy's convolve of each channel with its reversed taps, and cannot see the
@@ -368,6 +369,42 @@ def pin_head_shared_step_equals_masked_matrix_form(lib):
                                          P, euler)
             assert _rel(y, yr) < 1e-12, (euler, b, L, H, P, n)
             assert _rel(hl, hr) < 1e-12, (euler, b, L, H, P, n)
+
+
+def pin_head_shared_backward_matches_finite_differences(lib):
+    """ddt and dA of the per-head scan against central differences of
+    ``scan_heads`` (the other gradients are those of the per-channel backward,
+    pinned below)."""
+    rng = _rng(28)
+    for euler in (False, True):
+        b, L, H, P, n = 2, 7, 2, 3, 4
+        p = _rand_problem(rng, b, L, H * P, n)
+        dt = rng.uniform(0.05, 0.5, (b, L, H))
+        A = -rng.uniform(0.3, 1.5, H)
+        dy = rng.standard_normal(p["x"].shape)
+        dhl = rng.standard_normal(p["h0"].shape)
+        disc = "euler" if euler else "zoh"
+        g = oracle.scan_heads_bwd(p["x"], dt, A, p["B"], p["C"], p["D"], p["z"], p["h0"],
+                                  dy=dy, dh_last=dhl, headdim=P, lib=lib, discretization=disc)
+
+        def loss(dt_, A_):
+            y, h = oracle.scan_heads(p["x"], dt_, A_, p["B"], p["C"], p["D"], p["z"], p["h0"],
+                                     headdim=P, lib=lib, discretization=disc)
+            return float(np.sum(dy * y) + np.sum(dhl * h))
+
+        eps = 1e-6
+        for idx in [(0, 0, 0), (1, 3, 1), (0, 6, 1), (1, 0, 0)]:
+            dp, dm = dt.copy(), dt.copy()
+            dp[idx] += eps
+            dm[idx] -= eps
+            fd = (loss(dp, A) - loss(dm, A)) / (2 * eps)
+            assert abs(g["ddt"][idx] - fd) <= 1e-6 * (1 + abs(fd)), (disc, idx, g["ddt"][idx], fd)
+        for h in range(H):
+            ap, am = A.copy(), A.copy()
+            ap[h] += eps
+            am[h] -= eps
+            fd = (loss(dt, ap) - loss(dt, am)) / (2 * eps)
+            assert abs(g["dA"][h] - fd) <= 1e-6 * (1 + abs(fd)), (disc, h, g["dA"][h], fd)
 
 
 # --------------------------------------------------------------------------

@@ -287,6 +287,24 @@ def bench_ssd(steps: int, warmup: int):
     e1.record()
     torch.cuda.synchronize()
     rec_ms = e0.elapsed_time(e1) / rec_steps
+
+    # its backward (ssm_ssd_bwd: the recurrence's backward kernels, per-head sums)
+    g = torch.Generator(device=dev).manual_seed(19)
+    dy = torch.randn(f["x"].shape, generator=g, device=dev).to(f["x"].dtype)
+    nws = ssm.load_library().ssm_ssd_bwd_workspace_bytes(w.batch, w.seqlen, heads, P, N,
+                                                           1 if w.io_dtype == torch.bfloat16 else 0)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    bwd = lambda: ssm.ssd_bwd(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
+                              dy=dy, workspace=ws)
+    bwd()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(rec_steps):
+        bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    bwd_ms = e0.elapsed_time(e1) / rec_steps
+    del ws, dy
     return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
             "unit": "elements/s",
             "mfma": {"algorithmic_flop": flops, "achieved": flops / (ms * 1e-3) / 1e12,
@@ -295,7 +313,8 @@ def bench_ssd(steps: int, warmup: int):
             "hbm": {"algorithmic_bytes": nbytes, "achieved": nbytes / (ms * 1e-3) / 1e9,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-            "recurrence_ms_per_step": rec_ms, "speedup_vs_recurrence": rec_ms / ms}
+            "recurrence_ms_per_step": rec_ms, "speedup_vs_recurrence": rec_ms / ms,
+            "backward_ms_per_step": bwd_ms}
 
 
 def bench_backward(steps: int, warmup: int):

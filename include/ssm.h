@@ -331,6 +331,42 @@ int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                 const float *Dskip, const void *z, const float *h0, void *y,
                 float *h_last, void *stream);
 
+/*
+ * Workspace of ssm_ssd_bwd in bytes for these sizes (-1 for invalid sizes,
+ * 0 when nothing is needed).
+ */
+int64_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                    int64_t headdim, int64_t dstate, int io_dtype);
+
+/*
+ * Backward of ssm_ssd_fwd (step and decay shared per head): the gradients of
+ * a loss with respect to every input, given dy and dh_last.  It is the
+ * backward of ssm_scan_bwd applied to the per-channel problem the per-head
+ * one stands for (dt and A repeated over each head's channels, A per
+ * channel), with the per-channel gradients of dt and A summed over each
+ * head's channels (in fp32, in a fixed order).  It runs on the recurrence's
+ * backward kernels, not on the matrix cores.
+ *   inputs      : as ssm_ssd_fwd (dt [batch, seqlen, nheads], A [nheads]).
+ *   dy          : [batch, seqlen, nheads * headdim] io_dtype; dh_last as
+ *                 h_last, NULL => 0.
+ *   dx, dz      : [batch, seqlen, nheads * headdim] io_dtype (dz required
+ *                 when z is given, NULL otherwise).
+ *   ddt         : [batch, seqlen, nheads] io_dtype.  dA : [nheads] fp32.
+ *   dB, dC      : [batch, seqlen, dstate] io_dtype.  dD : [nheads * headdim]
+ *                 fp32, NULL => not written.  dh0 : as h0, NULL => not written.
+ *   workspace   : at least ssm_ssd_bwd_workspace_bytes(...) bytes.
+ * io_dtype fp32 or bf16, any headdim, dstate 16, 32, 64 or 128 (other:
+ * SSM_ERR_UNSUPPORTED).  Deterministic.  Outputs must not alias inputs, each
+ * other or the workspace.  Returns an SSM_* status.
+ */
+int ssm_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                int64_t dstate, int io_dtype, int discretization, const void *x,
+                const void *dt, const float *A, const void *B, const void *C,
+                const float *Dskip, const void *z, const float *h0, const void *dy,
+                const float *dh_last, void *dx, void *ddt, float *dA, void *dB, void *dC,
+                float *dD, void *dz, float *dh0, void *workspace, size_t workspace_bytes,
+                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,7 +12,7 @@ options; d_state 16, 32, 64, 128), ``scan_fwd_fused`` (with the causal
 conv1d + softplus prologue), ``scan_bwd`` and the autograd wrapper
 ``SelectiveScan`` (all input gradients), ``decode_step`` (one recurrent step
 on a resident state), ``ssd_scan`` (step and decay shared per head of 64
-channels, on the matrix cores).
+channels, on the matrix cores) and its backward ``ssd_bwd``.
 """
 from __future__ import annotations
 
@@ -23,6 +23,7 @@ import threading
 import torch
 
 __all__ = ["scan_fwd", "scan_fwd_fused", "scan_bwd", "SelectiveScan", "decode_step", "ssd_scan",
+           "ssd_bwd",
            "scan_plan", "scan_workspace_bytes", "scan_bwd_workspace_bytes", "load_library",
            "LIB_PATH", "SsmError"]
 
@@ -62,6 +63,9 @@ SIGNATURES = {
     "ssm_scan_bwd": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
                      + [_vp] * 15 + [_vp, _sz, _vp]),
     "ssm_ssd_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 10 + [_vp]),
+    "ssm_ssd_bwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _i64, _int]),
+    "ssm_ssd_bwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 18
+                    + [_vp, _sz, _vp]),
 }
 
 _lock = threading.Lock()
@@ -268,6 +272,68 @@ def ssd_scan(x, dt, A, B, C, D=None, z=None, h0=None, return_last_state=False,
         _stream(device))
     _check(st, "ssm_ssd_fwd")
     return (y, h_last) if return_last_state else y
+
+
+def ssd_bwd(x, dt, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None,
+            discretization: str = "zoh", need_dD: bool = True, need_dh0: bool = True,
+            workspace=None):
+    """Gradients of ``ssd_scan`` for upstream dy (and dh_last).  Returns a dict:
+    dx, dz (None without z), ddt, dB, dC in the I/O dtype; dA [nheads], dD
+    (None unless need_dD), dh0 (None unless need_dh0) in float32."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a [batch, seqlen, dim] tensor")
+    if not isinstance(dt, torch.Tensor) or dt.dim() != 3:
+        raise ValueError("dt must be a [batch, seqlen, nheads] tensor")
+    if not isinstance(B, torch.Tensor) or B.dim() != 3:
+        raise ValueError("B must be a [batch, seqlen, dstate] tensor")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    if discretization not in ("zoh", "euler"):
+        raise ValueError("discretization must be 'zoh' or 'euler'")
+    batch, seqlen, dim = x.shape
+    nheads = dt.shape[2]
+    if nheads == 0 or dim % nheads:
+        raise ValueError("x's channels must split evenly into dt's heads")
+    headdim, dstate = dim // nheads, B.shape[2]
+    io = x.dtype
+    code = _io_code(io)
+    _require(x, "x", (batch, seqlen, dim), io, device)
+    _require(dt, "dt", (batch, seqlen, nheads), io, device)
+    _require(A, "A", (nheads,), torch.float32, device)
+    _require(B, "B", (batch, seqlen, dstate), io, device)
+    _require(C, "C", (batch, seqlen, dstate), io, device)
+    _require(D, "D", (dim,), torch.float32, device)
+    _require(z, "z", (batch, seqlen, dim), io, device)
+    _require(h0, "h0", (batch, dim, dstate), torch.float32, device)
+    _require(dy, "dy", (batch, seqlen, dim), io, device)
+    _require(dh_last, "dh_last", (batch, dim, dstate), torch.float32, device)
+    if A is None or C is None or dy is None:
+        raise ValueError("A, C and dy are required")
+    g = {
+        "dx": torch.empty_like(x), "ddt": torch.empty_like(dt),
+        "dz": torch.empty_like(x) if z is not None else None,
+        "dA": torch.empty_like(A), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+        "dD": torch.empty(dim, dtype=torch.float32, device=device) if need_dD else None,
+        "dh0": (torch.empty((batch, dim, dstate), dtype=torch.float32, device=device)
+                if need_dh0 else None),
+    }
+    lib = load_library()
+    nbytes = lib.ssm_ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, code)
+    if nbytes < 0:
+        raise ValueError("invalid sizes")
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_ssd_bwd(batch, seqlen, nheads, headdim, dstate, code,
+                         SSM_DISC_EULER if discretization == "euler" else SSM_DISC_ZOH,
+                         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                         _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddt"]),
+                         _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                         _ptr(g["dz"]), _ptr(g["dh0"]), _ptr(workspace), ws_bytes,
+                         _stream(device))
+    _check(st, "ssm_ssd_bwd")
+    return g
 
 
 def scan_fwd_fused(x_raw, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None, z=None,

@@ -380,6 +380,42 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, fl
 // ---------------------------------------------------------------------------
 namespace {
 
+// Workspace pointers of a backward (chunk carries and partial sums).
+void set_bwd_workspace(ssm::BwdArgs& a, const ssm::BwdWorkspace& w, char* base, int K) {
+  if (K > 1) {
+    a.f.ws_hloc = reinterpret_cast<float*>(base + w.fwd.hloc_off);
+    a.f.ws_hin = reinterpret_cast<float*>(base + w.fwd.hin_off);
+    a.f.ws_sdelta = reinterpret_cast<double*>(base + w.fwd.sdelta_off);
+    a.ws_eloc = reinterpret_cast<float*>(base + w.rev_base + w.rev.hloc_off);
+    a.ws_ein = reinterpret_cast<float*>(base + w.rev_base + w.rev.hin_off);
+    a.ws_sdr = reinterpret_cast<double*>(base + w.rev_base + w.rev.sdelta_off);
+  }
+  a.ws_pdB = reinterpret_cast<float*>(base + w.pdB_off);
+  a.ws_pdC = reinterpret_cast<float*>(base + w.pdC_off);
+  a.ws_pdA = reinterpret_cast<float*>(base + w.pdA_off);
+  a.ws_pdD = reinterpret_cast<float*>(base + w.pdD_off);
+}
+
+// Workspace of the per-head backward: the sliced backward's, plus delta and A
+// repeated over each head's channels, the per-channel dA and (unused
+// afterwards) per-channel ddelta.
+struct SsdBwdLayout {
+  ssm::BwdSliceWorkspace s;
+  size_t delta_off, ach_off, dach_off, ddch_off, total;
+};
+SsdBwdLayout ssd_bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int K, int io_bytes) {
+  auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
+  SsdBwdLayout l{};
+  l.s = ssm::bwd_slice_layout(batch, seqlen, dim, K, io_bytes);
+  const size_t rows = (size_t)batch * seqlen * dim * io_bytes;
+  l.delta_off = align(l.s.total);
+  l.ach_off = l.delta_off + align(rows);
+  l.dach_off = l.ach_off + align((size_t)dim * sizeof(float));
+  l.ddch_off = l.dach_off + align((size_t)dim * sizeof(float));
+  l.total = l.ddch_off + align(rows);
+  return l;
+}
+
 // State sizes whose backward runs as 16-state slices.
 bool bwd_sliced(int64_t dstate) { return dstate == 32 || dstate == 64 || dstate == 128; }
 
@@ -468,6 +504,7 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
 
   char* base = static_cast<char*>(workspace);
   ssm::BwdArgs a{};
+  set_bwd_workspace(a, w, base, K);
   ssm::ScanArgs& f = a.f;
   f.x = x;
   f.delta = delta;
@@ -484,18 +521,6 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   f.nchunks = K;
   f.a_per_channel = a_per_channel;
   f.euler = discretization == SSM_DISC_EULER ? 1 : 0;
-  if (K > 1) {
-    f.ws_hloc = reinterpret_cast<float*>(base + w.fwd.hloc_off);
-    f.ws_hin = reinterpret_cast<float*>(base + w.fwd.hin_off);
-    f.ws_sdelta = reinterpret_cast<double*>(base + w.fwd.sdelta_off);
-    a.ws_eloc = reinterpret_cast<float*>(base + w.rev_base + w.rev.hloc_off);
-    a.ws_ein = reinterpret_cast<float*>(base + w.rev_base + w.rev.hin_off);
-    a.ws_sdr = reinterpret_cast<double*>(base + w.rev_base + w.rev.sdelta_off);
-  }
-  a.ws_pdB = reinterpret_cast<float*>(base + w.pdB_off);
-  a.ws_pdC = reinterpret_cast<float*>(base + w.pdC_off);
-  a.ws_pdA = reinterpret_cast<float*>(base + w.pdA_off);
-  a.ws_pdD = reinterpret_cast<float*>(base + w.pdD_off);
   a.dy = dy;
   a.dh_last = dh_last;
   a.dx = dx;
@@ -562,6 +587,122 @@ int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, 
   a.dim = (int)dim;
   a.euler = discretization == SSM_DISC_EULER ? 1 : 0;
   return hip_status(ssm::launch_ssd(a, (int)dstate, s));
+}
+
+int64_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                    int64_t headdim, int64_t dstate, int io_dtype) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim <= 0 || dstate <= 0 ||
+      !valid_dtype(io_dtype) || nheads > (int64_t)INT32_MAX / headdim)
+    return -1;
+  if (batch == 0 || seqlen == 0 || nheads == 0) return 0;
+  int64_t len;
+  int K;
+  bwd_plan(seqlen, &len, &K);
+  return (int64_t)ssd_bwd_layout(batch, seqlen, nheads * headdim, K,
+                                 io_dtype == SSM_DTYPE_BF16 ? 2 : 4)
+      .total;
+}
+
+int ssm_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                int io_dtype, int discretization, const void* x, const void* dt, const float* A,
+                const void* B, const void* C, const float* Dskip, const void* z,
+                const float* h0, const void* dy, const float* dh_last, void* dx, void* ddt,
+                float* dA, void* dB, void* dC, float* dD, void* dz, float* dh0,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim <= 0 || dstate <= 0 ||
+      !valid_dtype(io_dtype) || nheads > (int64_t)INT32_MAX / headdim)
+    return SSM_ERR_INVALID_ARG;
+  if (discretization != SSM_DISC_ZOH && discretization != SSM_DISC_EULER)
+    return SSM_ERR_INVALID_ARG;
+  if (dstate != kDState && !bwd_sliced(dstate)) return SSM_ERR_UNSUPPORTED;
+  if (!A || !dA) return SSM_ERR_INVALID_ARG;
+  if ((z == nullptr) != (dz == nullptr)) return SSM_ERR_INVALID_ARG;
+  const int64_t dim = nheads * headdim;
+  if (seqlen > 0 && batch > 0 && dim > 0 &&
+      (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
+    return SSM_ERR_INVALID_ARG;
+  const void* ins[] = {x, dt, A, B, C, Dskip, z, h0, dy, dh_last};
+  const void* outs[] = {dx, ddt, dA, dB, dC, dD, dz, dh0};
+  for (const void* o : outs) {
+    if (!o) continue;
+    for (const void* in : ins)
+      if (in == o) return SSM_ERR_INVALID_ARG;
+    int same = 0;
+    for (const void* o2 : outs) same += (o2 == o);
+    if (same > 1) return SSM_ERR_INVALID_ARG;
+  }
+  if (!all_aligned(x, dt, A, B, C, Dskip, z, h0, dy, dh_last, workspace) ||
+      !all_aligned(dx, ddt, dA, dB, dC, dD, dz, dh0))
+    return SSM_ERR_INVALID_ARG;
+  if (batch > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  auto s = static_cast<hipStream_t>(stream);
+  if (dim == 0) return SSM_OK;
+  if (batch == 0 || seqlen == 0) {
+    // no steps: dA = dD = 0, dh0 = dh_last (or 0)
+    hipError_t e = ssm::launch_copy_state(nullptr, dA, nheads, s);
+    if (e == hipSuccess && dD) e = ssm::launch_copy_state(nullptr, dD, dim, s);
+    if (e == hipSuccess && dh0 && batch > 0)
+      e = ssm::launch_copy_state(dh_last, dh0, batch * dim * dstate, s);
+    return hip_status(e);
+  }
+  int64_t chunk_len;
+  int K;
+  bwd_plan(seqlen, &chunk_len, &K);
+  if (K > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  const int io_bytes = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const SsdBwdLayout l = ssd_bwd_layout(batch, seqlen, dim, K, io_bytes);
+  if (!workspace || workspace_bytes < l.total) return SSM_ERR_WORKSPACE;
+  for (const void* p : ins)
+    if (p && p == workspace) return SSM_ERR_INVALID_ARG;
+  for (const void* o : outs)
+    if (o && o == workspace) return SSM_ERR_INVALID_ARG;
+
+  char* base = static_cast<char*>(workspace);
+  void* delta_ch = base + l.delta_off;
+  float* a_ch = reinterpret_cast<float*>(base + l.ach_off);
+  float* da_ch = reinterpret_cast<float*>(base + l.dach_off);
+  hipError_t e =
+      ssm::launch_repeat_heads(dt, delta_ch, batch * seqlen, (int)nheads, (int)headdim, io_bytes, s);
+  if (e == hipSuccess) e = ssm::launch_repeat_heads(A, a_ch, 1, (int)nheads, (int)headdim, 4, s);
+  if (e != hipSuccess) return hip_status(e);
+
+  ssm::BwdArgs a{};
+  set_bwd_workspace(a, l.s.base, base, K);
+  ssm::ScanArgs& f = a.f;
+  f.x = x;
+  f.delta = delta_ch;
+  f.A = a_ch;
+  f.B = B;
+  f.C = C;
+  f.Dskip = Dskip;
+  f.z = z;
+  f.h0 = h0;
+  f.seqlen = seqlen;
+  f.chunk_len = chunk_len;
+  f.dim = (int)dim;
+  f.batch = (int)batch;
+  f.nchunks = K;
+  f.a_per_channel = 1;
+  f.euler = discretization == SSM_DISC_EULER ? 1 : 0;
+  a.dy = dy;
+  a.dh_last = dh_last;
+  a.dx = dx;
+  a.ddelta = base + l.ddch_off;
+  a.dz = dz;
+  a.dA = da_ch;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = dD;
+  a.dh0 = dh0;
+  e = ssm::launch_scan_bwd_sliced(a, (int)dstate, io_dtype == SSM_DTYPE_BF16, base, l.s, s);
+  // per-head gradients: the channels' fp32 ddelta sums and dA, summed per head
+  if (e == hipSuccess)
+    e = ssm::launch_sum_heads(reinterpret_cast<const float*>(base + l.s.accd_off), ddt,
+                              batch * seqlen, (int)nheads, (int)headdim,
+                              io_dtype == SSM_DTYPE_BF16 ? 1 : 0, s);
+  if (e == hipSuccess)
+    e = ssm::launch_sum_heads(da_ch, dA, 1, (int)nheads, (int)headdim, 0, s);
+  return hip_status(e);
 }
 
 }  // extern "C"

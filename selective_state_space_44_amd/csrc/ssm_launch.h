@@ -153,6 +153,15 @@ BwdSliceWorkspace bwd_slice_layout(int64_t batch, int64_t seqlen, int64_t dim, i
 hipError_t launch_scan_bwd_sliced(const BwdArgs& a, int dstate, bool io_bf16, char* wsb,
                                   const BwdSliceWorkspace& w, hipStream_t stream);
 
+// Head <-> channel maps of the step and decay shared per head:
+// out[r, h * P + p] = in[r, h] (elements of 2 or 4 bytes), and
+// out[r, h] = sum over p of in[r, h * P + p] (fp32 in; out_kind 1 = bf16,
+// 0 = fp32).
+hipError_t launch_repeat_heads(const void* in, void* out, int64_t rows, int heads, int P,
+                               int elem_bytes, hipStream_t stream);
+hipError_t launch_sum_heads(const float* in, void* out, int64_t rows, int heads, int P,
+                            int out_kind, hipStream_t stream);
+
 // Scan for state sizes 32, 64, 128: one pass over the sequence, no
 // workspace (chunk fields of ScanArgs unused; no prologue).
 bool scan_wide_supported(int64_t dstate);

@@ -806,6 +806,64 @@ hipError_t launch_bwd_finish(const BwdArgs& a, const float* accx, const float* a
 
 }  // namespace
 
+namespace {
+
+// out[r, h * P + p] = in[r, h] for rows r, heads h, p < P.
+template <typename T>
+__global__ __launch_bounds__(256) void repeat_heads_kernel(const T* __restrict__ in,
+                                                           T* __restrict__ out, int64_t rows,
+                                                           int heads, int P) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)heads * P;
+  if (i >= rows * per_row) return;
+  const int64_t r = i / per_row;
+  out[i] = in[r * heads + (int)(i % per_row) / P];
+}
+
+// out[r, h] = sum over p < P of in[r, h * P + p], in a fixed order.
+template <typename OUT>
+__global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict__ in,
+                                                        OUT* __restrict__ out, int64_t rows,
+                                                        int heads, int P) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * heads) return;
+  const float* src = in + i * P;  // row r, head h: i = r * heads + h
+  float s = 0.0f;
+  for (int p = 0; p < P; ++p) s += src[p];
+  io<OUT>::store(out + i, s);
+}
+
+}  // namespace
+
+hipError_t launch_repeat_heads(const void* in, void* out, int64_t rows, int heads, int P,
+                               int elem_bytes, hipStream_t stream) {
+  const int64_t n = rows * heads * (int64_t)P;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(repeat_heads_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), rows,
+                       heads, P);
+  else
+    hipLaunchKernelGGL(repeat_heads_kernel<float>, grid, dim3(256), 0, stream,
+                       static_cast<const float*>(in), static_cast<float*>(out), rows, heads, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_heads(const float* in, void* out, int64_t rows, int heads, int P,
+                            int out_kind, hipStream_t stream) {
+  const int64_t n = rows * heads;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (out_kind == 1)
+    hipLaunchKernelGGL(sum_heads_kernel<bf16>, grid, dim3(256), 0, stream, in,
+                       static_cast<bf16*>(out), rows, heads, P);
+  else
+    hipLaunchKernelGGL(sum_heads_kernel<float>, grid, dim3(256), 0, stream, in,
+                       static_cast<float*>(out), rows, heads, P);
+  return hipGetLastError();
+}
+
 BwdSliceWorkspace bwd_slice_layout(int64_t batch, int64_t seqlen, int64_t dim, int nchunks,
                                    int io_bytes) {
   auto align = [](size_t v) { return (v + 255) & ~size_t(255); };

@@ -149,6 +149,23 @@ def test_backward_output_may_not_be_the_workspace(lib):
     assert st == ssm.SSM_ERR_INVALID_ARG
 
 
+def test_ssd_backward_rejects_bad_arguments(lib):
+    """Every case fails validation before any launch."""
+    q = [ctypes.c_void_p(0x1000 * k) for k in range(1, 30)]
+    def bwd(disc=ssm.SSM_DISC_ZOH, io=1, N=64, z=None, dz=None, dx=None, ws_bytes=1 << 40):
+        return lib.ssm_ssd_bwd(2, 8, 2, 64, N, io, disc, q[0], q[1], q[2], q[3], q[4], None, z,
+                               None, q[5], None, dx or q[6], q[7], q[8], q[9], q[10], None, dz,
+                               None, q[11], ws_bytes, None)
+    assert bwd(disc=2) == ssm.SSM_ERR_INVALID_ARG
+    assert bwd(io=7) == ssm.SSM_ERR_INVALID_ARG
+    assert bwd(N=24) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(z=q[12]) == ssm.SSM_ERR_INVALID_ARG             # z without dz
+    assert bwd(dx=q[0]) == ssm.SSM_ERR_INVALID_ARG             # dx aliases x
+    assert bwd(ws_bytes=16) == ssm.SSM_ERR_WORKSPACE
+    assert lib.ssm_ssd_bwd_workspace_bytes(2, 8, 2, 64, 64, 1) > 0
+    assert lib.ssm_ssd_bwd_workspace_bytes(-1, 8, 2, 64, 64, 1) == -1
+
+
 def test_ssd_rejects_bad_arguments(lib):
     """Every case fails validation (or is a no-op) before any launch."""
     def ssd(batch=2, L=8, H=2, P=64, N=128, io=1, disc=ssm.SSM_DISC_ZOH, x=FAKE, A=FAKE,

@@ -332,6 +332,30 @@ int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                 float *h_last, void *stream);
 
 /*
+ * ssm_ssd_fwd with the sequence cut into segments that separate blocks run:
+ * a state-only pass gives each segment's end state from a zero state and its
+ * decay, a carry composes them in order (the recurrence composes segment by
+ * segment: paperlens tutorial, "計算量: 系列長との付き合い方"), and the main
+ * pass starts every segment from its entering state.  This gives a few
+ * (batch row, head) pairs, e.g. one long sequence, enough blocks to fill the
+ * chip, at the price of the state-only pass over all segments but the last.
+ *   nsplit    : number of segments; 0 => automatic (none when there are at
+ *               least 640 blocks of (half head, batch row), else about 1280
+ *               blocks, no segment shorter than 256 steps); 1 => ssm_ssd_fwd.
+ *   workspace : at least ssm_ssd_fwd_workspace_bytes(..., nsplit) bytes (may
+ *               be NULL when that is 0).
+ * Other arguments, results and errors as ssm_ssd_fwd.
+ */
+int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                    int64_t headdim, int64_t dstate, int nsplit);
+int ssm_ssd_fwd_planned(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int io_dtype, int discretization, const void *x,
+                        const void *dt, const float *A, const void *B, const void *C,
+                        const float *Dskip, const void *z, const float *h0, void *y,
+                        float *h_last, int nsplit, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
  * Workspace of ssm_ssd_bwd in bytes for these sizes (-1 for invalid sizes,
  * 0 when nothing is needed).
  */

@@ -63,6 +63,9 @@ SIGNATURES = {
     "ssm_scan_bwd": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
                      + [_vp] * 15 + [_vp, _sz, _vp]),
     "ssm_ssd_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 10 + [_vp]),
+    "ssm_ssd_fwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _i64, _int]),
+    "ssm_ssd_fwd_planned": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 10
+                            + [_int, _vp, _sz, _vp]),
     "ssm_ssd_bwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _i64, _int]),
     "ssm_ssd_bwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 18
                     + [_vp, _sz, _vp]),
@@ -226,12 +229,14 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
 
 
 def ssd_scan(x, dt, A, B, C, D=None, z=None, h0=None, return_last_state=False,
-             discretization: str = "zoh", out=None):
-    """Scan with the step and decay rate shared by each head (``ssm_ssd_fwd``).
-    x, z: [batch, L, nheads * headdim]; dt: [batch, L, nheads]; B, C:
-    [batch, L, dstate] (all bfloat16); A [nheads], D [nheads * headdim], h0
-    [batch, nheads * headdim, dstate] float32.  headdim = x.shape[2] //
-    dt.shape[2].  Returns y (and the final state when ``return_last_state``)."""
+             discretization: str = "zoh", out=None, nsplit: int = 0, workspace=None):
+    """Scan with the step and decay rate shared by each head
+    (``ssm_ssd_fwd_planned``).  x, z: [batch, L, nheads * headdim]; dt:
+    [batch, L, nheads]; B, C: [batch, L, dstate] (all bfloat16); A [nheads],
+    D [nheads * headdim], h0 [batch, nheads * headdim, dstate] float32.
+    headdim = x.shape[2] // dt.shape[2].  ``nsplit`` sequence segments (0 =
+    automatic, 1 = none).  Returns y (and the final state when
+    ``return_last_state``)."""
     if not isinstance(x, torch.Tensor) or x.dim() != 3:
         raise ValueError("x must be a [batch, seqlen, dim] tensor")
     if not isinstance(dt, torch.Tensor) or dt.dim() != 3:
@@ -265,12 +270,19 @@ def ssd_scan(x, dt, A, B, C, D=None, z=None, h0=None, return_last_state=False,
     _require(y, "out", (batch, seqlen, dim), io, device)
     h_last = (torch.empty((batch, dim, dstate), dtype=torch.float32, device=device)
               if return_last_state else None)
-    st = load_library().ssm_ssd_fwd(
+    lib = load_library()
+    nbytes = lib.ssm_ssd_fwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, int(nsplit))
+    if nbytes < 0:
+        raise ValueError("invalid sizes")
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_ssd_fwd_planned(
         batch, seqlen, nheads, headdim, dstate, code,
         SSM_DISC_EULER if discretization == "euler" else SSM_DISC_ZOH, _ptr(x), _ptr(dt),
         _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
-        _stream(device))
-    _check(st, "ssm_ssd_fwd")
+        int(nsplit), _ptr(workspace), ws_bytes, _stream(device))
+    _check(st, "ssm_ssd_fwd_planned")
     return (y, h_last) if return_last_state else y
 
 

@@ -187,7 +187,18 @@ struct SsdArgs {
   int nheads;
   int dim;             // nheads * 64
   int euler;
+  // Sequence segments run by separate blocks (nseg > 1): a state-only pass
+  // writes each segment's end state from zero and the log2 of its decay, a
+  // carry composes them in order, and the main pass starts every segment from
+  // its entering state.
+  int nseg;            // 1 = one block walks the whole sequence
+  int64_t seg_len;     // steps per segment, a multiple of 32
+  float* ws_hloc;      // [batch, nseg, dim, dstate]
+  float* ws_hin;       // [batch, nseg, dim, dstate] (segment 0 unused)
+  float* ws_dlog;      // [batch, nseg, nheads]
 };
+size_t ssd_workspace_bytes(int64_t batch, int64_t dim, int64_t nheads, int64_t dstate,
+                           int nseg);
 bool ssd_supported(int64_t headdim, int64_t dstate);
 size_t ssd_smem_bytes(int64_t dstate);
 hipError_t launch_ssd(const SsdArgs& a, int dstate, hipStream_t stream);

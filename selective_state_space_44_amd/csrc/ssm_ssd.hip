@@ -165,7 +165,9 @@ __device__ __forceinline__ u32x4_t identity_pick4(int r16, int g) {
   return {e0 | (e1 << 16), e2 | (e3 << 16), 0u, 0u};
 }
 
-template <int N, bool HAS_Z, bool EULER>
+// PRE: the state-only pass over segments 0..nseg-2 (no outputs): end state
+// from zero and the log2 of the segment's decay, into the workspace.
+template <int N, bool HAS_Z, bool EULER, bool PRE>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void ssd_scan_kernel(SsdArgs a) {
   constexpr int NT2 = N / 32;   // state tiles per wave (half of the N/16)
@@ -205,17 +207,26 @@ void ssd_scan_kernel(SsdArgs a) {
   const int d = cb + p;
   const float Dp = a.Dskip ? a.Dskip[d] : 0.0f;
   const int ts = tid & (kQ - 1), cg = tid >> 5;  // staging: step, column group
+  // this block's steps [tb, te)
+  const int seg = blockIdx.z;
+  const int64_t tb = (int64_t)seg * a.seg_len;
+  const int64_t te = tb + a.seg_len < L ? tb + a.seg_len : L;
+  const size_t seg_row = (size_t)b * a.nseg + seg;  // (batch row, segment) of the workspace
+  const size_t soff = 16 * nh * NT2 + 4 * g;        // this lane's first state
 
   // state tile j: st[j][q] = h[n = 16 (nh NT2 + j) + 4 g + q][p]
   f32x4_t st[NT2];
-  if (a.h0) {
-    const float* src = a.h0 + ((size_t)b * dim + d) * N + 16 * nh * NT2 + 4 * g;
-#pragma unroll
-    for (int j = 0; j < NT2; ++j) st[j] = *reinterpret_cast<const f32x4_t*>(src + 16 * j);
-  } else {
-#pragma unroll
-    for (int j = 0; j < NT2; ++j) st[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float* src = nullptr;
+  if (!PRE) {
+    if (seg > 0)
+      src = a.ws_hin + (seg_row * dim + d) * N + soff;
+    else if (a.h0)
+      src = a.h0 + ((size_t)b * dim + d) * N + soff;
   }
+#pragma unroll
+  for (int j = 0; j < NT2; ++j)
+    st[j] = src ? *reinterpret_cast<const f32x4_t*>(src + 16 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float dlog = 0.0f;  // PRE: log2 of the segment's decay
 
   const u32x4_t ipick[2] = {identity_pick(0, r16, g), identity_pick(16, r16, g)};
   const u32x4_t ipick4 = identity_pick4(r16, g);
@@ -232,7 +243,7 @@ void ssd_scan_kernel(SsdArgs a) {
     uint32_t dt;
   };
   auto fetch = [&](Stage& sg, int64_t t0) {
-    const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
+    const uint32_t rows = (uint32_t)(te - t0 < kQ ? te - t0 : (int64_t)kQ);
     if (w == 3) {
       const __amdgpu_buffer_rsrc_t rsd = make_rsrc(
           static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows * (uint32_t)H * 2u);
@@ -244,7 +255,7 @@ void ssd_scan_kernel(SsdArgs a) {
     const __amdgpu_buffer_rsrc_t rsx = make_rsrc(
         static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
     sg.x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsx, ox, 0, 0));
-    if constexpr (HAS_Z) {
+    if constexpr (HAS_Z && !PRE) {
       const __amdgpu_buffer_rsrc_t rsz = make_rsrc(
           static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
       sg.z = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsz, ox, 0, 0));
@@ -258,8 +269,9 @@ void ssd_scan_kernel(SsdArgs a) {
     for (int j = 0; j < NBV; ++j) {
       sg.b[j] = __builtin_bit_cast(u32x4_t,
                                    __builtin_amdgcn_raw_buffer_load_b128(rsb, ob + 16u * j, 0, 0));
-      sg.c[j] = __builtin_bit_cast(u32x4_t,
-                                   __builtin_amdgcn_raw_buffer_load_b128(rsc, ob + 16u * j, 0, 0));
+      if constexpr (!PRE)
+        sg.c[j] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsc, ob + 16u * j, 0, 0));
     }
   };
   // wave 3: the chunk's decay exponents (inclusive prefix sum of a * dt over
@@ -282,25 +294,25 @@ void ssd_scan_kernel(SsdArgs a) {
     }
   };
 
-  const int64_t nck = (L + kQ - 1) / kQ;
+  const int64_t nck = (te - tb + kQ - 1) / kQ;
   auto chunk = [&](int64_t c, Stage& cur, const Stage& nxt) {
-    const int64_t t0 = c * kQ;
+    const int64_t t0 = tb + c * kQ;
     const int buf = (int)(c & 1);
     __syncthreads();  // every read of the previous chunk's LDS is done
 
     // ---- stage the chunk in natural layout ----------------------------
     *reinterpret_cast<u32x2_t*>(&sm.xs[ts][4 * cg]) = cur.x;
-    if constexpr (HAS_Z) *reinterpret_cast<u32x2_t*>(&sm.zs[ts][4 * cg]) = cur.z;
+    if constexpr (HAS_Z && !PRE) *reinterpret_cast<u32x2_t*>(&sm.zs[ts][4 * cg]) = cur.z;
 #pragma unroll
     for (int j = 0; j < NBV; ++j) {
       *reinterpret_cast<u32x4_t*>(&sm.bs[ts][NB * cg + 8 * j]) = cur.b[j];
-      *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = cur.c[j];
+      if constexpr (!PRE) *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = cur.c[j];
     }
     __syncthreads();
 
     if (c + 2 < nck) fetch(cur, t0 + 2 * kQ);
 
-    if (w < 3) {
+    if (!PRE && w < 3) {
       // ---- masked weights P: tiles (0,0), (1,0), (1,1) on waves 0..2 ----
       const int I = w > 0 ? 1 : 0, J = w == 1 ? 0 : I;
       // M^T tile: rows j (B rows), columns i (C rows), contraction over states
@@ -325,14 +337,15 @@ void ssd_scan_kernel(SsdArgs a) {
       split_bf16(v[2], v[3], h1w, l1w);
       *reinterpret_cast<u32x2_t*>(&sm.pmh[i][16 * J + 4 * g]) = u32x2_t{h0w, h1w};
       *reinterpret_cast<u32x2_t*>(&sm.pml[i][16 * J + 4 * g]) = u32x2_t{l0w, l1w};
-    } else if (c + 1 < nck) {
+    } else if (w == 3 && c + 1 < nck) {
       scan(nxt, buf ^ 1);  // wave 3: the next chunk's per-step values
     }
 
+    f32x4_t yst[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if constexpr (!PRE) {
     // ---- C h over this wave's state half, both row tiles ----------------
     // the entering state as B operands: slots 0..3 = tile 2k, 4..7 = tile
     // 2k + 1 of the half (states nh N/2 + 32k + 4g + q and + 16)
-    f32x4_t yst[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       uint32_t hw[4], lw[4];
@@ -352,6 +365,7 @@ void ssd_scan_kernel(SsdArgs a) {
     // the other half's wave finishes row tile 1 - nh
     *reinterpret_cast<f32x4_t*>(&sm.part[pt][1 - nh][lane][0]) = nh ? yst[0] : yst[1];
     __syncthreads();
+    }
 
     // ---- x (and z) of this wave's channels in result layout ------------
     // xc[tt][q] = x[16 tt + 4 g + q][p], exact, from identity products
@@ -360,6 +374,7 @@ void ssd_scan_kernel(SsdArgs a) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) xc[tt] = mfma_k32(lds128(&sm.xs[16 * tt + r16][8 * g]), ipick[pt], zero4);
 
+    if constexpr (!PRE) {
     // ---- outputs of row tile I = nh for this wave's 16 channels ---------
     {
       const int I = nh, i = 16 * I + r16;
@@ -400,6 +415,7 @@ void ssd_scan_kernel(SsdArgs a) {
           (uint32_t)(16 * I + r16) * (uint32_t)dim * 2u + (uint32_t)(cb + 16 * pt + 4 * g) * 2u, 0,
           0);
     }
+    }
 
     // ---- state update: h <- exp(s_last) h + (w x)^T B, this half --------
     // B operand: w_t x_t[p] (column p, slots t = 4g + q and 16 + 4g + q),
@@ -417,6 +433,7 @@ void ssd_scan_kernel(SsdArgs a) {
       wl = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
     }
     const float dec = fast_exp2(sm.s2[buf][kQ - 1]);
+    if constexpr (PRE) dlog += sm.s2[buf][kQ - 1];
 #pragma unroll
     for (int j2 = 0; j2 < NT2 / 2; ++j2) {
       // states 32 n32 .. 32 n32 + 31 (two tiles of this half) of B, rows t
@@ -439,24 +456,47 @@ void ssd_scan_kernel(SsdArgs a) {
 
   Stage sa, sb;
   sb.dt = 0u;
-  fetch(sa, 0);
-  if (nck > 1) fetch(sb, kQ);
+  fetch(sa, tb);
+  if (nck > 1) fetch(sb, tb + kQ);
   if (w == 3) scan(sa, 0);
   for (int64_t c = 0; c < nck; c += 2) {
     chunk(c, sa, sb);
     if (c + 1 < nck) chunk(c + 1, sb, sa);
   }
 
-  if (a.h_last) {
-    float* dst = a.h_last + ((size_t)b * dim + d) * N + 16 * nh * NT2 + 4 * g;
+  float* dst = nullptr;
+  if (PRE)
+    dst = a.ws_hloc + (seg_row * dim + d) * N + soff;
+  else if (a.h_last && seg == a.nseg - 1)
+    dst = a.h_last + ((size_t)b * dim + d) * N + soff;
+  if (dst) {
 #pragma unroll
     for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = st[j];
   }
+  if (PRE && half == 0 && tid == 0) a.ws_dlog[seg_row * H + h] = dlog;
 }
 
-template <int N, bool HAS_Z, bool EULER>
-hipError_t launch_ssd_t(SsdArgs a, hipStream_t stream) {
-  auto kern = ssd_scan_kernel<N, HAS_Z, EULER>;
+// Entering state of each segment: h_in[s + 1] = exp2(dlog[s]) h_in[s] + hloc[s]
+// from h_in[0] = h0 (or 0), one thread per (batch row, channel, state);
+// consecutive threads take consecutive (channel, state), so every step's
+// loads and stores are coalesced rows.
+__global__ __launch_bounds__(256) void ssd_carry_kernel(SsdArgs a, int N) {
+  const int64_t per_b = (int64_t)a.dim * N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.batch * per_b) return;
+  const int64_t b = i / per_b, dn = i % per_b;
+  const int h = (int)(dn / N) / kHD;
+  float v = a.h0 ? a.h0[i] : 0.0f;
+  for (int s = 0; s + 1 < a.nseg; ++s) {
+    const size_t row = (size_t)b * a.nseg + s;
+    v = __builtin_fmaf(fast_exp2(a.ws_dlog[row * a.nheads + h]), v, a.ws_hloc[row * per_b + dn]);
+    a.ws_hin[(row + 1) * per_b + dn] = v;
+  }
+}
+
+template <int N, bool HAS_Z, bool EULER, bool PRE>
+hipError_t launch_ssd_pass(SsdArgs a, int segs, hipStream_t stream) {
+  auto kern = ssd_scan_kernel<N, HAS_Z, EULER, PRE>;
   const size_t smem = sizeof(SsdSmem<N>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -465,11 +505,25 @@ hipError_t launch_ssd_t(SsdArgs a, hipStream_t stream) {
   for (int64_t r0 = 0; r0 < a.batch; r0 += kMaxRows) {
     a.row0 = r0;
     const int rows = (int)(a.batch - r0 < kMaxRows ? a.batch - r0 : kMaxRows);
-    hipLaunchKernelGGL(kern, dim3(2 * a.nheads, rows), dim3(kSsdThreads), smem, stream, a);
+    hipLaunchKernelGGL(kern, dim3(2 * a.nheads, rows, segs), dim3(kSsdThreads), smem, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int N, bool HAS_Z, bool EULER>
+hipError_t launch_ssd_t(const SsdArgs& a, hipStream_t stream) {
+  if (a.nseg > 1) {
+    hipError_t e = launch_ssd_pass<N, HAS_Z, EULER, true>(a, a.nseg - 1, stream);
+    if (e != hipSuccess) return e;
+    const int64_t n = a.batch * (int64_t)a.dim * N;
+    hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       a, N);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_ssd_pass<N, HAS_Z, EULER, false>(a, a.nseg, stream);
 }
 
 template <int N>
@@ -484,6 +538,14 @@ hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {
 
 bool ssd_supported(int64_t headdim, int64_t dstate) {
   return headdim == kHD && (dstate == 64 || dstate == 128);
+}
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t dim, int64_t nheads, int64_t dstate,
+                           int nseg) {
+  if (nseg <= 1) return 0;
+  auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
+  const size_t st = (size_t)batch * nseg * dim * dstate * sizeof(float);
+  return 2 * align(st) + align((size_t)batch * nseg * nheads * sizeof(float));
 }
 
 size_t ssd_smem_bytes(int64_t dstate) {

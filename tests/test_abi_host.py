@@ -149,6 +149,17 @@ def test_backward_output_may_not_be_the_workspace(lib):
     assert st == ssm.SSM_ERR_INVALID_ARG
 
 
+def test_ssd_segments_need_workspace(lib):
+    n = lib.ssm_ssd_fwd_workspace_bytes(1, 4096, 2, 64, 128, 4)
+    assert n > 0 and lib.ssm_ssd_fwd_workspace_bytes(1, 4096, 2, 64, 128, 1) == 0
+    st = lib.ssm_ssd_fwd_planned(1, 4096, 2, 64, 128, 1, ssm.SSM_DISC_ZOH, FAKE,
+                                 ctypes.c_void_p(0x6000), FAKE, ctypes.c_void_p(0x7000),
+                                 ctypes.c_void_p(0x8000), None, None, None,
+                                 ctypes.c_void_p(0x2000), None, 4, ctypes.c_void_p(0x9000), 16,
+                                 None)
+    assert st == ssm.SSM_ERR_WORKSPACE
+
+
 def test_ssd_backward_rejects_bad_arguments(lib):
     """Every case fails validation before any launch."""
     q = [ctypes.c_void_p(0x1000 * k) for k in range(1, 30)]

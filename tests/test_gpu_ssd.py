@@ -159,3 +159,47 @@ def test_ssd_backward_optional_inputs_and_empty():
                     dy=torch.empty_like(p["x"]), dh_last=dhl)
     torch.cuda.synchronize()
     assert torch.count_nonzero(g["dA"]) == 0 and torch.equal(g["dh0"], dhl)
+
+
+# ---------------------------------------------------------------------------
+# sequence segments (state-only pass, carry, main pass)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("nsplit", [2, 3, 7])
+@pytest.mark.parametrize("n,disc", [(64, "zoh"), (128, "euler"), (128, "zoh")])
+def test_ssd_segments_match_oracle(nsplit, n, disc):
+    """L = 203 and 1000 (ragged last segment and chunk) with h0 and h_last."""
+    for L in (203, 1000):
+        print(f"ssd segments nsplit={nsplit} N={n} {disc} L={L}", flush=True)
+        p = _inputs(n, batch=2, seqlen=L, nheads=2)
+        y, h = ssm.ssd_scan(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"],
+                            return_last_state=True, discretization=disc, nsplit=nsplit)
+        torch.cuda.synchronize()
+        y_ref, h_ref = parity.oracle_ssd(p, discretization=disc)
+        parity.check_y(parity.to_f64(y), y_ref, torch.bfloat16, what=f"y nsplit={nsplit} L={L}")
+        parity.check_state(parity.to_f64(h), h_ref, what=f"h_last nsplit={nsplit} L={L}")
+
+
+def test_ssd_automatic_segments_single_long_sequence():
+    """One sequence of 4096 steps, 2 heads: the automatic plan cuts it into
+    16 segments; results match the oracle and the unsplit launch."""
+    p = _inputs(128, batch=1, seqlen=4096, nheads=2)
+    print("ssd automatic segments 1 x 4096 x 2 heads", flush=True)
+    y, h = ssm.ssd_scan(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"],
+                        return_last_state=True)
+    y1, h1 = ssm.ssd_scan(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"],
+                          return_last_state=True, nsplit=1)
+    torch.cuda.synchronize()
+    assert ssm.load_library().ssm_ssd_fwd_workspace_bytes(1, 4096, 2, 64, 128, 0) > 0
+    y_ref, h_ref = parity.oracle_ssd(p)
+    parity.check_y(parity.to_f64(y), y_ref, torch.bfloat16, what="y auto")
+    parity.check_state(parity.to_f64(h), h_ref, what="h_last auto")
+    parity.check_y(parity.to_f64(y1), y_ref, torch.bfloat16, what="y unsplit")
+
+
+def test_ssd_segments_zero_step_keeps_state():
+    p = _inputs(64, batch=2, seqlen=300, nheads=2)
+    p["dt"] = torch.zeros_like(p["dt"])
+    _, h = ssm.ssd_scan(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"],
+                        return_last_state=True, nsplit=4)
+    torch.cuda.synchronize()
+    assert torch.equal(h, p["h0"]), "dt = 0 must leave the state bit-for-bit unchanged"

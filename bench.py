@@ -305,6 +305,27 @@ def bench_ssd(steps: int, warmup: int):
     torch.cuda.synchronize()
     bwd_ms = e0.elapsed_time(e1) / rec_steps
     del ws, dy
+
+    # one long sequence (1 x 16384, same layer): the automatic sequence segments
+    # against one block per (half head, batch row)
+    q = W.make_ssd_inputs(w, device=dev, batch=1, seqlen=16384, layer=2)
+    yq = torch.empty_like(q["x"])
+    single = {}
+    for tag, ns in (("segments_auto", 0), ("unsplit", 1)):
+        nb = ssm.load_library().ssm_ssd_fwd_workspace_bytes(1, 16384, heads, P, N, ns)
+        wsq = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        run = lambda: ssm.ssd_scan(q["x"], q["dt"], q["A"], q["B"], q["C"], q["D"], q["z"], None,
+                                   out=yq, nsplit=ns, workspace=wsq)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(rec_steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        single[tag + "_ms"] = e0.elapsed_time(e1) / rec_steps
+    del q, yq
     return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
             "unit": "elements/s",
             "mfma": {"algorithmic_flop": flops, "achieved": flops / (ms * 1e-3) / 1e12,
@@ -314,7 +335,8 @@ def bench_ssd(steps: int, warmup: int):
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "recurrence_ms_per_step": rec_ms, "speedup_vs_recurrence": rec_ms / ms,
-            "backward_ms_per_step": bwd_ms}
+            "backward_ms_per_step": bwd_ms,
+            "single_sequence_1x16384": single}
 
 
 def bench_backward(steps: int, warmup: int):

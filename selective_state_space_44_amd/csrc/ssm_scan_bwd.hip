@@ -387,7 +387,7 @@ __device__ __forceinline__ void bwd_chunk(
     stage_tile<IO, HAS_Z, false>(sm.st, x, delta, B, C, z, dy, k, seqlen, dim, ts, kWave * G);
     __syncthreads();
     // the tile's states and Abar, recomputed from the tile entry state
-    float hck[NPL], hs[kBT][NPL];
+    float hck[NPL], hs[kBT][NPL], as[kBT][NPL];
 #pragma unroll
     for (int n = 0; n < NPL; ++n) hck[n] = sm.ck[j][k.g][n][k.lane];
 #pragma unroll
@@ -399,9 +399,11 @@ __device__ __forceinline__ void bwd_chunk(
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
         const float a = fast_exp2(dv * A2[n]);
+        as[s][n] = a;
         hs[s][n] = __builtin_fmaf(a, s ? hs[s - 1][n] : hck[n],
                                   input_term<V, ZERO_A>(a, dv, iA[n], bn[n] * xv));
         pin(hs[s][n]);
+        pin(as[s][n]);
       }
     }
     // the adjoint backwards through the tile, in two halves of kBT / 2 steps;
@@ -423,7 +425,7 @@ __device__ __forceinline__ void bwd_chunk(
         read_states<NPL>(&sm.st.c[s][n0], cn);
 #pragma unroll
         for (int n = 0; n < NPL; ++n) {
-          const float a = fast_exp2(dv * A2[n]);
+          const float a = as[s][n];
           const float coef = coef_of<V, ZERO_A>(a, dv, iA[n]);
           const float prev = s ? hs[s - 1][n] : hck[n];
           const float Bn = bn[n], Cn = cn[n];

@@ -115,6 +115,13 @@ def cpu_baseline(inp, w, target_s: float):
                       f"(fp64 C loop, gcc -O2, OpenMP over channels)"}
 
 
+def percentiles(ms):
+    """p10, median and p90 of per-step times in ms (nearest rank)."""
+    v = sorted(ms)
+    pick = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
 def bench_scan(steps: int, warmup: int):
     import torch
     import selective_state_space_44_amd as ssm
@@ -157,7 +164,8 @@ def bench_scan(steps: int, warmup: int):
     ev_main = [e[1].elapsed_time(e[2]) for e in evs]
     ev_carry = [e[0].elapsed_time(e[1]) for e in evs]
     return dict(w=w, G=G, K=K, wall_s=wall, step_ms=sum(ev_step) / steps,
-                main_ms=sum(ev_main) / steps, carry_ms=sum(ev_carry) / steps, inp=sets[0])
+                main_ms=sum(ev_main) / steps, carry_ms=sum(ev_carry) / steps, inp=sets[0],
+                step_pct=percentiles(ev_step), main_pct=percentiles(ev_main))
 
 
 def bench_fused(steps: int, warmup: int):
@@ -403,7 +411,8 @@ def bench_decode(sweeps: int):
         evs[r][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sweep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / sweeps
+    sweep_list = [e[0].elapsed_time(e[1]) for e in evs]
+    sweep_ms = sum(sweep_list) / sweeps
     kern_ms = sweep_ms / w.layers
     per_layer_bytes = w.algorithmic_bytes()
     elems = w.elements * w.layers
@@ -412,6 +421,7 @@ def bench_decode(sweeps: int):
         "workload": w.name,
         "value": elems / (sweep_ms * 1e-3), "unit": "elements/s",
         "ms_per_sweep_64_layers": sweep_ms,
+        "sweep_ms_percentiles": percentiles(sweep_list),
         "us_per_layer": kern_ms * 1e3,
         "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                 "bytes_per_launch": per_layer_bytes},
@@ -499,6 +509,8 @@ def main():
             "unit": "GB/s",
             "frac": alg_bytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
+        "step_ms_percentiles": r["step_pct"],
+        "main_pass_ms_percentiles": r["main_pct"],
         "carry_ms_per_step": r["carry_ms"],
         "wall_s_timed": r["wall_s"],
     }

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
 SOURCES = ["ssm_abi.cpp", "ssm_scan.hip", "ssm_scan_wide.hip", "ssm_scan_bwd.hip", "ssm_decode.hip",
-           "ssm_ssd.hip"]
+           "ssm_ssd.hip", "ssm_ssd_bwd.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for every HIP translation unit.

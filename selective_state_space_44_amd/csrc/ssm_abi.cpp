@@ -440,6 +440,44 @@ SsdBwdLayout ssd_bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int K, i
   return l;
 }
 
+// The masked-matrix backward (chunk-parallel, matrix cores): bf16 I/O,
+// 64-channel heads, 64 or 128 states, at most kMaxGridYZ chunks of 32 steps;
+// other shapes take the recurrence kernels with dt repeated over channels.
+bool ssd_bwd_mm(int io_dtype, int64_t headdim, int64_t dstate, int64_t seqlen) {
+  return io_dtype == SSM_DTYPE_BF16 && ssm::ssd_supported(headdim, dstate) &&
+         (seqlen + 31) / 32 <= kMaxGridYZ;
+}
+
+struct SsdBwdMmLayout {
+  size_t hbuf, gbuf, dlog, glog, dd, db, dc, da, dh0, total;
+  int nchunks, ngroups;
+};
+SsdBwdMmLayout ssd_bwd_mm_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dim,
+                                 int64_t dstate) {
+  auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
+  SsdBwdMmLayout l{};
+  l.nchunks = (int)((seqlen + 31) / 32);
+  l.ngroups = (int)((nheads + ssm::kSsdBwdHeadsPerBlock - 1) / ssm::kSsdBwdHeadsPerBlock);
+  const size_t K = (size_t)l.nchunks, f = sizeof(float);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align(bytes);
+    return at;
+  };
+  l.hbuf = take((size_t)batch * K * dim * dstate * f);
+  l.gbuf = take((size_t)batch * K * dim * dstate * f);
+  l.dlog = take((size_t)batch * K * nheads * f);
+  l.glog = take((size_t)batch * K * nheads * f);
+  l.dd = take((size_t)batch * K * dim * f);
+  l.db = take((size_t)batch * seqlen * l.ngroups * dstate * f);
+  l.dc = take((size_t)batch * seqlen * l.ngroups * dstate * f);
+  l.da = take((size_t)batch * K * nheads * f);
+  l.dh0 = take((size_t)batch * dim * dstate * f);
+  l.total = o;
+  return l;
+}
+
 // State sizes whose backward runs as 16-state slices.
 bool bwd_sliced(int64_t dstate) { return dstate == 32 || dstate == 64 || dstate == 128; }
 
@@ -660,6 +698,8 @@ int64_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nhead
       !valid_dtype(io_dtype) || nheads > (int64_t)INT32_MAX / headdim)
     return -1;
   if (batch == 0 || seqlen == 0 || nheads == 0) return 0;
+  if (ssd_bwd_mm(io_dtype, headdim, dstate, seqlen))
+    return (int64_t)ssd_bwd_mm_layout(batch, seqlen, nheads, nheads * headdim, dstate).total;
   int64_t len;
   int K;
   bwd_plan(seqlen, &len, &K);
@@ -709,6 +749,55 @@ int ssm_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, 
     if (e == hipSuccess && dh0 && batch > 0)
       e = ssm::launch_copy_state(dh_last, dh0, batch * dim * dstate, s);
     return hip_status(e);
+  }
+  if (ssd_bwd_mm(io_dtype, headdim, dstate, seqlen)) {
+    // the kernels address one 32-step chunk of a [b, L, dim] tensor with
+    // 32-bit byte offsets
+    if (nheads > ((int64_t)1 << 24) / headdim) return SSM_ERR_UNSUPPORTED;
+    const SsdBwdMmLayout l = ssd_bwd_mm_layout(batch, seqlen, nheads, dim, dstate);
+    if (!workspace || workspace_bytes < l.total) return SSM_ERR_WORKSPACE;
+    for (const void* p : ins)
+      if (p && p == workspace) return SSM_ERR_INVALID_ARG;
+    for (const void* o : outs)
+      if (o && o == workspace) return SSM_ERR_INVALID_ARG;
+    char* base = static_cast<char*>(workspace);
+    auto fp = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+    ssm::SsdBwdArgs a{};
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.Dskip = Dskip;
+    a.z = z;
+    a.h0 = h0;
+    a.dy = dy;
+    a.dh_last = dh_last;
+    a.dx = dx;
+    a.ddt = ddt;
+    a.dA = dA;
+    a.dB = dB;
+    a.dC = dC;
+    a.dD = dD;
+    a.dz = dz;
+    a.dh0 = dh0 ? dh0 : fp(l.dh0);
+    a.seqlen = seqlen;
+    a.batch = batch;
+    a.nheads = (int)nheads;
+    a.dim = (int)dim;
+    a.dstate = (int)dstate;
+    a.euler = discretization == SSM_DISC_EULER ? 1 : 0;
+    a.nchunks = l.nchunks;
+    a.ngroups = l.ngroups;
+    a.hbuf = fp(l.hbuf);
+    a.gbuf = fp(l.gbuf);
+    a.dlog = fp(l.dlog);
+    a.glog = fp(l.glog);
+    a.dd_part = fp(l.dd);
+    a.db_part = fp(l.db);
+    a.dc_part = fp(l.dc);
+    a.da_part = fp(l.da);
+    return hip_status(ssm::launch_ssd_bwd_mm(a, s));
   }
   int64_t chunk_len;
   int K;

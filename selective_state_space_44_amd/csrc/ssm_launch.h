@@ -199,6 +199,52 @@ struct SsdArgs {
 };
 size_t ssd_workspace_bytes(int64_t batch, int64_t dim, int64_t nheads, int64_t dstate,
                            int nseg);
+// The state-only pass over segments 0..nseg-2 (end state from zero into
+// ws_hloc, log2 decay into ws_dlog); nothing for nseg < 2.
+hipError_t launch_ssd_state_pass(const SsdArgs& a, int dstate, hipStream_t stream);
+
+// Backward of the per-head scan in its masked-matrix form, chunk-parallel
+// (64-channel heads, 64 or 128 states, bf16 I/O).  Workspace carved by
+// ssd_bwd_mm_layout.
+struct SsdBwdArgs {
+  const void* x;        // [batch, seqlen, dim] bf16
+  const void* dt;       // [batch, seqlen, nheads]
+  const float* A;       // [nheads]
+  const void* B;        // [batch, seqlen, dstate]
+  const void* C;
+  const float* Dskip;   // nullable
+  const void* z;        // nullable
+  const float* h0;      // nullable
+  const void* dy;       // [batch, seqlen, dim]
+  const float* dh_last; // nullable
+  void* dx;
+  void* ddt;            // [batch, seqlen, nheads]
+  float* dA;            // [nheads]
+  void* dB;
+  void* dC;
+  float* dD;            // nullable
+  void* dz;             // nullable (with z)
+  float* dh0;           // [batch, dim, dstate]: the output, or workspace scratch
+  int64_t seqlen;
+  int64_t batch;
+  int nheads;
+  int dim;
+  int dstate;
+  int euler;
+  int nchunks;          // ceil(seqlen / 32)
+  int ngroups;          // ceil(nheads / heads per block)
+  // workspace
+  float* hbuf;          // [batch, nchunks, dim, dstate]: state entering each chunk
+  float* gbuf;          // [batch, nchunks, dim, dstate]: adjoint leaving each chunk
+  float* dlog;          // [batch, nchunks, nheads]: log2 decay of each chunk (forward)
+  float* glog;          // [batch, nchunks, nheads]: the same, from the adjoint pass
+  float* dd_part;       // [batch, nchunks, dim]
+  float* db_part;       // [batch, seqlen, ngroups, dstate]
+  float* dc_part;       // [batch, seqlen, ngroups, dstate]
+  float* da_part;       // [batch, nchunks, nheads]
+};
+constexpr int kSsdBwdHeadsPerBlock = 8;
+hipError_t launch_ssd_bwd_mm(const SsdBwdArgs& a, hipStream_t stream);
 bool ssd_supported(int64_t headdim, int64_t dstate);
 size_t ssd_smem_bytes(int64_t dstate);
 hipError_t launch_ssd(const SsdArgs& a, int dstate, hipStream_t stream);

@@ -117,8 +117,10 @@ SSD_GRADS = ("dx", "ddt", "dz", "dA", "dB", "dC", "dD", "dh0")
 SSD_IO = ("dx", "ddt", "dz", "dB", "dC")
 
 
-def _ssd_bwd_case(n, dtype, disc, batch=2, seqlen=77, nheads=2, drop=()):
+def _ssd_bwd_case(n, dtype, disc, batch=2, seqlen=77, nheads=2, drop=(), zero_a_head=None):
     p = _inputs(n, batch=batch, seqlen=seqlen, nheads=nheads)
+    if zero_a_head is not None:
+        p["A"][zero_a_head] = 0.0
     if dtype == torch.float32:
         p = {k: (v.float() if k in ("x", "dt", "z", "B", "C") and v is not None else v)
              for k, v in p.items()}
@@ -159,6 +161,71 @@ def test_ssd_backward_optional_inputs_and_empty():
                     dy=torch.empty_like(p["x"]), dh_last=dhl)
     torch.cuda.synchronize()
     assert torch.count_nonzero(g["dA"]) == 0 and torch.equal(g["dh0"], dhl)
+
+
+@pytest.mark.parametrize("n,disc", [(64, "zoh"), (128, "euler"), (128, "zoh")])
+def test_ssd_backward_head_groups_ragged(n, disc):
+    """11 heads (the chunk kernel's groups of 8 heads, the second partial),
+    L = 100 (a ragged last chunk) and 33 (one step past a chunk), h0 and
+    dh_last, one head with A = 0 (the hold's delta*B limit)."""
+    for seqlen in (100, 33):
+        print(f"ssd bwd 11 heads N={n} {disc} L={seqlen}", flush=True)
+        _ssd_bwd_case(n, torch.bfloat16, disc, batch=2, seqlen=seqlen, nheads=11, zero_a_head=5)
+
+
+def test_ssd_backward_deterministic():
+    p = _inputs(128, batch=2, seqlen=300, nheads=9)
+    g = torch.Generator(device=DEV).manual_seed(7)
+    dy = torch.randn(p["x"].shape, generator=g, device=DEV).to(p["x"].dtype)
+    dhl = torch.randn(p["h0"].shape, generator=g, device=DEV)
+
+    def run():
+        out = ssm.ssd_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"],
+                          dy=dy, dh_last=dhl)
+        torch.cuda.synchronize()
+        return out
+    a, b = run(), run()
+    for k in SSD_GRADS:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_ssd_backward_full_shape_sampled_heads():
+    """Mamba-2-like layer at full size (batch 4, L 4096, 80 heads, 128
+    states): dy nonzero on three heads only, so every gradient of the other
+    heads is exactly zero and dB, dC are the three heads' sums; those are
+    checked against the oracle run on the three heads."""
+    w = W.SSD_2P7B
+    print(f"ssd bwd full shape {w.name}", flush=True)
+    p = W.make_ssd_inputs(w, device=DEV)
+    heads = [0, 41, 79]
+    hidx = torch.as_tensor(heads, device=DEV)
+    cidx = (hidx[:, None] * P + torch.arange(P, device=DEV)).reshape(-1)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    dy = torch.zeros_like(p["x"])
+    dy[:, :, cidx] = torch.randn(w.batch, w.seqlen, cidx.numel(), generator=g,
+                                 device=DEV).to(dy.dtype)
+    got = ssm.ssd_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["z"], None, dy=dy)
+    torch.cuda.synchronize()
+    others = torch.ones(w.dim // P, dtype=torch.bool, device=DEV)
+    others[hidx] = False
+    ocidx = others.repeat_interleave(P).nonzero().squeeze(1)
+    for k in ("dx", "dz"):
+        assert torch.count_nonzero(got[k].index_select(2, ocidx)) == 0, k
+    assert torch.count_nonzero(got["ddt"][:, :, others]) == 0
+    assert torch.count_nonzero(got["dA"][others]) == 0
+    f = parity.to_f64
+    sel = lambda t, dim, idx: None if t is None else t.index_select(dim, idx)
+    ref = oracle.scan_heads_bwd(f(sel(p["x"], 2, cidx)), f(sel(p["dt"], 2, hidx)),
+                                f(sel(p["A"], 0, hidx)), f(p["B"]), f(p["C"]),
+                                f(sel(p["D"], 0, cidx)), f(sel(p["z"], 2, cidx)), None,
+                                dy=f(sel(dy, 2, cidx)), headdim=P)
+    sub = {"dx": sel(got["dx"], 2, cidx), "dz": sel(got["dz"], 2, cidx),
+           "ddt": sel(got["ddt"], 2, hidx), "dA": sel(got["dA"], 0, hidx),
+           "dB": got["dB"], "dC": got["dC"], "dD": sel(got["dD"], 0, cidx),
+           "dh0": sel(got["dh0"], 1, cidx)}
+    for k in SSD_GRADS:
+        parity.check_grad(f(sub[k]), ref[k], torch.bfloat16 if k in SSD_IO else torch.float32,
+                          f"full shape {k}")
 
 
 # ---------------------------------------------------------------------------

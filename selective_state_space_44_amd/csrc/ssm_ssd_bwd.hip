@@ -26,8 +26,8 @@
 // kappa itself, so the split-bf16 products keep their relative accuracy.
 //
 // Passes (all chunks of 32 steps):
-//   A  the forward's state-only pass per chunk (end state from zero, log2
-//      decay), then an in-place carry: hbuf[c] = state entering chunk c;
+//   A  the forward's state-only walk over the sequence from h0, storing
+//      hbuf[c] = state entering chunk c;
 //   B  per chunk the adjoint it injects at its start, sum_i e^{s_i} C_i
 //      dpre_i^T, and its log2 decay, then an in-place reverse carry:
 //      gbuf[c] = adjoint leaving chunk c (from dh_last), and dh0;
@@ -62,12 +62,13 @@ constexpr int kThreads = 256;
 
 // Eight bf16 values of one LDS column (rows 0..7 from p, stride in elements)
 // as an MFMA operand: slot s = row s.
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ u32x4_t lds_col8(const uint16_t* p, int stride) {
-  uint32_t w[4];
+  // element-wise into a 16-bit vector: 16-bit loads into register halves
+  u16x8_t v;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    w[m] = (uint32_t)p[(2 * m) * stride] | ((uint32_t)p[(2 * m + 1) * stride] << 16);
-  return {w[0], w[1], w[2], w[3]};
+  for (int s = 0; s < 8; ++s) v[s] = p[s * stride];
+  return __builtin_bit_cast(u32x4_t, v);
 }
 
 // Eight fp32 values as bf16 high and low operands.
@@ -204,29 +205,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_gloc_kernel(SsdBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// carries, one thread per (batch row, channel, state), chunks in order
+// reverse carry, one thread per (batch row, channel, state), chunks from the
+// last: gbuf[c] <- adjoint leaving chunk c (in place of what chunk c injects
+// at its start), from dh_last; dh0 = what reaches the initial state
 // ---------------------------------------------------------------------------
-// hbuf[c] <- state entering chunk c (in place of chunk c's end state from zero)
-__global__ __launch_bounds__(256) void ssd_bwd_carry_fwd_kernel(SsdBwdArgs a) {
-  const int N = a.dstate, K = a.nchunks;
-  const int64_t per_b = (int64_t)a.dim * N;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= a.batch * per_b) return;
-  const int64_t b = i / per_b, dn = i % per_b;
-  const int h = (int)(dn / N) / kHD;
-  float v = a.h0 ? a.h0[i] : 0.0f;
-  for (int c = 0; c < K; ++c) {
-    const size_t row = (size_t)b * K + c;
-    float* slot = a.hbuf + row * per_b + dn;
-    const float loc = c + 1 < K ? *slot : 0.0f;
-    *slot = v;
-    if (c + 1 < K) v = __builtin_fmaf(fast_exp2(a.dlog[row * a.nheads + h]), v, loc);
-  }
-}
-
-// gbuf[c] <- adjoint leaving chunk c (in place of what chunk c injects at its
-// start), from dh_last; dh0 = what reaches the initial state
-__global__ __launch_bounds__(256) void ssd_bwd_carry_rev_kernel(SsdBwdArgs a) {
+__global__ __launch_bounds__(256) void ssd_bwd_carry_kernel(SsdBwdArgs a) {
   const int N = a.dstate, K = a.nchunks;
   const int64_t per_b = (int64_t)a.dim * N;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -284,8 +267,12 @@ struct ChunkSmem {
   alignas(16) float gam[4];                      // <g_out, h_in> per wave
 };
 
+// 8 waves: 0..3 own 16 channels each (ys, u, dx, dz, per-step sums), 4..7 a
+// quarter of the states each (dB, dC, accumulated over the group's heads).
+constexpr int kChunkThreads = 512;
+
 template <int N, bool HAS_Z, bool EULER>
-__global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
+__global__ __launch_bounds__(kChunkThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
   constexpr int NB = N / 8, NBV = NB / 8;
   constexpr int NTW = N / 64;  // 16-state tiles of dB, dC per wave
   extern __shared__ __align__(16) unsigned char ssd_bwd_smem_raw[];
@@ -303,12 +290,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // the (0, 1) block of every matrix is never written: zero it once
-  for (int k = tid; k < 4 * 2 * 16 * 8; k += kThreads) {
+  for (int k = tid; k < 4 * 2 * 16 * 8; k += kChunkThreads) {
     const int m = k >> 7, r = (k >> 3) & 15, cc = k & 7;
     *reinterpret_cast<uint32_t*>(&sm.mat[m >> 1][m & 1][r][16 + 2 * cc]) = 0u;
   }
-  // B and C of the chunk (shared by the group's heads)
-  {
+  // B and C of the chunk (shared by the group's heads), threads < 256
+  if (tid < kThreads) {
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
         static_cast<const uint16_t*>(a.B) + (b * L + t0) * N, (uint32_t)rows * N * 2u);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
@@ -358,8 +345,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
   for (int h = h_begin; h < h_end; ++h) {
     const float Ah = a.A[h];
     __syncthreads();  // every read of the previous head's staging is done
-    // ---- stage x, dy, z and dpre = dy SiLU(z) of head h ----------------
-    {
+    // ---- stage x, dy, z and dpre = dy SiLU(z) of head h (threads < 256)
+    if (tid < kThreads) {
       const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(h * kHD + 8 * cg) * 2u;
       const u32x4_t xw =
           __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsx, ox, 0, 0));
@@ -443,11 +430,14 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
     const float* hin = a.hbuf + sbase;
     const float* gout = a.gbuf + sbase;
 
+    if (w < 4) {
     // ---- ys and u for channels p = 16 w + r16 (result column p, rows t) --
     const int p = 16 * w + r16;
     f32x4_t ys[2] = {zero4, zero4}, us[2] = {zero4, zero4};
     float gam = 0.0f;  // <g_out, h_in> over this lane's (channel, states)
-#pragma unroll
+    // two state steps at a time: the loads of all N/32 in flight together
+    // would exceed the register budget of 8 waves
+#pragma unroll 2
     for (int k = 0; k < N / 32; ++k) {
       // the states of channel p, states 32k + 8g .. + 7, as B operands
       const f32x4_t h0v = *reinterpret_cast<const f32x4_t*>(hin + p * N + 32 * k + 8 * g);
@@ -565,14 +555,15 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
       if (lane == 0) sm.gam[w] = gam;
     }
 
+    } else {
     // ---- dB and dC of this wave's state tiles ---------------------------
 #pragma unroll
     for (int ti = 0; ti < NTW; ++ti) {
-      const int n = 16 * (NTW * w + ti) + r16;  // this lane's state (result column)
+      const int n = 16 * (NTW * (w - 4) + ti) + r16;  // this lane's state (result column)
       f32x4_t tb[2] = {zero4, zero4}, tc[2] = {zero4, zero4};
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        // g_out and h_in of state n, channels 32k + 8g .. + 7, as B operands
+            // g_out and h_in of state n, channels 32k + 8g .. + 7, as B operands
         float gv[8], hv[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -617,6 +608,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
           accc[r][ti][q] += tc[r][q];
         }
       }
+    }
     }
     __syncthreads();  // per-step sums of all waves are in place
     if (w == 0) {
@@ -664,10 +656,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
   }
 
   // dB, dC partial sums of the group
+  if (w < 4) return;
   const int G = a.ngroups;
 #pragma unroll
   for (int ti = 0; ti < NTW; ++ti) {
-    const int n = 16 * (NTW * w + ti) + r16;
+    const int n = 16 * (NTW * (w - 4) + ti) + r16;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -702,21 +695,33 @@ __global__ __launch_bounds__(256) void ssd_bwd_sum_groups_kernel(SsdBwdArgs a) {
   static_cast<uint16_t*>(a.dC)[i] = f32_to_bf16_bits(sc);
 }
 
-// dA and dD: sums over (batch row, chunk)
-__global__ __launch_bounds__(256) void ssd_bwd_sum_params_kernel(SsdBwdArgs a) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < a.nheads) {
-    const int64_t rows = a.batch * a.nchunks;
-    float s = 0.0f;
-    for (int64_t r = 0; r < rows; ++r) s += a.da_part[r * a.nheads + i];
-    a.dA[i] = s;
+// dD: sums over (batch row, chunk); a block takes 64 channels, its 4 waves
+// every 4th row, combined in a fixed order
+__global__ __launch_bounds__(256) void ssd_bwd_sum_dd_kernel(SsdBwdArgs a) {
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int d = blockIdx.x * 64 + lane;
+  const int64_t rows = a.batch * a.nchunks;
+  float s = 0.0f;
+  if (d < a.dim) {
+#pragma unroll 8
+    for (int64_t r = w; r < rows; r += 4) s += a.dd_part[r * a.dim + d];
   }
-  if (a.dD && i < a.dim) {
-    const int64_t rows = a.batch * a.nchunks;
-    float s = 0.0f;
-    for (int64_t r = 0; r < rows; ++r) s += a.dd_part[r * a.dim + i];
-    a.dD[i] = s;
-  }
+  part[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && d < a.dim) a.dD[d] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+}
+
+// dA: one wave per head, sums over (batch row, chunk)
+__global__ __launch_bounds__(64) void ssd_bwd_sum_da_kernel(SsdBwdArgs a) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  const int64_t rows = a.batch * a.nchunks;
+  float s = 0.0f;
+#pragma unroll 4
+  for (int64_t r = lane; r < rows; r += 64) s += a.da_part[r * a.nheads + h];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) a.dA[h] = s;
 }
 
 template <int N, bool HAS_Z, bool EULER>
@@ -727,9 +732,8 @@ hipError_t launch_chunk_passes(const SsdBwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nst = a.batch * (int64_t)a.dim * N;
-  const dim3 grid_carry((unsigned)((nst + 255) / 256));
-  hipLaunchKernelGGL(ssd_bwd_carry_fwd_kernel, grid_carry, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(ssd_bwd_carry_rev_kernel, grid_carry, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_carry_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0,
+                     stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto kern = ssd_bwd_chunk_kernel<N, HAS_Z, EULER>;
@@ -737,15 +741,16 @@ hipError_t launch_chunk_passes(const SsdBwdArgs& a, hipStream_t stream) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.ngroups, a.nchunks, (unsigned)a.batch), dim3(kThreads), smem,
-                     stream, a);
+  hipLaunchKernelGGL(kern, dim3(a.ngroups, a.nchunks, (unsigned)a.batch), dim3(kChunkThreads),
+                     smem, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = a.batch * a.seqlen * N;
   hipLaunchKernelGGL(ssd_bwd_sum_groups_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
                      stream, a);
-  const int np = a.dim > a.nheads ? a.dim : a.nheads;
-  hipLaunchKernelGGL(ssd_bwd_sum_params_kernel, dim3((np + 255) / 256), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_sum_da_kernel, dim3(a.nheads), dim3(64), 0, stream, a);
+  if (a.dD)
+    hipLaunchKernelGGL(ssd_bwd_sum_dd_kernel, dim3((a.dim + 63) / 64), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -760,7 +765,7 @@ hipError_t launch_chunk_passes_n(const SsdBwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_ssd_bwd_mm(const SsdBwdArgs& a, hipStream_t stream) {
-  // pass A: the forward's state-only pass with one 32-step segment per chunk
+  // pass A: the forward's state-only walk, storing every chunk's entering state
   SsdArgs f{};
   f.x = a.x;
   f.dt = a.dt;
@@ -772,11 +777,11 @@ hipError_t launch_ssd_bwd_mm(const SsdBwdArgs& a, hipStream_t stream) {
   f.nheads = a.nheads;
   f.dim = a.dim;
   f.euler = a.euler;
-  f.nseg = a.nchunks;
-  f.seg_len = kQ;
-  f.ws_hloc = a.hbuf;
-  f.ws_dlog = a.dlog;
-  hipError_t e = launch_ssd_state_pass(f, a.dstate, stream);
+  f.h0 = a.h0;
+  f.nseg = 1;
+  f.seg_len = a.seqlen;
+  f.ws_chunk_h = a.hbuf;
+  hipError_t e = launch_ssd_state_walk(f, a.dstate, stream);
   if (e != hipSuccess) return e;
   switch (a.dstate) {
     case 64: return launch_chunk_passes_n<64>(a, stream);

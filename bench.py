@@ -296,7 +296,7 @@ def bench_ssd(steps: int, warmup: int):
     torch.cuda.synchronize()
     rec_ms = e0.elapsed_time(e1) / rec_steps
 
-    # its backward (ssm_ssd_bwd: the recurrence's backward kernels, per-head sums)
+    # its backward (ssm_ssd_bwd: the masked-matrix backward, chunk-parallel)
     g = torch.Generator(device=dev).manual_seed(19)
     dy = torch.randn(f["x"].shape, generator=g, device=dev).to(f["x"].dtype)
     nws = ssm.load_library().ssm_ssd_bwd_workspace_bytes(w.batch, w.seqlen, heads, P, N,
@@ -343,7 +343,7 @@ def bench_ssd(steps: int, warmup: int):
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "recurrence_ms_per_step": rec_ms, "speedup_vs_recurrence": rec_ms / ms,
-            "backward_ms_per_step": bwd_ms,
+            "backward_ms_per_step": bwd_ms, "backward_time_vs_forward": bwd_ms / ms,
             "single_sequence_1x16384": single}
 
 

@@ -364,12 +364,27 @@ int64_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nhead
 
 /*
  * Backward of ssm_ssd_fwd (step and decay shared per head): the gradients of
- * a loss with respect to every input, given dy and dh_last.  It is the
- * backward of ssm_scan_bwd applied to the per-channel problem the per-head
- * one stands for (dt and A repeated over each head's channels, A per
- * channel), with the per-channel gradients of dt and A summed over each
- * head's channels (in fp32, in a fixed order).  It runs on the recurrence's
- * backward kernels, not on the matrix cores.
+ * a loss with respect to every input, given dy and dh_last -- the chain rule
+ * through the recurrence the forward computes (a parameter shared by a
+ * head's channels gets the sum of their gradients).  Two implementations,
+ * chosen by shape:
+ *   - bf16 I/O, headdim 64, dstate 64 or 128, at most 65535 32-step chunks:
+ *     the masked-matrix form on the matrix cores, every 32-step chunk
+ *     independent (ihouse article on Mamba-3, section on Mamba's evolution:
+ *     the scalar-decay SSM as masked matrix products).  A state-only walk
+ *     stores the state entering every chunk, a per-chunk pass and a reverse
+ *     carry the adjoint leaving every chunk, and one kernel per (group of 8
+ *     heads, chunk, batch row) forms all gradients of the chunk from them;
+ *     the gradient of each step's log-decay is assembled inside its chunk
+ *     from the chunk's masked matrices and its two boundary states (no
+ *     prefix over the sequence).  Workspace: two fp32 states per chunk,
+ *     2 * batch * ceil(seqlen / 32) * nheads * 64 * dstate * 4 bytes, plus
+ *     about batch * seqlen * dstate * 8 * ceil(nheads / 8) bytes of partial
+ *     sums (2.87 GB at batch 4, L 4096, 80 heads, 128 states).
+ *   - otherwise: ssm_scan_bwd's recurrence kernels on the per-channel
+ *     problem the per-head one stands for (dt and A repeated over each
+ *     head's channels), the per-channel gradients of dt and A summed over
+ *     each head's channels in fp32 in a fixed order.
  *   inputs      : as ssm_ssd_fwd (dt [batch, seqlen, nheads], A [nheads]).
  *   dy          : [batch, seqlen, nheads * headdim] io_dtype; dh_last as
  *                 h_last, NULL => 0.

@@ -449,7 +449,7 @@ bool ssd_bwd_mm(int io_dtype, int64_t headdim, int64_t dstate, int64_t seqlen) {
 }
 
 struct SsdBwdMmLayout {
-  size_t hbuf, gbuf, glog, dd, db, dc, da, dh0, total;
+  size_t hbuf, gbuf, dd, db, dc, da, dh0, total;
   int nchunks, ngroups;
 };
 SsdBwdMmLayout ssd_bwd_mm_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dim,
@@ -467,7 +467,6 @@ SsdBwdMmLayout ssd_bwd_mm_layout(int64_t batch, int64_t seqlen, int64_t nheads, 
   };
   l.hbuf = take((size_t)batch * K * dim * dstate * f);
   l.gbuf = take((size_t)batch * K * dim * dstate * f);
-  l.glog = take((size_t)batch * K * nheads * f);
   l.dd = take((size_t)batch * K * dim * f);
   l.db = take((size_t)batch * seqlen * l.ngroups * dstate * f);
   l.dc = take((size_t)batch * seqlen * l.ngroups * dstate * f);
@@ -790,7 +789,6 @@ int ssm_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, 
     a.ngroups = l.ngroups;
     a.hbuf = fp(l.hbuf);
     a.gbuf = fp(l.gbuf);
-    a.glog = fp(l.glog);
     a.dd_part = fp(l.dd);
     a.db_part = fp(l.db);
     a.dc_part = fp(l.dc);

@@ -238,7 +238,6 @@ struct SsdBwdArgs {
   // workspace
   float* hbuf;          // [batch, nchunks, dim, dstate]: state entering each chunk
   float* gbuf;          // [batch, nchunks, dim, dstate]: adjoint leaving each chunk
-  float* glog;          // [batch, nchunks, nheads]: log2 decay of each chunk
   float* dd_part;       // [batch, nchunks, dim]
   float* db_part;       // [batch, seqlen, ngroups, dstate]
   float* dc_part;       // [batch, seqlen, ngroups, dstate]

@@ -28,9 +28,8 @@
 // Passes (all chunks of 32 steps):
 //   A  the forward's state-only walk over the sequence from h0, storing
 //      hbuf[c] = state entering chunk c;
-//   B  per chunk the adjoint it injects at its start, sum_i e^{s_i} C_i
-//      dpre_i^T, and its log2 decay, then an in-place reverse carry:
-//      gbuf[c] = adjoint leaving chunk c (from dh_last), and dh0;
+//   B  the adjoint walk over the chunks from the last, from dh_last,
+//      storing gbuf[c] = adjoint leaving chunk c, and dh0;
 //   C  per (head group, chunk, batch row): the chunk's gradients from hbuf[c]
 //      and gbuf[c] (below): dx, dz, ddt, dA's and D's partial sums, dB and
 //      dC summed over the group's heads;
@@ -116,115 +115,128 @@ __device__ __forceinline__ float chunk_steps(const void* dt, int64_t b, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// pass B: the adjoint each chunk injects at its start, per (head, chunk, row)
+// pass B: the adjoint walk.  One block per (half head, batch row) walks the
+// chunks from the last; it holds the adjoint g (N states x 32 channels) in
+// MFMA accumulators, stores it as the adjoint leaving each chunk, then
+//   g <- exp(s_last) g + sum_i exp(s_i) C_i dpre_i^T
+// (the adjoint entering the chunk); the last one is dh0.  Waves as the
+// forward's: (channel tile pt, state half nh); the next chunk's inputs are
+// loaded while the current one is computed.
 // ---------------------------------------------------------------------------
+constexpr int kBC = 32;          // channels per block (half a head)
+constexpr int kRowX = kBC + 8;   // bf16 per staged row of 32 channels
+
 template <int N>
-struct GlocSmem {
+struct AdjSmem {
   alignas(16) uint16_t cs[kQ][N + 8];  // C, [t][n]
-  alignas(16) uint16_t eh[kQ][kRowP];  // ein_t dpre_t, high part, [t][p]
-  alignas(16) uint16_t el[kQ][kRowP];  // low part
+  alignas(16) uint16_t eh[kQ][kRowX];  // ein_t dpre_t, high part, [t][p]
+  alignas(16) uint16_t el[kQ][kRowX];  // low part
   alignas(16) float s2[kQ], coef[kQ], ein[kQ];
 };
 
 template <int N, bool HAS_Z, bool EULER>
-__global__ __launch_bounds__(kThreads) void ssd_bwd_gloc_kernel(SsdBwdArgs a) {
+__global__ __launch_bounds__(kThreads) void ssd_bwd_adjoint_walk_kernel(SsdBwdArgs a) {
   constexpr int NB = N / 8, NBV = NB / 8;
-  __shared__ GlocSmem<N> sm;
-  const int h = blockIdx.x, c = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  constexpr int NT2 = N / 32;  // 16-state tiles per wave
+  __shared__ AdjSmem<N> sm;
+  const int h = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int64_t b = blockIdx.y;
   const int H = a.nheads, dim = a.dim, K = a.nchunks;
-  const int64_t L = a.seqlen, t0 = (int64_t)c * kQ;
-  const int rows = (int)(L - t0 < kQ ? L - t0 : kQ);
+  const int64_t L = a.seqlen;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int ts = tid & (kQ - 1), cg = tid >> 5;
+  const int pt = w & 1, nh = w >> 1;
+  const int ts = tid & (kQ - 1), cg = tid >> 5;  // staging: step, column group
+  const int cb = h * kHD + kBC * half;           // first channel of the block
+  const int d = cb + 16 * pt + r16;              // this lane's channel (result column)
   const float Ah = a.A[h];
+  const size_t soff = (size_t)16 * nh * NT2 + 4 * g;  // this lane's first state
 
-  // stage C and this thread's dpre values (step ts, channels 8cg..8cg+7)
+  f32x4_t acc[NT2];
   {
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
-        static_cast<const uint16_t*>(a.C) + (b * L + t0) * N, (uint32_t)rows * N * 2u);
+    const float* src = a.dh_last ? a.dh_last + ((size_t)b * dim + d) * N + soff : nullptr;
+#pragma unroll
+    for (int j = 0; j < NT2; ++j)
+      acc[j] = src ? *reinterpret_cast<const f32x4_t*>(src + 16 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // staging registers of one chunk: C (states NB cg .. + NB - 1 of step ts),
+  // dy and z (channels 4cg .. 4cg + 3 of step ts)
+  u32x4_t cr[NBV];
+  u32x2_t dyr, zr = {0u, 0u};
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+    const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
+    const __amdgpu_buffer_rsrc_t rsc =
+        make_rsrc(static_cast<const uint16_t*>(a.C) + (b * L + t0) * N, rows * N * 2u);
     const uint32_t oc = (uint32_t)ts * N * 2u + (uint32_t)(NB * cg) * 2u;
 #pragma unroll
     for (int j = 0; j < NBV; ++j)
-      *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsc, oc + 16u * j, 0, 0));
-  }
-  float dp[8];
-  {
-    const uint32_t rb = (uint32_t)rows * (uint32_t)dim * 2u;
-    const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(h * kHD + 8 * cg) * 2u;
-    const u32x4_t dyw = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                     make_rsrc(static_cast<const uint16_t*>(a.dy) + (b * L + t0) * dim, rb), ox,
-                     0, 0));
-    u32x4_t zw = {0u, 0u, 0u, 0u};
+      cr[j] = __builtin_bit_cast(u32x4_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(rsc, oc + 16u * j, 0, 0));
+    const uint32_t rb = rows * (uint32_t)dim * 2u;
+    const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(cb + 4 * cg) * 2u;
+    dyr = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                     make_rsrc(static_cast<const uint16_t*>(a.dy) + (b * L + t0) * dim, rb), ox, 0,
+                     0));
     if constexpr (HAS_Z)
-      zw = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+      zr = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
                        make_rsrc(static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rb), ox,
                        0, 0));
+  };
+
+  fetch(K - 1);
+  for (int64_t c = K - 1; c >= 0; --c) {
+    const int64_t t0 = c * kQ;
+    const int rows = (int)(L - t0 < kQ ? L - t0 : kQ);
+    // the adjoint leaving chunk c
+    float* dst = a.gbuf + (((size_t)b * K + c) * dim + d) * N + soff;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float d0 = bf16_lo(dyw[m]), d1 = bf16_hi(dyw[m]);
-      dp[2 * m] = HAS_Z ? d0 * silu(bf16_lo(zw[m])) : d0;
-      dp[2 * m + 1] = HAS_Z ? d1 * silu(bf16_hi(zw[m])) : d1;
+    for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = acc[j];
+
+    __syncthreads();  // every read of the previous chunk's LDS is done
+#pragma unroll
+    for (int j = 0; j < NBV; ++j) *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = cr[j];
+    float dp[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float d0 = bf16_lo(dyr[m]), d1 = bf16_hi(dyr[m]);
+      dp[2 * m] = HAS_Z ? d0 * silu(bf16_lo(zr[m])) : d0;
+      dp[2 * m + 1] = HAS_Z ? d1 * silu(bf16_hi(zr[m])) : d1;
+    }
+    if (w == 3)
+      chunk_steps(a.dt, b, L, t0, rows, H, h, Ah, EULER || Ah == 0.0f, lane, sm.s2, sm.coef,
+                  sm.ein, nullptr);
+    __syncthreads();
+    if (c > 0) fetch(c - 1);
+    {
+      const float e = sm.ein[ts];
+      uint32_t hw0, lw0, hw1, lw1;
+      split_bf16(e * dp[0], e * dp[1], hw0, lw0);
+      split_bf16(e * dp[2], e * dp[3], hw1, lw1);
+      *reinterpret_cast<u32x2_t*>(&sm.eh[ts][4 * cg]) = u32x2_t{hw0, hw1};
+      *reinterpret_cast<u32x2_t*>(&sm.el[ts][4 * cg]) = u32x2_t{lw0, lw1};
+    }
+    __syncthreads();
+    // g[n][p] <- exp(s_last) g + sum_t C[t][n] (ein dpre)[t][p]: A operand
+    // row n, slots t; B operand column p, slots t
+    const float dec = fast_exp2(sm.s2[kQ - 1]);
+    const int p = 16 * pt + r16;
+    const u32x4_t eh = lds_col8(&sm.eh[8 * g][p], kRowX);
+    const u32x4_t el = lds_col8(&sm.el[8 * g][p], kRowX);
+#pragma unroll
+    for (int j = 0; j < NT2; ++j) {
+      const u32x4_t ca = lds_col8(&sm.cs[8 * g][16 * (nh * NT2 + j) + r16], N + 8);
+      acc[j] *= dec;
+      acc[j] = mfma_k32(ca, eh, acc[j]);
+      acc[j] = mfma_k32(ca, el, acc[j]);
     }
   }
-  if (w == 0) {
-    const float last = chunk_steps(a.dt, b, L, t0, rows, H, h, Ah, EULER || Ah == 0.0f, lane,
-                                   sm.s2, sm.coef, sm.ein, nullptr);
-    if (lane == 0) a.glog[((size_t)b * K + c) * H + h] = last;
-  }
-  __syncthreads();
-  {
-    const float e = sm.ein[ts];
-    float v[8];
+  float* d0 = a.dh0 + ((size_t)b * dim + d) * N + soff;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = e * dp[k];
-    u32x4_t hi, lo;
-    split8(v, hi, lo);
-    *reinterpret_cast<u32x4_t*>(&sm.eh[ts][8 * cg]) = hi;
-    *reinterpret_cast<u32x4_t*>(&sm.el[ts][8 * cg]) = lo;
-  }
-  __syncthreads();
-
-  // gloc[p][n] = sum_t C[t][n] (ein dpre)[t][p]: result column p (channel
-  // tile w), rows n; A operand row n, slots t; B operand column p, slots t
-  const int p = 16 * w + r16;
-  const u32x4_t eh = lds_col8(&sm.eh[8 * g][p], kRowP), el = lds_col8(&sm.el[8 * g][p], kRowP);
-  float* out = a.gbuf + (((size_t)b * K + c) * dim + h * kHD + p) * N;
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int nt = 0; nt < N / 16; ++nt) {
-    const u32x4_t ca = lds_col8(&sm.cs[8 * g][16 * nt + r16], N + 8);
-    f32x4_t acc = mfma_k32(ca, eh, zero4);
-    acc = mfma_k32(ca, el, acc);
-    *reinterpret_cast<f32x4_t*>(out + 16 * nt + 4 * g) = acc;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// reverse carry, one thread per (batch row, channel, state), chunks from the
-// last: gbuf[c] <- adjoint leaving chunk c (in place of what chunk c injects
-// at its start), from dh_last; dh0 = what reaches the initial state
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void ssd_bwd_carry_kernel(SsdBwdArgs a) {
-  const int N = a.dstate, K = a.nchunks;
-  const int64_t per_b = (int64_t)a.dim * N;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= a.batch * per_b) return;
-  const int64_t b = i / per_b, dn = i % per_b;
-  const int h = (int)(dn / N) / kHD;
-  float v = a.dh_last ? a.dh_last[i] : 0.0f;
-  for (int c = K - 1; c >= 0; --c) {
-    const size_t row = (size_t)b * K + c;
-    float* slot = a.gbuf + row * per_b + dn;
-    const float loc = *slot;
-    *slot = v;
-    v = __builtin_fmaf(fast_exp2(a.glog[row * a.nheads + h]), v, loc);
-  }
-  a.dh0[i] = v;
+  for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(d0 + 16 * j) = acc[j];
 }
 
 // dcoef/dA of the hold: dt^2 psi(u), u = dt A, psi(u) = (u e^u - e^u + 1)/u^2
@@ -726,15 +738,9 @@ __global__ __launch_bounds__(64) void ssd_bwd_sum_da_kernel(SsdBwdArgs a) {
 
 template <int N, bool HAS_Z, bool EULER>
 hipError_t launch_chunk_passes(const SsdBwdArgs& a, hipStream_t stream) {
-  const dim3 grid_bc(a.nheads, a.nchunks, (unsigned)a.batch);
-  hipLaunchKernelGGL((ssd_bwd_gloc_kernel<N, HAS_Z, EULER>), grid_bc, dim3(kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((ssd_bwd_adjoint_walk_kernel<N, HAS_Z, EULER>),
+                     dim3(2 * a.nheads, (unsigned)a.batch), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t nst = a.batch * (int64_t)a.dim * N;
-  hipLaunchKernelGGL(ssd_bwd_carry_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0,
-                     stream, a);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto kern = ssd_bwd_chunk_kernel<N, HAS_Z, EULER>;
   const size_t smem = sizeof(ChunkSmem<N>);

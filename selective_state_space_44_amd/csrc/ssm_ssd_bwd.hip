@@ -87,15 +87,18 @@ __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __ex
 // step `lane` (0 past the sequence), written to s2 (log2 decay from the
 // chunk's start through the step), coef, ein and eout.  Returns the chunk's
 // log2 decay (all lanes).
-__device__ __forceinline__ float chunk_steps(const void* dt, int64_t b, int64_t L, int64_t t0,
-                                             int rows, int H, int h, float Ah, bool coef_is_dt,
-                                             int lane, float* s2, float* coef, float* ein,
-                                             float* eout, float* dts = nullptr) {
+__device__ __forceinline__ uint32_t load_dt(const void* dt, int64_t b, int64_t L, int64_t t0,
+                                            int rows, int H, int h, int lane) {
   const __amdgpu_buffer_rsrc_t rsd =
       make_rsrc(static_cast<const uint16_t*>(dt) + (b * L + t0) * H, (uint32_t)rows * H * 2u);
-  const uint32_t raw =
-      lane < kQ ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)(lane * H + h) * 2u, 0, 0)
-                : 0u;
+  return lane < kQ ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)(lane * H + h) * 2u, 0, 0)
+                   : 0u;
+}
+
+// The same from dt bits already loaded (load_dt).
+__device__ __forceinline__ float chunk_steps_raw(uint32_t raw, float Ah, bool coef_is_dt,
+                                                 int lane, float* s2, float* coef, float* ein,
+                                                 float* eout, float* dts) {
   const float dtv = bf16_bits_to_f32(raw);
   float s = dtv * Ah * kLog2e;
 #pragma unroll
@@ -112,6 +115,14 @@ __device__ __forceinline__ float chunk_steps(const void* dt, int64_t b, int64_t 
     if (dts) dts[lane] = dtv;
   }
   return last;
+}
+
+__device__ __forceinline__ float chunk_steps(const void* dt, int64_t b, int64_t L, int64_t t0,
+                                             int rows, int H, int h, float Ah, bool coef_is_dt,
+                                             int lane, float* s2, float* coef, float* ein,
+                                             float* eout, float* dts = nullptr) {
+  return chunk_steps_raw(load_dt(dt, b, L, t0, rows, H, h, lane), Ah, coef_is_dt, lane, s2, coef,
+                         ein, eout, dts);
 }
 
 // ---------------------------------------------------------------------------
@@ -354,22 +365,28 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs
   const __amdgpu_buffer_rsrc_t rsdz =
       make_rsrc(static_cast<uint16_t*>(HAS_Z ? a.dz : a.dx) + (b * L + t0) * dim, rb);
 
+  // staging registers of waves 4..7: step ts, channels 8cg..8cg+7 of a head
+  const int tsx = tid & (kQ - 1), cgx = (tid >> 5) & 7;
+  u32x4_t xw = {0u, 0u, 0u, 0u}, dyw = xw, zw = xw;
+  auto fetch_head = [&](int hh) {
+    const uint32_t ox = (uint32_t)tsx * (uint32_t)dim * 2u + (uint32_t)(hh * kHD + 8 * cgx) * 2u;
+    xw = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsx, ox, 0, 0));
+    dyw = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsdy, ox, 0, 0));
+    if constexpr (HAS_Z)
+      zw = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsz, ox, 0, 0));
+  };
+  if (w >= 4) fetch_head(h_begin);
+  uint32_t dt_raw = w == 3 ? load_dt(a.dt, b, L, t0, rows, H, h_begin, lane) : 0u;
+
   for (int h = h_begin; h < h_end; ++h) {
     const float Ah = a.A[h];
     __syncthreads();  // every read of the previous head's staging is done
-    // ---- stage x, dy, z and dpre = dy SiLU(z) of head h (threads < 256)
-    if (tid < kThreads) {
-      const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(h * kHD + 8 * cg) * 2u;
-      const u32x4_t xw =
-          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsx, ox, 0, 0));
-      const u32x4_t dyw =
-          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsdy, ox, 0, 0));
-      u32x4_t zw = {0u, 0u, 0u, 0u};
-      if constexpr (HAS_Z)
-        zw = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsz, ox, 0, 0));
-      *reinterpret_cast<u32x4_t*>(&sm.xs[ts][8 * cg]) = xw;
-      *reinterpret_cast<u32x4_t*>(&sm.dys[ts][8 * cg]) = dyw;
-      *reinterpret_cast<u32x4_t*>(&sm.zs[ts][8 * cg]) = zw;
+    // ---- stage x, dy, z and dpre = dy SiLU(z) of head h (waves 4..7, from
+    // registers loaded during the previous head), then load head h + 1 ----
+    if (w >= 4) {
+      *reinterpret_cast<u32x4_t*>(&sm.xs[tsx][8 * cgx]) = xw;
+      *reinterpret_cast<u32x4_t*>(&sm.dys[tsx][8 * cgx]) = dyw;
+      *reinterpret_cast<u32x4_t*>(&sm.zs[tsx][8 * cgx]) = zw;
       float dp[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -379,12 +396,15 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs
       }
       u32x4_t hi, lo;
       split8(dp, hi, lo);
-      *reinterpret_cast<u32x4_t*>(&sm.dph[ts][8 * cg]) = hi;
-      *reinterpret_cast<u32x4_t*>(&sm.dpl[ts][8 * cg]) = lo;
+      *reinterpret_cast<u32x4_t*>(&sm.dph[tsx][8 * cgx]) = hi;
+      *reinterpret_cast<u32x4_t*>(&sm.dpl[tsx][8 * cgx]) = lo;
+      if (h + 1 < h_end) fetch_head(h + 1);
     }
-    if (w == 3)
-      chunk_steps(a.dt, b, L, t0, rows, H, h, Ah, EULER || Ah == 0.0f, lane, sm.s2, sm.coef,
-                  sm.ein, sm.eout, sm.dtv);
+    if (w == 3) {
+      chunk_steps_raw(dt_raw, Ah, EULER || Ah == 0.0f, lane, sm.s2, sm.coef, sm.ein, sm.eout,
+                      sm.dtv);
+      if (h + 1 < h_end) dt_raw = load_dt(a.dt, b, L, t0, rows, H, h + 1, lane);
+    }
     __syncthreads();
 
     // ---- G = dpre x^T and the masked matrices (waves 0..2) -------------

@@ -83,10 +83,8 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) { return bf16_bits_t
 
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __expf(-v)); }
 
-// Per-step values of one head's chunk, from lanes < 32 of one wave: dt of
-// step `lane` (0 past the sequence), written to s2 (log2 decay from the
-// chunk's start through the step), coef, ein and eout.  Returns the chunk's
-// log2 decay (all lanes).
+// bf16 bits of dt of step `lane` of a chunk for head h (0 past the sequence
+// and for lanes >= 32).
 __device__ __forceinline__ uint32_t load_dt(const void* dt, int64_t b, int64_t L, int64_t t0,
                                             int rows, int H, int h, int lane) {
   const __amdgpu_buffer_rsrc_t rsd =
@@ -95,7 +93,10 @@ __device__ __forceinline__ uint32_t load_dt(const void* dt, int64_t b, int64_t L
                    : 0u;
 }
 
-// The same from dt bits already loaded (load_dt).
+// Per-step values of one head's chunk, from lanes < 32 of one wave, given
+// the dt bits of step `lane` (load_dt): s2 (log2 decay from the chunk's start
+// through the step), coef, and where given ein, eout and dt itself.  Returns
+// the chunk's log2 decay (all lanes).
 __device__ __forceinline__ float chunk_steps_raw(uint32_t raw, float Ah, bool coef_is_dt,
                                                  int lane, float* s2, float* coef, float* ein,
                                                  float* eout, float* dts) {
@@ -117,6 +118,7 @@ __device__ __forceinline__ float chunk_steps_raw(uint32_t raw, float Ah, bool co
   return last;
 }
 
+// The same, loading dt.
 __device__ __forceinline__ float chunk_steps(const void* dt, int64_t b, int64_t L, int64_t t0,
                                              int rows, int H, int h, float Ah, bool coef_is_dt,
                                              int lane, float* s2, float* coef, float* ein,

@@ -177,6 +177,22 @@ def test_ssd_backward_rejects_bad_arguments(lib):
     assert lib.ssm_ssd_bwd_workspace_bytes(-1, 8, 2, 64, 64, 1) == -1
 
 
+def test_ssd_backward_workspace_by_path(lib):
+    """bf16 with 64-channel heads and 64 or 128 states takes the masked-matrix
+    backward: its workspace is the fp32 states entering and leaving every
+    32-step chunk plus partial sums (dB, dC per group of 8 heads; dD, dA per
+    chunk) and a dh0 scratch, each 256-byte aligned.  fp32 I/O and other
+    state sizes take the recurrence path (a different layout)."""
+    al = lambda v: (v + 255) // 256 * 256
+    for B, L, H, N in ((2, 100, 3, 128), (1, 64, 11, 64), (3, 1, 9, 128)):
+        K, G, dim = (L + 31) // 32, (H + 7) // 8, H * 64
+        want = (2 * al(B * K * dim * N * 4) + 2 * al(B * L * G * N * 4) + al(B * K * dim * 4)
+                + al(B * K * H * 4) + al(B * dim * N * 4))
+        assert lib.ssm_ssd_bwd_workspace_bytes(B, L, H, 64, N, 1) == want, (B, L, H, N)
+        assert lib.ssm_ssd_bwd_workspace_bytes(B, L, H, 64, N, 0) not in (want, 0, -1)
+    assert lib.ssm_ssd_bwd_workspace_bytes(2, 100, 3, 64, 32, 1) > 0   # recurrence path
+
+
 def test_ssd_rejects_bad_arguments(lib):
     """Every case fails validation (or is a no-op) before any launch."""
     def ssd(batch=2, L=8, H=2, P=64, N=128, io=1, disc=ssm.SSM_DISC_ZOH, x=FAKE, A=FAKE,

@@ -196,14 +196,9 @@ struct SsdArgs {
   float* ws_hloc;      // [batch, nseg, dim, dstate]
   float* ws_hin;       // [batch, nseg, dim, dstate] (segment 0 unused)
   float* ws_dlog;      // [batch, nseg, nheads]
-  // State walk (launch_ssd_state_walk): the state-only pass over the whole
-  // sequence from h0, storing the state entering every 32-step chunk.
-  float* ws_chunk_h;   // [batch, ceil(seqlen / 32), dim, dstate]
 };
 size_t ssd_workspace_bytes(int64_t batch, int64_t dim, int64_t nheads, int64_t dstate,
                            int nseg);
-// The state walk (one segment, a.ws_chunk_h set).
-hipError_t launch_ssd_state_walk(const SsdArgs& a, int dstate, hipStream_t stream);
 
 // Backward of the per-head scan in its masked-matrix form, chunk-parallel
 // (64-channel heads, 64 or 128 states, bf16 I/O).  Workspace carved by

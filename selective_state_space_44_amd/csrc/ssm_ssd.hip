@@ -101,9 +101,7 @@ struct SsdSmem {
 };
 
 // PRE: the state-only pass over segments 0..nseg-2 (no outputs): end state
-// from zero and the log2 of the segment's decay, into the workspace; or,
-// with ws_chunk_h set (one segment), the walk from h0 that stores the state
-// entering every chunk.
+// from zero and the log2 of the segment's decay, into the workspace.
 template <int N, bool HAS_Z, bool EULER, bool PRE>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void ssd_scan_kernel(SsdArgs a) {
@@ -154,8 +152,6 @@ void ssd_scan_kernel(SsdArgs a) {
   // state tile j: st[j][q] = h[n = 16 (nh NT2 + j) + 4 g + q][p]
   f32x4_t st[NT2];
   const float* src = nullptr;
-  float* const walk = PRE ? a.ws_chunk_h : nullptr;
-  if (walk && a.h0) src = a.h0 + ((size_t)b * dim + d) * N + soff;
   if (!PRE) {
     if (seg > 0)
       src = a.ws_hin + (seg_row * dim + d) * N + soff;
@@ -237,11 +233,6 @@ void ssd_scan_kernel(SsdArgs a) {
   auto chunk = [&](int64_t c, Stage& cur, const Stage& nxt) {
     const int64_t t0 = tb + c * kQ;
     const int buf = (int)(c & 1);
-    if (walk) {  // the state entering chunk c
-      float* dst = walk + (((size_t)b * ((L + kQ - 1) / kQ) + c) * dim + d) * N + soff;
-#pragma unroll
-      for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = st[j];
-    }
     __syncthreads();  // every read of the previous chunk's LDS is done
 
     // ---- stage the chunk in natural layout ----------------------------
@@ -409,9 +400,7 @@ void ssd_scan_kernel(SsdArgs a) {
   }
 
   float* dst = nullptr;
-  if (walk)
-    dst = nullptr;
-  else if (PRE)
+  if (PRE)
     dst = a.ws_hloc + (seg_row * dim + d) * N + soff;
   else if (a.h_last && seg == a.nseg - 1)
     dst = a.h_last + ((size_t)b * dim + d) * N + soff;
@@ -419,7 +408,7 @@ void ssd_scan_kernel(SsdArgs a) {
 #pragma unroll
     for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = st[j];
   }
-  if (PRE && !walk && half == 0 && tid == 0) a.ws_dlog[seg_row * H + h] = dlog;
+  if (PRE && half == 0 && tid == 0) a.ws_dlog[seg_row * H + h] = dlog;
 }
 
 // Entering state of each segment: h_in[s + 1] = exp2(dlog[s]) h_in[s] + hloc[s]
@@ -496,19 +485,6 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t dim, int64_t nheads, int64_t d
 
 size_t ssd_smem_bytes(int64_t dstate) {
   return dstate == 64 ? sizeof(SsdSmem<64>) : sizeof(SsdSmem<128>);
-}
-
-hipError_t launch_ssd_state_walk(const SsdArgs& a, int dstate, hipStream_t stream) {
-  if (!a.ws_chunk_h || a.nseg != 1) return hipErrorInvalidValue;
-  switch (dstate) {
-    case 64:
-      return a.euler ? launch_ssd_pass<64, false, true, true>(a, 1, stream)
-                     : launch_ssd_pass<64, false, false, true>(a, 1, stream);
-    case 128:
-      return a.euler ? launch_ssd_pass<128, false, true, true>(a, 1, stream)
-                     : launch_ssd_pass<128, false, false, true>(a, 1, stream);
-  }
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ssd(const SsdArgs& a, int dstate, hipStream_t stream) {

@@ -26,10 +26,9 @@
 // kappa itself, so the split-bf16 products keep their relative accuracy.
 //
 // Passes (all chunks of 32 steps):
-//   A  the forward's state-only walk over the sequence from h0, storing
-//      hbuf[c] = state entering chunk c;
-//   B  the adjoint walk over the chunks from the last, from dh_last,
-//      storing gbuf[c] = adjoint leaving chunk c, and dh0;
+//   A, B  two walks over the chunks in one launch: forward from h0, storing
+//      hbuf[c] = state entering chunk c; backward from dh_last, storing
+//      gbuf[c] = adjoint leaving chunk c, and dh0;
 //   C  per (head group, chunk, batch row): the chunk's gradients from hbuf[c]
 //      and gbuf[c] (below): dx, dz, ddt, dA's and D's partial sums, dB and
 //      dC summed over the group's heads;
@@ -128,33 +127,41 @@ __device__ __forceinline__ float chunk_steps(const void* dt, int64_t b, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// pass B: the adjoint walk.  One block per (half head, batch row) walks the
-// chunks from the last; it holds the adjoint g (N states x 32 channels) in
-// MFMA accumulators, stores it as the adjoint leaving each chunk, then
-//   g <- exp(s_last) g + sum_i exp(s_i) C_i dpre_i^T
-// (the adjoint entering the chunk); the last one is dh0.  Waves as the
-// forward's: (channel tile pt, state half nh); the next chunk's inputs are
+// passes A and B: the two walks, one launch.  Blocks [0, 2H) walk forward:
+// one per (half head, batch row), the state h (N states x 32 channels) in
+// MFMA accumulators from h0, stored as the state entering each chunk, then
+//   h <- exp(s_last) h + sum_t exp(s_last - s_t) coef_t B_t x_t^T.
+// Blocks [2H, 4H) walk backward from dh_last with the adjoint g, stored as
+// the adjoint leaving each chunk, then
+//   g <- exp(s_last) g + sum_t exp(s_t) C_t dpre_t^T,
+// and what reaches the start is dh0.  Both are chains of 32-step chunks
+// (latency-bound, 2H blocks per batch row each), so they run side by side.
+// Waves: (channel tile pt, state half nh); the next chunk's inputs are
 // loaded while the current one is computed.
 // ---------------------------------------------------------------------------
 constexpr int kBC = 32;          // channels per block (half a head)
 constexpr int kRowX = kBC + 8;   // bf16 per staged row of 32 channels
 
 template <int N>
-struct AdjSmem {
-  alignas(16) uint16_t cs[kQ][N + 8];  // C, [t][n]
-  alignas(16) uint16_t eh[kQ][kRowX];  // ein_t dpre_t, high part, [t][p]
+struct WalkSmem {
+  alignas(16) uint16_t ms[kQ][N + 8];  // B (forward) or C (backward), [t][n]
+  alignas(16) uint16_t eh[kQ][kRowX];  // weighted x or dpre, high part, [t][p]
   alignas(16) uint16_t el[kQ][kRowX];  // low part
-  alignas(16) float s2[kQ], coef[kQ], ein[kQ];
+  alignas(16) float s2[kQ], coef[kQ], ein[kQ], eout[kQ];
 };
 
 template <int N, bool HAS_Z, bool EULER>
-__global__ __launch_bounds__(kThreads) void ssd_bwd_adjoint_walk_kernel(SsdBwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+void ssd_bwd_walk_kernel(SsdBwdArgs a) {
   constexpr int NB = N / 8, NBV = NB / 8;
   constexpr int NT2 = N / 32;  // 16-state tiles per wave
-  __shared__ AdjSmem<N> sm;
-  const int h = blockIdx.x >> 1, half = blockIdx.x & 1;
+  __shared__ WalkSmem<N> sm;
+  const int H = a.nheads;
+  const bool fwd = (int)blockIdx.x < 2 * H;
+  const int bx = fwd ? (int)blockIdx.x : (int)blockIdx.x - 2 * H;
+  const int h = bx >> 1, half = bx & 1;
   const int64_t b = blockIdx.y;
-  const int H = a.nheads, dim = a.dim, K = a.nchunks;
+  const int dim = a.dim, K = a.nchunks;
   const int64_t L = a.seqlen;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
@@ -164,92 +171,101 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_adjoint_walk_kernel(SsdBwdAr
   const int d = cb + 16 * pt + r16;              // this lane's channel (result column)
   const float Ah = a.A[h];
   const size_t soff = (size_t)16 * nh * NT2 + 4 * g;  // this lane's first state
+  const void* mat_in = fwd ? a.B : a.C;
+  float* const out = fwd ? a.hbuf : a.gbuf;
 
   f32x4_t acc[NT2];
   {
-    const float* src = a.dh_last ? a.dh_last + ((size_t)b * dim + d) * N + soff : nullptr;
+    const float* init = fwd ? a.h0 : a.dh_last;
+    const float* src = init ? init + ((size_t)b * dim + d) * N + soff : nullptr;
 #pragma unroll
     for (int j = 0; j < NT2; ++j)
       acc[j] = src ? *reinterpret_cast<const f32x4_t*>(src + 16 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // staging registers of one chunk: C (states NB cg .. + NB - 1 of step ts),
-  // dy and z (channels 4cg .. 4cg + 3 of step ts)
-  u32x4_t cr[NBV];
-  u32x2_t dyr, zr = {0u, 0u};
+  // staging registers of one chunk: B or C (states NB cg .. + NB - 1 of step
+  // ts); x, or dy and z (channels 4cg .. 4cg + 3 of step ts)
+  u32x4_t mr[NBV];
+  u32x2_t vr, zr = {0u, 0u};
   auto fetch = [&](int64_t c) {
     const int64_t t0 = c * kQ;
     const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
-    const __amdgpu_buffer_rsrc_t rsc =
-        make_rsrc(static_cast<const uint16_t*>(a.C) + (b * L + t0) * N, rows * N * 2u);
-    const uint32_t oc = (uint32_t)ts * N * 2u + (uint32_t)(NB * cg) * 2u;
+    const __amdgpu_buffer_rsrc_t rsm =
+        make_rsrc(static_cast<const uint16_t*>(mat_in) + (b * L + t0) * N, rows * N * 2u);
+    const uint32_t om = (uint32_t)ts * N * 2u + (uint32_t)(NB * cg) * 2u;
 #pragma unroll
     for (int j = 0; j < NBV; ++j)
-      cr[j] = __builtin_bit_cast(u32x4_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(rsc, oc + 16u * j, 0, 0));
+      mr[j] = __builtin_bit_cast(u32x4_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(rsm, om + 16u * j, 0, 0));
     const uint32_t rb = rows * (uint32_t)dim * 2u;
     const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(cb + 4 * cg) * 2u;
-    dyr = __builtin_bit_cast(
+    vr = __builtin_bit_cast(
         u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
-                     make_rsrc(static_cast<const uint16_t*>(a.dy) + (b * L + t0) * dim, rb), ox, 0,
-                     0));
-    if constexpr (HAS_Z)
+                     make_rsrc(static_cast<const uint16_t*>(fwd ? a.x : a.dy) + (b * L + t0) * dim,
+                               rb),
+                     ox, 0, 0));
+    if (HAS_Z && !fwd)
       zr = __builtin_bit_cast(
           u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
                        make_rsrc(static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rb), ox,
                        0, 0));
   };
 
-  fetch(K - 1);
-  for (int64_t c = K - 1; c >= 0; --c) {
+  fetch(fwd ? 0 : K - 1);
+  for (int i = 0; i < K; ++i) {
+    const int64_t c = fwd ? i : K - 1 - i;
     const int64_t t0 = c * kQ;
     const int rows = (int)(L - t0 < kQ ? L - t0 : kQ);
-    // the adjoint leaving chunk c
-    float* dst = a.gbuf + (((size_t)b * K + c) * dim + d) * N + soff;
+    // the state entering chunk c (forward) or the adjoint leaving it
+    float* dst = out + (((size_t)b * K + c) * dim + d) * N + soff;
 #pragma unroll
     for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = acc[j];
 
     __syncthreads();  // every read of the previous chunk's LDS is done
 #pragma unroll
-    for (int j = 0; j < NBV; ++j) *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = cr[j];
-    float dp[4];
+    for (int j = 0; j < NBV; ++j) *reinterpret_cast<u32x4_t*>(&sm.ms[ts][NB * cg + 8 * j]) = mr[j];
+    float v[4];  // x, or dpre = dy SiLU(z)
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const float d0 = bf16_lo(dyr[m]), d1 = bf16_hi(dyr[m]);
-      dp[2 * m] = HAS_Z ? d0 * silu(bf16_lo(zr[m])) : d0;
-      dp[2 * m + 1] = HAS_Z ? d1 * silu(bf16_hi(zr[m])) : d1;
+      const float v0 = bf16_lo(vr[m]), v1 = bf16_hi(vr[m]);
+      const bool gate = HAS_Z && !fwd;
+      v[2 * m] = gate ? v0 * silu(bf16_lo(zr[m])) : v0;
+      v[2 * m + 1] = gate ? v1 * silu(bf16_hi(zr[m])) : v1;
     }
     if (w == 3)
       chunk_steps(a.dt, b, L, t0, rows, H, h, Ah, EULER || Ah == 0.0f, lane, sm.s2, sm.coef,
-                  sm.ein, nullptr);
+                  sm.ein, sm.eout);
     __syncthreads();
-    if (c > 0) fetch(c - 1);
+    if (i + 1 < K) fetch(fwd ? c + 1 : c - 1);
     {
-      const float e = sm.ein[ts];
+      // weight of step ts: exp(s_last - s_t) coef_t forward, exp(s_t) backward
+      const float e = fwd ? sm.eout[ts] * sm.coef[ts] : sm.ein[ts];
       uint32_t hw0, lw0, hw1, lw1;
-      split_bf16(e * dp[0], e * dp[1], hw0, lw0);
-      split_bf16(e * dp[2], e * dp[3], hw1, lw1);
+      split_bf16(e * v[0], e * v[1], hw0, lw0);
+      split_bf16(e * v[2], e * v[3], hw1, lw1);
       *reinterpret_cast<u32x2_t*>(&sm.eh[ts][4 * cg]) = u32x2_t{hw0, hw1};
       *reinterpret_cast<u32x2_t*>(&sm.el[ts][4 * cg]) = u32x2_t{lw0, lw1};
     }
     __syncthreads();
-    // g[n][p] <- exp(s_last) g + sum_t C[t][n] (ein dpre)[t][p]: A operand
-    // row n, slots t; B operand column p, slots t
+    // acc[n][p] <- exp(s_last) acc + sum_t M[t][n] (weighted v)[t][p]: A
+    // operand row n, slots t; B operand column p, slots t
     const float dec = fast_exp2(sm.s2[kQ - 1]);
     const int p = 16 * pt + r16;
     const u32x4_t eh = lds_col8(&sm.eh[8 * g][p], kRowX);
     const u32x4_t el = lds_col8(&sm.el[8 * g][p], kRowX);
 #pragma unroll
     for (int j = 0; j < NT2; ++j) {
-      const u32x4_t ca = lds_col8(&sm.cs[8 * g][16 * (nh * NT2 + j) + r16], N + 8);
+      const u32x4_t ma = lds_col8(&sm.ms[8 * g][16 * (nh * NT2 + j) + r16], N + 8);
       acc[j] *= dec;
-      acc[j] = mfma_k32(ca, eh, acc[j]);
-      acc[j] = mfma_k32(ca, el, acc[j]);
+      acc[j] = mfma_k32(ma, eh, acc[j]);
+      acc[j] = mfma_k32(ma, el, acc[j]);
     }
   }
-  float* d0 = a.dh0 + ((size_t)b * dim + d) * N + soff;
+  if (!fwd) {
+    float* d0 = a.dh0 + ((size_t)b * dim + d) * N + soff;
 #pragma unroll
-  for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(d0 + 16 * j) = acc[j];
+    for (int j = 0; j < NT2; ++j) *reinterpret_cast<f32x4_t*>(d0 + 16 * j) = acc[j];
+  }
 }
 
 // dcoef/dA of the hold: dt^2 psi(u), u = dt A, psi(u) = (u e^u - e^u + 1)/u^2
@@ -760,8 +776,8 @@ __global__ __launch_bounds__(64) void ssd_bwd_sum_da_kernel(SsdBwdArgs a) {
 
 template <int N, bool HAS_Z, bool EULER>
 hipError_t launch_chunk_passes(const SsdBwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((ssd_bwd_adjoint_walk_kernel<N, HAS_Z, EULER>),
-                     dim3(2 * a.nheads, (unsigned)a.batch), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((ssd_bwd_walk_kernel<N, HAS_Z, EULER>),
+                     dim3(4 * a.nheads, (unsigned)a.batch), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto kern = ssd_bwd_chunk_kernel<N, HAS_Z, EULER>;
@@ -793,24 +809,6 @@ hipError_t launch_chunk_passes_n(const SsdBwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_ssd_bwd_mm(const SsdBwdArgs& a, hipStream_t stream) {
-  // pass A: the forward's state-only walk, storing every chunk's entering state
-  SsdArgs f{};
-  f.x = a.x;
-  f.dt = a.dt;
-  f.A = a.A;
-  f.B = a.B;
-  f.C = a.C;
-  f.seqlen = a.seqlen;
-  f.batch = a.batch;
-  f.nheads = a.nheads;
-  f.dim = a.dim;
-  f.euler = a.euler;
-  f.h0 = a.h0;
-  f.nseg = 1;
-  f.seg_len = a.seqlen;
-  f.ws_chunk_h = a.hbuf;
-  hipError_t e = launch_ssd_state_walk(f, a.dstate, stream);
-  if (e != hipSuccess) return e;
   switch (a.dstate) {
     case 64: return launch_chunk_passes_n<64>(a, stream);
     case 128: return launch_chunk_passes_n<128>(a, stream);

@@ -173,6 +173,14 @@ def test_ssd_backward_head_groups_ragged(n, disc):
         _ssd_bwd_case(n, torch.bfloat16, disc, batch=2, seqlen=seqlen, nheads=11, zero_a_head=5)
 
 
+@pytest.mark.parametrize("seqlen", [1, 31, 32, 64])
+def test_ssd_backward_short_sequences(seqlen):
+    """One step, a partial chunk, exactly one and two chunks (the walks' first
+    and last chunk coincide or meet), with h0 and dh_last."""
+    print(f"ssd bwd L={seqlen}", flush=True)
+    _ssd_bwd_case(128, torch.bfloat16, "zoh", batch=2, seqlen=seqlen, nheads=3)
+
+
 def test_ssd_backward_deterministic():
     p = _inputs(128, batch=2, seqlen=300, nheads=9)
     g = torch.Generator(device=DEV).manual_seed(7)

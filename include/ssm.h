@@ -373,14 +373,14 @@ int64_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nhead
  *     independent (ihouse article on Mamba-3, section on Mamba's evolution:
  *     the scalar-decay SSM as masked matrix products).  A state-only walk
  *     stores the state entering every chunk, a per-chunk pass and a reverse
- *     carry the adjoint leaving every chunk, and one kernel per (group of 8
+ *     carry the adjoint leaving every chunk, and one kernel per (group of 16
  *     heads, chunk, batch row) forms all gradients of the chunk from them;
  *     the gradient of each step's log-decay is assembled inside its chunk
  *     from the chunk's masked matrices and its two boundary states (no
  *     prefix over the sequence).  Workspace: two fp32 states per chunk,
  *     2 * batch * ceil(seqlen / 32) * nheads * 64 * dstate * 4 bytes, plus
- *     about batch * seqlen * dstate * 8 * ceil(nheads / 8) bytes of partial
- *     sums (2.87 GB at batch 4, L 4096, 80 heads, 128 states).
+ *     about batch * seqlen * dstate * 8 * ceil(nheads / 16) bytes of partial
+ *     sums (2.79 GB at batch 4, L 4096, 80 heads, 128 states).
  *   - otherwise: ssm_scan_bwd's recurrence kernels on the per-channel
  *     problem the per-head one stands for (dt and A repeated over each
  *     head's channels), the per-channel gradients of dt and A summed over

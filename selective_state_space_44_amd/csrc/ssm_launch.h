@@ -238,7 +238,7 @@ struct SsdBwdArgs {
   float* dc_part;       // [batch, seqlen, ngroups, dstate]
   float* da_part;       // [batch, nchunks, nheads]
 };
-constexpr int kSsdBwdHeadsPerBlock = 8;
+constexpr int kSsdBwdHeadsPerBlock = 16;
 hipError_t launch_ssd_bwd_mm(const SsdBwdArgs& a, hipStream_t stream);
 bool ssd_supported(int64_t headdim, int64_t dstate);
 size_t ssd_smem_bytes(int64_t dstate);

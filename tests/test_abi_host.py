@@ -180,12 +180,12 @@ def test_ssd_backward_rejects_bad_arguments(lib):
 def test_ssd_backward_workspace_by_path(lib):
     """bf16 with 64-channel heads and 64 or 128 states takes the masked-matrix
     backward: its workspace is the fp32 states entering and leaving every
-    32-step chunk plus partial sums (dB, dC per group of 8 heads; dD, dA per
+    32-step chunk plus partial sums (dB, dC per group of 16 heads; dD, dA per
     chunk) and a dh0 scratch, each 256-byte aligned.  fp32 I/O and other
     state sizes take the recurrence path (a different layout)."""
     al = lambda v: (v + 255) // 256 * 256
-    for B, L, H, N in ((2, 100, 3, 128), (1, 64, 11, 64), (3, 1, 9, 128)):
-        K, G, dim = (L + 31) // 32, (H + 7) // 8, H * 64
+    for B, L, H, N in ((2, 100, 3, 128), (1, 64, 19, 64), (3, 1, 17, 128)):
+        K, G, dim = (L + 31) // 32, (H + 15) // 16, H * 64
         want = (2 * al(B * K * dim * N * 4) + 2 * al(B * L * G * N * 4) + al(B * K * dim * 4)
                 + al(B * K * H * 4) + al(B * dim * N * 4))
         assert lib.ssm_ssd_bwd_workspace_bytes(B, L, H, 64, N, 1) == want, (B, L, H, N)

@@ -165,12 +165,12 @@ def test_ssd_backward_optional_inputs_and_empty():
 
 @pytest.mark.parametrize("n,disc", [(64, "zoh"), (128, "euler"), (128, "zoh")])
 def test_ssd_backward_head_groups_ragged(n, disc):
-    """11 heads (the chunk kernel's groups of 8 heads, the second partial),
+    """19 heads (the chunk kernel's groups of 16 heads, the second partial),
     L = 100 (a ragged last chunk) and 33 (one step past a chunk), h0 and
     dh_last, one head with A = 0 (the hold's delta*B limit)."""
     for seqlen in (100, 33):
-        print(f"ssd bwd 11 heads N={n} {disc} L={seqlen}", flush=True)
-        _ssd_bwd_case(n, torch.bfloat16, disc, batch=2, seqlen=seqlen, nheads=11, zero_a_head=5)
+        print(f"ssd bwd 19 heads N={n} {disc} L={seqlen}", flush=True)
+        _ssd_bwd_case(n, torch.bfloat16, disc, batch=2, seqlen=seqlen, nheads=19, zero_a_head=5)
 
 
 @pytest.mark.parametrize("seqlen", [1, 31, 32, 64])

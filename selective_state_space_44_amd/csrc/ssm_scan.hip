@@ -820,8 +820,6 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
                                             const LanePrologue& lp) {
   constexpr int NPL = kDState / G;
   const int lane = k.lane, n0 = k.g * NPL;
-  const uint32_t voff = (uint32_t)k.d * sizeof(IO);
-  const uint32_t row_bytes = (uint32_t)dim * sizeof(IO);
   const int nsteps = (int)(k.t_end - k.t_begin);
   const int nfull = nsteps / kT;
 

@@ -39,16 +39,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_mamba2p8b_b4_l4096_d512
 
 
 def source_hash() -> str:
-    """Hash of the library sources with // comments and blank lines removed
-    (a comment edit does not change a kernel; any code edit does)."""
+    """Hash of the library sources with /* */ and // comments and blank lines
+    removed (a comment edit does not change a kernel; any code edit does)."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "selective_state_space_44_amd", "csrc", "*")))
     for f in files + [os.path.join(ROOT, "include", "ssm.h")]:
         with open(f, encoding="utf-8") as fh:
-            for line in fh:
-                code = re.sub(r"//.*", "", line).rstrip()
-                if code:
-                    h.update(code.encode() + b"\n")
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = re.sub(r"//.*", "", line).rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

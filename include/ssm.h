@@ -19,7 +19,8 @@
  *     multiplied by SiLU of the z branch.
  * Also: the scan's variants (A per channel, Euler rule), its fused prologue
  * (causal conv1d, softplus of delta), its backward (all input gradients) and
- * its masked-matrix form for a step and decay shared per head (ssm_ssd_fwd).
+ * its masked-matrix form for a step and decay shared per head, forward and
+ * backward (ssm_ssd_fwd, ssm_ssd_bwd).
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers to contiguous row-major memory,
@@ -35,8 +36,9 @@
  *     returns SSM_ERR_UNSUPPORTED instead of running a slow path.
  *   - io_dtype selects the type of x, delta, z, B, C and y (all the same).
  *     A, D and every state tensor are always fp32; arithmetic is fp32.
- *   - dstate: 16 everywhere; 32, 64 and 128 for the forward scan (not fused)
- *     and the decode step; other values return SSM_ERR_UNSUPPORTED.
+ *   - dstate: 16 everywhere; 32, 64 and 128 also for the forward scan (not
+ *     fused), the decode step and the backward; 64 or 128 for the
+ *     masked-matrix forward; other values return SSM_ERR_UNSUPPORTED.
  *   - NaN/Inf in inputs propagate by IEEE rules; nothing is checked on device.
  */
 #ifndef SSM_H_

@@ -202,6 +202,22 @@ def test_ssd_backward_paths_agree():
                           f"masked-matrix vs recurrence {k}")
 
 
+def test_ssd_backward_random_shapes():
+    """Eight seeded draws of batch (1-3), length (1-300), heads (1-20: one
+    or two head groups), 64 or 128 states, the rule, and which of z, D, h0,
+    dh_last are given; every gradient against the oracle."""
+    rng = np.random.default_rng(2024)
+    for case in range(8):
+        n = int(rng.choice([64, 128]))
+        disc = str(rng.choice(["zoh", "euler"]))
+        batch, seqlen, nheads = int(rng.integers(1, 4)), int(rng.integers(1, 301)), int(rng.integers(1, 21))
+        drop = tuple(k for k in ("z", "D", "h0", "dh_last") if rng.random() < 0.3)
+        print(f"ssd bwd random case {case}: N={n} {disc} b={batch} L={seqlen} H={nheads} "
+              f"without {drop}", flush=True)
+        _ssd_bwd_case(n, torch.bfloat16, disc, batch=batch, seqlen=seqlen, nheads=nheads,
+                      drop=drop)
+
+
 def test_ssd_backward_deterministic():
     p = _inputs(128, batch=2, seqlen=300, nheads=9)
     g = torch.Generator(device=DEV).manual_seed(7)

@@ -1,5 +1,6 @@
 """GPU parity of the scan with step and decay shared per head (masked-matrix
-form on the matrix cores, ``ssm_ssd_fwd``) against the oracle's recurrence."""
+form on the matrix cores: ``ssm_ssd_fwd`` and its backward ``ssm_ssd_bwd``)
+against the oracle's recurrence and its fp64 backward."""
 import numpy as np
 import pytest
 import torch

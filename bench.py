@@ -3,13 +3,21 @@
 
 One step = one forward scan of the Mamba-2.8B layer shape
 (batch 4, L 4096, D 5120, N 16; bf16 x/delta/z/B/C/y, fp32 A/D and state)
-on seeded synthetic inputs already resident in HBM.  Prints one JSON line
-with whole-job throughput in B*L*D*N elements/s, the roofline of the
-dominant kernel (the main scan pass), the HBM view, the recurrent decode
-sweep (256 sequences x 64 layers of D 5120, N 16) and the fp64 CPU
-baseline timed on a bounded sample on this host.
+on seeded synthetic inputs already resident in HBM: both launches of the
+chunked scan (chunk 0's main pass beside the pre-pass of the middle chunks,
+the composition of the chunk maps, the main pass of the other chunks).
+Prints one JSON line with whole-job throughput in B*L*D*N elements/s, the
+roofline of the dominant kernel (the main pass), the other scan
+configurations (tiny fp32, Mamba-130M layer, the 262144-step single
+sequence), the recurrent decode sweep (256 sequences x 64 layers of D 5120,
+N 16), the NEXT-row paths and the fp64 CPU oracle timed on a bounded sample
+on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+The GPU's clock rises over the first ~30 ms of sustained work; an untimed
+clock ramp (``--ramp-seconds``, default 0.5 s of the same step) runs before
+the warm-up steps and is reported in the line (``clock_ramp``).
 """
 from __future__ import annotations
 
@@ -17,6 +25,7 @@ import argparse
 import glob
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -27,13 +36,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
-# ALU roofline of the scan element: per element (b, t, d, n) the main pass
-# issues 6 fp32 VALU ops + 1 transcendental (exp2).  Per SIMD per clock: 32 fp32
-# lanes (157.3 TFLOP/s fp32 vector = 256 CU x 4 SIMD x 32 lanes x 2 x 2.4 GHz)
-# and a quarter of that for transcendentals.
+# ALU roofline of the scan element.  Per element (b, t, d, n) the main pass
+# must issue 6 fp32 VALU operations (delta*A, B*x, *1/A, the input-term fma,
+# the update fma, the readout fma) and one transcendental (exp2).  Unit
+# counts: 256 CUs x 4 SIMDs at 2.4 GHz; the published fp32 vector peak
+# 157.3 TFLOP/s = 1024 SIMDs x 2.4 GHz x 32 lanes x 2 (FMA), i.e. 32 fp32
+# lanes per SIMD per clock (two 16-lane VALU issues per clock: the SQ counts
+# dual-issue cycles, SQ_ACTIVE_INST_VALU2); transcendentals at a quarter of
+# that rate.
 ALU_OPS_PER_ELEMENT = 7
 SIMDS, CLOCK_HZ, VALU_LANES, TRANS_LANES = 256 * 4, 2.4e9, 32, 8
 ALU_PEAK_ELEMS = SIMDS * CLOCK_HZ / (6 / VALU_LANES + 1 / TRANS_LANES)
+TILE_STEPS = 16  # chunks of the chunked scan start on a multiple of this many steps
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_mamba2p8b_b4_l4096_d5120_traffic.md")
 
@@ -69,22 +83,38 @@ def load_traffic():
     return int(b.group(1))
 
 
-def cpu_threads() -> int:
+def host_cpus():
+    """CPUs this job may use: OMP_NUM_THREADS when the host sets it (a GPU
+    box allots a share of its cores per GPU this way), else the affinity
+    mask; plus what the machine shows and its model name."""
     try:
-        n = len(os.sched_getaffinity(0))
+        visible = len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        visible = os.cpu_count() or 1
+    allotted = visible
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        allotted = min(visible, int(env))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return allotted, visible, model
 
 
 def cpu_baseline(inp, w, target_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
     the first ``nb`` batch rows, the first ``nch`` channels of each, over the
-    full sequence."""
+    full sequence, on every CPU the job is allotted."""
     import torch
     import oracle
 
-    nthreads = cpu_threads()
+    nthreads, visible, model = host_cpus()
 
     def take(nb, nch):
         idx = torch.arange(nch, device=inp["x"].device)
@@ -111,9 +141,10 @@ def cpu_baseline(inp, w, target_s: float):
     dt = run(nb, nch)
     elems = nb * w.seqlen * nch * w.dstate
     return {"value": elems / dt, "unit": "elements/s", "cores": nthreads, "kind": "oracle",
+            "cpus_visible": visible, "cpu_model": model,
             "sample": f"{nb} of {w.batch} batch rows x {nch} of {w.dim} channels, full "
                       f"L={w.seqlen}, N={w.dstate}: {elems:.3e} elements in {dt:.1f} s "
-                      f"(fp64 C loop, gcc -O2, OpenMP over channels)"}
+                      f"(fp64 C loop, gcc -O2, OpenMP over channels, {nthreads} threads)"}
 
 
 def percentiles(ms):
@@ -123,7 +154,35 @@ def percentiles(ms):
     return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
-def bench_scan(steps: int, warmup: int):
+def chunk_rows(seqlen: int, nchunks: int) -> int:
+    """Steps of each chunk (the last may be shorter) of a K-chunk plan."""
+    if nchunks <= 1:
+        return seqlen
+    per = -(-seqlen // nchunks)
+    return -(-per // TILE_STEPS) * TILE_STEPS
+
+
+def scan_bytes(w, rows: int) -> int:
+    """Algorithmic bytes of a scan over `rows` steps of every batch row of w:
+    x, delta, z in and y out, B and C in, A and D once."""
+    return (w.batch * rows * (4 * w.dim + 2 * w.dstate) * w.io_bytes
+            + 4 * w.dim * w.dstate + 4 * w.dim)
+
+
+def clock_ramp(step, seconds: float) -> int:
+    """Untimed steps until `seconds` of wall time have passed (synchronising
+    every few steps, so the GPU is busy throughout)."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def bench_scan(steps: int, warmup: int, ramp_s: float):
     import torch
     import selective_state_space_44_amd as ssm
     from selective_state_space_44_amd import workloads as W
@@ -151,22 +210,73 @@ def bench_scan(steps: int, warmup: int):
         if ev is not None:
             ev[2].record()
 
+    ramp_steps = clock_ramp(step, ramp_s) if ramp_s > 0 else 0
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t_all = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_all[0].record()
     for i in range(steps):
         step(i, evs[i])
+    t_all[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_step = [e[0].elapsed_time(e[2]) for e in evs]
     ev_main = [e[1].elapsed_time(e[2]) for e in evs]
-    ev_carry = [e[0].elapsed_time(e[1]) for e in evs]
-    return dict(w=w, G=G, K=K, wall_s=wall, step_ms=sum(ev_step) / steps,
-                main_ms=sum(ev_main) / steps, carry_ms=sum(ev_carry) / steps, inp=sets[0],
-                step_pct=percentiles(ev_step), main_pct=percentiles(ev_main))
+    ev_first = [e[0].elapsed_time(e[1]) for e in evs]
+    return dict(w=w, G=G, K=K, wall_s=wall, step_ms=t_all[0].elapsed_time(t_all[1]) / steps,
+                main_ms=sum(ev_main) / steps, first_ms=sum(ev_first) / steps, inp=sets[0],
+                step_pct=percentiles(ev_step), main_pct=percentiles(ev_main),
+                ramp_steps=ramp_steps)
+
+
+def bench_config(w, sets_n: int, steps: int, warmup: int):
+    """One scan configuration in its automatic plan: per-step times over
+    `sets_n` rotated input sets (so that no step reads what an earlier one
+    left in the 256 MB Infinity Cache)."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    dev = "cuda:0"
+    sets = [W.make_inputs(w, device=dev, layer=i) for i in range(sets_n)]
+    outs = [torch.empty_like(s["x"]) for s in sets]
+    G, K = ssm.scan_plan(w.batch, w.seqlen, w.dim, dtype=w.io_dtype)
+    nws = ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim, dtype=w.io_dtype, nchunks=K)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % sets_n]
+        ssm.scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], None,
+                     waves_per_group=G, nchunks=K, out=outs[i % sets_n], workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    mean = sum(ms) / len(ms)
+    nbytes = w.algorithmic_bytes()
+    res = {"batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+           "io_dtype": "f32" if w.io_dtype == torch.float32 else "bf16",
+           "plan": {"waves_per_group": G, "nchunks": K}, "steps": steps,
+           "input_sets": sets_n, "rotated_bytes": nbytes * sets_n,
+           "ms_per_step": mean, "ms_percentiles": percentiles(ms),
+           "value": w.elements / (mean * 1e-3), "unit": "elements/s",
+           "hbm": {"algorithmic_bytes": nbytes, "achieved": nbytes / (mean * 1e-3) / 1e9,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    del sets, outs, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_fused(steps: int, warmup: int):
@@ -296,6 +406,7 @@ def bench_ssd(steps: int, warmup: int):
     e1.record()
     torch.cuda.synchronize()
     rec_ms = e0.elapsed_time(e1) / rec_steps
+    del delta, a_ch, y2
 
     # its backward (ssm_ssd_bwd: the masked-matrix backward, chunk-parallel)
     g = torch.Generator(device=dev).manual_seed(19)
@@ -334,7 +445,8 @@ def bench_ssd(steps: int, warmup: int):
         e1.record()
         torch.cuda.synchronize()
         single[tag + "_ms"] = e0.elapsed_time(e1) / rec_steps
-    del q, yq
+    del q, yq, sets, outs
+    torch.cuda.empty_cache()
     return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
             "unit": "elements/s",
             "mfma": {"algorithmic_flop": flops, "achieved": flops / (ms * 1e-3) / 1e12,
@@ -378,6 +490,8 @@ def bench_backward(steps: int, warmup: int):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    del sets, dys, ws
+    torch.cuda.empty_cache()
     return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
             "unit": "elements/s", "workspace_bytes": nws}
 
@@ -418,6 +532,8 @@ def bench_decode(sweeps: int):
     per_layer_bytes = w.algorithmic_bytes()
     elems = w.elements * w.layers
     gbs = per_layer_bytes / (kern_ms * 1e-3) / 1e9
+    del layers, ys
+    torch.cuda.empty_cache()
     return {
         "workload": w.name,
         "value": elems / (sweep_ms * 1e-3), "unit": "elements/s",
@@ -433,11 +549,15 @@ def bench_decode(sweeps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ramp-seconds", type=float, default=0.5,
+                    help="untimed clock ramp before the warm-up steps (0 = none)")
     ap.add_argument("--decode-sweeps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other scan configurations (tiny, Mamba-130M, long context)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward of the scan")
@@ -447,6 +567,8 @@ def main():
                     help="skip the scan with the fused conv1d/softplus prologue")
     ap.add_argument("--no-ssd", action="store_true",
                     help="skip the masked-matrix scan with step and decay per head")
+    ap.add_argument("--only-scan", action="store_true",
+                    help="the headline scan only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -455,6 +577,10 @@ def main():
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "channels are independent, so a multi-GPU run would split D with no exchange", file=sys.stderr)
         sys.exit(2)
+    if args.only_scan:
+        args.no_configs = args.no_decode = args.no_backward = True
+        args.no_variants = args.no_fused = args.no_ssd = True
+        args.cpu_seconds = 0
 
     import torch
     if not torch.cuda.is_available():
@@ -470,12 +596,17 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": COPY_BYTES}), flush=True)
         return
 
-    r = bench_scan(args.steps, args.warmup)
+    r = bench_scan(args.steps, args.warmup, args.ramp_seconds)
     w = r["w"]
     elems = w.elements
     value = elems / (r["step_ms"] * 1e-3)
-    main_elems = elems / (r["main_ms"] * 1e-3)
     alg_bytes = w.algorithmic_bytes()
+    # the main-pass launch covers chunks 1 .. K-1 (chunk 0 runs in the first launch)
+    rows0 = chunk_rows(w.seqlen, r["K"]) if r["K"] > 1 else 0
+    main_rows = w.seqlen - rows0
+    main_elems = w.batch * main_rows * w.dim * w.dstate
+    main_bytes = scan_bytes(w, main_rows)
+    main_s = r["main_ms"] * 1e-3
     traffic = load_traffic()
     line = {
         "metric": "selective-scan B·L·D·N elems/s + % peak HBM GB/s, Mamba-2.8B layer shape",
@@ -488,20 +619,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": "bf16", "state_dtype": "f32",
-                   "plan": {"waves_per_group": r["G"], "nchunks": r["K"]}},
+                   "compute_dtype": "f32",
+                   "plan": {"waves_per_group": r["G"], "nchunks": r["K"],
+                            "schedule": "two-launch"}},
         "roofline": {
             "bound": "alu",
-            "kernel": "scan_fwd_kernel (main pass)",
-            "achieved": ALU_OPS_PER_ELEMENT * main_elems / 1e12,
+            "kernel": "scan_fwd_kernel (main pass, chunks 1..K-1)",
+            "achieved": ALU_OPS_PER_ELEMENT * main_elems / main_s / 1e12,
             "peak": ALU_OPS_PER_ELEMENT * ALU_PEAK_ELEMS / 1e12,
             "unit": "TOP/s",
-            "frac": main_elems / ALU_PEAK_ELEMS,
+            "frac": main_elems / main_s / ALU_PEAK_ELEMS,
             "traffic": traffic,
             "launch_ms": r["main_ms"],
+            "elements_per_launch": main_elems,
+            "hbm": {"algorithmic_bytes_per_launch": main_bytes,
+                    "achieved": main_bytes / main_s / 1e9, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": main_bytes / main_s / 1e9 / HBM_PEAK_GBS,
+                    "traffic_frac": (traffic / main_s / 1e9 / HBM_PEAK_GBS) if traffic else None},
         },
         "hbm": {
             "algorithmic_bytes": alg_bytes,
@@ -512,23 +650,37 @@ def main():
         },
         "step_ms_percentiles": r["step_pct"],
         "main_pass_ms_percentiles": r["main_pct"],
-        "carry_ms_per_step": r["carry_ms"],
+        "first_launch_ms_per_step": r["first_ms"],
+        "clock_ramp": {"seconds": args.ramp_seconds, "steps": r["ramp_steps"],
+                       "why": "untimed steps before the warm-up: the clock rises over "
+                              "the first ~30 ms of sustained work"},
         "wall_s_timed": r["wall_s"],
     }
+    del r["inp"]
+    if not args.no_configs:
+        from selective_state_space_44_amd import workloads as W
+        cfg = {}
+        cfg[W.TINY.name] = bench_config(W.TINY, 1, max(20, args.steps), 5)
+        # 6 sets of ~202 MB (1.2 GB) rotated past the 256 MB Infinity Cache
+        cfg[W.MAMBA_130M.name] = bench_config(W.MAMBA_130M, 6, max(30, args.steps), 6)
+        cfg[W.LONG_CTX.name] = bench_config(W.LONG_CTX, 1, 10, 2)
+        line["configs"] = cfg
     if not args.no_decode:
         line["decode"] = bench_decode(args.decode_sweeps)
     if not args.no_fused:
-        line["fused_prologue"] = bench_fused(max(10, args.steps // 4), max(10, args.warmup // 4))
+        line["fused_prologue"] = bench_fused(max(10, args.steps // 4), 10)
     if not args.no_variants:
-        line["variants"] = bench_variants(max(10, args.steps // 4), max(10, args.warmup // 4))
+        line["variants"] = bench_variants(max(10, args.steps // 4), 10)
     if not args.no_ssd:
-        line["ssd"] = bench_ssd(max(10, args.steps // 2), max(10, args.warmup // 10))
+        line["ssd"] = bench_ssd(max(10, args.steps // 2), 10)
     if not args.no_backward:
-        bwd = bench_backward(max(10, args.steps // 5), max(5, args.warmup // 20))
-        bwd["time_vs_forward"] = bwd["ms_per_step"] / r["step_ms"]
+        bwd = bench_backward(max(10, args.steps // 5), 5)
+        bwd["time_vs_forward"] = bwd["ms_per_step"] / line["ms_per_step"]
         line["backward"] = bwd
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(r["inp"], w, args.cpu_seconds)
+        from selective_state_space_44_amd import workloads as W
+        inp = W.make_inputs(W.MAMBA_2P8B, device="cuda:0", layer=0)
+        line["cpu_baseline"] = cpu_baseline(inp, W.MAMBA_2P8B, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

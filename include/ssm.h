@@ -114,14 +114,14 @@ int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
  * 64 and 128 (the larger states of the paperlens tutorial's d_state setting
  * and of Mamba-3, ihouse article "推論効率") run one pass per sequence with
  * more waves per channel group: their workspace size is 0, waves_per_group
- * and nchunks are ignored, ssm_scan_fwd_phase accepts only phase 3 and the
+ * and nchunks are ignored, ssm_scan_fwd_phase accepts only phase 3 (or 7) and the
  * fused prologue is not available (SSM_ERR_UNSUPPORTED).  Other dstate:
  * SSM_ERR_UNSUPPORTED.
  * Outputs must not alias inputs (exact pointer equality is rejected).
  * seqlen == 0 writes h_last (= h0, or zeros) when given and nothing else;
  * batch == 0 or dim == 0 is a no-op.  More than 65535 batch rows run as
  * consecutive launches of at most 65528 rows on the stream (ssm_scan_fwd_phase
- * then accepts only phase 3).  Returns an SSM_* status.
+ * then accepts only phase 3 or 7).  Returns an SSM_* status.
  */
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                  int io_dtype, const void *x, const void *delta, const float *A,
@@ -145,16 +145,26 @@ int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim,
                          int waves_per_group, int nchunks, void *stream);
 
 /*
- * The two phases of a chunked scan, for callers that enqueue them apart
- * (e.g. to time or overlap them):
- *   phase 1 -- every chunk but the last is run from a zero state and the
- *              chunk end states are composed into the state entering each
- *              chunk, written to the workspace (a no-op when nchunks == 1);
- *   phase 2 -- the main pass: every chunk from its entering state, writing y
- *              and h_last (reads the workspace written by phase 1);
- *   phase 3 -- both, in order (what ssm_scan_fwd_planned enqueues).
+ * The launches of a chunked scan, for callers that enqueue them apart (e.g.
+ * to time or overlap them).  The update composes associatively over chunks
+ * (paperlens tutorial, section "代償と、それを払う方法（並列スキャン）"), so
+ * every chunk but the first can start from a state that a cheaper pass has
+ * computed.  Default (two-launch) schedule, phase bits:
+ *   1 -- chunk 0's main pass (its part of y, and the state entering chunk 1)
+ *        in one launch with the pre-pass of chunks 1 .. nchunks-2 (each run
+ *        from a zero state, end state recorded), then the composition of
+ *        those chunk maps into the state entering every chunk, written to
+ *        the workspace;
+ *   2 -- the main pass of chunks 1 .. nchunks-1 from their entering states,
+ *        writing the rest of y and h_last (reads the workspace phase 1 wrote);
+ *   3 -- both, in order (what ssm_scan_fwd_planned enqueues).
+ * Adding 4 selects the three-pass schedule instead (kept for comparison):
+ *   5 -- the pre-pass of chunks 0 .. nchunks-2 and the composition (nothing
+ *        but the workspace written);  6 -- the main pass of every chunk;
+ *   7 -- both.
+ * With nchunks == 1 phase bit 1 is a no-op and bit 2 runs the whole scan.
  * Arguments, plan and workspace are those of ssm_scan_fwd_planned and must be
- * identical for the two phases of one scan.  Other phase values return
+ * identical for the launches of one scan.  Other phase values return
  * SSM_ERR_INVALID_ARG.
  */
 int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,

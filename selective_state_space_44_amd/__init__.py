@@ -162,9 +162,10 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
     (all float32 or all bfloat16); A [dim, dstate], D [dim], h0
     [batch, dim, dstate] float32.  Returns y (and the final state when
     ``return_last_state``).  ``waves_per_group``/``nchunks`` override the
-    automatic plan (0 = automatic); ``phase`` 1 or 2 enqueues only the chunk
-    carry passes or only the main pass (see ssm_scan_fwd_phase); both phases
-    of one scan must get the same ``workspace`` and ``out``.
+    automatic plan (0 = automatic); ``phase`` 1 or 2 enqueues only the first
+    or only the second launch of the chunked scan, 5, 6 or 7 the three-pass
+    schedule (see ssm_scan_fwd_phase); the phases of one scan must get the
+    same ``workspace`` and ``out``.
 
     Variants (``ssm_scan_fwd_ex``): ``A`` of shape [dim] holds one value per
     channel shared by its states (then ``B``/``C`` fix dstate);
@@ -187,6 +188,9 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
     variant = per_channel or discretization != "zoh"
     if variant and phase != 3:
         raise ValueError("the A-per-channel and Euler variants run as one call (phase 3)")
+    if phase not in (1, 2, 3, 5, 6, 7):
+        raise ValueError("phase must be 1, 2 or 3 (two-launch schedule) or 5, 6 or 7 "
+                         "(three-pass schedule)")
     io = x.dtype
     code = _io_code(io)
     _require(x, "x", (batch, seqlen, dim), io, device)

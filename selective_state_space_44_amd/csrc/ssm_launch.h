@@ -74,8 +74,18 @@ struct ScanWorkspace {
 ScanWorkspace scan_workspace_layout(int64_t batch, int64_t dim, int nchunks);
 
 // Enqueue a scan.  io_bf16 selects the I/O type; waves_per_group is one of
-// 2, 4, 8, 16.  phase: 1 = chunk carry passes only, 2 = main pass only,
-// 3 = both.  Returns hipSuccess or the launch error.
+// 2, 4, 8, 16.  With nchunks > 1 the default schedule takes two launches:
+//   phase bit 1 -- the first launch (main pass of chunk 0, writing its y and
+//                  the state entering chunk 1, beside carry pass 1 of chunks
+//                  1 .. K-2) and carry pass 2;
+//   phase bit 2 -- the main pass of chunks 1 .. K-1.
+// With kPhaseThreePass also set, the three-pass schedule runs instead:
+//   bit 1 -- carry pass 1 on chunks 0 .. K-2 and carry pass 2 from h0 (the
+//            state entering every chunk, nothing else written: the backward
+//            uses this);
+//   bit 2 -- the main pass of every chunk.
+// Returns hipSuccess or the launch error.
+constexpr int kPhaseThreePass = 4;
 hipError_t launch_scan(const ScanArgs& a, bool io_bf16, int waves_per_group, int phase,
                        hipStream_t stream);
 

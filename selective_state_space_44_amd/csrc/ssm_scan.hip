@@ -260,12 +260,15 @@ struct Chunk {
   int64_t t_begin, t_end;
 };
 
-__device__ __forceinline__ Chunk chunk_coords(int dim, int64_t seqlen, int64_t chunk_len) {
+// Coordinates of this thread's block: chunk c of batch row b, the 64
+// channels of group blockIdx.x.
+__device__ __forceinline__ Chunk chunk_coords(int dim, int64_t seqlen, int64_t chunk_len, int c,
+                                              int b) {
   Chunk k;
   k.lane = threadIdx.x % kWave;
   k.g = wave_id();
-  k.b = blockIdx.z;
-  k.c = blockIdx.y;
+  k.b = b;
+  k.c = c;
   const int draw = blockIdx.x * kWave + k.lane;
   k.active = draw < dim;
   k.d = k.active ? draw : dim - 1;
@@ -761,28 +764,21 @@ __device__ __forceinline__ void scan_chunk(const IO* __restrict__ x, const IO* _
   }
 }
 
+// Main pass of one block: its 64 channels over chunk k from the state
+// `hinit` (nullable = zero state; [.., 16] rows of the block's channels),
+// writing y and, when `hout` is given, the state at the end of the chunk.
 template <typename IO, int G, bool HAS_Z, bool FUSED, int V>
-__global__ __launch_bounds__(kWave* G)
-__attribute__((amdgpu_waves_per_eu(FUSED ? kFusedWavesPerSimd : kMainWavesPerSimd)))
-void scan_fwd_kernel(
+__device__ __forceinline__ void main_block(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
-    const IO* __restrict__ z, const float* __restrict__ h0, IO* __restrict__ y,
-    float* __restrict__ h_last, const float* __restrict__ ws_hin, int64_t seqlen,
-    int64_t chunk_len, int dim, int nchunks, Prologue pro) {
+    const IO* __restrict__ z, IO* __restrict__ y, const float* hinit, float* hout,
+    int64_t seqlen, int dim, const Chunk& k, MainSmem<G>& sm, const Prologue& pro) {
   constexpr int NPL = kDState / G;
-  __shared__ MainSmem<G> sm;
-  const Chunk k = chunk_coords(dim, seqlen, chunk_len);
   const int n0 = k.g * NPL;
   clear_stages<IO, true>(sm.st, kWave * G);
 
   float A2[NPL], iA[NPL], h[NPL];
   const bool zero = load_A<NPL, V>(A, k.d, n0, A2, iA);
-  const float* hinit = nullptr;
-  if (nchunks > 1)
-    hinit = ws_hin + (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
-  else if (h0)
-    hinit = h0 + ((size_t)k.b * dim + k.d) * kDState + n0;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) h[j] = hinit ? hinit[j] : 0.0f;
   const float Dd = Dskip ? Dskip[k.d] : 0.0f;
@@ -797,11 +793,37 @@ void scan_fwd_kernel(
     scan_chunk<IO, G, HAS_Z, false, FUSED, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, sm, A2,
                                               iA, h, lp);
 
-  if (k.c == nchunks - 1 && h_last && k.active) {
-    float* hl = h_last + ((size_t)k.b * dim + k.d) * kDState + n0;
+  if (hout && k.active) {
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) hl[j] = h[j];
+    for (int j = 0; j < NPL; ++j) hout[j] = h[j];
   }
+}
+
+// Main pass over chunks c_first .. nchunks-1 (grid y: chunk - c_first, grid
+// z: batch row).  A chunk c > 0 starts from ws_hin[b, c]; chunk 0 from h0.
+// The last chunk writes h_last.
+template <typename IO, int G, bool HAS_Z, bool FUSED, int V>
+__global__ __launch_bounds__(kWave* G)
+__attribute__((amdgpu_waves_per_eu(FUSED ? kFusedWavesPerSimd : kMainWavesPerSimd)))
+void scan_fwd_kernel(
+    const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
+    const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
+    const IO* __restrict__ z, const float* __restrict__ h0, IO* __restrict__ y,
+    float* __restrict__ h_last, const float* __restrict__ ws_hin, int64_t seqlen,
+    int64_t chunk_len, int dim, int nchunks, int c_first, Prologue pro) {
+  constexpr int NPL = kDState / G;
+  __shared__ MainSmem<G> sm;
+  const Chunk k = chunk_coords(dim, seqlen, chunk_len, (int)blockIdx.y + c_first, blockIdx.z);
+  const int n0 = k.g * NPL;
+  const size_t bd = (size_t)k.b * dim + k.d;
+  const float* hinit = nullptr;
+  if (k.c > 0)
+    hinit = ws_hin + (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
+  else if (h0)
+    hinit = h0 + bd * kDState + n0;
+  float* hout = (k.c == nchunks - 1 && h_last) ? h_last + bd * kDState + n0 : nullptr;
+  main_block<IO, G, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k,
+                                     sm, pro);
 }
 
 // ---------------------------------------------------------------------------
@@ -948,15 +970,16 @@ __device__ __forceinline__ void chunk_state(const IO* __restrict__ x,
   }
 }
 
+// Carry pass 1 of one block: its 64 channels over chunk k from a zero state;
+// stores the end state and (wave 0) the chunk's sum of delta.
 template <typename IO, int G, bool FUSED, int V>
-__global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kCarryWavesPerSimd)))
-void scan_chunk_state_kernel(
-    const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
-    const IO* __restrict__ B, float* __restrict__ ws_hloc, double* __restrict__ ws_sdelta,
-    int64_t seqlen, int64_t chunk_len, int dim, int nchunks, Prologue pro) {
+__device__ __forceinline__ void pre_block(const IO* __restrict__ x, const IO* __restrict__ delta,
+                                          const float* __restrict__ A, const IO* __restrict__ B,
+                                          float* __restrict__ ws_hloc,
+                                          double* __restrict__ ws_sdelta, int64_t seqlen,
+                                          int dim, int nchunks, const Chunk& k,
+                                          Stage<false>* stages, const Prologue& pro) {
   constexpr int NPL = kDState / G;
-  __shared__ Stage<false> stages[2];
-  const Chunk k = chunk_coords(dim, seqlen, chunk_len);  // k.c in [0, nchunks-2]
   const int n0 = k.g * NPL;
   clear_stages<IO, false>(stages, kWave * G);
   float A2[NPL], iA[NPL], h[NPL];
@@ -978,6 +1001,55 @@ void scan_chunk_state_kernel(
   }
 }
 
+// Carry pass 1 of the three-pass schedule: chunks 0 .. nchunks-2 (grid y),
+// each from a zero state.
+template <typename IO, int G, bool FUSED, int V>
+__global__ __launch_bounds__(kWave* G) __attribute__((amdgpu_waves_per_eu(kCarryWavesPerSimd)))
+void scan_chunk_state_kernel(
+    const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
+    const IO* __restrict__ B, float* __restrict__ ws_hloc, double* __restrict__ ws_sdelta,
+    int64_t seqlen, int64_t chunk_len, int dim, int nchunks, Prologue pro) {
+  __shared__ Stage<false> stages[2];
+  const Chunk k = chunk_coords(dim, seqlen, chunk_len, blockIdx.y, blockIdx.z);
+  pre_block<IO, G, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k, stages,
+                             pro);
+}
+
+// First launch of the two-launch schedule (grid x: channel group, y: batch
+// row, z: role).  Chunk 0 needs no carry, so its main pass runs here at once
+// (z == 0): it writes y of chunk 0 and the state entering chunk 1 into
+// ws_hin.  The other blocks (z = c in 1 .. nchunks-2) run chunk c from a zero
+// state, as carry pass 1 does.  The blocks of chunk 0 come first in dispatch
+// order; they are the longest.  Chunk 0's own pre-pass, which the three-pass
+// schedule spends, is never needed.
+template <typename IO, int G, bool HAS_Z, bool FUSED, int V>
+__global__ __launch_bounds__(kWave* G)
+__attribute__((amdgpu_waves_per_eu(FUSED ? kFusedWavesPerSimd : kMainWavesPerSimd)))
+void scan_first_kernel(
+    const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
+    const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
+    const IO* __restrict__ z, const float* __restrict__ h0, IO* __restrict__ y,
+    float* __restrict__ ws_hloc, double* __restrict__ ws_sdelta, float* __restrict__ ws_hin,
+    int64_t seqlen, int64_t chunk_len, int dim, int nchunks, Prologue pro) {
+  constexpr int NPL = kDState / G;
+  __shared__ union {
+    MainSmem<G> main;
+    Stage<false> pre[2];
+  } sm;
+  const Chunk k = chunk_coords(dim, seqlen, chunk_len, blockIdx.z, blockIdx.y);
+  if (k.c == 0) {
+    const int n0 = k.g * NPL;
+    const size_t bd = (size_t)k.b * dim + k.d;
+    const float* hinit = h0 ? h0 + bd * kDState + n0 : nullptr;
+    float* hout = ws_hin + (((size_t)k.b * nchunks + 1) * dim + k.d) * kDState + n0;
+    main_block<IO, G, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim,
+                                       k, sm.main, pro);
+  } else {
+    pre_block<IO, G, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k,
+                               sm.pre, pro);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Carry pass 2: the state entering every chunk.  Chunk c maps its entering
 // state h to P_c h + hloc_c with P_c = exp(A * sum of delta over chunk c) (the
@@ -988,6 +1060,10 @@ void scan_chunk_state_kernel(
 // (d, n), so every load and store of a step is one coalesced row, and the
 // loads of four steps are issued before their updates.
 //
+// In the two-launch schedule the first launch already gives the state
+// entering chunk 1 (chunk 0's main pass ends there), so the walk starts at
+// chunk c_first = 1.
+//
 // With `reverse` set the same composition runs from the last chunk to the
 // first (chunk c is addressed as nchunks - 1 - c): the backward pass uses it
 // for the adjoint of the state, which flows from the end of the sequence to
@@ -996,7 +1072,8 @@ void scan_chunk_state_kernel(
 __global__ __launch_bounds__(256) void scan_carry_kernel(
     const float* __restrict__ A, const float* __restrict__ h0,
     const float* __restrict__ ws_hloc, const double* __restrict__ ws_sdelta,
-    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int a_scalar, int reverse) {
+    float* __restrict__ ws_hin, int batch, int dim, int nchunks, int a_scalar, int reverse,
+    int c_first) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)batch * dim * kDState;
   if (gid >= total) return;
@@ -1008,10 +1085,17 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(
   auto cd = [&](int c) {
     return ((size_t)b * nchunks + (reverse ? nchunks - 1 - c : c)) * dim + d;
   };
-  float h = h0 ? h0[gid] : 0.0f;
-  ws_hin[cd(0) * kDState + n] = h;
+  // c_first == 0: from h0 (or zero), which is the state entering chunk 0;
+  // c_first > 0: from the state entering chunk c_first, already in ws_hin
+  float h;
+  if (c_first == 0) {
+    h = h0 ? h0[gid] : 0.0f;
+    ws_hin[cd(0) * kDState + n] = h;
+  } else {
+    h = ws_hin[cd(c_first) * kDState + n];
+  }
   constexpr int U = 4;
-  int c = 0;
+  int c = c_first;
   for (; c + U <= nchunks - 1; c += U) {
     float P[U], H[U];
 #pragma unroll
@@ -1044,36 +1128,74 @@ hipError_t launch_scan_t(const ScanArgs& a, int phase, hipStream_t stream) {
   const IO* delta = static_cast<const IO*>(a.delta);
   const IO* B = static_cast<const IO*>(a.B);
   const IO* C = static_cast<const IO*>(a.C);
+  const IO* z = static_cast<const IO*>(a.z);
+  IO* y = static_cast<IO*>(a.y);
   const unsigned gx = (unsigned)((a.dim + kWave - 1) / kWave);
-  if (a.nchunks > 1 && (phase & 1)) {
-    // the carry pass has no readout to share, so it splits the states over
-    // more waves (two per wave) for latency hiding
-    constexpr int GC = G < 8 ? 8 : G;
-    dim3 grid1(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, GC, FUSED, V>), grid1, dim3(kWave * GC), 0,
-                       stream, x, delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len,
-                       a.dim, a.nchunks, a.pro);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t threads = (int64_t)a.batch * a.dim * kDState;
-    hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, a.A, a.h0, a.ws_hloc, a.ws_sdelta, a.ws_hin, a.batch, a.dim,
-                       a.nchunks, (V & kScalarA) ? 1 : 0, 0);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)a.batch * a.dim * kDState;
+  const dim3 carry_grid((unsigned)((threads + 255) / 256));
+  const int vs = (V & kScalarA) ? 1 : 0;
+  hipError_t e;
+  if ((phase & kPhaseThreePass) || a.nchunks <= 1) {
+    // three-pass schedule: carry pass 1 on chunks 0 .. K-2, carry pass 2 from
+    // h0, main pass on every chunk (also the one-chunk case: main pass only)
+    if (a.nchunks > 1 && (phase & 1)) {
+      // the carry pass has no readout to share, so it splits the states over
+      // more waves (two per wave) for latency hiding
+      constexpr int GC = G < 8 ? 8 : G;
+      dim3 grid1(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
+      hipLaunchKernelGGL((scan_chunk_state_kernel<IO, GC, FUSED, V>), grid1, dim3(kWave * GC), 0,
+                         stream, x, delta, a.A, B, a.ws_hloc, a.ws_sdelta, a.seqlen, a.chunk_len,
+                         a.dim, a.nchunks, a.pro);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(scan_carry_kernel, carry_grid, dim3(256), 0, stream, a.A, a.h0,
+                         a.ws_hloc, a.ws_sdelta, a.ws_hin, a.batch, a.dim, a.nchunks, vs, 0, 0);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (!(phase & 2)) return hipSuccess;
+    dim3 grid(gx, (unsigned)a.nchunks, (unsigned)a.batch);
+    if (a.z)
+      hipLaunchKernelGGL((scan_fwd_kernel<IO, G, true, FUSED, V>), grid, dim3(kWave * G), 0,
+                         stream, x, delta, a.A, B, C, a.Dskip, z, a.h0, y, a.h_last, a.ws_hin,
+                         a.seqlen, a.chunk_len, a.dim, a.nchunks, 0, a.pro);
+    else
+      hipLaunchKernelGGL((scan_fwd_kernel<IO, G, false, FUSED, V>), grid, dim3(kWave * G), 0,
+                         stream, x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr),
+                         a.h0, y, a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim, a.nchunks, 0,
+                         a.pro);
+    return hipGetLastError();
+  }
+  // two-launch schedule (K >= 2): the first launch runs chunk 0's main pass
+  // beside carry pass 1 of chunks 1 .. K-2; carry pass 2 composes from the
+  // state entering chunk 1; the second launch is the main pass of chunks
+  // 1 .. K-1
+  if (phase & 1) {
+    dim3 grid1(gx, (unsigned)a.batch, (unsigned)(a.nchunks - 1));
+    if (a.z)
+      hipLaunchKernelGGL((scan_first_kernel<IO, G, true, FUSED, V>), grid1, dim3(kWave * G), 0,
+                         stream, x, delta, a.A, B, C, a.Dskip, z, a.h0, y, a.ws_hloc,
+                         a.ws_sdelta, a.ws_hin, a.seqlen, a.chunk_len, a.dim, a.nchunks, a.pro);
+    else
+      hipLaunchKernelGGL((scan_first_kernel<IO, G, false, FUSED, V>), grid1, dim3(kWave * G), 0,
+                         stream, x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr),
+                         a.h0, y, a.ws_hloc, a.ws_sdelta, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
+                         a.nchunks, a.pro);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.nchunks > 2) {
+      hipLaunchKernelGGL(scan_carry_kernel, carry_grid, dim3(256), 0, stream, a.A, a.h0,
+                         a.ws_hloc, a.ws_sdelta, a.ws_hin, a.batch, a.dim, a.nchunks, vs, 0, 1);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   if (!(phase & 2)) return hipSuccess;
-  dim3 grid(gx, (unsigned)a.nchunks, (unsigned)a.batch);
+  dim3 grid(gx, (unsigned)(a.nchunks - 1), (unsigned)a.batch);
   if (a.z)
     hipLaunchKernelGGL((scan_fwd_kernel<IO, G, true, FUSED, V>), grid, dim3(kWave * G), 0, stream,
-                       x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(a.z), a.h0,
-                       static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
-                       a.nchunks, a.pro);
+                       x, delta, a.A, B, C, a.Dskip, z, a.h0, y, a.h_last, a.ws_hin, a.seqlen,
+                       a.chunk_len, a.dim, a.nchunks, 1, a.pro);
   else
     hipLaunchKernelGGL((scan_fwd_kernel<IO, G, false, FUSED, V>), grid, dim3(kWave * G), 0, stream,
-                       x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr), a.h0,
-                       static_cast<IO*>(a.y), a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim,
-                       a.nchunks, a.pro);
+                       x, delta, a.A, B, C, a.Dskip, static_cast<const IO*>(nullptr), a.h0, y,
+                       a.h_last, a.ws_hin, a.seqlen, a.chunk_len, a.dim, a.nchunks, 1, a.pro);
   return hipGetLastError();
 }
 
@@ -1124,7 +1246,7 @@ hipError_t launch_carry(const float* A, int a_per_channel, const float* init,
   const int64_t threads = (int64_t)batch * dim * kDState;
   hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, A, init, ws_loc, ws_sdelta, ws_in, batch, dim, nchunks,
-                     a_per_channel, reverse ? 1 : 0);
+                     a_per_channel, reverse ? 1 : 0, 0);
   return hipGetLastError();
 }
 

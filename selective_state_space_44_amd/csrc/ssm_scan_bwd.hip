@@ -655,7 +655,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e;
   if (f.nchunks > 1) {
     // forward chunk entry states
-    e = launch_scan(f, sizeof(IO) == 2, 4, 1, stream);
+    e = launch_scan(f, sizeof(IO) == 2, 4, kPhaseThreePass | 1, stream);
     if (e != hipSuccess) return e;
     // adjoint chunk entry values
     hipLaunchKernelGGL((bwd_chunk_adjoint_kernel<IO, G, HAS_Z, V>),

@@ -125,6 +125,23 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(batch=0) == ssm.SSM_OK
 
 
+def test_scan_phase_values(lib):
+    """Phase bits 1 and 2 select the launches, 4 the three-pass schedule;
+    anything else is rejected before a launch (batch 0 would return OK after
+    the check, so a bad phase is seen first)."""
+    def phase(ph, batch=0):
+        return lib.ssm_scan_fwd_phase(batch, 8, 64, 16, 1, FAKE, ctypes.c_void_p(0x6000), FAKE,
+                                      ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), None,
+                                      None, None, ctypes.c_void_p(0x2000), None, None, 0, 0, 0,
+                                      ph, None)
+    for bad in (-1, 0, 4, 8, 11):
+        assert phase(bad) == ssm.SSM_ERR_INVALID_ARG, bad
+    for good in (1, 2, 3, 5, 6, 7):
+        assert phase(good) == ssm.SSM_OK, good
+    for split in (1, 2, 5, 6):                   # sliced batches take whole scans only
+        assert phase(split, batch=65536) == ssm.SSM_ERR_UNSUPPORTED
+
+
 def test_batch_limits(lib):
     """More than 65535 batch rows: the forward scan slices them (but not when
     its two phases are enqueued apart), the backward refuses; both checks

@@ -22,11 +22,17 @@ def _inputs(w, **kw):
     return inp
 
 
-def _run(inp, G=0, K=0, with_state=True, **over):
+# phase 3: the two-launch schedule (chunk 0's main pass beside the pre-pass
+# of chunks 1..K-2); phase 7: the three-pass schedule (pre-pass of chunks
+# 0..K-2, then the main pass of every chunk)
+SCHEDULES = {"two_launch": 3, "three_pass": 7}
+
+
+def _run(inp, G=0, K=0, with_state=True, phase=3, **over):
     p = dict(inp, **over)
     return ssm.scan_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p.get("D"), p.get("z"),
                         p.get("h0"), return_last_state=with_state, waves_per_group=G,
-                        nchunks=K)
+                        nchunks=K, phase=phase)
 
 
 @pytest.fixture(scope="module")
@@ -36,22 +42,24 @@ def tiny():
     return inp, y_ref, h_ref
 
 
+@pytest.mark.parametrize("schedule", list(SCHEDULES))
 @pytest.mark.parametrize("G,K", PLANS)
-def test_tiny_fp32_all_plans(tiny, G, K):
+def test_tiny_fp32_all_plans(tiny, G, K, schedule):
     inp, y_ref, h_ref = tiny
-    print(f"tiny fp32 G={G} K={K}", flush=True)
-    y, h = _run(inp, G, K)
+    print(f"tiny fp32 G={G} K={K} {schedule}", flush=True)
+    y, h = _run(inp, G, K, phase=SCHEDULES[schedule])
     torch.cuda.synchronize()
     parity.check_y(parity.to_f64(y), y_ref, torch.float32)
     parity.check_state(parity.to_f64(h), h_ref)
 
 
-@pytest.mark.parametrize("G,K", [(2, 1), (4, 1), (16, 1), (4, 4), (8, 3)])
+@pytest.mark.parametrize("G,K,phase", [(2, 1, 3), (4, 1, 3), (16, 1, 3), (4, 4, 3), (8, 3, 3),
+                                       (4, 2, 3), (4, 4, 7), (2, 6, 7)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_ragged_sizes_with_h0_and_no_gate(G, K, dtype):
+def test_ragged_sizes_with_h0_and_no_gate(G, K, phase, dtype):
     """batch 2, L=1003 (not a tile multiple), dim=200 (not a multiple of 64),
-    random initial state, with and without z and D."""
-    print(f"ragged {dtype} G={G} K={K}", flush=True)
+    random initial state, with and without z and D; both schedules."""
+    print(f"ragged {dtype} G={G} K={K} phase={phase}", flush=True)
     w = W.MAMBA_130M
     inp = _inputs(w, batch=2, seqlen=1003, dim=200)
     inp = {k: (v.to(dtype) if k in ("x", "delta", "z", "B", "C") else v) for k, v in inp.items()}
@@ -65,7 +73,7 @@ def test_ragged_sizes_with_h0_and_no_gate(G, K, dtype):
             over["D"] = None
         p = dict(inp, **over)
         y_ref, h_ref = parity.oracle_scan(p)
-        y, h = _run(p, G, K)
+        y, h = _run(p, G, K, phase=phase)
         torch.cuda.synchronize()
         parity.check_y(parity.to_f64(y), y_ref, dtype, what=f"y[{variant}]")
         parity.check_state(parity.to_f64(h), h_ref, what=f"h_last[{variant}]")
@@ -80,33 +88,83 @@ def _sampled_channels(dim, n, seed):
 
 @pytest.mark.parametrize("w", [W.MAMBA_130M, W.MAMBA_2P8B], ids=lambda w: w.name)
 def test_full_size_sampled_channels(w):
-    """Full benchmark shapes in the automatic plan; the oracle computes a
-    sample of channels over the whole sequence for every batch row."""
+    """Full benchmark shapes in the automatic plan (the launch configuration
+    the benchmark times); the oracle computes 256 sampled channels (plus the
+    first and last) over the whole sequence for every batch row."""
     print(f"full {w.name} plan={ssm.scan_plan(w.batch, w.seqlen, w.dim)}", flush=True)
     inp = _inputs(w)
     y, h = _run(inp)
     torch.cuda.synchronize()
-    ch = _sampled_channels(w.dim, 48, 5)
+    ch = _sampled_channels(w.dim, 256, 5)
+    assert len(ch) >= 256
     y_ref, h_ref = parity.oracle_scan(inp, channels=ch)
     parity.check_y(parity.pick(y, ch, 2), y_ref, w.io_dtype)
     parity.check_state(parity.pick(h, ch, 1), h_ref)
 
 
+def long_context_channels(delta, n=256, most_negative=8):
+    """Channels of the long-context workload that span its per-channel delta
+    bias: ranked by mean delta over the first 4096 steps (the bias dominates
+    it), the `most_negative` longest-memory channels plus channels at evenly
+    spaced ranks up to the shortest-memory one."""
+    rank = torch.argsort(delta[0, :4096].float().mean(0)).tolist()
+    picks = set(rank[:most_negative])
+    spaced = np.linspace(0, len(rank) - 1, n - most_negative).round().astype(int)
+    picks |= {rank[i] for i in spaced}
+    i = most_negative
+    while len(picks) < n:
+        picks.add(rank[i])
+        i += 1
+    return sorted(picks), rank
+
+
 def test_long_context_sampled_channels():
     """L = 262144 single sequence with per-channel delta bias: the plan cuts
-    it into chunks, so this checks the cross-chunk carry at full length.  The
-    sample includes the 8 channels with the most negative bias (longest
-    memory)."""
+    it into chunks, so this checks the cross-chunk carry at full length over
+    256 channels spanning the bias range, including the 8 channels with the
+    most negative bias (longest memory)."""
     w = W.LONG_CTX
     print(f"full {w.name} plan={ssm.scan_plan(w.batch, w.seqlen, w.dim)}", flush=True)
     inp = _inputs(w)
     y, h = _run(inp)
     torch.cuda.synchronize()
-    bias_rank = torch.argsort(inp["delta"][0, :4096].float().mean(0)).tolist()
-    ch = sorted(set(bias_rank[:8]) | set(_sampled_channels(w.dim, 24, 9)))
+    ch, rank = long_context_channels(inp["delta"])
+    assert len(ch) >= 256 and set(rank[:8]) <= set(ch) and rank[-1] in ch
     y_ref, h_ref = parity.oracle_scan(inp, channels=ch)
     parity.check_y(parity.pick(y, ch, 2), y_ref, w.io_dtype)
     parity.check_state(parity.pick(h, ch, 1), h_ref)
+
+
+@pytest.mark.parametrize("G,K", [(4, 4), (4, 2), (8, 5), (2, 3)])
+def test_phases_enqueued_apart(G, K):
+    """Phase 1 then phase 2 gives the same bytes as phase 3, for both
+    schedules; the two schedules agree within the fp32 rule (they round the
+    state entering chunk 1 along different paths)."""
+    inp = _inputs(W.MAMBA_130M, batch=2, seqlen=1000, dim=192)
+    g = torch.Generator(device=DEV).manual_seed(21)
+    inp["h0"] = torch.randn((2, 192, 16), generator=g, device=DEV)
+    res = {}
+    for base in (0, 4):
+        y3, h3 = _run(inp, G, K, phase=base | 3)
+        ws = torch.empty(ssm.scan_workspace_bytes(2, 1000, 192, nchunks=K) + 256,
+                         dtype=torch.uint8, device=DEV)
+        y = torch.empty_like(inp["x"])
+        hl = torch.empty_like(inp["h0"])
+        for ph in (base | 1, base | 2):
+            args = [inp[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")]
+            st = ssm.load_library().ssm_scan_fwd_phase(
+                2, 1000, 192, 16, ssm.SSM_DTYPE_BF16, *[ssm._ptr(a) for a in args],
+                ssm._ptr(y), ssm._ptr(hl), ssm._ptr(ws), ws.numel(), G, K, ph,
+                ssm._stream(inp["x"].device))
+            assert st == ssm.SSM_OK
+        torch.cuda.synchronize()
+        assert torch.equal(y, y3) and torch.equal(hl, h3), f"phase split, base {base}"
+        res[base] = (y3, h3)
+    parity.check_state(parity.to_f64(res[0][1]), parity.to_f64(res[4][1]), "h_last schedules")
+    y_ref, h_ref = parity.oracle_scan(inp)
+    for base in (0, 4):
+        parity.check_y(parity.to_f64(res[base][0]), y_ref, torch.bfloat16)
+        parity.check_state(parity.to_f64(res[base][1]), h_ref)
 
 
 def test_chunk_and_resume_invariance():

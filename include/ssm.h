@@ -68,6 +68,10 @@ extern "C" {
 #define SSM_ERR_WORKSPACE 3   /* workspace missing or smaller than required */
 #define SSM_ERR_HIP 4         /* a HIP runtime call or kernel launch failed */
 
+/* Capacity of the device scratch array of ssm_scan_fwd_noalloc (64 MiB, held
+ * by every GPU the library runs on until the process ends). */
+#define SSM_NOALLOC_SCRATCH_BYTES 67108864
+
 /* Version of this ABI (SSM_ABI_VERSION). */
 int ssm_abi_version(void);
 
@@ -173,6 +177,35 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
                        const float *Dskip, const void *z, const float *h0, void *y,
                        float *h_last, void *workspace, size_t workspace_bytes,
                        int waves_per_group, int nchunks, int phase, void *stream);
+
+/*
+ * ssm_scan_fwd_planned for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace argument: the chunk-carry workspace
+ * (per-chunk end states, entering states and delta sums) lives in a
+ * file-scope device array of SSM_NOALLOC_SCRATCH_BYTES bytes, which each GPU
+ * holds from the first call on it until the process ends.  The call makes no
+ * hipMalloc, hipFree or other allocating call.  The caller still passes
+ * inputs and outputs, with the meaning, layout and checks of ssm_scan_fwd.
+ * waves_per_group and nchunks: as ssm_scan_fwd_planned (<= 0 = automatic).
+ * A plan whose workspace (ssm_scan_workspace_bytes with the same nchunks)
+ * exceeds SSM_NOALLOC_SCRATCH_BYTES returns SSM_ERR_WORKSPACE before
+ * anything is enqueued (the single L = 262144, D = 4096 sequence, for
+ * instance, fits with at most 120 chunks; its automatic plan takes 128); such
+ * callers pass a smaller nchunks.  The first call on a device looks up that device's copy of the
+ * array (SSM_ERR_HIP if that fails).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; a call writes every scratch value before reading it, so nothing
+ * needs clearing, but calls that overlap on one GPU (on different streams, or
+ * from several threads) race on the array and must be serialised by the
+ * caller.
+ */
+int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int io_dtype, const void *x,
+                         const void *delta, const float *A, const void *B,
+                         const void *C, const float *Dskip, const void *z,
+                         const float *h0, void *y, float *h_last,
+                         int waves_per_group, int nchunks, void *stream);
 
 /*
  * ssm_scan_fwd_planned with two variants of the per-element formula:

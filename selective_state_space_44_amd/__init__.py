@@ -22,7 +22,7 @@ import threading
 
 import torch
 
-__all__ = ["scan_fwd", "scan_fwd_fused", "scan_bwd", "SelectiveScan", "decode_step", "ssd_scan",
+__all__ = ["scan_fwd", "scan_fwd_noalloc", "scan_fwd_fused", "scan_bwd", "SelectiveScan", "decode_step", "ssd_scan",
            "ssd_bwd",
            "scan_plan", "scan_workspace_bytes", "scan_bwd_workspace_bytes", "load_library",
            "LIB_PATH", "SsmError"]
@@ -38,6 +38,7 @@ SSM_ERR_INVALID_ARG = 1
 SSM_ERR_UNSUPPORTED = 2
 SSM_ERR_WORKSPACE = 3
 SSM_ERR_HIP = 4
+SSM_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/ssm.h declares, with its ctypes signature.
 _i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -52,6 +53,8 @@ SIGNATURES = {
                              + [_vp, _sz, _int, _int, _vp]),
     "ssm_scan_fwd_phase": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
                            + [_vp, _sz, _int, _int, _int, _vp]),
+    "ssm_scan_fwd_noalloc": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
+                             + [_int, _int, _vp]),
     "ssm_scan_fwd_ex": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
                         + [_vp] * 7 + [_vp, _sz, _int, _int, _vp]),
     "ssm_scan_fwd_fused": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int, _vp,
@@ -230,6 +233,46 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
                                 _stream(device))
     _check(st, "ssm_scan_fwd")
     return (y, h_last) if return_last_state else y
+
+
+def scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, h0=None, *, out,
+                     h_last=None, waves_per_group: int = 0, nchunks: int = 0):
+    """``ssm_scan_fwd_noalloc``: the scan of ``scan_fwd`` (per-state A, zero-
+    order hold) with its chunk-carry workspace in the library's device scratch
+    array, so that the call allocates nothing: the caller passes the output
+    ``out`` [batch, L, dim] and, optionally, ``h_last`` [batch, dim, dstate]
+    float32.  Raises SsmError(SSM_ERR_WORKSPACE) when the plan's workspace
+    exceeds SSM_NOALLOC_SCRATCH_BYTES.  Calls that overlap on one GPU race on
+    the scratch array."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a [batch, seqlen, dim] tensor")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    batch, seqlen, dim = x.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a [dim, dstate] tensor")
+    dstate = A.shape[1]
+    io = x.dtype
+    code = _io_code(io)
+    _require(x, "x", (batch, seqlen, dim), io, device)
+    _require(delta, "delta", (batch, seqlen, dim), io, device)
+    _require(A, "A", (dim, dstate), torch.float32, device)
+    _require(B, "B", (batch, seqlen, dstate), io, device)
+    _require(C, "C", (batch, seqlen, dstate), io, device)
+    _require(D, "D", (dim,), torch.float32, device)
+    _require(z, "z", (batch, seqlen, dim), io, device)
+    _require(h0, "h0", (batch, dim, dstate), torch.float32, device)
+    _require(out, "out", (batch, seqlen, dim), io, device)
+    _require(h_last, "h_last", (batch, dim, dstate), torch.float32, device)
+    if delta is None or B is None or C is None or out is None:
+        raise ValueError("delta, B, C and out are required")
+    st = load_library().ssm_scan_fwd_noalloc(
+        batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+        _ptr(D), _ptr(z), _ptr(h0), _ptr(out), _ptr(h_last), int(waves_per_group),
+        int(nchunks), _stream(device))
+    _check(st, "ssm_scan_fwd_noalloc")
+    return out
 
 
 def ssd_scan(x, dt, A, B, C, D=None, z=None, h0=None, return_last_state=False,

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ssm_launch.h"
 
@@ -86,6 +87,39 @@ bool sizes_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
 
+// Scratch of ssm_scan_fwd_noalloc: the chunk-carry workspace (per-chunk end
+// states, entering states and delta sums) lives in this file-scope device
+// array instead of a caller buffer.  Every GPU the library runs on holds its
+// own copy at its own address until the process ends.  In host code the name
+// `scratch` is a host-side stand-in, not a device address: kernels get the
+// address hipGetSymbolAddress returns for the device, looked up once per
+// device (with that device current) and kept in scratch_ptr.
+__device__ __align__(256) unsigned char scratch[SSM_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+void* scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of `scratch` on the device that runs `stream`.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  const hipError_t e0 = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e0 != hipSuccess) return SSM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SSM_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return SSM_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return SSM_ERR_HIP;
+    if (e != hipSuccess || !p) return SSM_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return SSM_OK;
+}
+
 // Every tensor pointer must be 16-byte aligned (the kernels use 16-byte
 // vector and 4-byte scalar accesses on these bases).
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -142,7 +176,7 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
                const float* Dskip, const void* z, const float* h0, void* y, float* h_last,
                void* workspace, size_t workspace_bytes, int waves_per_group, int nchunks,
                int phase, void* stream, const ssm::Prologue& pro, int a_per_channel = 0,
-               int euler = 0) {
+               int euler = 0, bool use_scratch = false) {
   if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype))
     return SSM_ERR_INVALID_ARG;
   // phase: bits 1 and 2 select the launches, bit 4 the three-pass schedule
@@ -190,7 +224,8 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
           at(delta, xrow), A, at(B, bcrow), at(C, bcrow), Dskip, at(z, xrow),
           reinterpret_cast<const float*>(at(h0, srow)), const_cast<char*>(at(y, xrow)),
           reinterpret_cast<float*>(const_cast<char*>(at(h_last, srow))), workspace,
-          workspace_bytes, waves_per_group, nchunks, phase, stream, pro, a_per_channel, euler);
+          workspace_bytes, waves_per_group, nchunks, phase, stream, pro, a_per_channel, euler,
+          use_scratch);
       if (st != SSM_OK) return st;
     }
     return SSM_OK;
@@ -228,6 +263,13 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
   K = effective_chunks(seqlen, dim, io_dtype, K);  // == ceil(seqlen / chunk_len)
 
   const ssm::ScanWorkspace ws = ssm::scan_workspace_layout(batch, dim, K);
+  if (use_scratch && ws.total > 0) {
+    // the file-scope scratch instead of a caller buffer (after every
+    // argument check: nothing before this point touches the GPU)
+    if (ws.total > workspace_bytes) return SSM_ERR_WORKSPACE;
+    const int st = scratch_for_stream(s, &workspace);
+    if (st != SSM_OK) return st;
+  }
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return SSM_ERR_WORKSPACE;
   if (ws.total > 0) {
     for (const void* in : ins)
@@ -331,6 +373,17 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  float* h_last, void* workspace, size_t workspace_bytes, void* stream) {
   return ssm_scan_fwd_planned(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip,
                               z, h0, y, h_last, workspace, workspace_bytes, 0, 0, stream);
+}
+
+int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int io_dtype, const void* x, const void* delta, const float* A,
+                         const void* B, const void* C, const float* Dskip, const void* z,
+                         const float* h0, void* y, float* h_last, int waves_per_group,
+                         int nchunks, void* stream) {
+  const ssm::Prologue none{};
+  return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
+                    h_last, nullptr, SSM_NOALLOC_SCRATCH_BYTES, waves_per_group, nchunks, 3,
+                    stream, none, 0, 0, true);
 }
 
 int ssm_decode_step_ex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* h,

@@ -142,6 +142,25 @@ def test_scan_phase_values(lib):
         assert phase(split, batch=65536) == ssm.SSM_ERR_UNSUPPORTED
 
 
+def test_noalloc_checks_come_first(lib):
+    """The allocation-free scan validates like the others and refuses a plan
+    whose workspace exceeds its scratch array, all before any HIP call (so
+    this runs without a GPU)."""
+    def na(batch=2, L=8, dim=64, N=16, io=1, x=FAKE, y=ctypes.c_void_p(0x2000), G=0, K=0):
+        return lib.ssm_scan_fwd_noalloc(batch, L, dim, N, io, x, ctypes.c_void_p(0x6000),
+                                        FAKE, ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000),
+                                        None, None, None, y, None, G, K, None)
+    assert na(batch=-1) == ssm.SSM_ERR_INVALID_ARG
+    assert na(x=None) == ssm.SSM_ERR_INVALID_ARG
+    assert na(y=FAKE) == ssm.SSM_ERR_INVALID_ARG                  # y aliases x
+    assert na(N=8) == ssm.SSM_ERR_UNSUPPORTED
+    assert na(G=3) == ssm.SSM_ERR_UNSUPPORTED
+    assert na(batch=0) == ssm.SSM_OK
+    # 128 chunks of the 262144-step, 4096-channel sequence need 71.3 MB
+    assert na(batch=1, L=262144, dim=4096, K=128) == ssm.SSM_ERR_WORKSPACE
+    assert lib.ssm_scan_workspace_bytes(1, 262144, 4096, 16, 1, 128) > ssm.SSM_NOALLOC_SCRATCH_BYTES
+
+
 def test_batch_limits(lib):
     """More than 65535 batch rows: the forward scan slices them (but not when
     its two phases are enqueued apart), the backward refuses; both checks

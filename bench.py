@@ -233,6 +233,54 @@ def bench_scan(steps: int, warmup: int, ramp_s: float):
                 ramp_steps=ramp_steps)
 
 
+def sweep_plans(spec: str, steps: int, ramp_s: float):
+    """Chunk plans "GxK,GxK,..." of the Mamba-2.8B layer scan under both
+    schedules (two-launch: phases 1 and 2; three-pass: phases 5 and 6): median
+    ms of each launch group and of the step over `steps` timed steps, two
+    input sets alternated."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.MAMBA_2P8B
+    dev = "cuda:0"
+    plans = [tuple(int(v) for v in p.split("x")) for p in spec.split(",") if p]
+    sets = [W.make_inputs(w, device=dev, layer=i) for i in range(2)]
+    outs = [torch.empty_like(s["x"]) for s in sets]
+    kmax = max(k for _, k in plans)
+    ws = torch.empty(ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim, nchunks=kmax) + 256,
+                     dtype=torch.uint8, device=dev)
+
+    def run(G, K, i, phase):
+        s = sets[i % 2]
+        ssm.scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], None,
+                     waves_per_group=G, nchunks=K, out=outs[i % 2], workspace=ws, phase=phase)
+
+    G0, K0 = ssm.scan_plan(w.batch, w.seqlen, w.dim)
+    ramp = clock_ramp(lambda i: run(G0, K0, i, 3), ramp_s) if ramp_s > 0 else 0
+    med = lambda v: sorted(v)[len(v) // 2]
+    rows = []
+    for G, K in plans:
+        for base, name in ((0, "two-launch"), (4, "three-pass")):
+            for i in range(10):
+                run(G, K, i, base | 3)
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+            for i in range(steps):
+                ev[i][0].record()
+                run(G, K, i, base | 1)
+                ev[i][1].record()
+                run(G, K, i, base | 2)
+                ev[i][2].record()
+            torch.cuda.synchronize()
+            rows.append({"waves_per_group": G, "nchunks": K, "schedule": name,
+                         "first_ms": med([e[0].elapsed_time(e[1]) for e in ev]),
+                         "main_ms": med([e[1].elapsed_time(e[2]) for e in ev]),
+                         "step_ms": med([e[0].elapsed_time(e[2]) for e in ev])})
+    return {"workload": w.name, "steps": steps, "clock_ramp_steps": ramp, "auto_plan": [G0, K0],
+            "plans": rows}
+
+
 def bench_config(w, sets_n: int, steps: int, warmup: int):
     """One scan configuration in its automatic plan: per-step times over
     `sets_n` rotated input sets (so that no step reads what an earlier one
@@ -569,6 +617,9 @@ def main():
                     help="skip the masked-matrix scan with step and decay per head")
     ap.add_argument("--only-scan", action="store_true",
                     help="the headline scan only (for profiler runs)")
+    ap.add_argument("--sweep-plans", default="",
+                    help="only time these chunk plans of the headline scan, e.g. 4x4,4x5,8x2 "
+                         "(waves per group x chunks), under both schedules")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -594,6 +645,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": COPY_BYTES}), flush=True)
+        return
+
+    if args.sweep_plans:
+        print(json.dumps({"plan_sweep": sweep_plans(args.sweep_plans, args.steps,
+                                                    args.ramp_seconds)}), flush=True)
         return
 
     r = bench_scan(args.steps, args.warmup, args.ramp_seconds)

@@ -39,25 +39,43 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 # ALU roofline of the scan element.  Per element (b, t, d, n) the main pass
 # must issue 6 fp32 VALU operations (delta*A, B*x, *1/A, the input-term fma,
 # the update fma, the readout fma) and one transcendental (exp2).  Unit
-# counts: 256 CUs x 4 SIMDs at 2.4 GHz; the published fp32 vector peak
-# 157.3 TFLOP/s = 1024 SIMDs x 2.4 GHz x 32 lanes x 2 (FMA), i.e. 32 fp32
-# lanes per SIMD per clock (two 16-lane VALU issues per clock: the SQ counts
-# dual-issue cycles, SQ_ACTIVE_INST_VALU2); transcendentals at a quarter of
-# that rate.
+# counts: 256 CUs x 4 SIMDs at 2.4 GHz; a SIMD issues a non-packed fp32
+# wave64 instruction in 4 cycles (16 lanes per clock) and an exp2 in 8 (8
+# lanes per clock), as the SQ counters of the scan kernels show
+# (SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU; packed fp32 is not used).  The
+# minimal mix then costs 6 x 4 + 8 = 32 cycles per 64 elements.  The
+# published 157.3 TFLOP/s fp32 vector figure counts 32 lanes per clock
+# (packed fp32, or two VALU instructions issued together): the same mix at
+# that rate costs 6 x 2 + 8 = 20 cycles, reported beside it.
 ALU_OPS_PER_ELEMENT = 7
-SIMDS, CLOCK_HZ, VALU_LANES, TRANS_LANES = 256 * 4, 2.4e9, 32, 8
-ALU_PEAK_ELEMS = SIMDS * CLOCK_HZ / (6 / VALU_LANES + 1 / TRANS_LANES)
+SIMDS, CLOCK_HZ = 256 * 4, 2.4e9
+FP32_CYCLES, TRANS_CYCLES = 4, 8
+ALU_PEAK_ELEMS = SIMDS * CLOCK_HZ * 64 / (6 * FP32_CYCLES + TRANS_CYCLES)
+ALU_PEAK_ELEMS_DUAL = SIMDS * CLOCK_HZ * 64 / (6 * FP32_CYCLES / 2 + TRANS_CYCLES)
 TILE_STEPS = 16  # chunks of the chunked scan start on a multiple of this many steps
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_mamba2p8b_b4_l4096_d5120_traffic.md")
 
 
-def source_hash() -> str:
-    """Hash of the library sources with /* */ and // comments and blank lines
-    removed (a comment edit does not change a kernel; any code edit does)."""
+# Sources that define the chunked scan's kernels and plan (the committed
+# traffic figure of its main pass is tied to these).
+SCAN_SOURCES = ["selective_state_space_44_amd/csrc/ssm_scan.hip",
+                "selective_state_space_44_amd/csrc/ssm_device.h",
+                "selective_state_space_44_amd/csrc/ssm_launch.h",
+                "selective_state_space_44_amd/csrc/ssm_abi.cpp", "include/ssm.h"]
+
+
+def source_hash(files=None) -> str:
+    """Hash of library sources with /* */ and // comments and blank lines
+    removed (a comment edit does not change a kernel; any code edit does):
+    every source by default, or the given files (paths from the repo root)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "selective_state_space_44_amd", "csrc", "*")))
-    for f in files + [os.path.join(ROOT, "include", "ssm.h")]:
+    if files is None:
+        files = sorted(glob.glob(os.path.join(ROOT, "selective_state_space_44_amd", "csrc", "*")))
+        files += [os.path.join(ROOT, "include", "ssm.h")]
+    else:
+        files = [os.path.join(ROOT, f) for f in files]
+    for f in files:
         with open(f, encoding="utf-8") as fh:
             text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
         for line in text.splitlines():
@@ -69,8 +87,9 @@ def source_hash() -> str:
 
 def load_traffic():
     """HBM bytes per launch of the main kernel, from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, when it was taken on the current sources
-    (its ``source_hash`` line matches); None otherwise."""
+    FETCH_SIZE/WRITE_SIZE summary, when it was taken on the current scan
+    sources (its ``source_hash`` line matches source_hash(SCAN_SOURCES));
+    None otherwise."""
     try:
         with open(TRAFFIC_FILE) as f:
             text = f.read()
@@ -78,7 +97,7 @@ def load_traffic():
         return None
     h = re.search(r"^source_hash:\s*(\w+)", text, re.M)
     b = re.search(r"^hbm_bytes_per_launch:\s*(\d+)", text, re.M)
-    if not h or not b or h.group(1) != source_hash():
+    if not h or not b or h.group(1) != source_hash(SCAN_SOURCES):
         return None
     return int(b.group(1))
 
@@ -563,8 +582,7 @@ def bench_decode(sweeps: int):
             ssm.decode_step(l["h"], l["x"], l["delta"], l["A"], l["B"], l["C"], l["D"], l["z"],
                             out=ys[i])
 
-    for _ in range(2):
-        sweep()
+    clock_ramp(lambda i: sweep(), 0.3)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(sweeps)]
     t0 = time.perf_counter()
@@ -617,6 +635,8 @@ def main():
                     help="skip the masked-matrix scan with step and decay per head")
     ap.add_argument("--only-scan", action="store_true",
                     help="the headline scan only (for profiler runs)")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="the decode sweep only (for profiler runs)")
     ap.add_argument("--sweep-plans", default="",
                     help="only time these chunk plans of the headline scan, e.g. 4x4,4x5,8x2 "
                          "(waves per group x chunks), under both schedules")
@@ -645,6 +665,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": COPY_BYTES}), flush=True)
+        return
+
+    if args.only_decode:
+        print(json.dumps({"decode": bench_decode(args.decode_sweeps)}), flush=True)
         return
 
     if args.sweep_plans:
@@ -689,6 +713,10 @@ def main():
             "peak": ALU_OPS_PER_ELEMENT * ALU_PEAK_ELEMS / 1e12,
             "unit": "TOP/s",
             "frac": main_elems / main_s / ALU_PEAK_ELEMS,
+            "peak_basis": "6 fp32 ops at 16 lanes/clk + 1 exp2 at 8 lanes/clk per element, "
+                          "1024 SIMDs x 2.4 GHz",
+            "peak_dual_issue": ALU_OPS_PER_ELEMENT * ALU_PEAK_ELEMS_DUAL / 1e12,
+            "frac_dual_issue": main_elems / main_s / ALU_PEAK_ELEMS_DUAL,
             "traffic": traffic,
             "launch_ms": r["main_ms"],
             "elements_per_launch": main_elems,

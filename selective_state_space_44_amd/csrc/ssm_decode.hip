@@ -79,6 +79,11 @@ __device__ __forceinline__ float var_update(float h, float abar, float k, float 
   return __builtin_fmaf(abar, h, k * bx);
 }
 
+// Batch rows per thread: each thread updates the same (channel, quarter) of
+// kRows consecutive rows, so the channel's A and D are loaded once for all of
+// them and kRows state loads are in flight per lane.
+constexpr int kRows = 2;
+
 template <typename IO, int N, int V>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   constexpr int L = N / 4;  // lanes per channel
@@ -86,9 +91,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const int d = t / L;
   const int q = t % L;
   if (d >= a.dim) return;  // a channel's lanes leave together
-  const int64_t b = a.row0 + blockIdx.y;
-  const size_t ch = (size_t)b * a.dim + d;
-  v4f* hp = reinterpret_cast<v4f*>(a.h) + ch * L + q;
+  const int64_t b0 = a.row0 + (int64_t)blockIdx.y * kRows;
+  // rows of this block (block-uniform; fewer in the last block of a ragged batch)
+  const int nr = (int)(a.batch - b0 < kRows ? a.batch - b0 : kRows);
   // Every load is issued before any result is waited on.  The small shared
   // and per-channel inputs go first and the streamed state (touched once per
   // step, so read and written non-temporally) last; on MI355X this order and
@@ -100,67 +105,94 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   } else {
     A = reinterpret_cast<const v4f*>(a.A)[(size_t)d * L + q];
   }
-  const float4 Bq = Quad<IO>::load(static_cast<const IO*>(a.B) + b * N + 4 * q);
-  const float4 Cq = Quad<IO>::load(static_cast<const IO*>(a.C) + b * N + 4 * q);
-  const float xv = io<IO>::load(static_cast<const IO*>(a.x) + ch);
-  const float dv = io<IO>::load(static_cast<const IO*>(a.delta) + ch);
   // optional inputs are read unconditionally (from a valid stand-in when
   // absent): a branch between loads makes the compiler wait for all of them
   const IO* zsrc = static_cast<const IO*>(a.z ? a.z : a.x);
   const float* dsrc = a.Dskip ? a.Dskip : a.A;
-  float zv = io<IO>::load(zsrc + ch);
   float dload = dsrc[d];
-  asm volatile("" : "+v"(zv), "+v"(dload));  // keep both loads here, unconditional
-  v4f h = __builtin_nontemporal_load(hp);
-  const float Dd = a.Dskip ? dload : 0.0f;
-  const float dl = dv * kLog2e;
-
-  if constexpr (V == 0) {
-    h.x = zoh_update(h.x, A.x, __builtin_amdgcn_rcpf(A.x), dl, dv, Bq.x * xv);
-    h.y = zoh_update(h.y, A.y, __builtin_amdgcn_rcpf(A.y), dl, dv, Bq.y * xv);
-    h.z = zoh_update(h.z, A.z, __builtin_amdgcn_rcpf(A.z), dl, dv, Bq.z * xv);
-    h.w = zoh_update(h.w, A.w, __builtin_amdgcn_rcpf(A.w), dl, dv, Bq.w * xv);
-  } else if constexpr (V & kDecScalarA) {
-    // one exp and one coefficient for the channel's states
-    const float abar = fast_exp2(dl * A.x);
-    const float k = (V & kDecEuler) ? dv
-                    : (A.x != 0.0f ? (abar - 1.0f) * __builtin_amdgcn_rcpf(A.x) : dv);
-    h.x = var_update(h.x, abar, k, Bq.x * xv);
-    h.y = var_update(h.y, abar, k, Bq.y * xv);
-    h.z = var_update(h.z, abar, k, Bq.z * xv);
-    h.w = var_update(h.w, abar, k, Bq.w * xv);
-  } else {  // Euler with A per state
-    h.x = var_update(h.x, fast_exp2(dl * A.x), dv, Bq.x * xv);
-    h.y = var_update(h.y, fast_exp2(dl * A.y), dv, Bq.y * xv);
-    h.z = var_update(h.z, fast_exp2(dl * A.z), dv, Bq.z * xv);
-    h.w = var_update(h.w, fast_exp2(dl * A.w), dv, Bq.w * xv);
+  float4 Bq[kRows], Cq[kRows];
+  float xv[kRows], dv[kRows], zv[kRows];
+  v4f h[kRows];
+  v4f* hp[kRows];
+  size_t ch[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int64_t b = b0 + (r < nr ? r : 0);  // rows past the batch repeat row b0 (not stored)
+    ch[r] = (size_t)b * a.dim + d;
+    hp[r] = reinterpret_cast<v4f*>(a.h) + ch[r] * L + q;
+    Bq[r] = Quad<IO>::load(static_cast<const IO*>(a.B) + b * N + 4 * q);
+    Cq[r] = Quad<IO>::load(static_cast<const IO*>(a.C) + b * N + 4 * q);
+    xv[r] = io<IO>::load(static_cast<const IO*>(a.x) + ch[r]);
+    dv[r] = io<IO>::load(static_cast<const IO*>(a.delta) + ch[r]);
+    zv[r] = io<IO>::load(zsrc + ch[r]);
   }
-  __builtin_nontemporal_store(h, hp);
+  asm volatile("" : "+v"(dload));  // keep the load here, unconditional
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    asm volatile("" : "+v"(zv[r]));
+    h[r] = __builtin_nontemporal_load(hp[r]);
+  }
+  const float Dd = a.Dskip ? dload : 0.0f;
+  v4f iA;
+  if constexpr (V == 0) {
+    iA = v4f{__builtin_amdgcn_rcpf(A.x), __builtin_amdgcn_rcpf(A.y), __builtin_amdgcn_rcpf(A.z),
+             __builtin_amdgcn_rcpf(A.w)};
+  }
 
-  float p = Cq.x * h.x;
-  p = __builtin_fmaf(Cq.y, h.y, p);
-  p = __builtin_fmaf(Cq.z, h.z, p);
-  p = __builtin_fmaf(Cq.w, h.w, p);
-  p += quad_swap<0xB1>(p);
-  p += quad_swap<0x4E>(p);
-  if constexpr (L >= 8) p += row_swap<0x141>(p);  // lanes i and 7 - i: the other quad
-  if constexpr (L >= 16) p += row_swap<0x140>(p);  // lanes i and 15 - i: the other half row
-  if constexpr (L >= 32) p += __shfl_xor(p, 16, kWave);
-  if (q == 0) {
-    const float pre = __builtin_fmaf(Dd, xv, p);
-    io<IO>::store(static_cast<IO*>(a.y) + ch, a.z ? pre * silu(zv) : pre);
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    if (r >= nr) break;
+    const float dl = dv[r] * kLog2e;
+    v4f& hr = h[r];
+    const float x = xv[r];
+    if constexpr (V == 0) {
+      hr.x = zoh_update(hr.x, A.x, iA.x, dl, dv[r], Bq[r].x * x);
+      hr.y = zoh_update(hr.y, A.y, iA.y, dl, dv[r], Bq[r].y * x);
+      hr.z = zoh_update(hr.z, A.z, iA.z, dl, dv[r], Bq[r].z * x);
+      hr.w = zoh_update(hr.w, A.w, iA.w, dl, dv[r], Bq[r].w * x);
+    } else if constexpr (V & kDecScalarA) {
+      // one exp and one coefficient for the channel's states
+      const float abar = fast_exp2(dl * A.x);
+      const float k = (V & kDecEuler) ? dv[r]
+                      : (A.x != 0.0f ? (abar - 1.0f) * __builtin_amdgcn_rcpf(A.x) : dv[r]);
+      hr.x = var_update(hr.x, abar, k, Bq[r].x * x);
+      hr.y = var_update(hr.y, abar, k, Bq[r].y * x);
+      hr.z = var_update(hr.z, abar, k, Bq[r].z * x);
+      hr.w = var_update(hr.w, abar, k, Bq[r].w * x);
+    } else {  // Euler with A per state
+      hr.x = var_update(hr.x, fast_exp2(dl * A.x), dv[r], Bq[r].x * x);
+      hr.y = var_update(hr.y, fast_exp2(dl * A.y), dv[r], Bq[r].y * x);
+      hr.z = var_update(hr.z, fast_exp2(dl * A.z), dv[r], Bq[r].z * x);
+      hr.w = var_update(hr.w, fast_exp2(dl * A.w), dv[r], Bq[r].w * x);
+    }
+    __builtin_nontemporal_store(hr, hp[r]);
+
+    float p = Cq[r].x * hr.x;
+    p = __builtin_fmaf(Cq[r].y, hr.y, p);
+    p = __builtin_fmaf(Cq[r].z, hr.z, p);
+    p = __builtin_fmaf(Cq[r].w, hr.w, p);
+    p += quad_swap<0xB1>(p);
+    p += quad_swap<0x4E>(p);
+    if constexpr (L >= 8) p += row_swap<0x141>(p);  // lanes i and 7 - i: the other quad
+    if constexpr (L >= 16) p += row_swap<0x140>(p);  // lanes i and 15 - i: the other half row
+    if constexpr (L >= 32) p += __shfl_xor(p, 16, kWave);
+    if (q == 0) {
+      const float pre = __builtin_fmaf(Dd, x, p);
+      io<IO>::store(static_cast<IO*>(a.y) + ch[r], a.z ? pre * silu(zv[r]) : pre);
+    }
   }
 }
 
 template <int N, int V>
 hipError_t launch_decode_n(const DecodeArgs& args, bool io_bf16, hipStream_t stream) {
   const int64_t threads = (int64_t)args.dim * (N / 4);  // per batch row
-  constexpr int64_t kMaxRows = 65535;              // grid y extent per launch
+  constexpr int64_t kMaxRows = 65535;              // rows per launch (grid y <= 65535)
   for (int64_t r0 = 0; r0 < args.batch; r0 += kMaxRows) {
     DecodeArgs a = args;
     a.row0 = r0;
     const int64_t rows = args.batch - r0 < kMaxRows ? args.batch - r0 : kMaxRows;
-    const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)rows);
+    a.batch = r0 + rows;  // last row (exclusive) of this launch
+    const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)((rows + kRows - 1) / kRows));
     if (io_bf16)
       hipLaunchKernelGGL((decode_step_kernel<bf16, N, V>), grid, dim3(256), 0, stream, a);
     else

@@ -81,3 +81,24 @@ def test_decode_edge_cases():
         ssm.decode_step(h, torch.zeros(2, 8, device=DEV), torch.zeros(2, 8, device=DEV),
                         torch.zeros(8, 4, device=DEV), torch.zeros(2, 4, device=DEV),
                         torch.zeros(2, 4, device=DEV))
+
+
+@pytest.mark.parametrize("batch", [1, 2, 5])
+@pytest.mark.parametrize("variant", ["zoh", "a_per_channel", "euler"])
+def test_decode_row_pairs(batch, variant):
+    """Each thread steps two batch rows; odd batches leave the last pair with
+    one row, whose partner must be neither written nor stored.  Checked
+    against the oracle's scan of length 1 from the resident state."""
+    inp = W.make_inputs(W.DECODE_64L, device=DEV, batch=batch, dim=200)
+    if variant == "a_per_channel":
+        inp["A"] = W.make_channel_A(W.DECODE_64L, device=DEV, dim=200)
+    disc = "euler" if variant == "euler" else "zoh"
+    h = inp["h"].clone()
+    y = ssm.decode_step(h, inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                        inp["z"], discretization=disc)
+    torch.cuda.synchronize()
+    seq = {k: inp[k][:, None] for k in ("x", "delta", "z", "B", "C")}
+    y_ref, h_ref = parity.oracle_scan(dict(seq, A=inp["A"], D=inp["D"], h0=inp["h"]),
+                                      discretization=disc)
+    parity.check_y(parity.to_f64(y), y_ref[:, 0], torch.bfloat16)
+    parity.check_state(parity.to_f64(h), h_ref)

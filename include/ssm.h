@@ -347,8 +347,8 @@ int ssm_decode_step_ex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
  * `headdim` consecutive channels, computed in the masked-matrix form on the
  * matrix cores (ihouse article, "Mambaの進化の道のり": with A reduced to a
  * scalar, most of the SSM's work is a masked matrix multiplication; paperlens
- * tutorial, "計算量: 系列長との付き合い方": the recurrence composes chunk by
- * chunk).  Channel d = h * headdim + p of head h uses
+ * tutorial, "代償と、それを払う方法（並列スキャン）": the recurrence composes
+ * chunk by chunk).  Channel d = h * headdim + p of head h uses
  *   delta[b,t,d] = dt[b,t,h]  and  A[d, n] = A[h]  for every state n,
  * and otherwise the recurrence, readout, skip and gate of ssm_scan_fwd:
  *   h_t = exp(dt_t A) h_{t-1} + coef_t x_t B_t,   y_t = (C_t . h_t + D x_t) SiLU(z_t),
@@ -380,7 +380,7 @@ int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
  * ssm_ssd_fwd with the sequence cut into segments that separate blocks run:
  * a state-only pass gives each segment's end state from a zero state and its
  * decay, a carry composes them in order (the recurrence composes segment by
- * segment: paperlens tutorial, "計算量: 系列長との付き合い方"), and the main
+ * segment: paperlens tutorial, "代償と、それを払う方法（並列スキャン）"), and the main
  * pass starts every segment from its entering state.  This gives a few
  * (batch row, head) pairs, e.g. one long sequence, enough blocks to fill the
  * chip, at the price of the state-only pass over all segments but the last.
@@ -416,10 +416,13 @@ int64_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nhead
  *   - bf16 I/O, headdim 64, dstate 64 or 128, at most 65535 32-step chunks:
  *     the masked-matrix form on the matrix cores, every 32-step chunk
  *     independent (ihouse article on Mamba-3, section on Mamba's evolution:
- *     the scalar-decay SSM as masked matrix products).  A state-only walk
- *     stores the state entering every chunk, a per-chunk pass and a reverse
- *     carry the adjoint leaving every chunk, and one kernel per (group of 16
- *     heads, chunk, batch row) forms all gradients of the chunk from them;
+ *     the scalar-decay SSM as masked matrix products).  One launch runs two
+ *     walks over the chunks per (half head, batch row): forward from h0,
+ *     storing the state entering every chunk, and backward from dh_last,
+ *     storing the adjoint leaving every chunk (what reaches the start is
+ *     dh0).  Then one kernel per (group of 16 heads, chunk, batch row) forms
+ *     all gradients of the chunk from them, and small passes sum dB, dC over
+ *     the head groups and dA, dD over (batch row, chunk);
  *     the gradient of each step's log-decay is assembled inside its chunk
  *     from the chunk's masked matrices and its two boundary states (no
  *     prefix over the sequence).  Workspace: two fp32 states per chunk,
@@ -440,8 +443,11 @@ int64_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nhead
  *                 fp32, NULL => not written.  dh0 : as h0, NULL => not written.
  *   workspace   : at least ssm_ssd_bwd_workspace_bytes(...) bytes.
  * io_dtype fp32 or bf16, any headdim, dstate 16, 32, 64 or 128 (other:
- * SSM_ERR_UNSUPPORTED).  Deterministic.  Outputs must not alias inputs, each
- * other or the workspace.  Returns an SSM_* status.
+ * SSM_ERR_UNSUPPORTED).  Batches of more than 65535 rows, and more than 65535
+ * chunks of the per-channel path, return SSM_ERR_UNSUPPORTED (the forward
+ * splits such batches into launches; the backward does not).  Deterministic.
+ * Outputs must not alias inputs, each other or the workspace.  Returns an
+ * SSM_* status.
  */
 int ssm_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                 int64_t dstate, int io_dtype, int discretization, const void *x,

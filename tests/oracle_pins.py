@@ -122,12 +122,16 @@ def pin_zoh_matches_ode(lib):
 # Recurrence against the convolution form (constant delta, B, C)
 # --------------------------------------------------------------------------
 def _conv_form(A, B, C, delta, x):
-    """y_t = sum_{k<=t} K_k x_{t-k},  K_k = C . (Abar^k * Bbar)."""
-    Abar = np.exp(delta * A)
-    Bbar = (Abar - 1.0) / A * B
+    """Output of the time-invariant system as a causal convolution: the
+    impulse response at lag k is K_k = sum_n C_n Abar_n^k Bbar_n, and y is
+    the first L terms of the full convolution of x with K."""
     L = len(x)
-    K = np.array([C @ (Abar ** k * Bbar) for k in range(L)])
-    return np.array([K[: t + 1][::-1] @ x[: t + 1] for t in range(L)])
+    gain = C * B * np.expm1(delta * A) / A                   # C_n Bbar_n
+    decay = np.exp(delta * A)                                 # Abar_n
+    lags = np.ones((L, len(A)))                               # Abar_n^k, k = 0 .. L-1
+    lags[1:] = decay
+    lags = np.cumprod(lags, axis=0)
+    return np.convolve(x, lags @ gain)[:L]
 
 
 def _scan_const(lib, A, B, C, delta, x):

@@ -418,6 +418,38 @@ def bench_variants(steps: int, warmup: int):
     return {"workload": w.name, **res}
 
 
+def bench_ssd_forward(steps: int, warmup: int):
+    """The masked-matrix forward alone at the Mamba-2-like layer (two input
+    sets alternated), for profiler runs."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.SSD_2P7B
+    dev = "cuda:0"
+    sets = [W.make_ssd_inputs(w, device=dev, layer=i) for i in range(2)]
+    outs = [torch.empty_like(s["x"]) for s in sets]
+
+    def step(i):
+        f = sets[i % 2]
+        ssm.ssd_scan(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
+                     out=outs[i % 2])
+
+    clock_ramp(step, 0.3)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
+            "unit": "elements/s"}
+
+
 def bench_ssd(steps: int, warmup: int):
     """The scan with step and decay shared per head, in its masked-matrix form
     on the matrix cores (``ssm_ssd_fwd``), at a Mamba-2-like layer: batch 4,
@@ -635,6 +667,8 @@ def main():
                     help="skip the masked-matrix scan with step and decay per head")
     ap.add_argument("--only-scan", action="store_true",
                     help="the headline scan only (for profiler runs)")
+    ap.add_argument("--only-ssd", action="store_true",
+                    help="the masked-matrix scan's forward only (for profiler runs)")
     ap.add_argument("--only-decode", action="store_true",
                     help="the decode sweep only (for profiler runs)")
     ap.add_argument("--sweep-plans", default="",
@@ -665,6 +699,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": COPY_BYTES}), flush=True)
+        return
+
+    if args.only_ssd:
+        print(json.dumps({"ssd": bench_ssd_forward(args.steps, args.warmup)}), flush=True)
         return
 
     if args.only_decode:

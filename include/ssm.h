@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 /* Values of the io_dtype arguments. */
 #define SSM_DTYPE_F32 0
@@ -366,15 +366,23 @@ int ssm_decode_step_ex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
  * ssm_scan_fwd_ex).  Products run on bf16 matrix cores with fp32
  * accumulation; operands that are not bf16 inputs (masked weights, state,
  * weighted inputs) are split into two bf16 parts, so results carry fp32-level
- * accuracy (relative error ~1e-5).  No workspace.  Outputs must not alias
- * inputs (nor each other); seqlen == 0 sets h_last to h0 (or zeros); batch
- * == 0 or nheads == 0 is a no-op.  Returns an SSM_* status.
+ * accuracy (relative error ~1e-5).
+ *   workspace : device memory of at least ssm_ssd_fwd_workspace_bytes(...,
+ *               nsplit = 1) bytes, owned by the caller: per 64-step chunk of
+ *               each batch row, the lower-triangular tiles of C B^T and B^T
+ *               (which every head reads), written before the scan; its
+ *               contents on entry do not matter.  NULL or too small (with
+ *               seqlen > 0) => SSM_ERR_WORKSPACE.
+ * Outputs must not alias inputs (nor each other, nor the workspace); seqlen
+ * == 0 sets h_last to h0 (or zeros); batch == 0 or nheads == 0 is a no-op.
+ * Returns an SSM_* status.
  */
 int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                 int64_t dstate, int io_dtype, int discretization, const void *x,
                 const void *dt, const float *A, const void *B, const void *C,
                 const float *Dskip, const void *z, const float *h0, void *y,
-                float *h_last, void *stream);
+                float *h_last, void *workspace, size_t workspace_bytes,
+                void *stream);
 
 /*
  * ssm_ssd_fwd with the sequence cut into segments that separate blocks run:
@@ -387,8 +395,9 @@ int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
  *   nsplit    : number of segments; 0 => automatic (none when there are at
  *               least 640 blocks of (half head, batch row), else about 1280
  *               blocks, no segment shorter than 256 steps); 1 => ssm_ssd_fwd.
- *   workspace : at least ssm_ssd_fwd_workspace_bytes(..., nsplit) bytes (may
- *               be NULL when that is 0).
+ *   workspace : at least ssm_ssd_fwd_workspace_bytes(..., nsplit) bytes: the
+ *               per-chunk products of ssm_ssd_fwd plus, with segments, each
+ *               segment's end state, entering state and decay.
  * Other arguments, results and errors as ssm_ssd_fwd.
  */
 int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,

@@ -65,7 +65,8 @@ SIGNATURES = {
     "ssm_scan_bwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _int]),
     "ssm_scan_bwd": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _int, _int]
                      + [_vp] * 15 + [_vp, _sz, _vp]),
-    "ssm_ssd_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 10 + [_vp]),
+    "ssm_ssd_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 10
+                    + [_vp, _sz, _vp]),
     "ssm_ssd_fwd_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _i64, _int]),
     "ssm_ssd_fwd_planned": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int] + [_vp] * 10
                             + [_int, _vp, _sz, _vp]),

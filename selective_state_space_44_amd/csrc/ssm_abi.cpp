@@ -438,25 +438,24 @@ int ssm_decode_step(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, fl
 namespace {
 
 // Sequence segments of the per-head scan.  With at least kSsdFullBlocks
-// blocks (2.5 per CU) none; with fewer, enough for about kSsdSplitBlocks
-// (measured on MI355X, 80 heads of 64 channels, 128 states: one sequence of
-// 16384 steps 0.87 ms unsplit, 0.60 at 640 blocks, 0.55 at 1280; two of 8192
-// best at 1280 blocks; four of 4096 best unsplit), none shorter than
-// kSsdMinSeg steps.  nsplit > 0 asks for that many.  Segments are whole
-// 32-step chunks.  Returns the number of segments and their length.
+// blocks (2.5 per CU) none; with fewer, enough for about kSsdSplitBlocks,
+// none shorter than kSsdMinSeg steps.  nsplit > 0 asks for that many.
+// Segments are whole chunks of ssm::kSsdChunk steps.  Returns the number of
+// segments and their length.
 constexpr int64_t kSsdFullBlocks = 640;
 constexpr int64_t kSsdSplitBlocks = 1280;
 constexpr int64_t kSsdMinSeg = 256;
 int ssd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int nsplit, int64_t* seg_len) {
+  constexpr int64_t Q = ssm::kSsdChunk;
   int64_t k = nsplit;
   if (k <= 0) {
     const int64_t blocks = std::max<int64_t>(1, 2 * nheads * batch);
     k = blocks >= kSsdFullBlocks ? 1 : (kSsdSplitBlocks + blocks - 1) / blocks;
     k = std::min<int64_t>(k, std::max<int64_t>(1, seqlen / kSsdMinSeg));
   }
-  k = std::max<int64_t>(1, std::min<int64_t>({k, (seqlen + 31) / 32, kMaxGridYZ}));
+  k = std::max<int64_t>(1, std::min<int64_t>({k, (seqlen + Q - 1) / Q, kMaxGridYZ}));
   int64_t len = (seqlen + k - 1) / k;
-  len = std::max<int64_t>(32, (len + 31) / 32 * 32);
+  len = std::max<int64_t>(Q, (len + Q - 1) / Q * Q);
   *seg_len = len;
   return (int)std::max<int64_t>(1, (seqlen + len - 1) / len);
 }
@@ -657,9 +656,11 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
 int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                 int io_dtype, int discretization, const void* x, const void* dt, const float* A,
                 const void* B, const void* C, const float* Dskip, const void* z,
-                const float* h0, void* y, float* h_last, void* stream) {
+                const float* h0, void* y, float* h_last, void* workspace,
+                size_t workspace_bytes, void* stream) {
   return ssm_ssd_fwd_planned(batch, seqlen, nheads, headdim, dstate, io_dtype, discretization, x,
-                             dt, A, B, C, Dskip, z, h0, y, h_last, 1, nullptr, 0, stream);
+                             dt, A, B, C, Dskip, z, h0, y, h_last, 1, workspace, workspace_bytes,
+                             stream);
 }
 
 int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
@@ -670,7 +671,7 @@ int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nhead
   if (batch == 0 || seqlen == 0 || nheads == 0) return 0;
   int64_t len;
   const int K = ssd_plan(batch, seqlen, nheads, nsplit, &len);
-  return (int64_t)ssm::ssd_workspace_bytes(batch, nheads * headdim, nheads, dstate, K);
+  return (int64_t)ssm::ssd_layout(batch, seqlen, nheads * headdim, nheads, dstate, K).total;
 }
 
 int ssm_ssd_fwd_planned(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
@@ -711,23 +712,23 @@ int ssm_ssd_fwd_planned(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
     return SSM_ERR_INVALID_ARG;
   int64_t seg_len;
   const int K = ssd_plan(batch, seqlen, nheads, nsplit, &seg_len);
-  const size_t need = ssm::ssd_workspace_bytes(batch, dim, nheads, dstate, K);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
-    for (const void* in : ins)
-      if (in && in == workspace) return SSM_ERR_INVALID_ARG;
-    if (workspace == y || workspace == (void*)h_last) return SSM_ERR_INVALID_ARG;
-  }
+  const ssm::SsdLayout l = ssm::ssd_layout(batch, seqlen, dim, nheads, dstate, K);
+  if (!workspace || workspace_bytes < l.total) return SSM_ERR_WORKSPACE;
+  for (const void* in : ins)
+    if (in && in == workspace) return SSM_ERR_INVALID_ARG;
+  if (workspace == y || workspace == (void*)h_last) return SSM_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(workspace);
   ssm::SsdArgs a{};
+  a.nck = (seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk;
+  a.ws_cp = base + l.cp_off;
+  a.ws_bt = base + l.bt_off;
+  a.ws_mt = reinterpret_cast<float*>(base + l.mt_off);
   a.nseg = K;
   a.seg_len = seg_len;
   if (K > 1) {
-    auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
-    const size_t st = align((size_t)batch * K * dim * dstate * sizeof(float));
-    char* base = static_cast<char*>(workspace);
-    a.ws_hloc = reinterpret_cast<float*>(base);
-    a.ws_hin = reinterpret_cast<float*>(base + st);
-    a.ws_dlog = reinterpret_cast<float*>(base + 2 * st);
+    a.ws_hloc = reinterpret_cast<float*>(base + l.hloc_off);
+    a.ws_hin = reinterpret_cast<float*>(base + l.hin_off);
+    a.ws_dlog = reinterpret_cast<float*>(base + l.dlog_off);
   }
   a.x = x;
   a.dt = dt;

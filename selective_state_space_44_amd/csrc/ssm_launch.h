@@ -180,6 +180,7 @@ hipError_t launch_scan_wide(const ScanArgs& a, int dstate, bool io_bf16, hipStre
 // Scan with the step and decay rate shared by each head of 64 channels, in
 // its masked-matrix form on the matrix cores (ssm_ssd.hip).  bf16 x, dt, B,
 // C, z, y; fp32 A [nheads], Dskip [dim], h0 / h_last [batch, dim, dstate].
+constexpr int kSsdChunk = 32;  // steps per chunk of the masked-matrix scan
 struct SsdArgs {
   const void* x;       // [batch, seqlen, dim]
   const void* dt;      // [batch, seqlen, nheads]
@@ -197,18 +198,30 @@ struct SsdArgs {
   int nheads;
   int dim;             // nheads * 64
   int euler;
+  // Per (batch row, chunk) operands shared by every head, written by a
+  // pre-pass: C with its states reordered, B^T and the lower-triangular
+  // tiles of C B^T.
+  int64_t nck;         // ceil(seqlen / kSsdChunk)
+  void* ws_cp;         // [batch, nck, kSsdChunk, dstate] bf16
+  void* ws_bt;         // [batch, nck, dstate, kSsdChunk] bf16
+  float* ws_mt;        // [batch, nck, 3, 64, 4]
   // Sequence segments run by separate blocks (nseg > 1): a state-only pass
   // writes each segment's end state from zero and the log2 of its decay, a
   // carry composes them in order, and the main pass starts every segment from
   // its entering state.
   int nseg;            // 1 = one block walks the whole sequence
-  int64_t seg_len;     // steps per segment, a multiple of 32
+  int64_t seg_len;     // steps per segment, a multiple of kSsdChunk
   float* ws_hloc;      // [batch, nseg, dim, dstate]
   float* ws_hin;       // [batch, nseg, dim, dstate] (segment 0 unused)
   float* ws_dlog;      // [batch, nseg, nheads]
 };
-size_t ssd_workspace_bytes(int64_t batch, int64_t dim, int64_t nheads, int64_t dstate,
-                           int nseg);
+// Workspace of the masked-matrix scan (byte offsets; segment buffers only
+// when nseg > 1).
+struct SsdLayout {
+  size_t cp_off, bt_off, mt_off, hloc_off, hin_off, dlog_off, total;
+};
+SsdLayout ssd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t nheads, int64_t dstate,
+                     int nseg);
 
 // Backward of the per-head scan in its masked-matrix form, chunk-parallel
 // (64-channel heads, 64 or 128 states, bf16 I/O).  Workspace carved by
@@ -251,7 +264,6 @@ struct SsdBwdArgs {
 constexpr int kSsdBwdHeadsPerBlock = 16;
 hipError_t launch_ssd_bwd_mm(const SsdBwdArgs& a, hipStream_t stream);
 bool ssd_supported(int64_t headdim, int64_t dstate);
-size_t ssd_smem_bytes(int64_t dstate);
 hipError_t launch_ssd(const SsdArgs& a, int dstate, hipStream_t stream);
 
 // Enqueue the seqlen == 0 case: h_last = h0 (or zeros).

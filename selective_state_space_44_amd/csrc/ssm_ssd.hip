@@ -10,40 +10,38 @@
 // the chunk and coef_t the input coefficient of step t ((exp(a dt_t) - 1)/a
 // for the zero-order hold, dt_t for the Euler rule, dt_t at a = 0):
 //
-//   y_i   = sum_{j<=i} (C_i . B_j) exp(s_i - s_j) coef_j x_j      in-chunk part
-//         + exp(s_i) C_i . h_in                                   entering state
+//   y_i   = sum_{j<=i} M_ij exp(s_i - s_j) coef_j x_j  +  exp(s_i) C_i . h_in
 //   h_out = exp(s_last) h_in + sum_j exp(s_last - s_j) coef_j x_j B_j^T
 //
-// and y = (y + D x) * SiLU(z).  Each sum is a matrix product:
-//   * M = C B^T per chunk (32 x 32, contraction over the N states),
-//   * Y_in = P X with P = M masked to j <= i and weighted by
-//     exp(s_i - s_j) coef_j (contraction over the chunk's steps),
-//   * Y_state = C h_in^T (contraction over the states),
-//   * h_out^T = B^T (w x) with w_t = exp(s_last - s_t) coef_t (contraction
-//     over the steps).
+// with M = C B^T (Q x Q, contraction over the N states), then
+// y = (y + D x) * SiLU(z).  Four products per chunk: M (the same for every
+// head of a batch row), P X with P = M masked to j <= i and weighted
+// (contraction over the steps), C h_in^T (over the states) and B^T (w x) with
+// w_t = exp(s_last - s_t) coef_t (over the steps).
 //
-// Organisation: one block per (half head of 32 channels, batch row) walks
-// 32-step chunks in order, so the state never leaves the registers and no
-// carry pass exists.  Its 4 waves are 2 channel tiles x 2 state halves: wave
-// (pt, nh) holds the state h[n][p] of channels p = 16pt..16pt+15 and states
-// n in half nh as N/32 MFMA accumulator tiles, updates them, and computes
-// C h over its half for the chunk's two 16-step row tiles; it finishes row
-// tile nh (its partial plus the other half's, passed through LDS).  The
-// chunk's 32 x 32 matrix P has three lower-triangular 16 x 16 tiles, one on
-// each of waves 0..2, passed through LDS.  At the Mamba-2-like shape (4 x 80
-// heads) this makes 640 blocks of 32.5 KB LDS (N = 128), all resident at once
-// (2-3 per CU).
+// Two kernels:
+//  * ssd_prep_kernel, one block per (batch row, chunk), writes what every
+//    head of the row reads: the three lower-triangular 16 x 16 tiles of M,
+//    B^T (states as rows, the chunk's steps contiguous) and C with its states
+//    in the order the C h_in product takes them.
+//  * ssd_scan_kernel, one block per (half head of 32 channels, batch row),
+//    walks the chunks in order, so the state never leaves the registers.
+//    Its 4 waves are 2 channel tiles x 2 state halves: wave (pt, nh) holds
+//    h[n][p] for 16 channels and N/2 states as MFMA accumulator tiles.
 //
-// Data movement per chunk: the chunk's x, z (32 steps x 32 channels), B, C
-// (32 steps x N) and dt are loaded into registers two chunks ahead and
-// staged in LDS in their natural layout.  The operand layouts the
-// contractions need -- x and B with the step index contiguous, x and z in the
-// result layout of the epilogue -- come from products with an identity
-// matrix (see identity_pick), and the outputs are transposed the same way
-// for 8-byte stores.  The decay exponents of a chunk (a prefix sum over its
-// steps) are computed one chunk ahead by the wave that has no P tile.  Three
-// barriers per chunk: staging written; P and the partial C h written; (next
-// chunk) all reads done.
+// One barrier per chunk.  Phase A: waves 0..2 build one tile of P each from
+// M, wave 3 the next chunk's per-step values (decay exponents, coefficients,
+// weights); every wave computes C h_in over its state half for the chunk's
+// two 16-step row tiles, keeps row tile nh and passes the other to the wave
+// holding the other state half of the same channels.  Barrier.  Phase B:
+// each wave finishes its row tile (P X, the two halves of C h_in, skip,
+// gate, store) and updates its part of the state.  C, B^T and x of a chunk
+// are copied into LDS by the buffer unit (buffer_load ... lds, 1 KB per wave
+// and transfer) one chunk ahead, double-buffered; P and the partial sums are
+// double-buffered and the per-step values triple-buffered, so a wave can run
+// the next chunk's phase A while others still finish phase B.  In LDS the
+// 16-byte pieces of each row are permuted by a function of the row, so that
+// the operand reads of 16 consecutive rows fall on distinct banks.
 //
 // Precision: B, C and x are bf16 inputs, exact as MFMA operands.  The other
 // operands -- the masked weights P, the state h and the weighted inputs w x --
@@ -52,18 +50,22 @@
 // product carries ~16 significant bits and all sums are fp32.  The state
 // stays fp32 between chunks.
 //
-// MFMA lane layouts used (v_mfma_f32_16x16x32_bf16 only; 16 x 16 tiles, lane
-// l, g = l / 16):
+// MFMA lane layouts (v_mfma_f32_16x16x32_bf16 only; 16 x 16 tiles, lane l,
+// g = l / 16):
 //   A operand: row l % 16, k slots 8g..8g+7
 //   B operand: column l % 16, the same k slots
 //   result:    column l % 16, rows 4g..4g+3
-// Only the row / column / result layout matters: a product pairs the k
-// slots of A and B one to one, so any permutation of the contraction index
-// applied to both operands gives the same sum.  The kernel uses that freedom
-// where a result tile becomes the next product's operand without a trip
-// through LDS (the state as the B operand of C h^T, the identity products).
-// The 16x16x16 form is not used: in one compiled schedule the result rows
-// 0-1 of such a product were read before it had completed.
+// A product pairs the k slots of A and B one to one, so any permutation of
+// the contraction index applied to both operands gives the same sum.  The
+// kernels use that freedom so that result tiles become the next product's
+// operand without a trip through LDS: slots 0..3 of lane group g hold
+// contraction indices 4g..4g+3 of a 32-wide step and slots 4..7 the indices
+// 16+4g..16+4g+3 (the rows of two result tiles).  B^T and C in the workspace
+// are stored in that order.  The 16x16x16 form is not used: in one compiled
+// schedule the result rows 0-1 of such a product were read before it had
+// completed.
+
+#include <type_traits>
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -72,43 +74,117 @@
 namespace ssm {
 namespace {
 
-constexpr int kQ = 32;            // steps per chunk
+constexpr int kQ = kSsdChunk;     // steps per chunk (32)
 constexpr int kHD = 64;           // channels per head
 constexpr int kBC = 32;           // channels per block (half a head)
 constexpr int kSsdThreads = 256;  // 4 waves: 2 channel tiles x 2 state halves
-constexpr int kRowT = kQ + 8;     // bf16 per row of P: 80 B, so 8 consecutive
-                                  // rows start on distinct banks
-constexpr int kRowX = kBC + 8;    // bf16 per row of the staged x and z
+constexpr int kTiles = 3;         // lower-triangular tiles (0,0), (1,0), (1,1)
+
+// s_waitcnt immediate: at most n (< 16) vector memory operations in flight,
+// LDS and export counters not waited for.
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15); }
+
+// Slot of 16-byte piece p in a 64-byte LDS row r is p ^ swz4(r): for any 8
+// (and any 16) consecutive rows and a fixed p the slots fall on distinct
+// banks.
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 template <int N>
 struct SsdSmem {
-  static constexpr int kRowN = N + 8;    // bf16 per state-contiguous row
-  alignas(16) uint16_t cs[kQ][kRowN];    // C of the chunk, [t][n]
-  alignas(16) uint16_t bs[kQ][kRowN];    // B, [t][n]
-  alignas(16) uint16_t xs[kQ][kRowX];    // x of the block's channels, [t][p]
-  alignas(16) uint16_t zs[kQ][kRowX];    // z, [t][p]
-  alignas(16) uint16_t pmh[kQ][kRowT];   // masked weights P[i][j], high part
-  alignas(16) uint16_t pml[kQ][kRowT];   // low part
-  // C h over one state half, for the row tile the other half's wave finishes:
-  // [channel tile][row tile][lane][result register]
-  alignas(16) float part[2][2][kWave][4];
-  // per-step values of the chunk (two buffers: the next chunk's are
-  // computed while the current one runs)
-  alignas(16) float s2[2][kQ];     // s_t * log2(e)
-  alignas(16) float coef[2][kQ];   // coef_t
-  alignas(16) float wgt[2][kQ];    // exp(s_last - s_t) coef_t
-  alignas(16) float ein[2][kQ];    // exp(s_t)
+  // C of a chunk (rows of N states in the workspace order); piece p of row t
+  // at slot p ^ (t & (N / 8 - 1))
+  alignas(16) uint16_t cs[2][kQ * N];
+  // B^T of a chunk (rows of 32 steps); piece p of row n at slot p ^ swz4(n)
+  alignas(16) uint16_t bts[2][N * kQ];
+  // x of the block's 32 channels (rows of 64 bytes); slot p ^ swz4(t)
+  alignas(16) uint16_t xs[2][kQ * kBC];
+  // masked weights per tile and lane: {hi q0q1, hi q2q3, lo q0q1, lo q2q3}
+  alignas(16) u32x4_t pm[2][kTiles][kWave];
+  // C h_in over one state half for the other half's wave:
+  // [channel tile][row tile][lane]
+  alignas(16) f32x4_t part[2][2][2][kWave];
+  // per-step values: s_t log2(e), coef_t, w_t, exp(s_t)
+  alignas(16) float ps[3][4][kQ];
 };
 
-// PRE: the state-only pass over segments 0..nseg-2 (no outputs): end state
-// from zero and the log2 of the segment's decay, into the workspace.
+// ---------------------------------------------------------------------------
+// Per (batch row, chunk) operands shared by every head, into the workspace:
+//   ws_mt: [batch][nck][3][64 lanes] f32x4, lane (r, g) of tile (I, J)
+//          holding M[16 I + r][16 J + 4 g + q], q = 0..3
+//   ws_bt: [batch][nck][N][32] bf16, row n holding B[t][n] with step 4g+s at
+//          position 8g + s and step 16+4g+s at 8g + 4 + s (s < 4)
+//   ws_cp: [batch][nck][32][N] bf16, row t holding C[t][n] with state
+//          32k+4g+s at position 32k + 8g + s and 32k+16+4g+s at 32k+8g+4+s
+// Steps past the end of the sequence are zero.
+template <int N>
+__global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs a) {
+  constexpr int kRow = N + 8;  // bf16 per staged row (16-byte pad: distinct banks)
+  __shared__ __align__(16) uint16_t bs[kQ][kRow];
+  __shared__ __align__(16) uint16_t cs[kQ][kRow];
+  const int64_t c = blockIdx.x;
+  const int64_t b = (int64_t)blockIdx.y + a.row0;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t L = a.seqlen, t0 = c * kQ;
+  const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
+  const __amdgpu_buffer_rsrc_t rsb =
+      make_rsrc(static_cast<const uint16_t*>(a.B) + (b * L + t0) * N, rows * N * 2u);
+  const __amdgpu_buffer_rsrc_t rsc =
+      make_rsrc(static_cast<const uint16_t*>(a.C) + (b * L + t0) * N, rows * N * 2u);
+  constexpr int kPer = N / 8;  // 16-byte pieces per row
+  for (int i = tid; i < kQ * kPer; i += 256) {
+    const int t = i / kPer, col = (i % kPer) * 8;
+    const uint32_t off = (uint32_t)(t * N + col) * 2u;
+    *reinterpret_cast<u32x4_t*>(&bs[t][col]) =
+        __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsb, off, 0, 0));
+    *reinterpret_cast<u32x4_t*>(&cs[t][col]) =
+        __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsc, off, 0, 0));
+  }
+  __syncthreads();
+
+  const size_t chunk = (size_t)b * a.nck + c;
+  // M^T tiles: A operand B rows (j), B operand C rows (i) -> m[q] = C_i . B_j
+  // with i = 16 I + r16 (the lane's column), j = 16 J + 4 g + q
+  if (w < kTiles) {
+    const int I = w > 0 ? 1 : 0, J = w == 1 ? 0 : I;
+    f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k)
+      m = mfma_k32(lds128(&bs[16 * J + r16][32 * k + 8 * g]),
+                   lds128(&cs[16 * I + r16][32 * k + 8 * g]), m);
+    reinterpret_cast<f32x4_t*>(a.ws_mt)[(chunk * kTiles + w) * kWave + lane] = m;
+  }
+  // B^T: 16-byte piece gg of row n
+  uint16_t* bt = static_cast<uint16_t*>(a.ws_bt) + chunk * N * kQ;
+  for (int i = tid; i < N * 4; i += 256) {
+    const int n = i >> 2, gg = i & 3;
+    const int tlo = 4 * gg, thi = tlo + 16;
+    const u32x4_t v = {bs[tlo][n] | ((uint32_t)bs[tlo + 1][n] << 16),
+                       bs[tlo + 2][n] | ((uint32_t)bs[tlo + 3][n] << 16),
+                       bs[thi][n] | ((uint32_t)bs[thi + 1][n] << 16),
+                       bs[thi + 2][n] | ((uint32_t)bs[thi + 3][n] << 16)};
+    *reinterpret_cast<u32x4_t*>(bt + (size_t)n * kQ + 8 * gg) = v;
+  }
+  // C reordered: 16-byte piece pc of row t
+  uint16_t* cp = static_cast<uint16_t*>(a.ws_cp) + chunk * kQ * N;
+  for (int i = tid; i < kQ * kPer; i += 256) {
+    const int t = i / kPer, pc = i % kPer;
+    const int lo = 32 * (pc >> 2) + 4 * (pc & 3);
+    *reinterpret_cast<u32x4_t*>(cp + (size_t)t * N + 8 * pc) =
+        cat(lds64(&cs[t][lo]), lds64(&cs[t][lo + 16]));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The chunk walk.  PRE: the state-only pass over segments 0..nseg-2 (no
+// outputs): end state from zero and the log2 of the segment's decay, into
+// the workspace.
 template <int N, bool HAS_Z, bool EULER, bool PRE>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void ssd_scan_kernel(SsdArgs a) {
-  constexpr int NT2 = N / 32;   // state tiles per wave (half of the N/16)
+  constexpr int NT2 = N / 32;   // 16-state tiles per wave (its half of the N)
   constexpr int NK = N / 64;    // 32-state contraction steps per state half
-  constexpr int NB = N / 8;     // B / C columns staged by each thread
-  constexpr int NBV = NB / 8;   // 16-byte pieces of them
+  constexpr int CPW = N / 64;   // 1 KB transfers per wave for C and for B^T
   extern __shared__ __align__(16) unsigned char ssd_smem_raw[];
   SsdSmem<N>& sm = *reinterpret_cast<SsdSmem<N>*>(ssd_smem_raw);
 
@@ -131,7 +207,7 @@ void ssd_scan_kernel(SsdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int pt = w & 1, nh = w >> 1;           // channel tile, state half (= row tile)
+  const int pt = w & 1, nh = w >> 1;  // channel tile, state half (= own row tile)
   const int dim = a.dim;
   const int64_t L = a.seqlen;
   const float Ah = a.A[h];
@@ -141,78 +217,111 @@ void ssd_scan_kernel(SsdArgs a) {
   const int p = 16 * pt + r16;                  // this lane's channel in the block
   const int d = cb + p;
   const float Dp = a.Dskip ? a.Dskip[d] : 0.0f;
-  const int ts = tid & (kQ - 1), cg = tid >> 5;  // staging: step, column group
-  // this block's steps [tb, te)
+  // this block's steps [tb, te), chunks gc0 .. gc_last of the workspace
   const int seg = blockIdx.z;
   const int64_t tb = (int64_t)seg * a.seg_len;
   const int64_t te = tb + a.seg_len < L ? tb + a.seg_len : L;
+  const int64_t gc0 = tb / kQ;
+  const int64_t nck = (te - tb + kQ - 1) / kQ;
+  const int64_t gc_last = gc0 + nck - 1;
   const size_t seg_row = (size_t)b * a.nseg + seg;  // (batch row, segment) of the workspace
   const size_t soff = 16 * nh * NT2 + 4 * g;        // this lane's first state
 
   // state tile j: st[j][q] = h[n = 16 (nh NT2 + j) + 4 g + q][p]
   f32x4_t st[NT2];
-  const float* src = nullptr;
-  if (!PRE) {
-    if (seg > 0)
-      src = a.ws_hin + (seg_row * dim + d) * N + soff;
-    else if (a.h0)
-      src = a.h0 + ((size_t)b * dim + d) * N + soff;
-  }
+  {
+    const float* src = nullptr;
+    if (!PRE) {
+      if (seg > 0)
+        src = a.ws_hin + (seg_row * dim + d) * N + soff;
+      else if (a.h0)
+        src = a.h0 + ((size_t)b * dim + d) * N + soff;
+    }
 #pragma unroll
-  for (int j = 0; j < NT2; ++j)
-    st[j] = src ? *reinterpret_cast<const f32x4_t*>(src + 16 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT2; ++j)
+      st[j] = src ? *reinterpret_cast<const f32x4_t*>(src + 16 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   float dlog = 0.0f;  // PRE: log2 of the segment's decay
 
-  const u32x4_t ipick[2] = {identity_pick(0, r16, g), identity_pick(16, r16, g)};
+  const u32x4_t ipick = identity_pick(16 * pt, r16, g);
   const u32x4_t ipick4 = identity_pick4(r16, g);
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // Staging registers: thread (ts, cg) holds step ts of a chunk -- channels
-  // 4cg..4cg+3 of the block for x and z, states NB cg .. NB cg + NB - 1 of B
-  // and C, and (wave 3, lanes < kQ) dt.  Two sets: the loads of chunk c + 2
-  // are issued while chunk c runs.  Rows past the end of the sequence read as
-  // zero (buffer bounds): steps with dt = 0, which leave the state unchanged,
-  // and whose outputs are not stored.
-  struct Stage {
-    u32x2_t x, z;
-    u32x4_t b[NBV], c[NBV];
-    uint32_t dt;
+  // valid steps of the chunk at t0 (0 past the segment: such loads read zeros)
+  auto rows_at = [&](int64_t t0) {
+    return (uint32_t)(t0 >= te ? 0 : te - t0 < kQ ? te - t0 : (int64_t)kQ);
   };
-  auto fetch = [&](Stage& sg, int64_t t0) {
-    const uint32_t rows = (uint32_t)(te - t0 < kQ ? te - t0 : (int64_t)kQ);
-    if (w == 3) {
-      const __amdgpu_buffer_rsrc_t rsd = make_rsrc(
-          static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows * (uint32_t)H * 2u);
-      sg.dt = lane < kQ
-                  ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)lane * H * 2u + h * 2u, 0, 0)
-                  : 0u;
-    }
-    const uint32_t ox = (uint32_t)ts * (uint32_t)dim * 2u + (uint32_t)(cb + 4 * cg) * 2u;
-    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(
-        static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
-    sg.x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsx, ox, 0, 0));
-    if constexpr (HAS_Z && !PRE) {
-      const __amdgpu_buffer_rsrc_t rsz = make_rsrc(
-          static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
-      sg.z = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsz, ox, 0, 0));
-    }
-    const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(static_cast<const uint16_t*>(a.B) + (b * L + t0) * N, rows * N * 2u);
-    const __amdgpu_buffer_rsrc_t rsc =
-        make_rsrc(static_cast<const uint16_t*>(a.C) + (b * L + t0) * N, rows * N * 2u);
-    const uint32_t ob = (uint32_t)ts * N * 2u + (uint32_t)(NB * cg) * 2u;
+
+  // ---- copies into LDS ------------------------------------------------------
+  // Transfer i of wave w fills LDS bytes [1024 (CPW w + i), + 1024) of a
+  // buffer; lane l the 16 bytes at 16 l of that.  The source piece of each
+  // slot follows the row permutation of the buffer.
+  // C and B^T of chunk gc into buffer `buf`
+  auto copy_cb = [&](int buf, int64_t gc) {
+    const size_t chunk = (size_t)b * a.nck + gc;
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
+        static_cast<const uint16_t*>(a.ws_cp) + chunk * kQ * N, (uint32_t)(kQ * N * 2));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
+        static_cast<const uint16_t*>(a.ws_bt) + chunk * N * kQ, (uint32_t)(N * kQ * 2));
 #pragma unroll
-    for (int j = 0; j < NBV; ++j) {
-      sg.b[j] = __builtin_bit_cast(u32x4_t,
-                                   __builtin_amdgcn_raw_buffer_load_b128(rsb, ob + 16u * j, 0, 0));
-      if constexpr (!PRE)
-        sg.c[j] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsc, ob + 16u * j, 0, 0));
+    for (int i = 0; i < CPW; ++i) {
+      const int pos = 1024 * (CPW * w + i) + 16 * lane;  // byte position in the buffer
+      if constexpr (!PRE) {
+        const int t = pos / (2 * N), slot = (pos >> 4) & (N / 8 - 1);
+        const int pc = slot ^ (t & (N / 8 - 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsc, (__attribute__((address_space(3))) void*)&sm.cs[buf][512 * (CPW * w + i)], 16,
+            (uint32_t)(t * N + 8 * pc) * 2u, 0, 0, 0);
+      }
+      const int n = pos >> 6, pc = ((pos >> 4) & 3) ^ swz4(n);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsb, (__attribute__((address_space(3))) void*)&sm.bts[buf][512 * (CPW * w + i)], 16,
+          (uint32_t)(n * kQ + 8 * pc) * 2u, 0, 0, 0);
     }
   };
-  // wave 3: the chunk's decay exponents (inclusive prefix sum of a * dt over
-  // its steps, lanes < kQ) and per-step weights, into buffer `buf`
-  auto scan = [&](const Stage& sg, int buf) {
-    const float dtv = bf16_bits_to_f32(sg.dt);
+  // x of the chunk at t0 into buffer `buf` (waves 0 and 1, 1 KB each)
+  auto copy_x = [&](int buf, int64_t t0) {
+    if (w < 2) {
+      const __amdgpu_buffer_rsrc_t rsx =
+          make_rsrc(static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim,
+                    rows_at(t0) * (uint32_t)dim * 2u);
+      const int t = 16 * w + (lane >> 2), pc = (lane & 3) ^ swz4(t);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (__attribute__((address_space(3))) void*)&sm.xs[buf][512 * w], 16,
+                                               (uint32_t)(t * dim + cb + 8 * pc) * 2u, 0, 0, 0);
+    }
+  };
+
+  // ---- register loads -------------------------------------------------------
+  // M tile w (waves 0..2) of chunk gc
+  f32x4_t mreg = zero4;
+  auto load_m = [&](int64_t gc) {
+    if (w < kTiles) {
+      const __amdgpu_buffer_rsrc_t rsm = make_rsrc(
+          a.ws_mt + ((size_t)b * a.nck + gc) * kTiles * kWave * 4, (uint32_t)(kTiles * kWave * 16));
+      mreg = __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsm, (uint32_t)lane * 16u, w * kWave * 16, 0));
+    }
+  };
+  // z of row tile nh as the identity A operand: row t, 32 channels
+  u32x4_t zop = {0u, 0u, 0u, 0u};
+  auto load_z = [&](int64_t t0) {
+    const __amdgpu_buffer_rsrc_t rsz = make_rsrc(
+        static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rows_at(t0) * (uint32_t)dim * 2u);
+    zop = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                     rsz, (uint32_t)((16 * nh + r16) * dim + cb + 8 * g) * 2u, 0, 0));
+  };
+  // wave 3: dt of a chunk, lane = step
+  auto load_dt = [&](int64_t t0) -> uint32_t {
+    const __amdgpu_buffer_rsrc_t rsd = make_rsrc(
+        static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows_at(t0) * (uint32_t)H * 2u);
+    return lane < kQ ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)(lane * H + h) * 2u, 0, 0)
+                     : 0u;
+  };
+
+  // ---- per-step values of a chunk (wave 3, lane = step < 32) ----------------
+  auto steps = [&](uint32_t dtbits, int buf) {
+    const float dtv = bf16_bits_to_f32(dtbits);
     float s = dtv * A2;
 #pragma unroll
     for (int o = 1; o < kQ; o <<= 1) {
@@ -222,183 +331,174 @@ void ssd_scan_kernel(SsdArgs a) {
     const float last = __shfl(s, kQ - 1);
     if (lane < kQ) {
       const float cf = coef_is_dt ? dtv : expm1f(dtv * Ah) / Ah;
-      sm.s2[buf][lane] = s;
-      sm.coef[buf][lane] = cf;
-      sm.wgt[buf][lane] = fast_exp2(last - s) * cf;
-      sm.ein[buf][lane] = fast_exp2(s);
+      sm.ps[buf][0][lane] = s;
+      sm.ps[buf][1][lane] = cf;
+      sm.ps[buf][2][lane] = fast_exp2(last - s) * cf;
+      sm.ps[buf][3][lane] = fast_exp2(s);
     }
   };
 
-  const int64_t nck = (te - tb + kQ - 1) / kQ;
-  auto chunk = [&](int64_t c, Stage& cur, const Stage& nxt) {
-    const int64_t t0 = tb + c * kQ;
-    const int buf = (int)(c & 1);
-    __syncthreads();  // every read of the previous chunk's LDS is done
+  // ---- prologue -------------------------------------------------------------
+  uint32_t dtr = 0;
+  copy_cb(0, gc0);
+  copy_x(0, tb);
+  if (w == 3) dtr = load_dt(tb);
+  if constexpr (!PRE) {
+    if constexpr (HAS_Z) load_z(tb);
+    load_m(gc0);
+  }
+  if (w == 3) {
+    steps(dtr, 0);
+    if (nck > 1) dtr = load_dt(tb + kQ);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's copies have landed
+  __syncthreads();
 
-    // ---- stage the chunk in natural layout ----------------------------
-    *reinterpret_cast<u32x2_t*>(&sm.xs[ts][4 * cg]) = cur.x;
-    if constexpr (HAS_Z && !PRE) *reinterpret_cast<u32x2_t*>(&sm.zs[ts][4 * cg]) = cur.z;
+  for (int64_t cc = 0; cc < nck; ++cc) {
+    const int64_t t0 = tb + cc * kQ;
+    const int pb = (int)(cc % 3), mb = (int)(cc & 1);
+
+    // ===== phase A ============================================================
+    if (w == 3 && cc + 1 < nck) steps(dtr, (int)((cc + 1) % 3));
+    [[maybe_unused]] f32x4_t ysown = zero4;  // C h_in over this half, row tile nh
+    if constexpr (!PRE) {
+      // masked weights: tile w of (0,0), (1,0), (1,1)
+      if (w < kTiles) {
+        const int I = w > 0 ? 1 : 0, J = w == 1 ? 0 : I;
+        const float si = sm.ps[pb][0][16 * I + r16];
+        const f32x4_t sj = *reinterpret_cast<const f32x4_t*>(&sm.ps[pb][0][16 * J + 4 * g]);
+        const f32x4_t cj = *reinterpret_cast<const f32x4_t*>(&sm.ps[pb][1][16 * J + 4 * g]);
+        float v[4];
 #pragma unroll
-    for (int j = 0; j < NBV; ++j) {
-      *reinterpret_cast<u32x4_t*>(&sm.bs[ts][NB * cg + 8 * j]) = cur.b[j];
-      if constexpr (!PRE) *reinterpret_cast<u32x4_t*>(&sm.cs[ts][NB * cg + 8 * j]) = cur.c[j];
+        for (int q = 0; q < 4; ++q)
+          v[q] = (I > J || 4 * g + q <= r16) ? mreg[q] * fast_exp2(si - sj[q]) * cj[q] : 0.0f;
+        uint32_t h01, l01, h23, l23;
+        split_bf16(v[0], v[1], h01, l01);
+        split_bf16(v[2], v[3], h23, l23);
+        sm.pm[mb][w][lane] = u32x4_t{h01, h23, l01, l23};
+        // the next chunk's tile into the register just freed
+        __builtin_amdgcn_sched_barrier(0);
+        load_m(gc0 + cc + 1 < gc_last ? gc0 + cc + 1 : gc_last);
+      }
+      // C h_in over this wave's state half, both row tiles; the entering
+      // state as B operands (slots 0..3 = tile 2k, 4..7 = tile 2k + 1)
+      f32x4_t yst[2] = {zero4, zero4};
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        uint32_t hw[4], lw[4];
+        split_bf16(st[2 * k][0], st[2 * k][1], hw[0], lw[0]);
+        split_bf16(st[2 * k][2], st[2 * k][3], hw[1], lw[1]);
+        split_bf16(st[2 * k + 1][0], st[2 * k + 1][1], hw[2], lw[2]);
+        split_bf16(st[2 * k + 1][2], st[2 * k + 1][3], hw[3], lw[3]);
+        const u32x4_t sh = {hw[0], hw[1], hw[2], hw[3]}, sl = {lw[0], lw[1], lw[2], lw[3]};
+        const int pc = nh * (N / 16) + 4 * k + g;  // piece of the C rows
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+          const int t = 16 * I + r16;
+          const u32x4_t co = lds128(&sm.cs[mb][t * N + 8 * (pc ^ (t & (N / 8 - 1)))]);
+          yst[I] = mfma_k32(co, sh, yst[I]);
+          yst[I] = mfma_k32(co, sl, yst[I]);
+        }
+      }
+      sm.part[mb][pt][1 - nh][lane] = nh ? yst[0] : yst[1];
+      ysown = nh ? yst[1] : yst[0];
     }
+    // Every wave's copies of this chunk's operands (issued a chunk ago) have
+    // landed before the barrier: vector memory operations complete in issue
+    // order, and of those issued after the copies at most the last one (the
+    // M tile just loaded, or the z load) may still be in flight.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PRE ? 0 : 1));
     __syncthreads();
 
-    if (c + 2 < nck) fetch(cur, t0 + 2 * kQ);
-
-    if (!PRE && w < 3) {
-      // ---- masked weights P: tiles (0,0), (1,0), (1,1) on waves 0..2 ----
-      const int I = w > 0 ? 1 : 0, J = w == 1 ? 0 : I;
-      // M^T tile: rows j (B rows), columns i (C rows), contraction over states
-      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < N / 32; ++k)
-        m = mfma_k32(lds128(&sm.bs[16 * J + r16][32 * k + 8 * g]),
-                     lds128(&sm.cs[16 * I + r16][32 * k + 8 * g]), m);
-      // m[q] = C_i . B_j with i = 16 I + r16, j = 16 J + 4 g + q
-      const int i = 16 * I + r16;
-      const float si = sm.s2[buf][i];
-      const f32x4_t sj = *reinterpret_cast<const f32x4_t*>(&sm.s2[buf][16 * J + 4 * g]);
-      const f32x4_t cj = *reinterpret_cast<const f32x4_t*>(&sm.coef[buf][16 * J + 4 * g]);
-      float v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = 16 * J + 4 * g + q;
-        v[q] = (j <= i) ? m[q] * fast_exp2(si - sj[q]) * cj[q] : 0.0f;
-      }
-      uint32_t h0w, l0w, h1w, l1w;
-      split_bf16(v[0], v[1], h0w, l0w);
-      split_bf16(v[2], v[3], h1w, l1w);
-      *reinterpret_cast<u32x2_t*>(&sm.pmh[i][16 * J + 4 * g]) = u32x2_t{h0w, h1w};
-      *reinterpret_cast<u32x2_t*>(&sm.pml[i][16 * J + 4 * g]) = u32x2_t{l0w, l1w};
-    } else if (w == 3 && c + 1 < nck) {
-      scan(nxt, buf ^ 1);  // wave 3: the next chunk's per-step values
+    // ===== phase B ============================================================
+    if (cc + 1 < nck) {
+      copy_cb(mb ^ 1, gc0 + cc + 1);
+      copy_x(mb ^ 1, t0 + kQ);
     }
-
-    f32x4_t yst[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (w == 3 && cc + 2 < nck) dtr = load_dt(t0 + 2 * kQ);
+    // x of the chunk in the result layout (exact), as packed bf16:
+    // xo[tt] = x[16 tt + 4g + q][p], q = 0..3
+    u32x2_t xo[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = 16 * tt + r16;
+      xo[tt] = to_bf16x4(mfma_k32(lds128(&sm.xs[mb][t * kBC + 8 * (g ^ swz4(t))]), ipick, zero4));
+    }
+    auto xval = [&](int tt, int q) {
+      const uint32_t wv = xo[tt][q >> 1];
+      return q & 1 ? bf16_hi(wv) : bf16_lo(wv);
+    };
     if constexpr (!PRE) {
-    // ---- C h over this wave's state half, both row tiles ----------------
-    // the entering state as B operands: slots 0..3 = tile 2k, 4..7 = tile
-    // 2k + 1 of the half (states nh N/2 + 32k + 4g + q and + 16)
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      uint32_t hw[4], lw[4];
-      split_bf16(st[2 * k][0], st[2 * k][1], hw[0], lw[0]);
-      split_bf16(st[2 * k][2], st[2 * k][3], hw[1], lw[1]);
-      split_bf16(st[2 * k + 1][0], st[2 * k + 1][1], hw[2], lw[2]);
-      split_bf16(st[2 * k + 1][2], st[2 * k + 1][3], hw[3], lw[3]);
-      const u32x4_t sh = {hw[0], hw[1], hw[2], hw[3]}, sl = {lw[0], lw[1], lw[2], lw[3]};
-      const int n0 = nh * (N / 2) + 32 * k + 4 * g;
-#pragma unroll
-      for (int I = 0; I < 2; ++I) {
-        const u32x4_t co = cat(lds64(&sm.cs[16 * I + r16][n0]), lds64(&sm.cs[16 * I + r16][n0 + 16]));
-        yst[I] = mfma_k32(co, sh, yst[I]);
-        yst[I] = mfma_k32(co, sl, yst[I]);
-      }
-    }
-    // the other half's wave finishes row tile 1 - nh
-    *reinterpret_cast<f32x4_t*>(&sm.part[pt][1 - nh][lane][0]) = nh ? yst[0] : yst[1];
-    __syncthreads();
-    }
-
-    // ---- x (and z) of this wave's channels in result layout ------------
-    // xc[tt][q] = x[16 tt + 4 g + q][p], exact, from identity products
-    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t xc[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) xc[tt] = mfma_k32(lds128(&sm.xs[16 * tt + r16][8 * g]), ipick[pt], zero4);
-
-    if constexpr (!PRE) {
-    // ---- outputs of row tile I = nh for this wave's 16 channels ---------
-    {
-      const int I = nh, i = 16 * I + r16;
-      // in-chunk part P x: row tile 0 has the diagonal tile alone (slots
-      // 4..7 zero), row tile 1 the tiles 0 and 1 in one product; x as the B
-      // operand (column p, slots j = 4g + q and 16 + 4g + q)
-      const u32x2_t zero = {0u, 0u};
-      const u32x4_t xo = cat(to_bf16x4(xc[0]), I ? to_bf16x4(xc[1]) : zero);
-      f32x4_t yin = mfma_k32(cat(lds64(&sm.pmh[i][4 * g]), I ? lds64(&sm.pmh[i][16 + 4 * g]) : zero),
-                             xo, zero4);
-      yin = mfma_k32(cat(lds64(&sm.pml[i][4 * g]), I ? lds64(&sm.pml[i][16 + 4 * g]) : zero), xo,
-                     yin);
-      const f32x4_t other = *reinterpret_cast<const f32x4_t*>(&sm.part[pt][I][lane][0]);
-      const f32x4_t ys = (nh ? yst[1] : yst[0]) + other;
-      // epilogue: rows 16 I + 4 g + q, column p
-      const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ein[buf][16 * I + 4 * g]);
-      const f32x4_t xv = nh ? xc[1] : xc[0];
-      f32x4_t zv = zero4;
-      if constexpr (HAS_Z) zv = mfma_k32(lds128(&sm.zs[16 * I + r16][8 * g]), ipick[pt], zero4);
-      float out[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        out[q] = __builtin_fmaf(e[q], ys[q], yin[q]) + Dp * xv[q];
-        if constexpr (HAS_Z) out[q] *= silu(zv[q]);
-      }
-      // Store: the bf16 outputs (rows 16 I + 4 g + q, column p) taken as an
-      // A operand (row p, slots t) times the identity give the tile
-      // transposed in the result layout, lane (row t = 16 I + r16, channels
-      // 16 pt + 4 g .. + 3): one 8-byte store per lane instead of four
-      // 2-byte ones.  Exact (bf16 values times 1).
-      const u32x4_t ya = {pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3]), 0u, 0u};
-      const f32x4_t yt = mfma_k32(ya, ipick4, zero4);
       const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
       const __amdgpu_buffer_rsrc_t rsy =
           make_rsrc(static_cast<uint16_t*>(a.y) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
-      __builtin_amdgcn_raw_buffer_store_b64(
-          __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, to_bf16x4(yt)), rsy,
-          (uint32_t)(16 * I + r16) * (uint32_t)dim * 2u + (uint32_t)(cb + 16 * pt + 4 * g) * 2u, 0,
-          0);
-    }
+      // outputs of row tile I = nh: rows 16 I + 4 g + q, column p
+      auto finish = [&](auto row) {
+        constexpr int I = decltype(row)::value;
+        // in-chunk part P x: row tile 0 has the diagonal tile alone (slots
+        // 4..7 zero), row tile 1 the tiles (1,0) and (1,1) in one product
+        const u32x4_t p0 = sm.pm[mb][I == 0 ? 0 : 1][lane];
+        const u32x4_t p1 = I == 0 ? u32x4_t{0u, 0u, 0u, 0u} : sm.pm[mb][2][lane];
+        const u32x4_t bx = cat(xo[0], xo[1]);
+        f32x4_t yin = mfma_k32(u32x4_t{p0[0], p0[1], p1[0], p1[1]}, bx, zero4);
+        yin = mfma_k32(u32x4_t{p0[2], p0[3], p1[2], p1[3]}, bx, yin);
+        const f32x4_t ys = ysown + sm.part[mb][pt][I][lane];
+        const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ps[pb][3][16 * I + 4 * g]);
+        f32x4_t zv = zero4;
+        if constexpr (HAS_Z) zv = mfma_k32(zop, ipick, zero4);
+        float out[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          out[q] = __builtin_fmaf(e[q], ys[q], yin[q]) + Dp * xval(I, q);
+          if constexpr (HAS_Z) out[q] *= silu(zv[q]);
+        }
+        // Store: the bf16 outputs taken as an A operand (row p, slots t)
+        // times the identity give the tile transposed in the result layout,
+        // lane (row t = 16 I + r16, channels 16 pt + 4 g .. + 3): one 8-byte
+        // store per lane instead of four 2-byte ones.  Exact.
+        const u32x4_t ya = {pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3]), 0u, 0u};
+        const f32x4_t yt = mfma_k32(ya, ipick4, zero4);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, to_bf16x4(yt)), rsy,
+            (uint32_t)r16 * (uint32_t)dim * 2u + (uint32_t)(cb + 16 * pt + 4 * g) * 2u,
+            16 * I * dim * 2, 0);
+      };
+      if (nh)
+        finish(std::integral_constant<int, 1>{});
+      else
+        finish(std::integral_constant<int, 0>{});
     }
 
-    // ---- state update: h <- exp(s_last) h + (w x)^T B, this half --------
-    // B operand: w_t x_t[p] (column p, slots t = 4g + q and 16 + 4g + q),
-    // split into bf16 high and low parts
-    u32x4_t wh, wl;
+    // ---- state update: h <- exp(s_last) h + B^T (w x), this half -----------
+    // B operand: w_t x_t[p] (column p, slots as B^T's steps), split
     {
-      const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(&sm.wgt[buf][4 * g]);
-      const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(&sm.wgt[buf][16 + 4 * g]);
+      const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(&sm.ps[pb][2][4 * g]);
+      const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(&sm.ps[pb][2][16 + 4 * g]);
       uint32_t hw[4], lw[4];
-      split_bf16(w0[0] * xc[0][0], w0[1] * xc[0][1], hw[0], lw[0]);
-      split_bf16(w0[2] * xc[0][2], w0[3] * xc[0][3], hw[1], lw[1]);
-      split_bf16(w1[0] * xc[1][0], w1[1] * xc[1][1], hw[2], lw[2]);
-      split_bf16(w1[2] * xc[1][2], w1[3] * xc[1][3], hw[3], lw[3]);
-      wh = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-      wl = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-    }
-    const float dec = fast_exp2(sm.s2[buf][kQ - 1]);
-    if constexpr (PRE) dlog += sm.s2[buf][kQ - 1];
+      split_bf16(w0[0] * xval(0, 0), w0[1] * xval(0, 1), hw[0], lw[0]);
+      split_bf16(w0[2] * xval(0, 2), w0[3] * xval(0, 3), hw[1], lw[1]);
+      split_bf16(w1[0] * xval(1, 0), w1[1] * xval(1, 1), hw[2], lw[2]);
+      split_bf16(w1[2] * xval(1, 2), w1[3] * xval(1, 3), hw[3], lw[3]);
+      const u32x4_t wh = {hw[0], hw[1], hw[2], hw[3]}, wl = {lw[0], lw[1], lw[2], lw[3]};
+      const float slast = sm.ps[pb][0][kQ - 1];
+      const float dec = fast_exp2(slast);
+      if constexpr (PRE) dlog += slast;
 #pragma unroll
-    for (int j2 = 0; j2 < NT2 / 2; ++j2) {
-      // states 32 n32 .. 32 n32 + 31 (two tiles of this half) of B, rows t
-      const int n32 = nh * (NT2 / 2) + j2;
-      const u32x4_t b0 = lds128(&sm.bs[r16][32 * n32 + 8 * g]);
-      const u32x4_t b1 = lds128(&sm.bs[16 + r16][32 * n32 + 8 * g]);
-#pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        // A operand: row n = 32 n32 + 16 o + r16, slots t (B transposed by
-        // identity products, exact)
-        const u32x4_t bo = cat(to_bf16x4(mfma_k32(b0, ipick[o], zero4)),
-                               to_bf16x4(mfma_k32(b1, ipick[o], zero4)));
-        f32x4_t& sj = st[2 * j2 + o];
-        sj *= dec;
+      for (int j = 0; j < NT2; ++j) {
+        const int n = nh * (N / 2) + 16 * j + r16;
+        const u32x4_t bo = lds128(&sm.bts[mb][n * kQ + 8 * (g ^ swz4(n))]);
+        f32x4_t sj = st[j] * dec;
         sj = mfma_k32(bo, wh, sj);
-        sj = mfma_k32(bo, wl, sj);
+        st[j] = mfma_k32(bo, wl, sj);
       }
     }
-  };
-
-  Stage sa, sb;
-  sb.dt = 0u;
-  fetch(sa, tb);
-  if (nck > 1) fetch(sb, tb + kQ);
-  if (w == 3) scan(sa, 0);
-  for (int64_t c = 0; c < nck; c += 2) {
-    chunk(c, sa, sb);
-    if (c + 1 < nck) chunk(c + 1, sb, sa);
+    // the next chunk's z into the register just freed
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!PRE && HAS_Z) load_z(t0 + kQ);
   }
 
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy into LDS outlives the block
   float* dst = nullptr;
   if (PRE)
     dst = a.ws_hloc + (seg_row * dim + d) * N + soff;
@@ -429,6 +529,20 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(SsdArgs a, int N) {
   }
 }
 
+constexpr int64_t kMaxRows = 65535;  // grid.y limit
+
+template <int N>
+hipError_t launch_prep(SsdArgs a, hipStream_t stream) {
+  for (int64_t r0 = 0; r0 < a.batch; r0 += kMaxRows) {
+    a.row0 = r0;
+    const int rows = (int)(a.batch - r0 < kMaxRows ? a.batch - r0 : kMaxRows);
+    hipLaunchKernelGGL(ssd_prep_kernel<N>, dim3((unsigned)a.nck, rows), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int N, bool HAS_Z, bool EULER, bool PRE>
 hipError_t launch_ssd_pass(SsdArgs a, int segs, hipStream_t stream) {
   auto kern = ssd_scan_kernel<N, HAS_Z, EULER, PRE>;
@@ -436,7 +550,6 @@ hipError_t launch_ssd_pass(SsdArgs a, int segs, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  constexpr int64_t kMaxRows = 65535;  // grid.y limit
   for (int64_t r0 = 0; r0 < a.batch; r0 += kMaxRows) {
     a.row0 = r0;
     const int rows = (int)(a.batch - r0 < kMaxRows ? a.batch - r0 : kMaxRows);
@@ -449,8 +562,10 @@ hipError_t launch_ssd_pass(SsdArgs a, int segs, hipStream_t stream) {
 
 template <int N, bool HAS_Z, bool EULER>
 hipError_t launch_ssd_t(const SsdArgs& a, hipStream_t stream) {
+  hipError_t e = launch_prep<N>(a, stream);
+  if (e != hipSuccess) return e;
   if (a.nseg > 1) {
-    hipError_t e = launch_ssd_pass<N, HAS_Z, EULER, true>(a, a.nseg - 1, stream);
+    e = launch_ssd_pass<N, HAS_Z, EULER, true>(a, a.nseg - 1, stream);
     if (e != hipSuccess) return e;
     const int64_t n = a.batch * (int64_t)a.dim * N;
     hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
@@ -475,16 +590,24 @@ bool ssd_supported(int64_t headdim, int64_t dstate) {
   return headdim == kHD && (dstate == 64 || dstate == 128);
 }
 
-size_t ssd_workspace_bytes(int64_t batch, int64_t dim, int64_t nheads, int64_t dstate,
-                           int nseg) {
-  if (nseg <= 1) return 0;
+SsdLayout ssd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t nheads, int64_t dstate,
+                     int nseg) {
   auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
-  const size_t st = (size_t)batch * nseg * dim * dstate * sizeof(float);
-  return 2 * align(st) + align((size_t)batch * nseg * nheads * sizeof(float));
-}
-
-size_t ssd_smem_bytes(int64_t dstate) {
-  return dstate == 64 ? sizeof(SsdSmem<64>) : sizeof(SsdSmem<128>);
+  SsdLayout l{};
+  const size_t nck = (size_t)((seqlen + kQ - 1) / kQ);
+  const size_t rows = (size_t)batch * nck * kQ * dstate * sizeof(uint16_t);  // C or B^T
+  l.cp_off = 0;
+  l.bt_off = align(rows);
+  l.mt_off = l.bt_off + align(rows);
+  l.total = l.mt_off + align((size_t)batch * nck * kTiles * kWave * 4 * sizeof(float));
+  if (nseg > 1) {
+    const size_t st = align((size_t)batch * nseg * dim * dstate * sizeof(float));
+    l.hloc_off = l.total;
+    l.hin_off = l.hloc_off + st;
+    l.dlog_off = l.hin_off + st;
+    l.total = l.dlog_off + align((size_t)batch * nseg * nheads * sizeof(float));
+  }
+  return l;
 }
 
 hipError_t launch_ssd(const SsdArgs& a, int dstate, hipStream_t stream) {

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
     for code in range(5):
         assert lib.ssm_status_str(code).startswith(b"SSM_")
     assert b"UNKNOWN" in lib.ssm_status_str(99)
@@ -185,14 +185,34 @@ def test_backward_output_may_not_be_the_workspace(lib):
     assert st == ssm.SSM_ERR_INVALID_ARG
 
 
-def test_ssd_segments_need_workspace(lib):
-    n = lib.ssm_ssd_fwd_workspace_bytes(1, 4096, 2, 64, 128, 4)
-    assert n > 0 and lib.ssm_ssd_fwd_workspace_bytes(1, 4096, 2, 64, 128, 1) == 0
-    st = lib.ssm_ssd_fwd_planned(1, 4096, 2, 64, 128, 1, ssm.SSM_DISC_ZOH, FAKE,
-                                 ctypes.c_void_p(0x6000), FAKE, ctypes.c_void_p(0x7000),
-                                 ctypes.c_void_p(0x8000), None, None, None,
-                                 ctypes.c_void_p(0x2000), None, 4, ctypes.c_void_p(0x9000), 16,
-                                 None)
+def test_ssd_workspace_sizes(lib):
+    """The masked-matrix forward's workspace: per 32-step chunk of each batch
+    row, C with its states reordered (32 x dstate bf16), B^T (dstate x 32
+    bf16) and three 16 x 16 fp32 tiles of C B^T; with segments, also two
+    [batch, nseg, dim, dstate] fp32 state arrays and the [batch, nseg,
+    nheads] decays; every part 256-byte aligned."""
+    def al(v):
+        return (v + 255) // 256 * 256
+
+    for B, L, H, N in [(1, 4096, 2, 128), (3, 1000, 5, 64), (2, 1, 1, 128)]:
+        nck = (L + 31) // 32
+        base = 2 * al(B * nck * 32 * N * 2) + al(B * nck * 3 * 64 * 16)
+        assert lib.ssm_ssd_fwd_workspace_bytes(B, L, H, 64, N, 1) == base, (B, L, H, N)
+    n4 = lib.ssm_ssd_fwd_workspace_bytes(1, 4096, 2, 64, 128, 4)
+    assert n4 == 2 * 1048576 + 393216 + 2 * al(4 * 128 * 128 * 4) + al(4 * 2 * 4)
+    assert lib.ssm_ssd_fwd_workspace_bytes(1, 0, 2, 64, 128, 1) == 0
+    assert lib.ssm_ssd_fwd_workspace_bytes(-1, 8, 2, 64, 128, 1) == -1
+    # too small a workspace is refused before any launch, with or without segments
+    for nsplit in (1, 4):
+        st = lib.ssm_ssd_fwd_planned(1, 4096, 2, 64, 128, 1, ssm.SSM_DISC_ZOH, FAKE,
+                                     ctypes.c_void_p(0x6000), FAKE, ctypes.c_void_p(0x7000),
+                                     ctypes.c_void_p(0x8000), None, None, None,
+                                     ctypes.c_void_p(0x2000), None, nsplit,
+                                     ctypes.c_void_p(0x9000), 16, None)
+        assert st == ssm.SSM_ERR_WORKSPACE, nsplit
+    st = lib.ssm_ssd_fwd(1, 4096, 2, 64, 128, 1, ssm.SSM_DISC_ZOH, FAKE, ctypes.c_void_p(0x6000),
+                         FAKE, ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), None, None,
+                         None, ctypes.c_void_p(0x2000), None, None, 0, None)
     assert st == ssm.SSM_ERR_WORKSPACE
 
 
@@ -235,7 +255,7 @@ def test_ssd_rejects_bad_arguments(lib):
             y=ctypes.c_void_p(0x2000), h_last=None):
         return lib.ssm_ssd_fwd(batch, L, H, P, N, io, disc, x, ctypes.c_void_p(0x6000), A,
                                ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), None, None,
-                               None, y, h_last, None)
+                               None, y, h_last, ctypes.c_void_p(0x9000), 1 << 30, None)
     assert ssd(batch=-1) == ssm.SSM_ERR_INVALID_ARG
     assert ssd(L=-1) == ssm.SSM_ERR_INVALID_ARG
     assert ssd(P=0) == ssm.SSM_ERR_INVALID_ARG

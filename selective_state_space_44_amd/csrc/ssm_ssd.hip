@@ -89,6 +89,38 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15); }
 // banks.
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
+// Inclusive prefix sum of v over lanes 0..31 (lanes 32..63 get that of
+// 32..63): shifts by 1, 2, 4, 8 within rows of 16 lanes, then row 0's total
+// added to row 1 (DPP row broadcast), with no trip through LDS.
+__device__ __forceinline__ float prefix32(float v) {
+  auto add = [](float x, int t) { return x + __int_as_float(t); };
+  float s = v;
+  s = add(s, __builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x111, 0xf, 0xf, false));  // row_shr:1
+  s = add(s, __builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x112, 0xf, 0xf, false));  // row_shr:2
+  s = add(s, __builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x114, 0xf, 0xf, false));  // row_shr:4
+  s = add(s, __builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x118, 0xf, 0xf, false));  // row_shr:8
+  return add(s, __builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x142, 0xa, 0xf, false));  // row_bcast:15
+}
+
+// Input coefficient of the zero-order hold, (exp(dt a) - 1) / a = dt phi(u)
+// with u = dt a and phi(u) = (exp(u) - 1) / u: for |u| <= 1/2 the Taylor
+// series of phi to u^7 (truncation below 2e-8 relative), else the hardware
+// exp2 (the difference exp(u) - 1 then loses at most a factor 1.6 of its
+// relative accuracy) times 1 / a.
+__device__ __forceinline__ float zoh_coef(float dt, float a, float inv_a) {
+  const float u = dt * a;
+  float ph = 1.0f / 40320.0f;
+  ph = __builtin_fmaf(ph, u, 1.0f / 5040.0f);
+  ph = __builtin_fmaf(ph, u, 1.0f / 720.0f);
+  ph = __builtin_fmaf(ph, u, 1.0f / 120.0f);
+  ph = __builtin_fmaf(ph, u, 1.0f / 24.0f);
+  ph = __builtin_fmaf(ph, u, 1.0f / 6.0f);
+  ph = __builtin_fmaf(ph, u, 0.5f);
+  ph = __builtin_fmaf(ph, u, 1.0f);
+  const float big = (fast_exp2(u * kLog2e) - 1.0f) * inv_a;
+  return __builtin_fabsf(u) <= 0.5f ? dt * ph : big;
+}
+
 template <int N>
 struct SsdSmem {
   // C of a chunk (rows of N states in the workspace order); piece p of row t
@@ -217,13 +249,12 @@ void ssd_scan_kernel(SsdArgs a) {
   const int p = 16 * pt + r16;                  // this lane's channel in the block
   const int d = cb + p;
   const float Dp = a.Dskip ? a.Dskip[d] : 0.0f;
-  // this block's steps [tb, te), chunks gc0 .. gc_last of the workspace
+  // this block's steps [tb, te), its first chunk gc0 of the workspace
   const int seg = blockIdx.z;
   const int64_t tb = (int64_t)seg * a.seg_len;
   const int64_t te = tb + a.seg_len < L ? tb + a.seg_len : L;
   const int64_t gc0 = tb / kQ;
   const int64_t nck = (te - tb + kQ - 1) / kQ;
-  const int64_t gc_last = gc0 + nck - 1;
   const size_t seg_row = (size_t)b * a.nseg + seg;  // (batch row, segment) of the workspace
   const size_t soff = 16 * nh * NT2 + 4 * g;        // this lane's first state
 
@@ -247,22 +278,34 @@ void ssd_scan_kernel(SsdArgs a) {
   const u32x4_t ipick4 = identity_pick4(r16, g);
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // valid steps of the chunk at t0 (0 past the segment: such loads read zeros)
-  auto rows_at = [&](int64_t t0) {
-    return (uint32_t)(t0 >= te ? 0 : te - t0 < kQ ? te - t0 : (int64_t)kQ);
+  // valid steps of a chunk with `rem` steps left in the segment from its
+  // start (none past the end: such loads read zeros)
+  auto rows_of = [](int64_t rem) {
+    return (uint32_t)(rem <= 0 ? 0 : rem < kQ ? rem : (int64_t)kQ);
   };
+  // Per-chunk base pointers, advanced by one chunk per iteration (scalar
+  // adds instead of 64-bit index arithmetic).
+  const size_t row0 = (size_t)b * L + tb;  // first step of the segment
+  const uint16_t* xp = static_cast<const uint16_t*>(a.x) + row0 * dim;
+  const uint16_t* zp = static_cast<const uint16_t*>(a.z) + row0 * dim;
+  uint16_t* yp = static_cast<uint16_t*>(a.y) + row0 * dim;
+  const uint16_t* dtp = static_cast<const uint16_t*>(a.dt) + row0 * H;
+  const size_t ck0 = (size_t)b * a.nck + gc0;  // first workspace chunk
+  const uint16_t* cpp = static_cast<const uint16_t*>(a.ws_cp) + ck0 * kQ * N;
+  const uint16_t* btp = static_cast<const uint16_t*>(a.ws_bt) + ck0 * N * kQ;
+  const float* mtp = a.ws_mt + ck0 * kTiles * kWave * 4;
+  const size_t xstep = (size_t)kQ * dim, dtstep = (size_t)kQ * H;
+  constexpr int kCk = kQ * N;                    // elements of a chunk of C or B^T
+  constexpr int kMk = kTiles * kWave * 4;        // floats of a chunk of M tiles
 
   // ---- copies into LDS ------------------------------------------------------
   // Transfer i of wave w fills LDS bytes [1024 (CPW w + i), + 1024) of a
   // buffer; lane l the 16 bytes at 16 l of that.  The source piece of each
   // slot follows the row permutation of the buffer.
-  // C and B^T of chunk gc into buffer `buf`
-  auto copy_cb = [&](int buf, int64_t gc) {
-    const size_t chunk = (size_t)b * a.nck + gc;
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
-        static_cast<const uint16_t*>(a.ws_cp) + chunk * kQ * N, (uint32_t)(kQ * N * 2));
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
-        static_cast<const uint16_t*>(a.ws_bt) + chunk * N * kQ, (uint32_t)(N * kQ * 2));
+  // C and B^T of a chunk (workspace pointers) into buffer `buf`
+  auto copy_cb = [&](int buf, const uint16_t* cpc, const uint16_t* btc) {
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(cpc, (uint32_t)(kCk * 2));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(btc, (uint32_t)(kCk * 2));
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int pos = 1024 * (CPW * w + i) + 16 * lane;  // byte position in the buffer
@@ -279,12 +322,11 @@ void ssd_scan_kernel(SsdArgs a) {
           (uint32_t)(n * kQ + 8 * pc) * 2u, 0, 0, 0);
     }
   };
-  // x of the chunk at t0 into buffer `buf` (waves 0 and 1, 1 KB each)
-  auto copy_x = [&](int buf, int64_t t0) {
+  // x of a chunk (pointer, valid rows) into buffer `buf` (waves 0 and 1,
+  // 1 KB each)
+  auto copy_x = [&](int buf, const uint16_t* xc, uint32_t rows) {
     if (w < 2) {
-      const __amdgpu_buffer_rsrc_t rsx =
-          make_rsrc(static_cast<const uint16_t*>(a.x) + (b * L + t0) * dim,
-                    rows_at(t0) * (uint32_t)dim * 2u);
+      const __amdgpu_buffer_rsrc_t rsx = make_rsrc(xc, rows * (uint32_t)dim * 2u);
       const int t = 16 * w + (lane >> 2), pc = (lane & 3) ^ swz4(t);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (__attribute__((address_space(3))) void*)&sm.xs[buf][512 * w], 16,
                                                (uint32_t)(t * dim + cb + 8 * pc) * 2u, 0, 0, 0);
@@ -292,45 +334,38 @@ void ssd_scan_kernel(SsdArgs a) {
   };
 
   // ---- register loads -------------------------------------------------------
-  // M tile w (waves 0..2) of chunk gc
+  // M tile w (waves 0..2) of a chunk
   f32x4_t mreg = zero4;
-  auto load_m = [&](int64_t gc) {
+  auto load_m = [&](const float* mtc) {
     if (w < kTiles) {
-      const __amdgpu_buffer_rsrc_t rsm = make_rsrc(
-          a.ws_mt + ((size_t)b * a.nck + gc) * kTiles * kWave * 4, (uint32_t)(kTiles * kWave * 16));
+      const __amdgpu_buffer_rsrc_t rsm = make_rsrc(mtc, (uint32_t)(kMk * 4));
       mreg = __builtin_bit_cast(
           f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsm, (uint32_t)lane * 16u, w * kWave * 16, 0));
     }
   };
   // z of row tile nh as the identity A operand: row t, 32 channels
   u32x4_t zop = {0u, 0u, 0u, 0u};
-  auto load_z = [&](int64_t t0) {
-    const __amdgpu_buffer_rsrc_t rsz = make_rsrc(
-        static_cast<const uint16_t*>(a.z) + (b * L + t0) * dim, rows_at(t0) * (uint32_t)dim * 2u);
+  auto load_z = [&](const uint16_t* zc, uint32_t rows) {
+    const __amdgpu_buffer_rsrc_t rsz = make_rsrc(zc, rows * (uint32_t)dim * 2u);
     zop = __builtin_bit_cast(
         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                      rsz, (uint32_t)((16 * nh + r16) * dim + cb + 8 * g) * 2u, 0, 0));
   };
   // wave 3: dt of a chunk, lane = step
-  auto load_dt = [&](int64_t t0) -> uint32_t {
-    const __amdgpu_buffer_rsrc_t rsd = make_rsrc(
-        static_cast<const uint16_t*>(a.dt) + (b * L + t0) * H, rows_at(t0) * (uint32_t)H * 2u);
+  auto load_dt = [&](const uint16_t* dtc, uint32_t rows) -> uint32_t {
+    const __amdgpu_buffer_rsrc_t rsd = make_rsrc(dtc, rows * (uint32_t)H * 2u);
     return lane < kQ ? __builtin_amdgcn_raw_buffer_load_b16(rsd, (uint32_t)(lane * H + h) * 2u, 0, 0)
                      : 0u;
   };
 
   // ---- per-step values of a chunk (wave 3, lane = step < 32) ----------------
+  const float inv_a = coef_is_dt ? 0.0f : 1.0f / Ah;
   auto steps = [&](uint32_t dtbits, int buf) {
     const float dtv = bf16_bits_to_f32(dtbits);
-    float s = dtv * A2;
-#pragma unroll
-    for (int o = 1; o < kQ; o <<= 1) {
-      const float v = __shfl_up(s, o);
-      if (lane >= o) s += v;
-    }
-    const float last = __shfl(s, kQ - 1);
+    const float s = prefix32(dtv * A2);
+    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kQ - 1));
     if (lane < kQ) {
-      const float cf = coef_is_dt ? dtv : expm1f(dtv * Ah) / Ah;
+      const float cf = coef_is_dt ? dtv : zoh_coef(dtv, Ah, inv_a);
       sm.ps[buf][0][lane] = s;
       sm.ps[buf][1][lane] = cf;
       sm.ps[buf][2][lane] = fast_exp2(last - s) * cf;
@@ -339,27 +374,34 @@ void ssd_scan_kernel(SsdArgs a) {
   };
 
   // ---- prologue -------------------------------------------------------------
+  // wave 3 keeps the per-step values two chunks ahead: those of chunk c + 2
+  // are computed at the end of chunk c's phase B from dt loaded a chunk
+  // earlier
+  const int64_t seg_steps = te - tb;
   uint32_t dtr = 0;
-  copy_cb(0, gc0);
-  copy_x(0, tb);
-  if (w == 3) dtr = load_dt(tb);
-  if constexpr (!PRE) {
-    if constexpr (HAS_Z) load_z(tb);
-    load_m(gc0);
-  }
+  copy_cb(0, cpp, btp);
+  copy_x(0, xp, rows_of(seg_steps));
   if (w == 3) {
-    steps(dtr, 0);
-    if (nck > 1) dtr = load_dt(tb + kQ);
+    const uint32_t d0 = load_dt(dtp, rows_of(seg_steps));
+    const uint32_t d1 = load_dt(dtp + dtstep, rows_of(seg_steps - kQ));
+    dtr = load_dt(dtp + 2 * dtstep, rows_of(seg_steps - 2 * kQ));
+    steps(d0, 0);
+    steps(d1, 1);
+  }
+  if constexpr (!PRE) {
+    if constexpr (HAS_Z) load_z(zp, rows_of(seg_steps));
+    load_m(mtp);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's copies have landed
   __syncthreads();
 
-  for (int64_t cc = 0; cc < nck; ++cc) {
-    const int64_t t0 = tb + cc * kQ;
-    const int pb = (int)(cc % 3), mb = (int)(cc & 1);
+  int pb = 0;  // chunk index mod 3 (per-step values)
+  for (int cc = 0; cc < (int)nck; ++cc) {
+    const int mb = cc & 1;                        // double buffers
+    const int64_t rem = seg_steps - (int64_t)cc * kQ;  // steps left from this chunk on
+    const bool more = cc + 1 < (int)nck;
 
     // ===== phase A ============================================================
-    if (w == 3 && cc + 1 < nck) steps(dtr, (int)((cc + 1) % 3));
     [[maybe_unused]] f32x4_t ysown = zero4;  // C h_in over this half, row tile nh
     if constexpr (!PRE) {
       // masked weights: tile w of (0,0), (1,0), (1,1)
@@ -378,7 +420,7 @@ void ssd_scan_kernel(SsdArgs a) {
         sm.pm[mb][w][lane] = u32x4_t{h01, h23, l01, l23};
         // the next chunk's tile into the register just freed
         __builtin_amdgcn_sched_barrier(0);
-        load_m(gc0 + cc + 1 < gc_last ? gc0 + cc + 1 : gc_last);
+        load_m(more ? mtp + kMk : mtp);
       }
       // C h_in over this wave's state half, both row tiles; the entering
       // state as B operands (slots 0..3 = tile 2k, 4..7 = tile 2k + 1)
@@ -412,11 +454,14 @@ void ssd_scan_kernel(SsdArgs a) {
     __syncthreads();
 
     // ===== phase B ============================================================
-    if (cc + 1 < nck) {
-      copy_cb(mb ^ 1, gc0 + cc + 1);
-      copy_x(mb ^ 1, t0 + kQ);
+    // dt of chunk c + 3 first, so that waiting for it later does not wait
+    // for the copies and stores issued after it
+    uint32_t dnext = 0;
+    if (w == 3) dnext = load_dt(dtp + 3 * dtstep, rows_of(rem - 3 * kQ));
+    if (more) {
+      copy_cb(mb ^ 1, cpp + kCk, btp + kCk);
+      copy_x(mb ^ 1, xp + xstep, rows_of(rem - kQ));
     }
-    if (w == 3 && cc + 2 < nck) dtr = load_dt(t0 + 2 * kQ);
     // x of the chunk in the result layout (exact), as packed bf16:
     // xo[tt] = x[16 tt + 4g + q][p], q = 0..3
     u32x2_t xo[2];
@@ -430,9 +475,7 @@ void ssd_scan_kernel(SsdArgs a) {
       return q & 1 ? bf16_hi(wv) : bf16_lo(wv);
     };
     if constexpr (!PRE) {
-      const uint32_t rows = (uint32_t)(L - t0 < kQ ? L - t0 : (int64_t)kQ);
-      const __amdgpu_buffer_rsrc_t rsy =
-          make_rsrc(static_cast<uint16_t*>(a.y) + (b * L + t0) * dim, rows * (uint32_t)dim * 2u);
+      const __amdgpu_buffer_rsrc_t rsy = make_rsrc(yp, rows_of(rem) * (uint32_t)dim * 2u);
       // outputs of row tile I = nh: rows 16 I + 4 g + q, column p
       auto finish = [&](auto row) {
         constexpr int I = decltype(row)::value;
@@ -493,9 +536,23 @@ void ssd_scan_kernel(SsdArgs a) {
         st[j] = mfma_k32(bo, wl, sj);
       }
     }
+    // wave 3: per-step values of chunk c + 2
+    if (w == 3) {
+      if (cc + 2 < (int)nck) steps(dtr, pb == 0 ? 2 : pb - 1);  // (cc + 2) mod 3
+      dtr = dnext;
+    }
     // the next chunk's z into the register just freed
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!PRE && HAS_Z) load_z(t0 + kQ);
+    if constexpr (!PRE && HAS_Z) load_z(zp + xstep, rows_of(rem - kQ));
+    // advance to the next chunk
+    xp += xstep;
+    zp += xstep;
+    yp += xstep;
+    dtp += dtstep;
+    cpp += kCk;
+    btp += kCk;
+    mtp += kMk;
+    pb = pb == 2 ? 0 : pb + 1;
   }
 
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy into LDS outlives the block

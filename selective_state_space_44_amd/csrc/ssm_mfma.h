@@ -26,10 +26,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo_elem, float hi_elem) {
 }
 
 // (a, b) ~= hi + lo with hi, lo packed bf16 pairs: hi = rounded value, lo =
-// rounded remainder (the remainder itself is exact in fp32).
+// rounded remainder (the remainder itself is exact in fp32).  The high part
+// of a is moved into place with a byte permute (v_perm_b32: bytes 1:0 of hi
+// to 3:2, zeros below), which the compiler keeps as one instruction.
 __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = pack_bf16(a, b);
-  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+  const float ah = __uint_as_float(__builtin_amdgcn_perm(0u, hi, 0x01000c0cu));
+  lo = pack_bf16(a - ah, b - __uint_as_float(hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -130,8 +130,9 @@ struct SsdSmem {
   alignas(16) uint16_t bts[2][N * kQ];
   // x of the block's 32 channels (rows of 64 bytes); slot p ^ swz4(t)
   alignas(16) uint16_t xs[2][kQ * kBC];
-  // masked weights per tile and lane: {hi q0q1, hi q2q3, lo q0q1, lo q2q3}
-  alignas(16) u32x4_t pm[2][kTiles][kWave];
+  // masked weights per tile and lane, bf16 high and low parts of q = 0..3
+  alignas(16) u32x2_t pmh[2][kTiles][kWave];
+  alignas(16) u32x2_t pml[2][kTiles][kWave];
   // C h_in over one state half for the other half's wave:
   // [channel tile][row tile][lane]
   alignas(16) f32x4_t part[2][2][2][kWave];
@@ -278,11 +279,11 @@ void ssd_scan_kernel(SsdArgs a) {
   const u32x4_t ipick4 = identity_pick4(r16, g);
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // valid steps of a chunk with `rem` steps left in the segment from its
-  // start (none past the end: such loads read zeros)
-  auto rows_of = [](int64_t rem) {
-    return (uint32_t)(rem <= 0 ? 0 : rem < kQ ? rem : (int64_t)kQ);
-  };
+  // valid steps of the segment's chunk k (none past the end: such loads read
+  // zeros); every chunk but the last is full
+  const int nck_i = (int)nck;
+  const int tail = (int)(te - tb - (int64_t)(nck_i - 1) * kQ);
+  auto rows_of = [&](int k) { return (uint32_t)(k < nck_i - 1 ? kQ : k == nck_i - 1 ? tail : 0); };
   // Per-chunk base pointers, advanced by one chunk per iteration (scalar
   // adds instead of 64-bit index arithmetic).
   const size_t row0 = (size_t)b * L + tb;  // first step of the segment
@@ -377,29 +378,27 @@ void ssd_scan_kernel(SsdArgs a) {
   // wave 3 keeps the per-step values two chunks ahead: those of chunk c + 2
   // are computed at the end of chunk c's phase B from dt loaded a chunk
   // earlier
-  const int64_t seg_steps = te - tb;
   uint32_t dtr = 0;
   copy_cb(0, cpp, btp);
-  copy_x(0, xp, rows_of(seg_steps));
+  copy_x(0, xp, rows_of(0));
   if (w == 3) {
-    const uint32_t d0 = load_dt(dtp, rows_of(seg_steps));
-    const uint32_t d1 = load_dt(dtp + dtstep, rows_of(seg_steps - kQ));
-    dtr = load_dt(dtp + 2 * dtstep, rows_of(seg_steps - 2 * kQ));
+    const uint32_t d0 = load_dt(dtp, rows_of(0));
+    const uint32_t d1 = load_dt(dtp + dtstep, rows_of(1));
+    dtr = load_dt(dtp + 2 * dtstep, rows_of(2));
     steps(d0, 0);
     steps(d1, 1);
   }
   if constexpr (!PRE) {
-    if constexpr (HAS_Z) load_z(zp, rows_of(seg_steps));
+    if constexpr (HAS_Z) load_z(zp, rows_of(0));
     load_m(mtp);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's copies have landed
   __syncthreads();
 
   int pb = 0;  // chunk index mod 3 (per-step values)
-  for (int cc = 0; cc < (int)nck; ++cc) {
-    const int mb = cc & 1;                        // double buffers
-    const int64_t rem = seg_steps - (int64_t)cc * kQ;  // steps left from this chunk on
-    const bool more = cc + 1 < (int)nck;
+  for (int cc = 0; cc < nck_i; ++cc) {
+    const int mb = cc & 1;  // double buffers
+    const bool more = cc + 1 < nck_i;
 
     // ===== phase A ============================================================
     [[maybe_unused]] f32x4_t ysown = zero4;  // C h_in over this half, row tile nh
@@ -417,7 +416,8 @@ void ssd_scan_kernel(SsdArgs a) {
         uint32_t h01, l01, h23, l23;
         split_bf16(v[0], v[1], h01, l01);
         split_bf16(v[2], v[3], h23, l23);
-        sm.pm[mb][w][lane] = u32x4_t{h01, h23, l01, l23};
+        sm.pmh[mb][w][lane] = u32x2_t{h01, h23};
+        sm.pml[mb][w][lane] = u32x2_t{l01, l23};
         // the next chunk's tile into the register just freed
         __builtin_amdgcn_sched_barrier(0);
         load_m(more ? mtp + kMk : mtp);
@@ -457,10 +457,10 @@ void ssd_scan_kernel(SsdArgs a) {
     // dt of chunk c + 3 first, so that waiting for it later does not wait
     // for the copies and stores issued after it
     uint32_t dnext = 0;
-    if (w == 3) dnext = load_dt(dtp + 3 * dtstep, rows_of(rem - 3 * kQ));
+    if (w == 3) dnext = load_dt(dtp + 3 * dtstep, rows_of(cc + 3));
     if (more) {
       copy_cb(mb ^ 1, cpp + kCk, btp + kCk);
-      copy_x(mb ^ 1, xp + xstep, rows_of(rem - kQ));
+      copy_x(mb ^ 1, xp + xstep, rows_of(cc + 1));
     }
     // x of the chunk in the result layout (exact), as packed bf16:
     // xo[tt] = x[16 tt + 4g + q][p], q = 0..3
@@ -475,17 +475,18 @@ void ssd_scan_kernel(SsdArgs a) {
       return q & 1 ? bf16_hi(wv) : bf16_lo(wv);
     };
     if constexpr (!PRE) {
-      const __amdgpu_buffer_rsrc_t rsy = make_rsrc(yp, rows_of(rem) * (uint32_t)dim * 2u);
+      const __amdgpu_buffer_rsrc_t rsy = make_rsrc(yp, rows_of(cc) * (uint32_t)dim * 2u);
       // outputs of row tile I = nh: rows 16 I + 4 g + q, column p
       auto finish = [&](auto row) {
         constexpr int I = decltype(row)::value;
         // in-chunk part P x: row tile 0 has the diagonal tile alone (slots
         // 4..7 zero), row tile 1 the tiles (1,0) and (1,1) in one product
-        const u32x4_t p0 = sm.pm[mb][I == 0 ? 0 : 1][lane];
-        const u32x4_t p1 = I == 0 ? u32x4_t{0u, 0u, 0u, 0u} : sm.pm[mb][2][lane];
+        const u32x2_t z2 = {0u, 0u};
+        const u32x4_t ph = cat(sm.pmh[mb][I == 0 ? 0 : 1][lane], I == 0 ? z2 : sm.pmh[mb][2][lane]);
+        const u32x4_t pl = cat(sm.pml[mb][I == 0 ? 0 : 1][lane], I == 0 ? z2 : sm.pml[mb][2][lane]);
         const u32x4_t bx = cat(xo[0], xo[1]);
-        f32x4_t yin = mfma_k32(u32x4_t{p0[0], p0[1], p1[0], p1[1]}, bx, zero4);
-        yin = mfma_k32(u32x4_t{p0[2], p0[3], p1[2], p1[3]}, bx, yin);
+        f32x4_t yin = mfma_k32(ph, bx, zero4);
+        yin = mfma_k32(pl, bx, yin);
         const f32x4_t ys = ysown + sm.part[mb][pt][I][lane];
         const f32x4_t e = *reinterpret_cast<const f32x4_t*>(&sm.ps[pb][3][16 * I + 4 * g]);
         f32x4_t zv = zero4;
@@ -538,12 +539,12 @@ void ssd_scan_kernel(SsdArgs a) {
     }
     // wave 3: per-step values of chunk c + 2
     if (w == 3) {
-      if (cc + 2 < (int)nck) steps(dtr, pb == 0 ? 2 : pb - 1);  // (cc + 2) mod 3
+      if (cc + 2 < nck_i) steps(dtr, pb == 0 ? 2 : pb - 1);  // (cc + 2) mod 3
       dtr = dnext;
     }
     // the next chunk's z into the register just freed
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!PRE && HAS_Z) load_z(zp + xstep, rows_of(rem - kQ));
+    if constexpr (!PRE && HAS_Z) load_z(zp + xstep, rows_of(cc + 1));
     // advance to the next chunk
     xp += xstep;
     zp += xstep;

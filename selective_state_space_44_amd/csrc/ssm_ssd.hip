@@ -303,20 +303,27 @@ void ssd_scan_kernel(SsdArgs a) {
   // Transfer i of wave w fills LDS bytes [1024 (CPW w + i), + 1024) of a
   // buffer; lane l the 16 bytes at 16 l of that.  The source piece of each
   // slot follows the row permutation of the buffer.
-  // C and B^T of a chunk (workspace pointers) into buffer `buf`
-  auto copy_cb = [&](int buf, const uint16_t* cpc, const uint16_t* btc) {
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(cpc, (uint32_t)(kCk * 2));
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(btc, (uint32_t)(kCk * 2));
+  // C of a chunk (workspace pointer) into buffer `buf`
+  auto copy_c = [&](int buf, const uint16_t* cpc) {
+    if constexpr (!PRE) {
+      const __amdgpu_buffer_rsrc_t rsc = make_rsrc(cpc, (uint32_t)(kCk * 2));
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int pos = 1024 * (CPW * w + i) + 16 * lane;  // byte position in the buffer
-      if constexpr (!PRE) {
+      for (int i = 0; i < CPW; ++i) {
+        const int pos = 1024 * (CPW * w + i) + 16 * lane;  // byte position in the buffer
         const int t = pos / (2 * N), slot = (pos >> 4) & (N / 8 - 1);
         const int pc = slot ^ (t & (N / 8 - 1));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsc, (__attribute__((address_space(3))) void*)&sm.cs[buf][512 * (CPW * w + i)], 16,
             (uint32_t)(t * N + 8 * pc) * 2u, 0, 0, 0);
       }
+    }
+  };
+  // B^T of a chunk (workspace pointer) into buffer `buf`
+  auto copy_bt = [&](int buf, const uint16_t* btc) {
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(btc, (uint32_t)(kCk * 2));
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int pos = 1024 * (CPW * w + i) + 16 * lane;
       const int n = pos >> 6, pc = ((pos >> 4) & 3) ^ swz4(n);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsb, (__attribute__((address_space(3))) void*)&sm.bts[buf][512 * (CPW * w + i)], 16,
@@ -329,8 +336,9 @@ void ssd_scan_kernel(SsdArgs a) {
     if (w < 2) {
       const __amdgpu_buffer_rsrc_t rsx = make_rsrc(xc, rows * (uint32_t)dim * 2u);
       const int t = 16 * w + (lane >> 2), pc = (lane & 3) ^ swz4(t);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (__attribute__((address_space(3))) void*)&sm.xs[buf][512 * w], 16,
-                                               (uint32_t)(t * dim + cb + 8 * pc) * 2u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsx, (__attribute__((address_space(3))) void*)&sm.xs[buf][512 * w], 16,
+          (uint32_t)(t * dim + cb + 8 * pc) * 2u, 0, 0, 0);
     }
   };
 
@@ -378,8 +386,13 @@ void ssd_scan_kernel(SsdArgs a) {
   // wave 3 keeps the per-step values two chunks ahead: those of chunk c + 2
   // are computed at the end of chunk c's phase B from dt loaded a chunk
   // earlier
+  // C is read in phase A, before the chunk's barrier, so it is copied two
+  // chunks ahead (into the buffer whose last reader finished before the
+  // previous barrier); B^T and x, read in phase B, one chunk ahead.
   uint32_t dtr = 0;
-  copy_cb(0, cpp, btp);
+  copy_c(0, cpp);
+  copy_c(1, nck_i > 1 ? cpp + kCk : cpp);
+  copy_bt(0, btp);
   copy_x(0, xp, rows_of(0));
   if (w == 3) {
     const uint32_t d0 = load_dt(dtp, rows_of(0));
@@ -418,9 +431,6 @@ void ssd_scan_kernel(SsdArgs a) {
         split_bf16(v[2], v[3], h23, l23);
         sm.pmh[mb][w][lane] = u32x2_t{h01, h23};
         sm.pml[mb][w][lane] = u32x2_t{l01, l23};
-        // the next chunk's tile into the register just freed
-        __builtin_amdgcn_sched_barrier(0);
-        load_m(more ? mtp + kMk : mtp);
       }
       // C h_in over this wave's state half, both row tiles; the entering
       // state as B operands (slots 0..3 = tile 2k, 4..7 = tile 2k + 1)
@@ -446,22 +456,26 @@ void ssd_scan_kernel(SsdArgs a) {
       ysown = nh ? yst[1] : yst[0];
     }
     // Every wave's copies of this chunk's operands (issued a chunk ago) have
-    // landed before the barrier: vector memory operations complete in issue
-    // order, and of those issued after the copies at most the last one (the
-    // M tile just loaded, or the z load) may still be in flight.
+    // landed before the barrier.  The wait is for all of this wave's vector
+    // memory operations: copies into LDS are not ordered with the register
+    // loads issued after them, and nothing issued since the last phase B
+    // start is still needed later than here.
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PRE ? 0 : 1));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
     // ===== phase B ============================================================
     // dt of chunk c + 3 first, so that waiting for it later does not wait
     // for the copies and stores issued after it
+    // dt of chunk c + 3 (wave 3), then the copies: B^T and x of the next
+    // chunk, C of the chunk after it (the last chunks' "next" copies read
+    // zeros or repeat a chunk into an idle buffer)
     uint32_t dnext = 0;
     if (w == 3) dnext = load_dt(dtp + 3 * dtstep, rows_of(cc + 3));
-    if (more) {
-      copy_cb(mb ^ 1, cpp + kCk, btp + kCk);
-      copy_x(mb ^ 1, xp + xstep, rows_of(cc + 1));
-    }
+    copy_bt(mb ^ 1, more ? btp + kCk : btp);
+    copy_x(mb ^ 1, xp + xstep, rows_of(cc + 1));
+    copy_c(mb, cc + 2 < nck_i ? cpp + 2 * kCk : cpp);  // chunk cc + 2
+    if constexpr (!PRE) load_m(more ? mtp + kMk : mtp);  // the next chunk's M tile
     // x of the chunk in the result layout (exact), as packed bf16:
     // xo[tt] = x[16 tt + 4g + q][p], q = 0..3
     u32x2_t xo[2];

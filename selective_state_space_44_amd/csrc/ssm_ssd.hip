@@ -353,10 +353,9 @@ void ssd_scan_kernel(SsdArgs a) {
     }
   };
   // z of row tile nh as the identity A operand: row t, 32 channels
-  u32x4_t zop = {0u, 0u, 0u, 0u};
   auto load_z = [&](const uint16_t* zc, uint32_t rows) {
     const __amdgpu_buffer_rsrc_t rsz = make_rsrc(zc, rows * (uint32_t)dim * 2u);
-    zop = __builtin_bit_cast(
+    return __builtin_bit_cast(
         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                      rsz, (uint32_t)((16 * nh + r16) * dim + cb + 8 * g) * 2u, 0, 0));
   };
@@ -389,7 +388,8 @@ void ssd_scan_kernel(SsdArgs a) {
   // C is read in phase A, before the chunk's barrier, so it is copied two
   // chunks ahead (into the buffer whose last reader finished before the
   // previous barrier); B^T and x, read in phase B, one chunk ahead.
-  uint32_t dtr = 0;
+  uint32_t da = 0;  // dt of chunk c + 2 when chunk c starts (wave 3)
+  u32x4_t za = {0u, 0u, 0u, 0u};  // z of the chunk
   copy_c(0, cpp);
   copy_c(1, nck_i > 1 ? cpp + kCk : cpp);
   copy_bt(0, btp);
@@ -397,19 +397,22 @@ void ssd_scan_kernel(SsdArgs a) {
   if (w == 3) {
     const uint32_t d0 = load_dt(dtp, rows_of(0));
     const uint32_t d1 = load_dt(dtp + dtstep, rows_of(1));
-    dtr = load_dt(dtp + 2 * dtstep, rows_of(2));
+    da = load_dt(dtp + 2 * dtstep, rows_of(2));
     steps(d0, 0);
     steps(d1, 1);
   }
   if constexpr (!PRE) {
-    if constexpr (HAS_Z) load_z(zp, rows_of(0));
+    if constexpr (HAS_Z) za = load_z(zp, rows_of(0));
     load_m(mtp);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's copies have landed
   __syncthreads();
 
+  // One chunk; the loop runs two per iteration with the registers of z and dt
+  // swapping roles, so that no register copy waits for a load in flight.
   int pb = 0;  // chunk index mod 3 (per-step values)
-  for (int cc = 0; cc < nck_i; ++cc) {
+  auto chunk_step = [&](int cc, const u32x4_t& zop, u32x4_t& znext, uint32_t dtr,
+                        uint32_t& dnext) {
     const int mb = cc & 1;  // double buffers
     const bool more = cc + 1 < nck_i;
 
@@ -470,12 +473,14 @@ void ssd_scan_kernel(SsdArgs a) {
     // dt of chunk c + 3 (wave 3), then the copies: B^T and x of the next
     // chunk, C of the chunk after it (the last chunks' "next" copies read
     // zeros or repeat a chunk into an idle buffer)
-    uint32_t dnext = 0;
     if (w == 3) dnext = load_dt(dtp + 3 * dtstep, rows_of(cc + 3));
     copy_bt(mb ^ 1, more ? btp + kCk : btp);
     copy_x(mb ^ 1, xp + xstep, rows_of(cc + 1));
     copy_c(mb, cc + 2 < nck_i ? cpp + 2 * kCk : cpp);  // chunk cc + 2
-    if constexpr (!PRE) load_m(more ? mtp + kMk : mtp);  // the next chunk's M tile
+    if constexpr (!PRE) {
+      load_m(more ? mtp + kMk : mtp);  // the next chunk's M tile and z
+      if constexpr (HAS_Z) znext = load_z(zp + xstep, rows_of(cc + 1));
+    }
     // x of the chunk in the result layout (exact), as packed bf16:
     // xo[tt] = x[16 tt + 4g + q][p], q = 0..3
     u32x2_t xo[2];
@@ -552,13 +557,7 @@ void ssd_scan_kernel(SsdArgs a) {
       }
     }
     // wave 3: per-step values of chunk c + 2
-    if (w == 3) {
-      if (cc + 2 < nck_i) steps(dtr, pb == 0 ? 2 : pb - 1);  // (cc + 2) mod 3
-      dtr = dnext;
-    }
-    // the next chunk's z into the register just freed
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!PRE && HAS_Z) load_z(zp + xstep, rows_of(cc + 1));
+    if (w == 3 && cc + 2 < nck_i) steps(dtr, pb == 0 ? 2 : pb - 1);  // (cc + 2) mod 3
     // advance to the next chunk
     xp += xstep;
     zp += xstep;
@@ -568,6 +567,12 @@ void ssd_scan_kernel(SsdArgs a) {
     btp += kCk;
     mtp += kMk;
     pb = pb == 2 ? 0 : pb + 1;
+  };
+  u32x4_t zb = {0u, 0u, 0u, 0u};
+  uint32_t db = 0;
+  for (int cc = 0; cc < nck_i; cc += 2) {
+    chunk_step(cc, za, zb, da, db);
+    if (cc + 1 < nck_i) chunk_step(cc + 1, zb, za, db, da);
   }
 
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy into LDS outlives the block

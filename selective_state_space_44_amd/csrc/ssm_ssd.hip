@@ -137,7 +137,7 @@ struct SsdSmem {
   // [channel tile][row tile][lane]
   alignas(16) f32x4_t part[2][2][2][kWave];
   // per-step values: s_t log2(e), coef_t, w_t, exp(s_t)
-  alignas(16) float ps[3][4][kQ];
+  alignas(16) float ps[4][4][kQ];
 };
 
 // ---------------------------------------------------------------------------
@@ -383,12 +383,13 @@ void ssd_scan_kernel(SsdArgs a) {
 
   // ---- prologue -------------------------------------------------------------
   // wave 3 keeps the per-step values two chunks ahead: those of chunk c + 2
-  // are computed at the end of chunk c's phase B from dt loaded a chunk
-  // earlier
+  // are computed in chunk c's phase A (while waves 0..2 build P) from dt
+  // loaded two chunks earlier, into the fourth buffer: its last readers (in
+  // chunk c - 2's phase B) are past the previous barrier
   // C is read in phase A, before the chunk's barrier, so it is copied two
   // chunks ahead (into the buffer whose last reader finished before the
   // previous barrier); B^T and x, read in phase B, one chunk ahead.
-  uint32_t da = 0;  // dt of chunk c + 2 when chunk c starts (wave 3)
+  uint32_t da = 0, db = 0;  // dt of chunk c + 2 when chunk c starts (wave 3)
   u32x4_t za = {0u, 0u, 0u, 0u};  // z of the chunk
   copy_c(0, cpp);
   copy_c(1, nck_i > 1 ? cpp + kCk : cpp);
@@ -398,6 +399,7 @@ void ssd_scan_kernel(SsdArgs a) {
     const uint32_t d0 = load_dt(dtp, rows_of(0));
     const uint32_t d1 = load_dt(dtp + dtstep, rows_of(1));
     da = load_dt(dtp + 2 * dtstep, rows_of(2));
+    db = load_dt(dtp + 3 * dtstep, rows_of(3));
     steps(d0, 0);
     steps(d1, 1);
   }
@@ -410,13 +412,13 @@ void ssd_scan_kernel(SsdArgs a) {
 
   // One chunk; the loop runs two per iteration with the registers of z and dt
   // swapping roles, so that no register copy waits for a load in flight.
-  int pb = 0;  // chunk index mod 3 (per-step values)
-  auto chunk_step = [&](int cc, const u32x4_t& zop, u32x4_t& znext, uint32_t dtr,
-                        uint32_t& dnext) {
+  auto chunk_step = [&](int cc, const u32x4_t& zop, u32x4_t& znext, uint32_t& dtr) {
+    const int pb = cc & 3;  // per-step values
     const int mb = cc & 1;  // double buffers
     const bool more = cc + 1 < nck_i;
 
     // ===== phase A ============================================================
+    if (w == 3 && cc + 2 < nck_i) steps(dtr, (cc + 2) & 3);
     [[maybe_unused]] f32x4_t ysown = zero4;  // C h_in over this half, row tile nh
     if constexpr (!PRE) {
       // masked weights: tile w of (0,0), (1,0), (1,1)
@@ -470,10 +472,10 @@ void ssd_scan_kernel(SsdArgs a) {
     // ===== phase B ============================================================
     // dt of chunk c + 3 first, so that waiting for it later does not wait
     // for the copies and stores issued after it
-    // dt of chunk c + 3 (wave 3), then the copies: B^T and x of the next
+    // dt of chunk c + 4 (wave 3), then the copies: B^T and x of the next
     // chunk, C of the chunk after it (the last chunks' "next" copies read
     // zeros or repeat a chunk into an idle buffer)
-    if (w == 3) dnext = load_dt(dtp + 3 * dtstep, rows_of(cc + 3));
+    if (w == 3) dtr = load_dt(dtp + 4 * dtstep, rows_of(cc + 4));  // chunk cc + 4
     copy_bt(mb ^ 1, more ? btp + kCk : btp);
     copy_x(mb ^ 1, xp + xstep, rows_of(cc + 1));
     copy_c(mb, cc + 2 < nck_i ? cpp + 2 * kCk : cpp);  // chunk cc + 2
@@ -557,7 +559,6 @@ void ssd_scan_kernel(SsdArgs a) {
       }
     }
     // wave 3: per-step values of chunk c + 2
-    if (w == 3 && cc + 2 < nck_i) steps(dtr, pb == 0 ? 2 : pb - 1);  // (cc + 2) mod 3
     // advance to the next chunk
     xp += xstep;
     zp += xstep;
@@ -566,13 +567,11 @@ void ssd_scan_kernel(SsdArgs a) {
     cpp += kCk;
     btp += kCk;
     mtp += kMk;
-    pb = pb == 2 ? 0 : pb + 1;
   };
   u32x4_t zb = {0u, 0u, 0u, 0u};
-  uint32_t db = 0;
   for (int cc = 0; cc < nck_i; cc += 2) {
-    chunk_step(cc, za, zb, da, db);
-    if (cc + 1 < nck_i) chunk_step(cc + 1, zb, za, db, da);
+    chunk_step(cc, za, zb, da);
+    if (cc + 1 < nck_i) chunk_step(cc + 1, zb, za, db);
   }
 
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy into LDS outlives the block

@@ -483,18 +483,17 @@ void ssd_scan_kernel(SsdArgs a) {
       load_m(more ? mtp + kMk : mtp);  // the next chunk's M tile and z
       if constexpr (HAS_Z) znext = load_z(zp + xstep, rows_of(cc + 1));
     }
-    // x of the chunk in the result layout (exact), as packed bf16:
-    // xo[tt] = x[16 tt + 4g + q][p], q = 0..3
+    // x of the chunk in the result layout (exact): xc[tt][q] = x[16 tt + 4g +
+    // q][p], q = 0..3, and as packed bf16 (the B operand of P x)
+    f32x4_t xc[2];
     u32x2_t xo[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = 16 * tt + r16;
-      xo[tt] = to_bf16x4(mfma_k32(lds128(&sm.xs[mb][t * kBC + 8 * (g ^ swz4(t))]), ipick, zero4));
+      xc[tt] = mfma_k32(lds128(&sm.xs[mb][t * kBC + 8 * (g ^ swz4(t))]), ipick, zero4);
+      xo[tt] = to_bf16x4(xc[tt]);
     }
-    auto xval = [&](int tt, int q) {
-      const uint32_t wv = xo[tt][q >> 1];
-      return q & 1 ? bf16_hi(wv) : bf16_lo(wv);
-    };
+    auto xval = [&](int tt, int q) { return xc[tt][q]; };
     if constexpr (!PRE) {
       const __amdgpu_buffer_rsrc_t rsy = make_rsrc(yp, rows_of(cc) * (uint32_t)dim * 2u);
       // outputs of row tile I = nh: rows 16 I + 4 g + q, column p

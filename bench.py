@@ -483,12 +483,14 @@ def bench_ssd(steps: int, warmup: int):
     ms = e0.elapsed_time(e1) / steps
 
     # matrix-core work of the masked-matrix form at the kernel's 32-step chunks:
-    # per (batch row, head, chunk) the lower triangle of C B^T (Q(Q+1)/2 N) and of
-    # P x (Q(Q+1)/2 P), C h (Q N P) and the state update (Q N P) multiply-adds
+    # per (batch row, chunk) the lower triangle of C B^T (Q(Q+1)/2 N, shared by
+    # the heads), per (batch row, head, chunk) that of P x (Q(Q+1)/2 P), C h
+    # (Q N P) and the state update (Q N P) multiply-adds
     Q, P, N = 32, w.headdim, w.dstate
     heads = w.dim // P
     chunks = (w.seqlen + Q - 1) // Q
-    flops = 2 * w.batch * heads * chunks * (Q * (Q + 1) // 2 * (N + P) + 2 * Q * N * P)
+    flops = 2 * w.batch * chunks * (Q * (Q + 1) // 2 * N
+                                    + heads * (Q * (Q + 1) // 2 * P + 2 * Q * N * P))
     nbytes = w.algorithmic_bytes()
 
     # the same problem on the per-channel recurrence kernels (one input set)

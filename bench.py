@@ -212,7 +212,8 @@ def bench_scan(steps: int, warmup: int, ramp_s: float):
     # the 256 MB Infinity Cache (one set is ~0.67 GB anyway)
     sets = [W.make_inputs(w, device=dev, layer=i) for i in range(2)]
     outs = [torch.empty_like(s["x"]) for s in sets]
-    G, K = ssm.scan_plan(w.batch, w.seqlen, w.dim)
+    G, K, ph = ssm.scan_plan(w.batch, w.seqlen, w.dim, with_phase=True)
+    base = ph & 4  # the plan's schedule: 0 two-launch, 4 three-pass
     nws = ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim, nchunks=K)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
@@ -222,10 +223,10 @@ def bench_scan(steps: int, warmup: int, ramp_s: float):
         kw = dict(waves_per_group=G, nchunks=K, out=y, workspace=ws)
         if ev is not None:
             ev[0].record()
-        ssm.scan_fwd(*args, phase=1, **kw)
+        ssm.scan_fwd(*args, phase=base | 1, **kw)
         if ev is not None:
             ev[1].record()
-        ssm.scan_fwd(*args, phase=2, **kw)
+        ssm.scan_fwd(*args, phase=base | 2, **kw)
         if ev is not None:
             ev[2].record()
 
@@ -246,37 +247,41 @@ def bench_scan(steps: int, warmup: int, ramp_s: float):
     ev_step = [e[0].elapsed_time(e[2]) for e in evs]
     ev_main = [e[1].elapsed_time(e[2]) for e in evs]
     ev_first = [e[0].elapsed_time(e[1]) for e in evs]
-    return dict(w=w, G=G, K=K, wall_s=wall, step_ms=t_all[0].elapsed_time(t_all[1]) / steps,
+    return dict(w=w, G=G, K=K, three_pass=bool(base), wall_s=wall, step_ms=t_all[0].elapsed_time(t_all[1]) / steps,
                 main_ms=sum(ev_main) / steps, first_ms=sum(ev_first) / steps, inp=sets[0],
                 step_pct=percentiles(ev_step), main_pct=percentiles(ev_main),
                 ramp_steps=ramp_steps)
 
 
-def sweep_plans(spec: str, steps: int, ramp_s: float):
-    """Chunk plans "GxK,GxK,..." of the Mamba-2.8B layer scan under both
-    schedules (two-launch: phases 1 and 2; three-pass: phases 5 and 6): median
-    ms of each launch group and of the step over `steps` timed steps, two
-    input sets alternated."""
+def sweep_plans(spec: str, steps: int, ramp_s: float, wname: str = ""):
+    """Chunk plans "GxK,GxK,..." of a scan workload (the Mamba-2.8B layer by
+    default) under both schedules (two-launch: phases 1 and 2; three-pass:
+    phases 5 and 6): median ms of each launch group and of the step over
+    `steps` timed steps, with input sets rotated (two, or six for the
+    Mamba-130M layer, so no step reads what an earlier one left in the 256 MB
+    Infinity Cache)."""
     import torch
     import selective_state_space_44_amd as ssm
     from selective_state_space_44_amd import workloads as W
 
-    w = W.MAMBA_2P8B
+    w = W.WORKLOADS[wname] if wname else W.MAMBA_2P8B
+    nsets = 6 if w.algorithmic_bytes() < 256 << 20 else 2
     dev = "cuda:0"
     plans = [tuple(int(v) for v in p.split("x")) for p in spec.split(",") if p]
-    sets = [W.make_inputs(w, device=dev, layer=i) for i in range(2)]
+    sets = [W.make_inputs(w, device=dev, layer=i) for i in range(nsets)]
     outs = [torch.empty_like(s["x"]) for s in sets]
     kmax = max(k for _, k in plans)
-    ws = torch.empty(ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim, nchunks=kmax) + 256,
+    ws = torch.empty(ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim, dtype=w.io_dtype,
+                                              nchunks=kmax) + 256,
                      dtype=torch.uint8, device=dev)
 
     def run(G, K, i, phase):
-        s = sets[i % 2]
+        s = sets[i % nsets]
         ssm.scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], None,
-                     waves_per_group=G, nchunks=K, out=outs[i % 2], workspace=ws, phase=phase)
+                     waves_per_group=G, nchunks=K, out=outs[i % nsets], workspace=ws, phase=phase)
 
-    G0, K0 = ssm.scan_plan(w.batch, w.seqlen, w.dim)
-    ramp = clock_ramp(lambda i: run(G0, K0, i, 3), ramp_s) if ramp_s > 0 else 0
+    G0, K0, P0 = ssm.scan_plan(w.batch, w.seqlen, w.dim, dtype=w.io_dtype, with_phase=True)
+    ramp = clock_ramp(lambda i: run(G0, K0, i, P0), ramp_s) if ramp_s > 0 else 0
     med = lambda v: sorted(v)[len(v) // 2]
     rows = []
     for G, K in plans:
@@ -296,7 +301,8 @@ def sweep_plans(spec: str, steps: int, ramp_s: float):
                          "first_ms": med([e[0].elapsed_time(e[1]) for e in ev]),
                          "main_ms": med([e[1].elapsed_time(e[2]) for e in ev]),
                          "step_ms": med([e[0].elapsed_time(e[2]) for e in ev])})
-    return {"workload": w.name, "steps": steps, "clock_ramp_steps": ramp, "auto_plan": [G0, K0],
+    return {"workload": w.name, "steps": steps, "clock_ramp_steps": ramp,
+            "auto_plan": [G0, K0, "three-pass" if P0 & 4 else "two-launch"],
             "plans": rows}
 
 
@@ -311,7 +317,7 @@ def bench_config(w, sets_n: int, steps: int, warmup: int):
     dev = "cuda:0"
     sets = [W.make_inputs(w, device=dev, layer=i) for i in range(sets_n)]
     outs = [torch.empty_like(s["x"]) for s in sets]
-    G, K = ssm.scan_plan(w.batch, w.seqlen, w.dim, dtype=w.io_dtype)
+    G, K, ph = ssm.scan_plan(w.batch, w.seqlen, w.dim, dtype=w.io_dtype, with_phase=True)
     nws = ssm.scan_workspace_bytes(w.batch, w.seqlen, w.dim, dtype=w.io_dtype, nchunks=K)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
@@ -334,7 +340,8 @@ def bench_config(w, sets_n: int, steps: int, warmup: int):
     nbytes = w.algorithmic_bytes()
     res = {"batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
            "io_dtype": "f32" if w.io_dtype == torch.float32 else "bf16",
-           "plan": {"waves_per_group": G, "nchunks": K}, "steps": steps,
+           "plan": {"waves_per_group": G, "nchunks": K,
+                    "schedule": "three-pass" if ph & 4 else "two-launch"}, "steps": steps,
            "input_sets": sets_n, "rotated_bytes": nbytes * sets_n,
            "ms_per_step": mean, "ms_percentiles": percentiles(ms),
            "value": w.elements / (mean * 1e-3), "unit": "elements/s",
@@ -448,6 +455,41 @@ def bench_ssd_forward(steps: int, warmup: int):
     ms = e0.elapsed_time(e1) / steps
     return {"workload": w.name, "ms_per_step": ms, "value": w.elements / (ms * 1e-3),
             "unit": "elements/s"}
+
+
+def bench_ssd_backward(steps: int, warmup: int):
+    """The masked-matrix backward alone at the Mamba-2-like layer (one input
+    set, one upstream dy), for profiler runs."""
+    import torch
+    import selective_state_space_44_amd as ssm
+    from selective_state_space_44_amd import workloads as W
+
+    w = W.SSD_2P7B
+    dev = "cuda:0"
+    f = W.make_ssd_inputs(w, device=dev, layer=0)
+    P, N = w.headdim, w.dstate
+    heads = w.dim // P
+    g = torch.Generator(device=dev).manual_seed(19)
+    dy = torch.randn(f["x"].shape, generator=g, device=dev).to(f["x"].dtype)
+    nws = ssm.load_library().ssm_ssd_bwd_workspace_bytes(w.batch, w.seqlen, heads, P, N,
+                                                           1 if w.io_dtype == torch.bfloat16 else 0)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        ssm.ssd_bwd(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
+                    dy=dy, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": w.name, "ms_per_step": ms, "workspace_bytes": nws}
 
 
 def bench_ssd(steps: int, warmup: int):
@@ -673,9 +715,16 @@ def main():
                     help="the masked-matrix scan's forward only (for profiler runs)")
     ap.add_argument("--only-decode", action="store_true",
                     help="the decode sweep only (for profiler runs)")
+    ap.add_argument("--only-config", default="",
+                    help="one of the other scan configurations only, by workload name "
+                         "(for profiler runs), e.g. mamba130m_b8_l2048_d1536")
+    ap.add_argument("--only-ssd-bwd", action="store_true",
+                    help="the masked-matrix scan's backward only (for profiler runs)")
     ap.add_argument("--sweep-plans", default="",
                     help="only time these chunk plans of the headline scan, e.g. 4x4,4x5,8x2 "
                          "(waves per group x chunks), under both schedules")
+    ap.add_argument("--sweep-workload", default="",
+                    help="the workload of --sweep-plans (default: the Mamba-2.8B layer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -711,9 +760,26 @@ def main():
         print(json.dumps({"decode": bench_decode(args.decode_sweeps)}), flush=True)
         return
 
+    if args.only_config:
+        from selective_state_space_44_amd import workloads as W
+        spec = {W.TINY.name: (1, max(20, args.steps), 5),
+                W.MAMBA_130M.name: (6, max(30, args.steps), 6),
+                W.LONG_CTX.name: (1, args.steps, 2)}
+        if args.only_config not in spec:
+            print(f"bench.py: --only-config takes one of {sorted(spec)}", file=sys.stderr)
+            sys.exit(2)
+        w = W.WORKLOADS[args.only_config]
+        print(json.dumps({"config": {w.name: bench_config(w, *spec[w.name])}}), flush=True)
+        return
+
+    if args.only_ssd_bwd:
+        print(json.dumps({"ssd_bwd": bench_ssd_backward(args.steps, args.warmup)}), flush=True)
+        return
+
     if args.sweep_plans:
         print(json.dumps({"plan_sweep": sweep_plans(args.sweep_plans, args.steps,
-                                                    args.ramp_seconds)}), flush=True)
+                                                    args.ramp_seconds, args.sweep_workload)}),
+              flush=True)
         return
 
     r = bench_scan(args.steps, args.warmup, args.ramp_seconds)
@@ -721,8 +787,9 @@ def main():
     elems = w.elements
     value = elems / (r["step_ms"] * 1e-3)
     alg_bytes = w.algorithmic_bytes()
-    # the main-pass launch covers chunks 1 .. K-1 (chunk 0 runs in the first launch)
-    rows0 = chunk_rows(w.seqlen, r["K"]) if r["K"] > 1 else 0
+    # the main-pass launch covers chunks 1 .. K-1 in the two-launch schedule
+    # (chunk 0 runs in the first launch), every chunk in the three-pass one
+    rows0 = chunk_rows(w.seqlen, r["K"]) if r["K"] > 1 and not r["three_pass"] else 0
     main_rows = w.seqlen - rows0
     main_elems = w.batch * main_rows * w.dim * w.dstate
     main_bytes = scan_bytes(w, main_rows)
@@ -745,10 +812,11 @@ def main():
                    "dstate": w.dstate, "io_dtype": "bf16", "state_dtype": "f32",
                    "compute_dtype": "f32",
                    "plan": {"waves_per_group": r["G"], "nchunks": r["K"],
-                            "schedule": "two-launch"}},
+                            "schedule": "three-pass" if r["three_pass"] else "two-launch"}},
         "roofline": {
             "bound": "alu",
-            "kernel": "scan_fwd_kernel (main pass, chunks 1..K-1)",
+            "kernel": "scan_fwd_kernel (main pass, chunks %s)"
+                      % ("0..K-1" if r["three_pass"] else "1..K-1"),
             "achieved": ALU_OPS_PER_ELEMENT * main_elems / main_s / 1e12,
             "peak": ALU_OPS_PER_ELEMENT * ALU_PEAK_ELEMS / 1e12,
             "unit": "TOP/s",

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 /* Values of the io_dtype arguments. */
 #define SSM_DTYPE_F32 0
@@ -85,11 +85,15 @@ const char *ssm_status_str(int status);
  * and are stitched by a cross-chunk carry.  The plan changes only the
  * schedule, never the definition of the result.
  *
- * ssm_scan_plan() fills in the plan ssm_scan_fwd() uses for these sizes.
- * Returns SSM_ERR_INVALID_ARG for negative sizes or NULL outputs.
+ * ssm_scan_plan() fills in the plan ssm_scan_fwd() uses for these sizes and,
+ * when `phase` is not NULL, the phase value of the schedule it runs in (3:
+ * two-launch, 7: three-pass; see ssm_scan_fwd_phase).  The chunk count and
+ * the schedule come from a cost model of the launches on MI355X's 256 CUs
+ * (blocks per CU, resident blocks, the pre-pass's cost per step).
+ * Returns SSM_ERR_INVALID_ARG for negative sizes or NULL plan outputs.
  */
 int ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                  int io_dtype, int *waves_per_group, int *nchunks);
+                  int io_dtype, int *waves_per_group, int *nchunks, int *phase);
 
 /*
  * Device workspace, in bytes, that ssm_scan_fwd_planned() needs for a scan
@@ -136,9 +140,10 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 /*
  * ssm_scan_fwd with an explicit plan (for tests and tuning).  A value <= 0
  * for waves_per_group or nchunks takes the automatic choice for that field.
- * nchunks is clamped to [1, seqlen].  Unsupported waves_per_group values
- * return SSM_ERR_UNSUPPORTED.  The workspace must be sized with the same
- * nchunks.
+ * nchunks is clamped to [1, seqlen].  The schedule (two-launch or
+ * three-pass, ssm_scan_fwd_phase) is the one the cost model prefers for the
+ * resulting chunk count.  Unsupported waves_per_group values return
+ * SSM_ERR_UNSUPPORTED.  The workspace must be sized with the same nchunks.
  */
 int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim,
                          int64_t dstate, int io_dtype, const void *x,
@@ -153,7 +158,7 @@ int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim,
  * to time or overlap them).  The update composes associatively over chunks
  * (paperlens tutorial, section "代償と、それを払う方法（並列スキャン）"), so
  * every chunk but the first can start from a state that a cheaper pass has
- * computed.  Default (two-launch) schedule, phase bits:
+ * computed.  Two-launch schedule, phase bits:
  *   1 -- chunk 0's main pass (its part of y, and the state entering chunk 1)
  *        in one launch with the pre-pass of chunks 1 .. nchunks-2 (each run
  *        from a zero state, end state recorded), then the composition of
@@ -161,8 +166,8 @@ int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim,
  *        the workspace;
  *   2 -- the main pass of chunks 1 .. nchunks-1 from their entering states,
  *        writing the rest of y and h_last (reads the workspace phase 1 wrote);
- *   3 -- both, in order (what ssm_scan_fwd_planned enqueues).
- * Adding 4 selects the three-pass schedule instead (kept for comparison):
+ *   3 -- both, in order.
+ * Adding 4 selects the three-pass schedule instead:
  *   5 -- the pre-pass of chunks 0 .. nchunks-2 and the composition (nothing
  *        but the workspace written);  6 -- the main pass of every chunk;
  *   7 -- both.

@@ -46,7 +46,7 @@ SIGNATURES = {
     "ssm_abi_version": (_int, []),
     "ssm_status_str": (ctypes.c_char_p, [_int]),
     "ssm_scan_plan": (_int, [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(_int),
-                             ctypes.POINTER(_int)]),
+                             ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "ssm_scan_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _int, _int]),
     "ssm_scan_fwd": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10 + [_vp, _sz, _vp]),
     "ssm_scan_fwd_planned": (_int, [_i64, _i64, _i64, _i64, _int] + [_vp] * 10
@@ -142,12 +142,15 @@ def _stream(device):
 
 
 def scan_plan(batch: int, seqlen: int, dim: int, dstate: int = 16,
-              dtype: torch.dtype = torch.bfloat16):
-    """(waves_per_group, nchunks) that ``scan_fwd`` uses for these sizes."""
-    g, k = ctypes.c_int(), ctypes.c_int()
+              dtype: torch.dtype = torch.bfloat16, with_phase: bool = False):
+    """(waves_per_group, nchunks) that ``scan_fwd`` uses for these sizes; with
+    ``with_phase`` also the phase value of its schedule (3: two-launch, 7:
+    three-pass, as ``scan_fwd``'s ``phase`` takes them)."""
+    g, k, ph = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(load_library().ssm_scan_plan(batch, seqlen, dim, dstate, _io_code(dtype),
-                                        ctypes.byref(g), ctypes.byref(k)), "ssm_scan_plan")
-    return g.value, k.value
+                                        ctypes.byref(g), ctypes.byref(k), ctypes.byref(ph)),
+           "ssm_scan_plan")
+    return (g.value, k.value, ph.value) if with_phase else (g.value, k.value)
 
 
 def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16,
@@ -161,20 +164,21 @@ def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16,
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False,
              waves_per_group: int = 0, nchunks: int = 0, out=None, workspace=None,
-             phase: int = 3, discretization: str = "zoh"):
+             phase: int = 0, discretization: str = "zoh"):
     """Selective scan.  x, delta, z: [batch, L, dim]; B, C: [batch, L, dstate]
     (all float32 or all bfloat16); A [dim, dstate], D [dim], h0
     [batch, dim, dstate] float32.  Returns y (and the final state when
     ``return_last_state``).  ``waves_per_group``/``nchunks`` override the
-    automatic plan (0 = automatic); ``phase`` 1 or 2 enqueues only the first
-    or only the second launch of the chunked scan, 5, 6 or 7 the three-pass
-    schedule (see ssm_scan_fwd_phase); the phases of one scan must get the
-    same ``workspace`` and ``out``.
+    automatic plan (0 = automatic).  ``phase`` 0 runs the whole scan in the
+    schedule the plan prefers (``ssm_scan_fwd_planned``); 1, 2 or 3 enqueue
+    the first, the second or both launches of the two-launch schedule, 5, 6
+    or 7 those of the three-pass schedule (``ssm_scan_fwd_phase``); the
+    phases of one scan must get the same ``workspace`` and ``out``.
 
     Variants (``ssm_scan_fwd_ex``): ``A`` of shape [dim] holds one value per
     channel shared by its states (then ``B``/``C`` fix dstate);
     ``discretization="euler"`` uses Bbar = delta*B instead of the zero-order
-    hold.  Both run as one call (``phase`` must be 3)."""
+    hold.  Both run as one call (``phase`` must be 0), in the plan's schedule."""
     if not isinstance(x, torch.Tensor) or x.dim() != 3:
         raise ValueError("x must be a [batch, seqlen, dim] tensor")
     device = x.device
@@ -190,11 +194,11 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
     per_channel = A.dim() == 1
     dstate = B.shape[2] if per_channel else A.shape[1]
     variant = per_channel or discretization != "zoh"
-    if variant and phase != 3:
-        raise ValueError("the A-per-channel and Euler variants run as one call (phase 3)")
-    if phase not in (1, 2, 3, 5, 6, 7):
-        raise ValueError("phase must be 1, 2 or 3 (two-launch schedule) or 5, 6 or 7 "
-                         "(three-pass schedule)")
+    if variant and phase != 0:
+        raise ValueError("the A-per-channel and Euler variants run as one call (phase 0)")
+    if phase not in (0, 1, 2, 3, 5, 6, 7):
+        raise ValueError("phase must be 0 (the plan's schedule), 1, 2 or 3 (two-launch "
+                         "schedule) or 5, 6 or 7 (three-pass schedule)")
     io = x.dtype
     code = _io_code(io)
     _require(x, "x", (batch, seqlen, dim), io, device)
@@ -227,12 +231,19 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_last_state=False
                                  int(nchunks), _stream(device))
         _check(st, "ssm_scan_fwd_ex")
         return (y, h_last) if return_last_state else y
-    st = lib.ssm_scan_fwd_phase(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
-                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                                _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,
-                                int(waves_per_group), int(nchunks), int(phase),
-                                _stream(device))
-    _check(st, "ssm_scan_fwd")
+    if phase == 0:
+        st = lib.ssm_scan_fwd_planned(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
+                                      _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,
+                                      int(waves_per_group), int(nchunks), _stream(device))
+        _check(st, "ssm_scan_fwd_planned")
+    else:
+        st = lib.ssm_scan_fwd_phase(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta),
+                                    _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                    _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,
+                                    int(waves_per_group), int(nchunks), int(phase),
+                                    _stream(device))
+        _check(st, "ssm_scan_fwd_phase")
     return (y, h_last) if return_last_state else y
 
 

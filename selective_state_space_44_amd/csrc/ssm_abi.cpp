@@ -16,35 +16,21 @@ namespace {
 constexpr int64_t kWave = 64;
 constexpr int64_t kDState = 16;
 // Design point of the schedule (MI355X: 256 CUs).  The scan's inner loop is
-// bound by VALU issue, which needs several resident waves per SIMD; measured
-// on the benchmark shapes, 4 waves per 64-channel group (4 states each) with
-// about five such blocks per CU is fastest, even though most chunks then run
-// a second, cheaper pre-pass.  In the two-launch schedule the second launch
-// holds the main pass of chunks 1 .. K-1, so the plan sizes K - 1 (not K) to
-// the target: at the Mamba-2.8B layer shape (320 groups) K = 5 measured
-// 0.474 ms per scan against 0.485 ms at K = 4 and 0.495 ms at K = 8.
+// bound by VALU issue, which needs several resident waves per SIMD: the plan
+// keeps 4 waves per 64-channel group (4 states each; at most five such blocks
+// fit a CU's LDS) and picks the chunk count K and the schedule with the cost
+// model of plan_cost below.
 constexpr int64_t kCUs = 256;
-constexpr int64_t kTargetBlocks = 5 * kCUs;
+constexpr int64_t kResident = 5;     // main-pass blocks per CU (30 KB of LDS each)
+constexpr int64_t kTargetBlocks = kResident * kCUs;
 constexpr int64_t kMinChunk = 256;   // shortest chunk the plan will cut
 // Longest chunk the plan leaves: long sequences with few channel groups get
 // at least L / kMaxChunk chunks, so that blocks stay short enough to balance
 // over the CUs (single sequence, L = 262144, D = 4096: 7.3 ms at 20 chunks,
-// 6.6 ms at 128 or more).
+// 6.6-6.9 ms at 64 to 256).
 constexpr int64_t kMaxChunk = 2048;
 
 bool valid_dtype(int t) { return t == SSM_DTYPE_F32 || t == SSM_DTYPE_BF16; }
-
-// Automatic plan: 4 waves per group of 64 channels, and enough chunks that
-// the main pass of chunks 1 .. K-1 makes about kTargetBlocks blocks (never
-// chunks shorter than kMinChunk, nor longer than kMaxChunk).
-void auto_plan(int64_t batch, int64_t seqlen, int64_t dim, int* G, int* K) {
-  const int64_t groups = batch * ((dim + kWave - 1) / kWave);
-  int64_t k = (kTargetBlocks + groups / 2) / std::max<int64_t>(1, groups) + 1;
-  k = std::min<int64_t>(k, std::max<int64_t>(1, seqlen / kMinChunk));
-  k = std::max<int64_t>(k, (seqlen + kMaxChunk - 1) / kMaxChunk);
-  *G = 4;
-  *K = (int)std::max<int64_t>(1, k);
-}
 
 constexpr int64_t kMaxGridYZ = 65535;  // HIP limit on grid.y and grid.z
 // Batch rows per launch when a scan has more than kMaxGridYZ rows: a multiple
@@ -74,6 +60,80 @@ int effective_chunks(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks)
   if (seqlen <= 0) return 1;
   const int64_t len = chunk_length(seqlen, dim, io_dtype, nchunks);
   return (int)((seqlen + len - 1) / len);
+}
+
+// Cost model of a chunk plan, in steps on the critical path (fitted to plan
+// sweeps of three layer shapes on MI355X: batch 4 x 4096 x 5120, 8 x 2048 x
+// 1536 and 1 x 262144 x 4096; it ranks the fastest measured plan first on
+// each).  A launch of n equal blocks of `len` steps keeps its most loaded CU
+// busy for ceil(n / 256) blocks; with fewer than kResident blocks on a CU its
+// VALU issue slots go partly idle (measured slow-down for 1 .. 4 resident
+// blocks).  A pre-pass step (state only, from a zero state) costs kPre4 of a
+// main-pass step in a 4-wave block (two-launch schedule, beside chunk 0's main
+// pass) and kPre8 in the 8-wave blocks of the three-pass schedule.
+constexpr double kPre4 = 0.78, kPre8 = 0.72;
+
+double launch_cost(int64_t nblocks, int64_t len, double weight) {
+  static const double slow[kResident] = {1.6, 1.6, 1.25, 1.10, 1.03};
+  const int64_t r = (nblocks + kCUs - 1) / kCUs;
+  return (double)len * (double)r * weight * (r < kResident ? slow[r] : 1.0);
+}
+
+// Cost of K chunks of `len` steps for `groups` channel groups in the two
+// schedules (see launch_scan: two-launch = chunk 0's main pass beside the
+// pre-pass of chunks 1 .. K-2, then the main pass of chunks 1 .. K-1;
+// three-pass = the pre-pass of chunks 0 .. K-2, then the main pass of all K).
+void plan_cost(int64_t groups, int64_t len, int64_t k, double* two, double* three) {
+  if (k <= 1) {
+    *two = *three = launch_cost(groups, len, 1.0);
+    return;
+  }
+  const int64_t nb = groups * (k - 1);
+  *two = launch_cost(nb, len, (1.0 + kPre4 * (double)(k - 2)) / (double)(k - 1)) +
+         launch_cost(nb, len, 1.0);
+  *three = launch_cost(nb, len, kPre8) + launch_cost(groups * k, len, 1.0);
+}
+
+int64_t channel_groups(int64_t batch, int64_t dim) {
+  return std::max<int64_t>(1, batch * ((dim + kWave - 1) / kWave));
+}
+
+// Schedule bits (0: two-launch, ssm::kPhaseThreePass) that the model prefers
+// for K effective chunks.
+int plan_schedule(int64_t batch, int64_t seqlen, int64_t dim, int io_dtype, int k) {
+  if (k <= 1) return 0;
+  double two, three;
+  plan_cost(channel_groups(batch, dim), chunk_length(seqlen, dim, io_dtype, k), k, &two,
+            &three);
+  return three < two ? ssm::kPhaseThreePass : 0;
+}
+
+// Automatic plan: 4 waves per group of 64 channels; the chunk count is the
+// cheapest under plan_cost among K from L / kMaxChunk up to about twice the
+// count that gives the main pass kTargetBlocks blocks (chunks no shorter than
+// kMinChunk unless L / kMaxChunk asks for it); between equal costs (within
+// 0.2%) the larger K, whose shorter blocks balance better over the CUs.
+void auto_plan(int64_t batch, int64_t seqlen, int64_t dim, int io_dtype, int* G, int* K) {
+  *G = 4;
+  const int64_t groups = channel_groups(batch, dim);
+  const int64_t kt = (kTargetBlocks + groups / 2) / groups + 1;
+  const int64_t kcap = std::max<int64_t>(1, seqlen / kMinChunk);
+  const int64_t lo = std::max<int64_t>(1, (seqlen + kMaxChunk - 1) / kMaxChunk);
+  const int64_t hi = std::max({lo, std::min(2 * kt, kcap), std::min(2 * lo, kcap)});
+  const int64_t stride = std::max<int64_t>(1, (hi - lo) / 64);  // at most ~65 candidates
+  int best_k = effective_chunks(seqlen, dim, io_dtype, lo);
+  double best = -1.0;
+  for (int64_t c = lo; c <= hi; c += stride) {
+    const int k = effective_chunks(seqlen, dim, io_dtype, c);
+    double two, three;
+    plan_cost(groups, chunk_length(seqlen, dim, io_dtype, k), k, &two, &three);
+    const double cost = std::min(two, three);
+    if (best < 0.0 || cost <= best * 1.002) {
+      if (best < 0.0 || cost < best) best = cost;
+      best_k = k;
+    }
+  }
+  *K = best_k;
 }
 
 size_t workspace_for(int64_t batch, int64_t dim, int K) {
@@ -143,12 +203,13 @@ const char* ssm_status_str(int status) {
 }
 
 int ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
-                  int* waves_per_group, int* nchunks) {
+                  int* waves_per_group, int* nchunks, int* phase) {
   if (!waves_per_group || !nchunks || !sizes_ok(batch, seqlen, dim, dstate) ||
       !valid_dtype(io_dtype))
     return SSM_ERR_INVALID_ARG;
-  auto_plan(batch, seqlen, dim, waves_per_group, nchunks);
+  auto_plan(batch, seqlen, dim, io_dtype, waves_per_group, nchunks);
   *nchunks = effective_chunks(seqlen, dim, io_dtype, *nchunks);
+  if (phase) *phase = 3 | plan_schedule(batch, seqlen, dim, io_dtype, *nchunks);
   return SSM_OK;
 }
 
@@ -157,7 +218,7 @@ int64_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int
   if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype)) return -1;
   if (nchunks <= 0) {
     int g;
-    auto_plan(batch, seqlen, dim, &g, &nchunks);
+    auto_plan(batch, seqlen, dim, io_dtype, &g, &nchunks);
   }
   if (batch == 0 || dim == 0 || seqlen == 0) return 0;
   if (dstate != kDState) return 0;  // wide states: one pass, no carry workspace
@@ -179,7 +240,10 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
                int euler = 0, bool use_scratch = false) {
   if (!sizes_ok(batch, seqlen, dim, dstate) || !valid_dtype(io_dtype))
     return SSM_ERR_INVALID_ARG;
-  // phase: bits 1 and 2 select the launches, bit 4 the three-pass schedule
+  // phase: bits 1 and 2 select the launches, bit 4 the three-pass schedule;
+  // 0 = both launches in the schedule plan_schedule prefers
+  const bool auto_schedule = phase == 0;
+  if (auto_schedule) phase = 3;
   if (phase < 1 || phase > 7 || (phase & 3) == 0) return SSM_ERR_INVALID_ARG;
   if (batch == 0 || dim == 0) return SSM_OK;
   // state sizes other than 16 run the one-pass wide-state kernels: no chunk
@@ -224,8 +288,8 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
           at(delta, xrow), A, at(B, bcrow), at(C, bcrow), Dskip, at(z, xrow),
           reinterpret_cast<const float*>(at(h0, srow)), const_cast<char*>(at(y, xrow)),
           reinterpret_cast<float*>(const_cast<char*>(at(h_last, srow))), workspace,
-          workspace_bytes, waves_per_group, nchunks, phase, stream, pro, a_per_channel, euler,
-          use_scratch);
+          workspace_bytes, waves_per_group, nchunks, auto_schedule ? 0 : phase, stream, pro,
+          a_per_channel, euler, use_scratch);
       if (st != SSM_OK) return st;
     }
     return SSM_OK;
@@ -253,7 +317,7 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
   }
 
   int G = 0, K = 0;
-  auto_plan(batch, seqlen, dim, &G, &K);
+  auto_plan(batch, seqlen, dim, io_dtype, &G, &K);
   if (waves_per_group > 0) G = waves_per_group;
   if (nchunks > 0) K = nchunks;
   if (G != 2 && G != 4 && G != 8 && G != 16) return SSM_ERR_UNSUPPORTED;
@@ -261,6 +325,7 @@ int scan_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int i
   if ((a_per_channel || euler) && G == 16) return SSM_ERR_UNSUPPORTED;  // variants: G <= 8
   const int64_t chunk_len = chunk_length(seqlen, dim, io_dtype, K);
   K = effective_chunks(seqlen, dim, io_dtype, K);  // == ceil(seqlen / chunk_len)
+  if (auto_schedule) phase |= plan_schedule(batch, seqlen, dim, io_dtype, K);
 
   const ssm::ScanWorkspace ws = ssm::scan_workspace_layout(batch, dim, K);
   if (use_scratch && ws.total > 0) {
@@ -313,6 +378,7 @@ int ssm_scan_fwd_phase(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
                        const float* h0, void* y, float* h_last, void* workspace,
                        size_t workspace_bytes, int waves_per_group, int nchunks, int phase,
                        void* stream) {
+  if (phase < 1) return SSM_ERR_INVALID_ARG;
   const ssm::Prologue none{};
   return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
                     h_last, workspace, workspace_bytes, waves_per_group, nchunks, phase, stream,
@@ -329,7 +395,7 @@ int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
     return SSM_ERR_INVALID_ARG;
   const ssm::Prologue none{};
   return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
-                    h_last, workspace, workspace_bytes, waves_per_group, nchunks, 3, stream,
+                    h_last, workspace, workspace_bytes, waves_per_group, nchunks, 0, stream,
                     none, a_per_channel, discretization == SSM_DISC_EULER ? 1 : 0);
 }
 
@@ -352,7 +418,7 @@ int ssm_scan_fwd_fused(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   pro.d_conv = d_conv;
   pro.conv_silu = conv_silu;
   return scan_entry(batch, seqlen, dim, dstate, io_dtype, x_raw, delta_raw, A, B, C, Dskip, z,
-                    h0, y, h_last, workspace, workspace_bytes, waves_per_group, nchunks, 3,
+                    h0, y, h_last, workspace, workspace_bytes, waves_per_group, nchunks, 0,
                     stream, pro);
 }
 
@@ -362,9 +428,10 @@ int ssm_scan_fwd_planned(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
                          const float* h0, void* y, float* h_last, void* workspace,
                          size_t workspace_bytes, int waves_per_group, int nchunks,
                          void* stream) {
-  return ssm_scan_fwd_phase(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z,
-                            h0, y, h_last, workspace, workspace_bytes, waves_per_group,
-                            nchunks, 3, stream);
+  const ssm::Prologue none{};
+  return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
+                    h_last, workspace, workspace_bytes, waves_per_group, nchunks, 0, stream,
+                    none);
 }
 
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
@@ -382,7 +449,7 @@ int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
                          int nchunks, void* stream) {
   const ssm::Prologue none{};
   return scan_entry(batch, seqlen, dim, dstate, io_dtype, x, delta, A, B, C, Dskip, z, h0, y,
-                    h_last, nullptr, SSM_NOALLOC_SCRATCH_BYTES, waves_per_group, nchunks, 3,
+                    h_last, nullptr, SSM_NOALLOC_SCRATCH_BYTES, waves_per_group, nchunks, 0,
                     stream, none, 0, 0, true);
 }
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
     for code in range(5):
         assert lib.ssm_status_str(code).startswith(b"SSM_")
     assert b"UNKNOWN" in lib.ssm_status_str(99)
@@ -289,6 +289,7 @@ def test_decode_variants_reject_bad_arguments(lib):
 
 
 def test_plan_and_workspace(lib):
+    import torch
     g, k = ssm.scan_plan(4, 4096, 5120)
     assert g in (1, 2, 4, 8, 16) and k >= 1
     assert ssm.scan_workspace_bytes(4, 4096, 5120, nchunks=1) == 0
@@ -301,6 +302,18 @@ def test_plan_and_workspace(lib):
     # the long single sequence is cut into chunks for parallelism
     g3, k3 = ssm.scan_plan(1, 262144, 4096)
     assert k3 > 1 and 262144 / k3 <= 2048   # chunks of at most 2048 steps
+    # the cost model's choices on the three measured layer shapes (the
+    # fastest plan of each sweep): Mamba-2.8B and Mamba-130M layers in the
+    # two-launch schedule, the long single sequence in the three-pass one
+    assert ssm.scan_plan(4, 4096, 5120, with_phase=True) == (4, 5, 3)
+    assert ssm.scan_plan(8, 2048, 1536, with_phase=True) == (4, 5, 3)
+    assert ssm.scan_plan(1, 262144, 4096, with_phase=True) == (4, 256, 7)
+    # one chunk when the sequence is too short to cut: no schedule to choose
+    assert ssm.scan_plan(1, 256, 64, dtype=torch.float32, with_phase=True) == (4, 1, 3)
+    lib = ssm.load_library()
+    g, k = ctypes.c_int(), ctypes.c_int()
+    assert lib.ssm_scan_plan(4, 4096, 5120, 16, ssm.SSM_DTYPE_BF16, ctypes.byref(g),
+                             ctypes.byref(k), None) == ssm.SSM_OK and k.value == 5
     with pytest.raises(ValueError):
         ssm.scan_workspace_bytes(-1, 10, 10)
 

@@ -24,11 +24,12 @@ def _inputs(w, **kw):
 
 # phase 3: the two-launch schedule (chunk 0's main pass beside the pre-pass
 # of chunks 1..K-2); phase 7: the three-pass schedule (pre-pass of chunks
-# 0..K-2, then the main pass of every chunk)
+# 0..K-2, then the main pass of every chunk); phase 0 (the default of _run):
+# the schedule the plan prefers, as ssm_scan_fwd runs it
 SCHEDULES = {"two_launch": 3, "three_pass": 7}
 
 
-def _run(inp, G=0, K=0, with_state=True, phase=3, **over):
+def _run(inp, G=0, K=0, with_state=True, phase=0, **over):
     p = dict(inp, **over)
     return ssm.scan_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p.get("D"), p.get("z"),
                         p.get("h0"), return_last_state=with_state, waves_per_group=G,
@@ -91,7 +92,8 @@ def test_full_size_sampled_channels(w):
     """Full benchmark shapes in the automatic plan (the launch configuration
     the benchmark times); the oracle computes 256 sampled channels (plus the
     first and last) over the whole sequence for every batch row."""
-    print(f"full {w.name} plan={ssm.scan_plan(w.batch, w.seqlen, w.dim)}", flush=True)
+    print(f"full {w.name} plan={ssm.scan_plan(w.batch, w.seqlen, w.dim, with_phase=True)}",
+          flush=True)
     inp = _inputs(w)
     y, h = _run(inp)
     torch.cuda.synchronize()
@@ -124,7 +126,8 @@ def test_long_context_sampled_channels():
     256 channels spanning the bias range, including the 8 channels with the
     most negative bias (longest memory)."""
     w = W.LONG_CTX
-    print(f"full {w.name} plan={ssm.scan_plan(w.batch, w.seqlen, w.dim)}", flush=True)
+    print(f"full {w.name} plan={ssm.scan_plan(w.batch, w.seqlen, w.dim, with_phase=True)}",
+          flush=True)
     inp = _inputs(w)
     y, h = _run(inp)
     torch.cuda.synchronize()

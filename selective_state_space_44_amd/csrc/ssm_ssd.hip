@@ -344,13 +344,11 @@ void ssd_scan_kernel(SsdArgs a) {
 
   // ---- register loads -------------------------------------------------------
   // M tile w (waves 0..2) of a chunk
-  f32x4_t mreg = zero4;
   auto load_m = [&](const float* mtc) {
-    if (w < kTiles) {
-      const __amdgpu_buffer_rsrc_t rsm = make_rsrc(mtc, (uint32_t)(kMk * 4));
-      mreg = __builtin_bit_cast(
-          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsm, (uint32_t)lane * 16u, w * kWave * 16, 0));
-    }
+    if (w >= kTiles) return f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const __amdgpu_buffer_rsrc_t rsm = make_rsrc(mtc, (uint32_t)(kMk * 4));
+    return __builtin_bit_cast(
+        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsm, (uint32_t)lane * 16u, w * kWave * 16, 0));
   };
   // z of row tile nh as the identity A operand: row t, 32 channels
   auto load_z = [&](const uint16_t* zc, uint32_t rows) {
@@ -403,16 +401,22 @@ void ssd_scan_kernel(SsdArgs a) {
     steps(d0, 0);
     steps(d1, 1);
   }
+  // M tiles two chunks ahead: those of chunk c + 2 are loaded in chunk c's
+  // phase B into the registers chunk c's phase A has just read
+  f32x4_t mta = zero4, mtb = zero4;
   if constexpr (!PRE) {
     if constexpr (HAS_Z) za = load_z(zp, rows_of(0));
-    load_m(mtp);
+    mta = load_m(mtp);
+    mtb = load_m(nck_i > 1 ? mtp + kMk : mtp);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's copies have landed
   __syncthreads();
 
-  // One chunk; the loop runs two per iteration with the registers of z and dt
-  // swapping roles, so that no register copy waits for a load in flight.
-  auto chunk_step = [&](int cc, const u32x4_t& zop, u32x4_t& znext, uint32_t& dtr) {
+  // One chunk; the loop runs two per iteration with the registers of z, dt
+  // and the M tile swapping roles, so that no register copy waits for a load
+  // in flight.
+  auto chunk_step = [&](int cc, const u32x4_t& zop, u32x4_t& znext, uint32_t& dtr,
+                        f32x4_t& mreg) {
     const int pb = cc & 3;  // per-step values
     const int mb = cc & 1;  // double buffers
     const bool more = cc + 1 < nck_i;
@@ -480,7 +484,7 @@ void ssd_scan_kernel(SsdArgs a) {
     copy_x(mb ^ 1, xp + xstep, rows_of(cc + 1));
     copy_c(mb, cc + 2 < nck_i ? cpp + 2 * kCk : cpp);  // chunk cc + 2
     if constexpr (!PRE) {
-      load_m(more ? mtp + kMk : mtp);  // the next chunk's M tile and z
+      mreg = load_m(cc + 2 < nck_i ? mtp + 2 * kMk : mtp);  // M of chunk cc + 2
       if constexpr (HAS_Z) znext = load_z(zp + xstep, rows_of(cc + 1));
     }
     // x of the chunk in the result layout (exact): xc[tt][q] = x[16 tt + 4g +
@@ -569,8 +573,8 @@ void ssd_scan_kernel(SsdArgs a) {
   };
   u32x4_t zb = {0u, 0u, 0u, 0u};
   for (int cc = 0; cc < nck_i; cc += 2) {
-    chunk_step(cc, za, zb, da);
-    if (cc + 1 < nck_i) chunk_step(cc + 1, zb, za, db);
+    chunk_step(cc, za, zb, da, mta);
+    if (cc + 1 < nck_i) chunk_step(cc + 1, zb, za, db, mtb);
   }
 
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy into LDS outlives the block

@@ -799,6 +799,351 @@ __device__ __forceinline__ void main_block(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Main pass, wave-independent form (default formula, 4 waves per group, no
+// fused prologue).  Wave w of the block owns the 16 channels
+// d0 + 16w .. d0 + 16w + 15 with all 16 states: lane l holds channel
+// c = l % 16 of the wave and the states 4r .. 4r + 3 of its row r = l / 16
+// (rows of 16 lanes).  Each wave stages its own tiles of x, delta, B and C
+// through its own LDS region (x and delta as [channel][step], B and C as
+// [step][state]; the row's 16 lanes read the same B/C values), so no barrier
+// couples the block's waves.  Readout: per step every lane forms its 4-state
+// partial; after four steps the partials of the four rows are transposed
+// and summed by two cross-row lane exchanges (rows 0/1 and 2/3, then the two
+// halves of the wave) and three adds, which leave in row r the total of the
+// group's step r, summed in a fixed order.  Row r then finishes that step
+// (skip term, gate, store): each lane stores two steps of a tile.
+// ---------------------------------------------------------------------------
+constexpr int kWCh = kWave / 4;  // channels per wave
+
+struct WStage {
+  float x[kWCh * kXS];
+  float d[kWCh * kXS];
+  float b[kTileBC];
+  float c[kTileBC];
+};
+struct WSmem {
+  WStage st[4][2];  // [wave][stage]
+};
+
+// Lane coordinates of the wave-independent form.
+struct WLane {
+  int c, r;     // channel of the wave (0..15), row (0..3)
+  int d;        // channel index (clamped to dim - 1 past the end)
+  bool active;  // d < dim
+};
+
+__device__ __forceinline__ WLane wlane(int dim) {
+  WLane w;
+  const int lane = threadIdx.x % kWave;
+  w.c = lane % kWCh;
+  w.r = lane / kWCh;
+  const int draw = blockIdx.x * kWave + wave_id() * kWCh + w.c;
+  w.active = draw < dim;
+  w.d = w.active ? draw : dim - 1;
+  return w;
+}
+
+// Sum over the four rows, transposed: p[s] is this lane's partial of step s;
+// returns in row r the total of step r over the rows of this lane's column,
+// as (rows 0 + 1) + (rows 2 + 3).  The exchanges are v_permlane16_swap (odd
+// rows of the first operand with even rows of the second) and
+// v_permlane32_swap (upper half of the first with lower half of the second),
+// written as inline asm with both operands read and written: through the
+// compiler's builtins the float sum of a swap's two results was folded into
+// twice the first result.  The s_nop gives the two wait states the swap
+// needs after a VALU write of its operands.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float rows_transpose_sum(float p0, float p1, float p2, float p3) {
+  // after the swap, row r of p0 + p1 holds step r & 1 summed over rows
+  // (r & 2) and (r & 2) + 1; of p2 + p3, step 2 + (r & 1)
+  swap16(p0, p1);
+  swap16(p2, p3);
+  float su = p0 + p1;
+  float sv = p2 + p3;
+  // after the swap, su holds rows 0 + 1 and sv rows 2 + 3 of step r in row r
+  swap32(su, sv);
+  return su + sv;
+}
+
+// Raw values of one tile fetched by a lane: x and delta at steps r and r + 4
+// of its channel; B and C as two consecutive tile values each (bf16: one
+// 32-bit load; fp32: two loads).
+template <typename IO> struct WRaw {
+  static constexpr int kBC = sizeof(IO) == 2 ? 1 : 2;
+  uint32_t x[2], d[2];
+  uint32_t b[kBC], c[kBC];
+};
+
+template <typename IO>
+struct WLoader {
+  __amdgpu_buffer_rsrc_t rx, rd, rb, rc;
+  uint32_t voff, row_bytes;  // voff: row r, channel d (bytes)
+
+  __device__ __forceinline__ void init(const IO* x, const IO* delta, const IO* B, const IO* C,
+                                       int64_t seqlen, int dim, const Chunk& k, const WLane& w) {
+    rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
+    rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
+    rb = bc_rsrc(B, k, seqlen);
+    rc = bc_rsrc(C, k, seqlen);
+    row_bytes = (uint32_t)dim * sizeof(IO);
+    voff = (uint32_t)w.r * row_bytes + (uint32_t)w.d * sizeof(IO);
+  }
+
+  // Loads of the (full) tile starting at step s0 of the chunk.
+  __device__ __forceinline__ void issue(WRaw<IO>& t, int s0, int lane) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t so = (uint32_t)(s0 + 4 * j) * row_bytes;
+      t.x[j] = Raw<IO>::load(rx, voff, so);
+      t.d[j] = Raw<IO>::load(rd, voff, so);
+    }
+    const uint32_t bo = (uint32_t)s0 * kDState * sizeof(IO);
+    if constexpr (sizeof(IO) == 2) {
+      t.b[0] = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * 4u, bo, 0);
+      t.c[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)lane * 4u, bo, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        t.b[e] = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(2 * lane + e) * 4u, bo, 0);
+        t.c[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(2 * lane + e) * 4u, bo, 0);
+      }
+    }
+  }
+
+  // Write a fetched tile into the wave's LDS stage.  The wave's LDS accesses
+  // execute in program order; the empty asm statements with a memory clobber
+  // keep the compiler from moving the stage's reads across these writes
+  // (with no barrier between them, type-based alias analysis would let it
+  // reorder the 16-byte reads and the 4- or 2-byte writes).
+  __device__ __forceinline__ void put(const WRaw<IO>& t, WStage& st, const WLane& w,
+                                      int lane) const {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      Raw<IO>::put(st.x + w.c * kXS + 4 * j + w.r, t.x[j]);
+      Raw<IO>::put(st.d + w.c * kXS + 4 * j + w.r, t.d[j]);
+    }
+    if constexpr (sizeof(IO) == 2) {
+      Raw<IO>::put(st.b + 2 * lane, t.b[0] & 0xffffu);
+      Raw<IO>::put(st.b + 2 * lane + 1, t.b[0] >> 16);
+      Raw<IO>::put(st.c + 2 * lane, t.c[0] & 0xffffu);
+      Raw<IO>::put(st.c + 2 * lane + 1, t.c[0] >> 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        Raw<IO>::put(st.b + 2 * lane + e, t.b[e]);
+        Raw<IO>::put(st.c + 2 * lane + e, t.c[e]);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+};
+
+template <typename IO, bool HAS_Z, bool ZERO_A>
+__device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
+                                             const IO* __restrict__ delta,
+                                             const IO* __restrict__ B, const IO* __restrict__ C,
+                                             const IO* __restrict__ z, IO* __restrict__ y,
+                                             float Dd, int64_t seqlen, int dim, const Chunk& k,
+                                             const WLane& w, WStage (&sts)[2],
+                                             const float (&A2)[4], const float (&iA)[4],
+                                             float (&h)[4]) {
+  const int lane = threadIdx.x % kWave;
+  const int n0 = 4 * w.r;
+  const __amdgpu_buffer_rsrc_t rz = rows_rsrc(HAS_Z ? z : x, k.b, seqlen, dim, k.t_begin, k.t_end);
+  const __amdgpu_buffer_rsrc_t ry = rows_rsrc(y, k.b, seqlen, dim, k.t_begin, k.t_end);
+  WLoader<IO> ld;
+  ld.init(x, delta, B, C, seqlen, dim, k, w);
+  const uint32_t row_bytes = ld.row_bytes;
+  // lanes past the last channel store out of the buffer's range (dropped)
+  const uint32_t voff_y = w.active ? ld.voff : 0x80000000u;
+  const int nsteps = (int)(k.t_end - k.t_begin);
+  const int nfull = nsteps / kT;
+
+  // z of this lane's two steps (r, r + 4) of tile `tidx` (clamped)
+  auto issue_z = [&](uint32_t (&zr)[2], int tidx) {
+    if constexpr (HAS_Z) {
+      const int s0 = min(tidx, nfull - 1) * kT;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        zr[j] = Raw<IO>::load(rz, ld.voff, (uint32_t)(s0 + 4 * j) * row_bytes);
+    }
+  };
+
+  // Epilogue of step s0 + 4j + r: total S, skip term, gate.
+  auto finish = [&](float S, float xe, uint32_t zraw) {
+    const float pre = __builtin_fmaf(Dd, xe, S);
+    if constexpr (HAS_Z)
+      return pre * silu(Raw<IO>::f(zraw));
+    else
+      return pre;
+  };
+
+  auto tile = [&](int tidx, int cur, WRaw<IO>& rissue, const WRaw<IO>& rput,
+                  const uint32_t (&zuse)[2], uint32_t (&znext)[2]) {
+    const int s0 = tidx * kT;
+    ld.issue(rissue, min(tidx + 2, nfull - 1) * kT, lane);
+    issue_z(znext, tidx + 1);
+    const WStage& st = sts[cur];
+    float xv[kT], dv[kT];
+    read_half(st.x + w.c * kXS, xv, 0);
+    read_half(st.d + w.c * kXS, dv, 0);
+    float bq[2][4], cq[2][4];
+    auto fetch = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      read_n<4>(st.b + s * kDState + n0, bq[s & 1]);
+      read_n<4>(st.c + s * kDState + n0, cq[s & 1]);
+    };
+    float ca[2][4], cb[2][4], cc[2][4];
+    auto coefs = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
+        pin(ca[s & 1][n]);
+      }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const float bx = bq[s & 1][n] * xv[s];
+        const float a = ca[s & 1][n];
+        if constexpr (!ZERO_A) {
+          const float q = bx * iA[n];
+          cb[s & 1][n] = __builtin_fmaf(a, q, -q);
+        } else {
+          cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
+        }
+        pin(cb[s & 1][n]);
+        cc[s & 1][n] = cq[s & 1][n];
+      }
+    };
+    float p[4], yv[2];
+    fetch(std::integral_constant<int, 0>{});
+    fetch(std::integral_constant<int, 1>{});
+    coefs(std::integral_constant<int, 0>{});
+    static_for<kT>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s + 1 < kT) coefs(std::integral_constant<int, s + 1>{});
+      if constexpr (s + 2 == kT / 2) {
+        read_half(st.x + w.c * kXS, xv, kT / 2);
+        read_half(st.d + w.c * kXS, dv, kT / 2);
+      }
+      if constexpr (s + 2 < kT) fetch(std::integral_constant<int, s + 2>{});
+      h[0] = __builtin_fmaf(ca[s & 1][0], h[0], cb[s & 1][0]);
+      float acc = cc[s & 1][0] * h[0];
+#pragma unroll
+      for (int n = 1; n < 4; ++n) {
+        h[n] = __builtin_fmaf(ca[s & 1][n], h[n], cb[s & 1][n]);
+        acc = __builtin_fmaf(cc[s & 1][n], h[n], acc);
+      }
+      pin(acc);
+      p[s & 3] = acc;
+      if constexpr ((s & 3) == 3) {
+        constexpr int j = s / 4;
+        const float S = rows_transpose_sum(p[0], p[1], p[2], p[3]);
+        const float xe = st.x[w.c * kXS + 4 * j + w.r];
+        yv[j] = finish(S, xe, zuse[j]);
+      }
+    });
+    ld.put(rput, sts[cur ^ 1], w, lane);
+    Out<IO>::store2(yv[0], yv[1], ry, voff_y, (uint32_t)s0 * row_bytes,
+                    (uint32_t)(s0 + 4) * row_bytes);
+  };
+
+  if (nfull > 0) {
+    WRaw<IO> ra, rb;
+    uint32_t za[2], zb[2];
+    ld.issue(ra, 0, lane);
+    ld.issue(rb, min(1, nfull - 1) * kT, lane);
+    issue_z(za, 0);
+    ld.put(ra, sts[0], w, lane);
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+      tile(i, 0, ra, rb, za, zb);
+      tile(i + 1, 1, rb, ra, zb, za);
+    }
+    if (i < nfull) tile(i, 0, ra, rb, za, zb);
+  }
+
+  // ragged end of the chunk (fewer than kT steps): groups of four steps
+  // straight from memory; steps past the end contribute a zero partial
+  const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
+  const __amdgpu_buffer_rsrc_t rcc = bc_rsrc(C, k, seqlen);
+  const uint32_t voff_c = (uint32_t)w.d * sizeof(IO);
+  for (int g0 = nfull * kT; g0 < nsteps; g0 += 4) {
+    float p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      p[u] = 0.0f;
+      const int s = g0 + u;
+      if (s < nsteps) {
+        const uint32_t so = (uint32_t)s * row_bytes;
+        const float xs = buf<IO>::load(ld.rx, voff_c, so);
+        const float ds = buf<IO>::load(ld.rd, voff_c, so);
+        const uint32_t bo = (uint32_t)(s * kDState + n0) * sizeof(IO);
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const float Bn = buf<IO>::load(rbb, bo + n * sizeof(IO), 0);
+          const float Cn = buf<IO>::load(rcc, bo + n * sizeof(IO), 0);
+          float a, b;
+          step_coef<0, ZERO_A>(ds, xs, Bn, A2[n], iA[n], a, b);
+          h[n] = __builtin_fmaf(a, h[n], b);
+          acc = __builtin_fmaf(Cn, h[n], acc);
+        }
+        p[u] = acc;
+      }
+    }
+    const float S = rows_transpose_sum(p[0], p[1], p[2], p[3]);
+    if (g0 + w.r < nsteps) {  // this row's step of the group
+      const uint32_t so = (uint32_t)g0 * row_bytes;
+      const float xs = buf<IO>::load(ld.rx, ld.voff, so);
+      const float yv = finish(S, xs, HAS_Z ? Raw<IO>::load(rz, ld.voff, so) : 0u);
+      Out<IO>::store(yv, ry, voff_y, so);
+    }
+  }
+}
+
+// The wave-independent form serves the default formula with 4 waves per
+// group and no fused prologue; other plans and variants use scan_chunk.
+template <int G, bool FUSED, int V>
+constexpr bool kWaveForm = (G == 4 && !FUSED && V == 0);
+
+// Main pass of one block in the wave-independent form: `hinit` and `hout`
+// point at this lane's 4 states (nullable).
+template <typename IO, bool HAS_Z>
+__device__ __forceinline__ void main_block_w(
+    const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
+    const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
+    const IO* __restrict__ z, IO* __restrict__ y, const float* hinit, float* hout,
+    int64_t seqlen, int dim, const Chunk& k, const WLane& w, WSmem& sm) {
+  WStage(&sts)[2] = sm.st[wave_id()];
+  if constexpr (std::is_same<IO, bf16>::value) {
+    // bf16 inputs rely on zero lower halves of the slots
+    float4* p = reinterpret_cast<float4*>(&sts[0]);
+    constexpr int n = (int)(2 * sizeof(WStage) / sizeof(float4));
+    for (int i = threadIdx.x % kWave; i < n; i += kWave) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float A2[4], iA[4], h[4];
+  const bool zero = load_A<4, 0>(A, w.d, 4 * w.r, A2, iA);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[j] = hinit ? hinit[j] : 0.0f;
+  const float Dd = Dskip ? Dskip[w.d] : 0.0f;
+  if (__builtin_amdgcn_ballot_w64(zero) != 0)
+    scan_chunk_w<IO, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, A2, iA, h);
+  else
+    scan_chunk_w<IO, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, A2, iA, h);
+  if (hout && w.active) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hout[j] = h[j];
+  }
+}
+
 // Main pass over chunks c_first .. nchunks-1 (grid y: chunk - c_first, grid
 // z: batch row).  A chunk c > 0 starts from ws_hin[b, c]; chunk 0 from h0.
 // The last chunk writes h_last.
@@ -812,18 +1157,32 @@ void scan_fwd_kernel(
     float* __restrict__ h_last, const float* __restrict__ ws_hin, int64_t seqlen,
     int64_t chunk_len, int dim, int nchunks, int c_first, Prologue pro) {
   constexpr int NPL = kDState / G;
-  __shared__ MainSmem<G> sm;
   const Chunk k = chunk_coords(dim, seqlen, chunk_len, (int)blockIdx.y + c_first, blockIdx.z);
-  const int n0 = k.g * NPL;
-  const size_t bd = (size_t)k.b * dim + k.d;
-  const float* hinit = nullptr;
-  if (k.c > 0)
-    hinit = ws_hin + (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
-  else if (h0)
-    hinit = h0 + bd * kDState + n0;
-  float* hout = (k.c == nchunks - 1 && h_last) ? h_last + bd * kDState + n0 : nullptr;
-  main_block<IO, G, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k,
-                                     sm, pro);
+  if constexpr (kWaveForm<G, FUSED, V>) {
+    __shared__ WSmem smw;
+    const WLane w = wlane(dim);
+    const int n0 = 4 * w.r;
+    const size_t bd = (size_t)k.b * dim + w.d;
+    const float* hinit = nullptr;
+    if (k.c > 0)
+      hinit = ws_hin + (((size_t)k.b * nchunks + k.c) * dim + w.d) * kDState + n0;
+    else if (h0)
+      hinit = h0 + bd * kDState + n0;
+    float* hout = (k.c == nchunks - 1 && h_last) ? h_last + bd * kDState + n0 : nullptr;
+    main_block_w<IO, HAS_Z>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w, smw);
+  } else {
+    __shared__ MainSmem<G> sm;
+    const int n0 = k.g * NPL;
+    const size_t bd = (size_t)k.b * dim + k.d;
+    const float* hinit = nullptr;
+    if (k.c > 0)
+      hinit = ws_hin + (((size_t)k.b * nchunks + k.c) * dim + k.d) * kDState + n0;
+    else if (h0)
+      hinit = h0 + bd * kDState + n0;
+    float* hout = (k.c == nchunks - 1 && h_last) ? h_last + bd * kDState + n0 : nullptr;
+    main_block<IO, G, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim,
+                                       k, sm, pro);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1032,18 +1391,29 @@ void scan_first_kernel(
     float* __restrict__ ws_hloc, double* __restrict__ ws_sdelta, float* __restrict__ ws_hin,
     int64_t seqlen, int64_t chunk_len, int dim, int nchunks, Prologue pro) {
   constexpr int NPL = kDState / G;
+  using MainS = std::conditional_t<kWaveForm<G, FUSED, V>, WSmem, MainSmem<G>>;
   __shared__ union {
-    MainSmem<G> main;
+    MainS main;
     Stage<false> pre[2];
   } sm;
   const Chunk k = chunk_coords(dim, seqlen, chunk_len, blockIdx.z, blockIdx.y);
   if (k.c == 0) {
-    const int n0 = k.g * NPL;
-    const size_t bd = (size_t)k.b * dim + k.d;
-    const float* hinit = h0 ? h0 + bd * kDState + n0 : nullptr;
-    float* hout = ws_hin + (((size_t)k.b * nchunks + 1) * dim + k.d) * kDState + n0;
-    main_block<IO, G, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim,
-                                       k, sm.main, pro);
+    if constexpr (kWaveForm<G, FUSED, V>) {
+      const WLane w = wlane(dim);
+      const int n0 = 4 * w.r;
+      const size_t bd = (size_t)k.b * dim + w.d;
+      const float* hinit = h0 ? h0 + bd * kDState + n0 : nullptr;
+      float* hout = ws_hin + (((size_t)k.b * nchunks + 1) * dim + w.d) * kDState + n0;
+      main_block_w<IO, HAS_Z>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w,
+                              sm.main);
+    } else {
+      const int n0 = k.g * NPL;
+      const size_t bd = (size_t)k.b * dim + k.d;
+      const float* hinit = h0 ? h0 + bd * kDState + n0 : nullptr;
+      float* hout = ws_hin + (((size_t)k.b * nchunks + 1) * dim + k.d) * kDState + n0;
+      main_block<IO, G, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen,
+                                         dim, k, sm.main, pro);
+    }
   } else {
     pre_block<IO, G, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k,
                                sm.pre, pro);

@@ -822,8 +822,10 @@ struct WStage {
   float b[kTileBC];
   float c[kTileBC];
 };
+constexpr int kTrRow = 20;  // floats per channel of the readout transpose (16-byte rows)
 struct WSmem {
-  WStage st[4][2];  // [wave][stage]
+  WStage st[4][2];             // [wave][stage]
+  float tr[4][kWCh * kTrRow];  // [wave] readout transpose
 };
 
 // Lane coordinates of the wave-independent form.
@@ -846,29 +848,22 @@ __device__ __forceinline__ WLane wlane(int dim) {
 
 // Sum over the four rows, transposed: p[s] is this lane's partial of step s;
 // returns in row r the total of step r over the rows of this lane's column,
-// as (rows 0 + 1) + (rows 2 + 3).  The exchanges are v_permlane16_swap (odd
-// rows of the first operand with even rows of the second) and
-// v_permlane32_swap (upper half of the first with lower half of the second),
-// written as inline asm with both operands read and written: through the
-// compiler's builtins the float sum of a swap's two results was folded into
-// twice the first result.  The s_nop gives the two wait states the swap
-// needs after a VALU write of its operands.
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap32(float& a, float& b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float rows_transpose_sum(float p0, float p1, float p2, float p3) {
-  // after the swap, row r of p0 + p1 holds step r & 1 summed over rows
-  // (r & 2) and (r & 2) + 1; of p2 + p3, step 2 + (r & 1)
-  swap16(p0, p1);
-  swap16(p2, p3);
-  float su = p0 + p1;
-  float sv = p2 + p3;
-  // after the swap, su holds rows 0 + 1 and sv rows 2 + 3 of step r in row r
-  swap32(su, sv);
-  return su + sv;
+// as (rows 0 + 1) + (rows 2 + 3).  Through the wave's own LDS area: lane
+// (c, r) writes its partial of step s to tw[c][4s + r], then reads the four
+// rows' partials of step r as one 16-byte row tw[c][4r .. 4r + 3] (the
+// wave's LDS accesses execute in program order; the memory clobbers keep the
+// compiler from moving these accesses across each other).
+__device__ __forceinline__ float rows_transpose_sum(float* tw, const WLane& w, float p0,
+                                                    float p1, float p2, float p3) {
+  float* wp = tw + w.c * kTrRow + w.r;
+  asm volatile("" ::: "memory");
+  wp[0] = p0;
+  wp[4] = p1;
+  wp[8] = p2;
+  wp[12] = p3;
+  asm volatile("" ::: "memory");
+  const float4 v = *reinterpret_cast<const float4*>(tw + w.c * kTrRow + 4 * w.r);
+  return (v.x + v.y) + (v.z + v.w);
 }
 
 // Raw values of one tile fetched by a lane: x and delta at steps r and r + 4
@@ -951,7 +946,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
                                              const IO* __restrict__ B, const IO* __restrict__ C,
                                              const IO* __restrict__ z, IO* __restrict__ y,
                                              float Dd, int64_t seqlen, int dim, const Chunk& k,
-                                             const WLane& w, WStage (&sts)[2],
+                                             const WLane& w, WStage (&sts)[2], float* tw,
                                              const float (&A2)[4], const float (&iA)[4],
                                              float (&h)[4]) {
   const int lane = threadIdx.x % kWave;
@@ -1045,7 +1040,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
       p[s & 3] = acc;
       if constexpr ((s & 3) == 3) {
         constexpr int j = s / 4;
-        const float S = rows_transpose_sum(p[0], p[1], p[2], p[3]);
+        const float S = rows_transpose_sum(tw, w, p[0], p[1], p[2], p[3]);
         const float xe = st.x[w.c * kXS + 4 * j + w.r];
         yv[j] = finish(S, xe, zuse[j]);
       }
@@ -1099,7 +1094,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
         p[u] = acc;
       }
     }
-    const float S = rows_transpose_sum(p[0], p[1], p[2], p[3]);
+    const float S = rows_transpose_sum(tw, w, p[0], p[1], p[2], p[3]);
     if (g0 + w.r < nsteps) {  // this row's step of the group
       const uint32_t so = (uint32_t)g0 * row_bytes;
       const float xs = buf<IO>::load(ld.rx, ld.voff, so);
@@ -1123,6 +1118,7 @@ __device__ __forceinline__ void main_block_w(
     const IO* __restrict__ z, IO* __restrict__ y, const float* hinit, float* hout,
     int64_t seqlen, int dim, const Chunk& k, const WLane& w, WSmem& sm) {
   WStage(&sts)[2] = sm.st[wave_id()];
+  float* tw = sm.tr[wave_id()];
   if constexpr (std::is_same<IO, bf16>::value) {
     // bf16 inputs rely on zero lower halves of the slots
     float4* p = reinterpret_cast<float4*>(&sts[0]);
@@ -1135,9 +1131,11 @@ __device__ __forceinline__ void main_block_w(
   for (int j = 0; j < 4; ++j) h[j] = hinit ? hinit[j] : 0.0f;
   const float Dd = Dskip ? Dskip[w.d] : 0.0f;
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    scan_chunk_w<IO, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, A2, iA, h);
+    scan_chunk_w<IO, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2, iA,
+                                  h);
   else
-    scan_chunk_w<IO, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, A2, iA, h);
+    scan_chunk_w<IO, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2, iA,
+                                   h);
   if (hout && w.active) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) hout[j] = h[j];

@@ -823,7 +823,7 @@ struct WStage {
   float c[kTileBC];
 };
 constexpr int kTrRow = 20;  // floats per channel of the readout transpose (16-byte rows)
-struct WSmem {
+struct alignas(16) WSmem {
   WStage st[4][2];             // [wave][stage]
   float tr[4][kWCh * kTrRow];  // [wave] readout transpose
 };
@@ -875,7 +875,7 @@ template <typename IO> struct WRaw {
   uint32_t b[kBC], c[kBC];
 };
 
-template <typename IO>
+template <typename IO, bool WITH_C = true>
 struct WLoader {
   __amdgpu_buffer_rsrc_t rx, rd, rb, rc;
   uint32_t voff, row_bytes;  // voff: row r, channel d (bytes)
@@ -901,12 +901,14 @@ struct WLoader {
     const uint32_t bo = (uint32_t)s0 * kDState * sizeof(IO);
     if constexpr (sizeof(IO) == 2) {
       t.b[0] = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * 4u, bo, 0);
-      t.c[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)lane * 4u, bo, 0);
+      if constexpr (WITH_C)
+        t.c[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)lane * 4u, bo, 0);
     } else {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         t.b[e] = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(2 * lane + e) * 4u, bo, 0);
-        t.c[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(2 * lane + e) * 4u, bo, 0);
+        if constexpr (WITH_C)
+          t.c[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(2 * lane + e) * 4u, bo, 0);
       }
     }
   }
@@ -927,13 +929,15 @@ struct WLoader {
     if constexpr (sizeof(IO) == 2) {
       Raw<IO>::put(st.b + 2 * lane, t.b[0] & 0xffffu);
       Raw<IO>::put(st.b + 2 * lane + 1, t.b[0] >> 16);
-      Raw<IO>::put(st.c + 2 * lane, t.c[0] & 0xffffu);
-      Raw<IO>::put(st.c + 2 * lane + 1, t.c[0] >> 16);
+      if constexpr (WITH_C) {
+        Raw<IO>::put(st.c + 2 * lane, t.c[0] & 0xffffu);
+        Raw<IO>::put(st.c + 2 * lane + 1, t.c[0] >> 16);
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         Raw<IO>::put(st.b + 2 * lane + e, t.b[e]);
-        Raw<IO>::put(st.c + 2 * lane + e, t.c[e]);
+        if constexpr (WITH_C) Raw<IO>::put(st.c + 2 * lane + e, t.c[e]);
       }
     }
     asm volatile("" ::: "memory");
@@ -1101,6 +1105,149 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
       const float yv = finish(S, xs, HAS_Z ? Raw<IO>::load(rz, ld.voff, so) : 0u);
       Out<IO>::store(yv, ry, voff_y, so);
     }
+  }
+}
+
+// Chunk pre-pass in the wave-independent form (carry pass 1 beside chunk 0's
+// main pass in the first launch): the lane layout and per-wave staging of the
+// main pass, without C and the readout.  With no A == 0 in the wave the
+// state is carried as g = A*h: g = fma(a, g, fma(a, B*x, -B*x)), converted
+// back (h = g/A) at the end of the full tiles.  Sum of delta: row r adds
+// steps 2r and 2r + 1 of every tile (fp32 pair, then fp64); the rows' sums
+// are added in row order at the end.
+template <typename IO, bool ZERO_A>
+__device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
+                                              const IO* __restrict__ delta,
+                                              const IO* __restrict__ B, int64_t seqlen, int dim,
+                                              const Chunk& k, const WLane& w,
+                                              WStage (&sts)[2], const float (&A2)[4],
+                                              const float (&iA)[4], float (&h)[4], double& sd) {
+  const int lane = threadIdx.x % kWave;
+  const int n0 = 4 * w.r;
+  WLoader<IO, false> ld;
+  ld.init(x, delta, B, B, seqlen, dim, k, w);
+  const int nsteps = (int)(k.t_end - k.t_begin);
+  const int nfull = nsteps / kT;
+  float gs[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) gs[n] = 0.0f;
+
+  auto tile = [&](int tidx, int cur, WRaw<IO>& rissue, const WRaw<IO>& rput) {
+    ld.issue(rissue, min(tidx + 2, nfull - 1) * kT, lane);
+    const WStage& st = sts[cur];
+    float xv[kT], dv[kT];
+    read_row(st.x + w.c * kXS, xv);
+    read_row(st.d + w.c * kXS, dv);
+    float bq[2][4];
+    auto fetch = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      read_n<4>(st.b + s * kDState + n0, bq[s & 1]);
+    };
+    float ca[2][4], cb[2][4];
+    auto coefs = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
+        pin(ca[s & 1][n]);
+      }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const float bx = bq[s & 1][n] * xv[s];
+        const float a = ca[s & 1][n];
+        if constexpr (!ZERO_A)
+          cb[s & 1][n] = __builtin_fmaf(a, bx, -bx);  // (a - 1) * B x, for g = A h
+        else
+          cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
+        pin(cb[s & 1][n]);
+      }
+    };
+    fetch(std::integral_constant<int, 0>{});
+    fetch(std::integral_constant<int, 1>{});
+    coefs(std::integral_constant<int, 0>{});
+    static_for<kT>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s + 1 < kT) coefs(std::integral_constant<int, s + 1>{});
+      if constexpr (s + 2 < kT) fetch(std::integral_constant<int, s + 2>{});
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        gs[n] = __builtin_fmaf(ca[s & 1][n], gs[n], cb[s & 1][n]);
+        pin(gs[n]);
+      }
+    });
+    const float2 dd = *reinterpret_cast<const float2*>(st.d + w.c * kXS + 2 * w.r);
+    sd += (double)(dd.x + dd.y);
+    ld.put(rput, sts[cur ^ 1], w, lane);
+  };
+
+  if (nfull > 0) {
+    WRaw<IO> ra, rb;
+    ld.issue(ra, 0, lane);
+    ld.issue(rb, min(1, nfull - 1) * kT, lane);
+    ld.put(ra, sts[0], w, lane);
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+      tile(i, 0, ra, rb);
+      tile(i + 1, 1, rb, ra);
+    }
+    if (i < nfull) tile(i, 0, ra, rb);
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) h[n] = ZERO_A ? gs[n] : gs[n] * iA[n];
+
+  // ragged end of the chunk, one step at a time from memory
+  const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
+  const uint32_t voff_c = (uint32_t)w.d * sizeof(IO);
+  for (int s0 = nfull * kT; s0 < nsteps; ++s0) {
+    const uint32_t so = (uint32_t)s0 * ld.row_bytes;
+    const float xs = buf<IO>::load(ld.rx, voff_c, so);
+    const float ds = buf<IO>::load(ld.rd, voff_c, so);
+    const uint32_t bo = (uint32_t)(s0 * kDState + n0) * sizeof(IO);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      float a, b;
+      step_coef<0, ZERO_A>(ds, xs, buf<IO>::load(rbb, bo + n * sizeof(IO), 0), A2[n], iA[n], a,
+                           b);
+      h[n] = __builtin_fmaf(a, h[n], b);
+    }
+    if (w.r == 0) sd += (double)ds;
+  }
+}
+
+// Pre-pass block (chunk c of one 64-channel group from a zero state) in the
+// wave-independent form: writes hloc and the chunk's sum of delta.
+template <typename IO>
+__device__ __forceinline__ void pre_block_w(const IO* __restrict__ x, const IO* __restrict__ delta,
+                                            const float* __restrict__ A,
+                                            const IO* __restrict__ B, float* __restrict__ ws_hloc,
+                                            double* __restrict__ ws_sdelta, int64_t seqlen,
+                                            int dim, int nchunks, const Chunk& k, WSmem& sm) {
+  const WLane w = wlane(dim);
+  WStage(&sts)[2] = sm.st[wave_id()];
+  if constexpr (std::is_same<IO, bf16>::value) {
+    float4* p = reinterpret_cast<float4*>(&sts[0]);
+    constexpr int n = (int)(2 * sizeof(WStage) / sizeof(float4));
+    for (int i = threadIdx.x % kWave; i < n; i += kWave) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float A2[4], iA[4], h[4];
+  const bool zero = load_A<4, 0>(A, w.d, 4 * w.r, A2, iA);
+  double sd = 0.0;
+  if (__builtin_amdgcn_ballot_w64(zero) != 0)
+    chunk_state_w<IO, true>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
+  else
+    chunk_state_w<IO, false>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
+  // the rows' sums of delta through the wave's transpose area
+  double* td = reinterpret_cast<double*>(sm.tr[wave_id()]);
+  asm volatile("" ::: "memory");
+  td[w.r * kWCh + w.c] = sd;
+  asm volatile("" ::: "memory");
+  if (w.active) {
+    const size_t cd = ((size_t)k.b * nchunks + k.c) * dim + w.d;
+    float* hl = ws_hloc + cd * kDState + 4 * w.r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hl[j] = h[j];
+    if (w.r == 0)
+      ws_sdelta[cd] = ((td[w.c] + td[kWCh + w.c]) + td[2 * kWCh + w.c]) + td[3 * kWCh + w.c];
   }
 }
 
@@ -1413,8 +1560,11 @@ void scan_first_kernel(
                                          dim, k, sm.main, pro);
     }
   } else {
-    pre_block<IO, G, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k,
-                               sm.pre, pro);
+    if constexpr (kWaveForm<G, FUSED, V>)
+      pre_block_w<IO>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k, sm.main);
+    else
+      pre_block<IO, G, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k,
+                                 sm.pre, pro);
   }
 }
 

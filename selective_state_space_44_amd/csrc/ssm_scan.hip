@@ -800,8 +800,8 @@ __device__ __forceinline__ void main_block(
 }
 
 // ---------------------------------------------------------------------------
-// Main pass, wave-independent form (default formula, 4 waves per group, no
-// fused prologue).  Wave w of the block owns the 16 channels
+// Main pass, wave-independent form (4 waves per group, no fused prologue, A
+// per (channel, state); ZOH or Euler rule).  Wave w of the block owns the 16 channels
 // d0 + 16w .. d0 + 16w + 15 with all 16 states: lane l holds channel
 // c = l % 16 of the wave and the states 4r .. 4r + 3 of its row r = l / 16
 // (rows of 16 lanes).  Each wave stages its own tiles of x, delta, B and C
@@ -850,20 +850,18 @@ __device__ __forceinline__ WLane wlane(int dim) {
 // returns in row r the total of step r over the rows of this lane's column,
 // as (rows 0 + 1) + (rows 2 + 3).  Through the wave's own LDS area: lane
 // (c, r) writes its partial of step s to tw[c][4s + r], then reads the four
-// rows' partials of step r as one 16-byte row tw[c][4r .. 4r + 3] (the
-// wave's LDS accesses execute in program order; the memory clobbers keep the
-// compiler from moving these accesses across each other).
+// rows' partials of step r, tw[c][4r .. 4r + 3].  The wave's LDS accesses
+// execute in program order, and these writes and reads are float accesses
+// of the same array, so the compiler keeps their order too.
 __device__ __forceinline__ float rows_transpose_sum(float* tw, const WLane& w, float p0,
                                                     float p1, float p2, float p3) {
   float* wp = tw + w.c * kTrRow + w.r;
-  asm volatile("" ::: "memory");
   wp[0] = p0;
   wp[4] = p1;
   wp[8] = p2;
   wp[12] = p3;
-  asm volatile("" ::: "memory");
-  const float4 v = *reinterpret_cast<const float4*>(tw + w.c * kTrRow + 4 * w.r);
-  return (v.x + v.y) + (v.z + v.w);
+  const float* rp = tw + w.c * kTrRow + 4 * w.r;
+  return (rp[0] + rp[1]) + (rp[2] + rp[3]);
 }
 
 // Raw values of one tile fetched by a lane: x and delta at steps r and r + 4
@@ -944,7 +942,7 @@ struct WLoader {
   }
 };
 
-template <typename IO, bool HAS_Z, bool ZERO_A>
+template <typename IO, bool HAS_Z, bool ZERO_A, int V>
 __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
                                              const IO* __restrict__ delta,
                                              const IO* __restrict__ B, const IO* __restrict__ C,
@@ -953,6 +951,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
                                              const WLane& w, WStage (&sts)[2], float* tw,
                                              const float (&A2)[4], const float (&iA)[4],
                                              float (&h)[4]) {
+  static_assert((V & kScalarA) == 0, "A per channel uses scan_chunk");
   const int lane = threadIdx.x % kWave;
   const int n0 = 4 * w.r;
   const __amdgpu_buffer_rsrc_t rz = rows_rsrc(HAS_Z ? z : x, k.b, seqlen, dim, k.t_begin, k.t_end);
@@ -1007,11 +1006,14 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
         ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
         pin(ca[s & 1][n]);
       }
+      const float dx = dv[s] * xv[s];  // Euler: Bbar*x = (delta*x) * B
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const float bx = bq[s & 1][n] * xv[s];
         const float a = ca[s & 1][n];
-        if constexpr (!ZERO_A) {
+        if constexpr ((V & kEuler) != 0) {
+          cb[s & 1][n] = dx * bq[s & 1][n];
+        } else if constexpr (!ZERO_A) {
           const float q = bx * iA[n];
           cb[s & 1][n] = __builtin_fmaf(a, q, -q);
         } else {
@@ -1091,7 +1093,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
           const float Bn = buf<IO>::load(rbb, bo + n * sizeof(IO), 0);
           const float Cn = buf<IO>::load(rcc, bo + n * sizeof(IO), 0);
           float a, b;
-          step_coef<0, ZERO_A>(ds, xs, Bn, A2[n], iA[n], a, b);
+          step_coef<V, ZERO_A>(ds, xs, Bn, A2[n], iA[n], a, b);
           h[n] = __builtin_fmaf(a, h[n], b);
           acc = __builtin_fmaf(Cn, h[n], acc);
         }
@@ -1115,13 +1117,14 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
 // back (h = g/A) at the end of the full tiles.  Sum of delta: row r adds
 // steps 2r and 2r + 1 of every tile (fp32 pair, then fp64); the rows' sums
 // are added in row order at the end.
-template <typename IO, bool ZERO_A>
+template <typename IO, bool ZERO_A, int V>
 __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
                                               const IO* __restrict__ delta,
                                               const IO* __restrict__ B, int64_t seqlen, int dim,
                                               const Chunk& k, const WLane& w,
                                               WStage (&sts)[2], const float (&A2)[4],
                                               const float (&iA)[4], float (&h)[4], double& sd) {
+  static_assert((V & kScalarA) == 0, "A per channel uses chunk_state");
   const int lane = threadIdx.x % kWave;
   const int n0 = 4 * w.r;
   WLoader<IO, false> ld;
@@ -1151,11 +1154,14 @@ __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
         ca[s & 1][n] = fast_exp2(dv[s] * A2[n]);
         pin(ca[s & 1][n]);
       }
+      const float dx = dv[s] * xv[s];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const float bx = bq[s & 1][n] * xv[s];
         const float a = ca[s & 1][n];
-        if constexpr (!ZERO_A)
+        if constexpr ((V & kEuler) != 0)
+          cb[s & 1][n] = dx * bq[s & 1][n];
+        else if constexpr (!ZERO_A)
           cb[s & 1][n] = __builtin_fmaf(a, bx, -bx);  // (a - 1) * B x, for g = A h
         else
           cb[s & 1][n] = (__builtin_isinf(iA[n]) ? dv[s] : (a - 1.0f) * iA[n]) * bx;
@@ -1193,7 +1199,7 @@ __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
     if (i < nfull) tile(i, 0, ra, rb);
   }
 #pragma unroll
-  for (int n = 0; n < 4; ++n) h[n] = ZERO_A ? gs[n] : gs[n] * iA[n];
+  for (int n = 0; n < 4; ++n) h[n] = (ZERO_A || (V & kEuler)) ? gs[n] : gs[n] * iA[n];
 
   // ragged end of the chunk, one step at a time from memory
   const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
@@ -1206,7 +1212,7 @@ __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       float a, b;
-      step_coef<0, ZERO_A>(ds, xs, buf<IO>::load(rbb, bo + n * sizeof(IO), 0), A2[n], iA[n], a,
+      step_coef<V, ZERO_A>(ds, xs, buf<IO>::load(rbb, bo + n * sizeof(IO), 0), A2[n], iA[n], a,
                            b);
       h[n] = __builtin_fmaf(a, h[n], b);
     }
@@ -1216,7 +1222,7 @@ __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
 
 // Pre-pass block (chunk c of one 64-channel group from a zero state) in the
 // wave-independent form: writes hloc and the chunk's sum of delta.
-template <typename IO>
+template <typename IO, int V>
 __device__ __forceinline__ void pre_block_w(const IO* __restrict__ x, const IO* __restrict__ delta,
                                             const float* __restrict__ A,
                                             const IO* __restrict__ B, float* __restrict__ ws_hloc,
@@ -1230,12 +1236,12 @@ __device__ __forceinline__ void pre_block_w(const IO* __restrict__ x, const IO* 
     for (int i = threadIdx.x % kWave; i < n; i += kWave) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float A2[4], iA[4], h[4];
-  const bool zero = load_A<4, 0>(A, w.d, 4 * w.r, A2, iA);
+  const bool zero = load_A<4, V>(A, w.d, 4 * w.r, A2, iA);
   double sd = 0.0;
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    chunk_state_w<IO, true>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
+    chunk_state_w<IO, true, V>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
   else
-    chunk_state_w<IO, false>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
+    chunk_state_w<IO, false, V>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
   // the rows' sums of delta through the wave's transpose area
   double* td = reinterpret_cast<double*>(sm.tr[wave_id()]);
   asm volatile("" ::: "memory");
@@ -1251,14 +1257,16 @@ __device__ __forceinline__ void pre_block_w(const IO* __restrict__ x, const IO* 
   }
 }
 
-// The wave-independent form serves the default formula with 4 waves per
-// group and no fused prologue; other plans and variants use scan_chunk.
+// The wave-independent form serves plans of 4 waves per group without the
+// fused prologue, for A per (channel, state) with either discretisation rule;
+// A per channel, other plans and the fused scan use scan_chunk and
+// chunk_state (with A per channel the wave form measured 9-22% slower).
 template <int G, bool FUSED, int V>
-constexpr bool kWaveForm = (G == 4 && !FUSED && V == 0);
+constexpr bool kWaveForm = (G == 4 && !FUSED && (V & kScalarA) == 0);
 
 // Main pass of one block in the wave-independent form: `hinit` and `hout`
 // point at this lane's 4 states (nullable).
-template <typename IO, bool HAS_Z>
+template <typename IO, bool HAS_Z, int V>
 __device__ __forceinline__ void main_block_w(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
@@ -1273,15 +1281,16 @@ __device__ __forceinline__ void main_block_w(
     for (int i = threadIdx.x % kWave; i < n; i += kWave) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float A2[4], iA[4], h[4];
-  const bool zero = load_A<4, 0>(A, w.d, 4 * w.r, A2, iA);
+  const bool zero = load_A<4, V>(A, w.d, 4 * w.r, A2, iA);
 #pragma unroll
   for (int j = 0; j < 4; ++j) h[j] = hinit ? hinit[j] : 0.0f;
   const float Dd = Dskip ? Dskip[w.d] : 0.0f;
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    scan_chunk_w<IO, HAS_Z, true>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2, iA,
+    scan_chunk_w<IO, HAS_Z, true, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2, iA,
                                   h);
   else
-    scan_chunk_w<IO, HAS_Z, false>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2, iA,
+    scan_chunk_w<IO, HAS_Z, false, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2,
+                                      iA,
                                    h);
   if (hout && w.active) {
 #pragma unroll
@@ -1314,7 +1323,7 @@ void scan_fwd_kernel(
     else if (h0)
       hinit = h0 + bd * kDState + n0;
     float* hout = (k.c == nchunks - 1 && h_last) ? h_last + bd * kDState + n0 : nullptr;
-    main_block_w<IO, HAS_Z>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w, smw);
+    main_block_w<IO, HAS_Z, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w, smw);
   } else {
     __shared__ MainSmem<G> sm;
     const int n0 = k.g * NPL;
@@ -1549,7 +1558,7 @@ void scan_first_kernel(
       const size_t bd = (size_t)k.b * dim + w.d;
       const float* hinit = h0 ? h0 + bd * kDState + n0 : nullptr;
       float* hout = ws_hin + (((size_t)k.b * nchunks + 1) * dim + w.d) * kDState + n0;
-      main_block_w<IO, HAS_Z>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w,
+      main_block_w<IO, HAS_Z, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w,
                               sm.main);
     } else {
       const int n0 = k.g * NPL;
@@ -1561,7 +1570,7 @@ void scan_first_kernel(
     }
   } else {
     if constexpr (kWaveForm<G, FUSED, V>)
-      pre_block_w<IO>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k, sm.main);
+      pre_block_w<IO, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k, sm.main);
     else
       pre_block<IO, G, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k,
                                  sm.pre, pro);

@@ -80,10 +80,12 @@ const char *ssm_status_str(int status);
 
 /*
  * Execution plan of a scan: `waves_per_group` (2, 4, 8 or 16) wavefronts
- * share one group of 64 channels, each owning 16/waves_per_group state
- * indices; the sequence is cut into `nchunks` chunks that run in parallel
- * and are stitched by a cross-chunk carry.  The plan changes only the
- * schedule, never the definition of the result.
+ * share one group of 64 channels (with 4, the automatic choice, each wave
+ * owns 16 of the channels with all 16 states; otherwise each wave owns
+ * 16/waves_per_group state indices of all 64 channels); the sequence is cut
+ * into `nchunks` chunks that run in parallel and are stitched by a
+ * cross-chunk carry.  The plan changes only the schedule and the rounding
+ * order of the readout's sum, never the definition of the result.
  *
  * ssm_scan_plan() fills in the plan ssm_scan_fwd() uses for these sizes and,
  * when `phase` is not NULL, the phase value of the schedule it runs in (3:

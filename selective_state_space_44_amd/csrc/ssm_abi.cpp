@@ -70,8 +70,9 @@ int effective_chunks(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks)
 // VALU issue slots go partly idle (measured slow-down for 1 .. 4 resident
 // blocks).  A pre-pass step (state only, from a zero state) costs kPre4 of a
 // main-pass step in a 4-wave block (two-launch schedule, beside chunk 0's main
-// pass) and kPre8 in the 8-wave blocks of the three-pass schedule.
-constexpr double kPre4 = 0.78, kPre8 = 0.72;
+// pass; the wave-independent pre-pass) and kPre8 in the 8-wave blocks of the
+// three-pass schedule.
+constexpr double kPre4 = 0.71, kPre8 = 0.72;
 
 double launch_cost(int64_t nblocks, int64_t len, double weight) {
   static const double slow[kResident] = {1.6, 1.6, 1.25, 1.10, 1.03};

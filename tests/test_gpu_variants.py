@@ -113,6 +113,35 @@ def test_zero_and_delta_edge_cases():
             assert torch.equal(h, h0), (a_kind, disc, G, K)
 
 
+def test_state_A_zeros_and_zero_delta_four_wave_plans():
+    """A per (channel, state) with zeros under both rules, at the 4-wave plans
+    (whose kernels give each wave 16 channels with all their states) with
+    one, three and five chunks and a ragged tail (L = 203), h0 given; and a
+    zero step keeps the state bit for bit under the Euler rule too."""
+    inp = _inputs(W.TINY, "state", seqlen=203)
+    A = inp["A"].clone()
+    A[5, 3] = 0.0
+    A[17, :] = 0.0
+    A[40, 15] = -0.0
+    g = torch.Generator(device=DEV).manual_seed(12)
+    h0 = torch.randn(1, 64, 16, generator=g, device=DEV)
+    p = dict(inp, A=A, h0=h0)
+    for disc in ("zoh", "euler"):
+        y_ref, h_ref = _oracle(p, disc)
+        for K in (1, 3, 5):
+            print(f"A zeros {disc} G=4 K={K}", flush=True)
+            y, h = _run(p, disc, 4, K)
+            torch.cuda.synchronize()
+            parity.check_y(parity.to_f64(y), y_ref, torch.float32, what=f"y {disc} K={K}")
+            parity.check_state(parity.to_f64(h), h_ref, what=f"h {disc} K={K}")
+    q = dict(p, delta=torch.zeros_like(p["delta"]))
+    for disc in ("zoh", "euler"):
+        for K in (1, 3):
+            _, h = _run(q, disc, 4, K)
+            torch.cuda.synchronize()
+            assert torch.equal(h, h0), (disc, K)
+
+
 def test_variant_edge_sizes():
     for a_kind, disc in VARIANTS:
         for (b, L, d) in ((1, 1, 64), (3, 5, 1), (2, 17, 65)):

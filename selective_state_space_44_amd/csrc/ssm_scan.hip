@@ -337,6 +337,14 @@ __device__ __forceinline__ LanePrologue lane_prologue(const Prologue& pro, int d
   return lp;
 }
 
+// x = act(conv_b + sum_k w_k x_raw[t - 3 + k]) for the 4 steps xs = x_raw[t-3 .. t].
+__device__ __forceinline__ float prologue_conv(const LanePrologue& lp, const float (&xs)[4]) {
+  float acc = lp.cb;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(lp.w[k], xs[k], acc);
+  return lp.silu ? silu(acc) : acc;
+}
+
 // softplus(v) = log(1 + exp(v)) in fp32.  log1p(e) with e = exp(v) uses the
 // series e - e^2/2 + e^3/3 - e^4/4 + e^5/5 when e < 2^-7 (truncation below
 // 2^-29 relative) and log(1 + e) through the hardware log2 otherwise; above
@@ -473,12 +481,7 @@ struct FusedLoader {
                          ok ? (uint32_t)(rel + xshift) * row_bytes : 0u);
   }
 
-  __device__ __forceinline__ float conv(const float (&xs)[4]) const {
-    float acc = lp.cb;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(lp.w[k], xs[k], acc);
-    return lp.silu ? silu(acc) : acc;
-  }
+  __device__ __forceinline__ float conv(const float (&xs)[4]) const { return prologue_conv(lp, xs); }
 
   __device__ __forceinline__ void issue(RawTile& r, int s0, int lane) const {
     const int t0 = s0 + g * kSteps;
@@ -800,8 +803,8 @@ __device__ __forceinline__ void main_block(
 }
 
 // ---------------------------------------------------------------------------
-// Main pass, wave-independent form (4 waves per group, no fused prologue, A
-// per (channel, state); ZOH or Euler rule).  Wave w of the block owns the 16 channels
+// Main pass, wave-independent form (4 waves per group, A per (channel,
+// state); ZOH or Euler rule; with or without the fused prologue).  Wave w of the block owns the 16 channels
 // d0 + 16w .. d0 + 16w + 15 with all 16 states: lane l holds channel
 // c = l % 16 of the wave and the states 4r .. 4r + 3 of its row r = l / 16
 // (rows of 16 lanes).  Each wave stages its own tiles of x, delta, B and C
@@ -875,17 +878,32 @@ template <typename IO> struct WRaw {
 
 template <typename IO, bool WITH_C = true>
 struct WLoader {
+  using RawTile = WRaw<IO>;
   __amdgpu_buffer_rsrc_t rx, rd, rb, rc;
-  uint32_t voff, row_bytes;  // voff: row r, channel d (bytes)
+  uint32_t voff, voff_c, row_bytes;  // voff: row r and channel d; voff_c: channel d (bytes)
 
   __device__ __forceinline__ void init(const IO* x, const IO* delta, const IO* B, const IO* C,
-                                       int64_t seqlen, int dim, const Chunk& k, const WLane& w) {
+                                       int64_t seqlen, int dim, const Chunk& k, const WLane& w,
+                                       const LanePrologue&) {
     rx = rows_rsrc(x, k.b, seqlen, dim, k.t_begin, k.t_end);
     rd = rows_rsrc(delta, k.b, seqlen, dim, k.t_begin, k.t_end);
     rb = bc_rsrc(B, k, seqlen);
     rc = bc_rsrc(C, k, seqlen);
     row_bytes = (uint32_t)dim * sizeof(IO);
-    voff = (uint32_t)w.r * row_bytes + (uint32_t)w.d * sizeof(IO);
+    voff_c = (uint32_t)w.d * sizeof(IO);
+    voff = (uint32_t)w.r * row_bytes + voff_c;
+  }
+
+  // x and delta of step s (uniform), straight from memory.
+  __device__ __forceinline__ void step(int s, float& xs, float& ds) const {
+    const uint32_t so = (uint32_t)s * row_bytes;
+    xs = buf<IO>::load(rx, voff_c, so);
+    ds = buf<IO>::load(rd, voff_c, so);
+  }
+
+  // x of step g0 + r (this lane's row), straight from memory.
+  __device__ __forceinline__ float x_row(int g0) const {
+    return buf<IO>::load(rx, voff, (uint32_t)g0 * row_bytes);
   }
 
   // Loads of the (full) tile starting at step s0 of the chunk.
@@ -942,7 +960,131 @@ struct WLoader {
   }
 };
 
-template <typename IO, bool HAS_Z, bool ZERO_A, int V>
+// Loader of the fused scan in the wave-independent form: lane (c, r) produces
+// x = act(conv1d(x_raw) + b) and delta = softplus(delta_raw + bias) of the
+// two consecutive steps 2r and 2r + 1 of each tile for its channel, from
+// x_raw of steps 2r - 3 .. 2r + 1 (zero before the start of the sequence)
+// and delta_raw of its two steps; B and C as in WLoader.
+template <typename IO> struct WFusedRaw {
+  static constexpr int kBC = sizeof(IO) == 2 ? 1 : 2;
+  uint32_t xr[5], dr[2];
+  uint32_t b[kBC], c[kBC];
+};
+
+template <typename IO, bool WITH_C = true>
+struct WFusedLoader {
+  using RawTile = WFusedRaw<IO>;
+  __amdgpu_buffer_rsrc_t rx, rd, rb, rc;
+  uint32_t voff, voff_c, row_bytes;
+  int xshift, r;     // xshift: rows of x_raw kept before the chunk start (0..3)
+  int64_t t_begin;
+  LanePrologue lp;
+
+  __device__ __forceinline__ void init(const IO* x_raw, const IO* delta_raw, const IO* B,
+                                       const IO* C, int64_t seqlen, int dim, const Chunk& k,
+                                       const WLane& w, const LanePrologue& lpin) {
+    const int64_t xb = k.t_begin >= 3 ? k.t_begin - 3 : 0;
+    xshift = (int)(k.t_begin - xb);
+    rx = rows_rsrc(x_raw, k.b, seqlen, dim, xb, k.t_end);
+    rd = rows_rsrc(delta_raw, k.b, seqlen, dim, k.t_begin, k.t_end);
+    rb = bc_rsrc(B, k, seqlen);
+    rc = bc_rsrc(C, k, seqlen);
+    row_bytes = (uint32_t)dim * sizeof(IO);
+    voff_c = (uint32_t)w.d * sizeof(IO);
+    voff = (uint32_t)w.r * row_bytes + voff_c;
+    r = w.r;
+    t_begin = k.t_begin;
+    lp = lpin;
+  }
+
+  // x_raw at step `rel` of the chunk (rel >= -3, uniform); zero before the sequence.
+  __device__ __forceinline__ uint32_t load_x(int rel) const {
+    const bool ok = t_begin + rel >= 0;
+    return Raw<IO>::load(rx, ok ? voff_c : 0x80000000u,
+                         ok ? (uint32_t)(rel + xshift) * row_bytes : 0u);
+  }
+
+  __device__ __forceinline__ void issue(RawTile& t, int s0, int lane) const {
+    // rows 2r - 3 .. 2r + 1 of the tile: the row offset is per lane
+    const int t0 = s0 + 2 * r;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int rel = t0 - 3 + j;
+      const bool ok = t_begin + rel >= 0;
+      t.xr[j] = Raw<IO>::load(rx, ok ? voff_c + (uint32_t)(rel + xshift) * row_bytes : 0x80000000u,
+                              0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      t.dr[j] = Raw<IO>::load(rd, voff_c + (uint32_t)(t0 + j) * row_bytes, 0u);
+    const uint32_t bo = (uint32_t)s0 * kDState * sizeof(IO);
+    if constexpr (sizeof(IO) == 2) {
+      t.b[0] = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * 4u, bo, 0);
+      if constexpr (WITH_C)
+        t.c[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)lane * 4u, bo, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        t.b[e] = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(2 * lane + e) * 4u, bo, 0);
+        if constexpr (WITH_C)
+          t.c[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(2 * lane + e) * 4u, bo, 0);
+      }
+    }
+  }
+
+  // Compute the tile's x and delta into the wave's LDS stage (memory clobbers
+  // as in WLoader::put).
+  __device__ __forceinline__ void put(const RawTile& t, WStage& st, const WLane& w,
+                                      int lane) const {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float xs[4] = {Raw<IO>::f(t.xr[j]), Raw<IO>::f(t.xr[j + 1]), Raw<IO>::f(t.xr[j + 2]),
+                           Raw<IO>::f(t.xr[j + 3])};
+      st.x[w.c * kXS + 2 * w.r + j] = prologue_conv(lp, xs);
+      st.d[w.c * kXS + 2 * w.r + j] = softplus_f32(Raw<IO>::f(t.dr[j]) + lp.db);
+    }
+    if constexpr (sizeof(IO) == 2) {
+      Raw<IO>::put(st.b + 2 * lane, t.b[0] & 0xffffu);
+      Raw<IO>::put(st.b + 2 * lane + 1, t.b[0] >> 16);
+      if constexpr (WITH_C) {
+        Raw<IO>::put(st.c + 2 * lane, t.c[0] & 0xffffu);
+        Raw<IO>::put(st.c + 2 * lane + 1, t.c[0] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        Raw<IO>::put(st.b + 2 * lane + e, t.b[e]);
+        if constexpr (WITH_C) Raw<IO>::put(st.c + 2 * lane + e, t.c[e]);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // x and delta of step s (uniform), computed from memory.
+  __device__ __forceinline__ void step(int s, float& xs, float& ds) const {
+    float w4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w4[k] = Raw<IO>::f(load_x(s - 3 + k));
+    xs = prologue_conv(lp, w4);
+    ds = softplus_f32(Raw<IO>::f(Raw<IO>::load(rd, voff_c, (uint32_t)s * row_bytes)) + lp.db);
+  }
+
+  // x of step g0 + r (this lane's row), computed from memory.
+  __device__ __forceinline__ float x_row(int g0) const {
+    float w4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rel = g0 + r - 3 + k;
+      const bool ok = t_begin + rel >= 0;
+      w4[k] = Raw<IO>::f(Raw<IO>::load(
+          rx, ok ? voff_c + (uint32_t)(rel + xshift) * row_bytes : 0x80000000u, 0u));
+    }
+    return prologue_conv(lp, w4);
+  }
+};
+
+template <typename IO, bool HAS_Z, bool ZERO_A, bool FUSED, int V>
 __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
                                              const IO* __restrict__ delta,
                                              const IO* __restrict__ B, const IO* __restrict__ C,
@@ -950,14 +1092,16 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
                                              float Dd, int64_t seqlen, int dim, const Chunk& k,
                                              const WLane& w, WStage (&sts)[2], float* tw,
                                              const float (&A2)[4], const float (&iA)[4],
-                                             float (&h)[4]) {
+                                             float (&h)[4], const LanePrologue& lp) {
   static_assert((V & kScalarA) == 0, "A per channel uses scan_chunk");
   const int lane = threadIdx.x % kWave;
   const int n0 = 4 * w.r;
   const __amdgpu_buffer_rsrc_t rz = rows_rsrc(HAS_Z ? z : x, k.b, seqlen, dim, k.t_begin, k.t_end);
   const __amdgpu_buffer_rsrc_t ry = rows_rsrc(y, k.b, seqlen, dim, k.t_begin, k.t_end);
-  WLoader<IO> ld;
-  ld.init(x, delta, B, C, seqlen, dim, k, w);
+  using LD = std::conditional_t<FUSED, WFusedLoader<IO, true>, WLoader<IO, true>>;
+  using RawT = typename LD::RawTile;
+  LD ld;
+  ld.init(x, delta, B, C, seqlen, dim, k, w, lp);
   const uint32_t row_bytes = ld.row_bytes;
   // lanes past the last channel store out of the buffer's range (dropped)
   const uint32_t voff_y = w.active ? ld.voff : 0x80000000u;
@@ -983,7 +1127,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
       return pre;
   };
 
-  auto tile = [&](int tidx, int cur, WRaw<IO>& rissue, const WRaw<IO>& rput,
+  auto tile = [&](int tidx, int cur, RawT& rissue, const RawT& rput,
                   const uint32_t (&zuse)[2], uint32_t (&znext)[2]) {
     const int s0 = tidx * kT;
     ld.issue(rissue, min(tidx + 2, nfull - 1) * kT, lane);
@@ -1057,7 +1201,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
   };
 
   if (nfull > 0) {
-    WRaw<IO> ra, rb;
+    RawT ra, rb;
     uint32_t za[2], zb[2];
     ld.issue(ra, 0, lane);
     ld.issue(rb, min(1, nfull - 1) * kT, lane);
@@ -1075,7 +1219,6 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
   // straight from memory; steps past the end contribute a zero partial
   const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
   const __amdgpu_buffer_rsrc_t rcc = bc_rsrc(C, k, seqlen);
-  const uint32_t voff_c = (uint32_t)w.d * sizeof(IO);
   for (int g0 = nfull * kT; g0 < nsteps; g0 += 4) {
     float p[4];
 #pragma unroll
@@ -1083,9 +1226,8 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
       p[u] = 0.0f;
       const int s = g0 + u;
       if (s < nsteps) {
-        const uint32_t so = (uint32_t)s * row_bytes;
-        const float xs = buf<IO>::load(ld.rx, voff_c, so);
-        const float ds = buf<IO>::load(ld.rd, voff_c, so);
+        float xs, ds;
+        ld.step(s, xs, ds);
         const uint32_t bo = (uint32_t)(s * kDState + n0) * sizeof(IO);
         float acc = 0.0f;
 #pragma unroll
@@ -1103,7 +1245,7 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
     const float S = rows_transpose_sum(tw, w, p[0], p[1], p[2], p[3]);
     if (g0 + w.r < nsteps) {  // this row's step of the group
       const uint32_t so = (uint32_t)g0 * row_bytes;
-      const float xs = buf<IO>::load(ld.rx, ld.voff, so);
+      const float xs = ld.x_row(g0);
       const float yv = finish(S, xs, HAS_Z ? Raw<IO>::load(rz, ld.voff, so) : 0u);
       Out<IO>::store(yv, ry, voff_y, so);
     }
@@ -1117,25 +1259,28 @@ __device__ __forceinline__ void scan_chunk_w(const IO* __restrict__ x,
 // back (h = g/A) at the end of the full tiles.  Sum of delta: row r adds
 // steps 2r and 2r + 1 of every tile (fp32 pair, then fp64); the rows' sums
 // are added in row order at the end.
-template <typename IO, bool ZERO_A, int V>
+template <typename IO, bool ZERO_A, bool FUSED, int V>
 __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
                                               const IO* __restrict__ delta,
                                               const IO* __restrict__ B, int64_t seqlen, int dim,
                                               const Chunk& k, const WLane& w,
                                               WStage (&sts)[2], const float (&A2)[4],
-                                              const float (&iA)[4], float (&h)[4], double& sd) {
+                                              const float (&iA)[4], float (&h)[4], double& sd,
+                                              const LanePrologue& lp) {
   static_assert((V & kScalarA) == 0, "A per channel uses chunk_state");
   const int lane = threadIdx.x % kWave;
   const int n0 = 4 * w.r;
-  WLoader<IO, false> ld;
-  ld.init(x, delta, B, B, seqlen, dim, k, w);
+  using LD = std::conditional_t<FUSED, WFusedLoader<IO, false>, WLoader<IO, false>>;
+  using RawT = typename LD::RawTile;
+  LD ld;
+  ld.init(x, delta, B, B, seqlen, dim, k, w, lp);
   const int nsteps = (int)(k.t_end - k.t_begin);
   const int nfull = nsteps / kT;
   float gs[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) gs[n] = 0.0f;
 
-  auto tile = [&](int tidx, int cur, WRaw<IO>& rissue, const WRaw<IO>& rput) {
+  auto tile = [&](int tidx, int cur, RawT& rissue, const RawT& rput) {
     ld.issue(rissue, min(tidx + 2, nfull - 1) * kT, lane);
     const WStage& st = sts[cur];
     float xv[kT], dv[kT];
@@ -1187,7 +1332,7 @@ __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
   };
 
   if (nfull > 0) {
-    WRaw<IO> ra, rb;
+    RawT ra, rb;
     ld.issue(ra, 0, lane);
     ld.issue(rb, min(1, nfull - 1) * kT, lane);
     ld.put(ra, sts[0], w, lane);
@@ -1203,11 +1348,9 @@ __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
 
   // ragged end of the chunk, one step at a time from memory
   const __amdgpu_buffer_rsrc_t rbb = bc_rsrc(B, k, seqlen);
-  const uint32_t voff_c = (uint32_t)w.d * sizeof(IO);
   for (int s0 = nfull * kT; s0 < nsteps; ++s0) {
-    const uint32_t so = (uint32_t)s0 * ld.row_bytes;
-    const float xs = buf<IO>::load(ld.rx, voff_c, so);
-    const float ds = buf<IO>::load(ld.rd, voff_c, so);
+    float xs, ds;
+    ld.step(s0, xs, ds);
     const uint32_t bo = (uint32_t)(s0 * kDState + n0) * sizeof(IO);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -1222,12 +1365,13 @@ __device__ __forceinline__ void chunk_state_w(const IO* __restrict__ x,
 
 // Pre-pass block (chunk c of one 64-channel group from a zero state) in the
 // wave-independent form: writes hloc and the chunk's sum of delta.
-template <typename IO, int V>
+template <typename IO, bool FUSED, int V>
 __device__ __forceinline__ void pre_block_w(const IO* __restrict__ x, const IO* __restrict__ delta,
                                             const float* __restrict__ A,
                                             const IO* __restrict__ B, float* __restrict__ ws_hloc,
                                             double* __restrict__ ws_sdelta, int64_t seqlen,
-                                            int dim, int nchunks, const Chunk& k, WSmem& sm) {
+                                            int dim, int nchunks, const Chunk& k, WSmem& sm,
+                                            const Prologue& pro) {
   const WLane w = wlane(dim);
   WStage(&sts)[2] = sm.st[wave_id()];
   if constexpr (std::is_same<IO, bf16>::value) {
@@ -1238,10 +1382,12 @@ __device__ __forceinline__ void pre_block_w(const IO* __restrict__ x, const IO* 
   float A2[4], iA[4], h[4];
   const bool zero = load_A<4, V>(A, w.d, 4 * w.r, A2, iA);
   double sd = 0.0;
+  LanePrologue lp{};
+  if constexpr (FUSED) lp = lane_prologue(pro, w.d);
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    chunk_state_w<IO, true, V>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
+    chunk_state_w<IO, true, FUSED, V>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd, lp);
   else
-    chunk_state_w<IO, false, V>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd);
+    chunk_state_w<IO, false, FUSED, V>(x, delta, B, seqlen, dim, k, w, sts, A2, iA, h, sd, lp);
   // the rows' sums of delta through the wave's transpose area
   double* td = reinterpret_cast<double*>(sm.tr[wave_id()]);
   asm volatile("" ::: "memory");
@@ -1257,21 +1403,21 @@ __device__ __forceinline__ void pre_block_w(const IO* __restrict__ x, const IO* 
   }
 }
 
-// The wave-independent form serves plans of 4 waves per group without the
-// fused prologue, for A per (channel, state) with either discretisation rule;
-// A per channel, other plans and the fused scan use scan_chunk and
+// The wave-independent form serves plans of 4 waves per group for A per
+// (channel, state) with either discretisation rule, with or without the
+// fused prologue; A per channel and other plans use scan_chunk and
 // chunk_state (with A per channel the wave form measured 9-22% slower).
 template <int G, bool FUSED, int V>
-constexpr bool kWaveForm = (G == 4 && !FUSED && (V & kScalarA) == 0);
+constexpr bool kWaveForm = (G == 4 && (V & kScalarA) == 0);
 
 // Main pass of one block in the wave-independent form: `hinit` and `hout`
 // point at this lane's 4 states (nullable).
-template <typename IO, bool HAS_Z, int V>
+template <typename IO, bool HAS_Z, bool FUSED, int V>
 __device__ __forceinline__ void main_block_w(
     const IO* __restrict__ x, const IO* __restrict__ delta, const float* __restrict__ A,
     const IO* __restrict__ B, const IO* __restrict__ C, const float* __restrict__ Dskip,
     const IO* __restrict__ z, IO* __restrict__ y, const float* hinit, float* hout,
-    int64_t seqlen, int dim, const Chunk& k, const WLane& w, WSmem& sm) {
+    int64_t seqlen, int dim, const Chunk& k, const WLane& w, WSmem& sm, const Prologue& pro) {
   WStage(&sts)[2] = sm.st[wave_id()];
   float* tw = sm.tr[wave_id()];
   if constexpr (std::is_same<IO, bf16>::value) {
@@ -1285,13 +1431,14 @@ __device__ __forceinline__ void main_block_w(
 #pragma unroll
   for (int j = 0; j < 4; ++j) h[j] = hinit ? hinit[j] : 0.0f;
   const float Dd = Dskip ? Dskip[w.d] : 0.0f;
+  LanePrologue lp{};
+  if constexpr (FUSED) lp = lane_prologue(pro, w.d);
   if (__builtin_amdgcn_ballot_w64(zero) != 0)
-    scan_chunk_w<IO, HAS_Z, true, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2, iA,
-                                  h);
+    scan_chunk_w<IO, HAS_Z, true, FUSED, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw,
+                                            A2, iA, h, lp);
   else
-    scan_chunk_w<IO, HAS_Z, false, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts, tw, A2,
-                                      iA,
-                                   h);
+    scan_chunk_w<IO, HAS_Z, false, FUSED, V>(x, delta, B, C, z, y, Dd, seqlen, dim, k, w, sts,
+                                             tw, A2, iA, h, lp);
   if (hout && w.active) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) hout[j] = h[j];
@@ -1323,7 +1470,8 @@ void scan_fwd_kernel(
     else if (h0)
       hinit = h0 + bd * kDState + n0;
     float* hout = (k.c == nchunks - 1 && h_last) ? h_last + bd * kDState + n0 : nullptr;
-    main_block_w<IO, HAS_Z, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w, smw);
+    main_block_w<IO, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k,
+                                      w, smw, pro);
   } else {
     __shared__ MainSmem<G> sm;
     const int n0 = k.g * NPL;
@@ -1558,8 +1706,8 @@ void scan_first_kernel(
       const size_t bd = (size_t)k.b * dim + w.d;
       const float* hinit = h0 ? h0 + bd * kDState + n0 : nullptr;
       float* hout = ws_hin + (((size_t)k.b * nchunks + 1) * dim + w.d) * kDState + n0;
-      main_block_w<IO, HAS_Z, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim, k, w,
-                              sm.main);
+      main_block_w<IO, HAS_Z, FUSED, V>(x, delta, A, B, C, Dskip, z, y, hinit, hout, seqlen, dim,
+                                        k, w, sm.main, pro);
     } else {
       const int n0 = k.g * NPL;
       const size_t bd = (size_t)k.b * dim + k.d;
@@ -1570,7 +1718,8 @@ void scan_first_kernel(
     }
   } else {
     if constexpr (kWaveForm<G, FUSED, V>)
-      pre_block_w<IO, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k, sm.main);
+      pre_block_w<IO, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k, sm.main,
+                                  pro);
     else
       pre_block<IO, G, FUSED, V>(x, delta, A, B, ws_hloc, ws_sdelta, seqlen, dim, nchunks, k,
                                  sm.pre, pro);

@@ -804,18 +804,18 @@ __device__ __forceinline__ void main_block(
 
 // ---------------------------------------------------------------------------
 // Main pass, wave-independent form (4 waves per group, A per (channel,
-// state); ZOH or Euler rule; with or without the fused prologue).  Wave w of the block owns the 16 channels
-// d0 + 16w .. d0 + 16w + 15 with all 16 states: lane l holds channel
-// c = l % 16 of the wave and the states 4r .. 4r + 3 of its row r = l / 16
-// (rows of 16 lanes).  Each wave stages its own tiles of x, delta, B and C
-// through its own LDS region (x and delta as [channel][step], B and C as
-// [step][state]; the row's 16 lanes read the same B/C values), so no barrier
-// couples the block's waves.  Readout: per step every lane forms its 4-state
-// partial; after four steps the partials of the four rows are transposed
-// and summed by two cross-row lane exchanges (rows 0/1 and 2/3, then the two
-// halves of the wave) and three adds, which leave in row r the total of the
-// group's step r, summed in a fixed order.  Row r then finishes that step
-// (skip term, gate, store): each lane stores two steps of a tile.
+// state); ZOH or Euler rule; with or without the fused prologue).  Wave w of
+// the block owns the 16 channels d0 + 16w .. d0 + 16w + 15 with all 16
+// states: lane l holds channel c = l % 16 of the wave and the states
+// 4r .. 4r + 3 of its row r = l / 16 (rows of 16 lanes).  Each wave stages
+// its own tiles of x, delta, B and C through its own LDS region (x and delta
+// as [channel][step], B and C as [step][state]; the row's 16 lanes read the
+// same B/C values), so no barrier couples the block's waves.  Readout: per
+// step every lane forms its 4-state partial; after four steps the partials
+// of the four rows are transposed through the wave's own LDS area and
+// summed, (rows 0 + 1) + (rows 2 + 3), which leaves in row r the total of
+// the group's step r.  Row r then finishes that step (skip term, gate,
+// store): each lane stores two steps of a tile.
 // ---------------------------------------------------------------------------
 constexpr int kWCh = kWave / 4;  // channels per wave
 

@@ -376,6 +376,7 @@ def bench_fused(steps: int, warmup: int):
                            f["delta_bias"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
                            conv_silu=True, out=outs[i % 2], workspace=ws)
 
+    clock_ramp(step, 0.2)  # untimed, as for the headline scan
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -414,6 +415,7 @@ def bench_variants(steps: int, warmup: int):
             ssm.scan_fwd(f["x"], f["delta"], A, f["B"], f["C"], f["D"], f["z"], None,
                          out=outs[i % 2], workspace=ws, discretization=disc)
 
+        clock_ramp(step, 0.2)  # untimed, as for the headline scan
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
@@ -863,9 +865,9 @@ def main():
     if not args.no_decode:
         line["decode"] = bench_decode(args.decode_sweeps)
     if not args.no_fused:
-        line["fused_prologue"] = bench_fused(max(10, args.steps // 4), 10)
+        line["fused_prologue"] = bench_fused(max(20, args.steps // 4), 10)
     if not args.no_variants:
-        line["variants"] = bench_variants(max(10, args.steps // 4), 10)
+        line["variants"] = bench_variants(max(20, args.steps // 4), 10)
     if not args.no_ssd:
         line["ssd"] = bench_ssd(max(10, args.steps // 2), 10)
     if not args.no_backward:

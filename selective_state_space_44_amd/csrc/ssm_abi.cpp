@@ -66,9 +66,10 @@ int effective_chunks(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks)
 // sweeps of three layer shapes on MI355X: batch 4 x 4096 x 5120, 8 x 2048 x
 // 1536 and 1 x 262144 x 4096; it ranks the fastest measured plan first on
 // each).  A launch of n equal blocks of `len` steps keeps its most loaded CU
-// busy for ceil(n / 256) blocks; with fewer than kResident blocks on a CU its
-// VALU issue slots go partly idle (measured slow-down for 1 .. 4 resident
-// blocks).  A pre-pass step (state only, from a zero state) costs kPre4 of a
+// busy for r = ceil(n / 256) blocks, in rounds of kResident resident blocks;
+// with fewer than kResident blocks on a CU (r < kResident, or the last round
+// of a larger r) its VALU issue slots go partly idle (measured slow-down for
+// 1 .. 4 resident blocks).  A pre-pass step (state only, from a zero state) costs kPre4 of a
 // main-pass step in a 4-wave block (two-launch schedule, beside chunk 0's main
 // pass; the wave-independent pre-pass) and kPre8 in the 8-wave blocks of the
 // three-pass schedule.
@@ -77,7 +78,11 @@ constexpr double kPre4 = 0.71, kPre8 = 0.72;
 double launch_cost(int64_t nblocks, int64_t len, double weight) {
   static const double slow[kResident] = {1.6, 1.6, 1.25, 1.10, 1.03};
   const int64_t r = (nblocks + kCUs - 1) / kCUs;
-  return (double)len * (double)r * weight * (r < kResident ? slow[r] : 1.0);
+  // rounds of kResident blocks, then a last round of `part` blocks that runs
+  // at the lower occupancy
+  const int64_t full = r / kResident, part = r % kResident;
+  return (double)len * weight *
+         ((double)(full * kResident) + (part ? (double)part * slow[part] : 0.0));
 }
 
 // Cost of K chunks of `len` steps for `groups` channel groups in the two

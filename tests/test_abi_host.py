@@ -302,14 +302,13 @@ def test_plan_and_workspace(lib):
     # the long single sequence is cut into chunks for parallelism
     g3, k3 = ssm.scan_plan(1, 262144, 4096)
     assert k3 > 1 and 262144 / k3 <= 2048   # chunks of at most 2048 steps
-    # the cost model's choices on the three measured layer shapes, all in the
-    # two-launch schedule: the fastest plan of the sweep for the Mamba-2.8B
-    # and Mamba-130M layers; for the long single sequence 169 chunks (one
-    # launch of exactly 42 blocks per CU), within 0.5% of the fastest measured
-    # plan (256 chunks)
+    # the cost model's choices on the three measured layer shapes (the
+    # fastest plan of each sweep), all in the two-launch schedule; the long
+    # single sequence takes 241 chunks, whose main launch fills 12 whole
+    # rounds of five blocks per CU
     assert ssm.scan_plan(4, 4096, 5120, with_phase=True) == (4, 5, 3)
     assert ssm.scan_plan(8, 2048, 1536, with_phase=True) == (4, 5, 3)
-    assert ssm.scan_plan(1, 262144, 4096, with_phase=True) == (4, 169, 3)
+    assert ssm.scan_plan(1, 262144, 4096, with_phase=True) == (4, 241, 3)
     # one chunk when the sequence is too short to cut: no schedule to choose
     assert ssm.scan_plan(1, 256, 64, dtype=torch.float32, with_phase=True) == (4, 1, 3)
     lib = ssm.load_library()

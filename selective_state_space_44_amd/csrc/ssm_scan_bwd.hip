@@ -152,7 +152,11 @@ __device__ __forceinline__ void stage_tile(TileIn& st, const IO* x, const IO* de
 // ---------------------------------------------------------------------------
 // Reverse pre-pass: the adjoint leaving each chunk (towards its start) when
 // nothing enters it from the right, and the chunk's delta sum.  Chunks
-// 1..nchunks-1 (chunk 0's result is not needed by the composition).
+// 1..nchunks-1 (chunk 0's result is not needed by the composition).  A chunk
+// has at most kBwdChunk steps, so the block stages all of its inputs (delta,
+// dp and C; zeros past the chunk's end, identity steps of the adjoint) with
+// one round of loads and one barrier, then walks the steps last to first; the
+// delta sum adds each 8-step tile's fp32 sum into fp64, tiles last to first.
 // ---------------------------------------------------------------------------
 template <typename IO, int G, bool HAS_Z, int V>
 __global__ __launch_bounds__(kWave* G) void bwd_chunk_adjoint_kernel(
@@ -160,49 +164,50 @@ __global__ __launch_bounds__(kWave* G) void bwd_chunk_adjoint_kernel(
     const IO* __restrict__ z, const IO* __restrict__ dy, float* __restrict__ ws_eloc,
     double* __restrict__ ws_sdr, int64_t seqlen, int64_t chunk_len, int dim, int nchunks) {
   constexpr int NPL = kDState / G;
-  __shared__ TileIn st;
+  __shared__ float sdl[kBwdChunk][kWave];
+  __shared__ float sdp[kBwdChunk][kWave];
+  __shared__ float sc[kBwdChunk][kDState];
   const BwdChunk k = bwd_coords(blockIdx.y + 1, dim, seqlen, chunk_len);
   const int n0 = k.g * NPL;
   float Af[NPL], A2[NPL], e[NPL];
   load_A_bwd<NPL, V>(A, k.d, n0, Af, A2);
 #pragma unroll
   for (int n = 0; n < NPL; ++n) e[n] = 0.0f;
+  // only the adjoint's inputs: delta, dp and C
+  for (int i = threadIdx.x; i < kBwdChunk * kWave; i += kWave * G) {
+    const int s = i / kWave, ch = i % kWave;
+    const int64_t t = k.t0 + s;
+    const int dd = k.d0 + ch;
+    const bool ok = t < k.t1 && dd < dim;
+    const size_t off = ((size_t)k.b * seqlen + (ok ? t : 0)) * dim + (ok ? dd : 0);
+    sdl[s][ch] = ok ? io<IO>::load(delta + off) : 0.0f;
+    const float dyv = ok ? io<IO>::load(dy + off) : 0.0f;
+    if constexpr (HAS_Z) {
+      const float zv = ok ? io<IO>::load(z + off) : 0.0f;
+      sdp[s][ch] = dyv * zv * sigmoid_f(zv);
+    } else {
+      sdp[s][ch] = dyv;
+    }
+  }
+  for (int i = threadIdx.x; i < kBwdChunk * kDState; i += kWave * G) {
+    const int s = i / kDState, n = i % kDState;
+    const int64_t t = k.t0 + s;
+    const bool ok = t < k.t1;
+    sc[s][n] = ok ? io<IO>::load(C + ((size_t)k.b * seqlen + (ok ? t : 0)) * kDState + n) : 0.0f;
+  }
+  __syncthreads();
+  static_assert(kBwdChunk % kBT == 0, "whole tiles per chunk");
   double sd = 0.0;
-  const int nt = (int)((k.t1 - k.t0 + kBT - 1) / kBT);
-  for (int j = nt - 1; j >= 0; --j) {
-    __syncthreads();
-    // only the adjoint's inputs: delta, dp and C
-    for (int i = threadIdx.x; i < kBT * kWave; i += kWave * G) {
-      const int s = i / kWave, ch = i % kWave;
-      const int64_t t = k.t0 + (int64_t)j * kBT + s;
-      const int dd = k.d0 + ch;
-      const bool ok = t < k.t1 && dd < dim;
-      const size_t off = ((size_t)k.b * seqlen + (ok ? t : 0)) * dim + (ok ? dd : 0);
-      st.dl[s][ch] = ok ? io<IO>::load(delta + off) : 0.0f;
-      const float dyv = ok ? io<IO>::load(dy + off) : 0.0f;
-      if constexpr (HAS_Z) {
-        const float zv = ok ? io<IO>::load(z + off) : 0.0f;
-        st.dp[s][ch] = dyv * zv * sigmoid_f(zv);
-      } else {
-        st.dp[s][ch] = dyv;
-      }
-    }
-    for (int i = threadIdx.x; i < kBT * kDState; i += kWave * G) {
-      const int s = i / kDState, n = i % kDState;
-      const int64_t t = k.t0 + (int64_t)j * kBT + s;
-      const bool ok = t < k.t1;
-      st.c[s][n] = ok ? io<IO>::load(C + ((size_t)k.b * seqlen + (ok ? t : 0)) * kDState + n)
-                      : 0.0f;
-    }
-    __syncthreads();
+  for (int j = kBwdChunk / kBT - 1; j >= 0; --j) {
     float tsum = 0.0f;
 #pragma unroll
-    for (int s = kBT - 1; s >= 0; --s) {
-      const float dv = st.dl[s][k.lane];
-      const float dpv = st.dp[s][k.lane];
+    for (int u = kBT - 1; u >= 0; --u) {
+      const int s = j * kBT + u;
+      const float dv = sdl[s][k.lane];
+      const float dpv = sdp[s][k.lane];
       if (k.g == 0) tsum += dv;  // only wave 0 publishes the delta sum
       float cn[NPL];
-      read_states<NPL>(&st.c[s][n0], cn);
+      read_states<NPL>(&sc[s][n0], cn);
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
         const float a = fast_exp2(dv * A2[n]);

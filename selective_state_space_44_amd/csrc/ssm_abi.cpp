@@ -72,11 +72,19 @@ int effective_chunks(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks)
 // 1 .. 4 resident blocks).  A pre-pass step (state only, from a zero state) costs kPre4 of a
 // main-pass step in a 4-wave block (two-launch schedule, beside chunk 0's main
 // pass; the wave-independent pre-pass) and kPre8 in the 8-wave blocks of the
-// three-pass schedule.
+// three-pass schedule.  Four resident blocks (4 waves per SIMD) issue as fast
+// as five: at batch 4 x 4096 x 5120 the main pass ran 60.1 ns per block-step
+// with four per CU against 59.5 with five.
 constexpr double kPre4 = 0.71, kPre8 = 0.72;
+// x and delta of every chunk that gets a pre-pass are read from HBM twice.
+// The issue model does not see that traffic; each whole extra read of x and
+// delta adds kReread to a plan's cost, so that of two plans it rates equal
+// the one that moves fewer bytes wins (the traffic is HBM bandwidth taken
+// from whatever else runs on the GPU).
+constexpr double kReread = 0.01;
 
 double launch_cost(int64_t nblocks, int64_t len, double weight) {
-  static const double slow[kResident] = {1.6, 1.6, 1.25, 1.10, 1.03};
+  static const double slow[kResident] = {1.6, 1.6, 1.25, 1.10, 1.0};
   const int64_t r = (nblocks + kCUs - 1) / kCUs;
   // rounds of kResident blocks, then a last round of `part` blocks that runs
   // at the lower occupancy
@@ -95,9 +103,12 @@ void plan_cost(int64_t groups, int64_t len, int64_t k, double* two, double* thre
     return;
   }
   const int64_t nb = groups * (k - 1);
-  *two = launch_cost(nb, len, (1.0 + kPre4 * (double)(k - 2)) / (double)(k - 1)) +
-         launch_cost(nb, len, 1.0);
-  *three = launch_cost(nb, len, kPre8) + launch_cost(groups * k, len, 1.0);
+  const double kd = (double)k;
+  *two = (launch_cost(nb, len, (1.0 + kPre4 * (double)(k - 2)) / (double)(k - 1)) +
+          launch_cost(nb, len, 1.0)) *
+         (1.0 + kReread * (kd - 2.0) / kd);
+  *three = (launch_cost(nb, len, kPre8) + launch_cost(groups * k, len, 1.0)) *
+           (1.0 + kReread * (kd - 1.0) / kd);
 }
 
 int64_t channel_groups(int64_t batch, int64_t dim) {

@@ -302,11 +302,12 @@ def test_plan_and_workspace(lib):
     # the long single sequence is cut into chunks for parallelism
     g3, k3 = ssm.scan_plan(1, 262144, 4096)
     assert k3 > 1 and 262144 / k3 <= 2048   # chunks of at most 2048 steps
-    # the cost model's choices on the three measured layer shapes (the
-    # fastest plan of each sweep), all in the two-launch schedule; the long
+    # the cost model's choices on the three measured layer shapes, all in the
+    # two-launch schedule: the Mamba-2.8B layer takes 4 chunks (timed equal to
+    # 5 within noise, with a third less of x and delta read twice); the long
     # single sequence takes 241 chunks, whose main launch fills 12 whole
     # rounds of five blocks per CU
-    assert ssm.scan_plan(4, 4096, 5120, with_phase=True) == (4, 5, 3)
+    assert ssm.scan_plan(4, 4096, 5120, with_phase=True) == (4, 4, 3)
     assert ssm.scan_plan(8, 2048, 1536, with_phase=True) == (4, 5, 3)
     assert ssm.scan_plan(1, 262144, 4096, with_phase=True) == (4, 241, 3)
     # one chunk when the sequence is too short to cut: no schedule to choose
@@ -314,7 +315,7 @@ def test_plan_and_workspace(lib):
     lib = ssm.load_library()
     g, k = ctypes.c_int(), ctypes.c_int()
     assert lib.ssm_scan_plan(4, 4096, 5120, 16, ssm.SSM_DTYPE_BF16, ctypes.byref(g),
-                             ctypes.byref(k), None) == ssm.SSM_OK and k.value == 5
+                             ctypes.byref(k), None) == ssm.SSM_OK and k.value == 4
     with pytest.raises(ValueError):
         ssm.scan_workspace_bytes(-1, 10, 10)
 

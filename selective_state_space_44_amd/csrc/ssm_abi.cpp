@@ -64,8 +64,9 @@ int effective_chunks(int64_t seqlen, int64_t dim, int io_dtype, int64_t nchunks)
 
 // Cost model of a chunk plan, in steps on the critical path (fitted to plan
 // sweeps of three layer shapes on MI355X: batch 4 x 4096 x 5120, 8 x 2048 x
-// 1536 and 1 x 262144 x 4096; it ranks the fastest measured plan first on
-// each).  A launch of n equal blocks of `len` steps keeps its most loaded CU
+// 1536 and 1 x 262144 x 4096; it ranks first the fastest measured plan of
+// each, at the first shape the one of two equally fast plans, K = 4 and 5,
+// that reads less).  A launch of n equal blocks of `len` steps keeps its most loaded CU
 // busy for r = ceil(n / 256) blocks, in rounds of kResident resident blocks;
 // with fewer than kResident blocks on a CU (r < kResident, or the last round
 // of a larger r) its VALU issue slots go partly idle (measured slow-down for

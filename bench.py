@@ -519,6 +519,7 @@ def bench_ssd(steps: int, warmup: int):
         ssm.ssd_scan(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], None,
                      out=outs[i % 2])
 
+    clock_ramp(step, 0.2)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()

@@ -104,6 +104,23 @@ def test_full_size_sampled_channels(w):
     parity.check_state(parity.pick(h, ch, 1), h_ref)
 
 
+@pytest.mark.parametrize("schedule", list(SCHEDULES))
+def test_full_size_five_chunks(schedule):
+    """The Mamba-2.8B layer under the five-chunk plan (1280 blocks per launch,
+    five per CU), which the planner rates equal in time to its four-chunk
+    choice: 96 sampled channels (plus the first and last) of every batch row
+    against the oracle, in both schedules."""
+    w = W.MAMBA_2P8B
+    print(f"full {w.name} G=4 K=5 {schedule}", flush=True)
+    inp = _inputs(w)
+    y, h = _run(inp, 4, 5, phase=SCHEDULES[schedule])
+    torch.cuda.synchronize()
+    ch = _sampled_channels(w.dim, 96, 9)
+    y_ref, h_ref = parity.oracle_scan(inp, channels=ch)
+    parity.check_y(parity.pick(y, ch, 2), y_ref, w.io_dtype)
+    parity.check_state(parity.pick(h, ch, 1), h_ref)
+
+
 def long_context_channels(delta, n=256, most_negative=8):
     """Channels of the long-context workload that span its per-channel delta
     bias: ranked by mean delta over the first 4096 steps (the bias dominates
